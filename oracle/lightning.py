@@ -1,0 +1,179 @@
+"""fp64 CPU oracle for the causal Lightning Attention forward pass and decode step.
+
+TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg use this module.  It shares no code with the HIP path: it
+imports NumPy and nothing else, and every function below is a plain
+transcription of the mathematics it cites, in float64.
+
+Sources (page title, then the passage):
+
+* "如何理解MiniMax股价创历史新高？拆解国产大模型技术底座" (vergex.cn), section
+  "Lightning Attention：长上下文为什么突然变得便宜了", the chunkwise teaching
+  code: a running d x dv state starts at zero; for each block the output is the
+  block's queries times the state plus the lower-triangular (diagonal included)
+  in-block score matrix times the block's values; only then is K_b^T V_b added
+  to the state.  The page omits normalisation and stabilisation, so the oracle
+  has none.
+* "MiniMax-01与Lightning Attention" (metaphor-xennon.pages.dev), section 2.2:
+  linear attention drops softmax and uses associativity, phi(Q) (phi(K)^T V);
+  its LinearAttentionCore is the non-causal form (one global K^T V).
+  Section 4.1 table: the key-value state is updated incrementally and the full
+  history is not kept (streaming decode).  Section 1.1 table: 128 attention
+  heads over 32 KV heads (grouped-query attention).
+* "奧特曼的“溫和奇點”愿景，線性注意力的勝利？MiniMax-M1技術報告深度解析"
+  (digipub.cc), the associativity passage: A*B*C = A*(B*C).
+
+Readings where the pages are silent (each pinned in tests/test_oracle.py):
+
+* no normalisation, no 1/sqrt(d) scaling and no feature map inside the
+  operator: inputs arrive already feature-mapped and scaled;
+* the causal mask keeps s <= t (the teaching code's tril keeps the diagonal);
+* the state is read before the block's own update (teaching code order);
+* query head h reads KV head g(h) = h // (Hq // Hkv) (contiguous groups);
+* an optional initial state s_in adds q_t . s_in to every output row;
+* decode updates the state with the new token first, then reads it, so the
+  current token attends to itself as in the forward pass.
+
+Every function is pinned by tests that do not re-type its formula: a
+hand-worked example, closed forms, brute force over Python loops, block-size
+invariance, causality, the final state against a library GEMM, the non-causal
+special case, linearity, GQA against repeated-head MHA, and recurrent/decode
+against the block form.  No function here is parity unpinned.
+
+Layouts: q [B, Hq, N, d], k [B, Hkv, N, d], v [B, Hkv, N, dv],
+o [B, Hq, N, dv], state [B, Hkv, d, dv].  Decode drops the N axis.
+"""
+import numpy as np
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def kv_group(h, Hq, Hkv):
+    """KV head read by query head h: contiguous groups of Hq // Hkv heads."""
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    return h // (Hq // Hkv)
+
+
+def _heads_to_groups(Hq, Hkv):
+    return np.array([kv_group(h, Hq, Hkv) for h in range(Hq)], dtype=np.int64)
+
+
+def _check(q, k, v, s_in):
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be [B, H, N, dim]")
+    B, Hq, N, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if (Bk, Nk, dk) != (B, N, d) or v.shape[:3] != (B, Hkv, N):
+        raise ValueError("shape mismatch between q, k, v")
+    if s_in is not None and s_in.shape != (B, Hkv, d, v.shape[3]):
+        raise ValueError("s_in must be [B, Hkv, d, dv]")
+    return B, Hq, Hkv, N, d, v.shape[3]
+
+
+def brute_force(q, k, v, s_in=None):
+    """Textbook causal sum: o_t = sum_{s<=t} (q_t . k_s) v_s (+ q_t . s_in).
+
+    Builds the full N x N score matrix per head, zeroes entries with s > t and
+    multiplies by V.  Quadratic in N: for small inputs only.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    s_in = None if s_in is None else _f64(s_in)
+    B, Hq, Hkv, N, d, dv = _check(q, k, v, s_in)
+    o = np.zeros((B, Hq, N, dv))
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_group(h, Hq, Hkv)
+            scores = q[b, h] @ k[b, g].T                  # [N, N], entry (t, s)
+            scores = scores * (np.arange(N)[None, :] <= np.arange(N)[:, None])
+            o[b, h] = scores @ v[b, g]
+            if s_in is not None:
+                o[b, h] += q[b, h] @ s_in[b, g]
+    return o
+
+
+def final_state(k, v, s_in=None):
+    """State after all tokens: s_in + K^T V per (batch, KV head)."""
+    k, v = _f64(k), _f64(v)
+    S = np.matmul(np.swapaxes(k, -1, -2), v)
+    if s_in is not None:
+        S = S + _f64(s_in)
+    return S
+
+
+def chunkwise(q, k, v, block, s_in=None):
+    """Block recurrence in the teaching code's order.
+
+    State S starts at s_in (zeros by default).  For each block of `block`
+    tokens (the last one may be shorter):
+        inter = Q_b S          (queries against every earlier block)
+        intra = tril(Q_b K_b^T) V_b   (diagonal kept)
+        O_b   = inter + intra
+        S    <- S + K_b^T V_b  (after the block's output)
+    Returns (o, S_final).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    s_in = None if s_in is None else _f64(s_in)
+    B, Hq, Hkv, N, d, dv = _check(q, k, v, s_in)
+    if block < 1:
+        raise ValueError("block must be >= 1")
+    gidx = _heads_to_groups(Hq, Hkv)
+    S = np.zeros((B, Hkv, d, dv)) if s_in is None else s_in.copy()
+    o = np.zeros((B, Hq, N, dv))
+    for a in range(0, N, block):
+        e = min(a + block, N)
+        qb = q[:, :, a:e]                       # [B, Hq, c, d]
+        kb = k[:, :, a:e]                       # [B, Hkv, c, d]
+        vb = v[:, :, a:e]                       # [B, Hkv, c, dv]
+        kq = kb[:, gidx]                        # KV rows seen by each q head
+        vq = vb[:, gidx]
+        inter = np.matmul(qb, S[:, gidx])
+        intra = np.matmul(np.tril(np.matmul(qb, np.swapaxes(kq, -1, -2))), vq)
+        o[:, :, a:e] = inter + intra
+        S = S + np.matmul(np.swapaxes(kb, -1, -2), vb)
+    return o, S
+
+
+def recurrent(q, k, v, s_in=None):
+    """Token-by-token form: S <- S + k_t^T v_t, then o_t = q_t S.
+
+    This is the tiling box of the xennon page run with one-token tiles
+    (update, then read), which is causal and keeps the diagonal.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    s_in = None if s_in is None else _f64(s_in)
+    B, Hq, Hkv, N, d, dv = _check(q, k, v, s_in)
+    S = np.zeros((B, Hkv, d, dv)) if s_in is None else s_in.copy()
+    o = np.zeros((B, Hq, N, dv))
+    for t in range(N):
+        S, o[:, :, t] = decode_step(S, q[:, :, t], k[:, :, t], v[:, :, t])
+    return o, S
+
+
+def decode_step(S, q, k, v):
+    """One decode token for every (batch, KV head) state.
+
+    S [B, Hkv, d, dv]; q [B, Hq, d]; k [B, Hkv, d]; v [B, Hkv, dv].
+    Rank-one update first (S + k^T v), then each query head in the group
+    reads the updated state.  Returns (S_new, o) with o [B, Hq, dv].
+    """
+    S, q, k, v = _f64(S), _f64(q), _f64(k), _f64(v)
+    B, Hkv, d, dv = S.shape
+    Hq = q.shape[1]
+    if q.shape != (B, Hq, d) or k.shape != (B, Hkv, d) or v.shape != (B, Hkv, dv):
+        raise ValueError("decode shapes do not match the state")
+    S_new = S + k[:, :, :, None] * v[:, :, None, :]
+    gidx = _heads_to_groups(Hq, Hkv)
+    o = np.matmul(q[:, :, None, :], S_new[:, gidx])[:, :, 0, :]
+    return S_new, o
+
+
+def noncausal(q, k, v):
+    """Non-causal linear attention (LinearAttentionCore): q_t (K^T V) for every t."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hq, Hkv, N, d, dv = _check(q, k, v, None)
+    gidx = _heads_to_groups(Hq, Hkv)
+    kv = final_state(k, v)
+    return np.matmul(q, kv[:, gidx])
