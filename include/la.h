@@ -1,0 +1,161 @@
+/*
+ * la.h — C ABI of liblightning.so: causal chunkwise linear attention
+ * (Lightning Attention) forward pass and batched single-token decode on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  Page "如何理解MiniMax股价创历史新高？拆解国产大模型技术底座"
+ * (vergex.cn), section "Lightning Attention：长上下文为什么突然变得便宜了", chunkwise
+ * teaching code: per head, with a running d x dv state S (zero unless s_in is
+ * given), each block of `block` tokens produces
+ *     O_b = Q_b S + tril(Q_b K_b^T) V_b      (diagonal kept)
+ * and only then updates S <- S + K_b^T V_b.  In exact arithmetic this equals
+ *     o_t = q_t . s_in + sum_{s <= t} (q_t . k_s) v_s,
+ * for every block size (associativity; page "MiniMax-01与Lightning Attention",
+ * section 2.2).  No normalisation, scaling or feature map is applied: q and k
+ * arrive already feature-mapped.  Query head h reads KV head h / (Hq / Hkv)
+ * (grouped-query attention with contiguous groups; same page, section 1.1
+ * table: 128 heads over 32 KV heads).
+ *
+ * Layouts (all row-major and contiguous, element strides implied by the
+ * sizes, every pointer 16-byte aligned):
+ *     q [B][Hq][N][d]    k [B][Hkv][N][d]    v [B][Hkv][N][dv]
+ *     o [B][Hq][N][dv]   state [B][Hkv][d][dv] (float32)
+ * Decode tensors drop the N axis: q [B][Hq][d], k [B][Hkv][d], v [B][Hkv][dv],
+ * o [B][Hq][dv].
+ *
+ * Ownership and errors.  Every buffer is device memory owned by the caller;
+ * the library keeps no global mutable state.  Calls are asynchronous on
+ * `stream` (a hipStream_t; NULL is the default stream).  Arguments are
+ * validated before anything is launched: on any error status nothing is
+ * written and nothing is enqueued.  LA_ERR_HIP reports a failed launch or
+ * runtime call; faults during execution surface at the next synchronisation.
+ * No C++ exception crosses this interface.
+ */
+#ifndef LIGHTNING_LA_H
+#define LIGHTNING_LA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LA_OK = 0,
+  LA_ERR_NULL = 1,        /* a required pointer is NULL */
+  LA_ERR_SHAPE = 2,       /* a size <= 0 (N may be 0 for forward), or Hq % Hkv != 0 */
+  LA_ERR_UNSUPPORTED = 3, /* head size, block size or dtype combination not built */
+  LA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  LA_ERR_ALIAS = 5,       /* an output overlaps an input */
+  LA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than la_forward_workspace_bytes */
+  LA_ERR_HIP = 7          /* HIP runtime or launch error */
+} la_status;
+
+typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
+
+/* hipStream_t, passed as an opaque pointer so this header needs no HIP headers. */
+typedef void* la_stream;
+
+/*
+ * Causal forward pass, zero initial state, final state discarded.
+ * in_dtype / out_dtype:
+ *   LA_F32  -> LA_F32   float32 arithmetic throughout (no reduced precision);
+ *                       d in 1..128, dv a multiple of 32 up to 128, block 1..64.
+ *   LA_BF16 -> LA_BF16 or LA_F32
+ *                       bf16 matrix-core products with float32 accumulation and
+ *                       a float32 state; d = dv = 128, block = 64.
+ * N may be 0 (then q, k, v and o may be NULL and only s_out is written) and
+ * need not be a multiple of block: the last block is shorter.  Temporary
+ * workspace (see la_forward_workspace_bytes) is allocated stream-ordered on
+ * `stream` and released after use.
+ */
+la_status la_forward(const void* q, const void* k, const void* v, void* o,
+                     int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                     int64_t d, int64_t dv, int64_t block,
+                     la_dtype in_dtype, la_dtype out_dtype, la_stream stream);
+
+/*
+ * la_forward with state carry and caller-owned workspace.
+ *   s_in   [B][Hkv][d][dv] float32 initial state, or NULL for zeros.
+ *   s_out  [B][Hkv][d][dv] float32 state after token N-1, or NULL.
+ *          s_out may equal s_in (in-place resume); any other overlap with an
+ *          input is LA_ERR_ALIAS.
+ *   workspace / workspace_bytes: at least la_forward_workspace_bytes(...)
+ *          bytes of device memory (may be NULL when that size is 0).  Its
+ *          contents are scratch and need no initialisation.  Concurrent calls
+ *          must not share one workspace.
+ * Resuming is exact up to rounding: forward_ex over tokens [0, M) with s_out,
+ * then over [M, N) with that state as s_in, equals one pass over [0, N).
+ */
+la_status la_forward_ex(const void* q, const void* k, const void* v, void* o,
+                        int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                        int64_t d, int64_t dv, int64_t block,
+                        la_dtype in_dtype, la_dtype out_dtype,
+                        const float* s_in, float* s_out,
+                        void* workspace, size_t workspace_bytes,
+                        la_stream stream);
+
+/*
+ * The two phases of la_forward_ex, for callers that schedule or time them
+ * separately (same arguments and validation as la_forward_ex).
+ *
+ * la_forward_states: the long sequence of each (batch, KV head) is processed
+ * as several segments in parallel; this phase writes into `workspace` the
+ * state at the start of every segment, s_in + sum over earlier tokens of
+ * k_s^T v_s (exact by associativity: page "奧特曼的“溫和奇點”愿景，線性注意力的
+ * 勝利？MiniMax-M1技術報告深度解析" (digipub.cc), the A*B*C = A*(B*C) passage).
+ * It reads k, v and s_in only.  A no-op when the workspace size is 0.
+ *
+ * la_forward_outputs: the outputs and s_out, starting every segment from the
+ * states la_forward_states left in `workspace`.  The caller must have run
+ * la_forward_states with the same sizes, dtype, k, v and s_in on the same
+ * stream first (or with an event dependency); the workspace is read only.
+ */
+la_status la_forward_states(const void* k, const void* v,
+                            int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                            int64_t d, int64_t dv, int64_t block, la_dtype in_dtype,
+                            const float* s_in, void* workspace, size_t workspace_bytes,
+                            la_stream stream);
+
+la_status la_forward_outputs(const void* q, const void* k, const void* v, void* o,
+                             int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                             int64_t d, int64_t dv, int64_t block,
+                             la_dtype in_dtype, la_dtype out_dtype,
+                             const float* s_in, float* s_out,
+                             const void* workspace, size_t workspace_bytes,
+                             la_stream stream);
+
+/*
+ * Workspace bytes la_forward_ex needs for this problem on the current device
+ * (0 when none).  Returns 0 for invalid arguments as well; la_forward_ex then
+ * reports the argument error itself.
+ */
+size_t la_forward_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                                  int64_t d, int64_t dv, int64_t block,
+                                  la_dtype in_dtype);
+
+/*
+ * One decode token for a batch of sequences (page "MiniMax-01与Lightning
+ * Attention", section 4.1 table: the key-value state is updated incrementally
+ * without keeping the history).  For every (b, KV head g):
+ *     S[b][g] <- S[b][g] + k[b][g]^T v[b][g]          (in place, float32)
+ * then for each query head h of group g:
+ *     o[b][h] = q[b][h] . S[b][g]                     (reads the updated state)
+ * so the new token attends to itself, as in the forward pass.
+ *   in_dtype  LA_BF16 or LA_F32 (q, k, v); out_dtype LA_F32 or LA_BF16 (o).
+ *   d in 1..128, dv a multiple of 4 up to 128.  Arithmetic is float32.
+ * Each state is read once and written once per call.
+ */
+la_status la_decode_step(float* S, const void* q, const void* k, const void* v, void* o,
+                         int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int64_t dv,
+                         la_dtype in_dtype, la_dtype out_dtype, la_stream stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* la_status_str(la_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIGHTNING_LA_H */

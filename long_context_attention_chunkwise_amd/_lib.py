@@ -1,0 +1,188 @@
+"""ctypes binding of liblightning.so (declared in include/la.h).
+
+Argument marshalling only: shapes, dtypes and device checks, output
+allocation with torch, and the current torch stream.  Every step of the
+computation runs in the library's HIP kernels; if the library is missing or
+fails to load, every call raises.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblightning.so")
+
+LA_F32, LA_BF16 = 0, 1
+LA_OK = 0
+STATUS_NAMES = {0: "LA_OK", 1: "LA_ERR_NULL", 2: "LA_ERR_SHAPE", 3: "LA_ERR_UNSUPPORTED", 4: "LA_ERR_ALIGN",
+                5: "LA_ERR_ALIAS", 6: "LA_ERR_WORKSPACE", 7: "LA_ERR_HIP"}
+EXPORTS = ("la_forward", "la_forward_ex", "la_forward_states", "la_forward_outputs", "la_forward_workspace_bytes",
+           "la_decode_step", "la_status_str")
+
+_lib = None
+
+
+class LAError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {STATUS_NAMES.get(status, status)} ({status_str(status)})")
+
+
+def load_library(path=LIB_PATH):
+    """Load liblightning.so and declare its C signatures (no GPU needed)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run long_context_attention_chunkwise_amd/build.py")
+    lib = ctypes.CDLL(path)
+    vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    i32 = ctypes.c_int
+    lib.la_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i32, i32, vp]
+    lib.la_forward.restype = i32
+    lib.la_forward_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i32, i32, vp, vp, vp, sz, vp]
+    lib.la_forward_ex.restype = i32
+    lib.la_forward_states.argtypes = [vp, vp, i64, i64, i64, i64, i64, i64, i64, i32, vp, vp, sz, vp]
+    lib.la_forward_states.restype = i32
+    lib.la_forward_outputs.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i32, i32, vp, vp, vp, sz,
+                                       vp]
+    lib.la_forward_outputs.restype = i32
+    lib.la_forward_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, i64, i32]
+    lib.la_forward_workspace_bytes.restype = sz
+    lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp]
+    lib.la_decode_step.restype = i32
+    lib.la_status_str.argtypes = [i32]
+    lib.la_status_str.restype = ctypes.c_char_p
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def status_str(status):
+    return load_library().la_status_str(int(status)).decode()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t == torch.float32:
+        return LA_F32
+    if t == torch.bfloat16:
+        return LA_BF16
+    raise TypeError(f"unsupported dtype {t}; expected float32 or bfloat16")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_tensor(name, t, ndim, device):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def workspace_bytes(B, Hq, Hkv, N, d, dv, block=64, dtype=None):
+    """Bytes of scratch la_forward_ex needs on the current device."""
+    torch = _torch()
+    code = _dtype_code(dtype if dtype is not None else torch.bfloat16)
+    return int(load_library().la_forward_workspace_bytes(B, Hq, Hkv, N, d, dv, block, code))
+
+
+def forward(q, k, v, block=64, out_dtype=None, s_in=None, return_state=False, out=None, s_out=None,
+            workspace=None):
+    """Causal chunkwise linear attention forward pass (la_forward_ex).
+
+    q [B,Hq,N,d], k [B,Hkv,N,d], v [B,Hkv,N,dv] on one GPU, float32 or
+    bfloat16 (all the same).  Returns o [B,Hq,N,dv] (out_dtype, default the
+    input dtype) and, with return_state, the float32 final state
+    [B,Hkv,d,dv].  s_in is an optional float32 initial state.
+    """
+    torch = _torch()
+    lib = load_library()
+    _check_tensor("q", q, 4, None)
+    dev = q.device
+    _check_tensor("k", k, 4, dev)
+    _check_tensor("v", v, 4, dev)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    B, Hq, N, d = q.shape
+    Hkv, dv = k.shape[1], v.shape[3]
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != (B, Hkv, N, dv):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    in_code = _dtype_code(q.dtype)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    out_code = _dtype_code(out_dtype)
+    if s_in is not None:
+        _check_tensor("s_in", s_in, 4, dev)
+        if s_in.dtype != torch.float32 or tuple(s_in.shape) != (B, Hkv, d, dv):
+            raise ValueError("s_in must be float32 [B, Hkv, d, dv]")
+    with torch.cuda.device(dev):
+        if out is None:
+            out = torch.empty((B, Hq, N, dv), dtype=out_dtype, device=dev)
+        else:
+            _check_tensor("out", out, 4, dev)
+            if out.dtype != out_dtype or tuple(out.shape) != (B, Hq, N, dv):
+                raise ValueError("out has the wrong dtype or shape")
+        if return_state and s_out is None:
+            s_out = torch.empty((B, Hkv, d, dv), dtype=torch.float32, device=dev)
+        if s_out is not None:
+            _check_tensor("s_out", s_out, 4, dev)
+            if s_out.dtype != torch.float32 or tuple(s_out.shape) != (B, Hkv, d, dv):
+                raise ValueError("s_out must be float32 [B, Hkv, d, dv]")
+        ws_bytes = int(lib.la_forward_workspace_bytes(B, Hq, Hkv, N, d, dv, block, in_code))
+        if ws_bytes > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.la_forward_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, N, d, dv, block, in_code,
+                               out_code, _ptr(s_in), _ptr(s_out), _ptr(workspace) if ws_bytes else None,
+                               ws_bytes, ctypes.c_void_p(stream))
+    if st != LA_OK:
+        raise LAError(st, "la_forward_ex")
+    if return_state:
+        return out, s_out
+    return out
+
+
+def decode_step(S, q, k, v, out_dtype=None, out=None):
+    """One decode token (la_decode_step): S += k^T v in place, o = q S.
+
+    S [B,Hkv,d,dv] float32; q [B,Hq,d], k [B,Hkv,d], v [B,Hkv,dv] bfloat16 or
+    float32.  Returns o [B,Hq,dv] (out_dtype, default float32).
+    """
+    torch = _torch()
+    lib = load_library()
+    _check_tensor("S", S, 4, None)
+    dev = S.device
+    _check_tensor("q", q, 3, dev)
+    _check_tensor("k", k, 3, dev)
+    _check_tensor("v", v, 3, dev)
+    if S.dtype != torch.float32:
+        raise TypeError("S must be float32")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    B, Hkv, d, dv = S.shape
+    Hq = q.shape[1]
+    if tuple(q.shape) != (B, Hq, d) or tuple(k.shape) != (B, Hkv, d) or tuple(v.shape) != (B, Hkv, dv):
+        raise ValueError("decode shapes do not match the state")
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    with torch.cuda.device(dev):
+        if out is None:
+            out = torch.empty((B, Hq, dv), dtype=out_dtype, device=dev)
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.la_decode_step(_ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, d, dv,
+                                _dtype_code(q.dtype), _dtype_code(out_dtype), ctypes.c_void_p(stream))
+    if st != LA_OK:
+        raise LAError(st, "la_decode_step")
+    return out

@@ -1,0 +1,277 @@
+// Host side of liblightning.so: argument validation, work planning and
+// dispatch to the HIP kernels.  Every check runs before any HIP call, so a
+// rejected call touches neither the device nor the stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "la_internal.h"
+
+namespace {
+
+constexpr int64_t kBf16Block = 64;  // tokens per block of the matrix-core path
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Half-open byte ranges [a, a+na) and [b, b+nb) overlap.
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+  uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+size_t esize(la_dtype t) { return t == LA_F32 ? 4 : 2; }
+
+bool valid_dtype(la_dtype t) { return t == LA_F32 || t == LA_BF16; }
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 256;
+  return cus;
+}
+
+// Shape/dtype checks shared by la_forward_ex and la_forward_workspace_bytes.
+la_status check_forward_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv,
+                              int64_t block, la_dtype in_dtype, la_dtype out_dtype) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || N < 0 || d <= 0 || dv <= 0 || block <= 0) return LA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return LA_ERR_SHAPE;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return LA_ERR_UNSUPPORTED;
+  if (in_dtype == LA_F32) {
+    if (out_dtype != LA_F32) return LA_ERR_UNSUPPORTED;
+    if (d > 128 || dv > 128 || dv % 32 != 0 || block > 64) return LA_ERR_UNSUPPORTED;
+  } else {
+    if (d != 128 || dv != 128 || block != kBf16Block) return LA_ERR_UNSUPPORTED;
+  }
+  // Grid dimensions are 32-bit; keep the workgroup counts well inside that.
+  if (B * Hq > (int64_t(1) << 24) || N > (int64_t(1) << 40)) return LA_ERR_UNSUPPORTED;
+  return LA_OK;
+}
+
+}  // namespace
+
+namespace la {
+
+Bf16Plan plan_bf16(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv, int cus) {
+  Bf16Plan p;
+  const int64_t G = Hq / Hkv;
+  p.gw = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+  p.subgroups = static_cast<int>(G / p.gw);
+  p.nblocks = (N + kBf16Block - 1) / kBf16Block;
+  if (p.nblocks == 0) return p;
+
+  const int64_t kv_chains = B * Hkv;
+  const int64_t main_chains = kv_chains * p.subgroups;
+  // Enough segments for one workgroup per compute unit, each at least
+  // kMinBlocks long so the pre-pass stays a small fraction of the traffic.
+  constexpr int64_t kMinBlocks = 4;
+  int64_t P = 1;
+  if (main_chains < cus) P = (cus + main_chains - 1) / main_chains;
+  P = std::min(P, std::max<int64_t>(1, p.nblocks / kMinBlocks));
+  p.blocks_per_seg = (p.nblocks + P - 1) / P;
+  P = (p.nblocks + p.blocks_per_seg - 1) / p.blocks_per_seg;
+  p.P = static_cast<int>(P);
+
+  if (P > 1) {
+    // Pre-pass parts: about four workgroups per compute unit in total, each
+    // summing at least kMinPartBlocks blocks (a part writes a 64 KiB partial).
+    constexpr int64_t kMinPartBlocks = 8;
+    int64_t R = (4 * int64_t(cus) + kv_chains * (P - 1) - 1) / (kv_chains * (P - 1));
+    R = std::max<int64_t>(1, std::min(R, p.blocks_per_seg / kMinPartBlocks));
+    p.blocks_per_part = (p.blocks_per_seg + R - 1) / R;
+    R = (p.blocks_per_seg + p.blocks_per_part - 1) / p.blocks_per_part;
+    p.R = static_cast<int>(R);
+  }
+  p.use_starts = (P > 1) || (p.subgroups > 1);
+  if (p.use_starts) {
+    p.partial_floats = size_t(kv_chains) * size_t(P - 1) * size_t(p.R) * size_t(d * dv);
+    p.start_floats = size_t(kv_chains) * size_t(P) * size_t(d * dv);
+    p.workspace_bytes = (p.partial_floats + p.start_floats) * sizeof(float);
+  }
+  return p;
+}
+
+}  // namespace la
+
+extern "C" {
+
+const char* la_status_str(la_status s) {
+  switch (s) {
+    case LA_OK: return "ok";
+    case LA_ERR_NULL: return "a required pointer is NULL";
+    case LA_ERR_SHAPE: return "invalid shape (non-positive size or Hq not a multiple of Hkv)";
+    case LA_ERR_UNSUPPORTED: return "unsupported head size, block size or dtype combination";
+    case LA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case LA_ERR_ALIAS: return "an output buffer overlaps an input buffer";
+    case LA_ERR_WORKSPACE: return "workspace missing or too small";
+    case LA_ERR_HIP: return "HIP runtime or launch error";
+  }
+  return "unknown status";
+}
+
+size_t la_forward_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv,
+                                  int64_t block, la_dtype in_dtype) {
+  la_dtype out = in_dtype;
+  if (check_forward_shape(B, Hq, Hkv, N, d, dv, block, in_dtype, out) != LA_OK) return 0;
+  if (in_dtype == LA_F32 || N == 0) return 0;
+  return la::plan_bf16(B, Hq, Hkv, N, d, dv, device_cus()).workspace_bytes;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Everything la_forward_ex, la_forward_states and la_forward_outputs check,
+// in one place.  need_q_o is false for la_forward_states (it reads only k, v).
+struct ForwardCall {
+  la::Bf16Plan plan;
+  size_t ns = 0;  // state bytes
+};
+
+la_status validate_forward(ForwardCall& fc, const void* q, const void* k, const void* v, const void* o,
+                           bool need_q_o, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv,
+                           int64_t block, la_dtype in_dtype, la_dtype out_dtype, const float* s_in,
+                           const float* s_out, const void* workspace, size_t workspace_bytes) {
+  la_status st = check_forward_shape(B, Hq, Hkv, N, d, dv, block, in_dtype, out_dtype);
+  if (st != LA_OK) return st;
+  // With N == 0 the token tensors are empty and may be NULL.
+  if (N > 0 && (k == nullptr || v == nullptr || (need_q_o && (q == nullptr || o == nullptr)))) return LA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(s_in) || !aligned16(s_out))
+    return LA_ERR_ALIGN;
+
+  const size_t ei = esize(in_dtype), eo = esize(out_dtype);
+  const size_t nq = size_t(B * Hq * N * d) * ei, nk = size_t(B * Hkv * N * d) * ei;
+  const size_t nv = size_t(B * Hkv * N * dv) * ei, no = size_t(B * Hq * N * dv) * eo;
+  const size_t ns = size_t(B * Hkv * d * dv) * sizeof(float);
+  fc.ns = ns;
+  if (overlap(o, no, q, nq) || overlap(o, no, k, nk) || overlap(o, no, v, nv) || overlap(o, no, s_in, ns))
+    return LA_ERR_ALIAS;
+  if (s_out != nullptr &&
+      (overlap(s_out, ns, q, nq) || overlap(s_out, ns, k, nk) || overlap(s_out, ns, v, nv) ||
+       overlap(s_out, ns, o, no) || (s_out != s_in && overlap(s_out, ns, s_in, ns))))
+    return LA_ERR_ALIAS;
+
+  if (in_dtype == LA_BF16 && N > 0) {
+    fc.plan = la::plan_bf16(B, Hq, Hkv, N, d, dv, device_cus());
+    const size_t nw = fc.plan.workspace_bytes;
+    if (nw > 0) {
+      if (workspace == nullptr || workspace_bytes < nw) return LA_ERR_WORKSPACE;
+      if (!aligned16(workspace)) return LA_ERR_ALIGN;
+      if (overlap(workspace, nw, q, nq) || overlap(workspace, nw, k, nk) || overlap(workspace, nw, v, nv) ||
+          overlap(workspace, nw, o, no) || overlap(workspace, nw, s_in, ns) || overlap(workspace, nw, s_out, ns))
+        return LA_ERR_ALIAS;
+    }
+  }
+  return LA_OK;
+}
+
+la_status run_states(const ForwardCall& fc, const void* k, const void* v, int64_t B, int64_t Hkv, int64_t N,
+                     la_dtype in_dtype, const float* s_in, void* workspace, hipStream_t hs) {
+  if (in_dtype != LA_BF16 || N == 0 || !fc.plan.use_starts) return LA_OK;
+  return la::launch_segment_states(k, v, s_in, B, Hkv, N, fc.plan, workspace, hs) == hipSuccess ? LA_OK
+                                                                                                  : LA_ERR_HIP;
+}
+
+la_status run_outputs(const ForwardCall& fc, const void* q, const void* k, const void* v, void* o, int64_t B,
+                      int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv, int64_t block, la_dtype in_dtype,
+                      la_dtype out_dtype, const float* s_in, float* s_out, const void* workspace,
+                      hipStream_t hs) {
+  hipError_t err = hipSuccess;
+  if (N == 0) {
+    // No tokens: the final state is the initial state (zeros without s_in).
+    if (s_out != nullptr && s_out != s_in) err = la::launch_copy_or_zero(s_out, s_in, fc.ns / sizeof(float), hs);
+  } else if (in_dtype == LA_F32) {
+    err = la::launch_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                             static_cast<const float*>(v), static_cast<float*>(o), s_in, s_out, B, Hq, Hkv, N,
+                             d, dv, block, hs);
+  } else {
+    err = la::launch_fwd_bf16(q, k, v, o, out_dtype == LA_F32, s_in, s_out, B, Hq, Hkv, N, fc.plan, workspace,
+                              hs);
+  }
+  return err == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+la_status la_forward_ex(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t Hq,
+                        int64_t Hkv, int64_t N, int64_t d, int64_t dv, int64_t block, la_dtype in_dtype,
+                        la_dtype out_dtype, const float* s_in, float* s_out, void* workspace,
+                        size_t workspace_bytes, la_stream stream) {
+  ForwardCall fc;
+  la_status st = validate_forward(fc, q, k, v, o, true, B, Hq, Hkv, N, d, dv, block, in_dtype, out_dtype, s_in,
+                                  s_out, workspace, workspace_bytes);
+  if (st != LA_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  st = run_states(fc, k, v, B, Hkv, N, in_dtype, s_in, workspace, hs);
+  if (st != LA_OK) return st;
+  return run_outputs(fc, q, k, v, o, B, Hq, Hkv, N, d, dv, block, in_dtype, out_dtype, s_in, s_out, workspace,
+                     hs);
+}
+
+la_status la_forward_states(const void* k, const void* v, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                            int64_t d, int64_t dv, int64_t block, la_dtype in_dtype, const float* s_in,
+                            void* workspace, size_t workspace_bytes, la_stream stream) {
+  ForwardCall fc;
+  la_status st = validate_forward(fc, nullptr, k, v, nullptr, false, B, Hq, Hkv, N, d, dv, block, in_dtype,
+                                  in_dtype, s_in, nullptr, workspace, workspace_bytes);
+  if (st != LA_OK) return st;
+  return run_states(fc, k, v, B, Hkv, N, in_dtype, s_in, workspace, static_cast<hipStream_t>(stream));
+}
+
+la_status la_forward_outputs(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t Hq,
+                             int64_t Hkv, int64_t N, int64_t d, int64_t dv, int64_t block, la_dtype in_dtype,
+                             la_dtype out_dtype, const float* s_in, float* s_out, const void* workspace,
+                             size_t workspace_bytes, la_stream stream) {
+  ForwardCall fc;
+  la_status st = validate_forward(fc, q, k, v, o, true, B, Hq, Hkv, N, d, dv, block, in_dtype, out_dtype, s_in,
+                                  s_out, workspace, workspace_bytes);
+  if (st != LA_OK) return st;
+  return run_outputs(fc, q, k, v, o, B, Hq, Hkv, N, d, dv, block, in_dtype, out_dtype, s_in, s_out, workspace,
+                     static_cast<hipStream_t>(stream));
+}
+
+la_status la_forward(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t Hq, int64_t Hkv,
+                     int64_t N, int64_t d, int64_t dv, int64_t block, la_dtype in_dtype, la_dtype out_dtype,
+                     la_stream stream) {
+  la_status st = check_forward_shape(B, Hq, Hkv, N, d, dv, block, in_dtype, out_dtype);
+  if (st != LA_OK) return st;
+  size_t ws = 0;
+  if (in_dtype == LA_BF16 && N > 0) ws = la::plan_bf16(B, Hq, Hkv, N, d, dv, device_cus()).workspace_bytes;
+  if (ws == 0)
+    return la_forward_ex(q, k, v, o, B, Hq, Hkv, N, d, dv, block, in_dtype, out_dtype, nullptr, nullptr,
+                         nullptr, 0, stream);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  void* buf = nullptr;
+  if (hipMallocAsync(&buf, ws, hs) != hipSuccess) return LA_ERR_HIP;
+  st = la_forward_ex(q, k, v, o, B, Hq, Hkv, N, d, dv, block, in_dtype, out_dtype, nullptr, nullptr, buf, ws,
+                     stream);
+  if (hipFreeAsync(buf, hs) != hipSuccess && st == LA_OK) st = LA_ERR_HIP;
+  return st;
+}
+
+la_status la_decode_step(float* S, const void* q, const void* k, const void* v, void* o, int64_t B, int64_t Hq,
+                         int64_t Hkv, int64_t d, int64_t dv, la_dtype in_dtype, la_dtype out_dtype,
+                         la_stream stream) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || dv <= 0 || Hq % Hkv != 0) return LA_ERR_SHAPE;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return LA_ERR_UNSUPPORTED;
+  if (d > 128 || dv > 128 || dv % 4 != 0 || Hq / Hkv > 8 || B * Hkv > (int64_t(1) << 30))
+    return LA_ERR_UNSUPPORTED;
+  if (S == nullptr || q == nullptr || k == nullptr || v == nullptr || o == nullptr) return LA_ERR_NULL;
+  if (!aligned16(S) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return LA_ERR_ALIGN;
+  const size_t ei = esize(in_dtype);
+  const size_t ns = size_t(B * Hkv * d * dv) * sizeof(float);
+  const size_t nq = size_t(B * Hq * d) * ei, nk = size_t(B * Hkv * d) * ei, nv = size_t(B * Hkv * dv) * ei;
+  const size_t no = size_t(B * Hq * dv) * esize(out_dtype);
+  if (overlap(S, ns, q, nq) || overlap(S, ns, k, nk) || overlap(S, ns, v, nv) || overlap(S, ns, o, no) ||
+      overlap(o, no, q, nq) || overlap(o, no, k, nk) || overlap(o, no, v, nv))
+    return LA_ERR_ALIAS;
+  hipError_t err = la::launch_decode(S, q, k, v, o, in_dtype == LA_BF16, out_dtype == LA_F32, B, Hq, Hkv, d,
+                                     dv, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+}  // extern "C"

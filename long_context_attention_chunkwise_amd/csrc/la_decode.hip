@@ -1,0 +1,140 @@
+// Batched single-token decode step of causal linear attention.
+//
+// Page "MiniMax-01与Lightning Attention", section 4.1 table: the key-value
+// state is updated incrementally and the history is not kept.  Per (batch,
+// KV head) state S (d x dv, float32):
+//     S <- S + k^T v                 (rank-one update, in place)
+//     o_h = q_h S   for the query heads h of the group (reads the updated S)
+// The step is bound by HBM bandwidth: each state is streamed from HBM once and
+// written back once, and the G query-head products are formed from the same
+// registers on the way (one pass, no second read of S).
+//
+// One workgroup of 256 threads per state.  Thread (row group rg, column group
+// cg) owns columns [4cg, 4cg+4) of rows rg, rg + nrg, ...: a wave reads whole
+// 512-byte rows with 16-byte accesses.  Per-thread partial products over its
+// rows are reduced across row groups through LDS in a fixed order, so results
+// are deterministic.
+#include "la_internal.h"
+
+namespace la {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxD = 128;
+constexpr int kMaxDV = 128;
+
+template <bool IN_BF16>
+__device__ __forceinline__ float load_in(const void* p, int64_t i) {
+  if (IN_BF16) {
+    const uint32_t bits = uint32_t(static_cast<const uint16_t*>(p)[i]) << 16;
+    return __builtin_bit_cast(float, bits);
+  }
+  return static_cast<const float*>(p)[i];
+}
+
+template <int G, bool IN_BF16, bool OUT_F32>
+__global__ __launch_bounds__(kThreads) void decode_kernel(float* __restrict__ S, const void* __restrict__ q,
+                                                         const void* __restrict__ k, const void* __restrict__ v,
+                                                         void* __restrict__ o, int Hkv, int d, int dv) {
+  __shared__ float qs[G][kMaxD];
+  __shared__ float ks[kMaxD];
+  __shared__ float vs[kMaxDV];
+  __shared__ float4 red[kThreads * G];  // [row group][head][column group]
+
+  const int bg = blockIdx.x;  // b * Hkv + g
+  const int tid = threadIdx.x;
+  const int64_t hq0 = int64_t(bg) * G;  // first query head of the group, flattened over batch
+  for (int i = tid; i < d; i += kThreads) ks[i] = load_in<IN_BF16>(k, int64_t(bg) * d + i);
+  for (int i = tid; i < dv; i += kThreads) vs[i] = load_in<IN_BF16>(v, int64_t(bg) * dv + i);
+  for (int i = tid; i < G * d; i += kThreads) qs[i / d][i % d] = load_in<IN_BF16>(q, hq0 * d + i);
+  __syncthreads();
+
+  const int ncg = dv / 4;        // column groups
+  const int nrg = kThreads / ncg;  // row groups
+  const int cg = tid % ncg, rg = tid / ncg;
+  float4 acc[G];
+  for (int h = 0; h < G; ++h) acc[h] = make_float4(0.f, 0.f, 0.f, 0.f);
+
+  if (rg < nrg) {
+    float4* Sg = reinterpret_cast<float4*>(S + int64_t(bg) * d * dv);
+    const float4 v4 = make_float4(vs[4 * cg], vs[4 * cg + 1], vs[4 * cg + 2], vs[4 * cg + 3]);
+#pragma unroll 4
+    for (int r = rg; r < d; r += nrg) {
+      float4 s = Sg[r * ncg + cg];
+      const float kr = ks[r];
+      s.x = fmaf(kr, v4.x, s.x);
+      s.y = fmaf(kr, v4.y, s.y);
+      s.z = fmaf(kr, v4.z, s.z);
+      s.w = fmaf(kr, v4.w, s.w);
+      Sg[r * ncg + cg] = s;
+      for (int h = 0; h < G; ++h) {
+        const float qr = qs[h][r];
+        acc[h].x = fmaf(qr, s.x, acc[h].x);
+        acc[h].y = fmaf(qr, s.y, acc[h].y);
+        acc[h].z = fmaf(qr, s.z, acc[h].z);
+        acc[h].w = fmaf(qr, s.w, acc[h].w);
+      }
+    }
+    for (int h = 0; h < G; ++h) red[(rg * G + h) * ncg + cg] = acc[h];
+  }
+  __syncthreads();
+
+  // o[h][4c..4c+3] = sum over row groups, in row-group order.
+  for (int e = tid; e < G * ncg; e += kThreads) {
+    const int h = e / ncg, c = e % ncg;
+    float4 sum = red[h * ncg + c];
+    for (int r = 1; r < nrg; ++r) {
+      const float4 x = red[(r * G + h) * ncg + c];
+      sum.x += x.x;
+      sum.y += x.y;
+      sum.z += x.z;
+      sum.w += x.w;
+    }
+    const int64_t off = (hq0 + h) * dv + 4 * c;
+    if (OUT_F32) {
+      *reinterpret_cast<float4*>(static_cast<float*>(o) + off) = sum;
+    } else {
+      uint16_t* ob = static_cast<uint16_t*>(o) + off;
+      const float vals[4] = {sum.x, sum.y, sum.z, sum.w};
+      for (int i = 0; i < 4; ++i) {
+        __bf16 hb = (__bf16)vals[i];
+        ob[i] = __builtin_bit_cast(uint16_t, hb);
+      }
+    }
+  }
+}
+
+template <int G>
+hipError_t launch_g(float* S, const void* q, const void* k, const void* v, void* o, bool in_bf16, bool out_f32,
+                    int64_t B, int64_t Hkv, int64_t d, int64_t dv, hipStream_t stream) {
+  const dim3 grid(unsigned(B * Hkv)), block(kThreads);
+  const int iHkv = int(Hkv), id = int(d), idv = int(dv);
+  if (in_bf16) {
+    if (out_f32) hipLaunchKernelGGL((decode_kernel<G, true, true>), grid, block, 0, stream, S, q, k, v, o, iHkv, id, idv);
+    else hipLaunchKernelGGL((decode_kernel<G, true, false>), grid, block, 0, stream, S, q, k, v, o, iHkv, id, idv);
+  } else {
+    if (out_f32) hipLaunchKernelGGL((decode_kernel<G, false, true>), grid, block, 0, stream, S, q, k, v, o, iHkv, id, idv);
+    else hipLaunchKernelGGL((decode_kernel<G, false, false>), grid, block, 0, stream, S, q, k, v, o, iHkv, id, idv);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(float* S, const void* q, const void* k, const void* v, void* o, bool in_bf16,
+                         bool out_f32, int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int64_t dv,
+                         hipStream_t stream) {
+  switch (Hq / Hkv) {
+    case 1: return launch_g<1>(S, q, k, v, o, in_bf16, out_f32, B, Hkv, d, dv, stream);
+    case 2: return launch_g<2>(S, q, k, v, o, in_bf16, out_f32, B, Hkv, d, dv, stream);
+    case 3: return launch_g<3>(S, q, k, v, o, in_bf16, out_f32, B, Hkv, d, dv, stream);
+    case 4: return launch_g<4>(S, q, k, v, o, in_bf16, out_f32, B, Hkv, d, dv, stream);
+    case 5: return launch_g<5>(S, q, k, v, o, in_bf16, out_f32, B, Hkv, d, dv, stream);
+    case 6: return launch_g<6>(S, q, k, v, o, in_bf16, out_f32, B, Hkv, d, dv, stream);
+    case 7: return launch_g<7>(S, q, k, v, o, in_bf16, out_f32, B, Hkv, d, dv, stream);
+    case 8: return launch_g<8>(S, q, k, v, o, in_bf16, out_f32, B, Hkv, d, dv, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace la

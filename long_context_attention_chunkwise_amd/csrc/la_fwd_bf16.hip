@@ -1,0 +1,457 @@
+// bf16 matrix-core forward pass of causal chunkwise linear attention (gfx950).
+//
+// Method: page "如何理解MiniMax股价创历史新高？拆解国产大模型技术底座" (vergex.cn),
+// section "Lightning Attention", chunkwise teaching code.  For each 64-token
+// block b of a head:
+//     inter = Q_b S                 (S = state before the block)
+//     intra = tril(Q_b K_b^T) V_b   (diagonal kept)
+//     O_b   = inter + intra
+//     S    <- S + K_b^T V_b
+// Query head h reads KV head h / (Hq / Hkv) (page "MiniMax-01与Lightning
+// Attention", section 1.1 table: 128 heads over 32 KV heads), so the state is
+// kept once per KV head and shared by the group's query heads.
+//
+// Design for MI355X:
+//  * One workgroup (8 waves) owns one (batch, KV head, query-head subgroup,
+//    sequence segment) and walks its segment block by block.  The float32
+//    state lives in VGPRs for the whole walk: wave w owns columns
+//    [16w, 16w+16) of S as eight 16x16 MFMA accumulator tiles.
+//  * All products run on v_mfma_f32_16x16x32_bf16 with float32 accumulation.
+//    Every product is computed transposed (O^T, P^T = K Q^T) so that the
+//    accumulator layout of one product is directly the operand layout of the
+//    next: the P^T tiles feed V^T P^T without a shuffle, and the state tiles
+//    are written once per block, rounded to bf16, into an n-major LDS copy
+//    that the Q S product reads with 16-byte loads.
+//  * K and V stay row-major in LDS; the token-contracting products (K^T V and
+//    V^T P^T) read their operands with the gfx950 LDS transpose load
+//    (ds_read_b64_tr_b16), so nothing is transposed in memory.
+//  * Q goes straight from HBM into operand registers (each Q row is read by
+//    exactly one wave); K, V and the bf16 state are double-buffered in LDS so
+//    one barrier per block suffices and the next block's loads are in flight
+//    while the current block computes.
+//  * The sequence split into segments needs each segment's starting state:
+//    a pre-pass sums K_b^T V_b over parts of every segment but the last, and
+//    a scan adds the parts up (s_in first, then parts in order), exact by
+//    associativity of the sums.
+#include "la_internal.h"
+
+namespace la {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(16)));
+typedef __bf16 bf16x4 __attribute__((__vector_size__(8)));
+typedef short short4v __attribute__((__vector_size__(8)));
+typedef float floatx4 __attribute__((__vector_size__(16)));
+typedef __attribute__((address_space(3))) short4v lds_short4v;
+
+constexpr int C = 64;          // tokens per block
+constexpr int D = 128;         // q/k head size
+constexpr int DV = 128;        // v head size
+constexpr int ROW = D + 8;     // LDS row pitch in bf16 elements (272 bytes)
+constexpr int kMainThreads = 512;
+constexpr int kPartThreads = 256;
+
+__device__ __forceinline__ floatx4 mfma(bf16x8 a, bf16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 ld_global16(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  bf16x8 z;
+  for (int i = 0; i < 8; ++i) z[i] = (__bf16)0.0f;
+  return z;
+}
+
+__device__ __forceinline__ bf16x8 ld_lds16(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+// LDS transpose load: each lane of a 16-lane group passes the address of 4
+// consecutive bf16 values; lane i receives column i of the 4 rows the group
+// addressed (see tr_operand).
+__device__ __forceinline__ bf16x4 ld_lds_tr(const uint16_t* p) {
+  lds_short4v* lp = (lds_short4v*)(uint16_t*)p;  // generic -> LDS address space
+  short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lp);
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+// Operand of a token-contracting product, from a row-major [token][col] LDS
+// tile: lane (l16, grp) gets column col0 + l16 at the eight token slots
+//   32p + 4grp + {0..3}  and  32p + 16 + 4grp + {0..3}.
+// The same slot order is used for both operands of every such product, and it
+// matches the accumulator layout of two vertically adjacent 16x16 P^T tiles.
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int p, int col0, int l16, int grp) {
+  const int r = 32 * p + 4 * grp + (l16 >> 2);
+  const int c = col0 + 4 * (l16 & 3);
+  bf16x4 lo = ld_lds_tr(tile + r * ROW + c);
+  bf16x4 hi = ld_lds_tr(tile + (r + 16) * ROW + c);
+  bf16x8 out;
+  for (int i = 0; i < 4; ++i) {
+    out[i] = lo[i];
+    out[i + 4] = hi[i];
+  }
+  return out;
+}
+
+__device__ __forceinline__ bf16x4 to_bf16x4(floatx4 x) {
+  bf16x4 r;
+  for (int i = 0; i < 4; ++i) r[i] = (__bf16)x[i];
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 pack_tiles(floatx4 lo, floatx4 hi) {
+  bf16x8 r;
+  for (int i = 0; i < 4; ++i) {
+    r[i] = (__bf16)lo[i];
+    r[i + 4] = (__bf16)hi[i];
+  }
+  return r;
+}
+
+// Zero the entries of a diagonal P^T tile above the causal boundary: entry
+// (s = 4grp + i, t = l16) within the tile is kept when s <= t.
+__device__ __forceinline__ floatx4 causal_mask(floatx4 x, int l16, int grp) {
+  for (int i = 0; i < 4; ++i)
+    if (4 * grp + i > l16) x[i] = 0.0f;
+  return x;
+}
+
+struct __align__(16) MainSmem {
+  uint16_t k[2][C * ROW];
+  uint16_t v[2][C * ROW];
+  uint16_t st[2][DV * ROW];  // bf16 copy of the state, n-major: st[n][d]
+};
+
+// One block's K and V: 64 rows x 256 bytes each; thread tid moves rows
+// tid/16 and tid/16 + 32, 16-byte chunk tid%16.
+struct KVRegs {
+  uint4 k[2], v[2];
+};
+
+__device__ __forceinline__ void load_kv(KVRegs& r, const uint16_t* kh, const uint16_t* vh, int64_t blk,
+                                        int64_t N, int tid) {
+  const int c = tid & 15;
+  for (int i = 0; i < 2; ++i) {
+    const int64_t t = blk * C + (tid >> 4) + 32 * i;
+    if (t < N) {
+      r.k[i] = *reinterpret_cast<const uint4*>(kh + t * D + 8 * c);
+      r.v[i] = *reinterpret_cast<const uint4*>(vh + t * DV + 8 * c);
+    } else {
+      r.k[i] = make_uint4(0, 0, 0, 0);
+      r.v[i] = make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+__device__ __forceinline__ void store_kv(const KVRegs& r, uint16_t* ks, uint16_t* vs, int tid) {
+  const int c = tid & 15;
+  for (int i = 0; i < 2; ++i) {
+    const int row = (tid >> 4) + 32 * i;
+    *reinterpret_cast<uint4*>(ks + row * ROW + 8 * c) = r.k[i];
+    *reinterpret_cast<uint4*>(vs + row * ROW + 8 * c) = r.v[i];
+  }
+}
+
+template <int GW, bool OUT_F32>
+__global__ __launch_bounds__(kMainThreads, 1) void fwd_bf16_main(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    void* __restrict__ o, const float* starts, const float* s_in, float* s_out, int Hq, int Hkv, int subgroups,
+    int64_t N, int64_t nblocks, int64_t blocks_per_seg, int P) {
+  __shared__ MainSmem sm;
+
+  constexpr int WPH = 8 / GW;  // waves per query head
+  constexpr int NT = 2 * GW;   // 16-column output tiles per wave
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+  const int seg = blockIdx.x % P;
+  const int chain = blockIdx.x / P;
+  const int sub = chain % subgroups;
+  const int bg = chain / subgroups;  // b * Hkv + g
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int G = Hq / Hkv;
+  const int64_t blk0 = int64_t(seg) * blocks_per_seg;
+  const int64_t blk1 = blk0 + blocks_per_seg < nblocks ? blk0 + blocks_per_seg : nblocks;
+
+  // Wave role: query head hw of the subgroup, row tiles {ta, tb} of every
+  // block (the pairing {0,3} / {1,2} balances the causal work), output
+  // columns [16*nt0, 16*(nt0+NT)).
+  const int hw = w / WPH, sw = w % WPH;
+  const int ta = sw & 1, tb = 3 - (sw & 1);
+  const int nt0 = (sw >> 1) * NT;
+
+  const int64_t head = int64_t(b) * Hq + int64_t(g) * G + int64_t(sub) * GW + hw;
+  const uint16_t* qh = q + head * N * D;
+  const uint16_t* kh = k + int64_t(bg) * N * D;
+  const uint16_t* vh = v + int64_t(bg) * N * DV;
+
+  // Starting state of the segment (float32), wave w's column tile.
+  const float* s0 = starts ? starts + (int64_t(bg) * P + seg) * (D * DV)
+                           : (s_in ? s_in + int64_t(bg) * (D * DV) : nullptr);
+  floatx4 sacc[8];
+  for (int dt = 0; dt < 8; ++dt)
+    for (int i = 0; i < 4; ++i)
+      sacc[dt][i] = s0 ? s0[(16 * dt + 4 * grp + i) * DV + 16 * w + l16] : 0.0f;
+
+  if (blk0 < blk1) {
+    KVRegs kv;
+    load_kv(kv, kh, vh, blk0, N, tid);
+    store_kv(kv, sm.k[0], sm.v[0], tid);
+  }
+  for (int dt = 0; dt < 8; ++dt)
+    *reinterpret_cast<bf16x4*>(&sm.st[0][(16 * w + l16) * ROW + 16 * dt + 4 * grp]) = to_bf16x4(sacc[dt]);
+
+  bf16x8 qa[2][4];
+  auto load_q = [&](int64_t blk) {
+    for (int tt = 0; tt < 2; ++tt) {
+      const int64_t t = blk * C + 16 * (tt ? tb : ta) + l16;
+      for (int ds = 0; ds < 4; ++ds)
+        qa[tt][ds] = (t < N) ? ld_global16(qh + t * D + 32 * ds + 8 * grp) : zero_bf16x8();
+    }
+  };
+  if (blk0 < blk1) load_q(blk0);
+  __syncthreads();
+
+  for (int64_t blk = blk0; blk < blk1; ++blk) {
+    const int cur = int(blk - blk0) & 1;
+    const bool has_next = blk + 1 < blk1;
+    const uint16_t* ks = sm.k[cur];
+    const uint16_t* vs = sm.v[cur];
+    const uint16_t* st = sm.st[cur];
+
+    KVRegs kvn;
+    if (has_next) load_kv(kvn, kh, vh, blk + 1, N, tid);
+
+    // inter: O^T[n][t] = sum_d S[d][n] Q[t][d]  (state before this block)
+    floatx4 acc[2][NT];
+    for (int tt = 0; tt < 2; ++tt)
+      for (int j = 0; j < NT; ++j) acc[tt][j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int ds = 0; ds < 4; ++ds) {
+      for (int j = 0; j < NT; ++j) {
+        const bf16x8 sa = ld_lds16(st + (16 * (nt0 + j) + l16) * ROW + 32 * ds + 8 * grp);
+        acc[0][j] = mfma(sa, qa[0][ds], acc[0][j]);
+        acc[1][j] = mfma(sa, qa[1][ds], acc[1][j]);
+      }
+    }
+
+    // scores: P^T[s][t] = sum_d K[s][d] Q[t][d] for s-tiles up to each t-tile
+    floatx4 pa[2], pb[4];
+    for (int i = 0; i < 2; ++i) pa[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = 0; i < 4; ++i) pb[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int ds = 0; ds < 4; ++ds) {
+      for (int si = 0; si < 4; ++si) {
+        if (si > tb) continue;
+        const bf16x8 ka = ld_lds16(ks + (16 * si + l16) * ROW + 32 * ds + 8 * grp);
+        if (si <= ta) pa[si] = mfma(ka, qa[0][ds], pa[si]);
+        pb[si] = mfma(ka, qa[1][ds], pb[si]);
+      }
+    }
+    if (has_next) load_q(blk + 1);
+
+    // causal mask on the diagonal tiles, then bf16 operands for V^T P^T
+    if (ta == 0) pa[0] = causal_mask(pa[0], l16, grp);
+    else pa[1] = causal_mask(pa[1], l16, grp);
+    if (tb == 2) pb[2] = causal_mask(pb[2], l16, grp);
+    else pb[3] = causal_mask(pb[3], l16, grp);
+    const floatx4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    const bf16x8 pA0 = pack_tiles(pa[0], ta == 1 ? pa[1] : zero4);
+    const bf16x8 pB0 = pack_tiles(pb[0], pb[1]);
+    const bf16x8 pB1 = pack_tiles(pb[2], tb == 3 ? pb[3] : zero4);
+
+    // intra: O^T[n][t] += sum_s V[s][n] P^T[s][t]
+    for (int j = 0; j < NT; ++j) {
+      const bf16x8 va0 = tr_operand(vs, 0, 16 * (nt0 + j), l16, grp);
+      const bf16x8 va1 = tr_operand(vs, 1, 16 * (nt0 + j), l16, grp);
+      acc[0][j] = mfma(va0, pA0, acc[0][j]);
+      acc[1][j] = mfma(va0, pB0, acc[1][j]);
+      acc[1][j] = mfma(va1, pB1, acc[1][j]);
+    }
+
+    // store O rows (each lane: 4 consecutive columns of one row per tile)
+    for (int tt = 0; tt < 2; ++tt) {
+      const int64_t t = blk * C + 16 * (tt ? tb : ta) + l16;
+      if (t < N) {
+        for (int j = 0; j < NT; ++j) {
+          const int64_t off = (head * N + t) * DV + 16 * (nt0 + j) + 4 * grp;
+          if (OUT_F32)
+            *reinterpret_cast<floatx4*>(static_cast<float*>(o) + off) = acc[tt][j];
+          else
+            *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(o) + off) = to_bf16x4(acc[tt][j]);
+        }
+      }
+    }
+
+    // state update: S[:, 16w:16w+16] += K_b^T V_b, then its bf16 copy
+    {
+      const bf16x8 vb0 = tr_operand(vs, 0, 16 * w, l16, grp);
+      const bf16x8 vb1 = tr_operand(vs, 1, 16 * w, l16, grp);
+      for (int dt = 0; dt < 8; ++dt) {
+        const bf16x8 k0 = tr_operand(ks, 0, 16 * dt, l16, grp);
+        const bf16x8 k1 = tr_operand(ks, 1, 16 * dt, l16, grp);
+        sacc[dt] = mfma(k0, vb0, sacc[dt]);
+        sacc[dt] = mfma(k1, vb1, sacc[dt]);
+      }
+      uint16_t* stn = sm.st[cur ^ 1];
+      for (int dt = 0; dt < 8; ++dt)
+        *reinterpret_cast<bf16x4*>(&stn[(16 * w + l16) * ROW + 16 * dt + 4 * grp]) = to_bf16x4(sacc[dt]);
+    }
+    if (has_next) store_kv(kvn, sm.k[cur ^ 1], sm.v[cur ^ 1], tid);
+    __syncthreads();
+  }
+
+  if (s_out != nullptr && seg == P - 1 && sub == 0) {
+    float* so = s_out + int64_t(bg) * (D * DV);
+    for (int dt = 0; dt < 8; ++dt)
+      for (int i = 0; i < 4; ++i) so[(16 * dt + 4 * grp + i) * DV + 16 * w + l16] = sacc[dt][i];
+  }
+}
+
+// Pre-pass: partial[c][j][r] = sum of K_b^T V_b over part r of segment j of
+// chain c (every segment but the last).  Four waves; wave w owns state
+// columns [32w, 32w+32).
+__global__ __launch_bounds__(kPartThreads) void state_parts(const uint16_t* __restrict__ k,
+                                                           const uint16_t* __restrict__ v,
+                                                           float* __restrict__ partial, int64_t N,
+                                                           int64_t nblocks, int64_t blocks_per_seg,
+                                                           int64_t blocks_per_part, int P, int R) {
+  __shared__ __align__(16) uint16_t ksm[2][C * ROW];
+  __shared__ __align__(16) uint16_t vsm[2][C * ROW];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+  const int per_chain = (P - 1) * R;
+  const int c = blockIdx.x / per_chain;
+  const int rem = blockIdx.x % per_chain;
+  const int j = rem / R, r = rem % R;
+  const int64_t seg_end = (int64_t(j) + 1) * blocks_per_seg;
+  int64_t b0 = int64_t(j) * blocks_per_seg + int64_t(r) * blocks_per_part;
+  int64_t b1 = b0 + blocks_per_part;
+  if (b1 > seg_end) b1 = seg_end;
+  if (b1 > nblocks) b1 = nblocks;
+
+  const uint16_t* kh = k + int64_t(c) * N * D;
+  const uint16_t* vh = v + int64_t(c) * N * DV;
+
+  floatx4 acc[2][8];
+  for (int jn = 0; jn < 2; ++jn)
+    for (int dt = 0; dt < 8; ++dt) acc[jn][dt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int ch = tid & 15;
+  auto load = [&](int64_t blk, uint4 (&kr)[4], uint4 (&vr)[4]) {
+    for (int i = 0; i < 4; ++i) {
+      const int64_t t = blk * C + (tid >> 4) + 16 * i;
+      if (t < N) {
+        kr[i] = *reinterpret_cast<const uint4*>(kh + t * D + 8 * ch);
+        vr[i] = *reinterpret_cast<const uint4*>(vh + t * DV + 8 * ch);
+      } else {
+        kr[i] = make_uint4(0, 0, 0, 0);
+        vr[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto store = [&](int buf, const uint4 (&kr)[4], const uint4 (&vr)[4]) {
+    for (int i = 0; i < 4; ++i) {
+      const int row = (tid >> 4) + 16 * i;
+      *reinterpret_cast<uint4*>(&ksm[buf][row * ROW + 8 * ch]) = kr[i];
+      *reinterpret_cast<uint4*>(&vsm[buf][row * ROW + 8 * ch]) = vr[i];
+    }
+  };
+
+  if (b0 < b1) {
+    uint4 kr[4], vr[4];
+    load(b0, kr, vr);
+    store(0, kr, vr);
+  }
+  __syncthreads();
+  for (int64_t blk = b0; blk < b1; ++blk) {
+    const int cur = int(blk - b0) & 1;
+    const bool has_next = blk + 1 < b1;
+    uint4 kr[4], vr[4];
+    if (has_next) load(blk + 1, kr, vr);
+    for (int p = 0; p < 2; ++p) {
+      const bf16x8 vb0 = tr_operand(vsm[cur], p, 32 * w, l16, grp);
+      const bf16x8 vb1 = tr_operand(vsm[cur], p, 32 * w + 16, l16, grp);
+      for (int dt = 0; dt < 8; ++dt) {
+        const bf16x8 ka = tr_operand(ksm[cur], p, 16 * dt, l16, grp);
+        acc[0][dt] = mfma(ka, vb0, acc[0][dt]);
+        acc[1][dt] = mfma(ka, vb1, acc[1][dt]);
+      }
+    }
+    if (has_next) store(cur ^ 1, kr, vr);
+    __syncthreads();
+  }
+
+  float* out = partial + ((int64_t(c) * (P - 1) + j) * R + r) * (D * DV);
+  for (int jn = 0; jn < 2; ++jn)
+    for (int dt = 0; dt < 8; ++dt)
+      for (int i = 0; i < 4; ++i) out[(16 * dt + 4 * grp + i) * DV + 32 * w + 16 * jn + l16] = acc[jn][dt][i];
+}
+
+// starts[c][j] = s_in[c] + sum over segments i < j and parts r of partial[c][i][r],
+// accumulated in that fixed order.
+__global__ __launch_bounds__(256) void scan_starts(const float* __restrict__ partial, float* __restrict__ starts,
+                                                   const float* s_in, int P, int R) {
+  constexpr int DD = D * DV;
+  const int64_t gid = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t c = gid / DD;
+  const int e = int(gid % DD);
+  float run = s_in ? s_in[c * DD + e] : 0.0f;
+  for (int j = 0; j < P; ++j) {
+    starts[(c * P + j) * DD + e] = run;
+    if (j < P - 1)
+      for (int r = 0; r < R; ++r) run += partial[((c * (P - 1) + j) * R + r) * DD + e];
+  }
+}
+
+template <int GW, bool OUT_F32>
+void launch_main(dim3 grid, hipStream_t stream, const void* q, const void* k, const void* v, void* o,
+                 const float* starts, const float* s_in, float* s_out, int Hq, int Hkv, int subgroups, int64_t N,
+                 int64_t nblocks, int64_t bps, int P) {
+  hipLaunchKernelGGL((fwd_bf16_main<GW, OUT_F32>), grid, dim3(kMainThreads), 0, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), o, starts, s_in, s_out, Hq, Hkv, subgroups, N, nblocks, bps,
+                     P);
+}
+
+}  // namespace
+
+hipError_t launch_segment_states(const void* k, const void* v, const float* s_in, int64_t B, int64_t Hkv,
+                                 int64_t N, const Bf16Plan& plan, void* workspace, hipStream_t stream) {
+  const int64_t kv_chains = B * Hkv;
+  float* partial = static_cast<float*>(workspace);
+  float* starts = partial + plan.partial_floats;
+  if (plan.P > 1) {
+    hipLaunchKernelGGL(state_parts, dim3(unsigned(kv_chains * (plan.P - 1) * plan.R)), dim3(kPartThreads), 0,
+                       stream, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), partial, N,
+                       plan.nblocks, plan.blocks_per_seg, plan.blocks_per_part, plan.P, plan.R);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(scan_starts, dim3(unsigned(kv_chains * D * DV / 256)), dim3(256), 0, stream, partial, starts,
+                     s_in, plan.P, plan.R);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, bool out_f32, const float* s_in,
+                           float* s_out, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, const Bf16Plan& plan,
+                           const void* workspace, hipStream_t stream) {
+  const int64_t kv_chains = B * Hkv;
+  const float* starts = plan.use_starts ? static_cast<const float*>(workspace) + plan.partial_floats : nullptr;
+  const dim3 grid(unsigned(kv_chains * plan.subgroups * plan.P));
+  const int iHq = int(Hq), iHkv = int(Hkv);
+#define LA_MAIN(GW, F32)                                                                                      \
+  launch_main<GW, F32>(grid, stream, q, k, v, o, starts, plan.use_starts ? nullptr : s_in, s_out, iHq, iHkv, \
+                       plan.subgroups, N, plan.nblocks, plan.blocks_per_seg, plan.P)
+  if (plan.gw == 4) {
+    if (out_f32) LA_MAIN(4, true); else LA_MAIN(4, false);
+  } else if (plan.gw == 2) {
+    if (out_f32) LA_MAIN(2, true); else LA_MAIN(2, false);
+  } else {
+    if (out_f32) LA_MAIN(1, true); else LA_MAIN(1, false);
+  }
+#undef LA_MAIN
+  return hipGetLastError();
+}
+
+}  // namespace la

@@ -1,0 +1,103 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/la.h declares, and rejects bad arguments with the documented status
+before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_attention_chunkwise_amd as la
+from long_context_attention_chunkwise_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "la.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, ALIAS, WORKSPACE = 0, 1, 2, 3, 4, 5, 6
+F32, BF16 = la.LA_F32, la.LA_BF16
+
+# Fake, widely spaced, 16-byte aligned device addresses: validation only
+# compares them, it never dereferences them.
+GB = 1 << 40
+Q, K, V, O, S_IN, S_OUT, WS = (ctypes.c_void_p(GB * i) for i in range(1, 8))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return la.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert names == sorted(_lib.EXPORTS)
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        s = lib.la_status_str(code).decode()
+        assert s and (code == 0) == (s == "ok")
+    assert lib.la_status_str(99).decode() == "unknown status"
+
+
+def fwd(lib, q=Q, k=K, v=V, o=O, B=1, Hq=4, Hkv=1, N=1000, d=128, dv=128, block=64, i=BF16, out=BF16,
+        s_in=None, s_out=None, ws=WS, ws_bytes=1 << 32):
+    return lib.la_forward_ex(q, k, v, o, B, Hq, Hkv, N, d, dv, block, i, out, s_in, s_out, ws, ws_bytes, None)
+
+
+def test_forward_validation(lib):
+    assert fwd(lib, q=None) == NULL
+    assert fwd(lib, o=None) == NULL
+    assert fwd(lib, Hq=6, Hkv=4) == SHAPE
+    assert fwd(lib, B=0) == SHAPE
+    assert fwd(lib, N=-1) == SHAPE
+    assert fwd(lib, d=64) == UNSUP                       # bf16 path is d = dv = 128
+    assert fwd(lib, block=128) == UNSUP
+    assert fwd(lib, i=BF16, out=2) == UNSUP
+    assert fwd(lib, i=F32, out=BF16) == UNSUP
+    assert fwd(lib, i=F32, out=F32, dv=48) == UNSUP       # fp32 path: dv multiple of 32
+    assert fwd(lib, i=F32, out=F32, block=65) == UNSUP
+    assert fwd(lib, q=ctypes.c_void_p(GB + 8)) == ALIGN
+    assert fwd(lib, s_out=ctypes.c_void_p(GB * 6 + 4)) == ALIGN
+    assert fwd(lib, o=ctypes.c_void_p(GB + 4096)) == ALIAS    # o inside q
+    assert fwd(lib, s_out=ctypes.c_void_p(GB * 3 + 64)) == ALIAS  # s_out inside v
+    assert fwd(lib, ws=None) == WORKSPACE
+    assert fwd(lib, ws_bytes=1024) == WORKSPACE
+    assert fwd(lib, ws=ctypes.c_void_p(GB * 2 + 256)) == ALIAS  # workspace inside k
+
+
+def test_decode_validation(lib):
+    def dec(S=S_IN, q=Q, k=K, v=V, o=O, B=2, Hq=8, Hkv=2, d=128, dv=128, i=BF16, out=F32):
+        return lib.la_decode_step(S, q, k, v, o, B, Hq, Hkv, d, dv, i, out, None)
+    assert dec(S=None) == NULL
+    assert dec(Hq=6, Hkv=4) == SHAPE
+    assert dec(dv=126) == UNSUP
+    assert dec(Hq=18, Hkv=2) == UNSUP                     # more than 8 query heads per KV head
+    assert dec(o=ctypes.c_void_p(GB * 4 + 2)) == ALIGN
+    assert dec(o=ctypes.c_void_p(GB * 5 + 16)) == ALIAS   # o inside S
+
+
+def test_workspace_plan(lib):
+    # Host planning with the default 256 compute units (no device here): the
+    # 1M-token GQA problem splits each of the 32 chains into 8 segments and
+    # every segment but the last into 5 pre-pass parts.
+    n = lib.la_forward_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, 64, BF16)
+    assert n == (32 * 7 * 5 + 32 * 8) * 128 * 128 * 4
+    assert lib.la_forward_workspace_bytes(1, 1, 1, 256, 64, 64, 64, F32) == 0
+    assert lib.la_forward_workspace_bytes(256, 128, 32, 8192, 128, 128, 64, BF16) == 0
+    assert lib.la_forward_workspace_bytes(1, 128, 32, 0, 128, 128, 64, BF16) == 0
+    assert lib.la_forward_workspace_bytes(1, 6, 4, 64, 128, 128, 64, BF16) == 0   # invalid -> 0
+
+
+def test_binding_requires_gpu_tensors():
+    import torch
+    x = torch.zeros((1, 1, 4, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        la.forward(x, x, x)
