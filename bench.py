@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Benchmark of the causal chunkwise linear attention (Lightning Attention) hot path.
+
+Forward pass (the headline): one step = la_forward_states + la_forward_outputs
+(exactly la_forward_ex) over the 1,048,576-token grouped-query workload
+(B=1, 128 query heads over 32 KV heads, d = dv = 128, bf16 inputs and output,
+float32 state, 64-token blocks), seeded synthetic inputs resident in HBM.
+Reported: tokens/s, TFLOP/s against the bf16 dense matrix-core peak, and the
+HBM roofline of the dominant kernel (the output kernel), timed with HIP
+events on the stream it runs on.
+
+Decode (secondary): 256 sequences x 32 KV heads of float32 128x128 state
+(512 MiB) initialised by the forward kernel over a seeded 8192-token prefix,
+then single-token steps; reported as HBM GB/s.
+
+CPU baseline: the fp64 oracle (test infrastructure) timed on a bounded sample
+of the same forward workload on this host.
+
+Prints ONE JSON line.  Single GPU only.
+"""
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Lightning-attn fwd tokens/s + % bf16 MFMA peak at N=1M; decode HBM GB/s"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak, TFLOP/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def forward_flops(w, N):
+    """Algorithmic flops of the causal forward (per the block recurrence).
+
+    Per token and query head: in-block scores d(C+1) and their product with V
+    dv(C+1) (lower triangle incl. diagonal, 2 flops per multiply-add), the
+    inter-block product 2 d dv, and the state update 2 d dv shared by the
+    Hq/Hkv query heads of a KV head.  The dense-tile count (what the matrix
+    cores execute) replaces C+1 by 2C.
+    """
+    C, d, dv, G = w.block, w.d, w.dv, w.Hq // w.Hkv
+    per_alg = (d + dv) * (C + 1) + 2 * d * dv + 2 * d * dv / G
+    per_tile = (d + dv) * 2 * C + 2 * d * dv + 2 * d * dv / G
+    n = w.B * w.Hq * N
+    return per_alg * n, per_tile * n
+
+
+def forward_bytes(w, N, out_bytes=2):
+    """Algorithmic HBM bytes of one forward pass: read q, k, v once, write o once."""
+    e = 2  # bf16
+    return w.B * N * (w.Hq * w.d * e + w.Hkv * (w.d + w.dv) * e + w.Hq * w.dv * out_bytes)
+
+
+def cpu_baseline(q, k, v, w, group=0):
+    """Time the fp64 oracle on one KV group (its G query heads, all tokens)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity mask
+        threads = len(os.sched_getaffinity(0))
+    G = w.Hq // w.Hkv
+    N = q.shape[2]
+    qs = q[:, group * G:(group + 1) * G].float().cpu().numpy().astype(np.float64)
+    ks = k[:, group:group + 1].float().cpu().numpy().astype(np.float64)
+    vs = v[:, group:group + 1].float().cpu().numpy().astype(np.float64)
+    t0 = time.perf_counter()
+    oracle.chunkwise(qs, ks, vs, w.block)
+    dt = time.perf_counter() - t0
+    # The sample is 1/Hkv of the work per token of the full workload.
+    return {"value": N / dt / w.Hkv, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 chunkwise oracle on KV head {group} (query heads {group * G}-{group * G + G - 1}), "
+                      f"all {N} tokens, {dt:.2f} s; value scaled to the full {w.Hkv}-KV-head workload "
+                      f"(x1/{w.Hkv})"}
+
+
+def bench_forward(la, synth, torch, w, steps, warmup):
+    import ctypes
+    lib = la.load_library()
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d} dv={w.dv}")
+    q, k, v = synth.make_qkv(w, dev, seed=0)
+    o = torch.empty((w.B, w.Hq, w.N, w.dv), dtype=torch.bfloat16, device=dev)
+    ws_bytes = la.workspace_bytes(w.B, w.Hq, w.Hkv, w.N, w.d, w.dv, w.block, torch.bfloat16)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = ctypes.c_void_p
+    args_states = (P(k.data_ptr()), P(v.data_ptr()), w.B, w.Hq, w.Hkv, w.N, w.d, w.dv, w.block, la.LA_BF16,
+                   None, P(ws.data_ptr()), ws_bytes, sp)
+    args_out = (P(q.data_ptr()), P(k.data_ptr()), P(v.data_ptr()), P(o.data_ptr()), w.B, w.Hq, w.Hkv, w.N, w.d,
+                w.dv, w.block, la.LA_BF16, la.LA_BF16, None, None, P(ws.data_ptr()), ws_bytes, sp)
+
+    def step(evs=None):
+        if evs:
+            evs[0].record(stream)
+        st = lib.la_forward_states(*args_states)
+        if evs:
+            evs[1].record(stream)
+        st2 = lib.la_forward_outputs(*args_out)
+        if evs:
+            evs[2].record(stream)
+        if st or st2:
+            raise RuntimeError(f"forward failed: {la.status_str(st or st2)}")
+
+    for _ in range(warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / steps
+    t_states = [e[0].elapsed_time(e[1]) for e in evs]
+    t_main = [e[1].elapsed_time(e[2]) for e in evs]
+    finite = bool(torch.isfinite(o).all().item())
+    if not finite:
+        raise RuntimeError("non-finite forward output")
+    return q, k, v, ms_step, statistics.mean(t_states), statistics.mean(t_main), ws_bytes
+
+
+def bench_decode(la, synth, torch, w, steps, warmup):
+    dev = torch.device("cuda:0")
+    S = torch.empty((w.B, w.Hkv, w.d, w.dv), dtype=torch.float32, device=dev)
+    batch = 32
+    log(f"[bench] decode prefix: {w.B} sequences x {w.N} tokens through the forward kernel, {batch} at a time")
+    for i in range(0, w.B, batch):
+        q, k, v = synth.make_qkv(w, dev, seed=1000 + i // batch, B=batch)
+        la.forward(q, k, v, s_out=S[i:i + batch])
+        del q, k, v
+    torch.cuda.synchronize()
+    T = steps + warmup
+    qs, ks, vs = synth.make_decode_steps(w, dev, seed=1, steps=T)
+    o = torch.empty((w.B, w.Hq, w.dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for t in range(warmup):
+        la.decode_step(S, qs[t], ks[t], vs[t], out=o)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        t = warmup + i
+        evs[i][0].record(stream)
+        la.decode_step(S, qs[t], ks[t], vs[t], out=o)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    per = [a.elapsed_time(b) for a, b in evs]
+    step_bytes = (2 * S.numel() * 4 + qs[0].numel() * 2 + ks[0].numel() * 2 + vs[0].numel() * 2 + o.numel() * 4)
+    mean_ms = statistics.mean(per)
+    gbs = step_bytes / (mean_ms * 1e-3) / 1e9
+    return {"steps": steps, "warmup": warmup, "ms_per_step": round(mean_ms, 5),
+            "ms_per_step_median": round(statistics.median(per), 5), "ms_per_step_wall": round(wall, 5),
+            "gb_per_s": round(gbs, 1), "unit": "GB/s",
+            "config": {"workload": w.name, "sequences": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "dv": w.dv,
+                       "prefix_tokens": w.N, "state_dtype": "f32", "io_dtype": "bf16 in, f32 out"},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "bytes_per_launch": step_bytes}}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gqa_1m", help="forward workload name (synth.WORKLOADS)")
+    ap.add_argument("--decode-steps", type=int, default=1000, help="0 skips the decode measurement")
+    ap.add_argument("--decode-warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (hardware-counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import long_context_attention_chunkwise_amd as la
+    from long_context_attention_chunkwise_amd import synth
+    la.load_library()  # fails loudly when the HIP library is missing
+
+    w = synth.WORKLOADS[args.workload]
+    props = torch.cuda.get_device_properties(0)
+    q, k, v, ms_step, ms_states, ms_main, ws_bytes = bench_forward(la, synth, torch, w, args.steps, args.warmup)
+    tokens = w.B * w.N
+    value = tokens / (ms_step * 1e-3)
+    f_alg, f_tile = forward_flops(w, w.N)
+    bytes_main = forward_bytes(w, w.N)
+    achieved = bytes_main / (ms_main * 1e-3) / 1e9
+    log(f"[bench] forward: {ms_step:.3f} ms/step (states {ms_states:.3f} ms, outputs {ms_main:.3f} ms)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] CPU baseline (fp64 oracle) ...")
+        cpu = cpu_baseline(q, k, v, w)
+    del q, k, v
+    torch.cuda.empty_cache()
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    decode = None
+    if args.decode_steps > 0:
+        decode = bench_decode(la, synth, torch, synth.WORKLOADS["decode_256"], args.decode_steps,
+                              args.decode_warmup)
+        log(f"[bench] decode: {decode['ms_per_step']:.4f} ms/step, {decode['gb_per_s']:.0f} GB/s")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "seq_len": w.N, "d": w.d,
+                   "dv": w.dv, "block": w.block, "io_dtype": "bf16", "state_dtype": "f32"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "fwd_bf16_main", "kernel_ms": round(ms_main, 4), "bytes_per_launch": bytes_main},
+        "mfma": {"tflops_alg": round(f_alg / (ms_step * 1e-3) / 1e12, 2),
+                 "frac_alg": round(f_alg / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                 "tflops_tile": round(f_tile / (ms_step * 1e-3) / 1e12, 2),
+                 "frac_tile": round(f_tile / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                 "peak_tflops": PEAK_BF16_TFLOPS, "flops_alg": f_alg, "flops_tile": f_tile},
+        "phases_ms": {"segment_states": round(ms_states, 4), "outputs": round(ms_main, 4)},
+        "workspace_bytes": ws_bytes,
+        "decode": decode,
+        "cpu_baseline": cpu,
+        "device": {"name": props.name, "gcnArchName": getattr(props, "gcnArchName", ""),
+                   "cus": props.multi_processor_count},
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
