@@ -47,7 +47,13 @@ typedef __attribute__((address_space(3))) short4v lds_short4v;
 constexpr int C = 64;          // tokens per block
 constexpr int D = 128;         // q/k head size
 constexpr int DV = 128;        // v head size
-constexpr int ROW = D + 8;     // LDS row pitch in bf16 elements (272 bytes)
+// LDS row pitches (bf16 elements).  K and V tiles are read mostly through the
+// transpose load (a half-wave touches 8 consecutive rows x 16 bytes): a
+// 288-byte pitch puts those rows on disjoint banks.  The bf16 state is read
+// with 16-byte loads of 16 consecutive rows: a 272-byte pitch does the same
+// for that pattern.
+constexpr int ROWKV = D + 16;
+constexpr int ROWST = D + 8;
 constexpr int kMainThreads = 512;
 constexpr int kPartThreads = 256;
 
@@ -84,8 +90,8 @@ __device__ __forceinline__ bf16x4 ld_lds_tr(const uint16_t* p) {
 __device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int p, int col0, int l16, int grp) {
   const int r = 32 * p + 4 * grp + (l16 >> 2);
   const int c = col0 + 4 * (l16 & 3);
-  bf16x4 lo = ld_lds_tr(tile + r * ROW + c);
-  bf16x4 hi = ld_lds_tr(tile + (r + 16) * ROW + c);
+  bf16x4 lo = ld_lds_tr(tile + r * ROWKV + c);
+  bf16x4 hi = ld_lds_tr(tile + (r + 16) * ROWKV + c);
   bf16x8 out;
   for (int i = 0; i < 4; ++i) {
     out[i] = lo[i];
@@ -118,9 +124,9 @@ __device__ __forceinline__ floatx4 causal_mask(floatx4 x, int l16, int grp) {
 }
 
 struct __align__(16) MainSmem {
-  uint16_t k[2][C * ROW];
-  uint16_t v[2][C * ROW];
-  uint16_t st[2][DV * ROW];  // bf16 copy of the state, n-major: st[n][d]
+  uint16_t k[2][C * ROWKV];
+  uint16_t v[2][C * ROWKV];
+  uint16_t st[2][DV * ROWST];  // bf16 copy of the state, n-major: st[n][d]
 };
 
 // One block's K and V: 64 rows x 256 bytes each; thread tid moves rows
@@ -148,8 +154,8 @@ __device__ __forceinline__ void store_kv(const KVRegs& r, uint16_t* ks, uint16_t
   const int c = tid & 15;
   for (int i = 0; i < 2; ++i) {
     const int row = (tid >> 4) + 32 * i;
-    *reinterpret_cast<uint4*>(ks + row * ROW + 8 * c) = r.k[i];
-    *reinterpret_cast<uint4*>(vs + row * ROW + 8 * c) = r.v[i];
+    *reinterpret_cast<uint4*>(ks + row * ROWKV + 8 * c) = r.k[i];
+    *reinterpret_cast<uint4*>(vs + row * ROWKV + 8 * c) = r.v[i];
   }
 }
 
@@ -200,19 +206,21 @@ __global__ __launch_bounds__(kMainThreads, 1) void fwd_bf16_main(
     store_kv(kv, sm.k[0], sm.v[0], tid);
   }
   for (int dt = 0; dt < 8; ++dt)
-    *reinterpret_cast<bf16x4*>(&sm.st[0][(16 * w + l16) * ROW + 16 * dt + 4 * grp]) = to_bf16x4(sacc[dt]);
+    *reinterpret_cast<bf16x4*>(&sm.st[0][(16 * w + l16) * ROWST + 16 * dt + 4 * grp]) = to_bf16x4(sacc[dt]);
 
-  bf16x8 qa[2][4];
-  auto load_q = [&](int64_t blk) {
+  bf16x8 qa[2][4], qn[2][4];
+  auto load_q = [&](bf16x8 (&dst)[2][4], int64_t blk) {
     for (int tt = 0; tt < 2; ++tt) {
       const int64_t t = blk * C + 16 * (tt ? tb : ta) + l16;
       for (int ds = 0; ds < 4; ++ds)
-        qa[tt][ds] = (t < N) ? ld_global16(qh + t * D + 32 * ds + 8 * grp) : zero_bf16x8();
+        dst[tt][ds] = (t < N) ? ld_global16(qh + t * D + 32 * ds + 8 * grp) : zero_bf16x8();
     }
   };
-  if (blk0 < blk1) load_q(blk0);
+  if (blk0 < blk1) load_q(qa, blk0);
   __syncthreads();
 
+  // qa holds this block's Q operands; the next block's Q is loaded into qn at
+  // the start, so it has a whole block to arrive.
   for (int64_t blk = blk0; blk < blk1; ++blk) {
     const int cur = int(blk - blk0) & 1;
     const bool has_next = blk + 1 < blk1;
@@ -221,7 +229,10 @@ __global__ __launch_bounds__(kMainThreads, 1) void fwd_bf16_main(
     const uint16_t* st = sm.st[cur];
 
     KVRegs kvn;
-    if (has_next) load_kv(kvn, kh, vh, blk + 1, N, tid);
+    if (has_next) {
+      load_q(qn, blk + 1);
+      load_kv(kvn, kh, vh, blk + 1, N, tid);
+    }
 
     // inter: O^T[n][t] = sum_d S[d][n] Q[t][d]  (state before this block)
     floatx4 acc[2][NT];
@@ -229,7 +240,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void fwd_bf16_main(
       for (int j = 0; j < NT; ++j) acc[tt][j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     for (int ds = 0; ds < 4; ++ds) {
       for (int j = 0; j < NT; ++j) {
-        const bf16x8 sa = ld_lds16(st + (16 * (nt0 + j) + l16) * ROW + 32 * ds + 8 * grp);
+        const bf16x8 sa = ld_lds16(st + (16 * (nt0 + j) + l16) * ROWST + 32 * ds + 8 * grp);
         acc[0][j] = mfma(sa, qa[0][ds], acc[0][j]);
         acc[1][j] = mfma(sa, qa[1][ds], acc[1][j]);
       }
@@ -242,12 +253,11 @@ __global__ __launch_bounds__(kMainThreads, 1) void fwd_bf16_main(
     for (int ds = 0; ds < 4; ++ds) {
       for (int si = 0; si < 4; ++si) {
         if (si > tb) continue;
-        const bf16x8 ka = ld_lds16(ks + (16 * si + l16) * ROW + 32 * ds + 8 * grp);
+        const bf16x8 ka = ld_lds16(ks + (16 * si + l16) * ROWKV + 32 * ds + 8 * grp);
         if (si <= ta) pa[si] = mfma(ka, qa[0][ds], pa[si]);
         pb[si] = mfma(ka, qa[1][ds], pb[si]);
       }
     }
-    if (has_next) load_q(blk + 1);
 
     // causal mask on the diagonal tiles, then bf16 operands for V^T P^T
     if (ta == 0) pa[0] = causal_mask(pa[0], l16, grp);
@@ -294,9 +304,13 @@ __global__ __launch_bounds__(kMainThreads, 1) void fwd_bf16_main(
       }
       uint16_t* stn = sm.st[cur ^ 1];
       for (int dt = 0; dt < 8; ++dt)
-        *reinterpret_cast<bf16x4*>(&stn[(16 * w + l16) * ROW + 16 * dt + 4 * grp]) = to_bf16x4(sacc[dt]);
+        *reinterpret_cast<bf16x4*>(&stn[(16 * w + l16) * ROWST + 16 * dt + 4 * grp]) = to_bf16x4(sacc[dt]);
     }
-    if (has_next) store_kv(kvn, sm.k[cur ^ 1], sm.v[cur ^ 1], tid);
+    if (has_next) {
+      store_kv(kvn, sm.k[cur ^ 1], sm.v[cur ^ 1], tid);
+      for (int tt = 0; tt < 2; ++tt)
+        for (int ds = 0; ds < 4; ++ds) qa[tt][ds] = qn[tt][ds];
+    }
     __syncthreads();
   }
 
@@ -315,8 +329,8 @@ __global__ __launch_bounds__(kPartThreads) void state_parts(const uint16_t* __re
                                                            float* __restrict__ partial, int64_t N,
                                                            int64_t nblocks, int64_t blocks_per_seg,
                                                            int64_t blocks_per_part, int P, int R) {
-  __shared__ __align__(16) uint16_t ksm[2][C * ROW];
-  __shared__ __align__(16) uint16_t vsm[2][C * ROW];
+  __shared__ __align__(16) uint16_t ksm[2][C * ROWKV];
+  __shared__ __align__(16) uint16_t vsm[2][C * ROWKV];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
@@ -353,8 +367,8 @@ __global__ __launch_bounds__(kPartThreads) void state_parts(const uint16_t* __re
   auto store = [&](int buf, const uint4 (&kr)[4], const uint4 (&vr)[4]) {
     for (int i = 0; i < 4; ++i) {
       const int row = (tid >> 4) + 16 * i;
-      *reinterpret_cast<uint4*>(&ksm[buf][row * ROW + 8 * ch]) = kr[i];
-      *reinterpret_cast<uint4*>(&vsm[buf][row * ROW + 8 * ch]) = vr[i];
+      *reinterpret_cast<uint4*>(&ksm[buf][row * ROWKV + 8 * ch]) = kr[i];
+      *reinterpret_cast<uint4*>(&vsm[buf][row * ROWKV + 8 * ch]) = vr[i];
     }
   };
 
