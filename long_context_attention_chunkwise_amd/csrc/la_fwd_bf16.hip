@@ -87,9 +87,15 @@ __device__ __forceinline__ bf16x4 ld_lds_tr(const uint16_t* p) {
 //   32p + 4grp + {0..3}  and  32p + 16 + 4grp + {0..3}.
 // The same slot order is used for both operands of every such product, and it
 // matches the accumulator layout of two vertically adjacent 16x16 P^T tiles.
-__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int p, int col0, int l16, int grp) {
+//
+// With cstride = 8 the 16 columns are col0 + 8j + {0..3} for j = 0..3: lane
+// l16 gets column col0 + 8(l16/4) + l16%4.  Two such tiles (col0 and col0+4)
+// cover 32 consecutive columns so that the accumulator of a product whose rows
+// are those columns holds 8 consecutive columns per lane.
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int p, int col0, int l16, int grp,
+                                             int cstride = 4) {
   const int r = 32 * p + 4 * grp + (l16 >> 2);
-  const int c = col0 + 4 * (l16 & 3);
+  const int c = col0 + cstride * (l16 & 3);
   bf16x4 lo = ld_lds_tr(tile + r * ROWKV + c);
   bf16x4 hi = ld_lds_tr(tile + (r + 16) * ROWKV + c);
   bf16x8 out;
@@ -321,6 +327,186 @@ __global__ __launch_bounds__(kMainThreads, 1) void fwd_bf16_main(
   }
 }
 
+struct KV4Regs {
+  uint4 k[4], v[4];
+};
+
+__device__ __forceinline__ void load_kv4(KV4Regs& r, const uint16_t* kh, const uint16_t* vh, int64_t blk,
+                                         int64_t N, int tid) {
+  const int c = tid & 15;
+  for (int i = 0; i < 4; ++i) {
+    const int64_t t = blk * C + (tid >> 4) + 16 * i;
+    if (t < N) {
+      r.k[i] = *reinterpret_cast<const uint4*>(kh + t * D + 8 * c);
+      r.v[i] = *reinterpret_cast<const uint4*>(vh + t * DV + 8 * c);
+    } else {
+      r.k[i] = make_uint4(0, 0, 0, 0);
+      r.v[i] = make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+__device__ __forceinline__ void store_kv4(const KV4Regs& r, uint16_t* ks, uint16_t* vs, int tid) {
+  const int c = tid & 15;
+  for (int i = 0; i < 4; ++i) {
+    const int row = (tid >> 4) + 16 * i;
+    *reinterpret_cast<uint4*>(ks + row * ROWKV + 8 * c) = r.k[i];
+    *reinterpret_cast<uint4*>(vs + row * ROWKV + 8 * c) = r.v[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Four-wave kernel for groups of four query heads (the 128/32-head shape).
+// One wave per SIMD: wave h computes every row of the block for query head h
+// of the group (each wave reads the bf16 state once per block: half the LDS
+// traffic of the eight-wave layout) and owns state columns [32h, 32h+32).
+//
+// Output columns are processed in quarters of 32 as two interleaved 16-column
+// tiles (columns 32m + 8j + {0..3} and 32m + 8j + {4..7}, j = 0..3), so each
+// lane holds 8 consecutive columns of one row and stores 16 bytes, and only
+// 32 accumulator registers are live at a time.
+//
+// LDS tiles are single-buffered (70 KiB).  The next block's Q and K/V loads
+// are issued once the current block's Q operands are dead (after the output
+// products), so they overlap the state update and the barriers without
+// competing with the matrix-heavy phase.  Three barriers per block: K/V and
+// the state are published, the inter term has finished reading the state,
+// and the state update has finished reading K/V.
+// ---------------------------------------------------------------------------
+template <bool OUT_F32>
+__global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    void* __restrict__ o, const float* starts, const float* s_in, float* s_out, int Hq, int Hkv, int subgroups,
+    int64_t N, int64_t nblocks, int64_t blocks_per_seg, int P) {
+  __shared__ __align__(16) uint16_t ks[C * ROWKV];
+  __shared__ __align__(16) uint16_t vs[C * ROWKV];
+  __shared__ __align__(16) uint16_t st[DV * ROWST];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+  const int seg = blockIdx.x % P;
+  const int chain = blockIdx.x / P;
+  const int sub = chain % subgroups;
+  const int bg = chain / subgroups;  // b * Hkv + g
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int G = Hq / Hkv;
+  const int64_t blk0 = int64_t(seg) * blocks_per_seg;
+  const int64_t blk1 = blk0 + blocks_per_seg < nblocks ? blk0 + blocks_per_seg : nblocks;
+
+  const int64_t head = int64_t(b) * Hq + int64_t(g) * G + int64_t(sub) * 4 + w;
+  const uint16_t* qh = q + head * N * D;
+  const uint16_t* kh = k + int64_t(bg) * N * D;
+  const uint16_t* vh = v + int64_t(bg) * N * DV;
+  const int nlane = 8 * (l16 >> 2) + (l16 & 3);
+
+  const float* s0 = starts ? starts + (int64_t(bg) * P + seg) * (D * DV)
+                           : (s_in ? s_in + int64_t(bg) * (D * DV) : nullptr);
+  floatx4 sacc[2][8];
+  for (int jn = 0; jn < 2; ++jn)
+    for (int dt = 0; dt < 8; ++dt)
+      for (int i = 0; i < 4; ++i)
+        sacc[jn][dt][i] = s0 ? s0[(16 * dt + 4 * grp + i) * DV + 32 * w + 16 * jn + l16] : 0.0f;
+  for (int jn = 0; jn < 2; ++jn)
+    for (int dt = 0; dt < 8; ++dt)
+      *reinterpret_cast<bf16x4*>(&st[(32 * w + 16 * jn + l16) * ROWST + 16 * dt + 4 * grp]) =
+          to_bf16x4(sacc[jn][dt]);
+
+  bf16x8 qa[4][4];
+  KV4Regs kv;
+  auto load_block = [&](int64_t blk) {
+    load_kv4(kv, kh, vh, blk, N, tid);
+    for (int ti = 0; ti < 4; ++ti) {
+      const int64_t t = blk * C + 16 * ti + l16;
+      for (int ds = 0; ds < 4; ++ds)
+        qa[ti][ds] = (t < N) ? ld_global16(qh + t * D + 32 * ds + 8 * grp) : zero_bf16x8();
+    }
+  };
+  if (blk0 < blk1) load_block(blk0);
+  for (int64_t blk = blk0; blk < blk1; ++blk) {
+    store_kv4(kv, ks, vs, tid);
+    __syncthreads();  // K, V and the state of the previous block are in LDS
+
+    // scores, one P^T tile at a time, packed to bf16 operands right away
+    const floatx4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    bf16x8 pop[4][2];
+    for (int ti = 0; ti < 4; ++ti) {
+      floatx4 pt[4];
+      for (int si = 0; si <= ti; ++si) {
+        pt[si] = z4;
+        for (int ds = 0; ds < 4; ++ds)
+          pt[si] = mfma(ld_lds16(ks + (16 * si + l16) * ROWKV + 32 * ds + 8 * grp), qa[ti][ds], pt[si]);
+      }
+      pt[ti] = causal_mask(pt[ti], l16, grp);
+      pop[ti][0] = pack_tiles(pt[0], ti >= 1 ? pt[1] : z4);
+      if (ti >= 2) pop[ti][1] = pack_tiles(pt[2], ti == 3 ? pt[3] : z4);
+    }
+
+    // Output columns in quarters of 32 (one interleaved column pair m), so
+    // only 32 accumulator registers are live at a time.
+    for (int m = 0; m < 4; ++m) {
+      floatx4 acc[2][4];
+      for (int h2 = 0; h2 < 2; ++h2)
+        for (int ti = 0; ti < 4; ++ti) acc[h2][ti] = z4;
+      // inter: O^T[n][t] = sum_d S[d][n] Q[t][d] (state before the block)
+      for (int ds = 0; ds < 4; ++ds)
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const bf16x8 sa = ld_lds16(st + (32 * m + 4 * h2 + nlane) * ROWST + 32 * ds + 8 * grp);
+          for (int ti = 0; ti < 4; ++ti) acc[h2][ti] = mfma(sa, qa[ti][ds], acc[h2][ti]);
+        }
+      // intra: O^T[n][t] += sum_s V[s][n] P^T[s][t]
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const bf16x8 va0 = tr_operand(vs, 0, 32 * m + 4 * h2, l16, grp, 8);
+        const bf16x8 va1 = tr_operand(vs, 1, 32 * m + 4 * h2, l16, grp, 8);
+        for (int ti = 0; ti < 4; ++ti) acc[h2][ti] = mfma(va0, pop[ti][0], acc[h2][ti]);
+        acc[h2][2] = mfma(va1, pop[2][1], acc[h2][2]);
+        acc[h2][3] = mfma(va1, pop[3][1], acc[h2][3]);
+      }
+      for (int ti = 0; ti < 4; ++ti) {
+        const int64_t t = blk * C + 16 * ti + l16;
+        if (t < N) {
+          const int64_t off = (head * N + t) * DV + 32 * m + 8 * grp;
+          if (OUT_F32) {
+            float* op = static_cast<float*>(o) + off;
+            *reinterpret_cast<floatx4*>(op) = acc[0][ti];
+            *reinterpret_cast<floatx4*>(op + 4) = acc[1][ti];
+          } else {
+            *reinterpret_cast<bf16x8*>(static_cast<uint16_t*>(o) + off) = pack_tiles(acc[0][ti], acc[1][ti]);
+          }
+        }
+      }
+    }
+    // The next block's loads go out now (Q operands are no longer needed), so
+    // they overlap the state update and the barriers.
+    if (blk + 1 < blk1) load_block(blk + 1);
+    __syncthreads();  // every wave has finished reading the state
+
+    // state update: S[:, 32w:32w+32] += K_b^T V_b, then its bf16 copy
+    {
+      bf16x8 vb[2][2];
+      for (int jn = 0; jn < 2; ++jn)
+        for (int p = 0; p < 2; ++p) vb[jn][p] = tr_operand(vs, p, 32 * w + 16 * jn, l16, grp);
+      for (int dt = 0; dt < 8; ++dt)
+        for (int p = 0; p < 2; ++p) {
+          const bf16x8 kt = tr_operand(ks, p, 16 * dt, l16, grp);
+          sacc[0][dt] = mfma(kt, vb[0][p], sacc[0][dt]);
+          sacc[1][dt] = mfma(kt, vb[1][p], sacc[1][dt]);
+        }
+      for (int jn = 0; jn < 2; ++jn)
+        for (int dt = 0; dt < 8; ++dt)
+          *reinterpret_cast<bf16x4*>(&st[(32 * w + 16 * jn + l16) * ROWST + 16 * dt + 4 * grp]) =
+              to_bf16x4(sacc[jn][dt]);
+    }
+    __syncthreads();  // K and V are free for the next block
+  }
+
+  if (s_out != nullptr && seg == P - 1 && sub == 0) {
+    float* so = s_out + int64_t(bg) * (D * DV);
+    for (int jn = 0; jn < 2; ++jn)
+      for (int dt = 0; dt < 8; ++dt)
+        for (int i = 0; i < 4; ++i) so[(16 * dt + 4 * grp + i) * DV + 32 * w + 16 * jn + l16] = sacc[jn][dt][i];
+  }
+}
+
 // Pre-pass: partial[c][j][r] = sum of K_b^T V_b over part r of segment j of
 // chain c (every segment but the last).  Four waves; wave w owns state
 // columns [32w, 32w+32).
@@ -418,6 +604,15 @@ __global__ __launch_bounds__(256) void scan_starts(const float* __restrict__ par
   }
 }
 
+template <bool OUT_F32>
+void launch_g4(dim3 grid, hipStream_t stream, const void* q, const void* k, const void* v, void* o,
+               const float* starts, const float* s_in, float* s_out, int Hq, int Hkv, int subgroups, int64_t N,
+               int64_t nblocks, int64_t bps, int P) {
+  hipLaunchKernelGGL((fwd_bf16_g4<OUT_F32>), grid, dim3(256), 0, stream, static_cast<const uint16_t*>(q),
+                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), o, starts, s_in, s_out, Hq,
+                     Hkv, subgroups, N, nblocks, bps, P);
+}
+
 template <int GW, bool OUT_F32>
 void launch_main(dim3 grid, hipStream_t stream, const void* q, const void* k, const void* v, void* o,
                  const float* starts, const float* s_in, float* s_out, int Hq, int Hkv, int subgroups, int64_t N,
@@ -458,7 +653,13 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
   launch_main<GW, F32>(grid, stream, q, k, v, o, starts, plan.use_starts ? nullptr : s_in, s_out, iHq, iHkv, \
                        plan.subgroups, N, plan.nblocks, plan.blocks_per_seg, plan.P)
   if (plan.gw == 4) {
-    if (out_f32) LA_MAIN(4, true); else LA_MAIN(4, false);
+    const float* si = plan.use_starts ? nullptr : s_in;
+    if (out_f32)
+      launch_g4<true>(grid, stream, q, k, v, o, starts, si, s_out, iHq, iHkv, plan.subgroups, N, plan.nblocks,
+                      plan.blocks_per_seg, plan.P);
+    else
+      launch_g4<false>(grid, stream, q, k, v, o, starts, si, s_out, iHq, iHkv, plan.subgroups, N, plan.nblocks,
+                       plan.blocks_per_seg, plan.P);
   } else if (plan.gw == 2) {
     if (out_f32) LA_MAIN(2, true); else LA_MAIN(2, false);
   } else {
