@@ -75,10 +75,13 @@ Bf16Plan plan_bf16(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int
   p.P = static_cast<int>(P);
 
   if (P > 1) {
-    // Pre-pass parts: about four workgroups per compute unit in total, each
-    // summing at least kMinPartBlocks blocks (a part writes a 64 KiB partial).
+    // Pre-pass parts: as many as fit the chip in one round (three pre-pass
+    // workgroups are resident per compute unit), so no partial last round
+    // leaves compute units idle; each part sums at least kMinPartBlocks blocks
+    // (a part writes a 64 KiB partial).
     constexpr int64_t kMinPartBlocks = 8;
-    int64_t R = (4 * int64_t(cus) + kv_chains * (P - 1) - 1) / (kv_chains * (P - 1));
+    constexpr int64_t kPartWgsPerCu = 3;
+    int64_t R = (kPartWgsPerCu * int64_t(cus)) / (kv_chains * (P - 1));
     R = std::max<int64_t>(1, std::min(R, p.blocks_per_seg / kMinPartBlocks));
     p.blocks_per_part = (p.blocks_per_seg + R - 1) / R;
     R = (p.blocks_per_seg + p.blocks_per_part - 1) / p.blocks_per_part;

@@ -509,14 +509,16 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
 
 // Pre-pass: partial[c][j][r] = sum of K_b^T V_b over part r of segment j of
 // chain c (every segment but the last).  Four waves; wave w owns state
-// columns [32w, 32w+32).
-__global__ __launch_bounds__(kPartThreads) void state_parts(const uint16_t* __restrict__ k,
+// columns [32w, 32w+32).  A pure HBM stream: the K/V tile is single-buffered
+// in LDS (36 KiB) so three workgroups share a CU, each with the next block's
+// loads in flight while it multiplies the current one.
+__global__ __launch_bounds__(kPartThreads, 3) void state_parts(const uint16_t* __restrict__ k,
                                                            const uint16_t* __restrict__ v,
                                                            float* __restrict__ partial, int64_t N,
                                                            int64_t nblocks, int64_t blocks_per_seg,
                                                            int64_t blocks_per_part, int P, int R) {
-  __shared__ __align__(16) uint16_t ksm[2][C * ROWKV];
-  __shared__ __align__(16) uint16_t vsm[2][C * ROWKV];
+  __shared__ __align__(16) uint16_t ksm[C * ROWKV];
+  __shared__ __align__(16) uint16_t vsm[C * ROWKV];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
@@ -550,36 +552,30 @@ __global__ __launch_bounds__(kPartThreads) void state_parts(const uint16_t* __re
       }
     }
   };
-  auto store = [&](int buf, const uint4 (&kr)[4], const uint4 (&vr)[4]) {
+  auto store = [&](const uint4 (&kr)[4], const uint4 (&vr)[4]) {
     for (int i = 0; i < 4; ++i) {
       const int row = (tid >> 4) + 16 * i;
-      *reinterpret_cast<uint4*>(&ksm[buf][row * ROWKV + 8 * ch]) = kr[i];
-      *reinterpret_cast<uint4*>(&vsm[buf][row * ROWKV + 8 * ch]) = vr[i];
+      *reinterpret_cast<uint4*>(&ksm[row * ROWKV + 8 * ch]) = kr[i];
+      *reinterpret_cast<uint4*>(&vsm[row * ROWKV + 8 * ch]) = vr[i];
     }
   };
 
-  if (b0 < b1) {
-    uint4 kr[4], vr[4];
-    load(b0, kr, vr);
-    store(0, kr, vr);
-  }
-  __syncthreads();
+  uint4 kr[4], vr[4];
+  if (b0 < b1) load(b0, kr, vr);
   for (int64_t blk = b0; blk < b1; ++blk) {
-    const int cur = int(blk - b0) & 1;
-    const bool has_next = blk + 1 < b1;
-    uint4 kr[4], vr[4];
-    if (has_next) load(blk + 1, kr, vr);
+    store(kr, vr);
+    __syncthreads();  // the block's K and V are in LDS
+    if (blk + 1 < b1) load(blk + 1, kr, vr);
     for (int p = 0; p < 2; ++p) {
-      const bf16x8 vb0 = tr_operand(vsm[cur], p, 32 * w, l16, grp);
-      const bf16x8 vb1 = tr_operand(vsm[cur], p, 32 * w + 16, l16, grp);
+      const bf16x8 vb0 = tr_operand(vsm, p, 32 * w, l16, grp);
+      const bf16x8 vb1 = tr_operand(vsm, p, 32 * w + 16, l16, grp);
       for (int dt = 0; dt < 8; ++dt) {
-        const bf16x8 ka = tr_operand(ksm[cur], p, 16 * dt, l16, grp);
+        const bf16x8 ka = tr_operand(ksm, p, 16 * dt, l16, grp);
         acc[0][dt] = mfma(ka, vb0, acc[0][dt]);
         acc[1][dt] = mfma(ka, vb1, acc[1][dt]);
       }
     }
-    if (has_next) store(cur ^ 1, kr, vr);
-    __syncthreads();
+    __syncthreads();  // every wave is done with this block's K and V
   }
 
   float* out = partial + ((int64_t(c) * (P - 1) + j) * R + r) * (D * DV);

@@ -87,9 +87,10 @@ def test_decode_validation(lib):
 def test_workspace_plan(lib):
     # Host planning with the default 256 compute units (no device here): the
     # 1M-token GQA problem splits each of the 32 chains into 8 segments and
-    # every segment but the last into 5 pre-pass parts.
+    # every segment but the last into 3 pre-pass parts (672 pre-pass
+    # workgroups: one round at three per compute unit).
     n = lib.la_forward_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, 64, BF16)
-    assert n == (32 * 7 * 5 + 32 * 8) * 128 * 128 * 4
+    assert n == (32 * 7 * 3 + 32 * 8) * 128 * 128 * 4
     assert lib.la_forward_workspace_bytes(1, 1, 1, 256, 64, 64, 64, F32) == 0
     assert lib.la_forward_workspace_bytes(256, 128, 32, 8192, 128, 128, 64, BF16) == 0
     assert lib.la_forward_workspace_bytes(1, 128, 32, 0, 128, 128, 64, BF16) == 0
