@@ -23,6 +23,20 @@ constexpr int kThreads = 256;
 constexpr int kMaxD = 128;
 constexpr int kMaxDV = 128;
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// The state is touched once per step: streaming (non-temporal) accesses keep
+// it from displacing other data in the caches and measured faster on gfx950.
+__device__ __forceinline__ float4 load_stream(const float4* p) {
+  const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return make_float4(x.x, x.y, x.z, x.w);
+}
+
+__device__ __forceinline__ void store_stream(float4* p, float4 v) {
+  const f32x4 x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
+}
+
 template <bool IN_BF16>
 __device__ __forceinline__ float load_in(const void* p, int64_t i) {
   if (IN_BF16) {
@@ -58,15 +72,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(float* __restrict__ S,
   if (rg < nrg) {
     float4* Sg = reinterpret_cast<float4*>(S + int64_t(bg) * d * dv);
     const float4 v4 = make_float4(vs[4 * cg], vs[4 * cg + 1], vs[4 * cg + 2], vs[4 * cg + 3]);
-#pragma unroll 4
+#pragma unroll 8
     for (int r = rg; r < d; r += nrg) {
-      float4 s = Sg[r * ncg + cg];
+      float4 s = load_stream(&Sg[r * ncg + cg]);
       const float kr = ks[r];
       s.x = fmaf(kr, v4.x, s.x);
       s.y = fmaf(kr, v4.y, s.y);
       s.z = fmaf(kr, v4.z, s.z);
       s.w = fmaf(kr, v4.w, s.w);
-      Sg[r * ncg + cg] = s;
+      store_stream(&Sg[r * ncg + cg], s);
       for (int h = 0; h < G; ++h) {
         const float qr = qs[h][r];
         acc[h].x = fmaf(qr, s.x, acc[h].x);

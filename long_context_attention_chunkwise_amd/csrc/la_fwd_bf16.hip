@@ -65,6 +65,17 @@ __device__ __forceinline__ bf16x8 ld_global16(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming (non-temporal) 16-byte load for data read exactly once in whole
+// rows (K and V tiles): measured faster on gfx950 than cached loads.  Q is not
+// loaded this way: each Q load covers half of a 128-byte line and relies on
+// the cache for the other half.
+__device__ __forceinline__ uint4 ld_stream16(const uint16_t* p) {
+  const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(x.x, x.y, x.z, x.w);
+}
+
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
   bf16x8 z;
   for (int i = 0; i < 8; ++i) z[i] = (__bf16)0.0f;
@@ -337,8 +348,8 @@ __device__ __forceinline__ void load_kv4(KV4Regs& r, const uint16_t* kh, const u
   for (int i = 0; i < 4; ++i) {
     const int64_t t = blk * C + (tid >> 4) + 16 * i;
     if (t < N) {
-      r.k[i] = *reinterpret_cast<const uint4*>(kh + t * D + 8 * c);
-      r.v[i] = *reinterpret_cast<const uint4*>(vh + t * DV + 8 * c);
+      r.k[i] = ld_stream16(kh + t * D + 8 * c);
+      r.v[i] = ld_stream16(vh + t * DV + 8 * c);
     } else {
       r.k[i] = make_uint4(0, 0, 0, 0);
       r.v[i] = make_uint4(0, 0, 0, 0);
@@ -544,8 +555,8 @@ __global__ __launch_bounds__(kPartThreads, 3) void state_parts(const uint16_t* _
     for (int i = 0; i < 4; ++i) {
       const int64_t t = blk * C + (tid >> 4) + 16 * i;
       if (t < N) {
-        kr[i] = *reinterpret_cast<const uint4*>(kh + t * D + 8 * ch);
-        vr[i] = *reinterpret_cast<const uint4*>(vh + t * DV + 8 * ch);
+        kr[i] = ld_stream16(kh + t * D + 8 * ch);
+        vr[i] = ld_stream16(vh + t * DV + 8 * ch);
       } else {
         kr[i] = make_uint4(0, 0, 0, 0);
         vr[i] = make_uint4(0, 0, 0, 0);
