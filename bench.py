@@ -38,6 +38,30 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_gqa_1m_decode_256.md")
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel's source has changed since the counters were taken."""
+    import hashlib
+    import re
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    for m in re.finditer(r"traffic (\S+) (\S+) bytes=(\d+) source=(\S+) sha256=([0-9a-f]+)", text):
+        if (m.group(1), m.group(2)) != (kernel, workload):
+            continue
+        src = os.path.join(ROOT, "long_context_attention_chunkwise_amd", "csrc", m.group(4))
+        try:
+            digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        except OSError:
+            return None
+        return int(m.group(3)) if digest == m.group(5) else None
+    return None
+
+
 def forward_flops(w, N):
     """Algorithmic flops of the causal forward (per the block recurrence).
 
@@ -168,7 +192,8 @@ def bench_decode(la, synth, torch, w, steps, warmup):
             "config": {"workload": w.name, "sequences": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "dv": w.dv,
                        "prefix_tokens": w.N, "state_dtype": "f32", "io_dtype": "bf16 in, f32 out"},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic("decode_kernel", w.name),
                          "bytes_per_launch": step_bytes}}
 
 
@@ -245,8 +270,9 @@ def main():
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "seq_len": w.N, "d": w.d,
                    "dv": w.dv, "block": w.block, "io_dtype": "bf16", "state_dtype": "f32"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                     "kernel": "fwd_bf16_main", "kernel_ms": round(ms_main, 4), "bytes_per_launch": bytes_main},
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic("fwd_bf16_g4", w.name),
+                     "kernel": "fwd_bf16_g4", "kernel_ms": round(ms_main, 4), "bytes_per_launch": bytes_main},
         "mfma": {"tflops_alg": round(f_alg / (ms_step * 1e-3) / 1e12, 2),
                  "frac_alg": round(f_alg / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                  "tflops_tile": round(f_tile / (ms_step * 1e-3) / 1e12, 2),

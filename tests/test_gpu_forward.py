@@ -74,11 +74,12 @@ def test_mha_4k_bf16():
         check_close("state", f64(S), ref_S, torch.bfloat16, torch.float32)
 
 
-# Group sizes 1, 2, 4, 8 (two subgroups of 4) and 3 (three subgroups of 1);
-# lengths that are not multiples of 64; short and long segment splits.
+# Group sizes 1, 2, 4, 8 (two subgroups of 4), 16 (four subgroups) and 3
+# (three subgroups of 1); lengths that are not multiples of 64; short and long
+# segment splits.
 @pytest.mark.parametrize("Hq,Hkv,N", [
     (2, 2, 1), (2, 2, 37), (4, 2, 64), (8, 2, 65), (8, 1, 1000), (3, 1, 777),
-    (4, 4, 4095), (8, 2, 3000), (16, 4, 2113),
+    (4, 4, 4095), (8, 2, 3000), (16, 4, 2113), (16, 1, 1500), (4, 1, 64 * 300 + 5),
 ])
 def test_bf16_shapes(Hq, Hkv, N):
     need_gpu()
