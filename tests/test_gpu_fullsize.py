@@ -1,7 +1,8 @@
 """Parity at the full workload sizes, in the launch configuration the benchmark
 times, on outputs and states the fp64 oracle can compute: whole KV groups at
 65,536 tokens, head/sequence slices and recomputed final states at 1,048,576
-tokens, and sampled sequences of the 256-sequence decode workload.
+tokens, sampled sequences of the 256-sequence decode workload, and a
+4,194,304-token sequence prefilled in 1M-token chunks with the state carried.
 """
 import numpy as np
 import pytest
@@ -141,3 +142,37 @@ def test_decode_256_sequences():
                 torch.float32)
     check_close("oracle recurrence vs closed form (2 sequences)", Sref, ref_final[:2], torch.float32,
                 torch.float32)
+
+
+def test_gqa_4m_chunked_prefill():
+    """4,194,304 tokens (the pages' longest context) as four 1M-token chunks
+    through la_forward_ex with the state carried in place (s_in = s_out).
+    Q/K/V/O of the whole sequence (320 GiB) do not fit one GPU; the chunks do.
+    Checked for KV groups 0 and 31: the first 4096 tokens of every chunk (each
+    starts from the carried state) and the state after every chunk, against
+    the oracle's running state."""
+    need_gpu()
+    w = synth.WORKLOADS["gqa_1m"]
+    G = w.Hq // w.Hkv
+    chunks = 4
+    say(f"case gqa_4m_chunked: {chunks} x {w.N} tokens, Hq={w.Hq} Hkv={w.Hkv}")
+    S = torch.zeros((w.B, w.Hkv, w.d, w.dv), dtype=torch.float32, device=DEV)
+    ws = torch.empty(la.workspace_bytes(w.B, w.Hq, w.Hkv, w.N, w.d, w.dv, w.block, torch.bfloat16),
+                     dtype=torch.uint8, device=DEV)
+    o = torch.empty((w.B, w.Hq, w.N, w.dv), dtype=torch.bfloat16, device=DEV)
+    groups = (0, 31)
+    S_ref = {g: np.zeros((1, 1, w.d, w.dv)) for g in groups}
+    W = 4096
+    for c in range(chunks):
+        q, k, v = synth.make_qkv(w, DEV, seed=100 + c)
+        la.forward(q, k, v, s_in=S, s_out=S, out=o, workspace=ws)
+        torch.cuda.synchronize()
+        for g in groups:
+            qs, ks, vs = group_slice(q, k, v, g, G, 0, W)
+            check_close(f"chunk {c} group {g} tokens [{c * w.N}, {c * w.N + W})",
+                        f64(o[:, g * G:(g + 1) * G, :W]),
+                        oracle.chunkwise(qs, ks, vs, w.block, S_ref[g])[0], torch.bfloat16, torch.bfloat16)
+            S_ref[g] = oracle.final_state(f64(k[:, g:g + 1]), f64(v[:, g:g + 1]), S_ref[g])
+            check_close(f"state after chunk {c} group {g}", f64(S[:, g:g + 1]), S_ref[g], torch.bfloat16,
+                        torch.float32)
+        del q, k, v
