@@ -12,4 +12,6 @@ from .lightning import (  # noqa: F401
     decode_step,
     final_state,
     noncausal,
+    backward_brute_force,
+    backward_chunkwise,
 )

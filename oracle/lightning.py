@@ -38,7 +38,9 @@ Every function is pinned by tests that do not re-type its formula: a
 hand-worked example, closed forms, brute force over Python loops, block-size
 invariance, causality, the final state against a library GEMM, the non-causal
 special case, linearity, GQA against repeated-head MHA, and recurrent/decode
-against the block form.  No function here is parity unpinned.
+against the block form (tests/test_oracle.py); the backward pass against
+central finite differences of the forward (tests/test_oracle_backward.py).
+No function here is parity unpinned.
 
 Layouts: q [B, Hq, N, d], k [B, Hkv, N, d], v [B, Hkv, N, dv],
 o [B, Hq, N, dv], state [B, Hkv, d, dv].  Decode drops the N axis.
@@ -177,3 +179,95 @@ def noncausal(q, k, v):
     gidx = _heads_to_groups(Hq, Hkv)
     kv = final_state(k, v)
     return np.matmul(q, kv[:, gidx])
+
+
+# ---------------------------------------------------------------------------
+# Backward pass (gradients of a scalar loss L given dO = dL/do).
+#
+# The pages give no backward; it follows from the forward definition by
+# matrix calculus.  With M = tril(Q K^T) per query head (diagonal kept) and
+# O = M V + Q s_in:
+#     dQ = tril(dO V^T) K + dO s_in^T
+#     dK = sum over the group's query heads of tril(dO V^T)^T Q
+#     dV = sum over the group's query heads of M^T dO
+#     ds_in = sum over the group's query heads of Q^T dO
+# backward_brute_force writes exactly that; backward_chunkwise evaluates the
+# same gradients block by block: dQ is the causal forward recurrence applied
+# to (dO, V, K) with initial state s_in^T, and dK, dV run backwards over the
+# blocks with a state R = sum over later tokens and the group's heads of
+# q_t^T dO_t (d x dv):
+#     dV_b = K_b R + sum_h triu(K_b Q_hb^T) dO_hb
+#     dK_b = V_b R^T + sum_h triu(V_b dO_hb^T) Q_hb
+#     R   <- R + sum_h Q_hb^T dO_hb          (after the block)
+# where triu keeps query positions t >= key position s.  Pinned in
+# tests/test_oracle_backward.py by central finite differences of the forward.
+# ---------------------------------------------------------------------------
+
+def _check_do(q, v, do):
+    if do.shape != (q.shape[0], q.shape[1], q.shape[2], v.shape[3]):
+        raise ValueError("dO must be [B, Hq, N, dv]")
+
+
+def backward_brute_force(q, k, v, do, s_in=None):
+    """Gradients from the N x N masked score matrix.  Returns (dq, dk, dv, ds_in)."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    s_in = None if s_in is None else _f64(s_in)
+    B, Hq, Hkv, N, d, dv = _check(q, k, v, s_in)
+    _check_do(q, v, do)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dvv = np.zeros_like(v)
+    ds = np.zeros((B, Hkv, d, dv))
+    mask = np.arange(N)[None, :] <= np.arange(N)[:, None]          # (t, s): s <= t
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_group(h, Hq, Hkv)
+            m = (q[b, h] @ k[b, g].T) * mask                         # [t, s]
+            dm = (do[b, h] @ v[b, g].T) * mask                       # dL/dM, [t, s]
+            dq[b, h] = dm @ k[b, g]
+            if s_in is not None:
+                dq[b, h] += do[b, h] @ s_in[b, g].T
+            dk[b, g] += dm.T @ q[b, h]
+            dvv[b, g] += m.T @ do[b, h]
+            ds[b, g] += q[b, h].T @ do[b, h]
+    return dq, dk, dvv, ds
+
+
+def backward_chunkwise(q, k, v, do, block, s_in=None):
+    """Gradients by the block recurrences (forward for dQ, reverse for dK, dV).
+    Returns (dq, dk, dv, ds_in)."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    s_in = None if s_in is None else _f64(s_in)
+    B, Hq, Hkv, N, d, dv = _check(q, k, v, s_in)
+    _check_do(q, v, do)
+    if block < 1:
+        raise ValueError("block must be >= 1")
+    # dQ: causal recurrence on (queries dO, keys V, values K), state s_in^T.
+    s_t = None if s_in is None else np.swapaxes(s_in, -1, -2)
+    dq, _ = chunkwise(do, v, k, block, s_t)
+    # dK, dV: reverse recurrence, state summed over each group's query heads.
+    G = Hq // Hkv
+    R = np.zeros((B, Hkv, d, dv))
+    dk = np.zeros_like(k)
+    dvv = np.zeros_like(v)
+    starts = list(range(0, N, block))
+    for a in reversed(starts):
+        e = min(a + block, N)
+        kb, vb = k[:, :, a:e], v[:, :, a:e]                            # [B, Hkv, c, *]
+        c = e - a
+        keep = np.arange(c)[None, :] >= np.arange(c)[:, None]           # (s, t): t >= s
+        dvb = np.matmul(kb, R)
+        dkb = np.matmul(vb, np.swapaxes(R, -1, -2))
+        upd = np.zeros_like(R)
+        for j in range(G):
+            qh = q[:, [g * G + j for g in range(Hkv)], a:e]            # head j of every group
+            doh = do[:, [g * G + j for g in range(Hkv)], a:e]
+            x = np.matmul(kb, np.swapaxes(qh, -1, -2)) * keep           # [s, t]
+            y = np.matmul(vb, np.swapaxes(doh, -1, -2)) * keep
+            dvb = dvb + np.matmul(x, doh)
+            dkb = dkb + np.matmul(y, qh)
+            upd = upd + np.matmul(np.swapaxes(qh, -1, -2), doh)
+        dvv[:, :, a:e] = dvb
+        dk[:, :, a:e] = dkb
+        R = R + upd
+    return dq, dk, dvv, R
