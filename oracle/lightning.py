@@ -191,6 +191,9 @@ def noncausal(q, k, v):
 #     dK = sum over the group's query heads of tril(dO V^T)^T Q
 #     dV = sum over the group's query heads of M^T dO
 #     ds_in = sum over the group's query heads of Q^T dO
+# A gradient ds_out on the final state S_out = s_in + K^T V (fed back by the
+# next chunk of a sequence processed in chunks) adds V ds_out^T to dK,
+# K ds_out to dV and ds_out to ds_in.
 # backward_brute_force writes exactly that; backward_chunkwise evaluates the
 # same gradients block by block: dQ is the causal forward recurrence applied
 # to (dO, V, K) with initial state s_in^T, and dK, dV run backwards over the
@@ -199,6 +202,7 @@ def noncausal(q, k, v):
 #     dV_b = K_b R + sum_h triu(K_b Q_hb^T) dO_hb
 #     dK_b = V_b R^T + sum_h triu(V_b dO_hb^T) Q_hb
 #     R   <- R + sum_h Q_hb^T dO_hb          (after the block)
+# starting from R = ds_out (zeros by default) and ending at R = ds_in,
 # where triu keeps query positions t >= key position s.  Pinned in
 # tests/test_oracle_backward.py by central finite differences of the forward.
 # ---------------------------------------------------------------------------
@@ -208,16 +212,27 @@ def _check_do(q, v, do):
         raise ValueError("dO must be [B, Hq, N, dv]")
 
 
-def backward_brute_force(q, k, v, do, s_in=None):
+def _check_ds_out(ds_out, B, Hkv, d, dv):
+    if ds_out is not None and ds_out.shape != (B, Hkv, d, dv):
+        raise ValueError("ds_out must be [B, Hkv, d, dv]")
+
+
+def backward_brute_force(q, k, v, do, s_in=None, ds_out=None):
     """Gradients from the N x N masked score matrix.  Returns (dq, dk, dv, ds_in)."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     s_in = None if s_in is None else _f64(s_in)
+    ds_out = None if ds_out is None else _f64(ds_out)
     B, Hq, Hkv, N, d, dv = _check(q, k, v, s_in)
     _check_do(q, v, do)
+    _check_ds_out(ds_out, B, Hkv, d, dv)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dvv = np.zeros_like(v)
     ds = np.zeros((B, Hkv, d, dv))
+    if ds_out is not None:
+        dk += np.matmul(v, np.swapaxes(ds_out, -1, -2))
+        dvv += np.matmul(k, ds_out)
+        ds += ds_out
     mask = np.arange(N)[None, :] <= np.arange(N)[:, None]          # (t, s): s <= t
     for b in range(B):
         for h in range(Hq):
@@ -233,13 +248,15 @@ def backward_brute_force(q, k, v, do, s_in=None):
     return dq, dk, dvv, ds
 
 
-def backward_chunkwise(q, k, v, do, block, s_in=None):
+def backward_chunkwise(q, k, v, do, block, s_in=None, ds_out=None):
     """Gradients by the block recurrences (forward for dQ, reverse for dK, dV).
     Returns (dq, dk, dv, ds_in)."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     s_in = None if s_in is None else _f64(s_in)
+    ds_out = None if ds_out is None else _f64(ds_out)
     B, Hq, Hkv, N, d, dv = _check(q, k, v, s_in)
     _check_do(q, v, do)
+    _check_ds_out(ds_out, B, Hkv, d, dv)
     if block < 1:
         raise ValueError("block must be >= 1")
     # dQ: causal recurrence on (queries dO, keys V, values K), state s_in^T.
@@ -247,7 +264,7 @@ def backward_chunkwise(q, k, v, do, block, s_in=None):
     dq, _ = chunkwise(do, v, k, block, s_t)
     # dK, dV: reverse recurrence, state summed over each group's query heads.
     G = Hq // Hkv
-    R = np.zeros((B, Hkv, d, dv))
+    R = np.zeros((B, Hkv, d, dv)) if ds_out is None else ds_out.copy()
     dk = np.zeros_like(k)
     dvv = np.zeros_like(v)
     starts = list(range(0, N, block))

@@ -22,10 +22,15 @@ def rand_problem(rng, B=1, Hq=4, Hkv=2, N=7, d=3, dv=2):
     return q, k, v, do, s_in
 
 
-def finite_difference_grads(q, k, v, do, s_in, block=3, eps=0.5):
-    """d/dx of L = sum(o * dO) by central differences of the forward oracle."""
+def finite_difference_grads(q, k, v, do, s_in, block=3, eps=0.5, ds_out=None):
+    """d/dx of L = sum(o * dO) (+ sum(S_out * ds_out)) by central differences
+    of the forward oracle."""
     def loss(qq, kk, vv, ss):
-        return float(np.sum(oracle.chunkwise(qq, kk, vv, block, ss)[0] * do))
+        o, S = oracle.chunkwise(qq, kk, vv, block, ss)
+        total = float(np.sum(o * do))
+        if ds_out is not None:
+            total += float(np.sum(S * ds_out))
+        return total
 
     grads = []
     args = [q, k, v, s_in]
@@ -106,6 +111,41 @@ def test_dq_is_the_forward_on_do_v_k():
     q, k, v, do, _ = rand_problem(rng, N=10, d=3, dv=3)
     dq = oracle.backward_chunkwise(q, k, v, do, 4)[0]
     assert close(dq, oracle.brute_force(do, v, k))
+
+
+def test_final_state_gradient_matches_finite_differences():
+    """A gradient ds_out on the final state: every output of both backward
+    forms against central differences of L = sum(o dO) + sum(S_out ds_out)."""
+    rng = np.random.default_rng(25)
+    for shape in ({}, {"Hq": 3, "Hkv": 1, "N": 8, "d": 2, "dv": 3}):
+        q, k, v, do, s_in = rand_problem(rng, **shape)
+        ds_out = rng.standard_normal(s_in.shape)
+        ref = finite_difference_grads(q, k, v, do, s_in, ds_out=ds_out)
+        for got in (oracle.backward_brute_force(q, k, v, do, s_in, ds_out),
+                    oracle.backward_chunkwise(q, k, v, do, 3, s_in, ds_out),
+                    oracle.backward_chunkwise(q, k, v, do, 64, s_in, ds_out)):
+            assert all(close(g, r) for g, r in zip(got, ref))
+        # without the ds_out term the gradients differ
+        plain = oracle.backward_chunkwise(q, k, v, do, 3, s_in)
+        assert not close(plain[1], ref[1]) and not close(plain[3], ref[3])
+
+
+def test_chunked_backward_equals_whole_sequence():
+    """Splitting a sequence in two chunks (the second starts from the first's
+    final state) and back-propagating the second chunk's ds_in into the first
+    as its ds_out gives the whole sequence's gradients."""
+    rng = np.random.default_rng(26)
+    q, k, v, do, s_in = rand_problem(rng, B=2, Hq=4, Hkv=2, N=13, d=3, dv=4)
+    whole = oracle.backward_chunkwise(q, k, v, do, 4, s_in)
+    a = 6
+    S_a = oracle.final_state(k[:, :, :a], v[:, :, :a], s_in)
+    dq2, dk2, dv2, ds2 = oracle.backward_chunkwise(q[:, :, a:], k[:, :, a:], v[:, :, a:], do[:, :, a:], 4, S_a)
+    dq1, dk1, dv1, ds1 = oracle.backward_chunkwise(q[:, :, :a], k[:, :, :a], v[:, :, :a], do[:, :, :a], 4, s_in,
+                                                   ds2)
+    assert close(np.concatenate([dq1, dq2], axis=2), whole[0])
+    assert close(np.concatenate([dk1, dk2], axis=2), whole[1])
+    assert close(np.concatenate([dv1, dv2], axis=2), whole[2])
+    assert close(ds1, whole[3])
 
 
 # ---------------------------------------------------------------------------
