@@ -1,7 +1,7 @@
 /*
  * la.h — C ABI of liblightning.so: causal chunkwise linear attention
- * (Lightning Attention) forward pass and batched single-token decode on
- * AMD Instinct MI355X (gfx950).
+ * (Lightning Attention) forward pass, its backward pass and batched
+ * single-token decode on AMD Instinct MI355X (gfx950).
  *
  * What is computed.  Page "如何理解MiniMax股价创历史新高？拆解国产大模型技术底座"
  * (vergex.cn), section "Lightning Attention：长上下文为什么突然变得便宜了", chunkwise
@@ -150,6 +150,57 @@ size_t la_forward_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
 la_status la_decode_step(float* S, const void* q, const void* k, const void* v, void* o,
                          int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int64_t dv,
                          la_dtype in_dtype, la_dtype out_dtype, la_stream stream);
+
+/*
+ * Backward pass of la_forward_ex: the gradients of a scalar loss L given
+ * grad_o = dL/do and, optionally, grad_s_out = dL/ds_out.  The pages define
+ * only the forward; differentiating its exact form (page
+ * "如何理解MiniMax股价创历史新高？拆解国产大模型技术底座", section "Lightning
+ * Attention", with the grouped heads of page "MiniMax-01与Lightning Attention",
+ * section 1.1)
+ *     o_t   = q_t . s_in + sum_{s <= t} (q_t . k_s) v_s
+ *     s_out = s_in + sum_s k_s^T v_s
+ * gives, with h over the query heads of a KV head's group,
+ *     dq_t  = grad_o_t . s_in^T + sum_{s <= t} (grad_o_t . v_s) k_s
+ *     dk_s  = v_s . grad_s_out^T + sum_h sum_{t >= s} (v_s . grad_o_ht) q_ht
+ *     dv_s  = k_s . grad_s_out   + sum_h sum_{t >= s} (k_s . q_ht) grad_o_ht
+ *     ds_in = grad_s_out + sum_h sum_t q_ht^T grad_o_ht
+ * dq is computed as the forward recurrence over (grad_o, v, k) from s_in^T;
+ * dk, dv and ds_in by the same block recurrence run from the last block to
+ * the first with a float32 d x dv state that starts at grad_s_out.
+ *
+ *   q, k, v        the forward's inputs (layouts as above).
+ *   grad_o         [B][Hq][N][dv], in_dtype.  in_dtype must be LA_BF16.
+ *   grad_q, grad_k, grad_v   outputs shaped like q, k, v, in grad_dtype
+ *                  (LA_BF16 or LA_F32); every element is written.
+ *   s_in           the forward's initial state, or NULL for zeros (used for dq).
+ *   grad_s_out     [B][Hkv][d][dv] float32 gradient on the forward's final
+ *                  state, or NULL for zeros.
+ *   grad_s_in      [B][Hkv][d][dv] float32 output, or NULL.  May equal
+ *                  grad_s_out (in place); no other output may overlap an
+ *                  input or another output (LA_ERR_ALIAS).
+ *   d = dv = 128, block = 64.  N may be 0 (then only grad_s_in is written).
+ *   workspace / workspace_bytes: at least la_backward_workspace_bytes(...)
+ *                  bytes of device memory, scratch, not shared by concurrent
+ *                  calls.
+ * A sequence processed in chunks with la_forward_ex (state carried from chunk
+ * to chunk) is differentiated by calling la_backward on the chunks from the
+ * last to the first, each with its own s_in and with the grad_s_in of the
+ * chunk after it as grad_s_out.
+ */
+la_status la_backward(const void* q, const void* k, const void* v, const void* grad_o,
+                      void* grad_q, void* grad_k, void* grad_v,
+                      int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                      int64_t d, int64_t dv, int64_t block,
+                      la_dtype in_dtype, la_dtype grad_dtype,
+                      const float* s_in, const float* grad_s_out, float* grad_s_in,
+                      void* workspace, size_t workspace_bytes, la_stream stream);
+
+/* Workspace bytes la_backward needs on the current device (0 for N = 0 or
+ * invalid arguments). */
+size_t la_backward_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                                   int64_t d, int64_t dv, int64_t block,
+                                   la_dtype in_dtype);
 
 /* Static, NUL-terminated description of a status code. */
 const char* la_status_str(la_status status);

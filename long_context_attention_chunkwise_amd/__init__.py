@@ -9,6 +9,8 @@ from ._lib import (  # noqa: F401
     LA_BF16,
     LA_F32,
     LAError,
+    backward,
+    backward_workspace_bytes,
     decode_step,
     forward,
     load_library,

@@ -16,7 +16,7 @@ LA_OK = 0
 STATUS_NAMES = {0: "LA_OK", 1: "LA_ERR_NULL", 2: "LA_ERR_SHAPE", 3: "LA_ERR_UNSUPPORTED", 4: "LA_ERR_ALIGN",
                 5: "LA_ERR_ALIAS", 6: "LA_ERR_WORKSPACE", 7: "LA_ERR_HIP"}
 EXPORTS = ("la_forward", "la_forward_ex", "la_forward_states", "la_forward_outputs", "la_forward_workspace_bytes",
-           "la_decode_step", "la_status_str")
+           "la_backward", "la_backward_workspace_bytes", "la_decode_step", "la_status_str")
 
 _lib = None
 
@@ -48,6 +48,11 @@ def load_library(path=LIB_PATH):
     lib.la_forward_outputs.restype = i32
     lib.la_forward_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, i64, i32]
     lib.la_forward_workspace_bytes.restype = sz
+    lib.la_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i32, i32, vp, vp,
+                                vp, vp, sz, vp]
+    lib.la_backward.restype = i32
+    lib.la_backward_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, i64, i32]
+    lib.la_backward_workspace_bytes.restype = sz
     lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp]
     lib.la_decode_step.restype = i32
     lib.la_status_str.argtypes = [i32]
@@ -153,6 +158,76 @@ def forward(q, k, v, block=64, out_dtype=None, s_in=None, return_state=False, ou
     if return_state:
         return out, s_out
     return out
+
+
+def backward_workspace_bytes(B, Hq, Hkv, N, d, dv, block=64, dtype=None):
+    """Bytes of scratch la_backward needs on the current device."""
+    torch = _torch()
+    code = _dtype_code(dtype if dtype is not None else torch.bfloat16)
+    return int(load_library().la_backward_workspace_bytes(B, Hq, Hkv, N, d, dv, block, code))
+
+
+def backward(q, k, v, grad_o, block=64, grad_dtype=None, s_in=None, grad_s_out=None, return_state_grad=False,
+             out=None, grad_s_in=None, workspace=None):
+    """Gradients of the forward pass (la_backward).
+
+    q, k, v and grad_o = dL/do (bfloat16, shaped like the forward's inputs
+    and output).  Returns (dq, dk, dv) in grad_dtype (default bfloat16) and,
+    with return_state_grad (or a grad_s_in buffer), the float32 gradient on
+    the initial state as a fourth item.  s_in is the forward's initial state;
+    grad_s_out an optional float32 gradient on its final state.  `out` may
+    supply the (dq, dk, dv) buffers.
+    """
+    torch = _torch()
+    lib = load_library()
+    _check_tensor("q", q, 4, None)
+    dev = q.device
+    for name, t in (("k", k), ("v", v), ("grad_o", grad_o)):
+        _check_tensor(name, t, 4, dev)
+    if not (q.dtype == k.dtype == v.dtype == grad_o.dtype):
+        raise TypeError("q, k, v, grad_o must share one dtype")
+    B, Hq, N, d = q.shape
+    Hkv, dv = k.shape[1], v.shape[3]
+    if (tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != (B, Hkv, N, dv)
+            or tuple(grad_o.shape) != (B, Hq, N, dv)):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}, "
+                         f"grad_o {tuple(grad_o.shape)}")
+    in_code = _dtype_code(q.dtype)
+    grad_dtype = torch.bfloat16 if grad_dtype is None else grad_dtype
+    g_code = _dtype_code(grad_dtype)
+    for name, t in (("s_in", s_in), ("grad_s_out", grad_s_out)):
+        if t is not None:
+            _check_tensor(name, t, 4, dev)
+            if t.dtype != torch.float32 or tuple(t.shape) != (B, Hkv, d, dv):
+                raise ValueError(f"{name} must be float32 [B, Hkv, d, dv]")
+    with torch.cuda.device(dev):
+        if out is None:
+            out = (torch.empty((B, Hq, N, d), dtype=grad_dtype, device=dev),
+                   torch.empty((B, Hkv, N, d), dtype=grad_dtype, device=dev),
+                   torch.empty((B, Hkv, N, dv), dtype=grad_dtype, device=dev))
+        for name, t, shape in zip(("dq", "dk", "dv"), out, ((B, Hq, N, d), (B, Hkv, N, d), (B, Hkv, N, dv))):
+            _check_tensor(name, t, 4, dev)
+            if t.dtype != grad_dtype or tuple(t.shape) != shape:
+                raise ValueError(f"{name} has the wrong dtype or shape")
+        if return_state_grad and grad_s_in is None:
+            grad_s_in = torch.empty((B, Hkv, d, dv), dtype=torch.float32, device=dev)
+        if grad_s_in is not None:
+            _check_tensor("grad_s_in", grad_s_in, 4, dev)
+            if grad_s_in.dtype != torch.float32 or tuple(grad_s_in.shape) != (B, Hkv, d, dv):
+                raise ValueError("grad_s_in must be float32 [B, Hkv, d, dv]")
+        ws_bytes = int(lib.la_backward_workspace_bytes(B, Hq, Hkv, N, d, dv, block, in_code))
+        if ws_bytes > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.la_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(grad_o), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]),
+                             B, Hq, Hkv, N, d, dv, block, in_code, g_code, _ptr(s_in), _ptr(grad_s_out),
+                             _ptr(grad_s_in), _ptr(workspace) if ws_bytes else None, ws_bytes,
+                             ctypes.c_void_p(stream))
+    if st != LA_OK:
+        raise LAError(st, "la_backward")
+    if grad_s_in is not None:
+        return out[0], out[1], out[2], grad_s_in
+    return tuple(out)
 
 
 def decode_step(S, q, k, v, out_dtype=None, out=None):

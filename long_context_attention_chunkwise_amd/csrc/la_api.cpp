@@ -96,6 +96,57 @@ Bf16Plan plan_bf16(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int
   return p;
 }
 
+BwdPlan plan_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv, int cus) {
+  BwdPlan p;
+  // dQ is the forward over (dO, V, K): head sizes swap.
+  p.fwd = plan_bf16(B, Hq, Hkv, N, dv, d, cus);
+  p.nblocks = (N + kBf16Block - 1) / kBf16Block;
+  if (p.nblocks == 0) return p;
+
+  // dK/dV: one workgroup per (batch, KV head, segment), one per compute unit.
+  const int64_t chains = B * Hkv;
+  constexpr int64_t kMinBlocks = 4;
+  int64_t P = 1;
+  if (chains < cus) P = (cus + chains - 1) / chains;
+  P = std::min(P, std::max<int64_t>(1, p.nblocks / kMinBlocks));
+  p.blocks_per_seg = (p.nblocks + P - 1) / P;
+  P = (p.nblocks + p.blocks_per_seg - 1) / p.blocks_per_seg;
+  p.P = static_cast<int>(P);
+
+  if (P > 1) {
+    // Pre-pass over (Q, dO) of every query head and every segment but the
+    // first.  Parts per segment: the count with the least (rounds of resident
+    // workgroups, three per compute unit) x (blocks per part + the cost of
+    // its 64 KiB partial, written once and read once by the scan: about four
+    // 32 KiB blocks of streaming), i.e. the shortest pre-pass when every part
+    // streams at the same rate; ties go to fewer parts.
+    constexpr int64_t kMinPartBlocks = 8;
+    constexpr int64_t kPartWgsPerCu = 3;
+    constexpr int64_t kPartialCostBlocks = 4;
+    const int64_t pre_chains = B * Hq * (P - 1);
+    const int64_t slots = kPartWgsPerCu * int64_t(cus);
+    int64_t best_R = 1, best_cost = -1;
+    const int64_t max_R = std::max<int64_t>(1, p.blocks_per_seg / kMinPartBlocks);
+    for (int64_t R = 1; R <= max_R; ++R) {
+      const int64_t bpp = (p.blocks_per_seg + R - 1) / R;
+      const int64_t rounds = (pre_chains * R + slots - 1) / slots;
+      const int64_t cost = rounds * (bpp + kPartialCostBlocks);
+      if (best_cost < 0 || cost < best_cost) {
+        best_cost = cost;
+        best_R = R;
+      }
+    }
+    p.blocks_per_part = (p.blocks_per_seg + best_R - 1) / best_R;
+    p.R = static_cast<int>((p.blocks_per_seg + p.blocks_per_part - 1) / p.blocks_per_part);
+    p.partial_floats = size_t(B * Hq) * size_t(P - 1) * size_t(p.R) * size_t(d * dv);
+    p.rstart_floats = size_t(chains) * size_t(P) * size_t(d * dv);
+  }
+  p.fwd_floats = p.fwd.workspace_bytes / sizeof(float);
+  p.sin_t_floats = size_t(chains) * size_t(d * dv);
+  p.workspace_bytes = (p.fwd_floats + p.sin_t_floats + p.partial_floats + p.rstart_floats) * sizeof(float);
+  return p;
+}
+
 }  // namespace la
 
 extern "C" {
@@ -275,6 +326,105 @@ la_status la_decode_step(float* S, const void* q, const void* k, const void* v, 
   hipError_t err = la::launch_decode(S, q, k, v, o, in_dtype == LA_BF16, out_dtype == LA_F32, B, Hq, Hkv, d,
                                      dv, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+}  // extern "C"
+
+namespace {
+
+la_status check_backward_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv,
+                               int64_t block, la_dtype in_dtype, la_dtype grad_dtype) {
+  la_status st = check_forward_shape(B, Hq, Hkv, N, d, dv, block, in_dtype, grad_dtype);
+  if (st != LA_OK) return st;
+  if (in_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
+  return LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t la_backward_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv,
+                                   int64_t block, la_dtype in_dtype) {
+  if (check_backward_shape(B, Hq, Hkv, N, d, dv, block, in_dtype, in_dtype) != LA_OK || N == 0) return 0;
+  return la::plan_backward(B, Hq, Hkv, N, d, dv, device_cus()).workspace_bytes;
+}
+
+la_status la_backward(const void* q, const void* k, const void* v, const void* grad_o, void* grad_q,
+                      void* grad_k, void* grad_v, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                      int64_t dv, int64_t block, la_dtype in_dtype, la_dtype grad_dtype, const float* s_in,
+                      const float* grad_s_out, float* grad_s_in, void* workspace, size_t workspace_bytes,
+                      la_stream stream) {
+  la_status st = check_backward_shape(B, Hq, Hkv, N, d, dv, block, in_dtype, grad_dtype);
+  if (st != LA_OK) return st;
+  if (N > 0 && (q == nullptr || k == nullptr || v == nullptr || grad_o == nullptr || grad_q == nullptr ||
+                grad_k == nullptr || grad_v == nullptr))
+    return LA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(grad_o) || !aligned16(grad_q) ||
+      !aligned16(grad_k) || !aligned16(grad_v) || !aligned16(s_in) || !aligned16(grad_s_out) ||
+      !aligned16(grad_s_in) || !aligned16(workspace))
+    return LA_ERR_ALIGN;
+
+  const size_t ei = esize(in_dtype), eg = esize(grad_dtype);
+  const size_t nq = size_t(B * Hq * N * d) * ei, nk = size_t(B * Hkv * N * d) * ei;
+  const size_t nv = size_t(B * Hkv * N * dv) * ei, ndo = size_t(B * Hq * N * dv) * ei;
+  const size_t gq = size_t(B * Hq * N * d) * eg, gk = size_t(B * Hkv * N * d) * eg;
+  const size_t gv = size_t(B * Hkv * N * dv) * eg;
+  const size_t ns = size_t(B * Hkv * d * dv) * sizeof(float);
+  struct Range {
+    const void* p;
+    size_t n;
+  };
+  const Range inputs[] = {{q, nq}, {k, nk}, {v, nv}, {grad_o, ndo}, {s_in, ns}, {grad_s_out, ns}};
+  const Range outputs[] = {{grad_q, gq}, {grad_k, gk}, {grad_v, gv}, {grad_s_in, ns}};
+  for (int i = 0; i < 4; ++i) {
+    for (const Range& in : inputs) {
+      // grad_s_in may be grad_s_out itself (in-place chunk chaining)
+      if (i == 3 && in.p == grad_s_out && grad_s_in == grad_s_out) continue;
+      if (overlap(outputs[i].p, outputs[i].n, in.p, in.n)) return LA_ERR_ALIAS;
+    }
+    for (int j = 0; j < i; ++j)
+      if (overlap(outputs[i].p, outputs[i].n, outputs[j].p, outputs[j].n)) return LA_ERR_ALIAS;
+  }
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (N == 0) {
+    // No tokens: the state gradient passes through unchanged.
+    if (grad_s_in == nullptr || grad_s_in == grad_s_out) return LA_OK;
+    return la::launch_copy_or_zero(grad_s_in, grad_s_out, ns / sizeof(float), hs) == hipSuccess ? LA_OK
+                                                                                                  : LA_ERR_HIP;
+  }
+
+  const la::BwdPlan plan = la::plan_backward(B, Hq, Hkv, N, d, dv, device_cus());
+  const size_t nw = plan.workspace_bytes;
+  if (workspace == nullptr || workspace_bytes < nw) return LA_ERR_WORKSPACE;
+  for (const Range& in : inputs)
+    if (overlap(workspace, nw, in.p, in.n)) return LA_ERR_ALIAS;
+  for (const Range& out : outputs)
+    if (overlap(workspace, nw, out.p, out.n)) return LA_ERR_ALIAS;
+
+  float* ws = static_cast<float*>(workspace);
+  float* ws_fwd = ws;
+  float* sin_t = ws_fwd + plan.fwd_floats;
+  float* ws_kv = sin_t + plan.sin_t_floats;
+  const bool out_f32 = grad_dtype == LA_F32;
+
+  // dQ: the forward over (queries dO, keys V, values K) from s_in^T.
+  const float* s_t = nullptr;
+  if (s_in != nullptr) {
+    if (la::launch_transpose_states(s_in, sin_t, B * Hkv, hs) != hipSuccess) return LA_ERR_HIP;
+    s_t = sin_t;
+  }
+  if (plan.fwd.use_starts && la::launch_segment_states(v, k, s_t, B, Hkv, N, plan.fwd, ws_fwd, hs) != hipSuccess)
+    return LA_ERR_HIP;
+  if (la::launch_fwd_bf16(grad_o, v, k, grad_q, out_f32, s_t, nullptr, B, Hq, Hkv, N, plan.fwd, ws_fwd, hs) !=
+      hipSuccess)
+    return LA_ERR_HIP;
+  // dK, dV, ds_in: the reverse recurrence.
+  if (la::launch_bwd_kv(q, k, v, grad_o, grad_k, grad_v, out_f32, grad_s_out, grad_s_in, B, Hq, Hkv, N, plan,
+                        ws_kv, hs) != hipSuccess)
+    return LA_ERR_HIP;
+  return LA_OK;
 }
 
 }  // extern "C"

@@ -34,111 +34,16 @@
 //    a scan adds the parts up (s_in first, then parts in order), exact by
 //    associativity of the sums.
 #include "la_internal.h"
+#include "la_mfma.h"
 
 namespace la {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((__vector_size__(16)));
-typedef __bf16 bf16x4 __attribute__((__vector_size__(8)));
-typedef short short4v __attribute__((__vector_size__(8)));
-typedef float floatx4 __attribute__((__vector_size__(16)));
-typedef __attribute__((address_space(3))) short4v lds_short4v;
+using namespace mfma16;
 
-constexpr int C = 64;          // tokens per block
-constexpr int D = 128;         // q/k head size
-constexpr int DV = 128;        // v head size
-// LDS row pitches (bf16 elements).  K and V tiles are read mostly through the
-// transpose load (a half-wave touches 8 consecutive rows x 16 bytes): a
-// 288-byte pitch puts those rows on disjoint banks.  The bf16 state is read
-// with 16-byte loads of 16 consecutive rows: a 272-byte pitch does the same
-// for that pattern.
-constexpr int ROWKV = D + 16;
-constexpr int ROWST = D + 8;
+
 constexpr int kMainThreads = 512;
 constexpr int kPartThreads = 256;
-
-__device__ __forceinline__ floatx4 mfma(bf16x8 a, bf16x8 b, floatx4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ bf16x8 ld_global16(const uint16_t* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
-}
-
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
-// Streaming (non-temporal) 16-byte load for data read exactly once in whole
-// rows (K and V tiles): measured faster on gfx950 than cached loads.  Q is not
-// loaded this way: each Q load covers half of a 128-byte line and relies on
-// the cache for the other half.
-__device__ __forceinline__ uint4 ld_stream16(const uint16_t* p) {
-  const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(x.x, x.y, x.z, x.w);
-}
-
-__device__ __forceinline__ bf16x8 zero_bf16x8() {
-  bf16x8 z;
-  for (int i = 0; i < 8; ++i) z[i] = (__bf16)0.0f;
-  return z;
-}
-
-__device__ __forceinline__ bf16x8 ld_lds16(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
-
-// LDS transpose load: each lane of a 16-lane group passes the address of 4
-// consecutive bf16 values; lane i receives column i of the 4 rows the group
-// addressed (see tr_operand).
-__device__ __forceinline__ bf16x4 ld_lds_tr(const uint16_t* p) {
-  lds_short4v* lp = (lds_short4v*)(uint16_t*)p;  // generic -> LDS address space
-  short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lp);
-  return __builtin_bit_cast(bf16x4, r);
-}
-
-// Operand of a token-contracting product, from a row-major [token][col] LDS
-// tile: lane (l16, grp) gets column col0 + l16 at the eight token slots
-//   32p + 4grp + {0..3}  and  32p + 16 + 4grp + {0..3}.
-// The same slot order is used for both operands of every such product, and it
-// matches the accumulator layout of two vertically adjacent 16x16 P^T tiles.
-//
-// With cstride = 8 the 16 columns are col0 + 8j + {0..3} for j = 0..3: lane
-// l16 gets column col0 + 8(l16/4) + l16%4.  Two such tiles (col0 and col0+4)
-// cover 32 consecutive columns so that the accumulator of a product whose rows
-// are those columns holds 8 consecutive columns per lane.
-__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int p, int col0, int l16, int grp,
-                                             int cstride = 4) {
-  const int r = 32 * p + 4 * grp + (l16 >> 2);
-  const int c = col0 + cstride * (l16 & 3);
-  bf16x4 lo = ld_lds_tr(tile + r * ROWKV + c);
-  bf16x4 hi = ld_lds_tr(tile + (r + 16) * ROWKV + c);
-  bf16x8 out;
-  for (int i = 0; i < 4; ++i) {
-    out[i] = lo[i];
-    out[i + 4] = hi[i];
-  }
-  return out;
-}
-
-__device__ __forceinline__ bf16x4 to_bf16x4(floatx4 x) {
-  bf16x4 r;
-  for (int i = 0; i < 4; ++i) r[i] = (__bf16)x[i];
-  return r;
-}
-
-__device__ __forceinline__ bf16x8 pack_tiles(floatx4 lo, floatx4 hi) {
-  bf16x8 r;
-  for (int i = 0; i < 4; ++i) {
-    r[i] = (__bf16)lo[i];
-    r[i + 4] = (__bf16)hi[i];
-  }
-  return r;
-}
-
-// Zero the entries of a diagonal P^T tile above the causal boundary: entry
-// (s = 4grp + i, t = l16) within the tile is kept when s <= t.
-__device__ __forceinline__ floatx4 causal_mask(floatx4 x, int l16, int grp) {
-  for (int i = 0; i < 4; ++i)
-    if (4 * grp + i > l16) x[i] = 0.0f;
-  return x;
-}
 
 struct __align__(16) MainSmem {
   uint16_t k[2][C * ROWKV];
@@ -518,8 +423,10 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
   }
 }
 
-// Pre-pass: partial[c][j][r] = sum of K_b^T V_b over part r of segment j of
-// chain c (every segment but the last).  Four waves; wave w owns state
+// Pre-pass: partial[c][j][r] = sum of K_b^T V_b over part r of segment
+// j + seg_offset of chain c, for j < P - 1 (the forward sums every segment but
+// the last with seg_offset 0; the backward every segment but the first with
+// seg_offset 1).  Four waves; wave w owns state
 // columns [32w, 32w+32).  A pure HBM stream: the K/V tile is single-buffered
 // in LDS (36 KiB) so three workgroups share a CU, each with the next block's
 // loads in flight while it multiplies the current one.
@@ -527,7 +434,8 @@ __global__ __launch_bounds__(kPartThreads, 3) void state_parts(const uint16_t* _
                                                            const uint16_t* __restrict__ v,
                                                            float* __restrict__ partial, int64_t N,
                                                            int64_t nblocks, int64_t blocks_per_seg,
-                                                           int64_t blocks_per_part, int P, int R) {
+                                                           int64_t blocks_per_part, int P, int R,
+                                                           int seg_offset) {
   __shared__ __align__(16) uint16_t ksm[C * ROWKV];
   __shared__ __align__(16) uint16_t vsm[C * ROWKV];
 
@@ -537,8 +445,9 @@ __global__ __launch_bounds__(kPartThreads, 3) void state_parts(const uint16_t* _
   const int c = blockIdx.x / per_chain;
   const int rem = blockIdx.x % per_chain;
   const int j = rem / R, r = rem % R;
-  const int64_t seg_end = (int64_t(j) + 1) * blocks_per_seg;
-  int64_t b0 = int64_t(j) * blocks_per_seg + int64_t(r) * blocks_per_part;
+  const int64_t js = int64_t(j) + seg_offset;  // segment summed by this part
+  const int64_t seg_end = (js + 1) * blocks_per_seg;
+  int64_t b0 = js * blocks_per_seg + int64_t(r) * blocks_per_part;
   int64_t b1 = b0 + blocks_per_part;
   if (b1 > seg_end) b1 = seg_end;
   if (b1 > nblocks) b1 = nblocks;
@@ -640,12 +549,21 @@ hipError_t launch_segment_states(const void* k, const void* v, const float* s_in
   if (plan.P > 1) {
     hipLaunchKernelGGL(state_parts, dim3(unsigned(kv_chains * (plan.P - 1) * plan.R)), dim3(kPartThreads), 0,
                        stream, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), partial, N,
-                       plan.nblocks, plan.blocks_per_seg, plan.blocks_per_part, plan.P, plan.R);
+                       plan.nblocks, plan.blocks_per_seg, plan.blocks_per_part, plan.P, plan.R, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(scan_starts, dim3(unsigned(kv_chains * D * DV / 256)), dim3(256), 0, stream, partial, starts,
                      s_in, plan.P, plan.R);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_parts(const void* a, const void* b, float* partial, int64_t chains, int64_t N,
+                              int64_t nblocks, int64_t blocks_per_seg, int64_t blocks_per_part, int P, int R,
+                              int seg_offset, hipStream_t stream) {
+  hipLaunchKernelGGL(state_parts, dim3(unsigned(chains * (P - 1) * R)), dim3(kPartThreads), 0, stream,
+                     static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), partial, N, nblocks,
+                     blocks_per_seg, blocks_per_part, P, R, seg_offset);
   return hipGetLastError();
 }
 

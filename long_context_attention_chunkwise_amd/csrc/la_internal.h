@@ -49,6 +49,39 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                            const float* s_in, float* s_out, int64_t B, int64_t Hq, int64_t Hkv,
                            int64_t N, const Bf16Plan& plan, const void* workspace, hipStream_t stream);
 
+// Pre-pass over `chains` row-major [N][128] tile pairs (a, b): partial sums of
+// a_b^T b_b over part r of segment j + seg_offset, j < P - 1.
+hipError_t launch_state_parts(const void* a, const void* b, float* partial, int64_t chains, int64_t N,
+                              int64_t nblocks, int64_t blocks_per_seg, int64_t blocks_per_part, int P, int R,
+                              int seg_offset, hipStream_t stream);
+
+// Backward work split: dK/dV walk each chain's segments from the end; segment
+// j starts from the sum of q^T dO over later segments and the group's heads.
+struct BwdPlan {
+  Bf16Plan fwd;                 // dQ = forward over (dO, V, K)
+  int64_t nblocks = 0;
+  int64_t blocks_per_seg = 0;
+  int64_t blocks_per_part = 0;
+  int P = 1;
+  int R = 1;
+  size_t fwd_floats = 0;        // forward workspace
+  size_t sin_t_floats = 0;      // transposed initial state for dQ
+  size_t partial_floats = 0;    // B*Hq*(P-1)*R*d*dv
+  size_t rstart_floats = 0;     // B*Hkv*P*d*dv
+  size_t workspace_bytes = 0;   // all four, in that order
+};
+
+BwdPlan plan_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv, int cus);
+
+hipError_t launch_transpose_states(const float* in, float* out, int64_t count, hipStream_t stream);
+
+// dK, dV and (if ds_in) the initial-state gradient; the reverse state starts
+// from ds_out (zeros if NULL).  workspace_f holds the plan's partials and
+// segment start states.
+hipError_t launch_bwd_kv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dvg,
+                         bool out_f32, const float* ds_out, float* ds_in, int64_t B, int64_t Hq, int64_t Hkv,
+                         int64_t N, const BwdPlan& plan, float* workspace_f, hipStream_t stream);
+
 // dst[i] = src ? src[i] : 0 for i < n.
 hipError_t launch_copy_or_zero(float* dst, const float* src, size_t n, hipStream_t stream);
 

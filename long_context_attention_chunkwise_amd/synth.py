@@ -6,7 +6,8 @@ fixed: every q head, then every k head, then every v head, each as an
 [N, dim] float32 standard-normal draw from one generator seeded with `seed`,
 then transformed (ReLU for q and k where the workload says so, then a scale)
 and rounded to the storage dtype (round-to-nearest-even by torch).
-Decode steps draw q, k, v for step 0, then step 1, and so on.
+Decode steps draw q, k, v for step 0, then step 1, and so on.  Upstream
+gradients for the backward pass are N(0,1) draws of their own generator.
 """
 import math
 from dataclasses import dataclass
@@ -90,6 +91,21 @@ def make_decode_steps(w, device, seed=1, steps=None, B=None):
                 x.mul_(sc)
             dst.copy_(x)
     return q, k, v
+
+
+def make_grad(shape, device, seed=3, dtype=torch.bfloat16, chunk_rows=1 << 20):
+    """An upstream gradient dL/do of `shape` [B, H, N, dv]: N(0,1) draws head
+    by head (rows in chunks of chunk_rows), rounded to dtype."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    out = torch.empty(shape, dtype=dtype, device=device)
+    B, H, N, dv = shape
+    for b in range(B):
+        for h in range(H):
+            for a in range(0, N, chunk_rows):
+                e = min(a + chunk_rows, N)
+                out[b, h, a:e].copy_(torch.randn((e - a, dv), generator=gen, device=device, dtype=torch.float32))
+    return out
 
 
 def random_state(shape, device, seed=2, scale=1.0):

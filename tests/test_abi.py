@@ -19,7 +19,7 @@ F32, BF16 = la.LA_F32, la.LA_BF16
 # Fake, widely spaced, 16-byte aligned device addresses: validation only
 # compares them, it never dereferences them.
 GB = 1 << 40
-Q, K, V, O, S_IN, S_OUT, WS = (ctypes.c_void_p(GB * i) for i in range(1, 8))
+Q, K, V, O, S_IN, S_OUT, WS, DO, DQ, DK, DV, DS = (ctypes.c_void_p(GB * i) for i in range(1, 13))
 
 
 def declared_functions():
@@ -84,6 +84,30 @@ def test_decode_validation(lib):
     assert dec(o=ctypes.c_void_p(GB * 5 + 16)) == ALIAS   # o inside S
 
 
+def bwd(lib, q=Q, k=K, v=V, do=DO, dq=DQ, dk=DK, dv=DV, B=1, Hq=4, Hkv=1, N=1000, d=128, dvs=128, block=64,
+        i=BF16, g=BF16, s_in=S_IN, ds_out=S_OUT, ds_in=DS, ws=WS, ws_bytes=1 << 32):
+    return lib.la_backward(q, k, v, do, dq, dk, dv, B, Hq, Hkv, N, d, dvs, block, i, g, s_in, ds_out, ds_in, ws,
+                           ws_bytes, None)
+
+
+def test_backward_validation(lib):
+    assert bwd(lib, do=None) == NULL
+    assert bwd(lib, dk=None) == NULL
+    assert bwd(lib, Hq=6, Hkv=4) == SHAPE
+    assert bwd(lib, N=-1) == SHAPE
+    assert bwd(lib, i=F32, g=F32) == UNSUP                 # bf16 inputs only
+    assert bwd(lib, d=64) == UNSUP
+    assert bwd(lib, g=2) == UNSUP
+    assert bwd(lib, dq=ctypes.c_void_p(GB * 9 + 8)) == ALIGN
+    assert bwd(lib, dq=ctypes.c_void_p(GB * 1 + 4096)) == ALIAS       # dq inside q
+    assert bwd(lib, dv=ctypes.c_void_p(GB * 9 + 4096)) == ALIAS       # dv inside dq
+    assert bwd(lib, ds_in=ctypes.c_void_p(GB * 6 + 64)) == ALIAS      # partial overlap with ds_out
+    assert bwd(lib, ds_in=ctypes.c_void_p(GB * 8 + 64)) == ALIAS      # ds_in inside dO
+    assert bwd(lib, ws=None) == WORKSPACE
+    assert bwd(lib, ws_bytes=1024) == WORKSPACE
+    assert bwd(lib, ws=ctypes.c_void_p(GB * 10 + 256)) == ALIAS       # workspace inside dk
+
+
 def test_workspace_plan(lib):
     # Host planning with the default 256 compute units (no device here): the
     # 1M-token GQA problem splits each of the 32 chains into 8 segments and
@@ -95,6 +119,15 @@ def test_workspace_plan(lib):
     assert lib.la_forward_workspace_bytes(256, 128, 32, 8192, 128, 128, 64, BF16) == 0
     assert lib.la_forward_workspace_bytes(1, 128, 32, 0, 128, 128, 64, BF16) == 0
     assert lib.la_forward_workspace_bytes(1, 6, 4, 64, 128, 128, 64, BF16) == 0   # invalid -> 0
+    # Backward at 1M tokens: the dQ forward's workspace, the transposed
+    # initial states, and for dK/dV 8 segments per chain whose 7 later
+    # segments are summed over (Q, dO) of 128 query heads in 6 parts each
+    # (5376 pre-pass workgroups: seven full rounds), plus 8 start states per
+    # chain.
+    n = lib.la_backward_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, 64, BF16)
+    assert n == ((32 * 7 * 3 + 32 * 8) + 32 + 128 * 7 * 6 + 32 * 8) * 128 * 128 * 4
+    assert lib.la_backward_workspace_bytes(1, 128, 32, 0, 128, 128, 64, BF16) == 0
+    assert lib.la_backward_workspace_bytes(1, 4, 2, 64, 128, 128, 64, F32) == 0
 
 
 def test_binding_requires_gpu_tensors():

@@ -1,0 +1,153 @@
+"""Backward-pass parity: la_backward through the C ABI against the fp64
+oracle's block-wise backward (itself pinned by finite differences in
+test_oracle_backward.py).
+
+Inputs are seeded and synthetic: q, k, v from synth.make_qkv (the forward
+workloads' distributions), the upstream gradient dO ~ N(0,1) from
+synth.make_grad, optional initial state and final-state gradient N(0,1)*0.5.
+Sizes span several 64-token blocks, several reverse segments per chain (the
+pre-pass over (Q, dO) and the reverse scan), ragged tails, group sizes 1 to 4
+and both gradient dtypes; the 1M-token workload is checked on its first and
+last 4096 tokens, where the oracle can compute the gradients exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_chunkwise_amd as la
+import oracle
+from long_context_attention_chunkwise_amd import synth
+from gpu_util import check_close, f64, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+BF16 = torch.bfloat16
+
+
+def inputs(B, Hq, Hkv, N, seed):
+    w = synth.Workload("t", B, Hq, Hkv, N, 128, 128, 64, BF16, True, False)
+    q, k, v = synth.make_qkv(w, DEV, seed=seed)
+    do = synth.make_grad((B, Hq, N, 128), DEV, seed=seed + 1)
+    return q, k, v, do
+
+
+def check_grads(tag, got, ref, grad_dtype):
+    for name, g, r in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
+        check_close(f"{tag} {name}", f64(g), r, BF16, grad_dtype)
+    if len(got) > 3:
+        check_close(f"{tag} ds_in", f64(got[3]), ref[3], BF16, torch.float32)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,grad_dtype,s_in,ds_out", [
+    (1, 4, 1, 3000, torch.float32, False, False),     # G = 4, 11 segments, ragged tail
+    (2, 8, 2, 777, BF16, True, True),                 # G = 4, bf16 gradients, both state terms
+    (1, 2, 2, 100, torch.float32, True, False),       # G = 1, two blocks
+    (1, 6, 2, 1000, torch.float32, False, True),      # G = 3 (dQ forward with one head per workgroup)
+    (1, 4, 2, 64, BF16, False, False),                # one full block
+    (1, 4, 2, 1, torch.float32, True, True),          # one token
+    (1, 8, 1, 4100, BF16, False, False),              # G = 8, dQ forward subgroups
+])
+def test_backward_matches_oracle(B, Hq, Hkv, N, grad_dtype, s_in, ds_out):
+    need_gpu()
+    say(f"case backward B={B} Hq={Hq} Hkv={Hkv} N={N} grad={grad_dtype} s_in={s_in} ds_out={ds_out}")
+    q, k, v, do = inputs(B, Hq, Hkv, N, seed=N + Hq)
+    S0 = synth.random_state((B, Hkv, 128, 128), DEV, seed=N + 11, scale=0.5) if s_in else None
+    dS = synth.random_state((B, Hkv, 128, 128), DEV, seed=N + 12, scale=0.5) if ds_out else None
+    got = la.backward(q, k, v, do, grad_dtype=grad_dtype, s_in=S0, grad_s_out=dS, return_state_grad=True)
+    torch.cuda.synchronize()
+    ref = oracle.backward_chunkwise(f64(q), f64(k), f64(v), f64(do), 64, None if S0 is None else f64(S0),
+                                    None if dS is None else f64(dS))
+    check_grads("", got, ref, grad_dtype)
+
+
+def test_backward_empty_sequence():
+    """N = 0: no gradients to write; ds_in equals ds_out (zeros without it)."""
+    need_gpu()
+    q = torch.empty((1, 4, 0, 128), dtype=BF16, device=DEV)
+    k = torch.empty((1, 1, 0, 128), dtype=BF16, device=DEV)
+    dS = synth.random_state((1, 1, 128, 128), DEV, seed=5)
+    got = la.backward(q, k, k, q, grad_s_out=dS, return_state_grad=True)
+    zero = la.backward(q, k, k, q, return_state_grad=True)
+    torch.cuda.synchronize()
+    assert torch.equal(got[3], dS) and bool((zero[3] == 0).all())
+
+
+def test_backward_in_place_state_gradient_and_chunks():
+    """A 6000-token sequence as two chunks: forward with the state carried,
+    then backward from the last chunk to the first with grad_s_in written in
+    place over grad_s_out; equals the oracle's whole-sequence gradients."""
+    need_gpu()
+    B, Hq, Hkv, N, a = 1, 8, 2, 6000, 2500
+    say(f"case backward chunks B={B} Hq={Hq} Hkv={Hkv} N={N} split={a}")
+    q, k, v, do = inputs(B, Hq, Hkv, N, seed=31)
+    S0 = synth.random_state((B, Hkv, 128, 128), DEV, seed=32, scale=0.5)
+    parts = [(0, a), (a, N)]
+    S_a = la.forward(q[:, :, :a].contiguous(), k[:, :, :a].contiguous(), v[:, :, :a].contiguous(), s_in=S0,
+                     return_state=True)[1]
+    dS = torch.zeros((B, Hkv, 128, 128), dtype=torch.float32, device=DEV)
+    grads = {}
+    for (lo, hi), s in reversed(list(zip(parts, (S0, S_a)))):
+        sl = [x[:, :, lo:hi].contiguous() for x in (q, k, v, do)]
+        dq, dk, dv = la.backward(*sl, grad_dtype=torch.float32, s_in=s, grad_s_out=dS, grad_s_in=dS)[:3]
+        grads[lo] = (dq, dk, dv)
+    torch.cuda.synchronize()
+    got = [torch.cat([grads[0][i], grads[a][i]], dim=2) for i in range(3)] + [dS]
+    ref = oracle.backward_chunkwise(f64(q), f64(k), f64(v), f64(do), 64, f64(S0))
+    check_grads("chunked", got, ref, torch.float32)
+
+
+def test_backward_repeatable():
+    """Two calls on the same inputs give bitwise-identical gradients (fixed
+    reduction orders everywhere)."""
+    need_gpu()
+    q, k, v, do = inputs(1, 8, 2, 20000, seed=41)
+    a = la.backward(q, k, v, do, return_state_grad=True)
+    b = la.backward(q, k, v, do, return_state_grad=True)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+def test_backward_gqa_1m_slices():
+    """B=1, 128/32 heads, N=1,048,576 (the forward workload), bf16 gradients.
+    For KV groups 0 and 31: dk, dv of the last 4096 tokens (they depend on
+    those tokens only), dk, dv, dq of the first 4096 tokens (the reverse state
+    entering them is sum over the group's heads of Q^T dO over every later
+    token, computed in float64 here), dq of the last 4096 tokens (from the
+    forward state of (V, K) before them) and the initial-state gradient."""
+    need_gpu()
+    w = synth.WORKLOADS["gqa_1m"]
+    G = w.Hq // w.Hkv
+    N, W = w.N, 4096
+    say(f"case backward gqa_1m: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={N}")
+    q, k, v = synth.make_qkv(w, DEV, seed=0)
+    do = synth.make_grad((w.B, w.Hq, N, w.dv), DEV, seed=1)
+    dq, dk, dv, ds = la.backward(q, k, v, do, return_state_grad=True)
+    torch.cuda.synchronize()
+    for x in (dq, dk, dv):
+        assert bool(torch.isfinite(x).all())
+    for g in (0, 31):
+        hs = slice(g * G, (g + 1) * G)
+        gs = slice(g, g + 1)
+        a = N - W
+        # last W tokens: dk, dv from the tokens after them only
+        tail = oracle.backward_chunkwise(f64(q[:, hs, a:]), f64(k[:, gs, a:]), f64(v[:, gs, a:]),
+                                         f64(do[:, hs, a:]), 64)
+        check_close(f"group {g} dk tokens [{a}, {N})", f64(dk[:, gs, a:]), tail[1], BF16, BF16)
+        check_close(f"group {g} dv tokens [{a}, {N})", f64(dv[:, gs, a:]), tail[2], BF16, BF16)
+        # dq of the last W tokens: forward state of (V, K) over the earlier tokens
+        S_vk = oracle.final_state(f64(v[:, gs, :a]), f64(k[:, gs, :a]))
+        ref_dq = oracle.chunkwise(f64(do[:, hs, a:]), f64(v[:, gs, a:]), f64(k[:, gs, a:]), 64, S_vk)[0]
+        check_close(f"group {g} dq tokens [{a}, {N})", f64(dq[:, hs, a:]), ref_dq, BF16, BF16)
+        # first W tokens: the reverse state after them
+        R = np.zeros((1, 1, w.d, w.dv))
+        for h in range(G):
+            qh = f64(q[:, g * G + h, W:])[0]
+            doh = f64(do[:, g * G + h, W:])[0]
+            R[0, 0] += qh.T @ doh
+            del qh, doh
+        head = oracle.backward_chunkwise(f64(q[:, hs, :W]), f64(k[:, gs, :W]), f64(v[:, gs, :W]),
+                                         f64(do[:, hs, :W]), 64, None, R)
+        check_close(f"group {g} dk tokens [0, {W})", f64(dk[:, gs, :W]), head[1], BF16, BF16)
+        check_close(f"group {g} dv tokens [0, {W})", f64(dv[:, gs, :W]), head[2], BF16, BF16)
+        check_close(f"group {g} dq tokens [0, {W})", f64(dq[:, hs, :W]), head[0], BF16, BF16)
+        check_close(f"group {g} ds_in", f64(ds[:, gs]), head[3], BF16, torch.float32)
