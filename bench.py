@@ -9,6 +9,10 @@ Reported: tokens/s, TFLOP/s against the bf16 dense matrix-core peak, and the
 HBM roofline of the dominant kernel (the output kernel), timed with HIP
 events on the stream it runs on.
 
+Backward (secondary): la_backward (dQ, dK, dV and the initial-state gradient)
+on the same workload with a seeded N(0,1) upstream gradient, timed with HIP
+events per call; reported as tokens/s and algorithmic HBM GB/s.
+
 Decode (secondary): 256 sequences x 32 KV heads of float32 128x128 state
 (512 MiB) initialised by the forward kernel over a seeded 8192-token prefix,
 then single-token steps; reported as HBM GB/s.
@@ -53,12 +57,15 @@ def measured_traffic(kernel, workload):
     for m in re.finditer(r"traffic (\S+) (\S+) bytes=(\d+) source=(\S+) sha256=([0-9a-f]+)", text):
         if (m.group(1), m.group(2)) != (kernel, workload):
             continue
-        src = os.path.join(ROOT, "long_context_attention_chunkwise_amd", "csrc", m.group(4))
+        # source: the kernel's file and the headers it includes, joined by '+';
+        # the digest covers their concatenated bytes in that order.
+        h = hashlib.sha256()
         try:
-            digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+            for name in m.group(4).split("+"):
+                h.update(open(os.path.join(ROOT, "long_context_attention_chunkwise_amd", "csrc", name), "rb").read())
         except OSError:
             return None
-        return int(m.group(3)) if digest == m.group(5) else None
+        return int(m.group(3)) if h.hexdigest() == m.group(5) else None
     return None
 
 
@@ -156,6 +163,75 @@ def bench_forward(la, synth, torch, w, steps, warmup):
     return q, k, v, ms_step, statistics.mean(t_states), statistics.mean(t_main), ws_bytes
 
 
+def backward_flops(w, N):
+    """Algorithmic flops of the backward pass (per the block recurrences).
+
+    Per token and query head: dQ is a forward pass over (dO, V, K); dK and dV
+    take two masked score products (Q K^T, dO V^T) and their two products
+    with dO and Q, (d + dv)(C + 1) each pair, the reverse-state update 2 d dv,
+    and the two inter products 4 d dv shared by the Hq/Hkv query heads.
+    """
+    C, d, dv, G = w.block, w.d, w.dv, w.Hq // w.Hkv
+    per = 3 * (d + dv) * (C + 1) + 4 * d * dv + 6 * d * dv / G
+    return per * w.B * w.Hq * N
+
+
+def backward_bytes(w, N, grad_bytes=2):
+    """Algorithmic HBM bytes of one backward pass: read q, k, v, dO once,
+    write dq, dk, dv once."""
+    e = 2
+    reads = w.B * N * (w.Hq * w.d + w.Hkv * (w.d + w.dv) + w.Hq * w.dv) * e
+    writes = w.B * N * (w.Hq * w.d + w.Hkv * (w.d + w.dv)) * grad_bytes
+    return reads + writes
+
+
+def bench_backward(la, synth, torch, w, q, k, v, steps, warmup):
+    import ctypes
+    lib = la.load_library()
+    dev = torch.device("cuda:0")
+    log(f"[bench] backward: upstream gradient for {w.name}")
+    do = synth.make_grad((w.B, w.Hq, w.N, w.dv), dev, seed=1)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ds = torch.empty((w.B, w.Hkv, w.d, w.dv), dtype=torch.float32, device=dev)
+    ws_bytes = la.backward_workspace_bytes(w.B, w.Hq, w.Hkv, w.N, w.d, w.dv, w.block, torch.bfloat16)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    P = ctypes.c_void_p
+    args = (P(q.data_ptr()), P(k.data_ptr()), P(v.data_ptr()), P(do.data_ptr()), P(dq.data_ptr()),
+            P(dk.data_ptr()), P(dv.data_ptr()), w.B, w.Hq, w.Hkv, w.N, w.d, w.dv, w.block, la.LA_BF16, la.LA_BF16,
+            None, None, P(ds.data_ptr()), P(ws.data_ptr()), ws_bytes, P(stream.cuda_stream))
+    for _ in range(warmup):
+        st = lib.la_backward(*args)
+        if st:
+            raise RuntimeError(f"backward failed: {la.status_str(st)}")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        evs[i][0].record(stream)
+        st = lib.la_backward(*args)
+        evs[i][1].record(stream)
+        if st:
+            raise RuntimeError(f"backward failed: {la.status_str(st)}")
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    if not all(bool(torch.isfinite(x).all().item()) for x in (dq, dk, dv, ds)):
+        raise RuntimeError("non-finite gradient")
+    per = [a.elapsed_time(b) for a, b in evs]
+    ms = statistics.mean(per)
+    nbytes = backward_bytes(w, w.N)
+    flops = backward_flops(w, w.N)
+    del do, dq, dk, dv, ds, ws
+    return {"steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4), "ms_per_step_wall": round(wall, 4),
+            "tokens_per_s": round(w.B * w.N / (ms * 1e-3), 1),
+            "config": {"workload": w.name, "grad_dtype": "bf16", "s_in": False, "grad_s_out": False},
+            "hbm": {"bytes_alg": nbytes, "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+            "mfma": {"flops_alg": flops, "tflops_alg": round(flops / (ms * 1e-3) / 1e12, 2),
+                     "frac_alg": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+            "workspace_bytes": ws_bytes}
+
+
 def bench_decode(la, synth, torch, w, steps, warmup):
     dev = torch.device("cuda:0")
     S = torch.empty((w.B, w.Hkv, w.d, w.dv), dtype=torch.float32, device=dev)
@@ -205,6 +281,8 @@ def main():
     ap.add_argument("--workload", default="gqa_1m", help="forward workload name (synth.WORKLOADS)")
     ap.add_argument("--decode-steps", type=int, default=1000, help="0 skips the decode measurement")
     ap.add_argument("--decode-warmup", type=int, default=10)
+    ap.add_argument("--backward-steps", type=int, default=5, help="0 skips the backward measurement")
+    ap.add_argument("--backward-warmup", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (hardware-counter calibration)")
@@ -237,6 +315,10 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline (fp64 oracle) ...")
         cpu = cpu_baseline(q, k, v, w)
+    backward = None
+    if args.backward_steps > 0:
+        backward = bench_backward(la, synth, torch, w, q, k, v, args.backward_steps, args.backward_warmup)
+        log(f"[bench] backward: {backward['ms_per_step']:.3f} ms/step")
     del q, k, v
     torch.cuda.empty_cache()
 
@@ -280,6 +362,7 @@ def main():
                  "peak_tflops": PEAK_BF16_TFLOPS, "flops_alg": f_alg, "flops_tile": f_tile},
         "phases_ms": {"segment_states": round(ms_states, 4), "outputs": round(ms_main, 4)},
         "workspace_bytes": ws_bytes,
+        "backward": backward,
         "decode": decode,
         "cpu_baseline": cpu,
         "device": {"name": props.name, "gcnArchName": getattr(props, "gcnArchName", ""),
