@@ -12,6 +12,7 @@ from .lightning import (  # noqa: F401
     decode_step,
     final_state,
     noncausal,
+    variant,
     backward_brute_force,
     backward_chunkwise,
 )

@@ -22,6 +22,9 @@ Sources (page title, then the passage):
   heads over 32 KV heads (grouped-query attention).
 * "奧特曼的“溫和奇點”愿景，線性注意力的勝利？MiniMax-M1技術報告深度解析"
   (digipub.cc), the associativity passage: A*B*C = A*(B*C).
+* "从 Transformer 到 Lightning Attention，从 PPO 到 CISPO" (space.minimaxi.com),
+  the "Transformers are RNNs" entry: softmax approximated by a kernel feature
+  map (the family of the normalised variant in `variant`).
 
 Readings where the pages are silent (each pinned in tests/test_oracle.py):
 
@@ -39,7 +42,9 @@ hand-worked example, closed forms, brute force over Python loops, block-size
 invariance, causality, the final state against a library GEMM, the non-causal
 special case, linearity, GQA against repeated-head MHA, and recurrent/decode
 against the block form (tests/test_oracle.py); the backward pass against
-central finite differences of the forward (tests/test_oracle_backward.py).
+central finite differences of the forward (tests/test_oracle_backward.py);
+the variants against their special cases, closed forms and the token-by-token
+recurrence (tests/test_oracle_variants.py).
 No function here is parity unpinned.
 
 Layouts: q [B, Hq, N, d], k [B, Hkv, N, d], v [B, Hkv, N, dv],
@@ -179,6 +184,63 @@ def noncausal(q, k, v):
     gidx = _heads_to_groups(Hq, Hkv)
     kv = final_state(k, v)
     return np.matmul(q, kv[:, gidx])
+
+
+# ---------------------------------------------------------------------------
+# Variants of the forward (feature map, non-causal, normalised).
+#
+# The LinearAttentionCore code ("MiniMax-01与Lightning Attention", section
+# 2.2) applies a feature map phi (a linear layer and a ReLU; the learned layer
+# is not part of the operator, the ReLU is) to Q and K and computes the
+# non-causal phi(Q) (phi(K)^T V).  The kernel-approximation family it belongs
+# to ("从 Transformer 到 Lightning Attention，从 PPO 到 CISPO", the
+# "Transformers are RNNs" entry) divides each output by the same weights summed
+# without the values, phi(q_t) . sum_s phi(k_s); the teaching code of the
+# vergex page leaves that normalisation (and its stabilisation) out.  Reading
+# taken here: the denominator runs over the same tokens as the numerator, and
+# eps is added to it (eps = 0 divides exactly).
+# ---------------------------------------------------------------------------
+
+def variant(q, k, v, causal=True, relu=False, normalize=False, eps=0.0, s_in=None, z_in=None):
+    """Forward variants written from the N x N weight matrix.
+
+    phi = ReLU (relu=True) or the identity, applied to q and k.  With
+    W[t, s] = phi(q_t) . phi(k_s), kept for s <= t when causal:
+        numerator_t   = sum_s W[t, s] v_s + phi(q_t) . s_in
+        denominator_t = sum_s W[t, s]     + phi(q_t) . z_in
+        o_t = numerator_t                         (normalize=False)
+        o_t = numerator_t / (denominator_t + eps) (normalize=True)
+    Returns (o, S_out, z_out) with S_out = s_in + sum_s phi(k_s)^T v_s and
+    z_out = z_in + sum_s phi(k_s) per (batch, KV head); z_in is [B, Hkv, d].
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    s_in = None if s_in is None else _f64(s_in)
+    z_in = None if z_in is None else _f64(z_in)
+    B, Hq, Hkv, N, d, dv = _check(q, k, v, s_in)
+    if z_in is not None and z_in.shape != (B, Hkv, d):
+        raise ValueError("z_in must be [B, Hkv, d]")
+    if relu:
+        q, k = np.maximum(q, 0.0), np.maximum(k, 0.0)
+    keep = np.tril(np.ones((N, N))) if causal else np.ones((N, N))
+    o = np.zeros((B, Hq, N, dv))
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_group(h, Hq, Hkv)
+            W = (q[b, h] @ k[b, g].T) * keep                            # [t, s]
+            num = W @ v[b, g]
+            den = W.sum(axis=1)
+            if s_in is not None:
+                num = num + q[b, h] @ s_in[b, g]
+            if z_in is not None:
+                den = den + q[b, h] @ z_in[b, g]
+            o[b, h] = num / (den + eps)[:, None] if normalize else num
+    S = np.matmul(np.swapaxes(k, -1, -2), v)
+    if s_in is not None:
+        S = S + s_in
+    z = k.sum(axis=2)
+    if z_in is not None:
+        z = z + z_in
+    return o, S, z
 
 
 # ---------------------------------------------------------------------------
