@@ -152,6 +152,44 @@ la_status la_decode_step(float* S, const void* q, const void* k, const void* v, 
                          la_dtype in_dtype, la_dtype out_dtype, la_stream stream);
 
 /*
+ * Forward variants: feature map, non-causal form and normalisation.
+ *   fmap      LA_FMAP_IDENTITY (q, k used as given) or LA_FMAP_RELU: phi = ReLU
+ *             applied to q and k inside the kernels (the feature map of the
+ *             LinearAttentionCore code, page "MiniMax-01与Lightning Attention",
+ *             section 2.2, without its learned linear layer).
+ *   causal    1: o_t sums over s <= t, as la_forward_ex; 0: over every token
+ *             of the sequence (LinearAttentionCore: phi(Q) (phi(K)^T V)).
+ *   normalize 0: o_t = phi(q_t) . S_t.  1: o_t = phi(q_t) . S_t / (phi(q_t) . z_t + eps),
+ *             z_t = z_in + sum of phi(k_s) over the same tokens as S_t (the
+ *             kernel-approximation family cited on page "从 Transformer 到
+ *             Lightning Attention，从 PPO 到 CISPO", "Transformers are RNNs").
+ *             eps >= 0, finite.  A row whose denominator is 0 (eps = 0 and no
+ *             positive weight) comes out as the IEEE quotient (NaN or inf).
+ *   S_t       = s_in + sum of phi(k_s)^T v_s over the same tokens.
+ *   s_in, s_out   as la_forward_ex (s_out = s_in + sum over all tokens).
+ *   z_in, z_out   [B][Hkv][d] float32 normaliser sums, or NULL; only with
+ *                 normalize = 1 (LA_ERR_UNSUPPORTED otherwise).  z_out may
+ *                 equal z_in.
+ * in_dtype LA_BF16, d = dv = 128, block = 64, Hq / Hkv a multiple of 4.
+ * causal = 1, LA_FMAP_IDENTITY, normalize = 0 computes exactly la_forward_ex.
+ * Workspace: la_forward_variant_workspace_bytes (may be 0).
+ */
+typedef enum { LA_FMAP_IDENTITY = 0, LA_FMAP_RELU = 1 } la_feature_map;
+
+la_status la_forward_variant(const void* q, const void* k, const void* v, void* o,
+                             int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                             int64_t d, int64_t dv, int64_t block,
+                             la_dtype in_dtype, la_dtype out_dtype,
+                             int causal, la_feature_map fmap, int normalize, float eps,
+                             const float* s_in, float* s_out,
+                             const float* z_in, float* z_out,
+                             void* workspace, size_t workspace_bytes, la_stream stream);
+
+size_t la_forward_variant_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                                          int64_t d, int64_t dv, int64_t block,
+                                          la_dtype in_dtype, int causal, int normalize);
+
+/*
  * Backward pass of la_forward_ex: the gradients of a scalar loss L given
  * grad_o = dL/do and, optionally, grad_s_out = dL/ds_out.  The pages define
  * only the forward; differentiating its exact form (page

@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     backward_workspace_bytes,
     decode_step,
     forward,
+    forward_variant,
     load_library,
     status_str,
     workspace_bytes,

@@ -16,7 +16,9 @@ LA_OK = 0
 STATUS_NAMES = {0: "LA_OK", 1: "LA_ERR_NULL", 2: "LA_ERR_SHAPE", 3: "LA_ERR_UNSUPPORTED", 4: "LA_ERR_ALIGN",
                 5: "LA_ERR_ALIAS", 6: "LA_ERR_WORKSPACE", 7: "LA_ERR_HIP"}
 EXPORTS = ("la_forward", "la_forward_ex", "la_forward_states", "la_forward_outputs", "la_forward_workspace_bytes",
-           "la_backward", "la_backward_workspace_bytes", "la_decode_step", "la_status_str")
+           "la_forward_variant", "la_forward_variant_workspace_bytes", "la_backward", "la_backward_workspace_bytes",
+           "la_decode_step", "la_status_str")
+LA_FMAP_IDENTITY, LA_FMAP_RELU = 0, 1
 
 _lib = None
 
@@ -48,6 +50,12 @@ def load_library(path=LIB_PATH):
     lib.la_forward_outputs.restype = i32
     lib.la_forward_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, i64, i32]
     lib.la_forward_workspace_bytes.restype = sz
+    f32 = ctypes.c_float
+    lib.la_forward_variant.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i32, i32, i32, i32, i32,
+                                       f32, vp, vp, vp, vp, vp, sz, vp]
+    lib.la_forward_variant.restype = i32
+    lib.la_forward_variant_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, i64, i32, i32, i32]
+    lib.la_forward_variant_workspace_bytes.restype = sz
     lib.la_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i32, i32, vp, vp,
                                 vp, vp, sz, vp]
     lib.la_backward.restype = i32
@@ -157,6 +165,69 @@ def forward(q, k, v, block=64, out_dtype=None, s_in=None, return_state=False, ou
         raise LAError(st, "la_forward_ex")
     if return_state:
         return out, s_out
+    return out
+
+
+def forward_variant(q, k, v, causal=True, feature_map="identity", normalize=False, eps=0.0, block=64,
+                    out_dtype=None, s_in=None, z_in=None, return_state=False, out=None, s_out=None, z_out=None,
+                    workspace=None):
+    """Forward variants (la_forward_variant): feature map "identity" or "relu"
+    (phi = ReLU on q and k), causal or non-causal, optionally normalised by
+    phi(q_t) . z_t + eps.  bf16 q, k, v with d = dv = 128 and Hq/Hkv a
+    multiple of 4.  Returns o and, with return_state, (S_out, z_out) (z_out
+    None unless normalize)."""
+    torch = _torch()
+    lib = load_library()
+    _check_tensor("q", q, 4, None)
+    dev = q.device
+    _check_tensor("k", k, 4, dev)
+    _check_tensor("v", v, 4, dev)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    B, Hq, N, d = q.shape
+    Hkv, dv = k.shape[1], v.shape[3]
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != (B, Hkv, N, dv):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    fmaps = {"identity": LA_FMAP_IDENTITY, "relu": LA_FMAP_RELU}
+    if feature_map not in fmaps:
+        raise ValueError(f"feature_map must be one of {sorted(fmaps)}")
+    in_code = _dtype_code(q.dtype)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    out_code = _dtype_code(out_dtype)
+    for name, t, shape in (("s_in", s_in, (B, Hkv, d, dv)), ("z_in", z_in, (B, Hkv, d))):
+        if t is not None:
+            _check_tensor(name, t, len(shape), dev)
+            if t.dtype != torch.float32 or tuple(t.shape) != shape:
+                raise ValueError(f"{name} must be float32 {list(shape)}")
+    with torch.cuda.device(dev):
+        if out is None:
+            out = torch.empty((B, Hq, N, dv), dtype=out_dtype, device=dev)
+        _check_tensor("out", out, 4, dev)
+        if out.dtype != out_dtype or tuple(out.shape) != (B, Hq, N, dv):
+            raise ValueError("out has the wrong dtype or shape")
+        if return_state:
+            if s_out is None:
+                s_out = torch.empty((B, Hkv, d, dv), dtype=torch.float32, device=dev)
+            if normalize and z_out is None:
+                z_out = torch.empty((B, Hkv, d), dtype=torch.float32, device=dev)
+        for name, t, shape in (("s_out", s_out, (B, Hkv, d, dv)), ("z_out", z_out, (B, Hkv, d))):
+            if t is not None:
+                _check_tensor(name, t, len(shape), dev)
+                if t.dtype != torch.float32 or tuple(t.shape) != shape:
+                    raise ValueError(f"{name} must be float32 {list(shape)}")
+        ws_bytes = int(lib.la_forward_variant_workspace_bytes(B, Hq, Hkv, N, d, dv, block, in_code, int(causal),
+                                                              int(normalize)))
+        if ws_bytes > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.la_forward_variant(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, N, d, dv, block, in_code,
+                                    out_code, int(causal), fmaps[feature_map], int(normalize), float(eps),
+                                    _ptr(s_in), _ptr(s_out), _ptr(z_in), _ptr(z_out),
+                                    _ptr(workspace) if ws_bytes else None, ws_bytes, ctypes.c_void_p(stream))
+    if st != LA_OK:
+        raise LAError(st, "la_forward_variant")
+    if return_state:
+        return out, s_out, z_out
     return out
 
 

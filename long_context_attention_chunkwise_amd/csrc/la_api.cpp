@@ -96,6 +96,42 @@ Bf16Plan plan_bf16(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int
   return p;
 }
 
+VarPlan plan_variant(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv, int cus, bool causal,
+                     bool norm) {
+  VarPlan vp;
+  vp.causal = causal;
+  vp.norm = norm;
+  vp.base = plan_bf16(B, Hq, Hkv, N, d, dv, cus);
+  Bf16Plan& p = vp.base;
+  if (p.nblocks == 0) return vp;
+  const size_t chains = size_t(B * Hkv);
+  size_t Ppre = size_t(p.P);  // scanned entries per chain
+  if (!causal) {
+    // the pre-pass sums every segment; one part per segment when unsplit
+    if (p.P == 1) {
+      p.R = 1;
+      p.blocks_per_part = p.blocks_per_seg;
+    }
+    Ppre = size_t(p.P) + 1;
+    // output kernel: independent blocks, one workgroup per compute unit
+    const int64_t out_chains = B * Hkv * p.subgroups;
+    int64_t P = std::max<int64_t>(1, (cus + out_chains - 1) / out_chains);
+    P = std::min(P, p.nblocks);
+    vp.bps_out = (p.nblocks + P - 1) / P;
+    vp.P_out = static_cast<int>((p.nblocks + vp.bps_out - 1) / vp.bps_out);
+  } else if (!p.use_starts) {
+    return vp;  // one segment, one subgroup: s_in and z_in are read directly
+  }
+  vp.partial_floats = chains * (Ppre - 1) * size_t(p.R) * size_t(d * dv);
+  vp.start_floats = chains * Ppre * size_t(d * dv);
+  if (norm) {
+    vp.zpart_floats = chains * (Ppre - 1) * size_t(p.R) * size_t(d);
+    vp.zstart_floats = chains * Ppre * size_t(d);
+  }
+  vp.workspace_bytes = (vp.partial_floats + vp.start_floats + vp.zpart_floats + vp.zstart_floats) * sizeof(float);
+  return vp;
+}
+
 BwdPlan plan_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv, int cus) {
   BwdPlan p;
   // dQ is the forward over (dO, V, K): head sizes swap.
@@ -425,6 +461,95 @@ la_status la_backward(const void* q, const void* k, const void* v, const void* g
                         ws_kv, hs) != hipSuccess)
     return LA_ERR_HIP;
   return LA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+la_status check_variant_args(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv, int64_t block,
+                             la_dtype in_dtype, la_dtype out_dtype, int causal, int fmap, int normalize, float eps,
+                             const float* z_in, const float* z_out) {
+  la_status st = check_forward_shape(B, Hq, Hkv, N, d, dv, block, in_dtype, out_dtype);
+  if (st != LA_OK) return st;
+  if (in_dtype != LA_BF16 || (Hq / Hkv) % 4 != 0) return LA_ERR_UNSUPPORTED;
+  if ((causal != 0 && causal != 1) || (fmap != LA_FMAP_IDENTITY && fmap != LA_FMAP_RELU) ||
+      (normalize != 0 && normalize != 1))
+    return LA_ERR_UNSUPPORTED;
+  if (normalize) {
+    if (!(eps >= 0.0f) || eps > 3.0e38f) return LA_ERR_UNSUPPORTED;  // also rejects NaN
+  } else if (z_in != nullptr || z_out != nullptr) {
+    return LA_ERR_UNSUPPORTED;
+  }
+  return LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t la_forward_variant_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv,
+                                          int64_t block, la_dtype in_dtype, int causal, int normalize) {
+  if (check_variant_args(B, Hq, Hkv, N, d, dv, block, in_dtype, in_dtype, causal, LA_FMAP_IDENTITY, normalize, 0.0f,
+                         nullptr, nullptr) != LA_OK ||
+      N == 0)
+    return 0;
+  return la::plan_variant(B, Hq, Hkv, N, d, dv, device_cus(), causal != 0, normalize != 0).workspace_bytes;
+}
+
+la_status la_forward_variant(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t Hq,
+                             int64_t Hkv, int64_t N, int64_t d, int64_t dv, int64_t block, la_dtype in_dtype,
+                             la_dtype out_dtype, int causal, la_feature_map fmap, int normalize, float eps,
+                             const float* s_in, float* s_out, const float* z_in, float* z_out, void* workspace,
+                             size_t workspace_bytes, la_stream stream) {
+  la_status st = check_variant_args(B, Hq, Hkv, N, d, dv, block, in_dtype, out_dtype, causal, fmap, normalize, eps,
+                                    z_in, z_out);
+  if (st != LA_OK) return st;
+  if (N > 0 && (q == nullptr || k == nullptr || v == nullptr || o == nullptr)) return LA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(s_in) || !aligned16(s_out) ||
+      !aligned16(z_in) || !aligned16(z_out) || !aligned16(workspace))
+    return LA_ERR_ALIGN;
+  const size_t ei = esize(in_dtype), eo = esize(out_dtype);
+  const size_t nq = size_t(B * Hq * N * d) * ei, nk = size_t(B * Hkv * N * d) * ei;
+  const size_t nv = size_t(B * Hkv * N * dv) * ei, no = size_t(B * Hq * N * dv) * eo;
+  const size_t ns = size_t(B * Hkv * d * dv) * sizeof(float), nz = size_t(B * Hkv * d) * sizeof(float);
+  struct Range {
+    const void* p;
+    size_t n;
+  };
+  const Range inputs[] = {{q, nq}, {k, nk}, {v, nv}, {s_in, ns}, {z_in, nz}};
+  const Range outputs[] = {{o, no}, {s_out, ns}, {z_out, nz}};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 5; ++j) {
+      // s_out may be s_in itself and z_out z_in itself (in-place resume)
+      if ((i == 1 && j == 3 && s_out == s_in) || (i == 2 && j == 4 && z_out == z_in)) continue;
+      if (overlap(outputs[i].p, outputs[i].n, inputs[j].p, inputs[j].n)) return LA_ERR_ALIAS;
+    }
+    for (int j = 0; j < i; ++j)
+      if (overlap(outputs[i].p, outputs[i].n, outputs[j].p, outputs[j].n)) return LA_ERR_ALIAS;
+  }
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (N == 0) {
+    if (s_out != nullptr && s_out != s_in && la::launch_copy_or_zero(s_out, s_in, ns / sizeof(float), hs) != hipSuccess)
+      return LA_ERR_HIP;
+    if (z_out != nullptr && z_out != z_in && la::launch_copy_or_zero(z_out, z_in, nz / sizeof(float), hs) != hipSuccess)
+      return LA_ERR_HIP;
+    return LA_OK;
+  }
+  const la::VarPlan vp = la::plan_variant(B, Hq, Hkv, N, d, dv, device_cus(), causal != 0, normalize != 0);
+  const size_t nw = vp.workspace_bytes;
+  if (nw > 0) {
+    if (workspace == nullptr || workspace_bytes < nw) return LA_ERR_WORKSPACE;
+    for (const Range& r : inputs)
+      if (overlap(workspace, nw, r.p, r.n)) return LA_ERR_ALIAS;
+    for (const Range& r : outputs)
+      if (overlap(workspace, nw, r.p, r.n)) return LA_ERR_ALIAS;
+  }
+  return la::launch_variant(q, k, v, o, out_dtype == LA_F32, fmap == LA_FMAP_RELU, s_in, s_out, z_in, z_out, eps, B,
+                            Hq, Hkv, N, vp, workspace, hs) == hipSuccess
+             ? LA_OK
+             : LA_ERR_HIP;
 }
 
 }  // extern "C"

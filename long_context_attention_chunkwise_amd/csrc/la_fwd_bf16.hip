@@ -289,14 +289,26 @@ __device__ __forceinline__ void store_kv4(const KV4Regs& r, uint16_t* ks, uint16
 // the state are published, the inter term has finished reading the state,
 // and the state update has finished reading K/V.
 // ---------------------------------------------------------------------------
-template <bool OUT_F32>
+//
+// Feature-map variants (FL): kRelu applies phi = ReLU to the Q operands and
+// to K as it enters LDS.  kNorm divides each output row t by
+// phi(q_t) . z_t + eps, where z_t = z at the segment start + sum of phi(k_s)
+// over s <= t: the in-block part is the column sum of the float32 P^T tiles,
+// the earlier part phi(q_t) . z with z (float32, d entries) kept like the
+// state: wave w accumulates entries [32w, 32w+32) on the matrix cores (K^T
+// times a ones operand) and publishes them in LDS once per block.
+template <bool OUT_F32, int FL>
 __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     void* __restrict__ o, const float* starts, const float* s_in, float* s_out, int Hq, int Hkv, int subgroups,
-    int64_t N, int64_t nblocks, int64_t blocks_per_seg, int P) {
+    int64_t N, int64_t nblocks, int64_t blocks_per_seg, int P, const float* zstarts, const float* z_in,
+    float* z_out, float eps) {
+  constexpr bool kN = (FL & kNorm) != 0;
+  constexpr bool kR = (FL & kRelu) != 0;
   __shared__ __align__(16) uint16_t ks[C * ROWKV];
   __shared__ __align__(16) uint16_t vs[C * ROWKV];
   __shared__ __align__(16) uint16_t st[DV * ROWST];
+  __shared__ __align__(16) float zs[kN ? D : 4];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
@@ -327,6 +339,18 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
       *reinterpret_cast<bf16x4*>(&st[(32 * w + 16 * jn + l16) * ROWST + 16 * dt + 4 * grp]) =
           to_bf16x4(sacc[jn][dt]);
 
+  // normaliser sums, entries 32w + 16jj + 4grp + i (every column equal)
+  floatx4 zacc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+  if constexpr (kN) {
+    const float* z0 = zstarts ? zstarts + (int64_t(bg) * P + seg) * D : (z_in ? z_in + int64_t(bg) * D : nullptr);
+    if (z0 != nullptr)
+      for (int jj = 0; jj < 2; ++jj)
+        for (int i = 0; i < 4; ++i) zacc[jj][i] = z0[32 * w + 16 * jj + 4 * grp + i];
+    if (l16 == 0)
+      for (int jj = 0; jj < 2; ++jj)
+        *reinterpret_cast<floatx4*>(&zs[32 * w + 16 * jj + 4 * grp]) = zacc[jj];
+  }
+
   bf16x8 qa[4][4];
   KV4Regs kv;
   auto load_block = [&](int64_t blk) {
@@ -339,12 +363,20 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
   };
   if (blk0 < blk1) load_block(blk0);
   for (int64_t blk = blk0; blk < blk1; ++blk) {
+    if constexpr (kR) {
+      for (int i = 0; i < 4; ++i) kv.k[i] = relu_bf16x8(kv.k[i]);
+      for (int ti = 0; ti < 4; ++ti)
+        for (int ds = 0; ds < 4; ++ds) qa[ti][ds] = relu_bf16x8(qa[ti][ds]);
+    }
     store_kv4(kv, ks, vs, tid);
     __syncthreads();  // K, V and the state of the previous block are in LDS
 
     // scores, one P^T tile at a time, packed to bf16 operands right away
     const floatx4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
     bf16x8 pop[4][2];
+    float den[4], inv[4];  // normaliser of row 16ti + l16 (kNorm only)
+    (void)den;
+    (void)inv;
     for (int ti = 0; ti < 4; ++ti) {
       floatx4 pt[4];
       for (int si = 0; si <= ti; ++si) {
@@ -353,8 +385,33 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
           pt[si] = mfma(ld_lds16(ks + (16 * si + l16) * ROWKV + 32 * ds + 8 * grp), qa[ti][ds], pt[si]);
       }
       pt[ti] = causal_mask(pt[ti], l16, grp);
+      if constexpr (kN) {
+        // this lane's share of sum_s P^T[s][t] for t = 16ti + l16
+        float sum = 0.0f;
+        for (int si = 0; si <= ti; ++si) sum += (pt[si][0] + pt[si][1]) + (pt[si][2] + pt[si][3]);
+        den[ti] = sum;
+      }
       pop[ti][0] = pack_tiles(pt[0], ti >= 1 ? pt[1] : z4);
       if (ti >= 2) pop[ti][1] = pack_tiles(pt[2], ti == 3 ? pt[3] : z4);
+    }
+    if constexpr (kN) {
+      // earlier tokens: phi(q_t) . z; lane (l16, grp) holds q_t entries 32ds + 8grp + j
+      for (int ds = 0; ds < 4; ++ds) {
+        const floatx4 za = *reinterpret_cast<const floatx4*>(&zs[32 * ds + 8 * grp]);
+        const floatx4 zb = *reinterpret_cast<const floatx4*>(&zs[32 * ds + 8 * grp + 4]);
+        for (int ti = 0; ti < 4; ++ti) {
+          float dsum = 0.0f;
+          for (int j = 0; j < 4; ++j)
+            dsum += float(qa[ti][ds][j]) * za[j] + float(qa[ti][ds][j + 4]) * zb[j];
+          den[ti] += dsum;
+        }
+      }
+      for (int ti = 0; ti < 4; ++ti) {
+        float x = den[ti];
+        x += __shfl_xor(x, 16);
+        x += __shfl_xor(x, 32);
+        inv[ti] = 1.0f / (x + eps);
+      }
     }
 
     // Output columns in quarters of 32 (one interleaved column pair m), so
@@ -377,6 +434,10 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
         acc[h2][2] = mfma(va1, pop[2][1], acc[h2][2]);
         acc[h2][3] = mfma(va1, pop[3][1], acc[h2][3]);
       }
+      if constexpr (kN)
+        for (int h2 = 0; h2 < 2; ++h2)
+          for (int ti = 0; ti < 4; ++ti)
+            for (int i = 0; i < 4; ++i) acc[h2][ti][i] *= inv[ti];
       for (int ti = 0; ti < 4; ++ti) {
         const int64_t t = blk * C + 16 * ti + l16;
         if (t < N) {
@@ -411,6 +472,14 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
         for (int dt = 0; dt < 8; ++dt)
           *reinterpret_cast<bf16x4*>(&st[(32 * w + 16 * jn + l16) * ROWST + 16 * dt + 4 * grp]) =
               to_bf16x4(sacc[jn][dt]);
+      if constexpr (kN) {
+        for (int p = 0; p < 2; ++p)
+          for (int jj = 0; jj < 2; ++jj)
+            zacc[jj] = mfma(tr_operand(ks, p, 32 * w + 16 * jj, l16, grp), ones_bf16x8(), zacc[jj]);
+        if (l16 == 0)
+          for (int jj = 0; jj < 2; ++jj)
+            *reinterpret_cast<floatx4*>(&zs[32 * w + 16 * jj + 4 * grp]) = zacc[jj];
+      }
     }
     __syncthreads();  // K and V are free for the next block
   }
@@ -421,6 +490,10 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
       for (int dt = 0; dt < 8; ++dt)
         for (int i = 0; i < 4; ++i) so[(16 * dt + 4 * grp + i) * DV + 32 * w + 16 * jn + l16] = sacc[jn][dt][i];
   }
+  if constexpr (kN)
+    if (z_out != nullptr && seg == P - 1 && sub == 0 && l16 == 0)
+      for (int jj = 0; jj < 2; ++jj)
+        for (int i = 0; i < 4; ++i) z_out[int64_t(bg) * D + 32 * w + 16 * jj + 4 * grp + i] = zacc[jj][i];
 }
 
 // Pre-pass: partial[c][j][r] = sum of K_b^T V_b over part r of segment
@@ -430,9 +503,16 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
 // columns [32w, 32w+32).  A pure HBM stream: the K/V tile is single-buffered
 // in LDS (36 KiB) so three workgroups share a CU, each with the next block's
 // loads in flight while it multiplies the current one.
+//
+// Flags (feature-map variants): kRelu applies phi = ReLU to k as it enters
+// LDS; kNorm also writes zpart[c][j][r] = sum of phi(k_b) over the part
+// (wave w: entries [32w, 32w+32), as K^T times a ones operand on the matrix
+// cores).
+template <int FL>
 __global__ __launch_bounds__(kPartThreads, 3) void state_parts(const uint16_t* __restrict__ k,
                                                            const uint16_t* __restrict__ v,
-                                                           float* __restrict__ partial, int64_t N,
+                                                           float* __restrict__ partial,
+                                                           float* __restrict__ zpart, int64_t N,
                                                            int64_t nblocks, int64_t blocks_per_seg,
                                                            int64_t blocks_per_part, int P, int R,
                                                            int seg_offset) {
@@ -458,6 +538,7 @@ __global__ __launch_bounds__(kPartThreads, 3) void state_parts(const uint16_t* _
   floatx4 acc[2][8];
   for (int jn = 0; jn < 2; ++jn)
     for (int dt = 0; dt < 8; ++dt) acc[jn][dt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  floatx4 zacc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 
   const int ch = tid & 15;
   auto load = [&](int64_t blk, uint4 (&kr)[4], uint4 (&vr)[4]) {
@@ -475,7 +556,7 @@ __global__ __launch_bounds__(kPartThreads, 3) void state_parts(const uint16_t* _
   auto store = [&](const uint4 (&kr)[4], const uint4 (&vr)[4]) {
     for (int i = 0; i < 4; ++i) {
       const int row = (tid >> 4) + 16 * i;
-      *reinterpret_cast<uint4*>(&ksm[row * ROWKV + 8 * ch]) = kr[i];
+      *reinterpret_cast<uint4*>(&ksm[row * ROWKV + 8 * ch]) = (FL & kRelu) ? relu_bf16x8(kr[i]) : kr[i];
       *reinterpret_cast<uint4*>(&vsm[row * ROWKV + 8 * ch]) = vr[i];
     }
   };
@@ -494,8 +575,18 @@ __global__ __launch_bounds__(kPartThreads, 3) void state_parts(const uint16_t* _
         acc[0][dt] = mfma(ka, vb0, acc[0][dt]);
         acc[1][dt] = mfma(ka, vb1, acc[1][dt]);
       }
+      if constexpr ((FL & kNorm) != 0)
+        for (int jj = 0; jj < 2; ++jj)
+          zacc[jj] = mfma(tr_operand(ksm, p, 32 * w + 16 * jj, l16, grp), ones_bf16x8(), zacc[jj]);
     }
     __syncthreads();  // every wave is done with this block's K and V
+  }
+  if constexpr ((FL & kNorm) != 0) {
+    // every column of the ones product holds the sum; lanes of column 0 write it
+    float* zo = zpart + ((int64_t(c) * (P - 1) + j) * R + r) * D;
+    if (l16 == 0)
+      for (int jj = 0; jj < 2; ++jj)
+        for (int i = 0; i < 4; ++i) zo[32 * w + 16 * jj + 4 * grp + i] = zacc[jj][i];
   }
 
   float* out = partial + ((int64_t(c) * (P - 1) + j) * R + r) * (D * DV);
@@ -505,28 +596,151 @@ __global__ __launch_bounds__(kPartThreads, 3) void state_parts(const uint16_t* _
 }
 
 // starts[c][j] = s_in[c] + sum over segments i < j and parts r of partial[c][i][r],
-// accumulated in that fixed order.
+// accumulated in that fixed order; E elements per chain (d*dv for the state,
+// d for the normaliser sums), `total` threads.
 __global__ __launch_bounds__(256) void scan_starts(const float* __restrict__ partial, float* __restrict__ starts,
-                                                   const float* s_in, int P, int R) {
-  constexpr int DD = D * DV;
+                                                   const float* s_in, int P, int R, int E, int64_t total) {
   const int64_t gid = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t c = gid / DD;
-  const int e = int(gid % DD);
-  float run = s_in ? s_in[c * DD + e] : 0.0f;
+  if (gid >= total) return;
+  const int64_t c = gid / E;
+  const int e = int(gid % E);
+  float run = s_in ? s_in[c * E + e] : 0.0f;
   for (int j = 0; j < P; ++j) {
-    starts[(c * P + j) * DD + e] = run;
+    starts[(c * P + j) * E + e] = run;
     if (j < P - 1)
-      for (int r = 0; r < R; ++r) run += partial[((c * (P - 1) + j) * R + r) * DD + e];
+      for (int r = 0; r < R; ++r) run += partial[((c * (P - 1) + j) * R + r) * E + e];
   }
 }
 
-template <bool OUT_F32>
+// ---------------------------------------------------------------------------
+// Non-causal variant (LinearAttentionCore of page "MiniMax-01与Lightning
+// Attention", section 2.2): o_t = phi(q_t) . S_tot for every t, with S_tot =
+// s_in + sum over all tokens of phi(k_s)^T v_s, optionally divided by
+// phi(q_t) . z_tot + eps.  With the state fixed every block is independent:
+// a streaming product Q S_tot per query head (read q, write o) with no
+// barrier in the loop; the next block's Q operands load while the current
+// block multiplies.  Grid: B * Hkv * (G/4) * P workgroups of four waves, wave
+// h serving query head h of its group of four.  S_tot comes in float32 from
+// the pre-pass and is rounded once to the bf16 n-major LDS layout of the
+// causal kernel's state copy.
+// ---------------------------------------------------------------------------
+template <bool OUT_F32, int FL>
+__global__ __launch_bounds__(256, 1) void fwd_noncausal_g4(
+    const uint16_t* __restrict__ q, void* __restrict__ o, const float* __restrict__ stot,
+    const float* __restrict__ ztot, int64_t tot_stride, float* s_out, float* z_out, int Hq, int Hkv,
+    int subgroups, int64_t N, int64_t nblocks, int64_t blocks_per_seg, int P, float eps) {
+  constexpr bool kN = (FL & kNorm) != 0;
+  constexpr bool kR = (FL & kRelu) != 0;
+  __shared__ __align__(16) uint16_t st[DV * ROWST];
+  __shared__ __align__(16) float zs[kN ? D : 4];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+  const int seg = blockIdx.x % P;
+  const int chain = blockIdx.x / P;
+  const int sub = chain % subgroups;
+  const int bg = chain / subgroups;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int G = Hq / Hkv;
+  const int64_t blk0 = int64_t(seg) * blocks_per_seg;
+  const int64_t blk1 = blk0 + blocks_per_seg < nblocks ? blk0 + blocks_per_seg : nblocks;
+  const int64_t head = int64_t(b) * Hq + int64_t(g) * G + int64_t(sub) * 4 + w;
+  const uint16_t* qh = q + head * N * D;
+  const int nlane = 8 * (l16 >> 2) + (l16 & 3);
+
+  const float* S = stot + int64_t(bg) * tot_stride * (D * DV);
+  for (int jn = 0; jn < 2; ++jn)
+    for (int dt = 0; dt < 8; ++dt) {
+      floatx4 x;
+      for (int i = 0; i < 4; ++i) x[i] = S[(16 * dt + 4 * grp + i) * DV + 32 * w + 16 * jn + l16];
+      *reinterpret_cast<bf16x4*>(&st[(32 * w + 16 * jn + l16) * ROWST + 16 * dt + 4 * grp]) = to_bf16x4(x);
+      if (s_out != nullptr && seg == 0 && sub == 0)
+        for (int i = 0; i < 4; ++i)
+          s_out[int64_t(bg) * (D * DV) + (16 * dt + 4 * grp + i) * DV + 32 * w + 16 * jn + l16] = x[i];
+    }
+  if constexpr (kN) {
+    const float* Z = ztot + int64_t(bg) * tot_stride * D;
+    if (tid < D) {
+      zs[tid] = Z[tid];
+      if (z_out != nullptr && seg == 0 && sub == 0) z_out[int64_t(bg) * D + tid] = Z[tid];
+    }
+  }
+  __syncthreads();  // S_tot (and z_tot) are in LDS
+
+  auto load_q = [&](bf16x8 (&qa)[4][4], int64_t blk) {
+    for (int ti = 0; ti < 4; ++ti) {
+      const int64_t t = blk * C + 16 * ti + l16;
+      for (int ds = 0; ds < 4; ++ds)
+        qa[ti][ds] = (t < N) ? ld_global16(qh + t * D + 32 * ds + 8 * grp) : zero_bf16x8();
+    }
+  };
+  bf16x8 qa[4][4], qn[4][4];
+  if (blk0 < blk1) load_q(qa, blk0);
+  const floatx4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int64_t blk = blk0; blk < blk1; ++blk) {
+    if (blk + 1 < blk1) load_q(qn, blk + 1);
+    if constexpr (kR)
+      for (int ti = 0; ti < 4; ++ti)
+        for (int ds = 0; ds < 4; ++ds) qa[ti][ds] = relu_bf16x8(qa[ti][ds]);
+    float inv[4];
+    (void)inv;
+    if constexpr (kN) {
+      float den[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int ds = 0; ds < 4; ++ds) {
+        const floatx4 za = *reinterpret_cast<const floatx4*>(&zs[32 * ds + 8 * grp]);
+        const floatx4 zb = *reinterpret_cast<const floatx4*>(&zs[32 * ds + 8 * grp + 4]);
+        for (int ti = 0; ti < 4; ++ti)
+          for (int j = 0; j < 4; ++j)
+            den[ti] += float(qa[ti][ds][j]) * za[j] + float(qa[ti][ds][j + 4]) * zb[j];
+      }
+      for (int ti = 0; ti < 4; ++ti) {
+        float x = den[ti];
+        x += __shfl_xor(x, 16);
+        x += __shfl_xor(x, 32);
+        inv[ti] = 1.0f / (x + eps);
+      }
+    }
+    for (int m = 0; m < 4; ++m) {
+      floatx4 acc[2][4];
+      for (int h2 = 0; h2 < 2; ++h2)
+        for (int ti = 0; ti < 4; ++ti) acc[h2][ti] = z4;
+      for (int ds = 0; ds < 4; ++ds)
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const bf16x8 sa = ld_lds16(st + (32 * m + 4 * h2 + nlane) * ROWST + 32 * ds + 8 * grp);
+          for (int ti = 0; ti < 4; ++ti) acc[h2][ti] = mfma(sa, qa[ti][ds], acc[h2][ti]);
+        }
+      if constexpr (kN)
+        for (int h2 = 0; h2 < 2; ++h2)
+          for (int ti = 0; ti < 4; ++ti)
+            for (int i = 0; i < 4; ++i) acc[h2][ti][i] *= inv[ti];
+      for (int ti = 0; ti < 4; ++ti) {
+        const int64_t t = blk * C + 16 * ti + l16;
+        if (t < N) {
+          const int64_t off = (head * N + t) * DV + 32 * m + 8 * grp;
+          if (OUT_F32) {
+            float* op = static_cast<float*>(o) + off;
+            *reinterpret_cast<floatx4*>(op) = acc[0][ti];
+            *reinterpret_cast<floatx4*>(op + 4) = acc[1][ti];
+          } else {
+            *reinterpret_cast<bf16x8*>(static_cast<uint16_t*>(o) + off) = pack_tiles(acc[0][ti], acc[1][ti]);
+          }
+        }
+      }
+    }
+    for (int ti = 0; ti < 4; ++ti)
+      for (int ds = 0; ds < 4; ++ds) qa[ti][ds] = qn[ti][ds];
+  }
+}
+
+template <bool OUT_F32, int FL = 0>
 void launch_g4(dim3 grid, hipStream_t stream, const void* q, const void* k, const void* v, void* o,
                const float* starts, const float* s_in, float* s_out, int Hq, int Hkv, int subgroups, int64_t N,
-               int64_t nblocks, int64_t bps, int P) {
-  hipLaunchKernelGGL((fwd_bf16_g4<OUT_F32>), grid, dim3(256), 0, stream, static_cast<const uint16_t*>(q),
+               int64_t nblocks, int64_t bps, int P, const float* zstarts = nullptr, const float* z_in = nullptr,
+               float* z_out = nullptr, float eps = 0.0f) {
+  hipLaunchKernelGGL((fwd_bf16_g4<OUT_F32, FL>), grid, dim3(256), 0, stream, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), o, starts, s_in, s_out, Hq,
-                     Hkv, subgroups, N, nblocks, bps, P);
+                     Hkv, subgroups, N, nblocks, bps, P, zstarts, z_in, z_out, eps);
 }
 
 template <int GW, bool OUT_F32>
@@ -547,24 +761,111 @@ hipError_t launch_segment_states(const void* k, const void* v, const float* s_in
   float* partial = static_cast<float*>(workspace);
   float* starts = partial + plan.partial_floats;
   if (plan.P > 1) {
-    hipLaunchKernelGGL(state_parts, dim3(unsigned(kv_chains * (plan.P - 1) * plan.R)), dim3(kPartThreads), 0,
-                       stream, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), partial, N,
-                       plan.nblocks, plan.blocks_per_seg, plan.blocks_per_part, plan.P, plan.R, 0);
+    hipLaunchKernelGGL(state_parts<0>, dim3(unsigned(kv_chains * (plan.P - 1) * plan.R)), dim3(kPartThreads), 0,
+                       stream, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), partial, nullptr,
+                       N, plan.nblocks, plan.blocks_per_seg, plan.blocks_per_part, plan.P, plan.R, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(scan_starts, dim3(unsigned(kv_chains * D * DV / 256)), dim3(256), 0, stream, partial, starts,
-                     s_in, plan.P, plan.R);
+  const int64_t total = kv_chains * D * DV;
+  hipLaunchKernelGGL(scan_starts, dim3(unsigned((total + 255) / 256)), dim3(256), 0, stream, partial, starts, s_in,
+                     plan.P, plan.R, D * DV, total);
   return hipGetLastError();
 }
 
 hipError_t launch_state_parts(const void* a, const void* b, float* partial, int64_t chains, int64_t N,
                               int64_t nblocks, int64_t blocks_per_seg, int64_t blocks_per_part, int P, int R,
                               int seg_offset, hipStream_t stream) {
-  hipLaunchKernelGGL(state_parts, dim3(unsigned(chains * (P - 1) * R)), dim3(kPartThreads), 0, stream,
-                     static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), partial, N, nblocks,
-                     blocks_per_seg, blocks_per_part, P, R, seg_offset);
+  hipLaunchKernelGGL(state_parts<0>, dim3(unsigned(chains * (P - 1) * R)), dim3(kPartThreads), 0, stream,
+                     static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), partial, nullptr, N,
+                     nblocks, blocks_per_seg, blocks_per_part, P, R, seg_offset);
   return hipGetLastError();
+}
+
+namespace {
+
+template <int FL>
+hipError_t variant_states(const void* k, const void* v, const float* s_in, const float* z_in, int64_t kv_chains,
+                          int64_t N, const VarPlan& vp, float* ws, hipStream_t stream) {
+  // Segment starts (causal) or the totals (non-causal: the scan over Ppre + 1
+  // entries ends with the sum over every segment).
+  const Bf16Plan& p = vp.base;
+  const int Ppre = vp.causal ? p.P : p.P + 1;
+  float* partial = ws;
+  float* starts = partial + vp.partial_floats;
+  float* zpart = starts + vp.start_floats;
+  float* zstarts = zpart + vp.zpart_floats;
+  if (Ppre > 1) {
+    hipLaunchKernelGGL(state_parts<FL>, dim3(unsigned(kv_chains * (Ppre - 1) * p.R)), dim3(kPartThreads), 0,
+                       stream, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), partial, zpart, N,
+                       p.nblocks, p.blocks_per_seg, p.blocks_per_part, Ppre, p.R, 0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t total = kv_chains * D * DV;
+  hipLaunchKernelGGL(scan_starts, dim3(unsigned((total + 255) / 256)), dim3(256), 0, stream, partial, starts, s_in,
+                     Ppre, p.R, D * DV, total);
+  if ((FL & kNorm) != 0) {
+    const int64_t zt = kv_chains * D;
+    hipLaunchKernelGGL(scan_starts, dim3(unsigned((zt + 255) / 256)), dim3(256), 0, stream, zpart, zstarts, z_in,
+                       Ppre, p.R, D, zt);
+  }
+  return hipGetLastError();
+}
+
+template <bool OUT_F32, int FL>
+hipError_t variant_outputs(const void* q, const void* k, const void* v, void* o, const float* s_in, float* s_out,
+                           const float* z_in, float* z_out, float eps, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                           const VarPlan& vp, float* ws, hipStream_t stream) {
+  const Bf16Plan& p = vp.base;
+  const float* starts = ws + vp.partial_floats;
+  const float* zstarts = starts + vp.start_floats + vp.zpart_floats;
+  const int iHq = int(Hq), iHkv = int(Hkv);
+  if (vp.causal) {
+    const dim3 grid(unsigned(B * Hkv * p.subgroups * p.P));
+    const bool st = p.use_starts;
+    launch_g4<OUT_F32, FL>(grid, stream, q, k, v, o, st ? starts : nullptr, st ? nullptr : s_in, s_out, iHq, iHkv,
+                           p.subgroups, N, p.nblocks, p.blocks_per_seg, p.P,
+                           (FL & kNorm) && st ? zstarts : nullptr, (FL & kNorm) && !st ? z_in : nullptr, z_out, eps);
+  } else {
+    // totals sit at entry P of each chain's P + 1 scanned entries
+    const int64_t stride = p.P + 1;
+    const dim3 grid(unsigned(B * Hkv * p.subgroups * vp.P_out));
+    hipLaunchKernelGGL((fwd_noncausal_g4<OUT_F32, FL>), grid, dim3(256), 0, stream, static_cast<const uint16_t*>(q),
+                       o, starts + p.P * (D * DV), zstarts + p.P * D, stride, s_out, z_out, iHq, iHkv, p.subgroups,
+                       N, p.nblocks, vp.bps_out, vp.P_out, eps);
+  }
+  return hipGetLastError();
+}
+
+template <int FL>
+hipError_t variant_run(const void* q, const void* k, const void* v, void* o, bool out_f32, const float* s_in,
+                       float* s_out, const float* z_in, float* z_out, float eps, int64_t B, int64_t Hq, int64_t Hkv,
+                       int64_t N, const VarPlan& vp, float* ws, hipStream_t stream) {
+  if (!vp.causal || vp.base.use_starts) {
+    hipError_t e = variant_states<FL>(k, v, s_in, z_in, B * Hkv, N, vp, ws, stream);
+    if (e != hipSuccess) return e;
+  }
+  return out_f32 ? variant_outputs<true, FL>(q, k, v, o, s_in, s_out, z_in, z_out, eps, B, Hq, Hkv, N, vp, ws, stream)
+                 : variant_outputs<false, FL>(q, k, v, o, s_in, s_out, z_in, z_out, eps, B, Hq, Hkv, N, vp, ws,
+                                              stream);
+}
+
+}  // namespace
+
+hipError_t launch_variant(const void* q, const void* k, const void* v, void* o, bool out_f32, bool relu,
+                          const float* s_in, float* s_out, const float* z_in, float* z_out, float eps, int64_t B,
+                          int64_t Hq, int64_t Hkv, int64_t N, const VarPlan& vp, void* workspace,
+                          hipStream_t stream) {
+  float* ws = static_cast<float*>(workspace);
+  if (vp.norm)
+    return relu ? variant_run<kRelu | kNorm>(q, k, v, o, out_f32, s_in, s_out, z_in, z_out, eps, B, Hq, Hkv, N, vp,
+                                             ws, stream)
+                : variant_run<kNorm>(q, k, v, o, out_f32, s_in, s_out, z_in, z_out, eps, B, Hq, Hkv, N, vp, ws,
+                                     stream);
+  return relu ? variant_run<kRelu>(q, k, v, o, out_f32, s_in, s_out, z_in, z_out, eps, B, Hq, Hkv, N, vp, ws,
+                                   stream)
+              : variant_run<0>(q, k, v, o, out_f32, s_in, s_out, z_in, z_out, eps, B, Hq, Hkv, N, vp, ws, stream);
 }
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, bool out_f32, const float* s_in,

@@ -55,6 +55,32 @@ hipError_t launch_state_parts(const void* a, const void* b, float* partial, int6
                               int64_t nblocks, int64_t blocks_per_seg, int64_t blocks_per_part, int P, int R,
                               int seg_offset, hipStream_t stream);
 
+// Forward variants (feature map, non-causal, normalised), bf16 inputs and
+// groups of four query heads.  Causal: the forward's split, with the
+// normaliser sums carried beside the state.  Non-causal: the pre-pass sums
+// every segment (the scan's last entry is the total) and the output kernel
+// splits each chain into P_out segments of bps_out blocks.
+struct VarPlan {
+  Bf16Plan base;
+  bool causal = true;
+  bool norm = false;
+  int P_out = 1;
+  int64_t bps_out = 0;
+  size_t partial_floats = 0;    // B*Hkv*(Ppre-1)*R*d*dv
+  size_t start_floats = 0;      // B*Hkv*Ppre*d*dv
+  size_t zpart_floats = 0;      // B*Hkv*(Ppre-1)*R*d      (norm)
+  size_t zstart_floats = 0;     // B*Hkv*Ppre*d            (norm)
+  size_t workspace_bytes = 0;   // all four, in that order
+};
+
+VarPlan plan_variant(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv, int cus, bool causal,
+                     bool norm);
+
+hipError_t launch_variant(const void* q, const void* k, const void* v, void* o, bool out_f32, bool relu,
+                          const float* s_in, float* s_out, const float* z_in, float* z_out, float eps, int64_t B,
+                          int64_t Hq, int64_t Hkv, int64_t N, const VarPlan& plan, void* workspace,
+                          hipStream_t stream);
+
 // Backward work split: dK/dV walk each chain's segments from the end; segment
 // j starts from the sum of q^T dO over later segments and the group's heads.
 struct BwdPlan {

@@ -103,6 +103,32 @@ __device__ __forceinline__ bf16x8 pack_tiles(floatx4 lo, floatx4 hi) {
   return r;
 }
 
+// Feature-map variants (flags of the forward kernels).
+constexpr int kRelu = 1;  // phi = ReLU on q and k
+constexpr int kNorm = 2;  // outputs divided by phi(q) . z + eps
+
+typedef short short8v __attribute__((ext_vector_type(8)));
+
+// ReLU of eight bf16 values.  A bf16 bit pattern read as int16 is negative
+// exactly when its sign bit is set, so max(x, 0) over int16 lanes keeps
+// non-negative values and turns negative ones (and -0) into +0: one packed
+// 16-bit integer max per register.
+__device__ __forceinline__ bf16x8 relu_bf16x8(bf16x8 x) {
+  const short8v zero = {0, 0, 0, 0, 0, 0, 0, 0};
+  return __builtin_bit_cast(bf16x8, __builtin_elementwise_max(__builtin_bit_cast(short8v, x), zero));
+}
+
+__device__ __forceinline__ uint4 relu_bf16x8(uint4 x) {
+  const short8v zero = {0, 0, 0, 0, 0, 0, 0, 0};
+  return __builtin_bit_cast(uint4, __builtin_elementwise_max(__builtin_bit_cast(short8v, x), zero));
+}
+
+__device__ __forceinline__ bf16x8 ones_bf16x8() {
+  bf16x8 r;
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)1.0f;
+  return r;
+}
+
 // Zero the entries of a diagonal P^T tile above the causal boundary: entry
 // (s = 4grp + i, t = l16) within the tile is kept when s <= t.
 __device__ __forceinline__ floatx4 causal_mask(floatx4 x, int l16, int grp) {

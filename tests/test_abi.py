@@ -108,6 +108,29 @@ def test_backward_validation(lib):
     assert bwd(lib, ws=ctypes.c_void_p(GB * 10 + 256)) == ALIAS       # workspace inside dk
 
 
+def var(lib, q=Q, k=K, v=V, o=O, B=1, Hq=4, Hkv=1, N=1000, d=128, dv=128, block=64, i=BF16, out=BF16, causal=1,
+        fmap=1, norm=1, eps=1e-6, s_in=None, s_out=None, z_in=None, z_out=None, ws=WS, ws_bytes=1 << 32):
+    return lib.la_forward_variant(q, k, v, o, B, Hq, Hkv, N, d, dv, block, i, out, causal, fmap, norm, eps, s_in,
+                                  s_out, z_in, z_out, ws, ws_bytes, None)
+
+
+def test_variant_validation(lib):
+    assert var(lib, q=None) == NULL
+    assert var(lib, Hq=6, Hkv=4) == SHAPE
+    assert var(lib, Hq=2, Hkv=1) == UNSUP                 # groups of four query heads only
+    assert var(lib, i=F32, out=F32) == UNSUP              # bf16 inputs only
+    assert var(lib, fmap=2) == UNSUP
+    assert var(lib, causal=2) == UNSUP
+    assert var(lib, eps=-1.0) == UNSUP
+    assert var(lib, eps=float("nan")) == UNSUP
+    assert var(lib, norm=0, z_out=DS) == UNSUP            # normaliser sums only when normalising
+    assert var(lib, z_out=ctypes.c_void_p(GB * 12 + 4)) == ALIGN
+    assert var(lib, z_out=ctypes.c_void_p(GB * 3 + 512)) == ALIAS    # z_out inside v
+    assert var(lib, s_out=ctypes.c_void_p(GB * 4 + 64)) == ALIAS     # s_out inside o
+    assert var(lib, ws=None) == WORKSPACE
+    assert var(lib, ws=ctypes.c_void_p(GB * 1 + 256)) == ALIAS       # workspace inside q
+
+
 def test_workspace_plan(lib):
     # Host planning with the default 256 compute units (no device here): the
     # 1M-token GQA problem splits each of the 32 chains into 8 segments and
@@ -128,6 +151,16 @@ def test_workspace_plan(lib):
     assert n == ((32 * 7 * 3 + 32 * 8) + 32 + 128 * 7 * 6 + 32 * 8) * 128 * 128 * 4
     assert lib.la_backward_workspace_bytes(1, 128, 32, 0, 128, 128, 64, BF16) == 0
     assert lib.la_backward_workspace_bytes(1, 4, 2, 64, 128, 128, 64, F32) == 0
+    # Variants at 1M tokens: causal = the forward's split (+ normaliser sums);
+    # non-causal sums all 8 segments of each chain (3 parts each) and scans
+    # 9 entries, the last being the total.
+    DD, d = 128 * 128, 128
+    causal = lib.la_forward_variant_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, 64, BF16, 1, 1)
+    assert causal == ((32 * 7 * 3 + 32 * 8) * DD + (32 * 7 * 3 + 32 * 8) * d) * 4
+    nonc = lib.la_forward_variant_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, 64, BF16, 0, 0)
+    assert nonc == (32 * 8 * 3 + 32 * 9) * DD * 4
+    assert lib.la_forward_variant_workspace_bytes(1, 8, 2, 256, 128, 128, 64, BF16, 0, 1) > 0  # one segment still sums
+    assert lib.la_forward_variant_workspace_bytes(1, 2, 1, 256, 128, 128, 64, BF16, 1, 0) == 0  # unsupported -> 0
 
 
 def test_binding_requires_gpu_tensors():

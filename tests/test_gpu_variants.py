@@ -1,0 +1,126 @@
+"""GPU parity of la_forward_variant (ReLU feature map, non-causal,
+normalised) against the fp64 oracle's `variant`.
+
+Tolerance: the forward's bar (2e-2 of the output RMS, + 2^-8|ref| for bf16
+output), except that normalised outputs, weighted averages of value rows
+whose RMS shrinks as the averages widen, measure it in units of RMS(v).
+
+Inputs are seeded and synthetic (synth): q, k ~ N(0,1)/sqrt(d) raw (so the
+ReLU inside the kernels matters) or ReLU'd by the generator (for the
+normalised identity-map case, whose weights must be non-negative); v ~ N(0,1);
+initial states N(0,1)*0.5 (normaliser sums |N(0,1)|).  Sizes span several
+segments per chain and a ragged last block; the 1M-token workload is checked
+on its first and last 4096 tokens with the carried state and normaliser sums
+computed in float64.
+"""
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_chunkwise_amd as la
+import oracle
+from long_context_attention_chunkwise_amd import synth
+from gpu_util import check_close, f64, need_gpu, rms, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+BF16 = torch.bfloat16
+
+
+def inputs(B, Hq, Hkv, N, seed, relu_gen=False):
+    w = synth.Workload("t", B, Hq, Hkv, N, 128, 128, 64, BF16, relu_gen, False)
+    return synth.make_qkv(w, DEV, seed=seed)
+
+
+CASES = [
+    # causal, fmap, normalize, eps, s_in, z_in, out dtype, B, Hq, Hkv, N, generator ReLU
+    (1, "relu", 0, 0.0, True, False, BF16, 1, 8, 2, 3000, False),
+    (1, "relu", 1, 1e-6, True, True, torch.float32, 1, 8, 2, 3000, False),
+    (1, "identity", 1, 0.0, False, False, torch.float32, 2, 4, 1, 1000, True),
+    (0, "identity", 0, 0.0, True, False, torch.float32, 1, 8, 2, 2100, False),
+    (0, "relu", 1, 1e-3, False, True, BF16, 1, 8, 2, 3000, False),
+    (0, "relu", 0, 0.0, False, False, torch.float32, 1, 8, 1, 777, False),   # G = 8: two subgroups
+    (1, "relu", 1, 0.0, True, True, torch.float32, 1, 8, 1, 2500, False),    # G = 8, causal
+    (1, "relu", 1, 1e-6, True, True, torch.float32, 1, 8, 2, 100, False),    # one segment: s_in/z_in read directly
+    (0, "relu", 1, 1e-6, True, True, torch.float32, 1, 8, 2, 1, False),      # one token
+]
+
+
+@pytest.mark.parametrize("causal,fmap,norm,eps,use_s,use_z,out_dtype,B,Hq,Hkv,N,relu_gen", CASES)
+def test_variant_matches_oracle(causal, fmap, norm, eps, use_s, use_z, out_dtype, B, Hq, Hkv, N, relu_gen):
+    need_gpu()
+    say(f"case variant causal={causal} fmap={fmap} norm={norm} eps={eps} s_in={use_s} z_in={use_z} "
+        f"out={out_dtype} B={B} Hq={Hq} Hkv={Hkv} N={N}")
+    q, k, v = inputs(B, Hq, Hkv, N, seed=N + 7 * Hq + causal, relu_gen=relu_gen)
+    S0 = synth.random_state((B, Hkv, 128, 128), DEV, seed=N + 3, scale=0.5) if use_s else None
+    Z0 = synth.random_state((B, Hkv, 128), DEV, seed=N + 4).abs() if use_z else None
+    o, S, Z = la.forward_variant(q, k, v, causal=bool(causal), feature_map=fmap, normalize=bool(norm), eps=eps,
+                                 out_dtype=out_dtype, s_in=S0, z_in=Z0, return_state=True)
+    torch.cuda.synchronize()
+    ref_o, ref_S, ref_z = oracle.variant(f64(q), f64(k), f64(v), causal=bool(causal), relu=(fmap == "relu"),
+                                         normalize=bool(norm), eps=eps, s_in=None if S0 is None else f64(S0),
+                                         z_in=None if Z0 is None else f64(Z0))
+    # normalised outputs are weighted averages of value rows: tolerance in units of RMS(v)
+    check_close("o", f64(o), ref_o, BF16, out_dtype, scale=rms(f64(v)) if norm else None)
+    check_close("S_out", f64(S), ref_S, BF16, torch.float32)
+    if norm:
+        check_close("z_out", f64(Z), ref_z, BF16, torch.float32)
+
+
+def test_plain_variant_is_the_forward():
+    """causal, identity map, no normalisation: bit for bit la_forward_ex."""
+    need_gpu()
+    q, k, v = inputs(1, 8, 2, 5000, seed=5)
+    S0 = synth.random_state((1, 2, 128, 128), DEV, seed=6, scale=0.5)
+    a, Sa, _ = la.forward_variant(q, k, v, s_in=S0, return_state=True)
+    b, Sb = la.forward(q, k, v, s_in=S0, return_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(Sa, Sb)
+
+
+def test_variants_gqa_1m_slices():
+    """The 1M-token GQA workload (raw q, k; phi = ReLU inside): the causal
+    normalised variant on the first and last 4096 tokens of KV groups 0 and
+    31 with the oracle's carried (S, z), its final (S, z); and the
+    non-causal ReLU variant (normalised and not) on the same slices against
+    the totals."""
+    need_gpu()
+    w = synth.WORKLOADS["gqa_1m"]
+    G = w.Hq // w.Hkv
+    N, W = w.N, 4096
+    say(f"case variants gqa_1m: N={N}")
+    q, k, v = inputs(w.B, w.Hq, w.Hkv, N, seed=0)
+    eps = 1e-6
+    o, S, Z = la.forward_variant(q, k, v, causal=True, feature_map="relu", normalize=True, eps=eps,
+                                 return_state=True)
+    onc = la.forward_variant(q, k, v, causal=False, feature_map="relu", normalize=True, eps=eps)
+    onc_plain, S_nc, _ = la.forward_variant(q, k, v, causal=False, feature_map="relu", return_state=True)
+    torch.cuda.synchronize()
+    for x in (o, onc, onc_plain):
+        assert bool(torch.isfinite(x).all())
+    a = N - W
+    for g in (0, 31):
+        hs, gs = slice(g * G, (g + 1) * G), slice(g, g + 1)
+        kr = np.maximum(f64(k[:, gs]), 0.0)
+        vg = f64(v[:, gs])
+        ones = np.ones(kr.shape[:3] + (1,))
+        S_a, z_a = oracle.final_state(kr[:, :, :a], vg[:, :, :a]), oracle.final_state(kr[:, :, :a], ones[:, :, :a])[..., 0]
+        S_t, z_t = oracle.final_state(kr, vg), oracle.final_state(kr, ones)[..., 0]
+        del kr, ones
+        for lo, hi, s_in, z_in in ((0, W, None, None), (a, N, S_a, z_a)):
+            qs, ks, vs = f64(q[:, hs, lo:hi]), f64(k[:, gs, lo:hi]), vg[:, :, lo:hi]
+            ref = oracle.variant(qs, ks, vs, causal=True, relu=True, normalize=True, eps=eps, s_in=s_in, z_in=z_in)
+            vscale = rms(vs)
+            check_close(f"causal normalised group {g} tokens [{lo}, {hi})", f64(o[:, hs, lo:hi]), ref[0], BF16, BF16,
+                        scale=vscale)
+            # non-causal: zero keys add nothing, the totals come in as the initial state
+            zk, zv = np.zeros_like(ks), np.zeros_like(vs)
+            ref_nc = oracle.variant(qs, zk, zv, causal=False, relu=True, normalize=True, eps=eps, s_in=S_t, z_in=z_t)
+            check_close(f"non-causal normalised group {g} tokens [{lo}, {hi})", f64(onc[:, hs, lo:hi]), ref_nc[0],
+                        BF16, BF16, scale=vscale)
+            ref_np = oracle.variant(qs, zk, zv, causal=False, relu=True, s_in=S_t)
+            check_close(f"non-causal group {g} tokens [{lo}, {hi})", f64(onc_plain[:, hs, lo:hi]), ref_np[0], BF16,
+                        BF16)
+        check_close(f"causal final state group {g}", f64(S[:, gs]), S_t, BF16, torch.float32)
+        check_close(f"causal final z group {g}", f64(Z[:, gs]), z_t, BF16, torch.float32)
+        check_close(f"non-causal state group {g}", f64(S_nc[:, gs]), S_t, BF16, torch.float32)
