@@ -13,6 +13,9 @@ Backward (secondary): la_backward (dQ, dK, dV and the initial-state gradient)
 on the same workload with a seeded N(0,1) upstream gradient, timed with HIP
 events per call; reported as tokens/s and algorithmic HBM GB/s.
 
+Forward variants (secondary): la_forward_variant with the ReLU feature map,
+causal normalised and non-causal, on the same workload.
+
 Decode (secondary): 256 sequences x 32 KV heads of float32 128x128 state
 (512 MiB) initialised by the forward kernel over a seeded 8192-token prefix,
 then single-token steps; reported as HBM GB/s.
@@ -232,6 +235,58 @@ def bench_backward(la, synth, torch, w, q, k, v, steps, warmup):
             "workspace_bytes": ws_bytes}
 
 
+VARIANTS = (
+    # name, causal, feature map, normalize, eps
+    ("relu_normalised_causal", True, "relu", True, 1e-6),
+    ("relu_noncausal", False, "relu", False, 0.0),
+)
+
+
+def bench_variants(la, torch, w, q, k, v, steps, warmup):
+    """la_forward_variant on the forward workload: per-call HIP-event time and
+    the algorithmic HBM rate (q, k, v read once, o written once)."""
+    import ctypes
+    lib = la.load_library()
+    dev = torch.device("cuda:0")
+    o = torch.empty((w.B, w.Hq, w.N, w.dv), dtype=torch.bfloat16, device=dev)
+    S = torch.empty((w.B, w.Hkv, w.d, w.dv), dtype=torch.float32, device=dev)
+    Z = torch.empty((w.B, w.Hkv, w.d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    P = ctypes.c_void_p
+    nbytes = forward_bytes(w, w.N)
+    out = {}
+    for name, causal, fmap, norm, eps in VARIANTS:
+        ws_bytes = lib.la_forward_variant_workspace_bytes(w.B, w.Hq, w.Hkv, w.N, w.d, w.dv, w.block, la.LA_BF16,
+                                                          int(causal), int(norm))
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        args = (P(q.data_ptr()), P(k.data_ptr()), P(v.data_ptr()), P(o.data_ptr()), w.B, w.Hq, w.Hkv, w.N, w.d,
+                w.dv, w.block, la.LA_BF16, la.LA_BF16, int(causal), 1 if fmap == "relu" else 0, int(norm),
+                float(eps), None, P(S.data_ptr()), None, P(Z.data_ptr()) if norm else None, P(ws.data_ptr()),
+                ws_bytes, P(stream.cuda_stream))
+        for _ in range(warmup):
+            st = lib.la_forward_variant(*args)
+            if st:
+                raise RuntimeError(f"variant {name} failed: {la.status_str(st)}")
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            a.record(stream)
+            lib.la_forward_variant(*args)
+            b.record(stream)
+        torch.cuda.synchronize()
+        if not bool(torch.isfinite(o).all().item()):
+            raise RuntimeError(f"non-finite output in variant {name}")
+        ms = statistics.mean(a.elapsed_time(b) for a, b in evs)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"causal": causal, "feature_map": fmap, "normalize": norm, "eps": eps,
+                     "ms_per_call": round(ms, 4), "tokens_per_s": round(w.B * w.N / (ms * 1e-3), 1),
+                     "hbm_gb_per_s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "bytes_alg": nbytes}
+        del ws
+    del o, S, Z
+    return {"steps": steps, "warmup": warmup, "workload": w.name, "variants": out}
+
+
 def bench_decode(la, synth, torch, w, steps, warmup):
     dev = torch.device("cuda:0")
     S = torch.empty((w.B, w.Hkv, w.d, w.dv), dtype=torch.float32, device=dev)
@@ -281,6 +336,7 @@ def main():
     ap.add_argument("--workload", default="gqa_1m", help="forward workload name (synth.WORKLOADS)")
     ap.add_argument("--decode-steps", type=int, default=1000, help="0 skips the decode measurement")
     ap.add_argument("--decode-warmup", type=int, default=10)
+    ap.add_argument("--variant-steps", type=int, default=5, help="0 skips the forward-variant measurement")
     ap.add_argument("--backward-steps", type=int, default=5, help="0 skips the backward measurement")
     ap.add_argument("--backward-warmup", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -315,6 +371,10 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline (fp64 oracle) ...")
         cpu = cpu_baseline(q, k, v, w)
+    variants = None
+    if args.variant_steps > 0:
+        variants = bench_variants(la, torch, w, q, k, v, args.variant_steps, 1)
+        log("[bench] variants: " + ", ".join(f"{n} {r['ms_per_call']:.3f} ms" for n, r in variants["variants"].items()))
     backward = None
     if args.backward_steps > 0:
         backward = bench_backward(la, synth, torch, w, q, k, v, args.backward_steps, args.backward_warmup)
@@ -362,6 +422,7 @@ def main():
                  "peak_tflops": PEAK_BF16_TFLOPS, "flops_alg": f_alg, "flops_tile": f_tile},
         "phases_ms": {"segment_states": round(ms_states, 4), "outputs": round(ms_main, 4)},
         "workspace_bytes": ws_bytes,
+        "variants": variants,
         "backward": backward,
         "decode": decode,
         "cpu_baseline": cpu,
