@@ -15,18 +15,21 @@
 // walked from the last block to the first.  (dQ is the causal forward on
 // (dO, V, K) and runs on the forward kernels.)
 //
-// Design for MI355X: one workgroup of four waves (one per SIMD) per (batch,
-// KV head, sequence segment); segment j starts from the sum over later
-// segments, produced by the forward's pre-pass kernel run on (Q, dO) pairs and
-// a reverse scan here.  Wave w owns dV columns, dK columns and state columns
-// [32w, 32w+32); the fp32 state stays in VGPRs and is rounded to bf16 once
-// per block into an n-major LDS copy for the inter terms.  Query heads are
-// processed one at a time through LDS; the next head's (or next block's)
-// tiles are loaded into registers while the current one computes.  Products
-// are v_mfma_f32_16x16x32_bf16 with the transposed-product layout of the
-// forward kernel: the accumulators of the masked score tiles X^T = Q K^T and
-// Y^T = dO V^T are the B operands of the token-contracting products, shared
-// between waves through LDS in operand order.
+// Design for MI355X: one workgroup of eight waves (two per SIMD, so one
+// wave's LDS and memory waits overlap the other's products) per (batch, KV
+// head, sequence segment); segment j starts from the sum over later segments,
+// produced by the forward's pre-pass kernel run on (Q, dO) pairs and a
+// reverse scan here.  Wave w owns columns [16w, 16w+16) of dV, dK and the
+// state R; the fp32 state stays in VGPRs and is rounded to bf16 once per
+// block into an n-major LDS copy for the inter terms.  Query heads are
+// processed one at a time through LDS: the K/V pair and each head's (Q, dO)
+// pair form one stream of 32 KiB items rotating over two register slots (two
+// items in flight).  Products are v_mfma_f32_16x16x32_bf16 with the
+// transposed-product layout of the forward kernel: wave w computes the score
+// tiles X^T = Q K^T (w < 4) or Y^T = dO V^T (w >= 4) of key tile w % 4 for all
+// four query tiles, masks t >= s arithmetically (no branch depends on the
+// wave) and publishes them in LDS as bf16 B operands of the token-contracting
+// products.
 #include "la_internal.h"
 #include "la_mfma.h"
 
@@ -35,53 +38,12 @@ namespace {
 
 using namespace mfma16;
 
-constexpr int kThreads = 256;
-#ifndef LA_BWD_SLOTS
-#define LA_BWD_SLOTS 2
-#endif
-constexpr int kSlots = LA_BWD_SLOTS;  // 32 KiB tile pairs in flight per workgroup
+constexpr int kThreads = 512;  // eight waves, two per SIMD
+constexpr int kSlots = 2;      // 32 KiB tile pairs in flight per workgroup
 constexpr int DD = D * DV;
-
-// Two row-major [64][128] bf16 tiles of one block: thread tid moves rows
-// tid/16 + 16i (i < 4), 16-byte chunk tid%16.  `rows` (1..64) is the number
-// of the block's tokens before N; rows past it re-read the last valid row
-// (every load is issued on every path, so the compiler counts the loads in
-// flight exactly) and are stored to LDS as zeros.
-struct PairRegs {
-  u32x4 a[4], b[4];  // clang vector type: selects and copies stay in registers
-};
 
 __device__ __forceinline__ u32x4 ld_stream_v(const uint16_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
-
-// ab, bb: the block's first row (uniform); offsets within the block are 32-bit.
-__device__ __forceinline__ void load_pair(PairRegs& r, const uint16_t* ab, const uint16_t* bb, int rows, int tid) {
-  const int c = tid & 15;
-  for (int i = 0; i < 4; ++i) {
-    int row = (tid >> 4) + 16 * i;
-    row = row < rows ? row : rows - 1;
-    r.a[i] = ld_stream_v(ab + row * D + 8 * c);
-    r.b[i] = ld_stream_v(bb + row * DV + 8 * c);
-  }
-}
-
-__device__ __forceinline__ void store_pair(const PairRegs& r, uint16_t* as, uint16_t* bs, int rows, int tid) {
-  const int c = tid & 15;
-  if (rows == C) {  // uniform: every block but possibly the sequence's last
-    for (int i = 0; i < 4; ++i) {
-      const int row = (tid >> 4) + 16 * i;
-      *reinterpret_cast<u32x4*>(as + row * ROWKV + 8 * c) = r.a[i];
-      *reinterpret_cast<u32x4*>(bs + row * ROWKV + 8 * c) = r.b[i];
-    }
-  } else {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    for (int i = 0; i < 4; ++i) {
-      const int row = (tid >> 4) + 16 * i;
-      *reinterpret_cast<u32x4*>(as + row * ROWKV + 8 * c) = row < rows ? r.a[i] : z;
-      *reinterpret_cast<u32x4*>(bs + row * ROWKV + 8 * c) = row < rows ? r.b[i] : z;
-    }
-  }
 }
 
 struct __align__(16) BwdSmem {
@@ -101,8 +63,45 @@ __device__ __forceinline__ void store_row4(void* base, int64_t off, floatx4 x) {
     *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(base) + off) = to_bf16x4(x);
 }
 
+// Two row-major [64][128] bf16 tiles of one block (a K/V or a Q/dO pair):
+// thread tid moves rows tid/16 + 32i (i < 2), 16-byte chunk tid%16.  `rows`
+// (1..64) is the number of the block's tokens before N; rows past it re-read
+// the last valid row (every load is issued on every path, so the compiler
+// counts the loads in flight exactly) and are stored to LDS as zeros.
+struct PairRegs8 {
+  u32x4 a[2], b[2];
+};
+
+__device__ __forceinline__ void load_pair8(PairRegs8& r, const uint16_t* ab, const uint16_t* bb, int rows, int tid) {
+  const int c = tid & 15;
+  for (int i = 0; i < 2; ++i) {
+    int row = (tid >> 4) + 32 * i;
+    row = row < rows ? row : rows - 1;
+    r.a[i] = ld_stream_v(ab + row * D + 8 * c);
+    r.b[i] = ld_stream_v(bb + row * DV + 8 * c);
+  }
+}
+
+__device__ __forceinline__ void store_pair8(const PairRegs8& r, uint16_t* as, uint16_t* bs, int rows, int tid) {
+  const int c = tid & 15;
+  if (rows == C) {
+    for (int i = 0; i < 2; ++i) {
+      const int row = (tid >> 4) + 32 * i;
+      *reinterpret_cast<u32x4*>(as + row * ROWKV + 8 * c) = r.a[i];
+      *reinterpret_cast<u32x4*>(bs + row * ROWKV + 8 * c) = r.b[i];
+    }
+  } else {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int i = 0; i < 2; ++i) {
+      const int row = (tid >> 4) + 32 * i;
+      *reinterpret_cast<u32x4*>(as + row * ROWKV + 8 * c) = row < rows ? r.a[i] : z;
+      *reinterpret_cast<u32x4*>(bs + row * ROWKV + 8 * c) = row < rows ? r.b[i] : z;
+    }
+  }
+}
+
 template <bool OUT_F32, int NS>
-__global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(
+__global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel8(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, void* __restrict__ dk, void* __restrict__ dvg,
     const float* __restrict__ rstarts, float* __restrict__ ds_in, int Hq, int Hkv, int64_t N,
@@ -111,10 +110,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(
   __shared__ BwdSmem sm;
 
   const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7, uniform
   const int lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
   const int seg = blockIdx.x % P;
-  const int bg = blockIdx.x / P;  // b * Hkv + g
+  const int bg = blockIdx.x / P;
   const int b = bg / Hkv, g = bg % Hkv;
   const int G = Hq / Hkv;
   const int64_t blk0 = int64_t(seg) * blocks_per_seg;
@@ -122,38 +121,28 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(
 
   const uint16_t* kh = k + int64_t(bg) * N * D;
   const uint16_t* vh = v + int64_t(bg) * N * DV;
-  const uint16_t* qg = q + (int64_t(b) * Hq + int64_t(g) * G) * N * D;        // head 0 of the group
+  const uint16_t* qg = q + (int64_t(b) * Hq + int64_t(g) * G) * N * D;
   const uint16_t* og = dout + (int64_t(b) * Hq + int64_t(g) * G) * N * DV;
 
-  // State of the later tokens, wave w's columns [32w, 32w+32).
+  // R columns [16w, 16w+16): tile it holds rows 16it + 4grp + i, column 16w + l16
   const float* r0 = rstarts ? rstarts + (int64_t(bg) * P + seg) * DD : nullptr;
-  floatx4 racc[2][8];
-  for (int jn = 0; jn < 2; ++jn)
-    for (int it = 0; it < 8; ++it)
-      for (int i = 0; i < 4; ++i) racc[jn][it][i] = 0.0f;
+  floatx4 racc[8];
+  for (int it = 0; it < 8; ++it)
+    for (int i = 0; i < 4; ++i) racc[it][i] = 0.0f;
   if (r0 != nullptr)
-    for (int jn = 0; jn < 2; ++jn)
-      for (int it = 0; it < 8; ++it)
-        for (int i = 0; i < 4; ++i) racc[jn][it][i] = r0[(16 * it + 4 * grp + i) * DV + 32 * w + 16 * jn + l16];
-  for (int jn = 0; jn < 2; ++jn)
     for (int it = 0; it < 8; ++it)
-      *reinterpret_cast<bf16x4*>(&sm.rt[(32 * w + 16 * jn + l16) * ROWST + 16 * it + 4 * grp]) =
-          to_bf16x4(racc[jn][it]);
+      for (int i = 0; i < 4; ++i) racc[it][i] = r0[(16 * it + 4 * grp + i) * DV + 16 * w + l16];
+  for (int it = 0; it < 8; ++it)
+    *reinterpret_cast<bf16x4*>(&sm.rt[(16 * w + l16) * ROWST + 16 * it + 4 * grp]) = to_bf16x4(racc[it]);
 
-  // The segment's tiles as one stream of 32 KiB items, last block first: for
-  // each block its K/V pair (item 0), then the (Q, dO) pair of each query
-  // head (items 1..G).  NS register slots rotate over the stream so that NS
-  // items are in flight while one is computed on.  Stream positions are
-  // carried as (block, item) counters; loads past the end repeat the last
-  // item and are never stored.
   const int per_blk = G + 1;
   int64_t ld_blk = blk1 - 1;
   int ld_r = 0;
-  auto load_next = [&](PairRegs& r) __attribute__((always_inline)) {
+  auto load_next = [&](PairRegs8& r) __attribute__((always_inline)) {
     const int rows = int(N - ld_blk * C < C ? N - ld_blk * C : C);
     const uint16_t* a = ld_r == 0 ? kh : qg + int64_t(ld_r - 1) * N * D;
     const uint16_t* bb = ld_r == 0 ? vh : og + int64_t(ld_r - 1) * N * DV;
-    load_pair(r, a + ld_blk * C * D, bb + ld_blk * C * DV, rows, tid);
+    load_pair8(r, a + ld_blk * C * D, bb + ld_blk * C * DV, rows, tid);
     if (ld_blk > blk0 || ld_r < G) {
       if (++ld_r == per_blk) {
         ld_r = 0;
@@ -163,137 +152,99 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(
   };
 
   const int64_t nitems = (blk1 - blk0) * per_blk;
-  PairRegs s0, s1;  // named, not an array: each stays in registers
+  PairRegs8 s0, s1;
   if (nitems > 0) {
     load_next(s0);
     if constexpr (NS == 2) load_next(s1);
   }
 
   const floatx4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
-  floatx4 adv[2][4], adk[2][4];  // dV^T / dK^T tiles: [column tile of 32w + 16j][s-tile]
-  int64_t blk = blk1 - 1;        // block of the item being computed
-  int r_in = 0;                  // its position in the block
+  floatx4 adv[4], adk[4];  // dV^T / dK^T tiles of columns 16w.. for s-tiles 0..3
+  int64_t blk = blk1 - 1;
+  int r_in = 0;
+  const bool is_y = w >= 4;   // uniform: this wave's score tiles are Y^T = dO V^T
+  const int skey = w & 3;     // its key tile
 
-  // Always inlined: each call site then binds its own slot's registers.
-  auto step = [&](PairRegs& cur) __attribute__((always_inline)) {
+  auto step = [&](PairRegs8& cur) __attribute__((always_inline)) {
     const int rows = int(N - blk * C < C ? N - blk * C : C);
     if (r_in == 0) {
-      // K/V of the block; the previous block's last item ended with a barrier
-      store_pair(cur, sm.k, sm.v, rows, tid);
+      store_pair8(cur, sm.k, sm.v, rows, tid);
       load_next(cur);
-      for (int j = 0; j < 2; ++j)
-        for (int si = 0; si < 4; ++si) {
-          adv[j][si] = z4;
-          adk[j][si] = z4;
-        }
+      for (int si = 0; si < 4; ++si) {
+        adv[si] = z4;
+        adk[si] = z4;
+      }
       r_in = 1;
       return;
     }
     const int h = r_in - 1;
-    store_pair(cur, sm.q, sm.o, rows, tid);
+    store_pair8(cur, sm.q, sm.o, rows, tid);
     __syncthreads();  // K/V, this head's Q/dO and the state copy are in LDS
     load_next(cur);
 
     if (h == 0) {
       // inter: dV^T[n][s] += sum_i R[i][n] K[s][i];  dK^T[i][s] += sum_n R[i][n] V[s][n]
       for (int p = 0; p < 4; ++p) {
-        bf16x8 ra[2], rb[2];
-        for (int j = 0; j < 2; ++j) {
-          ra[j] = ld_lds16(sm.rt + (32 * w + 16 * j + l16) * ROWST + 32 * p + 8 * grp);
-          rb[j] = tr_operand(sm.rt, p, 32 * w + 16 * j, l16, grp, 4, ROWST);
-        }
+        const bf16x8 ra = ld_lds16(sm.rt + (16 * w + l16) * ROWST + 32 * p + 8 * grp);
+        const bf16x8 rb = tr_operand(sm.rt, p, 16 * w, l16, grp, 4, ROWST);
         for (int si = 0; si < 4; ++si) {
           const uint16_t* krow = sm.k + (16 * si + l16) * ROWKV;
           const uint16_t* vrow = sm.v + (16 * si + l16) * ROWKV;
           const bf16x8 bk = ld_lds16(krow + 32 * p + 8 * grp);
-          // V[s] at the transpose load's slots 32p + 4grp + {0..3}, 32p + 16 + 4grp + {0..3}
           const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(vrow + 32 * p + 4 * grp);
           const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(vrow + 32 * p + 16 + 4 * grp);
           const bf16x8 bv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-          for (int j = 0; j < 2; ++j) {
-            adv[j][si] = mfma(ra[j], bk, adv[j][si]);
-            adk[j][si] = mfma(rb[j], bv, adk[j][si]);
-          }
+          adv[si] = mfma(ra, bk, adv[si]);
+          adk[si] = mfma(rb, bv, adk[si]);
         }
       }
     }
 
-    // Scores of key tile w: X^T[t][s] = Q[t].K[s], Y^T[t][s] = dO[t].V[s] for
-    // all four query tiles, then the causal mask keeps t >= s (query tiles
-    // before the key tile come out all zero).  No branch depends on the wave.
+    // scores of key tile skey for all four query tiles: X^T = Q K^T or Y^T = dO V^T
     {
-      floatx4 xt[4], yt[4];
-      for (int ti = 0; ti < 4; ++ti) {
-        xt[ti] = z4;
-        yt[ti] = z4;
-      }
+      const uint16_t* arows = is_y ? sm.o : sm.q;
+      const uint16_t* brows = (is_y ? sm.v : sm.k) + (16 * skey + l16) * ROWKV;
+      floatx4 xt[4];
+      for (int ti = 0; ti < 4; ++ti) xt[ti] = z4;
       for (int ds = 0; ds < 4; ++ds) {
-        const bf16x8 bk = ld_lds16(sm.k + (16 * w + l16) * ROWKV + 32 * ds + 8 * grp);
-        const bf16x8 bv = ld_lds16(sm.v + (16 * w + l16) * ROWKV + 32 * ds + 8 * grp);
-        for (int ti = 0; ti < 4; ++ti) {
-          const bf16x8 aq = ld_lds16(sm.q + (16 * ti + l16) * ROWKV + 32 * ds + 8 * grp);
-          const bf16x8 ao = ld_lds16(sm.o + (16 * ti + l16) * ROWKV + 32 * ds + 8 * grp);
-          xt[ti] = mfma(aq, bk, xt[ti]);
-          yt[ti] = mfma(ao, bv, yt[ti]);
-        }
+        const bf16x8 bop = ld_lds16(brows + 32 * ds + 8 * grp);
+        for (int ti = 0; ti < 4; ++ti)
+          xt[ti] = mfma(ld_lds16(arows + (16 * ti + l16) * ROWKV + 32 * ds + 8 * grp), bop, xt[ti]);
       }
-      // entry i of tile ti: t = 16ti + 4grp + i, s = 16w + l16
-      const int lim = 16 * w + l16 - 4 * grp;
+      // entry i of tile ti: t = 16ti + 4grp + i, s = 16skey + l16; keep t >= s
+      const int lim = 16 * skey + l16 - 4 * grp;
       for (int ti = 0; ti < 4; ++ti)
         for (int i = 0; i < 4; ++i)
-          if (16 * ti + i < lim) {
-            xt[ti][i] = 0.0f;
-            yt[ti][i] = 0.0f;
-          }
-      // operand packs for token steps p = 0 (t-tiles 0, 1) and p = 1 (t-tiles 2, 3)
-      for (int p = 0; p < 2; ++p) {
-        sm.xb[0][4 * p + w][lane] = pack_tiles(xt[2 * p], xt[2 * p + 1]);
-        sm.xb[1][4 * p + w][lane] = pack_tiles(yt[2 * p], yt[2 * p + 1]);
-      }
+          if (16 * ti + i < lim) xt[ti][i] = 0.0f;
+      for (int p = 0; p < 2; ++p) sm.xb[is_y ? 1 : 0][4 * p + skey][lane] = pack_tiles(xt[2 * p], xt[2 * p + 1]);
     }
     __syncthreads();  // every wave's score packs are in LDS
 
-    // intra: dV^T[n][s] += sum_t dO[t][n] X^T[t][s];  dK^T[i][s] += sum_t Q[t][i] Y^T[t][s]
-    // and the state update R[i][n] += sum_t Q[t][i] dO[t][n]
+    // intra (dV, dK columns 16w..) and the state update (R columns 16w..)
     for (int p = 0; p < 2; ++p) {
-      bf16x8 ao[2], aq[2];
-      for (int j = 0; j < 2; ++j) {
-        ao[j] = tr_operand(sm.o, p, 32 * w + 16 * j, l16, grp);
-        aq[j] = tr_operand(sm.q, p, 32 * w + 16 * j, l16, grp);
-      }
+      const bf16x8 ao = tr_operand(sm.o, p, 16 * w, l16, grp);
+      const bf16x8 aq = tr_operand(sm.q, p, 16 * w, l16, grp);
       for (int si = 0; si < 4; ++si) {
         if (p == 0 && si >= 2) continue;  // tokens 0..31 are all before key tiles 2, 3
-        const bf16x8 bx = sm.xb[0][4 * p + si][lane];
-        const bf16x8 by = sm.xb[1][4 * p + si][lane];
-        for (int j = 0; j < 2; ++j) {
-          adv[j][si] = mfma(ao[j], bx, adv[j][si]);
-          adk[j][si] = mfma(aq[j], by, adk[j][si]);
-        }
+        adv[si] = mfma(ao, sm.xb[0][4 * p + si][lane], adv[si]);
+        adk[si] = mfma(aq, sm.xb[1][4 * p + si][lane], adk[si]);
       }
-      for (int it = 0; it < 8; ++it) {
-        const bf16x8 qa = tr_operand(sm.q, p, 16 * it, l16, grp);
-        racc[0][it] = mfma(qa, ao[0], racc[0][it]);
-        racc[1][it] = mfma(qa, ao[1], racc[1][it]);
-      }
+      for (int it = 0; it < 8; ++it) racc[it] = mfma(tr_operand(sm.q, p, 16 * it, l16, grp), ao, racc[it]);
     }
     __syncthreads();  // Q/dO and the packs may be overwritten
 
     if (h == G - 1) {
-      // dV, dK rows of the block: tile (j, si) holds columns 32w + 16j + 4grp + {0..3} of row 16si + l16
+      // dV, dK rows of the block: tile si holds columns 16w + 4grp + {0..3} of row 16si + l16
       for (int si = 0; si < 4; ++si) {
         const int64_t s = blk * C + 16 * si + l16;
-        if (s < N)
-          for (int j = 0; j < 2; ++j) {
-            const int64_t off = (int64_t(bg) * N + s) * DV + 32 * w + 16 * j + 4 * grp;
-            store_row4<OUT_F32>(dvg, off, adv[j][si]);
-            store_row4<OUT_F32>(dk, off, adk[j][si]);
-          }
+        if (s < N) {
+          const int64_t off = (int64_t(bg) * N + s) * DV + 16 * w + 4 * grp;
+          store_row4<OUT_F32>(dvg, off, adv[si]);
+          store_row4<OUT_F32>(dk, off, adk[si]);
+        }
       }
-      // bf16 copy of the updated state for the next (earlier) block's inter terms
-      for (int jn = 0; jn < 2; ++jn)
-        for (int it = 0; it < 8; ++it)
-          *reinterpret_cast<bf16x4*>(&sm.rt[(32 * w + 16 * jn + l16) * ROWST + 16 * it + 4 * grp]) =
-              to_bf16x4(racc[jn][it]);
+      for (int it = 0; it < 8; ++it)
+        *reinterpret_cast<bf16x4*>(&sm.rt[(16 * w + l16) * ROWST + 16 * it + 4 * grp]) = to_bf16x4(racc[it]);
       r_in = 0;
       --blk;
     } else {
@@ -309,9 +260,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(
 
   if (ds_in != nullptr && seg == 0) {
     float* so = ds_in + int64_t(bg) * DD;
-    for (int jn = 0; jn < 2; ++jn)
-      for (int it = 0; it < 8; ++it)
-        for (int i = 0; i < 4; ++i) so[(16 * it + 4 * grp + i) * DV + 32 * w + 16 * jn + l16] = racc[jn][it][i];
+    for (int it = 0; it < 8; ++it)
+      for (int i = 0; i < 4; ++i) so[(16 * it + 4 * grp + i) * DV + 16 * w + l16] = racc[it][i];
   }
 }
 
@@ -373,11 +323,11 @@ hipError_t launch_bwd_kv(const void* q, const void* k, const void* v, const void
   const auto* v16 = static_cast<const uint16_t*>(v);
   const auto* o16 = static_cast<const uint16_t*>(dout);
   if (out_f32)
-    hipLaunchKernelGGL((bwd_kv_kernel<true, kSlots>), grid, dim3(kThreads), 0, stream, q16, k16, v16, o16, dk, dvg, rs,
-                       ds_in, int(Hq), int(Hkv), N, plan.nblocks, plan.blocks_per_seg, plan.P);
+    hipLaunchKernelGGL((bwd_kv_kernel8<true, kSlots>), grid, dim3(kThreads), 0, stream, q16, k16, v16, o16, dk, dvg,
+                       rs, ds_in, int(Hq), int(Hkv), N, plan.nblocks, plan.blocks_per_seg, plan.P);
   else
-    hipLaunchKernelGGL((bwd_kv_kernel<false, kSlots>), grid, dim3(kThreads), 0, stream, q16, k16, v16, o16, dk, dvg, rs,
-                       ds_in, int(Hq), int(Hkv), N, plan.nblocks, plan.blocks_per_seg, plan.P);
+    hipLaunchKernelGGL((bwd_kv_kernel8<false, kSlots>), grid, dim3(kThreads), 0, stream, q16, k16, v16, o16, dk, dvg,
+                       rs, ds_in, int(Hq), int(Hkv), N, plan.nblocks, plan.blocks_per_seg, plan.P);
   return hipGetLastError();
 }
 
