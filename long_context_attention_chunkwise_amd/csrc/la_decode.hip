@@ -9,7 +9,8 @@
 // written back once, and the G query-head products are formed from the same
 // registers on the way (one pass, no second read of S).
 //
-// One workgroup of 256 threads per state.  Thread (row group rg, column group
+// One workgroup of 512 threads per state (measured against 128, 256 and 1024
+// at d = dv = 128: 512 streams fastest).  Thread (row group rg, column group
 // cg) owns columns [4cg, 4cg+4) of rows rg, rg + nrg, ...: a wave reads whole
 // 512-byte rows with 16-byte accesses.  Per-thread partial products over its
 // rows are reduced across row groups through LDS in a fixed order, so results
@@ -19,7 +20,7 @@
 namespace la {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kMaxD = 128;
 constexpr int kMaxDV = 128;
 
