@@ -619,13 +619,14 @@ __global__ __launch_bounds__(256) void scan_starts(const float* __restrict__ par
 // phi(q_t) . z_tot + eps.  With the state fixed every block is independent:
 // a streaming product Q S_tot per query head (read q, write o) with no
 // barrier in the loop; the next block's Q operands load while the current
-// block multiplies.  Grid: B * Hkv * (G/4) * P workgroups of four waves, wave
-// h serving query head h of its group of four.  S_tot comes in float32 from
-// the pre-pass and is rounded once to the bf16 n-major LDS layout of the
-// causal kernel's state copy.
+// block multiplies.  Grid: B * Hkv * (G/4) * P workgroups of eight waves (two
+// per SIMD), wave w serving query head w % 4 of its group of four on query
+// tiles {2(w/4), 2(w/4) + 1} of each block.  S_tot comes in float32 from the
+// pre-pass and is rounded once to the bf16 n-major LDS layout of the causal
+// kernel's state copy.
 // ---------------------------------------------------------------------------
 template <bool OUT_F32, int FL>
-__global__ __launch_bounds__(256, 1) void fwd_noncausal_g4(
+__global__ __launch_bounds__(512, 1) void fwd_noncausal_g4(
     const uint16_t* __restrict__ q, void* __restrict__ o, const float* __restrict__ stot,
     const float* __restrict__ ztot, int64_t tot_stride, float* s_out, float* z_out, int Hq, int Hkv,
     int subgroups, int64_t N, int64_t nblocks, int64_t blocks_per_seg, int P, float eps) {
@@ -635,7 +636,8 @@ __global__ __launch_bounds__(256, 1) void fwd_noncausal_g4(
   __shared__ __align__(16) float zs[kN ? D : 4];
 
   const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
+  const int hw = w & 3, t0 = 2 * (w >> 2);                 // head in the group, first query tile
   const int lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
   const int seg = blockIdx.x % P;
   const int chain = blockIdx.x / P;
@@ -645,20 +647,19 @@ __global__ __launch_bounds__(256, 1) void fwd_noncausal_g4(
   const int G = Hq / Hkv;
   const int64_t blk0 = int64_t(seg) * blocks_per_seg;
   const int64_t blk1 = blk0 + blocks_per_seg < nblocks ? blk0 + blocks_per_seg : nblocks;
-  const int64_t head = int64_t(b) * Hq + int64_t(g) * G + int64_t(sub) * 4 + w;
+  const int64_t head = int64_t(b) * Hq + int64_t(g) * G + int64_t(sub) * 4 + hw;
   const uint16_t* qh = q + head * N * D;
   const int nlane = 8 * (l16 >> 2) + (l16 & 3);
 
+  // wave w rounds state columns [16w, 16w+16)
   const float* S = stot + int64_t(bg) * tot_stride * (D * DV);
-  for (int jn = 0; jn < 2; ++jn)
-    for (int dt = 0; dt < 8; ++dt) {
-      floatx4 x;
-      for (int i = 0; i < 4; ++i) x[i] = S[(16 * dt + 4 * grp + i) * DV + 32 * w + 16 * jn + l16];
-      *reinterpret_cast<bf16x4*>(&st[(32 * w + 16 * jn + l16) * ROWST + 16 * dt + 4 * grp]) = to_bf16x4(x);
-      if (s_out != nullptr && seg == 0 && sub == 0)
-        for (int i = 0; i < 4; ++i)
-          s_out[int64_t(bg) * (D * DV) + (16 * dt + 4 * grp + i) * DV + 32 * w + 16 * jn + l16] = x[i];
-    }
+  for (int dt = 0; dt < 8; ++dt) {
+    floatx4 x;
+    for (int i = 0; i < 4; ++i) x[i] = S[(16 * dt + 4 * grp + i) * DV + 16 * w + l16];
+    *reinterpret_cast<bf16x4*>(&st[(16 * w + l16) * ROWST + 16 * dt + 4 * grp]) = to_bf16x4(x);
+    if (s_out != nullptr && seg == 0 && sub == 0)
+      for (int i = 0; i < 4; ++i) s_out[int64_t(bg) * (D * DV) + (16 * dt + 4 * grp + i) * DV + 16 * w + l16] = x[i];
+  }
   if constexpr (kN) {
     const float* Z = ztot + int64_t(bg) * tot_stride * D;
     if (tid < D) {
@@ -668,68 +669,68 @@ __global__ __launch_bounds__(256, 1) void fwd_noncausal_g4(
   }
   __syncthreads();  // S_tot (and z_tot) are in LDS
 
-  auto load_q = [&](bf16x8 (&qa)[4][4], int64_t blk) {
-    for (int ti = 0; ti < 4; ++ti) {
-      const int64_t t = blk * C + 16 * ti + l16;
+  auto load_q = [&](bf16x8 (&qa)[2][4], int64_t blk) {
+    for (int tj = 0; tj < 2; ++tj) {
+      const int64_t t = blk * C + 16 * (t0 + tj) + l16;
       for (int ds = 0; ds < 4; ++ds)
-        qa[ti][ds] = (t < N) ? ld_global16(qh + t * D + 32 * ds + 8 * grp) : zero_bf16x8();
+        qa[tj][ds] = (t < N) ? ld_global16(qh + t * D + 32 * ds + 8 * grp) : zero_bf16x8();
     }
   };
-  bf16x8 qa[4][4], qn[4][4];
+  bf16x8 qa[2][4], qn[2][4];
   if (blk0 < blk1) load_q(qa, blk0);
   const floatx4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int64_t blk = blk0; blk < blk1; ++blk) {
     if (blk + 1 < blk1) load_q(qn, blk + 1);
     if constexpr (kR)
-      for (int ti = 0; ti < 4; ++ti)
-        for (int ds = 0; ds < 4; ++ds) qa[ti][ds] = relu_bf16x8(qa[ti][ds]);
-    float inv[4];
+      for (int tj = 0; tj < 2; ++tj)
+        for (int ds = 0; ds < 4; ++ds) qa[tj][ds] = relu_bf16x8(qa[tj][ds]);
+    float inv[2];
     (void)inv;
     if constexpr (kN) {
-      float den[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      float den[2] = {0.0f, 0.0f};
       for (int ds = 0; ds < 4; ++ds) {
         const floatx4 za = *reinterpret_cast<const floatx4*>(&zs[32 * ds + 8 * grp]);
         const floatx4 zb = *reinterpret_cast<const floatx4*>(&zs[32 * ds + 8 * grp + 4]);
-        for (int ti = 0; ti < 4; ++ti)
+        for (int tj = 0; tj < 2; ++tj)
           for (int j = 0; j < 4; ++j)
-            den[ti] += float(qa[ti][ds][j]) * za[j] + float(qa[ti][ds][j + 4]) * zb[j];
+            den[tj] += float(qa[tj][ds][j]) * za[j] + float(qa[tj][ds][j + 4]) * zb[j];
       }
-      for (int ti = 0; ti < 4; ++ti) {
-        float x = den[ti];
+      for (int tj = 0; tj < 2; ++tj) {
+        float x = den[tj];
         x += __shfl_xor(x, 16);
         x += __shfl_xor(x, 32);
-        inv[ti] = 1.0f / (x + eps);
+        inv[tj] = 1.0f / (x + eps);
       }
     }
     for (int m = 0; m < 4; ++m) {
-      floatx4 acc[2][4];
+      floatx4 acc[2][2];
       for (int h2 = 0; h2 < 2; ++h2)
-        for (int ti = 0; ti < 4; ++ti) acc[h2][ti] = z4;
+        for (int tj = 0; tj < 2; ++tj) acc[h2][tj] = z4;
       for (int ds = 0; ds < 4; ++ds)
         for (int h2 = 0; h2 < 2; ++h2) {
           const bf16x8 sa = ld_lds16(st + (32 * m + 4 * h2 + nlane) * ROWST + 32 * ds + 8 * grp);
-          for (int ti = 0; ti < 4; ++ti) acc[h2][ti] = mfma(sa, qa[ti][ds], acc[h2][ti]);
+          for (int tj = 0; tj < 2; ++tj) acc[h2][tj] = mfma(sa, qa[tj][ds], acc[h2][tj]);
         }
       if constexpr (kN)
         for (int h2 = 0; h2 < 2; ++h2)
-          for (int ti = 0; ti < 4; ++ti)
-            for (int i = 0; i < 4; ++i) acc[h2][ti][i] *= inv[ti];
-      for (int ti = 0; ti < 4; ++ti) {
-        const int64_t t = blk * C + 16 * ti + l16;
+          for (int tj = 0; tj < 2; ++tj)
+            for (int i = 0; i < 4; ++i) acc[h2][tj][i] *= inv[tj];
+      for (int tj = 0; tj < 2; ++tj) {
+        const int64_t t = blk * C + 16 * (t0 + tj) + l16;
         if (t < N) {
           const int64_t off = (head * N + t) * DV + 32 * m + 8 * grp;
           if (OUT_F32) {
             float* op = static_cast<float*>(o) + off;
-            *reinterpret_cast<floatx4*>(op) = acc[0][ti];
-            *reinterpret_cast<floatx4*>(op + 4) = acc[1][ti];
+            *reinterpret_cast<floatx4*>(op) = acc[0][tj];
+            *reinterpret_cast<floatx4*>(op + 4) = acc[1][tj];
           } else {
-            *reinterpret_cast<bf16x8*>(static_cast<uint16_t*>(o) + off) = pack_tiles(acc[0][ti], acc[1][ti]);
+            *reinterpret_cast<bf16x8*>(static_cast<uint16_t*>(o) + off) = pack_tiles(acc[0][tj], acc[1][tj]);
           }
         }
       }
     }
-    for (int ti = 0; ti < 4; ++ti)
-      for (int ds = 0; ds < 4; ++ds) qa[ti][ds] = qn[ti][ds];
+    for (int tj = 0; tj < 2; ++tj)
+      for (int ds = 0; ds < 4; ++ds) qa[tj][ds] = qn[tj][ds];
   }
 }
 
@@ -831,7 +832,7 @@ hipError_t variant_outputs(const void* q, const void* k, const void* v, void* o,
     // totals sit at entry P of each chain's P + 1 scanned entries
     const int64_t stride = p.P + 1;
     const dim3 grid(unsigned(B * Hkv * p.subgroups * vp.P_out));
-    hipLaunchKernelGGL((fwd_noncausal_g4<OUT_F32, FL>), grid, dim3(256), 0, stream, static_cast<const uint16_t*>(q),
+    hipLaunchKernelGGL((fwd_noncausal_g4<OUT_F32, FL>), grid, dim3(512), 0, stream, static_cast<const uint16_t*>(q),
                        o, starts + p.P * (D * DV), zstarts + p.P * D, stride, s_out, z_out, iHq, iHkv, p.subgroups,
                        N, p.nblocks, vp.bps_out, vp.P_out, eps);
   }
