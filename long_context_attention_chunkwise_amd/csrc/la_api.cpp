@@ -45,8 +45,11 @@ la_status check_forward_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int
   } else {
     if (d != 128 || dv != 128 || block != kBf16Block) return LA_ERR_UNSUPPORTED;
   }
-  // Grid dimensions are 32-bit; keep the workgroup counts well inside that.
+  // Grid dimensions are 32-bit; keep the workgroup counts well inside that,
+  // and keep every byte count (B * Hq * N * 128 elements of up to 4 bytes)
+  // far from 64-bit overflow.
   if (B * Hq > (int64_t(1) << 24) || N > (int64_t(1) << 40)) return LA_ERR_UNSUPPORTED;
+  if (N > 0 && B * Hq > (int64_t(1) << 44) / N) return LA_ERR_UNSUPPORTED;
   return LA_OK;
 }
 

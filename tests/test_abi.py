@@ -60,6 +60,7 @@ def test_forward_validation(lib):
     assert fwd(lib, N=-1) == SHAPE
     assert fwd(lib, d=64) == UNSUP                       # bf16 path is d = dv = 128
     assert fwd(lib, block=128) == UNSUP
+    assert fwd(lib, B=1 << 12, Hq=1 << 12, Hkv=1 << 12, N=1 << 30) == UNSUP   # byte counts would overflow
     assert fwd(lib, i=BF16, out=2) == UNSUP
     assert fwd(lib, i=F32, out=BF16) == UNSUP
     assert fwd(lib, i=F32, out=F32, dv=48) == UNSUP       # fp32 path: dv multiple of 32
