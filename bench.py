@@ -51,7 +51,6 @@ TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_gqa_1m_decode_256.
 def measured_traffic(kernel, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when the kernel's source has changed since the counters were taken."""
-    import hashlib
     import re
     try:
         text = open(TRAFFIC_PROFILE).read()
@@ -60,16 +59,30 @@ def measured_traffic(kernel, workload):
     for m in re.finditer(r"traffic (\S+) (\S+) bytes=(\d+) source=(\S+) sha256=([0-9a-f]+)", text):
         if (m.group(1), m.group(2)) != (kernel, workload):
             continue
-        # source: the kernel's file and the headers it includes, joined by '+';
-        # the digest covers their concatenated bytes in that order.
-        h = hashlib.sha256()
+        # source: the kernel's file and the headers it includes, joined by '+'.
         try:
-            for name in m.group(4).split("+"):
-                h.update(open(os.path.join(ROOT, "long_context_attention_chunkwise_amd", "csrc", name), "rb").read())
+            texts = [open(os.path.join(ROOT, "long_context_attention_chunkwise_amd", "csrc", name)).read()
+                     for name in m.group(4).split("+")]
         except OSError:
             return None
-        return int(m.group(3)) if h.hexdigest() == m.group(5) else None
+        return int(m.group(3)) if code_digest(texts) == m.group(5) else None
     return None
+
+
+def code_digest(texts):
+    """SHA-256 of C++/HIP sources with comments removed, whitespace runs
+    inside a line collapsed to one space and blank lines dropped (string and
+    character literals kept as written), so that an edit to comments,
+    indentation or blank lines leaves it unchanged and any edit to the code
+    changes it.  The texts are taken in order."""
+    import hashlib
+    import re
+    token = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'', re.S)
+    lines = []
+    for text in texts:
+        code = token.sub(lambda m: " " if m.group(0)[0] == "/" else m.group(0), text)
+        lines.extend(" ".join(line.split()) for line in code.splitlines())
+    return hashlib.sha256("\n".join(line for line in lines if line).encode()).hexdigest()
 
 
 def forward_flops(w, N):

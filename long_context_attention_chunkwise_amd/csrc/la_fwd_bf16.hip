@@ -12,10 +12,10 @@
 // kept once per KV head and shared by the group's query heads.
 //
 // Design for MI355X:
-//  * One workgroup (8 waves) owns one (batch, KV head, query-head subgroup,
-//    sequence segment) and walks its segment block by block.  The float32
-//    state lives in VGPRs for the whole walk: wave w owns columns
-//    [16w, 16w+16) of S as eight 16x16 MFMA accumulator tiles.
+//  * One workgroup owns one (batch, KV head, query-head subgroup, sequence
+//    segment) and walks its segment block by block.  The float32 state lives
+//    in VGPRs for the whole walk as 16x16 MFMA accumulator tiles, each wave
+//    owning a slice of its columns.
 //  * All products run on v_mfma_f32_16x16x32_bf16 with float32 accumulation.
 //    Every product is computed transposed (O^T, P^T = K Q^T) so that the
 //    accumulator layout of one product is directly the operand layout of the
@@ -26,13 +26,18 @@
 //    V^T P^T) read their operands with the gfx950 LDS transpose load
 //    (ds_read_b64_tr_b16), so nothing is transposed in memory.
 //  * Q goes straight from HBM into operand registers (each Q row is read by
-//    exactly one wave); K, V and the bf16 state are double-buffered in LDS so
-//    one barrier per block suffices and the next block's loads are in flight
-//    while the current block computes.
+//    exactly one wave).
+//  * Two layouts.  fwd_bf16_main (eight waves, groups of one or two query
+//    heads): K, V and the bf16 state are double-buffered in LDS, one barrier
+//    per block, wave w owns state columns [16w, 16w+16).  fwd_bf16_g4 (four
+//    waves, groups of four query heads, the 128/32-head shape): one wave per
+//    query head, single-buffered LDS, described above the kernel.
 //  * The sequence split into segments needs each segment's starting state:
-//    a pre-pass sums K_b^T V_b over parts of every segment but the last, and
-//    a scan adds the parts up (s_in first, then parts in order), exact by
-//    associativity of the sums.
+//    a pre-pass (state_parts) sums K_b^T V_b over parts of every segment but
+//    the last, and a scan (scan_starts) adds the parts up (s_in first, then
+//    parts in order), exact by associativity of the sums.
+//  * fwd_noncausal_g4 serves the non-causal variant: every output row reads
+//    the total state, which the same pre-pass computes.
 #include "la_internal.h"
 #include "la_mfma.h"
 
