@@ -106,6 +106,20 @@ def _check_tensor(name, t, ndim, device):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _workspace(workspace, nbytes, device):
+    """The scratch buffer for one call: None when the call needs none, a new
+    buffer when none is given or the given one is smaller than `nbytes`, else
+    the caller's buffer, which must be a contiguous tensor on `device`."""
+    torch = _torch()
+    if nbytes == 0:
+        return None
+    if workspace is not None:
+        _check_tensor("workspace", workspace, workspace.dim() if isinstance(workspace, torch.Tensor) else 1, device)
+        if workspace.numel() * workspace.element_size() >= nbytes:
+            return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
 def workspace_bytes(B, Hq, Hkv, N, d, dv, block=64, dtype=None):
     """Bytes of scratch la_forward_ex needs on the current device."""
     torch = _torch()
@@ -155,11 +169,10 @@ def forward(q, k, v, block=64, out_dtype=None, s_in=None, return_state=False, ou
             if s_out.dtype != torch.float32 or tuple(s_out.shape) != (B, Hkv, d, dv):
                 raise ValueError("s_out must be float32 [B, Hkv, d, dv]")
         ws_bytes = int(lib.la_forward_workspace_bytes(B, Hq, Hkv, N, d, dv, block, in_code))
-        if ws_bytes > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
-            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        workspace = _workspace(workspace, ws_bytes, dev)
         stream = torch.cuda.current_stream(dev).cuda_stream
         st = lib.la_forward_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, N, d, dv, block, in_code,
-                               out_code, _ptr(s_in), _ptr(s_out), _ptr(workspace) if ws_bytes else None,
+                               out_code, _ptr(s_in), _ptr(s_out), _ptr(workspace),
                                ws_bytes, ctypes.c_void_p(stream))
     if st != LA_OK:
         raise LAError(st, "la_forward_ex")
@@ -217,13 +230,12 @@ def forward_variant(q, k, v, causal=True, feature_map="identity", normalize=Fals
                     raise ValueError(f"{name} must be float32 {list(shape)}")
         ws_bytes = int(lib.la_forward_variant_workspace_bytes(B, Hq, Hkv, N, d, dv, block, in_code, int(causal),
                                                               int(normalize)))
-        if ws_bytes > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
-            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        workspace = _workspace(workspace, ws_bytes, dev)
         stream = torch.cuda.current_stream(dev).cuda_stream
         st = lib.la_forward_variant(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, N, d, dv, block, in_code,
                                     out_code, int(causal), fmaps[feature_map], int(normalize), float(eps),
                                     _ptr(s_in), _ptr(s_out), _ptr(z_in), _ptr(z_out),
-                                    _ptr(workspace) if ws_bytes else None, ws_bytes, ctypes.c_void_p(stream))
+                                    _ptr(workspace), ws_bytes, ctypes.c_void_p(stream))
     if st != LA_OK:
         raise LAError(st, "la_forward_variant")
     if return_state:
@@ -287,12 +299,11 @@ def backward(q, k, v, grad_o, block=64, grad_dtype=None, s_in=None, grad_s_out=N
             if grad_s_in.dtype != torch.float32 or tuple(grad_s_in.shape) != (B, Hkv, d, dv):
                 raise ValueError("grad_s_in must be float32 [B, Hkv, d, dv]")
         ws_bytes = int(lib.la_backward_workspace_bytes(B, Hq, Hkv, N, d, dv, block, in_code))
-        if ws_bytes > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
-            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        workspace = _workspace(workspace, ws_bytes, dev)
         stream = torch.cuda.current_stream(dev).cuda_stream
         st = lib.la_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(grad_o), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]),
                              B, Hq, Hkv, N, d, dv, block, in_code, g_code, _ptr(s_in), _ptr(grad_s_out),
-                             _ptr(grad_s_in), _ptr(workspace) if ws_bytes else None, ws_bytes,
+                             _ptr(grad_s_in), _ptr(workspace), ws_bytes,
                              ctypes.c_void_p(stream))
     if st != LA_OK:
         raise LAError(st, "la_backward")
@@ -326,6 +337,9 @@ def decode_step(S, q, k, v, out_dtype=None, out=None):
     with torch.cuda.device(dev):
         if out is None:
             out = torch.empty((B, Hq, dv), dtype=out_dtype, device=dev)
+        _check_tensor("out", out, 3, dev)
+        if out.dtype != out_dtype or tuple(out.shape) != (B, Hq, dv):
+            raise ValueError("out has the wrong dtype or shape")
         stream = torch.cuda.current_stream(dev).cuda_stream
         st = lib.la_decode_step(_ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, d, dv,
                                 _dtype_code(q.dtype), _dtype_code(out_dtype), ctypes.c_void_p(stream))
