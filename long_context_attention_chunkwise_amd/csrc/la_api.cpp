@@ -475,7 +475,7 @@ la_status check_variant_args(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int6
                              const float* z_in, const float* z_out) {
   la_status st = check_forward_shape(B, Hq, Hkv, N, d, dv, block, in_dtype, out_dtype);
   if (st != LA_OK) return st;
-  if (in_dtype != LA_BF16 || (Hq / Hkv) % 4 != 0) return LA_ERR_UNSUPPORTED;
+  if (in_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
   if ((causal != 0 && causal != 1) || (fmap != LA_FMAP_IDENTITY && fmap != LA_FMAP_RELU) ||
       (normalize != 0 && normalize != 1))
     return LA_ERR_UNSUPPORTED;

@@ -36,7 +36,7 @@
 //    a pre-pass (state_parts) sums K_b^T V_b over parts of every segment but
 //    the last, and a scan (scan_starts) adds the parts up (s_in first, then
 //    parts in order), exact by associativity of the sums.
-//  * fwd_noncausal_g4 serves the non-causal variant: every output row reads
+//  * fwd_noncausal serves the non-causal variant: every output row reads
 //    the total state, which the same pre-pass computes.
 #include "la_internal.h"
 #include "la_mfma.h"
@@ -86,12 +86,23 @@ __device__ __forceinline__ void store_kv(const KVRegs& r, uint16_t* ks, uint16_t
   }
 }
 
-template <int GW, bool OUT_F32>
+//
+// Feature-map variants (FL) as in fwd_bf16_g4: kRelu applies phi = ReLU to
+// the Q operands and to K as it enters LDS; kNorm divides output row t by
+// phi(q_t) . z_t + eps, with the in-block part of z_t from the float32 score
+// tiles the wave already holds for its rows and the earlier part from z (d
+// floats, double-buffered in LDS like the state copy; wave w accumulates
+// entries [16w, 16w+16) as K^T times a ones operand).
+template <int GW, bool OUT_F32, int FL>
 __global__ __launch_bounds__(kMainThreads, 1) void fwd_bf16_main(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     void* __restrict__ o, const float* starts, const float* s_in, float* s_out, int Hq, int Hkv, int subgroups,
-    int64_t N, int64_t nblocks, int64_t blocks_per_seg, int P) {
+    int64_t N, int64_t nblocks, int64_t blocks_per_seg, int P, const float* zstarts, const float* z_in,
+    float* z_out, float eps) {
+  constexpr bool kN = (FL & kNorm) != 0;
+  constexpr bool kR = (FL & kRelu) != 0;
   __shared__ MainSmem sm;
+  __shared__ __align__(16) float zs[2][kN ? D : 4];
 
   constexpr int WPH = 8 / GW;  // waves per query head
   constexpr int NT = 2 * GW;   // 16-column output tiles per wave
@@ -127,9 +138,20 @@ __global__ __launch_bounds__(kMainThreads, 1) void fwd_bf16_main(
     for (int i = 0; i < 4; ++i)
       sacc[dt][i] = s0 ? s0[(16 * dt + 4 * grp + i) * DV + 16 * w + l16] : 0.0f;
 
+  // normaliser sums, entries 16w + 4grp + i (every column equal)
+  floatx4 zacc = {0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (kN) {
+    const float* z0 = zstarts ? zstarts + (int64_t(bg) * P + seg) * D : (z_in ? z_in + int64_t(bg) * D : nullptr);
+    if (z0 != nullptr)
+      for (int i = 0; i < 4; ++i) zacc[i] = z0[16 * w + 4 * grp + i];
+    if (l16 == 0) *reinterpret_cast<floatx4*>(&zs[0][16 * w + 4 * grp]) = zacc;
+  }
+
   if (blk0 < blk1) {
     KVRegs kv;
     load_kv(kv, kh, vh, blk0, N, tid);
+    if constexpr (kR)
+      for (int i = 0; i < 2; ++i) kv.k[i] = relu_bf16x8(kv.k[i]);
     store_kv(kv, sm.k[0], sm.v[0], tid);
   }
   for (int dt = 0; dt < 8; ++dt)
@@ -154,6 +176,9 @@ __global__ __launch_bounds__(kMainThreads, 1) void fwd_bf16_main(
     const uint16_t* ks = sm.k[cur];
     const uint16_t* vs = sm.v[cur];
     const uint16_t* st = sm.st[cur];
+    if constexpr (kR)
+      for (int tt = 0; tt < 2; ++tt)
+        for (int ds = 0; ds < 4; ++ds) qa[tt][ds] = relu_bf16x8(qa[tt][ds]);
 
     KVRegs kvn;
     if (has_next) {
@@ -191,6 +216,35 @@ __global__ __launch_bounds__(kMainThreads, 1) void fwd_bf16_main(
     else pa[1] = causal_mask(pa[1], l16, grp);
     if (tb == 2) pb[2] = causal_mask(pb[2], l16, grp);
     else pb[3] = causal_mask(pb[3], l16, grp);
+    float inv[2];  // normaliser of rows 16ta + l16 and 16tb + l16 (kNorm only)
+    (void)inv;
+    if constexpr (kN) {
+      // this lane's share of sum_s P^T[s][t] over s <= t, plus phi(q_t) . z
+      // over this lane's 32 entries of q_t; the four lane groups then add up
+      float den[2];
+      den[0] = (pa[0][0] + pa[0][1]) + (pa[0][2] + pa[0][3]);
+      if (ta == 1) den[0] += (pa[1][0] + pa[1][1]) + (pa[1][2] + pa[1][3]);
+      den[1] = 0.0f;
+      for (int si = 0; si < 4; ++si)
+        if (si <= tb) den[1] += (pb[si][0] + pb[si][1]) + (pb[si][2] + pb[si][3]);
+      const float* zc = zs[cur];
+      for (int ds = 0; ds < 4; ++ds) {
+        const floatx4 za = *reinterpret_cast<const floatx4*>(&zc[32 * ds + 8 * grp]);
+        const floatx4 zb = *reinterpret_cast<const floatx4*>(&zc[32 * ds + 8 * grp + 4]);
+        for (int tt = 0; tt < 2; ++tt) {
+          float dsum = 0.0f;
+          for (int j = 0; j < 4; ++j)
+            dsum += float(qa[tt][ds][j]) * za[j] + float(qa[tt][ds][j + 4]) * zb[j];
+          den[tt] += dsum;
+        }
+      }
+      for (int tt = 0; tt < 2; ++tt) {
+        float x = den[tt];
+        x += __shfl_xor(x, 16);
+        x += __shfl_xor(x, 32);
+        inv[tt] = 1.0f / (x + eps);
+      }
+    }
     const floatx4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
     const bf16x8 pA0 = pack_tiles(pa[0], ta == 1 ? pa[1] : zero4);
     const bf16x8 pB0 = pack_tiles(pb[0], pb[1]);
@@ -204,6 +258,11 @@ __global__ __launch_bounds__(kMainThreads, 1) void fwd_bf16_main(
       acc[1][j] = mfma(va0, pB0, acc[1][j]);
       acc[1][j] = mfma(va1, pB1, acc[1][j]);
     }
+
+    if constexpr (kN)
+      for (int tt = 0; tt < 2; ++tt)
+        for (int j = 0; j < NT; ++j)
+          for (int i = 0; i < 4; ++i) acc[tt][j][i] *= inv[tt];
 
     // store O rows (each lane: 4 consecutive columns of one row per tile)
     for (int tt = 0; tt < 2; ++tt) {
@@ -232,8 +291,14 @@ __global__ __launch_bounds__(kMainThreads, 1) void fwd_bf16_main(
       uint16_t* stn = sm.st[cur ^ 1];
       for (int dt = 0; dt < 8; ++dt)
         *reinterpret_cast<bf16x4*>(&stn[(16 * w + l16) * ROWST + 16 * dt + 4 * grp]) = to_bf16x4(sacc[dt]);
+      if constexpr (kN) {
+        for (int p = 0; p < 2; ++p) zacc = mfma(tr_operand(ks, p, 16 * w, l16, grp), ones_bf16x8(), zacc);
+        if (l16 == 0) *reinterpret_cast<floatx4*>(&zs[cur ^ 1][16 * w + 4 * grp]) = zacc;
+      }
     }
     if (has_next) {
+      if constexpr (kR)
+        for (int i = 0; i < 2; ++i) kvn.k[i] = relu_bf16x8(kvn.k[i]);
       store_kv(kvn, sm.k[cur ^ 1], sm.v[cur ^ 1], tid);
       for (int tt = 0; tt < 2; ++tt)
         for (int ds = 0; ds < 4; ++ds) qa[tt][ds] = qn[tt][ds];
@@ -246,6 +311,9 @@ __global__ __launch_bounds__(kMainThreads, 1) void fwd_bf16_main(
     for (int dt = 0; dt < 8; ++dt)
       for (int i = 0; i < 4; ++i) so[(16 * dt + 4 * grp + i) * DV + 16 * w + l16] = sacc[dt][i];
   }
+  if constexpr (kN)
+    if (z_out != nullptr && seg == P - 1 && sub == 0 && l16 == 0)
+      for (int i = 0; i < 4; ++i) z_out[int64_t(bg) * D + 16 * w + 4 * grp + i] = zacc[i];
 }
 
 struct KV4Regs {
@@ -623,15 +691,16 @@ __global__ __launch_bounds__(256) void scan_starts(const float* __restrict__ par
 // s_in + sum over all tokens of phi(k_s)^T v_s, optionally divided by
 // phi(q_t) . z_tot + eps.  With the state fixed every block is independent:
 // a streaming product Q S_tot per query head (read q, write o) with no
-// barrier in the loop; the next block's Q operands load while the current
-// block multiplies.  Grid: B * Hkv * (G/4) * P workgroups of eight waves (two
-// per SIMD), wave w serving query head w % 4 of its group of four on query
-// tiles {2(w/4), 2(w/4) + 1} of each block.  S_tot comes in float32 from the
-// pre-pass and is rounded once to the bf16 n-major LDS layout of the causal
-// kernel's state copy.
+// barrier in the loop; the next step's Q operands load while the current
+// step multiplies.  Grid: B * Hkv * (G/GW) * P workgroups of eight waves (two
+// per SIMD) serving GW = 4, 2 or 1 query heads of a KV head's group: wave w
+// takes query head w % GW and 16-token query tiles {2(w/GW), 2(w/GW) + 1} of
+// each step of 4/GW blocks (one block for GW = 4).  S_tot comes in float32
+// from the pre-pass and is rounded once to the bf16 n-major LDS layout of the
+// causal kernel's state copy.
 // ---------------------------------------------------------------------------
-template <bool OUT_F32, int FL>
-__global__ __launch_bounds__(512, 1) void fwd_noncausal_g4(
+template <int GW, bool OUT_F32, int FL>
+__global__ __launch_bounds__(512, 1) void fwd_noncausal(
     const uint16_t* __restrict__ q, void* __restrict__ o, const float* __restrict__ stot,
     const float* __restrict__ ztot, int64_t tot_stride, float* s_out, float* z_out, int Hq, int Hkv,
     int subgroups, int64_t N, int64_t nblocks, int64_t blocks_per_seg, int P, float eps) {
@@ -642,7 +711,7 @@ __global__ __launch_bounds__(512, 1) void fwd_noncausal_g4(
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
-  const int hw = w & 3, t0 = 2 * (w >> 2);                 // head in the group, first query tile
+  const int hw = w % GW, t0 = 2 * (w / GW);               // head in the subgroup, first query tile
   const int lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
   const int seg = blockIdx.x % P;
   const int chain = blockIdx.x / P;
@@ -652,9 +721,12 @@ __global__ __launch_bounds__(512, 1) void fwd_noncausal_g4(
   const int G = Hq / Hkv;
   const int64_t blk0 = int64_t(seg) * blocks_per_seg;
   const int64_t blk1 = blk0 + blocks_per_seg < nblocks ? blk0 + blocks_per_seg : nblocks;
-  const int64_t head = int64_t(b) * Hq + int64_t(g) * G + int64_t(sub) * 4 + hw;
+  const int64_t head = int64_t(b) * Hq + int64_t(g) * G + int64_t(sub) * GW + hw;
   const uint16_t* qh = q + head * N * D;
   const int nlane = 8 * (l16 >> 2) + (l16 & 3);
+  constexpr int SB = 4 / GW;  // blocks per step
+  // tokens of this segment (a step of several blocks may run past its end)
+  const int64_t tend = GW == 4 ? N : (blk1 * C < N ? blk1 * C : N);
 
   // wave w rounds state columns [16w, 16w+16)
   const float* S = stot + int64_t(bg) * tot_stride * (D * DV);
@@ -678,14 +750,14 @@ __global__ __launch_bounds__(512, 1) void fwd_noncausal_g4(
     for (int tj = 0; tj < 2; ++tj) {
       const int64_t t = blk * C + 16 * (t0 + tj) + l16;
       for (int ds = 0; ds < 4; ++ds)
-        qa[tj][ds] = (t < N) ? ld_global16(qh + t * D + 32 * ds + 8 * grp) : zero_bf16x8();
+        qa[tj][ds] = (t < tend) ? ld_global16(qh + t * D + 32 * ds + 8 * grp) : zero_bf16x8();
     }
   };
   bf16x8 qa[2][4], qn[2][4];
   if (blk0 < blk1) load_q(qa, blk0);
   const floatx4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int64_t blk = blk0; blk < blk1; ++blk) {
-    if (blk + 1 < blk1) load_q(qn, blk + 1);
+  for (int64_t blk = blk0; blk < blk1; blk += SB) {
+    if (blk + SB < blk1) load_q(qn, blk + SB);
     if constexpr (kR)
       for (int tj = 0; tj < 2; ++tj)
         for (int ds = 0; ds < 4; ++ds) qa[tj][ds] = relu_bf16x8(qa[tj][ds]);
@@ -722,7 +794,7 @@ __global__ __launch_bounds__(512, 1) void fwd_noncausal_g4(
             for (int i = 0; i < 4; ++i) acc[h2][tj][i] *= inv[tj];
       for (int tj = 0; tj < 2; ++tj) {
         const int64_t t = blk * C + 16 * (t0 + tj) + l16;
-        if (t < N) {
+        if (t < tend) {
           const int64_t off = (head * N + t) * DV + 32 * m + 8 * grp;
           if (OUT_F32) {
             float* op = static_cast<float*>(o) + off;
@@ -749,14 +821,15 @@ void launch_g4(dim3 grid, hipStream_t stream, const void* q, const void* k, cons
                      Hkv, subgroups, N, nblocks, bps, P, zstarts, z_in, z_out, eps);
 }
 
-template <int GW, bool OUT_F32>
+template <int GW, bool OUT_F32, int FL = 0>
 void launch_main(dim3 grid, hipStream_t stream, const void* q, const void* k, const void* v, void* o,
                  const float* starts, const float* s_in, float* s_out, int Hq, int Hkv, int subgroups, int64_t N,
-                 int64_t nblocks, int64_t bps, int P) {
-  hipLaunchKernelGGL((fwd_bf16_main<GW, OUT_F32>), grid, dim3(kMainThreads), 0, stream,
+                 int64_t nblocks, int64_t bps, int P, const float* zstarts = nullptr, const float* z_in = nullptr,
+                 float* z_out = nullptr, float eps = 0.0f) {
+  hipLaunchKernelGGL((fwd_bf16_main<GW, OUT_F32, FL>), grid, dim3(kMainThreads), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), o, starts, s_in, s_out, Hq, Hkv, subgroups, N, nblocks, bps,
-                     P);
+                     P, zstarts, z_in, z_out, eps);
 }
 
 }  // namespace
@@ -830,16 +903,27 @@ hipError_t variant_outputs(const void* q, const void* k, const void* v, void* o,
   if (vp.causal) {
     const dim3 grid(unsigned(B * Hkv * p.subgroups * p.P));
     const bool st = p.use_starts;
-    launch_g4<OUT_F32, FL>(grid, stream, q, k, v, o, st ? starts : nullptr, st ? nullptr : s_in, s_out, iHq, iHkv,
-                           p.subgroups, N, p.nblocks, p.blocks_per_seg, p.P,
-                           (FL & kNorm) && st ? zstarts : nullptr, (FL & kNorm) && !st ? z_in : nullptr, z_out, eps);
+    const float* zs = (FL & kNorm) && st ? zstarts : nullptr;
+    const float* zi = (FL & kNorm) && !st ? z_in : nullptr;
+#define LA_VAR(LAUNCH)                                                                                              \
+  LAUNCH(grid, stream, q, k, v, o, st ? starts : nullptr, st ? nullptr : s_in, s_out, iHq, iHkv, p.subgroups, N, \
+         p.nblocks, p.blocks_per_seg, p.P, zs, zi, z_out, eps)
+    if (p.gw == 4) LA_VAR((launch_g4<OUT_F32, FL>));
+    else if (p.gw == 2) LA_VAR((launch_main<2, OUT_F32, FL>));
+    else LA_VAR((launch_main<1, OUT_F32, FL>));
+#undef LA_VAR
   } else {
     // totals sit at entry P of each chain's P + 1 scanned entries
     const int64_t stride = p.P + 1;
     const dim3 grid(unsigned(B * Hkv * p.subgroups * vp.P_out));
-    hipLaunchKernelGGL((fwd_noncausal_g4<OUT_F32, FL>), grid, dim3(512), 0, stream, static_cast<const uint16_t*>(q),
-                       o, starts + p.P * (D * DV), zstarts + p.P * D, stride, s_out, z_out, iHq, iHkv, p.subgroups,
-                       N, p.nblocks, vp.bps_out, vp.P_out, eps);
+#define LA_NC(GW)                                                                                                   \
+  hipLaunchKernelGGL((fwd_noncausal<GW, OUT_F32, FL>), grid, dim3(512), 0, stream, static_cast<const uint16_t*>(q), o, \
+                     starts + p.P * (D * DV), zstarts + p.P * D, stride, s_out, z_out, iHq, iHkv, p.subgroups, N,    \
+                     p.nblocks, vp.bps_out, vp.P_out, eps)
+    if (p.gw == 4) LA_NC(4);
+    else if (p.gw == 2) LA_NC(2);
+    else LA_NC(1);
+#undef LA_NC
   }
   return hipGetLastError();
 }

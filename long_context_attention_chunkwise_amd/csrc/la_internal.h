@@ -55,8 +55,8 @@ hipError_t launch_state_parts(const void* a, const void* b, float* partial, int6
                               int64_t nblocks, int64_t blocks_per_seg, int64_t blocks_per_part, int P, int R,
                               int seg_offset, hipStream_t stream);
 
-// Forward variants (feature map, non-causal, normalised), bf16 inputs and
-// groups of four query heads.  Causal: the forward's split, with the
+// Forward variants (feature map, non-causal, normalised), bf16 inputs, any
+// query-head group size.  Causal: the forward's split, with the
 // normaliser sums carried beside the state.  Non-causal: the pre-pass sums
 // every segment (the scan's last entry is the total) and the output kernel
 // splits each chain into P_out segments of bps_out blocks.

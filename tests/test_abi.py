@@ -118,7 +118,7 @@ def var(lib, q=Q, k=K, v=V, o=O, B=1, Hq=4, Hkv=1, N=1000, d=128, dv=128, block=
 def test_variant_validation(lib):
     assert var(lib, q=None) == NULL
     assert var(lib, Hq=6, Hkv=4) == SHAPE
-    assert var(lib, Hq=2, Hkv=1) == UNSUP                 # groups of four query heads only
+    assert var(lib, d=64, dv=64) == UNSUP                 # bf16 path: d = dv = 128
     assert var(lib, i=F32, out=F32) == UNSUP              # bf16 inputs only
     assert var(lib, fmap=2) == UNSUP
     assert var(lib, causal=2) == UNSUP

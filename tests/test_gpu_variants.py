@@ -43,6 +43,13 @@ CASES = [
     (1, "relu", 1, 0.0, True, True, torch.float32, 1, 8, 1, 2500, False),    # G = 8, causal
     (1, "relu", 1, 1e-6, True, True, torch.float32, 1, 8, 2, 100, False),    # one segment: s_in/z_in read directly
     (0, "relu", 1, 1e-6, True, True, torch.float32, 1, 8, 2, 1, False),      # one token
+    # groups of 1, 2 and 3 query heads (eight-wave causal kernel; non-causal steps of 4/GW blocks)
+    (1, "relu", 1, 1e-6, True, True, torch.float32, 2, 8, 8, 3000, False),   # G = 1
+    (1, "relu", 0, 0.0, False, False, BF16, 1, 4, 2, 2500, False),           # G = 2
+    (1, "identity", 1, 0.0, False, False, torch.float32, 1, 6, 2, 1200, True),  # G = 3
+    (0, "identity", 0, 0.0, True, False, BF16, 2, 4, 4, 2900, False),        # G = 1: segments of 2 blocks, steps of 4
+    (0, "relu", 0, 0.0, False, False, torch.float32, 1, 4, 2, 777, False),   # G = 2
+    (0, "relu", 1, 1e-3, True, True, torch.float32, 1, 6, 2, 1500, False),   # G = 3
 ]
 
 
@@ -67,11 +74,13 @@ def test_variant_matches_oracle(causal, fmap, norm, eps, use_s, use_z, out_dtype
         check_close("z_out", f64(Z), ref_z, BF16, torch.float32)
 
 
-def test_plain_variant_is_the_forward():
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (4, 2), (3, 3)])
+def test_plain_variant_is_the_forward(Hq, Hkv):
     """causal, identity map, no normalisation: bit for bit la_forward_ex."""
     need_gpu()
-    q, k, v = inputs(1, 8, 2, 5000, seed=5)
-    S0 = synth.random_state((1, 2, 128, 128), DEV, seed=6, scale=0.5)
+    say(f"case plain variant = forward, Hq={Hq} Hkv={Hkv}")
+    q, k, v = inputs(1, Hq, Hkv, 5000, seed=5)
+    S0 = synth.random_state((1, Hkv, 128, 128), DEV, seed=6, scale=0.5)
     a, Sa, _ = la.forward_variant(q, k, v, s_in=S0, return_state=True)
     b, Sb = la.forward(q, k, v, s_in=S0, return_state=True)
     torch.cuda.synchronize()
