@@ -757,6 +757,10 @@ __global__ __launch_bounds__(512, 1) void fwd_noncausal(
   if (blk0 < blk1) load_q(qa, blk0);
   const floatx4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int64_t blk = blk0; blk < blk1; blk += SB) {
+    // The state operands are re-read from LDS every step rather than held in
+    // registers across the loop: holding them leaves the normalised forms too
+    // few registers (they spill) and measured no faster for the others.
+    asm volatile("" ::: "memory");
     if (blk + SB < blk1) load_q(qn, blk + SB);
     if constexpr (kR)
       for (int tj = 0; tj < 2; ++tj)
