@@ -144,8 +144,10 @@ size_t la_forward_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
  *     o[b][h] = q[b][h] . S[b][g]                     (reads the updated state)
  * so the new token attends to itself, as in the forward pass.
  *   in_dtype  LA_BF16 or LA_F32 (q, k, v); out_dtype LA_F32 or LA_BF16 (o).
- *   d in 1..128, dv a multiple of 4 up to 128.  Arithmetic is float32.
- * Each state is read once and written once per call.
+ *   d in 1..128, dv a multiple of 4 up to 128, Hq / Hkv up to 1024.
+ *   Arithmetic is float32.
+ * Each state is read once and written once per call; groups of more than 8
+ * query heads per KV head read it once more for every further 8 heads.
  */
 la_status la_decode_step(float* S, const void* q, const void* k, const void* v, void* o,
                          int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int64_t dv,

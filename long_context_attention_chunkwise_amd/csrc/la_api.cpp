@@ -351,7 +351,7 @@ la_status la_decode_step(float* S, const void* q, const void* k, const void* v, 
                          la_stream stream) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || dv <= 0 || Hq % Hkv != 0) return LA_ERR_SHAPE;
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return LA_ERR_UNSUPPORTED;
-  if (d > 128 || dv > 128 || dv % 4 != 0 || Hq / Hkv > 8 || B * Hkv > (int64_t(1) << 30))
+  if (d > 128 || dv > 128 || dv % 4 != 0 || B * Hkv > (int64_t(1) << 30) || Hq / Hkv > 1024)
     return LA_ERR_UNSUPPORTED;
   if (S == nullptr || q == nullptr || k == nullptr || v == nullptr || o == nullptr) return LA_ERR_NULL;
   if (!aligned16(S) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return LA_ERR_ALIGN;

@@ -10,7 +10,11 @@
 // registers on the way (one pass, no second read of S).
 //
 // One workgroup of 512 threads per state (measured against 128, 256 and 1024
-// at d = dv = 128: 512 streams fastest).  Thread (row group rg, column group
+// at d = dv = 128: 512 streams fastest).  Groups of more than eight query
+// heads are served in chunks of eight: the first launch updates the state and
+// serves the first chunk, each further launch re-reads the updated state
+// without writing it and serves the next chunk (stream order keeps them in
+// sequence).  Thread (row group rg, column group
 // cg) owns columns [4cg, 4cg+4) of rows rg, rg + nrg, ...: a wave reads whole
 // 512-byte rows with 16-byte accesses.  Per-thread partial products over its
 // rows are reduced across row groups through LDS in a fixed order, so results
@@ -23,6 +27,7 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kMaxD = 128;
 constexpr int kMaxDV = 128;
+constexpr int kMaxChunk = 8;  // query heads per launch
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -47,10 +52,14 @@ __device__ __forceinline__ float load_in(const void* p, int64_t i) {
   return static_cast<const float*>(p)[i];
 }
 
-template <int G, bool IN_BF16, bool OUT_F32>
+// G: query heads served by this launch.  CHUNKED: one chunk [h0, h0 + G) of a
+// larger group of Gfull heads (otherwise the whole group, Gfull = G, h0 = 0);
+// UPDATE: add k^T v to the state and write it back (otherwise read only).
+template <int G, bool IN_BF16, bool OUT_F32, bool CHUNKED, bool UPDATE>
 __global__ __launch_bounds__(kThreads) void decode_kernel(float* __restrict__ S, const void* __restrict__ q,
                                                          const void* __restrict__ k, const void* __restrict__ v,
-                                                         void* __restrict__ o, int Hkv, int d, int dv) {
+                                                         void* __restrict__ o, int Hkv, int d, int dv, int Gfull,
+                                                         int h0) {
   __shared__ float qs[G][kMaxD];
   __shared__ float ks[kMaxD];
   __shared__ float vs[kMaxDV];
@@ -58,9 +67,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(float* __restrict__ S,
 
   const int bg = blockIdx.x;  // b * Hkv + g
   const int tid = threadIdx.x;
-  const int64_t hq0 = int64_t(bg) * G;  // first query head of the group, flattened over batch
-  for (int i = tid; i < d; i += kThreads) ks[i] = load_in<IN_BF16>(k, int64_t(bg) * d + i);
-  for (int i = tid; i < dv; i += kThreads) vs[i] = load_in<IN_BF16>(v, int64_t(bg) * dv + i);
+  // first query head served, flattened over batch
+  const int64_t hq0 = CHUNKED ? int64_t(bg) * Gfull + h0 : int64_t(bg) * G;
+  if (UPDATE) {
+    for (int i = tid; i < d; i += kThreads) ks[i] = load_in<IN_BF16>(k, int64_t(bg) * d + i);
+    for (int i = tid; i < dv; i += kThreads) vs[i] = load_in<IN_BF16>(v, int64_t(bg) * dv + i);
+  }
   for (int i = tid; i < G * d; i += kThreads) qs[i / d][i % d] = load_in<IN_BF16>(q, hq0 * d + i);
   __syncthreads();
 
@@ -72,16 +84,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(float* __restrict__ S,
 
   if (rg < nrg) {
     float4* Sg = reinterpret_cast<float4*>(S + int64_t(bg) * d * dv);
-    const float4 v4 = make_float4(vs[4 * cg], vs[4 * cg + 1], vs[4 * cg + 2], vs[4 * cg + 3]);
+    const float4 v4 = UPDATE ? make_float4(vs[4 * cg], vs[4 * cg + 1], vs[4 * cg + 2], vs[4 * cg + 3])
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 8
     for (int r = rg; r < d; r += nrg) {
       float4 s = load_stream(&Sg[r * ncg + cg]);
-      const float kr = ks[r];
-      s.x = fmaf(kr, v4.x, s.x);
-      s.y = fmaf(kr, v4.y, s.y);
-      s.z = fmaf(kr, v4.z, s.z);
-      s.w = fmaf(kr, v4.w, s.w);
-      store_stream(&Sg[r * ncg + cg], s);
+      if (UPDATE) {
+        const float kr = ks[r];
+        s.x = fmaf(kr, v4.x, s.x);
+        s.y = fmaf(kr, v4.y, s.y);
+        s.z = fmaf(kr, v4.z, s.z);
+        s.w = fmaf(kr, v4.w, s.w);
+        store_stream(&Sg[r * ncg + cg], s);
+      }
       for (int h = 0; h < G; ++h) {
         const float qr = qs[h][r];
         acc[h].x = fmaf(qr, s.x, acc[h].x);
@@ -119,19 +134,38 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(float* __restrict__ S,
   }
 }
 
-template <int G>
+template <int G, bool CHUNKED, bool UPDATE>
 hipError_t launch_g(float* S, const void* q, const void* k, const void* v, void* o, bool in_bf16, bool out_f32,
-                    int64_t B, int64_t Hkv, int64_t d, int64_t dv, hipStream_t stream) {
+                    int64_t B, int64_t Hkv, int64_t d, int64_t dv, int Gfull, int h0, hipStream_t stream) {
   const dim3 grid(unsigned(B * Hkv)), block(kThreads);
   const int iHkv = int(Hkv), id = int(d), idv = int(dv);
+#define LA_DEC(BF, F32)                                                                                          \
+  hipLaunchKernelGGL((decode_kernel<G, BF, F32, CHUNKED, UPDATE>), grid, block, 0, stream, S, q, k, v, o, iHkv, id, \
+                     idv, Gfull, h0)
   if (in_bf16) {
-    if (out_f32) hipLaunchKernelGGL((decode_kernel<G, true, true>), grid, block, 0, stream, S, q, k, v, o, iHkv, id, idv);
-    else hipLaunchKernelGGL((decode_kernel<G, true, false>), grid, block, 0, stream, S, q, k, v, o, iHkv, id, idv);
+    if (out_f32) LA_DEC(true, true);
+    else LA_DEC(true, false);
   } else {
-    if (out_f32) hipLaunchKernelGGL((decode_kernel<G, false, true>), grid, block, 0, stream, S, q, k, v, o, iHkv, id, idv);
-    else hipLaunchKernelGGL((decode_kernel<G, false, false>), grid, block, 0, stream, S, q, k, v, o, iHkv, id, idv);
+    if (out_f32) LA_DEC(false, true);
+    else LA_DEC(false, false);
   }
+#undef LA_DEC
   return hipGetLastError();
+}
+
+// The first chunk of a group of more than eight heads (state update) or a
+// later one (read only), of g heads starting at h0.
+template <bool UPDATE>
+hipError_t launch_chunk(int g, float* S, const void* q, const void* k, const void* v, void* o, bool in_bf16,
+                        bool out_f32, int64_t B, int64_t Hkv, int64_t d, int64_t dv, int Gfull, int h0,
+                        hipStream_t stream) {
+  switch (g) {
+#define LA_C(N)                                                                                                 \
+  case N: return launch_g<N, true, UPDATE>(S, q, k, v, o, in_bf16, out_f32, B, Hkv, d, dv, Gfull, h0, stream);
+    LA_C(1) LA_C(2) LA_C(3) LA_C(4) LA_C(5) LA_C(6) LA_C(7) LA_C(8)
+#undef LA_C
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -139,15 +173,21 @@ hipError_t launch_g(float* S, const void* q, const void* k, const void* v, void*
 hipError_t launch_decode(float* S, const void* q, const void* k, const void* v, void* o, bool in_bf16,
                          bool out_f32, int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int64_t dv,
                          hipStream_t stream) {
-  switch (Hq / Hkv) {
-    case 1: return launch_g<1>(S, q, k, v, o, in_bf16, out_f32, B, Hkv, d, dv, stream);
-    case 2: return launch_g<2>(S, q, k, v, o, in_bf16, out_f32, B, Hkv, d, dv, stream);
-    case 3: return launch_g<3>(S, q, k, v, o, in_bf16, out_f32, B, Hkv, d, dv, stream);
-    case 4: return launch_g<4>(S, q, k, v, o, in_bf16, out_f32, B, Hkv, d, dv, stream);
-    case 5: return launch_g<5>(S, q, k, v, o, in_bf16, out_f32, B, Hkv, d, dv, stream);
-    case 6: return launch_g<6>(S, q, k, v, o, in_bf16, out_f32, B, Hkv, d, dv, stream);
-    case 7: return launch_g<7>(S, q, k, v, o, in_bf16, out_f32, B, Hkv, d, dv, stream);
-    case 8: return launch_g<8>(S, q, k, v, o, in_bf16, out_f32, B, Hkv, d, dv, stream);
+  const int64_t G = Hq / Hkv;
+  if (G > kMaxChunk) {
+    const int Gf = int(G);
+    hipError_t e = launch_chunk<true>(kMaxChunk, S, q, k, v, o, in_bf16, out_f32, B, Hkv, d, dv, Gf, 0, stream);
+    for (int h0 = kMaxChunk; e == hipSuccess && h0 < Gf; h0 += kMaxChunk) {
+      const int g = Gf - h0 < kMaxChunk ? Gf - h0 : kMaxChunk;
+      e = launch_chunk<false>(g, S, q, k, v, o, in_bf16, out_f32, B, Hkv, d, dv, Gf, h0, stream);
+    }
+    return e;
+  }
+  switch (G) {
+#define LA_G(N) \
+  case N: return launch_g<N, false, true>(S, q, k, v, o, in_bf16, out_f32, B, Hkv, d, dv, N, 0, stream);
+    LA_G(1) LA_G(2) LA_G(3) LA_G(4) LA_G(5) LA_G(6) LA_G(7) LA_G(8)
+#undef LA_G
     default: return hipErrorInvalidValue;
   }
 }

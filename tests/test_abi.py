@@ -80,7 +80,7 @@ def test_decode_validation(lib):
     assert dec(S=None) == NULL
     assert dec(Hq=6, Hkv=4) == SHAPE
     assert dec(dv=126) == UNSUP
-    assert dec(Hq=18, Hkv=2) == UNSUP                     # more than 8 query heads per KV head
+    assert dec(Hq=2050, Hkv=2) == UNSUP                   # more than 1024 query heads per KV head
     assert dec(o=ctypes.c_void_p(GB * 4 + 2)) == ALIGN
     assert dec(o=ctypes.c_void_p(GB * 5 + 16)) == ALIAS   # o inside S
 

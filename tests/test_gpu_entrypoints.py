@@ -105,6 +105,9 @@ def test_rejected_call_writes_nothing():
     (4, 64, 96, torch.float32, torch.float32),
     (8, 128, 128, torch.bfloat16, torch.float32),
     (3, 100, 36, torch.float32, torch.bfloat16),
+    (12, 128, 128, torch.bfloat16, torch.float32),   # groups above 8: chunks of 8 + 4
+    (17, 128, 64, torch.bfloat16, torch.bfloat16),   # 8 + 8 + 1
+    (32, 64, 64, torch.float32, torch.float32),      # four chunks of 8
 ])
 def test_decode_variants(G, d, dv, in_dtype, out_dtype):
     """20 decode steps on a random initial state against the oracle's decode_step."""
