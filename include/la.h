@@ -210,16 +210,20 @@ size_t la_forward_variant_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, in
  * the first with a float32 d x dv state that starts at grad_s_out.
  *
  *   q, k, v        the forward's inputs (layouts as above).
- *   grad_o         [B][Hq][N][dv], in_dtype.  in_dtype must be LA_BF16.
- *   grad_q, grad_k, grad_v   outputs shaped like q, k, v, in grad_dtype
- *                  (LA_BF16 or LA_F32); every element is written.
+ *   grad_o         [B][Hq][N][dv], in_dtype.
+ *   in_dtype       LA_BF16: matrix-core kernels, d = dv = 128, block = 64,
+ *                  grad_dtype LA_BF16 or LA_F32.  LA_F32: float32 FMA
+ *                  kernels (a small-problem path), d and dv multiples of 32
+ *                  up to 128, block up to 64, grad_dtype LA_F32.
+ *   grad_q, grad_k, grad_v   outputs shaped like q, k, v, in grad_dtype;
+ *                  every element is written.
  *   s_in           the forward's initial state, or NULL for zeros (used for dq).
  *   grad_s_out     [B][Hkv][d][dv] float32 gradient on the forward's final
  *                  state, or NULL for zeros.
  *   grad_s_in      [B][Hkv][d][dv] float32 output, or NULL.  May equal
  *                  grad_s_out (in place); no other output may overlap an
  *                  input or another output (LA_ERR_ALIAS).
- *   d = dv = 128, block = 64.  N may be 0 (then only grad_s_in is written).
+ *   N may be 0 (then only grad_s_in is written).
  *   workspace / workspace_bytes: at least la_backward_workspace_bytes(...)
  *                  bytes of device memory, scratch, not shared by concurrent
  *                  calls.

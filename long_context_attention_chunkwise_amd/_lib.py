@@ -254,8 +254,9 @@ def backward(q, k, v, grad_o, block=64, grad_dtype=None, s_in=None, grad_s_out=N
              out=None, grad_s_in=None, workspace=None):
     """Gradients of the forward pass (la_backward).
 
-    q, k, v and grad_o = dL/do (bfloat16, shaped like the forward's inputs
-    and output).  Returns (dq, dk, dv) in grad_dtype (default bfloat16) and,
+    q, k, v and grad_o = dL/do (bfloat16 or float32, shaped like the
+    forward's inputs and output).  Returns (dq, dk, dv) in grad_dtype (default
+    the input dtype; float32 inputs take float32 gradients) and,
     with return_state_grad (or a grad_s_in buffer), the float32 gradient on
     the initial state as a fourth item.  s_in is the forward's initial state;
     grad_s_out an optional float32 gradient on its final state.  `out` may
@@ -276,7 +277,7 @@ def backward(q, k, v, grad_o, block=64, grad_dtype=None, s_in=None, grad_s_out=N
         raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}, "
                          f"grad_o {tuple(grad_o.shape)}")
     in_code = _dtype_code(q.dtype)
-    grad_dtype = torch.bfloat16 if grad_dtype is None else grad_dtype
+    grad_dtype = q.dtype if grad_dtype is None else grad_dtype
     g_code = _dtype_code(grad_dtype)
     for name, t in (("s_in", s_in), ("grad_s_out", grad_s_out)):
         if t is not None:

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "liblightning.so")
-SOURCES = ["la_api.cpp", "la_fwd_f32.hip", "la_fwd_bf16.hip", "la_bwd_bf16.hip", "la_decode.hip"]
+SOURCES = ["la_api.cpp", "la_fwd_f32.hip", "la_fwd_bf16.hip", "la_bwd_bf16.hip", "la_bwd_f32.hip", "la_decode.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 instructions stay disabled: every float operation is scalar.

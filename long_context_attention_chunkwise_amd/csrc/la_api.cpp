@@ -375,8 +375,14 @@ la_status check_backward_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, in
                                int64_t block, la_dtype in_dtype, la_dtype grad_dtype) {
   la_status st = check_forward_shape(B, Hq, Hkv, N, d, dv, block, in_dtype, grad_dtype);
   if (st != LA_OK) return st;
-  if (in_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
+  // float32: dK is computed in 32-column slices of d (dv is already a multiple of 32)
+  if (in_dtype == LA_F32 && d % 32 != 0) return LA_ERR_UNSUPPORTED;
   return LA_OK;
+}
+
+size_t backward_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv, la_dtype in_dtype) {
+  if (in_dtype == LA_F32) return la::bwd_f32_workspace_floats(B, Hkv, d, dv) * sizeof(float);
+  return la::plan_backward(B, Hq, Hkv, N, d, dv, device_cus()).workspace_bytes;
 }
 
 }  // namespace
@@ -386,7 +392,7 @@ extern "C" {
 size_t la_backward_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv,
                                    int64_t block, la_dtype in_dtype) {
   if (check_backward_shape(B, Hq, Hkv, N, d, dv, block, in_dtype, in_dtype) != LA_OK || N == 0) return 0;
-  return la::plan_backward(B, Hq, Hkv, N, d, dv, device_cus()).workspace_bytes;
+  return backward_workspace(B, Hq, Hkv, N, d, dv, in_dtype);
 }
 
 la_status la_backward(const void* q, const void* k, const void* v, const void* grad_o, void* grad_q,
@@ -434,14 +440,23 @@ la_status la_backward(const void* q, const void* k, const void* v, const void* g
                                                                                                   : LA_ERR_HIP;
   }
 
-  const la::BwdPlan plan = la::plan_backward(B, Hq, Hkv, N, d, dv, device_cus());
-  const size_t nw = plan.workspace_bytes;
+  const size_t nw = backward_workspace(B, Hq, Hkv, N, d, dv, in_dtype);
   if (workspace == nullptr || workspace_bytes < nw) return LA_ERR_WORKSPACE;
   for (const Range& in : inputs)
     if (overlap(workspace, nw, in.p, in.n)) return LA_ERR_ALIAS;
   for (const Range& out : outputs)
     if (overlap(workspace, nw, out.p, out.n)) return LA_ERR_ALIAS;
 
+  if (in_dtype == LA_F32)
+    return la::launch_bwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                              static_cast<const float*>(v), static_cast<const float*>(grad_o),
+                              static_cast<float*>(grad_q), static_cast<float*>(grad_k), static_cast<float*>(grad_v),
+                              s_in, grad_s_out, grad_s_in, B, Hq, Hkv, N, d, dv, block,
+                              static_cast<float*>(workspace), hs) == hipSuccess
+               ? LA_OK
+               : LA_ERR_HIP;
+
+  const la::BwdPlan plan = la::plan_backward(B, Hq, Hkv, N, d, dv, device_cus());
   float* ws = static_cast<float*>(workspace);
   float* ws_fwd = ws;
   float* sin_t = ws_fwd + plan.fwd_floats;

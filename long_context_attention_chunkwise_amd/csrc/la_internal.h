@@ -108,6 +108,16 @@ hipError_t launch_bwd_kv(const void* q, const void* k, const void* v, const void
                          bool out_f32, const float* ds_out, float* ds_in, int64_t B, int64_t Hq, int64_t Hkv,
                          int64_t N, const BwdPlan& plan, float* workspace_f, hipStream_t stream);
 
+// float32 backward (float32 inputs and gradients, d and dv multiples of 32 up
+// to 128, blocks of up to 64 tokens): dQ by the float32 forward over
+// (dO, V, K) from s_in^T, then dK and dV (and ds_in) by the reverse
+// recurrence.  The workspace holds s_in^T (bwd_f32_workspace_floats floats).
+size_t bwd_f32_workspace_floats(int64_t B, int64_t Hkv, int64_t d, int64_t dv);
+hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* dout, float* dq, float* dk,
+                          float* dvg, const float* s_in, const float* ds_out, float* ds_in, int64_t B, int64_t Hq,
+                          int64_t Hkv, int64_t N, int64_t d, int64_t dv, int64_t block, float* workspace,
+                          hipStream_t stream);
+
 // dst[i] = src ? src[i] : 0 for i < n.
 hipError_t launch_copy_or_zero(float* dst, const float* src, size_t n, hipStream_t stream);
 

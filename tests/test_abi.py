@@ -96,7 +96,10 @@ def test_backward_validation(lib):
     assert bwd(lib, dk=None) == NULL
     assert bwd(lib, Hq=6, Hkv=4) == SHAPE
     assert bwd(lib, N=-1) == SHAPE
-    assert bwd(lib, i=F32, g=F32) == UNSUP                 # bf16 inputs only
+    assert bwd(lib, i=F32, g=BF16) == UNSUP                # float32 inputs take float32 gradients
+    assert bwd(lib, i=F32, g=F32, d=48, dvs=64) == UNSUP   # float32: d a multiple of 32
+    assert bwd(lib, i=F32, g=F32, d=64, dvs=64, block=128) == UNSUP   # float32: blocks of up to 64
+    assert bwd(lib, i=F32, g=F32, d=64, dvs=64, ws=None) == WORKSPACE
     assert bwd(lib, d=64) == UNSUP
     assert bwd(lib, g=2) == UNSUP
     assert bwd(lib, dq=ctypes.c_void_p(GB * 9 + 8)) == ALIGN
@@ -151,7 +154,8 @@ def test_workspace_plan(lib):
     n = lib.la_backward_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, 64, BF16)
     assert n == ((32 * 7 * 3 + 32 * 8) + 32 + 128 * 7 * 6 + 32 * 8) * 128 * 128 * 4
     assert lib.la_backward_workspace_bytes(1, 128, 32, 0, 128, 128, 64, BF16) == 0
-    assert lib.la_backward_workspace_bytes(1, 4, 2, 64, 128, 128, 64, F32) == 0
+    assert lib.la_backward_workspace_bytes(1, 4, 2, 64, 128, 96, 64, F32) == 2 * 128 * 96 * 4   # s_in^T
+    assert lib.la_backward_workspace_bytes(1, 4, 2, 64, 48, 96, 64, F32) == 0                  # d not a multiple of 32
     # Variants at 1M tokens: causal = the forward's split (+ normaliser sums);
     # non-causal sums all 8 segments of each chain (3 parts each) and scans
     # 9 entries, the last being the total.

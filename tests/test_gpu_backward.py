@@ -151,3 +151,45 @@ def test_backward_gqa_1m_slices():
         check_close(f"group {g} dv tokens [0, {W})", f64(dv[:, gs, :W]), head[2], BF16, BF16)
         check_close(f"group {g} dq tokens [0, {W})", f64(dq[:, hs, :W]), head[0], BF16, BF16)
         check_close(f"group {g} ds_in", f64(ds[:, gs]), head[3], BF16, torch.float32)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,dv,block,state", [
+    (1, 3, 1, 300, 64, 64, 64, True),      # G = 3, ragged tail, both state terms
+    (2, 3, 3, 130, 128, 96, 32, False),    # G = 1, d != dv, 32-token blocks
+    (1, 8, 2, 257, 32, 128, 16, True),     # G = 4, 16-token blocks
+    (1, 4, 1, 1, 64, 64, 64, True),        # one token
+])
+def test_backward_f32_matches_oracle(B, Hq, Hkv, N, d, dv, block, state):
+    """float32 inputs and gradients (the float32 FMA kernels) against the
+    oracle at the float32 bar, 1e-5 of each gradient's RMS."""
+    need_gpu()
+    say(f"case backward f32 B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} dv={dv} block={block} state={state}")
+    w = synth.Workload("t", B, Hq, Hkv, N, d, dv, block, torch.float32, False, True)
+    q, k, v = synth.make_qkv(w, DEV, seed=N + d)
+    do = synth.make_grad((B, Hq, N, dv), DEV, seed=N + d + 1, dtype=torch.float32)
+    S0 = synth.random_state((B, Hkv, d, dv), DEV, seed=N + 21, scale=0.5) if state else None
+    dS = synth.random_state((B, Hkv, d, dv), DEV, seed=N + 22, scale=0.5) if state else None
+    got = la.backward(q, k, v, do, block=block, s_in=S0, grad_s_out=dS, return_state_grad=True)
+    torch.cuda.synchronize()
+    assert all(g.dtype == torch.float32 for g in got)
+    ref = oracle.backward_chunkwise(f64(q), f64(k), f64(v), f64(do), block, None if S0 is None else f64(S0),
+                                    None if dS is None else f64(dS))
+    for name, g, r in zip(("dq", "dk", "dv", "ds_in"), got, ref):
+        check_close(f"f32 {name}", f64(g), r, torch.float32, torch.float32)
+
+
+def test_backward_f32_in_place_state_gradient():
+    """float32: grad_s_in written over grad_s_out gives the same gradients."""
+    need_gpu()
+    say("case backward f32 in place ds")
+    w = synth.Workload("t", 1, 4, 2, 200, 64, 96, 64, torch.float32, False, True)
+    q, k, v = synth.make_qkv(w, DEV, seed=31)
+    do = synth.make_grad((1, 4, 200, 96), DEV, seed=32, dtype=torch.float32)
+    dS = synth.random_state((1, 2, 64, 96), DEV, seed=33, scale=0.5)
+    ref = la.backward(q, k, v, do, grad_s_out=dS, return_state_grad=True)
+    buf = dS.clone()
+    got = la.backward(q, k, v, do, grad_s_out=buf, grad_s_in=buf)
+    torch.cuda.synchronize()
+    for a, b in zip(ref[:3], got[:3]):
+        assert torch.equal(a, b)
+    assert torch.equal(ref[3], buf)
