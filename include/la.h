@@ -172,7 +172,9 @@ la_status la_decode_step(float* S, const void* q, const void* k, const void* v, 
  *   z_in, z_out   [B][Hkv][d] float32 normaliser sums, or NULL; only with
  *                 normalize = 1 (LA_ERR_UNSUPPORTED otherwise).  z_out may
  *                 equal z_in.
- * in_dtype LA_BF16, d = dv = 128, block = 64, any Hq / Hkv.
+ * in_dtype LA_BF16 (matrix-core kernels: d = dv = 128, block = 64) or LA_F32
+ * (float32 FMA kernels, out_dtype LA_F32: d up to 128, dv a multiple of 32 up
+ * to 128, block up to 64; workspace size 0); any Hq / Hkv.
  * causal = 1, LA_FMAP_IDENTITY, normalize = 0 computes exactly la_forward_ex.
  * Workspace: la_forward_variant_workspace_bytes (may be 0).
  */

@@ -490,7 +490,6 @@ la_status check_variant_args(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int6
                              const float* z_in, const float* z_out) {
   la_status st = check_forward_shape(B, Hq, Hkv, N, d, dv, block, in_dtype, out_dtype);
   if (st != LA_OK) return st;
-  if (in_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
   if ((causal != 0 && causal != 1) || (fmap != LA_FMAP_IDENTITY && fmap != LA_FMAP_RELU) ||
       (normalize != 0 && normalize != 1))
     return LA_ERR_UNSUPPORTED;
@@ -510,7 +509,7 @@ size_t la_forward_variant_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, in
                                           int64_t block, la_dtype in_dtype, int causal, int normalize) {
   if (check_variant_args(B, Hq, Hkv, N, d, dv, block, in_dtype, in_dtype, causal, LA_FMAP_IDENTITY, normalize, 0.0f,
                          nullptr, nullptr) != LA_OK ||
-      N == 0)
+      N == 0 || in_dtype == LA_F32)
     return 0;
   return la::plan_variant(B, Hq, Hkv, N, d, dv, device_cus(), causal != 0, normalize != 0).workspace_bytes;
 }
@@ -555,6 +554,13 @@ la_status la_forward_variant(const void* q, const void* k, const void* v, void* 
       return LA_ERR_HIP;
     return LA_OK;
   }
+  if (in_dtype == LA_F32)
+    return la::launch_fwd_f32_variant(static_cast<const float*>(q), static_cast<const float*>(k),
+                                      static_cast<const float*>(v), static_cast<float*>(o), causal != 0,
+                                      fmap == LA_FMAP_RELU, normalize != 0, eps, s_in, s_out, z_in, z_out, B, Hq,
+                                      Hkv, N, d, dv, block, hs) == hipSuccess
+               ? LA_OK
+               : LA_ERR_HIP;
   const la::VarPlan vp = la::plan_variant(B, Hq, Hkv, N, d, dv, device_cus(), causal != 0, normalize != 0);
   const size_t nw = vp.workspace_bytes;
   if (nw > 0) {

@@ -9,7 +9,9 @@
 // every query head of the group, with the state slice, the block's K and V
 // slice and, one head at a time, Q and the score matrix staged in LDS.  The
 // state is read from s_in and written to s_out by the same workgroup, so the
-// two may be the same buffer.
+// two may be the same buffer.  The same kernel, with template flags, serves
+// the forward variants for float32 inputs (ReLU feature map, normalisation,
+// non-causal form).
 #include "la_internal.h"
 
 namespace la {
@@ -19,18 +21,32 @@ constexpr int kThreads = 256;
 constexpr int kSlice = 32;     // dv columns per workgroup
 constexpr int kMaxD = 128;
 constexpr int kMaxBlock = 64;
+constexpr int kFlagRelu = 1;  // same values as the bf16 kernels' flags
+constexpr int kFlagNorm = 2;
 
+// Feature-map variants (FL, the flags of the bf16 kernels) and the
+// non-causal form: kRelu maps q and k through phi = ReLU as they enter LDS;
+// kNorm divides output row t by phi(q_t) . z + eps, with z (d floats per KV
+// head) the running sum of phi(k) kept in LDS beside the state slice (each
+// slice's workgroup keeps its own copy).  Non-causal (CAUSAL false): a first
+// pass sums the state (and z) over every block, a second pass forms
+// o_t = phi(q_t) S_tot for every row.
+template <int FL, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restrict__ q,
                                                           const float* __restrict__ k,
                                                           const float* __restrict__ v, float* __restrict__ o,
-                                                          const float* s_in,
-                                                          float* s_out, int Hq, int Hkv,
-                                                          int64_t N, int d, int dv, int C) {
+                                                          const float* s_in, float* s_out, const float* z_in,
+                                                          float eps, int Hq, int Hkv, int64_t N, int d, int dv,
+                                                          int C) {
+  constexpr bool kR = (FL & kFlagRelu) != 0;
+  constexpr bool kN = (FL & kFlagNorm) != 0;
   __shared__ float Qs[kMaxBlock][kMaxD + 1];
   __shared__ float Ks[kMaxBlock][kMaxD + 1];
   __shared__ float Vs[kMaxBlock][kSlice];
   __shared__ float Ps[kMaxBlock][kMaxBlock + 1];
   __shared__ float Ss[kMaxD][kSlice];
+  __shared__ float Zs[kN ? kMaxD : 1];       // z before the current block (kNorm)
+  __shared__ float Den[kN ? kMaxBlock : 1];  // row denominators of the current head (kNorm)
 
   const int nslices = dv / kSlice;
   const int slice = blockIdx.x % nslices;
@@ -43,58 +59,103 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
   const float* kh = k + int64_t(bg) * N * d;
   const float* vh = v + int64_t(bg) * N * dv;
   const int64_t sbase = int64_t(bg) * d * dv;
+  auto phi = [](float x) { return kR ? fmaxf(x, 0.0f) : x; };
 
   for (int e = tid; e < d * kSlice; e += kThreads) {
     int i = e / kSlice, n = e % kSlice;
     Ss[i][n] = s_in ? s_in[sbase + int64_t(i) * dv + c0 + n] : 0.0f;
   }
+  if constexpr (kN)
+    for (int i = tid; i < d; i += kThreads) Zs[i] = z_in ? z_in[int64_t(bg) * d + i] : 0.0f;
 
-  for (int64_t a = 0; a < N; a += C) {
-    const int c = int(N - a < C ? N - a : C);
-    __syncthreads();  // previous block finished with Ks/Vs/Ss
+  // K and V of the block starting at a (c rows) into LDS.
+  auto load_kv = [&](int64_t a, int c) {
     for (int e = tid; e < c * d; e += kThreads) {
       int t = e / d, i = e % d;
-      Ks[t][i] = kh[(a + t) * d + i];
+      Ks[t][i] = phi(kh[(a + t) * d + i]);
     }
     for (int e = tid; e < c * kSlice; e += kThreads) {
       int t = e / kSlice, n = e % kSlice;
       Vs[t][n] = vh[(a + t) * dv + c0 + n];
     }
-    for (int hh = 0; hh < G; ++hh) {
-      const int64_t bh = int64_t(b) * Hq + int64_t(g) * G + hh;
-      const float* qh = q + bh * N * d;
-      float* oh = o + bh * N * dv;
-      __syncthreads();  // previous head finished with Qs/Ps
-      for (int e = tid; e < c * d; e += kThreads) {
-        int t = e / d, i = e % d;
-        Qs[t][i] = qh[(a + t) * d + i];
-      }
-      __syncthreads();
-      // In-block scores with the causal mask (s <= t kept).
-      for (int e = tid; e < c * c; e += kThreads) {
-        int t = e / c, s = e % c;
-        float acc = 0.0f;
-        if (s <= t)
-          for (int i = 0; i < d; ++i) acc = fmaf(Qs[t][i], Ks[s][i], acc);
-        Ps[t][s] = acc;
-      }
-      __syncthreads();
-      // O = Q S (state before this block) + P V.
-      for (int e = tid; e < c * kSlice; e += kThreads) {
-        int t = e / kSlice, n = e % kSlice;
-        float inter = 0.0f, intra = 0.0f;
-        for (int i = 0; i < d; ++i) inter = fmaf(Qs[t][i], Ss[i][n], inter);
-        for (int s = 0; s <= t; ++s) intra = fmaf(Ps[t][s], Vs[s][n], intra);
-        oh[(a + t) * dv + c0 + n] = inter + intra;
-      }
-    }
-    __syncthreads();
-    // S += K^T V after the block's output.
+  };
+  // S += K^T V (and z += sum of the K rows) after the block's outputs.
+  auto update_state = [&](int c) {
     for (int e = tid; e < d * kSlice; e += kThreads) {
       int i = e / kSlice, n = e % kSlice;
       float acc = Ss[i][n];
       for (int s = 0; s < c; ++s) acc = fmaf(Ks[s][i], Vs[s][n], acc);
       Ss[i][n] = acc;
+    }
+    if constexpr (kN)
+      for (int i = tid; i < d; i += kThreads) {
+        float acc = Zs[i];
+        for (int s = 0; s < c; ++s) acc += Ks[s][i];
+        Zs[i] = acc;
+      }
+  };
+
+  if constexpr (!CAUSAL) {
+    for (int64_t a = 0; a < N; a += C) {
+      const int c = int(N - a < C ? N - a : C);
+      __syncthreads();
+      load_kv(a, c);
+      __syncthreads();
+      update_state(c);
+    }
+  }
+
+  for (int64_t a = 0; a < N; a += C) {
+    const int c = int(N - a < C ? N - a : C);
+    __syncthreads();  // previous block finished with Ks/Vs/Ss
+    if constexpr (CAUSAL) load_kv(a, c);
+    for (int hh = 0; hh < G; ++hh) {
+      const int64_t bh = int64_t(b) * Hq + int64_t(g) * G + hh;
+      const float* qh = q + bh * N * d;
+      float* oh = o + bh * N * dv;
+      __syncthreads();  // previous head finished with Qs/Ps/Den
+      for (int e = tid; e < c * d; e += kThreads) {
+        int t = e / d, i = e % d;
+        Qs[t][i] = phi(qh[(a + t) * d + i]);
+      }
+      __syncthreads();
+      if constexpr (CAUSAL) {
+        // In-block scores with the causal mask (s <= t kept).
+        for (int e = tid; e < c * c; e += kThreads) {
+          int t = e / c, s = e % c;
+          float acc = 0.0f;
+          if (s <= t)
+            for (int i = 0; i < d; ++i) acc = fmaf(Qs[t][i], Ks[s][i], acc);
+          Ps[t][s] = acc;
+        }
+        __syncthreads();
+      }
+      if constexpr (kN) {
+        // denominator of row t: its weights summed without values
+        for (int t = tid; t < c; t += kThreads) {
+          float acc = 0.0f;
+          for (int i = 0; i < d; ++i) acc = fmaf(Qs[t][i], Zs[i], acc);
+          if constexpr (CAUSAL)
+            for (int s = 0; s <= t; ++s) acc += Ps[t][s];
+          Den[t] = acc + eps;
+        }
+        __syncthreads();
+      }
+      // O = Q S (state before this block, or the total) + P V.
+      for (int e = tid; e < c * kSlice; e += kThreads) {
+        int t = e / kSlice, n = e % kSlice;
+        float inter = 0.0f, intra = 0.0f;
+        for (int i = 0; i < d; ++i) inter = fmaf(Qs[t][i], Ss[i][n], inter);
+        if constexpr (CAUSAL)
+          for (int s = 0; s <= t; ++s) intra = fmaf(Ps[t][s], Vs[s][n], intra);
+        float out = inter + intra;
+        if constexpr (kN) out = out / Den[t];
+        oh[(a + t) * dv + c0 + n] = out;
+      }
+    }
+    if constexpr (CAUSAL) {
+      __syncthreads();
+      update_state(c);
     }
   }
   __syncthreads();
@@ -104,6 +165,22 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
       s_out[sbase + int64_t(i) * dv + c0 + n] = Ss[i][n];
     }
   }
+}
+
+// z_out[c][i] = z_in[c][i] (or 0) + sum over every token of phi(k[c][t][i]);
+// one thread per (KV chain, i).  Runs after the output kernel, so z_out may be
+// z_in itself.
+template <bool RELU>
+__global__ void z_sum_f32(const float* __restrict__ k, const float* z_in, float* z_out, int64_t chains, int64_t N,
+                          int d) {
+  const int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (e >= chains * d) return;
+  const int64_t c = e / d;
+  const int i = int(e % d);
+  const float* kc = k + c * N * d + i;
+  float acc = z_in ? z_in[e] : 0.0f;
+  for (int64_t t = 0; t < N; ++t) acc += RELU ? fmaxf(kc[t * d], 0.0f) : kc[t * d];
+  z_out[e] = acc;
 }
 
 __global__ void copy_or_zero_kernel(float* __restrict__ dst, const float* __restrict__ src, size_t n) {
@@ -123,8 +200,41 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
                           float* s_out, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv,
                           int64_t block, hipStream_t stream) {
   const int64_t grid = B * Hkv * (dv / kSlice);
-  hipLaunchKernelGGL(fwd_f32_kernel, dim3(unsigned(grid)), dim3(kThreads), 0, stream, q, k, v, o, s_in, s_out,
-                     int(Hq), int(Hkv), N, int(d), int(dv), int(block));
+  hipLaunchKernelGGL((fwd_f32_kernel<0, true>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, q, k, v, o, s_in,
+                     s_out, nullptr, 0.0f, int(Hq), int(Hkv), N, int(d), int(dv), int(block));
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_f32_variant(const float* q, const float* k, const float* v, float* o, bool causal, bool relu,
+                                  bool norm, float eps, const float* s_in, float* s_out, const float* z_in,
+                                  float* z_out, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                                  int64_t dv, int64_t block, hipStream_t stream) {
+  const dim3 grid(unsigned(B * Hkv * (dv / kSlice)));
+  const int iHq = int(Hq), iHkv = int(Hkv), id = int(d), idv = int(dv), ib = int(block);
+#define LA_F32V(FL, CAUSAL)                                                                                         \
+  hipLaunchKernelGGL((fwd_f32_kernel<FL, CAUSAL>), grid, dim3(kThreads), 0, stream, q, k, v, o, s_in, s_out, z_in, \
+                     eps, iHq, iHkv, N, id, idv, ib)
+  const int fl = (relu ? kFlagRelu : 0) | (norm ? kFlagNorm : 0);
+  switch (fl + (causal ? 4 : 0)) {
+    case 0: LA_F32V(0, false); break;
+    case 1: LA_F32V(1, false); break;
+    case 2: LA_F32V(2, false); break;
+    case 3: LA_F32V(3, false); break;
+    case 4: LA_F32V(0, true); break;
+    case 5: LA_F32V(1, true); break;
+    case 6: LA_F32V(2, true); break;
+    default: LA_F32V(3, true); break;
+  }
+#undef LA_F32V
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !norm || z_out == nullptr) return e;
+  const int64_t nz = B * Hkv * d;
+  if (relu)
+    hipLaunchKernelGGL((z_sum_f32<true>), dim3(unsigned((nz + 255) / 256)), dim3(256), 0, stream, k, z_in, z_out,
+                       B * Hkv, N, id);
+  else
+    hipLaunchKernelGGL((z_sum_f32<false>), dim3(unsigned((nz + 255) / 256)), dim3(256), 0, stream, k, z_in, z_out,
+                       B * Hkv, N, id);
   return hipGetLastError();
 }
 

@@ -38,6 +38,15 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
                           const float* s_in, float* s_out, int64_t B, int64_t Hq, int64_t Hkv,
                           int64_t N, int64_t d, int64_t dv, int64_t block, hipStream_t stream);
 
+// Forward variants for float32 inputs (same shapes as launch_fwd_f32): phi =
+// ReLU on q and k (relu), division by phi(q_t) . z_t + eps (norm, with z_in /
+// z_out the normaliser sums; z_out may be z_in), causal or non-causal.  No
+// workspace.
+hipError_t launch_fwd_f32_variant(const float* q, const float* k, const float* v, float* o, bool causal, bool relu,
+                                  bool norm, float eps, const float* s_in, float* s_out, const float* z_in,
+                                  float* z_out, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                                  int64_t dv, int64_t block, hipStream_t stream);
+
 // Segment start states into the workspace (pre-pass + scan); only when
 // plan.use_starts.
 hipError_t launch_segment_states(const void* k, const void* v, const float* s_in, int64_t B, int64_t Hkv,

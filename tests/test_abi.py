@@ -122,7 +122,9 @@ def test_variant_validation(lib):
     assert var(lib, q=None) == NULL
     assert var(lib, Hq=6, Hkv=4) == SHAPE
     assert var(lib, d=64, dv=64) == UNSUP                 # bf16 path: d = dv = 128
-    assert var(lib, i=F32, out=F32) == UNSUP              # bf16 inputs only
+    assert var(lib, i=F32, out=BF16) == UNSUP             # float32 inputs give float32 outputs
+    assert var(lib, i=F32, out=F32, d=64, dv=48) == UNSUP  # float32: dv a multiple of 32
+    assert lib.la_forward_variant_workspace_bytes(1, 4, 1, 1000, 64, 64, 64, F32, 0, 1) == 0   # float32: none
     assert var(lib, fmap=2) == UNSUP
     assert var(lib, causal=2) == UNSUP
     assert var(lib, eps=-1.0) == UNSUP

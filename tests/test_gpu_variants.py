@@ -133,3 +133,59 @@ def test_variants_gqa_1m_slices():
         check_close(f"causal final state group {g}", f64(S[:, gs]), S_t, BF16, torch.float32)
         check_close(f"causal final z group {g}", f64(Z[:, gs]), z_t, BF16, torch.float32)
         check_close(f"non-causal state group {g}", f64(S_nc[:, gs]), S_t, BF16, torch.float32)
+
+
+F32_CASES = [
+    # causal, fmap, normalize, eps, s_in, z_in, B, Hq, Hkv, N, d, dv, block, generator ReLU
+    (1, "relu", 1, 1e-6, True, True, 1, 4, 2, 300, 64, 64, 64, False),
+    (0, "relu", 1, 1e-3, True, True, 1, 3, 1, 200, 128, 96, 32, False),
+    (0, "identity", 0, 0.0, True, False, 2, 2, 2, 150, 32, 32, 64, False),
+    (1, "identity", 1, 0.0, False, False, 1, 4, 4, 257, 64, 128, 16, True),
+    (1, "relu", 0, 0.0, False, False, 1, 8, 2, 100, 128, 64, 64, False),
+]
+
+
+@pytest.mark.parametrize("causal,fmap,norm,eps,use_s,use_z,B,Hq,Hkv,N,d,dv,block,relu_gen", F32_CASES)
+def test_variant_f32_matches_oracle(causal, fmap, norm, eps, use_s, use_z, B, Hq, Hkv, N, d, dv, block, relu_gen):
+    """float32 inputs (the float32 FMA kernel with the variant flags) at the
+    float32 bar, 1e-5 of the output RMS (of RMS(v) when normalised)."""
+    need_gpu()
+    say(f"case variant f32 causal={causal} fmap={fmap} norm={norm} B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} dv={dv} "
+        f"block={block}")
+    F32 = torch.float32
+    w = synth.Workload("t", B, Hq, Hkv, N, d, dv, block, F32, relu_gen, True)
+    q, k, v = synth.make_qkv(w, DEV, seed=N + d + causal)
+    S0 = synth.random_state((B, Hkv, d, dv), DEV, seed=N + 5, scale=0.5) if use_s else None
+    Z0 = synth.random_state((B, Hkv, d), DEV, seed=N + 6).abs() if use_z else None
+    o, S, Z = la.forward_variant(q, k, v, causal=bool(causal), feature_map=fmap, normalize=bool(norm), eps=eps,
+                                 block=block, s_in=S0, z_in=Z0, return_state=True)
+    torch.cuda.synchronize()
+    assert o.dtype == F32
+    ref_o, ref_S, ref_z = oracle.variant(f64(q), f64(k), f64(v), causal=bool(causal), relu=(fmap == "relu"),
+                                         normalize=bool(norm), eps=eps, s_in=None if S0 is None else f64(S0),
+                                         z_in=None if Z0 is None else f64(Z0))
+    check_close("f32 o", f64(o), ref_o, F32, F32, scale=rms(f64(v)) if norm else None)
+    check_close("f32 S_out", f64(S), ref_S, F32, F32)
+    if norm:
+        check_close("f32 z_out", f64(Z), ref_z, F32, F32)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, BF16])
+def test_variant_in_place_state_and_normaliser(dtype):
+    """s_out written over s_in and z_out over z_in give the results of
+    separate buffers (non-causal normalised, the float32 path computes z_out
+    after every workgroup has read z_in)."""
+    need_gpu()
+    say(f"case variant in place S, z {dtype}")
+    d = 64 if dtype == torch.float32 else 128
+    w = synth.Workload("t", 1, 4, 2, 500, d, d, 64, dtype, False, dtype == torch.float32)
+    q, k, v = synth.make_qkv(w, DEV, seed=41)
+    S0 = synth.random_state((1, 2, d, d), DEV, seed=42, scale=0.5)
+    Z0 = synth.random_state((1, 2, d), DEV, seed=43).abs()
+    ref = la.forward_variant(q, k, v, causal=False, feature_map="relu", normalize=True, eps=1e-6, s_in=S0, z_in=Z0,
+                             return_state=True)
+    S, Z = S0.clone(), Z0.clone()
+    o = la.forward_variant(q, k, v, causal=False, feature_map="relu", normalize=True, eps=1e-6, s_in=S, z_in=Z,
+                           s_out=S, z_out=Z)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref[0]) and torch.equal(S, ref[1]) and torch.equal(Z, ref[2])
