@@ -300,6 +300,27 @@ def bench_variants(la, torch, w, q, k, v, steps, warmup):
     return {"steps": steps, "warmup": warmup, "workload": w.name, "variants": out}
 
 
+def copy_bandwidth(torch, mib=1024, reps=7):
+    """Read + write GB/s of a plain device-to-device copy of `mib` MiB (the
+    runtime's copy kernel), median of `reps` event-timed copies: the practical
+    streaming ceiling the HBM-bound kernels are also compared with."""
+    n = mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record()
+        b.copy_(a)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = statistics.median(e0.elapsed_time(e1) for e0, e1 in evs)
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * n / (ms * 1e-3) / 1e9
+
+
 def bench_decode(la, synth, torch, w, steps, warmup):
     dev = torch.device("cuda:0")
     S = torch.empty((w.B, w.Hkv, w.d, w.dv), dtype=torch.float32, device=dev)
@@ -403,10 +424,14 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    copy_gbs = copy_bandwidth(torch)
+    log(f"[bench] device copy: {copy_gbs:.0f} GB/s (read + write)")
+
     decode = None
     if args.decode_steps > 0:
         decode = bench_decode(la, synth, torch, synth.WORKLOADS["decode_256"], args.decode_steps,
                               args.decode_warmup)
+        decode["roofline"]["frac_of_copy"] = round(decode["gb_per_s"] / copy_gbs, 4)
         log(f"[bench] decode: {decode['ms_per_step']:.4f} ms/step, {decode['gb_per_s']:.0f} GB/s")
 
     rec = {
@@ -427,7 +452,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic("fwd_bf16_g4", w.name),
-                     "kernel": "fwd_bf16_g4", "kernel_ms": round(ms_main, 4), "bytes_per_launch": bytes_main},
+                     "kernel": "fwd_bf16_g4", "kernel_ms": round(ms_main, 4), "bytes_per_launch": bytes_main,
+                     "frac_of_copy": round(achieved / copy_gbs, 4)},
         "mfma": {"tflops_alg": round(f_alg / (ms_step * 1e-3) / 1e12, 2),
                  "frac_alg": round(f_alg / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                  "tflops_tile": round(f_tile / (ms_step * 1e-3) / 1e12, 2),
@@ -440,7 +466,7 @@ def main():
         "decode": decode,
         "cpu_baseline": cpu,
         "device": {"name": props.name, "gcnArchName": getattr(props, "gcnArchName", ""),
-                   "cus": props.multi_processor_count},
+                   "cus": props.multi_processor_count, "copy_gb_per_s": round(copy_gbs, 1)},
     }
     print(json.dumps(rec), flush=True)
 
