@@ -49,10 +49,20 @@ typedef enum {
   LA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
   LA_ERR_ALIAS = 5,       /* an output overlaps an input */
   LA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than la_forward_workspace_bytes */
-  LA_ERR_HIP = 7          /* HIP runtime or launch error */
+  LA_ERR_HIP = 7,         /* HIP runtime or launch error */
+  /* Range sentinels (not statuses): every 32-bit int is a value of the type, so
+   * an out-of-range code passed in from C is well defined and reported as such
+   * (the same holds for la_dtype and la_feature_map below). */
+  LA_STATUS_RANGE_MIN_ = -2147483647 - 1,
+  LA_STATUS_RANGE_MAX_ = 2147483647
 } la_status;
 
-typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
+typedef enum {
+  LA_F32 = 0,
+  LA_BF16 = 1,
+  LA_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  LA_DTYPE_RANGE_MAX_ = 2147483647
+} la_dtype;
 
 /* hipStream_t, passed as an opaque pointer so this header needs no HIP headers. */
 typedef void* la_stream;
@@ -178,7 +188,12 @@ la_status la_decode_step(float* S, const void* q, const void* k, const void* v, 
  * causal = 1, LA_FMAP_IDENTITY, normalize = 0 computes exactly la_forward_ex.
  * Workspace: la_forward_variant_workspace_bytes (may be 0).
  */
-typedef enum { LA_FMAP_IDENTITY = 0, LA_FMAP_RELU = 1 } la_feature_map;
+typedef enum {
+  LA_FMAP_IDENTITY = 0,
+  LA_FMAP_RELU = 1,
+  LA_FMAP_RANGE_MIN_ = -2147483647 - 1,
+  LA_FMAP_RANGE_MAX_ = 2147483647
+} la_feature_map;
 
 la_status la_forward_variant(const void* q, const void* k, const void* v, void* o,
                              int64_t B, int64_t Hq, int64_t Hkv, int64_t N,

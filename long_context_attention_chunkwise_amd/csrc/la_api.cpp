@@ -48,7 +48,10 @@ la_status check_forward_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int
   // Grid dimensions are 32-bit; keep the workgroup counts well inside that,
   // and keep every byte count (B * Hq * N * 128 elements of up to 4 bytes)
   // far from 64-bit overflow.
-  if (B * Hq > (int64_t(1) << 24) || N > (int64_t(1) << 40)) return LA_ERR_UNSUPPORTED;
+  // (each factor is bounded before the product, which therefore cannot overflow)
+  if (B > (int64_t(1) << 24) || Hq > (int64_t(1) << 24) || B * Hq > (int64_t(1) << 24) ||
+      N > (int64_t(1) << 40))
+    return LA_ERR_UNSUPPORTED;
   if (N > 0 && B * Hq > (int64_t(1) << 44) / N) return LA_ERR_UNSUPPORTED;
   return LA_OK;
 }
@@ -200,6 +203,7 @@ const char* la_status_str(la_status s) {
     case LA_ERR_ALIAS: return "an output buffer overlaps an input buffer";
     case LA_ERR_WORKSPACE: return "workspace missing or too small";
     case LA_ERR_HIP: return "HIP runtime or launch error";
+    default: break;
   }
   return "unknown status";
 }
@@ -351,7 +355,8 @@ la_status la_decode_step(float* S, const void* q, const void* k, const void* v, 
                          la_stream stream) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || dv <= 0 || Hq % Hkv != 0) return LA_ERR_SHAPE;
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return LA_ERR_UNSUPPORTED;
-  if (d > 128 || dv > 128 || dv % 4 != 0 || B * Hkv > (int64_t(1) << 30) || Hq / Hkv > 1024)
+  if (d > 128 || dv > 128 || dv % 4 != 0 || B > (int64_t(1) << 30) || Hkv > (int64_t(1) << 30) ||
+      B * Hkv > (int64_t(1) << 30) || Hq / Hkv > 1024)
     return LA_ERR_UNSUPPORTED;
   if (S == nullptr || q == nullptr || k == nullptr || v == nullptr || o == nullptr) return LA_ERR_NULL;
   if (!aligned16(S) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return LA_ERR_ALIGN;

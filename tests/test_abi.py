@@ -61,6 +61,7 @@ def test_forward_validation(lib):
     assert fwd(lib, d=64) == UNSUP                       # bf16 path is d = dv = 128
     assert fwd(lib, block=128) == UNSUP
     assert fwd(lib, B=1 << 12, Hq=1 << 12, Hkv=1 << 12, N=1 << 30) == UNSUP   # byte counts would overflow
+    assert fwd(lib, B=1 << 40, Hq=1 << 40, Hkv=1 << 40, N=1) == UNSUP          # B * Hq itself would overflow
     assert fwd(lib, i=BF16, out=2) == UNSUP
     assert fwd(lib, i=F32, out=BF16) == UNSUP
     assert fwd(lib, i=F32, out=F32, dv=48) == UNSUP       # fp32 path: dv multiple of 32
@@ -81,6 +82,7 @@ def test_decode_validation(lib):
     assert dec(Hq=6, Hkv=4) == SHAPE
     assert dec(dv=126) == UNSUP
     assert dec(Hq=2050, Hkv=2) == UNSUP                   # more than 1024 query heads per KV head
+    assert dec(B=1 << 40, Hq=1 << 40, Hkv=1 << 40) == UNSUP   # no overflow in the size checks
     assert dec(o=ctypes.c_void_p(GB * 4 + 2)) == ALIGN
     assert dec(o=ctypes.c_void_p(GB * 5 + 16)) == ALIAS   # o inside S
 
