@@ -92,9 +92,11 @@ def test_gqa_1m_slices_and_states():
 
 def test_decode_256_sequences():
     """256 sequences, 128/32 heads, d = dv = 128: state from the forward kernel
-    over a seeded 8192-token prefix, then 1000 decode steps.  Checked: 16
-    sampled prefix states, every step's outputs of 2 sampled sequences, and the
-    final states of 16 sampled sequences, against the oracle's recurrence."""
+    over a seeded 8192-token prefix, then 1000 decode steps.  Checked against
+    the oracle: 16 sampled prefix states; every step's outputs of 2 of those
+    sequences (the oracle's token recurrence); the outputs of all 16 at sampled
+    steps (the oracle's state before the step in closed form, then its decode
+    step); and the final states of the 16."""
     need_gpu()
     w = synth.WORKLOADS["decode_256"]
     G = w.Hq // w.Hkv
@@ -102,6 +104,7 @@ def test_decode_256_sequences():
     rng = np.random.default_rng(123)
     seqs = np.sort(rng.choice(w.B, 16, replace=False))
     out_seqs = seqs[:2]
+    check_steps = [0, 1, 2, 99, 500, 998, 999]
     S = torch.empty((w.B, w.Hkv, w.d, w.dv), dtype=torch.float32, device=DEV)
     batch = 32
     pre_k, pre_v, pre_q = {}, {}, {}
@@ -120,14 +123,16 @@ def test_decode_256_sequences():
     qs, ks, vs = synth.make_decode_steps(w, DEV, seed=1, steps=w.steps)
     o = torch.empty((w.B, w.Hq, w.dv), dtype=torch.float32, device=DEV)
     idx = torch.as_tensor(out_seqs, device=DEV)
-    outs = []
+    sidx = torch.as_tensor(seqs, device=DEV)
+    outs, sampled = [], {}
     for t in range(w.steps):
         la.decode_step(S, qs[t], ks[t], vs[t], out=o)
         outs.append(o.index_select(0, idx))
+        if t in check_steps:
+            sampled[t] = o.index_select(0, sidx)
     torch.cuda.synchronize()
     got = np.stack([f64(x) for x in outs])            # [T, 2, Hq, dv]
 
-    sidx = torch.as_tensor(seqs, device=DEV)
     q_s, k_s, v_s = (f64(x.index_select(1, sidx)) for x in (qs, ks, vs))   # [T, 16, H, d]
     # outputs of 2 sequences, all steps, by the oracle's token recurrence
     Sref = np.concatenate([ref_pre[s] for s in out_seqs])
@@ -135,6 +140,14 @@ def test_decode_256_sequences():
     for t in range(w.steps):
         Sref, ref_out[t] = oracle.decode_step(Sref, q_s[t, :2], k_s[t, :2], v_s[t, :2])
     check_close("decode outputs (2 sequences x 1000 steps)", got, ref_out, torch.bfloat16, torch.float32)
+    # outputs of all 16 sequences at sampled steps: state before step t in closed form
+    pre16 = np.concatenate([ref_pre[s] for s in seqs])
+    for t in check_steps:
+        S_before = oracle.final_state(np.transpose(k_s[:t], (1, 2, 0, 3)), np.transpose(v_s[:t], (1, 2, 0, 3)),
+                                      pre16)
+        _, o_ref = oracle.decode_step(S_before, q_s[t], k_s[t], v_s[t])
+        check_close(f"decode outputs (16 sequences, step {t})", f64(sampled[t]), o_ref, torch.bfloat16,
+                    torch.float32)
     # final states of 16 sequences: prefix state + sum over steps of k^T v
     ref_final = oracle.final_state(np.transpose(k_s, (1, 2, 0, 3)), np.transpose(v_s, (1, 2, 0, 3)),
                                    np.concatenate([ref_pre[s] for s in seqs]))
