@@ -50,6 +50,8 @@ CASES = [
     (0, "identity", 0, 0.0, True, False, BF16, 2, 4, 4, 2900, False),        # G = 1: segments of 2 blocks, steps of 4
     (0, "relu", 0, 0.0, False, False, torch.float32, 1, 4, 2, 777, False),   # G = 2
     (0, "relu", 1, 1e-3, True, True, torch.float32, 1, 6, 2, 1500, False),   # G = 3
+    (1, "relu", 1, 1e-6, True, True, torch.float32, 1, 2, 2, 100, False),    # G = 1, one segment: s_in, z_in direct
+    (1, "identity", 1, 1e-6, True, True, BF16, 1, 4, 2, 64, True),           # G = 2, one block
 ]
 
 
