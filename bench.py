@@ -321,7 +321,28 @@ def copy_bandwidth(torch, mib=1024, reps=7):
     return 2 * n / (ms * 1e-3) / 1e9
 
 
-def bench_decode(la, synth, torch, w, steps, warmup):
+def cpu_decode_baseline(S, qs, ks, vs, nseq=4, nsteps=10):
+    """Time the fp64 oracle's decode step on `nseq` of the sequences (all their
+    heads) for `nsteps` steps; sequence-steps per second."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    f64 = lambda t: t[:nseq].float().cpu().numpy().astype(np.float64)
+    St = f64(S)
+    steps = [(f64(qs[t]), f64(ks[t]), f64(vs[t])) for t in range(nsteps)]
+    t0 = time.perf_counter()
+    for q, k, v in steps:
+        St, _ = oracle.decode_step(St, q, k, v)
+    dt = time.perf_counter() - t0
+    return {"value": nseq * nsteps / dt, "unit": "sequence-steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 oracle decode_step on {nseq} sequences (all heads) x {nsteps} steps, {dt:.2f} s"}
+
+
+def bench_decode(la, synth, torch, w, steps, warmup, cpu=False):
     dev = torch.device("cuda:0")
     S = torch.empty((w.B, w.Hkv, w.d, w.dv), dtype=torch.float32, device=dev)
     batch = 32
@@ -351,7 +372,9 @@ def bench_decode(la, synth, torch, w, steps, warmup):
     step_bytes = (2 * S.numel() * 4 + qs[0].numel() * 2 + ks[0].numel() * 2 + vs[0].numel() * 2 + o.numel() * 4)
     mean_ms = statistics.mean(per)
     gbs = step_bytes / (mean_ms * 1e-3) / 1e9
+    cpu_rec = cpu_decode_baseline(S, qs, ks, vs) if cpu else None
     return {"steps": steps, "warmup": warmup, "ms_per_step": round(mean_ms, 5),
+            "sequence_steps_per_s": round(w.B / (mean_ms * 1e-3), 1), "cpu_baseline": cpu_rec,
             "ms_per_step_median": round(statistics.median(per), 5), "ms_per_step_wall": round(wall, 5),
             "gb_per_s": round(gbs, 1), "unit": "GB/s",
             "config": {"workload": w.name, "sequences": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "dv": w.dv,
@@ -430,7 +453,7 @@ def main():
     decode = None
     if args.decode_steps > 0:
         decode = bench_decode(la, synth, torch, synth.WORKLOADS["decode_256"], args.decode_steps,
-                              args.decode_warmup)
+                              args.decode_warmup, cpu=not args.no_cpu_baseline)
         decode["roofline"]["frac_of_copy"] = round(decode["gb_per_s"] / copy_gbs, 4)
         log(f"[bench] decode: {decode['ms_per_step']:.4f} ms/step, {decode['gb_per_s']:.0f} GB/s")
 
