@@ -173,10 +173,13 @@ def bench_forward(la, synth, torch, w, steps, warmup):
     ms_step = (t1 - t0) * 1e3 / steps
     t_states = [e[0].elapsed_time(e[1]) for e in evs]
     t_main = [e[1].elapsed_time(e[2]) for e in evs]
+    t_step = [e[0].elapsed_time(e[2]) for e in evs]
     finite = bool(torch.isfinite(o).all().item())
     if not finite:
         raise RuntimeError("non-finite forward output")
-    return q, k, v, ms_step, statistics.mean(t_states), statistics.mean(t_main), ws_bytes
+    events = {"median": round(statistics.median(t_step), 4), "min": round(min(t_step), 4),
+              "mean": round(statistics.mean(t_step), 4)}
+    return q, k, v, ms_step, statistics.mean(t_states), statistics.mean(t_main), ws_bytes, events
 
 
 def backward_flops(w, N):
@@ -416,7 +419,8 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     props = torch.cuda.get_device_properties(0)
-    q, k, v, ms_step, ms_states, ms_main, ws_bytes = bench_forward(la, synth, torch, w, args.steps, args.warmup)
+    q, k, v, ms_step, ms_states, ms_main, ws_bytes, step_events = bench_forward(la, synth, torch, w, args.steps,
+                                                                                args.warmup)
     tokens = w.B * w.N
     value = tokens / (ms_step * 1e-3)
     f_alg, f_tile = forward_flops(w, w.N)
@@ -483,6 +487,7 @@ def main():
                  "frac_tile": round(f_tile / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                  "peak_tflops": PEAK_BF16_TFLOPS, "flops_alg": f_alg, "flops_tile": f_tile},
         "phases_ms": {"segment_states": round(ms_states, 4), "outputs": round(ms_main, 4)},
+        "ms_per_step_events": step_events,
         "workspace_bytes": ws_bytes,
         "variants": variants,
         "backward": backward,
