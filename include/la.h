@@ -1,7 +1,8 @@
 /*
  * la.h — C ABI of liblightning.so: causal chunkwise linear attention
- * (Lightning Attention) forward pass, its backward pass and batched
- * single-token decode on AMD Instinct MI355X (gfx950).
+ * (Lightning Attention) forward pass, its backward pass, its feature-map,
+ * normalised and non-causal variants, and batched single-token decode on AMD
+ * Instinct MI355X (gfx950).
  *
  * What is computed.  Page "如何理解MiniMax股价创历史新高？拆解国产大模型技术底座"
  * (vergex.cn), section "Lightning Attention：长上下文为什么突然变得便宜了", chunkwise
@@ -11,8 +12,8 @@
  * and only then updates S <- S + K_b^T V_b.  In exact arithmetic this equals
  *     o_t = q_t . s_in + sum_{s <= t} (q_t . k_s) v_s,
  * for every block size (associativity; page "MiniMax-01与Lightning Attention",
- * section 2.2).  No normalisation, scaling or feature map is applied: q and k
- * arrive already feature-mapped.  Query head h reads KV head h / (Hq / Hkv)
+ * section 2.2).  Apart from la_forward_variant, no normalisation, scaling or
+ * feature map is applied: q and k arrive already feature-mapped.  Query head h reads KV head h / (Hq / Hkv)
  * (grouped-query attention with contiguous groups; same page, section 1.1
  * table: 128 heads over 32 KV heads).
  *
