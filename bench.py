@@ -393,7 +393,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="gqa_1m", help="forward workload name (synth.WORKLOADS)")
+    ap.add_argument("--workload", default="gqa_1m", choices=["mha_4k", "gqa_64k", "gqa_1m"],
+                    help="bf16 forward workload (synth.WORKLOADS); the default is the 1M-token one")
     ap.add_argument("--decode-steps", type=int, default=1000, help="0 skips the decode measurement")
     ap.add_argument("--decode-warmup", type=int, default=10)
     ap.add_argument("--variant-steps", type=int, default=5, help="0 skips the forward-variant measurement")
@@ -418,6 +419,8 @@ def main():
     la.load_library()  # fails loudly when the HIP library is missing
 
     w = synth.WORKLOADS[args.workload]
+    # the output kernel that serves this workload's query-head group size
+    main_kernel = "fwd_bf16_g4" if (w.Hq // w.Hkv) % 4 == 0 else "fwd_bf16_main"
     props = torch.cuda.get_device_properties(0)
     q, k, v, ms_step, ms_states, ms_main, ws_bytes, step_events = bench_forward(la, synth, torch, w, args.steps,
                                                                                 args.warmup)
@@ -478,8 +481,8 @@ def main():
                    "dv": w.dv, "block": w.block, "io_dtype": "bf16", "state_dtype": "f32"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": measured_traffic("fwd_bf16_g4", w.name),
-                     "kernel": "fwd_bf16_g4", "kernel_ms": round(ms_main, 4), "bytes_per_launch": bytes_main,
+                     "traffic": measured_traffic(main_kernel, w.name),
+                     "kernel": main_kernel, "kernel_ms": round(ms_main, 4), "bytes_per_launch": bytes_main,
                      "frac_of_copy": round(achieved / copy_gbs, 4)},
         "mfma": {"tflops_alg": round(f_alg / (ms_step * 1e-3) / 1e12, 2),
                  "frac_alg": round(f_alg / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
