@@ -186,8 +186,9 @@ def forward_variant(q, k, v, causal=True, feature_map="identity", normalize=Fals
                     workspace=None):
     """Forward variants (la_forward_variant): feature map "identity" or "relu"
     (phi = ReLU on q and k), causal or non-causal, optionally normalised by
-    phi(q_t) . z_t + eps.  bf16 q, k, v with d = dv = 128, or float32 q, k,
-    v with the float32 forward's shapes (any Hq/Hkv).  Returns o and, with
+    phi(q_t) . z_t + eps.  bf16 or float32 q, k, v; the matrix-core kernels
+    serve bf16 at d = dv = 128 and 64-token blocks, the float32 FMA kernels
+    every other shape the float32 forward takes (any Hq/Hkv).  Returns o and, with
     return_state, (S_out, z_out) (z_out None unless normalize)."""
     torch = _torch()
     lib = load_library()

@@ -33,18 +33,22 @@ int device_cus() {
   return cus;
 }
 
+// bf16 inputs with d = dv = 128 and 64-token blocks run on the matrix-core
+// kernels; every other supported shape (float32 inputs, or bf16 at other head
+// or block sizes) on the scalar float32-FMA kernels.
+bool mfma_path(la_dtype in_dtype, int64_t d, int64_t dv, int64_t block) {
+  return in_dtype == LA_BF16 && d == 128 && dv == 128 && block == kBf16Block;
+}
+
 // Shape/dtype checks shared by la_forward_ex and la_forward_workspace_bytes.
 la_status check_forward_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv,
                               int64_t block, la_dtype in_dtype, la_dtype out_dtype) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || N < 0 || d <= 0 || dv <= 0 || block <= 0) return LA_ERR_SHAPE;
   if (Hq % Hkv != 0) return LA_ERR_SHAPE;
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return LA_ERR_UNSUPPORTED;
-  if (in_dtype == LA_F32) {
-    if (out_dtype != LA_F32) return LA_ERR_UNSUPPORTED;
-    if (d > 128 || dv > 128 || dv % 32 != 0 || block > 64) return LA_ERR_UNSUPPORTED;
-  } else {
-    if (d != 128 || dv != 128 || block != kBf16Block) return LA_ERR_UNSUPPORTED;
-  }
+  if (in_dtype == LA_F32 && out_dtype != LA_F32) return LA_ERR_UNSUPPORTED;
+  if (!mfma_path(in_dtype, d, dv, block) && (d > 128 || dv > 128 || dv % 32 != 0 || block > 64))
+    return LA_ERR_UNSUPPORTED;
   // Grid dimensions are 32-bit; keep the workgroup counts well inside that,
   // and keep every byte count (B * Hq * N * 128 elements of up to 4 bytes)
   // far from 64-bit overflow.
@@ -212,7 +216,7 @@ size_t la_forward_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
                                   int64_t block, la_dtype in_dtype) {
   la_dtype out = in_dtype;
   if (check_forward_shape(B, Hq, Hkv, N, d, dv, block, in_dtype, out) != LA_OK) return 0;
-  if (in_dtype == LA_F32 || N == 0) return 0;
+  if (!mfma_path(in_dtype, d, dv, block) || N == 0) return 0;
   return la::plan_bf16(B, Hq, Hkv, N, d, dv, device_cus()).workspace_bytes;
 }
 
@@ -224,7 +228,8 @@ namespace {
 // in one place.  need_q_o is false for la_forward_states (it reads only k, v).
 struct ForwardCall {
   la::Bf16Plan plan;
-  size_t ns = 0;  // state bytes
+  size_t ns = 0;        // state bytes
+  bool scalar = false;  // the scalar kernels serve this call (no workspace)
 };
 
 la_status validate_forward(ForwardCall& fc, const void* q, const void* k, const void* v, const void* o,
@@ -243,6 +248,7 @@ la_status validate_forward(ForwardCall& fc, const void* q, const void* k, const 
   const size_t nv = size_t(B * Hkv * N * dv) * ei, no = size_t(B * Hq * N * dv) * eo;
   const size_t ns = size_t(B * Hkv * d * dv) * sizeof(float);
   fc.ns = ns;
+  fc.scalar = !mfma_path(in_dtype, d, dv, block);
   if (overlap(o, no, q, nq) || overlap(o, no, k, nk) || overlap(o, no, v, nv) || overlap(o, no, s_in, ns))
     return LA_ERR_ALIAS;
   if (s_out != nullptr &&
@@ -250,7 +256,7 @@ la_status validate_forward(ForwardCall& fc, const void* q, const void* k, const 
        overlap(s_out, ns, o, no) || (s_out != s_in && overlap(s_out, ns, s_in, ns))))
     return LA_ERR_ALIAS;
 
-  if (in_dtype == LA_BF16 && N > 0) {
+  if (!fc.scalar && N > 0) {
     fc.plan = la::plan_bf16(B, Hq, Hkv, N, d, dv, device_cus());
     const size_t nw = fc.plan.workspace_bytes;
     if (nw > 0) {
@@ -266,7 +272,8 @@ la_status validate_forward(ForwardCall& fc, const void* q, const void* k, const 
 
 la_status run_states(const ForwardCall& fc, const void* k, const void* v, int64_t B, int64_t Hkv, int64_t N,
                      la_dtype in_dtype, const float* s_in, void* workspace, hipStream_t hs) {
-  if (in_dtype != LA_BF16 || N == 0 || !fc.plan.use_starts) return LA_OK;
+  (void)in_dtype;
+  if (fc.scalar || N == 0 || !fc.plan.use_starts) return LA_OK;
   return la::launch_segment_states(k, v, s_in, B, Hkv, N, fc.plan, workspace, hs) == hipSuccess ? LA_OK
                                                                                                   : LA_ERR_HIP;
 }
@@ -279,10 +286,9 @@ la_status run_outputs(const ForwardCall& fc, const void* q, const void* k, const
   if (N == 0) {
     // No tokens: the final state is the initial state (zeros without s_in).
     if (s_out != nullptr && s_out != s_in) err = la::launch_copy_or_zero(s_out, s_in, fc.ns / sizeof(float), hs);
-  } else if (in_dtype == LA_F32) {
-    err = la::launch_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
-                             static_cast<const float*>(v), static_cast<float*>(o), s_in, s_out, B, Hq, Hkv, N,
-                             d, dv, block, hs);
+  } else if (fc.scalar) {
+    err = la::launch_fwd_f32(q, k, v, o, in_dtype == LA_BF16, out_dtype == LA_BF16, s_in, s_out, B, Hq, Hkv, N, d,
+                             dv, block, hs);
   } else {
     err = la::launch_fwd_bf16(q, k, v, o, out_dtype == LA_F32, s_in, s_out, B, Hq, Hkv, N, fc.plan, workspace,
                               hs);
@@ -337,7 +343,7 @@ la_status la_forward(const void* q, const void* k, const void* v, void* o, int64
   la_status st = check_forward_shape(B, Hq, Hkv, N, d, dv, block, in_dtype, out_dtype);
   if (st != LA_OK) return st;
   size_t ws = 0;
-  if (in_dtype == LA_BF16 && N > 0) ws = la::plan_bf16(B, Hq, Hkv, N, d, dv, device_cus()).workspace_bytes;
+  if (mfma_path(in_dtype, d, dv, block) && N > 0) ws = la::plan_bf16(B, Hq, Hkv, N, d, dv, device_cus()).workspace_bytes;
   if (ws == 0)
     return la_forward_ex(q, k, v, o, B, Hq, Hkv, N, d, dv, block, in_dtype, out_dtype, nullptr, nullptr,
                          nullptr, 0, stream);
@@ -380,13 +386,14 @@ la_status check_backward_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, in
                                int64_t block, la_dtype in_dtype, la_dtype grad_dtype) {
   la_status st = check_forward_shape(B, Hq, Hkv, N, d, dv, block, in_dtype, grad_dtype);
   if (st != LA_OK) return st;
-  // float32: dK is computed in 32-column slices of d (dv is already a multiple of 32)
-  if (in_dtype == LA_F32 && d % 32 != 0) return LA_ERR_UNSUPPORTED;
+  // scalar kernels: dK is computed in 32-column slices of d (dv is already a multiple of 32)
+  if (!mfma_path(in_dtype, d, dv, block) && d % 32 != 0) return LA_ERR_UNSUPPORTED;
   return LA_OK;
 }
 
-size_t backward_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv, la_dtype in_dtype) {
-  if (in_dtype == LA_F32) return la::bwd_f32_workspace_floats(B, Hkv, d, dv) * sizeof(float);
+size_t backward_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv, int64_t block,
+                          la_dtype in_dtype) {
+  if (!mfma_path(in_dtype, d, dv, block)) return la::bwd_f32_workspace_floats(B, Hkv, d, dv) * sizeof(float);
   return la::plan_backward(B, Hq, Hkv, N, d, dv, device_cus()).workspace_bytes;
 }
 
@@ -397,7 +404,7 @@ extern "C" {
 size_t la_backward_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv,
                                    int64_t block, la_dtype in_dtype) {
   if (check_backward_shape(B, Hq, Hkv, N, d, dv, block, in_dtype, in_dtype) != LA_OK || N == 0) return 0;
-  return backward_workspace(B, Hq, Hkv, N, d, dv, in_dtype);
+  return backward_workspace(B, Hq, Hkv, N, d, dv, block, in_dtype);
 }
 
 la_status la_backward(const void* q, const void* k, const void* v, const void* grad_o, void* grad_q,
@@ -445,17 +452,15 @@ la_status la_backward(const void* q, const void* k, const void* v, const void* g
                                                                                                   : LA_ERR_HIP;
   }
 
-  const size_t nw = backward_workspace(B, Hq, Hkv, N, d, dv, in_dtype);
+  const size_t nw = backward_workspace(B, Hq, Hkv, N, d, dv, block, in_dtype);
   if (workspace == nullptr || workspace_bytes < nw) return LA_ERR_WORKSPACE;
   for (const Range& in : inputs)
     if (overlap(workspace, nw, in.p, in.n)) return LA_ERR_ALIAS;
   for (const Range& out : outputs)
     if (overlap(workspace, nw, out.p, out.n)) return LA_ERR_ALIAS;
 
-  if (in_dtype == LA_F32)
-    return la::launch_bwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
-                              static_cast<const float*>(v), static_cast<const float*>(grad_o),
-                              static_cast<float*>(grad_q), static_cast<float*>(grad_k), static_cast<float*>(grad_v),
+  if (!mfma_path(in_dtype, d, dv, block))
+    return la::launch_bwd_f32(q, k, v, grad_o, grad_q, grad_k, grad_v, in_dtype == LA_BF16, grad_dtype == LA_BF16,
                               s_in, grad_s_out, grad_s_in, B, Hq, Hkv, N, d, dv, block,
                               static_cast<float*>(workspace), hs) == hipSuccess
                ? LA_OK
@@ -514,7 +519,7 @@ size_t la_forward_variant_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, in
                                           int64_t block, la_dtype in_dtype, int causal, int normalize) {
   if (check_variant_args(B, Hq, Hkv, N, d, dv, block, in_dtype, in_dtype, causal, LA_FMAP_IDENTITY, normalize, 0.0f,
                          nullptr, nullptr) != LA_OK ||
-      N == 0 || in_dtype == LA_F32)
+      N == 0 || !mfma_path(in_dtype, d, dv, block))
     return 0;
   return la::plan_variant(B, Hq, Hkv, N, d, dv, device_cus(), causal != 0, normalize != 0).workspace_bytes;
 }
@@ -559,9 +564,8 @@ la_status la_forward_variant(const void* q, const void* k, const void* v, void* 
       return LA_ERR_HIP;
     return LA_OK;
   }
-  if (in_dtype == LA_F32)
-    return la::launch_fwd_f32_variant(static_cast<const float*>(q), static_cast<const float*>(k),
-                                      static_cast<const float*>(v), static_cast<float*>(o), causal != 0,
+  if (!mfma_path(in_dtype, d, dv, block))
+    return la::launch_fwd_f32_variant(q, k, v, o, in_dtype == LA_BF16, out_dtype == LA_BF16, causal != 0,
                                       fmap == LA_FMAP_RELU, normalize != 0, eps, s_in, s_out, z_in, z_out, B, Hq,
                                       Hkv, N, d, dv, block, hs) == hipSuccess
                ? LA_OK

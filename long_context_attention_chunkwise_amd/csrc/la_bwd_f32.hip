@@ -20,6 +20,7 @@
 // dv (it holds R's columns of its slice); the dK kernel slices d (it holds R's
 // rows of its slice); each recomputes the score block it needs.
 #include "la_internal.h"
+#include "la_scalar.h"
 
 namespace la {
 namespace {
@@ -29,9 +30,11 @@ constexpr int kSlice = 32;
 constexpr int kMaxD = 128;
 constexpr int kMaxBlock = 64;
 
-// dV[:, c0:c0+32] and ds_in[:, c0:c0+32].
-__global__ __launch_bounds__(kThreads) void bwd_dv_f32(const float* __restrict__ q, const float* __restrict__ k,
-                                                      const float* __restrict__ dout, float* __restrict__ dvg,
+// dV[:, c0:c0+32] and ds_in[:, c0:c0+32].  TI / TG: storage types of the
+// inputs and of the gradients (float or bf16 bits); float32 arithmetic.
+template <typename TI, typename TG>
+__global__ __launch_bounds__(kThreads) void bwd_dv_f32(const TI* __restrict__ q, const TI* __restrict__ k,
+                                                      const TI* __restrict__ dout, TG* __restrict__ dvg,
                                                       const float* ds_out, float* ds_in, int Hq, int Hkv,
                                                       int64_t N, int d, int dv, int C) {
   __shared__ float Ks[kMaxBlock][kMaxD + 1];    // K_b
@@ -48,7 +51,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dv_f32(const float* __restrict__
   const int G = Hq / Hkv;
   const int tid = threadIdx.x;
   const int c0 = slice * kSlice;
-  const float* kh = k + int64_t(bg) * N * d;
+  const TI* kh = k + int64_t(bg) * N * d;
   const int64_t sbase = int64_t(bg) * d * dv;
 
   for (int e = tid; e < d * kSlice; e += kThreads) {
@@ -62,7 +65,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dv_f32(const float* __restrict__
     __syncthreads();  // the previous block's stores and R updates are done
     for (int e = tid; e < c * d; e += kThreads) {
       const int t = e / d, i = e % d;
-      Ks[t][i] = kh[(a + t) * d + i];
+      Ks[t][i] = ldf(kh, (a + t) * d + i);
     }
     __syncthreads();
     // inter: K_b R with R over later tokens only
@@ -77,11 +80,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dv_f32(const float* __restrict__
       __syncthreads();  // the inter term and the previous head are done with Qs, Os, Xs, Rs
       for (int e = tid; e < c * d; e += kThreads) {
         const int t = e / d, i = e % d;
-        Qs[t][i] = q[(bh * N + a + t) * d + i];
+        Qs[t][i] = ldf(q, (bh * N + a + t) * d + i);
       }
       for (int e = tid; e < c * kSlice; e += kThreads) {
         const int t = e / kSlice, n = e % kSlice;
-        Os[t][n] = dout[(bh * N + a + t) * dv + c0 + n];
+        Os[t][n] = ldf(dout, (bh * N + a + t) * dv + c0 + n);
       }
       __syncthreads();
       for (int e = tid; e < c * c; e += kThreads) {
@@ -109,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dv_f32(const float* __restrict__
     __syncthreads();
     for (int e = tid; e < c * kSlice; e += kThreads) {
       const int s = e / kSlice, n = e % kSlice;
-      dvg[(int64_t(bg) * N + a + s) * dv + c0 + n] = As[s][n];
+      stf(dvg, (int64_t(bg) * N + a + s) * dv + c0 + n, As[s][n]);
     }
   }
   __syncthreads();
@@ -121,8 +124,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dv_f32(const float* __restrict__
 }
 
 // dK[:, c0:c0+32].
-__global__ __launch_bounds__(kThreads) void bwd_dk_f32(const float* __restrict__ q, const float* __restrict__ v,
-                                                      const float* __restrict__ dout, float* __restrict__ dkg,
+template <typename TI, typename TG>
+__global__ __launch_bounds__(kThreads) void bwd_dk_f32(const TI* __restrict__ q, const TI* __restrict__ v,
+                                                      const TI* __restrict__ dout, TG* __restrict__ dkg,
                                                       const float* ds_out, int Hq, int Hkv, int64_t N, int d,
                                                       int dv, int C) {
   __shared__ float Vs[kMaxBlock][kMaxD + 1];    // V_b
@@ -139,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dk_f32(const float* __restrict__
   const int G = Hq / Hkv;
   const int tid = threadIdx.x;
   const int c0 = slice * kSlice;
-  const float* vh = v + int64_t(bg) * N * dv;
+  const TI* vh = v + int64_t(bg) * N * dv;
   const int64_t sbase = int64_t(bg) * d * dv;
 
   for (int e = tid; e < kSlice * dv; e += kThreads) {
@@ -153,7 +157,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dk_f32(const float* __restrict__
     __syncthreads();
     for (int e = tid; e < c * dv; e += kThreads) {
       const int t = e / dv, n = e % dv;
-      Vs[t][n] = vh[(a + t) * dv + n];
+      Vs[t][n] = ldf(vh, (a + t) * dv + n);
     }
     __syncthreads();
     // inter: V_b R^T over this slice's rows of R
@@ -168,11 +172,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dk_f32(const float* __restrict__
       __syncthreads();
       for (int e = tid; e < c * dv; e += kThreads) {
         const int t = e / dv, n = e % dv;
-        Os[t][n] = dout[(bh * N + a + t) * dv + n];
+        Os[t][n] = ldf(dout, (bh * N + a + t) * dv + n);
       }
       for (int e = tid; e < c * kSlice; e += kThreads) {
         const int t = e / kSlice, i = e % kSlice;
-        Qs[t][i] = q[(bh * N + a + t) * d + c0 + i];
+        Qs[t][i] = ldf(q, (bh * N + a + t) * d + c0 + i);
       }
       __syncthreads();
       for (int e = tid; e < c * c; e += kThreads) {
@@ -199,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dk_f32(const float* __restrict__
     __syncthreads();
     for (int e = tid; e < c * kSlice; e += kThreads) {
       const int s = e / kSlice, i = e % kSlice;
-      dkg[(int64_t(bg) * N + a + s) * d + c0 + i] = As[s][i];
+      stf(dkg, (int64_t(bg) * N + a + s) * d + c0 + i, As[s][i]);
     }
   }
 }
@@ -220,11 +224,30 @@ size_t bwd_f32_workspace_floats(int64_t B, int64_t Hkv, int64_t d, int64_t dv) {
   return size_t(B * Hkv) * size_t(d * dv);
 }
 
-hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* dout, float* dq, float* dk,
-                          float* dvg, const float* s_in, const float* ds_out, float* ds_in, int64_t B, int64_t Hq,
-                          int64_t Hkv, int64_t N, int64_t d, int64_t dv, int64_t block, float* workspace,
-                          hipStream_t stream) {
-  // dQ: the float32 forward over (queries dO, keys V, values K) from s_in^T
+namespace {
+
+template <typename TI, typename TG>
+void launch_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dvg,
+                 const float* ds_out, float* ds_in, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                 int64_t dv, int64_t block, hipStream_t stream) {
+  const TI *qt = static_cast<const TI*>(q), *kt = static_cast<const TI*>(k), *vt = static_cast<const TI*>(v);
+  const TI* ot = static_cast<const TI*>(dout);
+  // dK first: it reads ds_out, which the dV kernel may overwrite (ds_in may be
+  // ds_out itself; each dV workgroup reads and writes only its own columns).
+  hipLaunchKernelGGL((bwd_dk_f32<TI, TG>), dim3(unsigned(B * Hkv * (d / kSlice))), dim3(kThreads), 0, stream, qt,
+                     vt, ot, static_cast<TG*>(dk), ds_out, int(Hq), int(Hkv), N, int(d), int(dv), int(block));
+  hipLaunchKernelGGL((bwd_dv_f32<TI, TG>), dim3(unsigned(B * Hkv * (dv / kSlice))), dim3(kThreads), 0, stream, qt,
+                     kt, ot, static_cast<TG*>(dvg), ds_out, ds_in, int(Hq), int(Hkv), N, int(d), int(dv),
+                     int(block));
+}
+
+}  // namespace
+
+hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
+                          void* dvg, bool in_bf16, bool grad_bf16, const float* s_in, const float* ds_out,
+                          float* ds_in, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv,
+                          int64_t block, float* workspace, hipStream_t stream) {
+  // dQ: the scalar forward over (queries dO, keys V, values K) from s_in^T
   const float* s_t = nullptr;
   if (s_in != nullptr) {
     const int64_t n = B * Hkv * d * dv;
@@ -232,14 +255,16 @@ hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const 
                        B * Hkv, int(d), int(dv));
     s_t = workspace;
   }
-  hipError_t e = launch_fwd_f32(dout, v, k, dq, s_t, nullptr, B, Hq, Hkv, N, dv, d, block, stream);
+  hipError_t e = launch_fwd_f32(dout, v, k, dq, in_bf16, grad_bf16, s_t, nullptr, B, Hq, Hkv, N, dv, d, block,
+                                stream);
   if (e != hipSuccess) return e;
-  // dK first: it reads ds_out, which the dV kernel may overwrite (ds_in may be
-  // ds_out itself; each dV workgroup reads and writes only its own columns).
-  hipLaunchKernelGGL(bwd_dk_f32, dim3(unsigned(B * Hkv * (d / kSlice))), dim3(kThreads), 0, stream, q, v, dout, dk,
-                     ds_out, int(Hq), int(Hkv), N, int(d), int(dv), int(block));
-  hipLaunchKernelGGL(bwd_dv_f32, dim3(unsigned(B * Hkv * (dv / kSlice))), dim3(kThreads), 0, stream, q, k, dout, dvg,
-                     ds_out, ds_in, int(Hq), int(Hkv), N, int(d), int(dv), int(block));
+  if (in_bf16) {
+    if (grad_bf16) launch_dkdv<uint16_t, uint16_t>(q, k, v, dout, dk, dvg, ds_out, ds_in, B, Hq, Hkv, N, d, dv, block, stream);
+    else launch_dkdv<uint16_t, float>(q, k, v, dout, dk, dvg, ds_out, ds_in, B, Hq, Hkv, N, d, dv, block, stream);
+  } else {
+    if (grad_bf16) launch_dkdv<float, uint16_t>(q, k, v, dout, dk, dvg, ds_out, ds_in, B, Hq, Hkv, N, d, dv, block, stream);
+    else launch_dkdv<float, float>(q, k, v, dout, dk, dvg, ds_out, ds_in, B, Hq, Hkv, N, d, dv, block, stream);
+  }
   return hipGetLastError();
 }
 

@@ -13,6 +13,7 @@
 // the forward variants for float32 inputs (ReLU feature map, normalisation,
 // non-causal form).
 #include "la_internal.h"
+#include "la_scalar.h"
 
 namespace la {
 namespace {
@@ -31,10 +32,12 @@ constexpr int kFlagNorm = 2;
 // slice's workgroup keeps its own copy).  Non-causal (CAUSAL false): a first
 // pass sums the state (and z) over every block, a second pass forms
 // o_t = phi(q_t) S_tot for every row.
-template <int FL, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restrict__ q,
-                                                          const float* __restrict__ k,
-                                                          const float* __restrict__ v, float* __restrict__ o,
+//
+// TI / TO: storage types of q, k, v and of o (float or bf16 bits); the
+// arithmetic is float32 either way.
+template <typename TI, typename TO, int FL, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
+                                                          const TI* __restrict__ v, TO* __restrict__ o,
                                                           const float* s_in, float* s_out, const float* z_in,
                                                           float eps, int Hq, int Hkv, int64_t N, int d, int dv,
                                                           int C) {
@@ -56,8 +59,8 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
   const int tid = threadIdx.x;
   const int c0 = slice * kSlice;
 
-  const float* kh = k + int64_t(bg) * N * d;
-  const float* vh = v + int64_t(bg) * N * dv;
+  const TI* kh = k + int64_t(bg) * N * d;
+  const TI* vh = v + int64_t(bg) * N * dv;
   const int64_t sbase = int64_t(bg) * d * dv;
   auto phi = [](float x) { return kR ? fmaxf(x, 0.0f) : x; };
 
@@ -72,11 +75,11 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
   auto load_kv = [&](int64_t a, int c) {
     for (int e = tid; e < c * d; e += kThreads) {
       int t = e / d, i = e % d;
-      Ks[t][i] = phi(kh[(a + t) * d + i]);
+      Ks[t][i] = phi(ldf(kh, (a + t) * d + i));
     }
     for (int e = tid; e < c * kSlice; e += kThreads) {
       int t = e / kSlice, n = e % kSlice;
-      Vs[t][n] = vh[(a + t) * dv + c0 + n];
+      Vs[t][n] = ldf(vh, (a + t) * dv + c0 + n);
     }
   };
   // S += K^T V (and z += sum of the K rows) after the block's outputs.
@@ -111,12 +114,12 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
     if constexpr (CAUSAL) load_kv(a, c);
     for (int hh = 0; hh < G; ++hh) {
       const int64_t bh = int64_t(b) * Hq + int64_t(g) * G + hh;
-      const float* qh = q + bh * N * d;
-      float* oh = o + bh * N * dv;
+      const TI* qh = q + bh * N * d;
+      TO* oh = o + bh * N * dv;
       __syncthreads();  // previous head finished with Qs/Ps/Den
       for (int e = tid; e < c * d; e += kThreads) {
         int t = e / d, i = e % d;
-        Qs[t][i] = phi(qh[(a + t) * d + i]);
+        Qs[t][i] = phi(ldf(qh, (a + t) * d + i));
       }
       __syncthreads();
       if constexpr (CAUSAL) {
@@ -150,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
           for (int s = 0; s <= t; ++s) intra = fmaf(Ps[t][s], Vs[s][n], intra);
         float out = inter + intra;
         if constexpr (kN) out = out / Den[t];
-        oh[(a + t) * dv + c0 + n] = out;
+        stf(oh, (a + t) * dv + c0 + n, out);
       }
     }
     if constexpr (CAUSAL) {
@@ -170,16 +173,19 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
 // z_out[c][i] = z_in[c][i] (or 0) + sum over every token of phi(k[c][t][i]);
 // one thread per (KV chain, i).  Runs after the output kernel, so z_out may be
 // z_in itself.
-template <bool RELU>
-__global__ void z_sum_f32(const float* __restrict__ k, const float* z_in, float* z_out, int64_t chains, int64_t N,
+template <typename TI, bool RELU>
+__global__ void z_sum_f32(const TI* __restrict__ k, const float* z_in, float* z_out, int64_t chains, int64_t N,
                           int d) {
   const int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (e >= chains * d) return;
   const int64_t c = e / d;
   const int i = int(e % d);
-  const float* kc = k + c * N * d + i;
+  const TI* kc = k + c * N * d + i;
   float acc = z_in ? z_in[e] : 0.0f;
-  for (int64_t t = 0; t < N; ++t) acc += RELU ? fmaxf(kc[t * d], 0.0f) : kc[t * d];
+  for (int64_t t = 0; t < N; ++t) {
+    const float x = ldf(kc, t * d);
+    acc += RELU ? fmaxf(x, 0.0f) : x;
+  }
   z_out[e] = acc;
 }
 
@@ -196,24 +202,22 @@ hipError_t launch_copy_or_zero(float* dst, const float* src, size_t n, hipStream
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, const float* s_in,
-                          float* s_out, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv,
-                          int64_t block, hipStream_t stream) {
-  const int64_t grid = B * Hkv * (dv / kSlice);
-  hipLaunchKernelGGL((fwd_f32_kernel<0, true>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, q, k, v, o, s_in,
-                     s_out, nullptr, 0.0f, int(Hq), int(Hkv), N, int(d), int(dv), int(block));
-  return hipGetLastError();
-}
+namespace {
 
-hipError_t launch_fwd_f32_variant(const float* q, const float* k, const float* v, float* o, bool causal, bool relu,
-                                  bool norm, float eps, const float* s_in, float* s_out, const float* z_in,
-                                  float* z_out, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
-                                  int64_t dv, int64_t block, hipStream_t stream) {
+template <typename TI, typename TO>
+hipError_t launch_scalar(const void* q, const void* k, const void* v, void* o, bool causal, bool relu, bool norm,
+                         float eps, const float* s_in, float* s_out, const float* z_in, float* z_out, int64_t B,
+                         int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv, int64_t block,
+                         hipStream_t stream) {
   const dim3 grid(unsigned(B * Hkv * (dv / kSlice)));
   const int iHq = int(Hq), iHkv = int(Hkv), id = int(d), idv = int(dv), ib = int(block);
-#define LA_F32V(FL, CAUSAL)                                                                                         \
-  hipLaunchKernelGGL((fwd_f32_kernel<FL, CAUSAL>), grid, dim3(kThreads), 0, stream, q, k, v, o, s_in, s_out, z_in, \
-                     eps, iHq, iHkv, N, id, idv, ib)
+  const TI* qt = static_cast<const TI*>(q);
+  const TI* kt = static_cast<const TI*>(k);
+  const TI* vt = static_cast<const TI*>(v);
+  TO* ot = static_cast<TO*>(o);
+#define LA_F32V(FL, CAUSAL)                                                                                     \
+  hipLaunchKernelGGL((fwd_f32_kernel<TI, TO, FL, CAUSAL>), grid, dim3(kThreads), 0, stream, qt, kt, vt, ot, s_in, \
+                     s_out, z_in, eps, iHq, iHkv, N, id, idv, ib)
   const int fl = (relu ? kFlagRelu : 0) | (norm ? kFlagNorm : 0);
   switch (fl + (causal ? 4 : 0)) {
     case 0: LA_F32V(0, false); break;
@@ -230,12 +234,37 @@ hipError_t launch_fwd_f32_variant(const float* q, const float* k, const float* v
   if (e != hipSuccess || !norm || z_out == nullptr) return e;
   const int64_t nz = B * Hkv * d;
   if (relu)
-    hipLaunchKernelGGL((z_sum_f32<true>), dim3(unsigned((nz + 255) / 256)), dim3(256), 0, stream, k, z_in, z_out,
-                       B * Hkv, N, id);
+    hipLaunchKernelGGL((z_sum_f32<TI, true>), dim3(unsigned((nz + 255) / 256)), dim3(256), 0, stream, kt, z_in,
+                       z_out, B * Hkv, N, id);
   else
-    hipLaunchKernelGGL((z_sum_f32<false>), dim3(unsigned((nz + 255) / 256)), dim3(256), 0, stream, k, z_in, z_out,
-                       B * Hkv, N, id);
+    hipLaunchKernelGGL((z_sum_f32<TI, false>), dim3(unsigned((nz + 255) / 256)), dim3(256), 0, stream, kt, z_in,
+                       z_out, B * Hkv, N, id);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_f32_variant(const void* q, const void* k, const void* v, void* o, bool in_bf16,
+                                  bool out_bf16, bool causal, bool relu, bool norm, float eps, const float* s_in,
+                                  float* s_out, const float* z_in, float* z_out, int64_t B, int64_t Hq,
+                                  int64_t Hkv, int64_t N, int64_t d, int64_t dv, int64_t block,
+                                  hipStream_t stream) {
+  if (in_bf16)
+    return out_bf16 ? launch_scalar<uint16_t, uint16_t>(q, k, v, o, causal, relu, norm, eps, s_in, s_out, z_in,
+                                                         z_out, B, Hq, Hkv, N, d, dv, block, stream)
+                    : launch_scalar<uint16_t, float>(q, k, v, o, causal, relu, norm, eps, s_in, s_out, z_in,
+                                                      z_out, B, Hq, Hkv, N, d, dv, block, stream);
+  return out_bf16 ? launch_scalar<float, uint16_t>(q, k, v, o, causal, relu, norm, eps, s_in, s_out, z_in, z_out, B,
+                                                    Hq, Hkv, N, d, dv, block, stream)
+                  : launch_scalar<float, float>(q, k, v, o, causal, relu, norm, eps, s_in, s_out, z_in, z_out, B, Hq,
+                                                 Hkv, N, d, dv, block, stream);
+}
+
+hipError_t launch_fwd_f32(const void* q, const void* k, const void* v, void* o, bool in_bf16, bool out_bf16,
+                          const float* s_in, float* s_out, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                          int64_t dv, int64_t block, hipStream_t stream) {
+  return launch_fwd_f32_variant(q, k, v, o, in_bf16, out_bf16, true, false, false, 0.0f, s_in, s_out, nullptr,
+                                nullptr, B, Hq, Hkv, N, d, dv, block, stream);
 }
 
 }  // namespace la

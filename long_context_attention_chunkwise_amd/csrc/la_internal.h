@@ -34,18 +34,23 @@ struct Bf16Plan {
 
 Bf16Plan plan_bf16(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv, int cus);
 
-hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o,
-                          const float* s_in, float* s_out, int64_t B, int64_t Hq, int64_t Hkv,
-                          int64_t N, int64_t d, int64_t dv, int64_t block, hipStream_t stream);
+// Scalar (float32 FMA) forward: q, k, v stored as float32 or bf16 (in_bf16),
+// o as float32 or bf16 (out_bf16); d up to 128, dv a multiple of 32 up to
+// 128, blocks of up to 64 tokens.  It serves float32 inputs, and bf16 inputs
+// at shapes the matrix-core kernels are not built for.  No workspace.
+hipError_t launch_fwd_f32(const void* q, const void* k, const void* v, void* o, bool in_bf16, bool out_bf16,
+                          const float* s_in, float* s_out, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                          int64_t dv, int64_t block, hipStream_t stream);
 
-// Forward variants for float32 inputs (same shapes as launch_fwd_f32): phi =
-// ReLU on q and k (relu), division by phi(q_t) . z_t + eps (norm, with z_in /
-// z_out the normaliser sums; z_out may be z_in), causal or non-causal.  No
-// workspace.
-hipError_t launch_fwd_f32_variant(const float* q, const float* k, const float* v, float* o, bool causal, bool relu,
-                                  bool norm, float eps, const float* s_in, float* s_out, const float* z_in,
-                                  float* z_out, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
-                                  int64_t dv, int64_t block, hipStream_t stream);
+// Forward variants on the scalar kernel (same storage types and shapes as
+// launch_fwd_f32): phi = ReLU on q and k (relu), division by phi(q_t) . z_t +
+// eps (norm, with z_in / z_out the normaliser sums; z_out may be z_in), causal
+// or non-causal.  No workspace.
+hipError_t launch_fwd_f32_variant(const void* q, const void* k, const void* v, void* o, bool in_bf16,
+                                  bool out_bf16, bool causal, bool relu, bool norm, float eps, const float* s_in,
+                                  float* s_out, const float* z_in, float* z_out, int64_t B, int64_t Hq,
+                                  int64_t Hkv, int64_t N, int64_t d, int64_t dv, int64_t block,
+                                  hipStream_t stream);
 
 // Segment start states into the workspace (pre-pass + scan); only when
 // plan.use_starts.
@@ -117,15 +122,16 @@ hipError_t launch_bwd_kv(const void* q, const void* k, const void* v, const void
                          bool out_f32, const float* ds_out, float* ds_in, int64_t B, int64_t Hq, int64_t Hkv,
                          int64_t N, const BwdPlan& plan, float* workspace_f, hipStream_t stream);
 
-// float32 backward (float32 inputs and gradients, d and dv multiples of 32 up
-// to 128, blocks of up to 64 tokens): dQ by the float32 forward over
-// (dO, V, K) from s_in^T, then dK and dV (and ds_in) by the reverse
-// recurrence.  The workspace holds s_in^T (bwd_f32_workspace_floats floats).
+// Scalar (float32 FMA) backward (inputs and gradients stored as float32 or
+// bf16, d and dv multiples of 32 up to 128, blocks of up to 64 tokens): dQ by
+// the scalar forward over (dO, V, K) from s_in^T, then dK and dV (and ds_in)
+// by the reverse recurrence.  The workspace holds s_in^T
+// (bwd_f32_workspace_floats floats).
 size_t bwd_f32_workspace_floats(int64_t B, int64_t Hkv, int64_t d, int64_t dv);
-hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* dout, float* dq, float* dk,
-                          float* dvg, const float* s_in, const float* ds_out, float* ds_in, int64_t B, int64_t Hq,
-                          int64_t Hkv, int64_t N, int64_t d, int64_t dv, int64_t block, float* workspace,
-                          hipStream_t stream);
+hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
+                          void* dvg, bool in_bf16, bool grad_bf16, const float* s_in, const float* ds_out,
+                          float* ds_in, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv,
+                          int64_t block, float* workspace, hipStream_t stream);
 
 // dst[i] = src ? src[i] : 0 for i < n.
 hipError_t launch_copy_or_zero(float* dst, const float* src, size_t n, hipStream_t stream);

@@ -58,7 +58,8 @@ def test_forward_validation(lib):
     assert fwd(lib, Hq=6, Hkv=4) == SHAPE
     assert fwd(lib, B=0) == SHAPE
     assert fwd(lib, N=-1) == SHAPE
-    assert fwd(lib, d=64) == UNSUP                       # bf16 path is d = dv = 128
+    assert fwd(lib, d=64, dv=48) == UNSUP                # scalar kernels: dv a multiple of 32
+    assert fwd(lib, d=256) == UNSUP                      # head sizes up to 128
     assert fwd(lib, block=128) == UNSUP
     assert fwd(lib, B=1 << 12, Hq=1 << 12, Hkv=1 << 12, N=1 << 30) == UNSUP   # byte counts would overflow
     assert fwd(lib, B=1 << 40, Hq=1 << 40, Hkv=1 << 40, N=1) == UNSUP          # B * Hq itself would overflow
@@ -102,7 +103,7 @@ def test_backward_validation(lib):
     assert bwd(lib, i=F32, g=F32, d=48, dvs=64) == UNSUP   # float32: d a multiple of 32
     assert bwd(lib, i=F32, g=F32, d=64, dvs=64, block=128) == UNSUP   # float32: blocks of up to 64
     assert bwd(lib, i=F32, g=F32, d=64, dvs=64, ws=None) == WORKSPACE
-    assert bwd(lib, d=64) == UNSUP
+    assert bwd(lib, d=48) == UNSUP                         # scalar kernels: d a multiple of 32
     assert bwd(lib, g=2) == UNSUP
     assert bwd(lib, dq=ctypes.c_void_p(GB * 9 + 8)) == ALIGN
     assert bwd(lib, dq=ctypes.c_void_p(GB * 1 + 4096)) == ALIAS       # dq inside q
@@ -123,7 +124,7 @@ def var(lib, q=Q, k=K, v=V, o=O, B=1, Hq=4, Hkv=1, N=1000, d=128, dv=128, block=
 def test_variant_validation(lib):
     assert var(lib, q=None) == NULL
     assert var(lib, Hq=6, Hkv=4) == SHAPE
-    assert var(lib, d=64, dv=64) == UNSUP                 # bf16 path: d = dv = 128
+    assert var(lib, d=64, dv=48) == UNSUP                 # scalar kernels: dv a multiple of 32
     assert var(lib, i=F32, out=BF16) == UNSUP             # float32 inputs give float32 outputs
     assert var(lib, i=F32, out=F32, d=64, dv=48) == UNSUP  # float32: dv a multiple of 32
     assert lib.la_forward_variant_workspace_bytes(1, 4, 1, 1000, 64, 64, 64, F32, 0, 1) == 0   # float32: none
@@ -160,6 +161,9 @@ def test_workspace_plan(lib):
     assert lib.la_backward_workspace_bytes(1, 128, 32, 0, 128, 128, 64, BF16) == 0
     assert lib.la_backward_workspace_bytes(1, 4, 2, 64, 128, 96, 64, F32) == 2 * 128 * 96 * 4   # s_in^T
     assert lib.la_backward_workspace_bytes(1, 4, 2, 64, 48, 96, 64, F32) == 0                  # d not a multiple of 32
+    # bf16 at other head sizes runs on the scalar kernels: no forward workspace, s_in^T for the backward
+    assert lib.la_forward_workspace_bytes(1, 4, 1, 1000, 64, 64, 64, BF16) == 0
+    assert lib.la_backward_workspace_bytes(1, 4, 2, 64, 64, 96, 64, BF16) == 2 * 64 * 96 * 4
     # Variants at 1M tokens: causal = the forward's split (+ normaliser sums);
     # non-causal sums all 8 segments of each chain (3 parts each) and scans
     # 9 entries, the last being the total.
