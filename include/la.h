@@ -13,9 +13,9 @@
  *     o_t = q_t . s_in + sum_{s <= t} (q_t . k_s) v_s,
  * for every block size (associativity; page "MiniMax-01与Lightning Attention",
  * section 2.2).  Apart from la_forward_variant, no normalisation, scaling or
- * feature map is applied: q and k arrive already feature-mapped.  Query head h reads KV head h / (Hq / Hkv)
- * (grouped-query attention with contiguous groups; same page, section 1.1
- * table: 128 heads over 32 KV heads).
+ * feature map is applied: q and k arrive already feature-mapped.  Query head
+ * h reads KV head h / (Hq / Hkv) (grouped-query attention with contiguous
+ * groups; same page, section 1.1 table: 128 heads over 32 KV heads).
  *
  * Layouts (all row-major and contiguous, element strides implied by the
  * sizes, every pointer 16-byte aligned):

@@ -14,7 +14,9 @@
 // walked from the last block to the first; ds_in is the final R.
 //
 // All arithmetic is float32 FMA, so this path serves float32 inputs at float32
-// accuracy.  Like the float32 forward it is the small-problem path: one
+// accuracy, and bf16 inputs (widened exactly as they are loaded) at the shapes
+// the matrix-core kernels are not built for.  Like the float32 forward it is
+// the small-problem path: one
 // workgroup per (batch, KV head, 32-column slice) walks the whole sequence
 // backwards and serves every query head of the group.  The dV kernel slices
 // dv (it holds R's columns of its slice); the dK kernel slices d (it holds R's

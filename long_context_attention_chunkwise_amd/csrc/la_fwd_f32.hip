@@ -4,7 +4,9 @@
 // 技术底座" (vergex.cn), section "Lightning Attention", chunkwise teaching code:
 // O_b = Q_b S + tril(Q_b K_b^T) V_b, then S += K_b^T V_b.  All arithmetic is
 // float32 FMA (no reduced-precision products), so this path serves float32
-// inputs at float32 accuracy.  It is the small-problem path: one workgroup per
+// inputs at float32 accuracy, and bf16 inputs (widened exactly as they are
+// loaded) at the shapes the matrix-core kernels are not built for.  It is the
+// small-problem path: one workgroup per
 // (batch, KV head, 32-column slice of dv) walks the whole sequence and serves
 // every query head of the group, with the state slice, the block's K and V
 // slice and, one head at a time, Q and the score matrix staged in LDS.  The
