@@ -72,13 +72,19 @@ typedef void* la_stream;
  * Causal forward pass, zero initial state, final state discarded.
  * in_dtype / out_dtype:
  *   LA_F32  -> LA_F32   float32 arithmetic throughout (no reduced precision);
- *                       d in 1..128, dv a multiple of 32 up to 128, block 1..64.
+ *                       d in 1..128, dv a multiple of 32 up to 128.
  *   LA_BF16 -> LA_BF16 or LA_F32
- *                       d = dv = 128, block = 64: bf16 matrix-core products with
- *                       float32 accumulation and a float32 state.  Other shapes
- *                       within the LA_F32 limits: the float32 FMA kernels on the
+ *                       d = dv = 128: bf16 matrix-core products with float32
+ *                       accumulation and a float32 state.  Other shapes within
+ *                       the LA_F32 limits: the float32 FMA kernels on the
  *                       exactly widened inputs (a small-problem path, workspace
  *                       size 0).
+ * block: 1..64, or any multiple of 64 up to 2^20 tokens (the pages' chunkwise
+ * code defaults to 128-token blocks).  A multiple of 64 is computed as 64-token
+ * blocks, the tile the kernels are built for: since the chunkwise form is an
+ * exact re-association of the causal sum, the result is the same for every
+ * block size up to rounding.  A block below 64 is taken as given (float32 FMA
+ * kernels only; the matrix-core kernels need a multiple of 64).
  * N may be 0 (then q, k, v and o may be NULL and only s_out is written) and
  * need not be a multiple of block: the last block is shorter.  Temporary
  * workspace (see la_forward_workspace_bytes) is allocated stream-ordered on
@@ -186,10 +192,11 @@ la_status la_decode_step(float* S, const void* q, const void* k, const void* v, 
  *   z_in, z_out   [B][Hkv][d] float32 normaliser sums, or NULL; only with
  *                 normalize = 1 (LA_ERR_UNSUPPORTED otherwise).  z_out may
  *                 equal z_in.
- * in_dtype LA_BF16 (matrix-core kernels at d = dv = 128, block = 64; out_dtype
- * LA_BF16 or LA_F32) or LA_F32 (out_dtype LA_F32).  Other shapes, d up to 128,
- * dv a multiple of 32 up to 128, block up to 64, run on the float32 FMA kernels
- * (workspace size 0), for bf16 inputs too.  Any Hq / Hkv.
+ * in_dtype LA_BF16 (matrix-core kernels at d = dv = 128, block a multiple of
+ * 64; out_dtype LA_BF16 or LA_F32) or LA_F32 (out_dtype LA_F32).  Other shapes,
+ * d up to 128, dv a multiple of 32 up to 128, block as for la_forward, run on
+ * the float32 FMA kernels (workspace size 0), for bf16 inputs too.  Any
+ * Hq / Hkv.
  * causal = 1, LA_FMAP_IDENTITY, normalize = 0 computes exactly la_forward_ex.
  * Workspace: la_forward_variant_workspace_bytes (may be 0).
  */
@@ -234,10 +241,10 @@ size_t la_forward_variant_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, in
  *   q, k, v        the forward's inputs (layouts as above).
  *   grad_o         [B][Hq][N][dv], in_dtype.
  *   in_dtype       LA_BF16: grad_dtype LA_BF16 or LA_F32; matrix-core
- *                  kernels at d = dv = 128, block = 64.  LA_F32: grad_dtype
- *                  LA_F32.  Other shapes, d and dv multiples of 32 up to 128
- *                  and block up to 64, run on float32 FMA kernels (a
- *                  small-problem path), for bf16 inputs too.
+ *                  kernels at d = dv = 128, block a multiple of 64.  LA_F32:
+ *                  grad_dtype LA_F32.  Other shapes, d and dv multiples of 32
+ *                  up to 128 and block as for la_forward, run on float32 FMA
+ *                  kernels (a small-problem path), for bf16 inputs too.
  *   grad_q, grad_k, grad_v   outputs shaped like q, k, v, in grad_dtype;
  *                  every element is written.
  *   s_in           the forward's initial state, or NULL for zeros (used for dq).

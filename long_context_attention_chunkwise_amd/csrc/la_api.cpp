@@ -33,11 +33,18 @@ int device_cus() {
   return cus;
 }
 
-// bf16 inputs with d = dv = 128 and 64-token blocks run on the matrix-core
+// Block sizes.  The result does not depend on the block size (the chunkwise
+// form re-associates the causal sum exactly), so a block that is a multiple
+// of 64 tokens is computed as 64-token blocks, the tile both kernel families
+// are built for; a shorter block is honoured by the scalar kernels.
+constexpr int64_t kMaxBlockArg = int64_t(1) << 20;
+int64_t tile_block(int64_t block) { return block % kBf16Block == 0 ? kBf16Block : block; }
+
+// bf16 inputs with d = dv = 128 and 64-token tiles run on the matrix-core
 // kernels; every other supported shape (float32 inputs, or bf16 at other head
 // or block sizes) on the scalar float32-FMA kernels.
 bool mfma_path(la_dtype in_dtype, int64_t d, int64_t dv, int64_t block) {
-  return in_dtype == LA_BF16 && d == 128 && dv == 128 && block == kBf16Block;
+  return in_dtype == LA_BF16 && d == 128 && dv == 128 && tile_block(block) == kBf16Block;
 }
 
 // Shape/dtype checks shared by la_forward_ex and la_forward_workspace_bytes.
@@ -47,7 +54,8 @@ la_status check_forward_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int
   if (Hq % Hkv != 0) return LA_ERR_SHAPE;
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return LA_ERR_UNSUPPORTED;
   if (in_dtype == LA_F32 && out_dtype != LA_F32) return LA_ERR_UNSUPPORTED;
-  if (!mfma_path(in_dtype, d, dv, block) && (d > 128 || dv > 128 || dv % 32 != 0 || block > 64))
+  if (block > kMaxBlockArg) return LA_ERR_UNSUPPORTED;
+  if (!mfma_path(in_dtype, d, dv, block) && (d > 128 || dv > 128 || dv % 32 != 0 || tile_block(block) > 64))
     return LA_ERR_UNSUPPORTED;
   // Grid dimensions are 32-bit; keep the workgroup counts well inside that,
   // and keep every byte count (B * Hq * N * 128 elements of up to 4 bytes)
@@ -288,7 +296,7 @@ la_status run_outputs(const ForwardCall& fc, const void* q, const void* k, const
     if (s_out != nullptr && s_out != s_in) err = la::launch_copy_or_zero(s_out, s_in, fc.ns / sizeof(float), hs);
   } else if (fc.scalar) {
     err = la::launch_fwd_f32(q, k, v, o, in_dtype == LA_BF16, out_dtype == LA_BF16, s_in, s_out, B, Hq, Hkv, N, d,
-                             dv, block, hs);
+                             dv, tile_block(block), hs);
   } else {
     err = la::launch_fwd_bf16(q, k, v, o, out_dtype == LA_F32, s_in, s_out, B, Hq, Hkv, N, fc.plan, workspace,
                               hs);
@@ -461,7 +469,7 @@ la_status la_backward(const void* q, const void* k, const void* v, const void* g
 
   if (!mfma_path(in_dtype, d, dv, block))
     return la::launch_bwd_f32(q, k, v, grad_o, grad_q, grad_k, grad_v, in_dtype == LA_BF16, grad_dtype == LA_BF16,
-                              s_in, grad_s_out, grad_s_in, B, Hq, Hkv, N, d, dv, block,
+                              s_in, grad_s_out, grad_s_in, B, Hq, Hkv, N, d, dv, tile_block(block),
                               static_cast<float*>(workspace), hs) == hipSuccess
                ? LA_OK
                : LA_ERR_HIP;
@@ -567,7 +575,7 @@ la_status la_forward_variant(const void* q, const void* k, const void* v, void* 
   if (!mfma_path(in_dtype, d, dv, block))
     return la::launch_fwd_f32_variant(q, k, v, o, in_dtype == LA_BF16, out_dtype == LA_BF16, causal != 0,
                                       fmap == LA_FMAP_RELU, normalize != 0, eps, s_in, s_out, z_in, z_out, B, Hq,
-                                      Hkv, N, d, dv, block, hs) == hipSuccess
+                                      Hkv, N, d, dv, tile_block(block), hs) == hipSuccess
                ? LA_OK
                : LA_ERR_HIP;
   const la::VarPlan vp = la::plan_variant(B, Hq, Hkv, N, d, dv, device_cus(), causal != 0, normalize != 0);

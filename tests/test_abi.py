@@ -60,7 +60,8 @@ def test_forward_validation(lib):
     assert fwd(lib, N=-1) == SHAPE
     assert fwd(lib, d=64, dv=48) == UNSUP                # scalar kernels: dv a multiple of 32
     assert fwd(lib, d=256) == UNSUP                      # head sizes up to 128
-    assert fwd(lib, block=128) == UNSUP
+    assert fwd(lib, block=96) == UNSUP                   # above 64 tokens, multiples of 64 only
+    assert fwd(lib, block=(1 << 20) + 64) == UNSUP       # blocks of up to 2^20 tokens
     assert fwd(lib, B=1 << 12, Hq=1 << 12, Hkv=1 << 12, N=1 << 30) == UNSUP   # byte counts would overflow
     assert fwd(lib, B=1 << 40, Hq=1 << 40, Hkv=1 << 40, N=1) == UNSUP          # B * Hq itself would overflow
     assert fwd(lib, i=BF16, out=2) == UNSUP
@@ -101,7 +102,7 @@ def test_backward_validation(lib):
     assert bwd(lib, N=-1) == SHAPE
     assert bwd(lib, i=F32, g=BF16) == UNSUP                # float32 inputs take float32 gradients
     assert bwd(lib, i=F32, g=F32, d=48, dvs=64) == UNSUP   # float32: d a multiple of 32
-    assert bwd(lib, i=F32, g=F32, d=64, dvs=64, block=128) == UNSUP   # float32: blocks of up to 64
+    assert bwd(lib, i=F32, g=F32, d=64, dvs=64, block=96) == UNSUP    # float32: above 64, multiples of 64 only
     assert bwd(lib, i=F32, g=F32, d=64, dvs=64, ws=None) == WORKSPACE
     assert bwd(lib, d=48) == UNSUP                         # scalar kernels: d a multiple of 32
     assert bwd(lib, g=2) == UNSUP
@@ -148,6 +149,12 @@ def test_workspace_plan(lib):
     n = lib.la_forward_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, 64, BF16)
     assert n == (32 * 7 * 3 + 32 * 8) * 128 * 128 * 4
     assert lib.la_forward_workspace_bytes(1, 1, 1, 256, 64, 64, 64, F32) == 0
+    # a block that is a multiple of 64 tokens is computed as 64-token blocks: same plan
+    for blk in (128, 4096):
+        assert lib.la_forward_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, blk, BF16) == n
+        assert lib.la_backward_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, blk, BF16) == \
+            lib.la_backward_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, 64, BF16)
+    assert lib.la_forward_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, 96, BF16) == 0   # unsupported -> 0
     assert lib.la_forward_workspace_bytes(256, 128, 32, 8192, 128, 128, 64, BF16) == 0
     assert lib.la_forward_workspace_bytes(1, 128, 32, 0, 128, 128, 64, BF16) == 0
     assert lib.la_forward_workspace_bytes(1, 6, 4, 64, 128, 128, 64, BF16) == 0   # invalid -> 0
