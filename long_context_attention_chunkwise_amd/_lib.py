@@ -187,9 +187,10 @@ def forward_variant(q, k, v, causal=True, feature_map="identity", normalize=Fals
     """Forward variants (la_forward_variant): feature map "identity" or "relu"
     (phi = ReLU on q and k), causal or non-causal, optionally normalised by
     phi(q_t) . z_t + eps.  bf16 or float32 q, k, v; the matrix-core kernels
-    serve bf16 at d = dv = 128 and 64-token blocks, the float32 FMA kernels
-    every other shape the float32 forward takes (any Hq/Hkv).  Returns o and, with
-    return_state, (S_out, z_out) (z_out None unless normalize)."""
+    serve bf16 at d = dv = 128 (blocks that are multiples of 64), the float32
+    FMA kernels every other shape the float32 forward takes (any Hq/Hkv).
+    Returns o and, with return_state, (S_out, z_out) (z_out None unless
+    normalize)."""
     torch = _torch()
     lib = load_library()
     _check_tensor("q", q, 4, None)
