@@ -101,6 +101,14 @@ la_status la_forward(const void* q, const void* k, const void* v, void* o,
  *   s_out  [B][Hkv][d][dv] float32 state after token N-1, or NULL.
  *          s_out may equal s_in (in-place resume); any other overlap with an
  *          input is LA_ERR_ALIAS.
+ *   o      may be q itself (the output overwrites the queries, saving one
+ *          [B][Hq][N][dv] buffer) when in_dtype = out_dtype = LA_BF16,
+ *          d = dv = 128, block a multiple of 64 and Hq / Hkv a multiple of 4:
+ *          there each query row is read before the same output row is
+ *          written, by the same wave.  The result equals the out-of-place
+ *          one bit for bit.  Any other overlap of o with an input is
+ *          LA_ERR_ALIAS (la_forward and la_forward_outputs follow the same
+ *          rule).
  *   workspace / workspace_bytes: at least la_forward_workspace_bytes(...)
  *          bytes of device memory (may be NULL when that size is 0).  Its
  *          contents are scratch and need no initialisation.  Concurrent calls

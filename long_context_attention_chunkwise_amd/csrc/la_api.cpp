@@ -257,7 +257,13 @@ la_status validate_forward(ForwardCall& fc, const void* q, const void* k, const 
   const size_t ns = size_t(B * Hkv * d * dv) * sizeof(float);
   fc.ns = ns;
   fc.scalar = !mfma_path(in_dtype, d, dv, block);
-  if (overlap(o, no, q, nq) || overlap(o, no, k, nk) || overlap(o, no, v, nv) || overlap(o, no, s_in, ns))
+  // o may be q itself on the four-head matrix-core kernel, where each query
+  // head's rows are read and then written by one wave in program order.
+  const bool in_place = o != nullptr && o == q;
+  if (in_place && !(mfma_path(in_dtype, d, dv, block) && out_dtype == in_dtype && (Hq / Hkv) % 4 == 0))
+    return LA_ERR_ALIAS;
+  if ((!in_place && overlap(o, no, q, nq)) || overlap(o, no, k, nk) || overlap(o, no, v, nv) ||
+      overlap(o, no, s_in, ns))
     return LA_ERR_ALIAS;
   if (s_out != nullptr &&
       (overlap(s_out, ns, q, nq) || overlap(s_out, ns, k, nk) || overlap(s_out, ns, v, nv) ||

@@ -71,6 +71,11 @@ def test_forward_validation(lib):
     assert fwd(lib, q=ctypes.c_void_p(GB + 8)) == ALIGN
     assert fwd(lib, s_out=ctypes.c_void_p(GB * 6 + 4)) == ALIGN
     assert fwd(lib, o=ctypes.c_void_p(GB + 4096)) == ALIAS    # o inside q
+    # o == q (in place) only on the four-head matrix-core kernel, bf16 in and out
+    assert fwd(lib, o=Q, i=F32, out=F32) == ALIAS
+    assert fwd(lib, o=Q, out=F32) == ALIAS
+    assert fwd(lib, o=Q, Hq=2, Hkv=1) == ALIAS
+    assert fwd(lib, o=Q, d=64, dv=64) == ALIAS
     assert fwd(lib, s_out=ctypes.c_void_p(GB * 3 + 64)) == ALIAS  # s_out inside v
     assert fwd(lib, ws=None) == WORKSPACE
     assert fwd(lib, ws_bytes=1024) == WORKSPACE

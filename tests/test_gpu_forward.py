@@ -138,6 +138,29 @@ def test_bf16_deterministic():
     assert torch.equal(a, b) and torch.equal(Sa, Sb)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,N", [(1, 8, 2, 3001), (2, 8, 1, 1000), (1, 4, 1, 64)])
+def test_bf16_in_place_output(B, Hq, Hkv, N):
+    """o written over q (group sizes 4 and 8, ragged tail, state carry) equals
+    the out-of-place result bit for bit."""
+    need_gpu()
+    say(f"case in-place B={B} Hq={Hq} Hkv={Hkv} N={N}")
+    q, k, v = qkv(B, Hq, Hkv, N, 128, 128, torch.bfloat16, seed=N + Hq)
+    S0 = synth.random_state((B, Hkv, 128, 128), DEV, seed=N, scale=0.5)
+    o, S = la.forward(q, k, v, s_in=S0, return_state=True)
+    qi = q.clone()
+    oi, Si = la.forward(qi, k, v, s_in=S0, return_state=True, out=qi)
+    torch.cuda.synchronize()
+    assert oi.data_ptr() == qi.data_ptr()
+    assert torch.equal(oi, o) and torch.equal(Si, S)
+
+
+def test_bf16_in_place_rejected_off_the_four_head_kernel():
+    need_gpu()
+    q, k, v = qkv(1, 2, 1, 500, 128, 128, torch.bfloat16, seed=3)
+    with pytest.raises(la.LAError, match="LA_ERR_ALIAS"):
+        la.forward(q, k, v, out=q)
+
+
 def test_empty_sequence_state_passthrough():
     need_gpu()
     for dtype in (torch.bfloat16, torch.float32):
