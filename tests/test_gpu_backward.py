@@ -8,7 +8,8 @@ synth.make_grad, optional initial state and final-state gradient N(0,1)*0.5.
 Sizes span several 64-token blocks, several reverse segments per chain (the
 pre-pass over (Q, dO) and the reverse scan), ragged tails, group sizes 1 to 4
 and both gradient dtypes; the 1M-token workload is checked on its first and
-last 4096 tokens, where the oracle can compute the gradients exactly.
+last 4096 tokens and on a window across a segment boundary in the middle, with
+the states entering each window computed in float64.
 """
 import numpy as np
 import pytest
@@ -113,7 +114,9 @@ def test_backward_gqa_1m_slices():
     those tokens only), dk, dv, dq of the first 4096 tokens (the reverse state
     entering them is sum over the group's heads of Q^T dO over every later
     token, computed in float64 here), dq of the last 4096 tokens (from the
-    forward state of (V, K) before them) and the initial-state gradient."""
+    forward state of (V, K) before them) and the initial-state gradient; for
+    KV group 13, dq, dk, dv of a 4096-token window across a segment boundary
+    in the middle of the sequence."""
     need_gpu()
     w = synth.WORKLOADS["gqa_1m"]
     G = w.Hq // w.Hkv
@@ -151,6 +154,22 @@ def test_backward_gqa_1m_slices():
         check_close(f"group {g} dv tokens [0, {W})", f64(dv[:, gs, :W]), head[2], BF16, BF16)
         check_close(f"group {g} dq tokens [0, {W})", f64(dq[:, hs, :W]), head[0], BF16, BF16)
         check_close(f"group {g} ds_in", f64(ds[:, gs]), head[3], BF16, torch.float32)
+    # KV group 13: a window across the boundary of segments 3/4 (4 of 8 segments per chain),
+    # from the forward state of (K, V) before it and the reverse state after it, in float64
+    g, c = 13, N // 2
+    a, b = c - W // 2, c + W // 2
+    hs, gs = slice(g * G, (g + 1) * G), slice(g, g + 1)
+    S_a = oracle.final_state(f64(k[:, gs, :a]), f64(v[:, gs, :a]))
+    R = np.zeros((1, 1, w.d, w.dv))
+    for h in range(G):
+        qh = f64(q[:, g * G + h, b:])[0]
+        doh = f64(do[:, g * G + h, b:])[0]
+        R[0, 0] += qh.T @ doh
+        del qh, doh
+    mid = oracle.backward_chunkwise(f64(q[:, hs, a:b]), f64(k[:, gs, a:b]), f64(v[:, gs, a:b]),
+                                    f64(do[:, hs, a:b]), 64, S_a, R)
+    for name, x, r in zip(("dq", "dk", "dv"), (dq[:, hs, a:b], dk[:, gs, a:b], dv[:, gs, a:b]), mid[:3]):
+        check_close(f"group {g} {name} tokens [{a}, {b})", f64(x), r, BF16, BF16)
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,N,d,dv,block,state", [

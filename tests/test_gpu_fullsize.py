@@ -42,9 +42,10 @@ def test_gqa_64k_groups_and_states():
 
 def test_gqa_1m_slices_and_states():
     """B=1, 128/32 heads, N=1,048,576, through la_forward_states +
-    la_forward_outputs (the benchmark's step): KV groups 0 and 31 on the first
-    and last 65,536 tokens, their final states, finiteness of every output and
-    bitwise repeatability of the whole pass."""
+    la_forward_outputs (the benchmark's step): KV groups 0, 13 and 31 on the
+    first and last 65,536 tokens and on 8192-token windows across the
+    boundaries of segments 0/1 and 3/4, their final states, finiteness of every
+    output and bitwise repeatability of the whole pass."""
     need_gpu()
     w = synth.WORKLOADS["gqa_1m"]
     G = w.Hq // w.Hkv
@@ -71,11 +72,19 @@ def test_gqa_1m_slices_and_states():
     torch.cuda.synchronize()
     assert bool(torch.isfinite(o).all())
     W = 65536
-    for g in (0, 31):
+    seg = w.N // 8   # 8 segments per chain at 1M tokens, one workgroup each
+    for g in (0, 13, 31):
         ks_all, vs_all = f64(k[:, g:g + 1]), f64(v[:, g:g + 1])
         qs, ks, vs = group_slice(q, k, v, g, G, 0, W)
         check_close(f"group {g} tokens [0, {W})", f64(o[:, g * G:(g + 1) * G, :W]),
                     oracle.chunkwise(qs, ks, vs, w.block)[0], torch.bfloat16, torch.bfloat16)
+        # windows across the boundaries of segments 0/1 and 3/4, from the fp64 state before them
+        for c in (seg, 4 * seg):
+            a, b = c - 4096, c + 4096
+            S_a = oracle.final_state(ks_all[:, :, :a], vs_all[:, :, :a])
+            qs, ks, vs = group_slice(q, k, v, g, G, a, b)
+            check_close(f"group {g} tokens [{a}, {b})", f64(o[:, g * G:(g + 1) * G, a:b]),
+                        oracle.chunkwise(qs, ks, vs, w.block, S_a)[0], torch.bfloat16, torch.bfloat16)
         a = w.N - W
         S_a = oracle.final_state(ks_all[:, :, :a], vs_all[:, :, :a])
         qs, ks, vs = group_slice(q, k, v, g, G, a, w.N)
