@@ -503,6 +503,9 @@ def main():
         "cpu_baseline": cpu,
         "device": {"name": props.name, "gcnArchName": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count, "copy_gb_per_s": round(copy_gbs, 1)},
+        "inputs": {"generator": "synth.make_qkv (seeded torch draws)", "seed": 0,
+                   "outputs_checked_finite": True},
+        "software": {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None)},
     }
     print(json.dumps(rec), flush=True)
 
