@@ -74,7 +74,8 @@ typedef void* la_stream;
  *   LA_F32  -> LA_F32   float32 arithmetic throughout (no reduced precision);
  *                       d in 1..128, dv a multiple of 32 up to 128.
  *   LA_BF16 -> LA_BF16 or LA_F32
- *                       d = dv = 128: bf16 matrix-core products with float32
+ *                       d = dv = 128, and d = dv = 64 when Hq / Hkv is a
+ *                       multiple of 4: bf16 matrix-core products with float32
  *                       accumulation and a float32 state.  Other shapes within
  *                       the LA_F32 limits: the float32 FMA kernels on the
  *                       exactly widened inputs (a small-problem path, workspace
@@ -103,7 +104,8 @@ la_status la_forward(const void* q, const void* k, const void* v, void* o,
  *          input is LA_ERR_ALIAS.
  *   o      may be q itself (the output overwrites the queries, saving one
  *          [B][Hq][N][dv] buffer) when in_dtype = out_dtype = LA_BF16,
- *          d = dv = 128, block a multiple of 64 and Hq / Hkv a multiple of 4:
+ *          d = dv = 128 or 64, block a multiple of 64 and Hq / Hkv a
+ *          multiple of 4:
  *          there each query row is read before the same output row is
  *          written, by the same wave.  The result equals the out-of-place
  *          one bit for bit.  Any other overlap of o with an input is

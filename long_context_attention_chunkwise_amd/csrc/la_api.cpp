@@ -47,6 +47,15 @@ bool mfma_path(la_dtype in_dtype, int64_t d, int64_t dv, int64_t block) {
   return in_dtype == LA_BF16 && d == 128 && dv == 128 && tile_block(block) == kBf16Block;
 }
 
+// The forward also runs on the matrix cores at d = dv = 64 for groups of a
+// multiple of four query heads (the four-wave output kernel and its pre-pass
+// are built for head sizes 64 and 128).
+bool fwd_mfma_path(la_dtype in_dtype, int64_t d, int64_t dv, int64_t block, int64_t Hq, int64_t Hkv) {
+  if (mfma_path(in_dtype, d, dv, block)) return true;
+  return in_dtype == LA_BF16 && d == 64 && dv == 64 && tile_block(block) == kBf16Block && Hkv > 0 &&
+         Hq % Hkv == 0 && (Hq / Hkv) % 4 == 0;
+}
+
 // Shape/dtype checks shared by la_forward_ex and la_forward_workspace_bytes.
 la_status check_forward_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv,
                               int64_t block, la_dtype in_dtype, la_dtype out_dtype) {
@@ -75,6 +84,8 @@ namespace la {
 Bf16Plan plan_bf16(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv, int cus) {
   Bf16Plan p;
   const int64_t G = Hq / Hkv;
+  p.hd = static_cast<int>(d);
+  (void)dv;  // d = dv on the matrix-core path
   p.gw = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
   p.subgroups = static_cast<int>(G / p.gw);
   p.nblocks = (N + kBf16Block - 1) / kBf16Block;
@@ -224,7 +235,7 @@ size_t la_forward_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
                                   int64_t block, la_dtype in_dtype) {
   la_dtype out = in_dtype;
   if (check_forward_shape(B, Hq, Hkv, N, d, dv, block, in_dtype, out) != LA_OK) return 0;
-  if (!mfma_path(in_dtype, d, dv, block) || N == 0) return 0;
+  if (!fwd_mfma_path(in_dtype, d, dv, block, Hq, Hkv) || N == 0) return 0;
   return la::plan_bf16(B, Hq, Hkv, N, d, dv, device_cus()).workspace_bytes;
 }
 
@@ -256,11 +267,11 @@ la_status validate_forward(ForwardCall& fc, const void* q, const void* k, const 
   const size_t nv = size_t(B * Hkv * N * dv) * ei, no = size_t(B * Hq * N * dv) * eo;
   const size_t ns = size_t(B * Hkv * d * dv) * sizeof(float);
   fc.ns = ns;
-  fc.scalar = !mfma_path(in_dtype, d, dv, block);
+  fc.scalar = !fwd_mfma_path(in_dtype, d, dv, block, Hq, Hkv);
   // o may be q itself on the four-head matrix-core kernel, where each query
   // head's rows are read and then written by one wave in program order.
   const bool in_place = o != nullptr && o == q;
-  if (in_place && !(mfma_path(in_dtype, d, dv, block) && out_dtype == in_dtype && (Hq / Hkv) % 4 == 0))
+  if (in_place && !(fwd_mfma_path(in_dtype, d, dv, block, Hq, Hkv) && out_dtype == in_dtype && (Hq / Hkv) % 4 == 0))
     return LA_ERR_ALIAS;
   if ((!in_place && overlap(o, no, q, nq)) || overlap(o, no, k, nk) || overlap(o, no, v, nv) ||
       overlap(o, no, s_in, ns))
@@ -357,7 +368,8 @@ la_status la_forward(const void* q, const void* k, const void* v, void* o, int64
   la_status st = check_forward_shape(B, Hq, Hkv, N, d, dv, block, in_dtype, out_dtype);
   if (st != LA_OK) return st;
   size_t ws = 0;
-  if (mfma_path(in_dtype, d, dv, block) && N > 0) ws = la::plan_bf16(B, Hq, Hkv, N, d, dv, device_cus()).workspace_bytes;
+  if (fwd_mfma_path(in_dtype, d, dv, block, Hq, Hkv) && N > 0)
+    ws = la::plan_bf16(B, Hq, Hkv, N, d, dv, device_cus()).workspace_bytes;
   if (ws == 0)
     return la_forward_ex(q, k, v, o, B, Hq, Hkv, N, d, dv, block, in_dtype, out_dtype, nullptr, nullptr,
                          nullptr, 0, stream);

@@ -316,18 +316,24 @@ __global__ __launch_bounds__(kMainThreads, 1) void fwd_bf16_main(
       for (int i = 0; i < 4; ++i) z_out[int64_t(bg) * D + 16 * w + 4 * grp + i] = zacc[i];
 }
 
-struct KV4Regs {
-  uint4 k[4], v[4];
+// K and V tiles of a head size HD (d = dv = HD): 256 threads move the 64
+// rows of HD bf16 values in 16-byte chunks, HD / 8 chunks per row; thread tid
+// takes chunk tid % (HD / 8) of rows tid / (HD / 8) + (2048 / HD) i.
+template <int HD>
+struct KVTile {
+  uint4 k[HD / 32], v[HD / 32];
 };
 
-__device__ __forceinline__ void load_kv4(KV4Regs& r, const uint16_t* kh, const uint16_t* vh, int64_t blk,
-                                         int64_t N, int tid) {
-  const int c = tid & 15;
-  for (int i = 0; i < 4; ++i) {
-    const int64_t t = blk * C + (tid >> 4) + 16 * i;
+template <int HD>
+__device__ __forceinline__ void load_kv_tile(KVTile<HD>& r, const uint16_t* kh, const uint16_t* vh, int64_t blk,
+                                             int64_t N, int tid) {
+  constexpr int CPR = HD / 8, RPP = 256 / CPR;
+  const int c = tid % CPR;
+  for (int i = 0; i < HD / 32; ++i) {
+    const int64_t t = blk * C + tid / CPR + RPP * i;
     if (t < N) {
-      r.k[i] = ld_stream16(kh + t * D + 8 * c);
-      r.v[i] = ld_stream16(vh + t * DV + 8 * c);
+      r.k[i] = ld_stream16(kh + t * HD + 8 * c);
+      r.v[i] = ld_stream16(vh + t * HD + 8 * c);
     } else {
       r.k[i] = make_uint4(0, 0, 0, 0);
       r.v[i] = make_uint4(0, 0, 0, 0);
@@ -335,12 +341,14 @@ __device__ __forceinline__ void load_kv4(KV4Regs& r, const uint16_t* kh, const u
   }
 }
 
-__device__ __forceinline__ void store_kv4(const KV4Regs& r, uint16_t* ks, uint16_t* vs, int tid) {
-  const int c = tid & 15;
-  for (int i = 0; i < 4; ++i) {
-    const int row = (tid >> 4) + 16 * i;
-    *reinterpret_cast<uint4*>(ks + row * ROWKV + 8 * c) = r.k[i];
-    *reinterpret_cast<uint4*>(vs + row * ROWKV + 8 * c) = r.v[i];
+template <int HD>
+__device__ __forceinline__ void store_kv_tile(const KVTile<HD>& r, uint16_t* ks, uint16_t* vs, int tid) {
+  constexpr int CPR = HD / 8, RPP = 256 / CPR, PITCH = HD + 16;
+  const int c = tid % CPR;
+  for (int i = 0; i < HD / 32; ++i) {
+    const int row = tid / CPR + RPP * i;
+    *reinterpret_cast<uint4*>(ks + row * PITCH + 8 * c) = r.k[i];
+    *reinterpret_cast<uint4*>(vs + row * PITCH + 8 * c) = r.v[i];
   }
 }
 
@@ -370,7 +378,7 @@ __device__ __forceinline__ void store_kv4(const KV4Regs& r, uint16_t* ks, uint16
 // the earlier part phi(q_t) . z with z (float32, d entries) kept like the
 // state: wave w accumulates entries [32w, 32w+32) on the matrix cores (K^T
 // times a ones operand) and publishes them in LDS once per block.
-template <bool OUT_F32, int FL>
+template <bool OUT_F32, int FL, int HD = 128>
 __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     void* __restrict__ o, const float* starts, const float* s_in, float* s_out, int Hq, int Hkv, int subgroups,
@@ -378,10 +386,16 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
     float* z_out, float eps) {
   constexpr bool kN = (FL & kNorm) != 0;
   constexpr bool kR = (FL & kRelu) != 0;
-  __shared__ __align__(16) uint16_t ks[C * ROWKV];
-  __shared__ __align__(16) uint16_t vs[C * ROWKV];
-  __shared__ __align__(16) uint16_t st[DV * ROWST];
-  __shared__ __align__(16) float zs[kN ? D : 4];
+  // Head size HD = d = dv (64 or 128): 32-wide chunks of d, 16-row tiles of
+  // the state, 32-column output quarters, state columns per wave and their
+  // 16-column tiles; LDS pitches as for 128 (16 and 8 elements of padding).
+  static_assert(HD == 64 || HD == 128, "head sizes 64 and 128");
+  constexpr int NDS = HD / 32, NDT = HD / 16, NM = HD / 32, WC = HD / 4, NJ = WC / 16;
+  constexpr int RKV = HD + 16, RST = HD + 8;
+  __shared__ __align__(16) uint16_t ks[C * RKV];
+  __shared__ __align__(16) uint16_t vs[C * RKV];
+  __shared__ __align__(16) uint16_t st[HD * RST];
+  __shared__ __align__(16) float zs[kN ? HD : 4];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
@@ -395,53 +409,54 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
   const int64_t blk1 = blk0 + blocks_per_seg < nblocks ? blk0 + blocks_per_seg : nblocks;
 
   const int64_t head = int64_t(b) * Hq + int64_t(g) * G + int64_t(sub) * 4 + w;
-  const uint16_t* qh = q + head * N * D;
-  const uint16_t* kh = k + int64_t(bg) * N * D;
-  const uint16_t* vh = v + int64_t(bg) * N * DV;
+  const uint16_t* qh = q + head * N * HD;
+  const uint16_t* kh = k + int64_t(bg) * N * HD;
+  const uint16_t* vh = v + int64_t(bg) * N * HD;
   const int nlane = 8 * (l16 >> 2) + (l16 & 3);
 
-  const float* s0 = starts ? starts + (int64_t(bg) * P + seg) * (D * DV)
-                           : (s_in ? s_in + int64_t(bg) * (D * DV) : nullptr);
-  floatx4 sacc[2][8];
-  for (int jn = 0; jn < 2; ++jn)
-    for (int dt = 0; dt < 8; ++dt)
+  const float* s0 = starts ? starts + (int64_t(bg) * P + seg) * (HD * HD)
+                           : (s_in ? s_in + int64_t(bg) * (HD * HD) : nullptr);
+  floatx4 sacc[NJ][NDT];
+  for (int jn = 0; jn < NJ; ++jn)
+    for (int dt = 0; dt < NDT; ++dt)
       for (int i = 0; i < 4; ++i)
-        sacc[jn][dt][i] = s0 ? s0[(16 * dt + 4 * grp + i) * DV + 32 * w + 16 * jn + l16] : 0.0f;
-  for (int jn = 0; jn < 2; ++jn)
-    for (int dt = 0; dt < 8; ++dt)
-      *reinterpret_cast<bf16x4*>(&st[(32 * w + 16 * jn + l16) * ROWST + 16 * dt + 4 * grp]) =
+        sacc[jn][dt][i] = s0 ? s0[(16 * dt + 4 * grp + i) * HD + WC * w + 16 * jn + l16] : 0.0f;
+  for (int jn = 0; jn < NJ; ++jn)
+    for (int dt = 0; dt < NDT; ++dt)
+      *reinterpret_cast<bf16x4*>(&st[(WC * w + 16 * jn + l16) * RST + 16 * dt + 4 * grp]) =
           to_bf16x4(sacc[jn][dt]);
 
-  // normaliser sums, entries 32w + 16jj + 4grp + i (every column equal)
-  floatx4 zacc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+  // normaliser sums, entries WC w + 16jj + 4grp + i (every column equal)
+  floatx4 zacc[NJ];
+  for (int jj = 0; jj < NJ; ++jj) zacc[jj] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   if constexpr (kN) {
-    const float* z0 = zstarts ? zstarts + (int64_t(bg) * P + seg) * D : (z_in ? z_in + int64_t(bg) * D : nullptr);
+    const float* z0 = zstarts ? zstarts + (int64_t(bg) * P + seg) * HD : (z_in ? z_in + int64_t(bg) * HD : nullptr);
     if (z0 != nullptr)
-      for (int jj = 0; jj < 2; ++jj)
-        for (int i = 0; i < 4; ++i) zacc[jj][i] = z0[32 * w + 16 * jj + 4 * grp + i];
+      for (int jj = 0; jj < NJ; ++jj)
+        for (int i = 0; i < 4; ++i) zacc[jj][i] = z0[WC * w + 16 * jj + 4 * grp + i];
     if (l16 == 0)
-      for (int jj = 0; jj < 2; ++jj)
-        *reinterpret_cast<floatx4*>(&zs[32 * w + 16 * jj + 4 * grp]) = zacc[jj];
+      for (int jj = 0; jj < NJ; ++jj)
+        *reinterpret_cast<floatx4*>(&zs[WC * w + 16 * jj + 4 * grp]) = zacc[jj];
   }
 
-  bf16x8 qa[4][4];
-  KV4Regs kv;
+  bf16x8 qa[4][NDS];
+  KVTile<HD> kv;
   auto load_block = [&](int64_t blk) {
-    load_kv4(kv, kh, vh, blk, N, tid);
+    load_kv_tile<HD>(kv, kh, vh, blk, N, tid);
     for (int ti = 0; ti < 4; ++ti) {
       const int64_t t = blk * C + 16 * ti + l16;
-      for (int ds = 0; ds < 4; ++ds)
-        qa[ti][ds] = (t < N) ? ld_global16(qh + t * D + 32 * ds + 8 * grp) : zero_bf16x8();
+      for (int ds = 0; ds < NDS; ++ds)
+        qa[ti][ds] = (t < N) ? ld_global16(qh + t * HD + 32 * ds + 8 * grp) : zero_bf16x8();
     }
   };
   if (blk0 < blk1) load_block(blk0);
   for (int64_t blk = blk0; blk < blk1; ++blk) {
     if constexpr (kR) {
-      for (int i = 0; i < 4; ++i) kv.k[i] = relu_bf16x8(kv.k[i]);
+      for (int i = 0; i < HD / 32; ++i) kv.k[i] = relu_bf16x8(kv.k[i]);
       for (int ti = 0; ti < 4; ++ti)
-        for (int ds = 0; ds < 4; ++ds) qa[ti][ds] = relu_bf16x8(qa[ti][ds]);
+        for (int ds = 0; ds < NDS; ++ds) qa[ti][ds] = relu_bf16x8(qa[ti][ds]);
     }
-    store_kv4(kv, ks, vs, tid);
+    store_kv_tile<HD>(kv, ks, vs, tid);
     __syncthreads();  // K, V and the state of the previous block are in LDS
 
     // scores, one P^T tile at a time, packed to bf16 operands right away
@@ -454,8 +469,8 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
       floatx4 pt[4];
       for (int si = 0; si <= ti; ++si) {
         pt[si] = z4;
-        for (int ds = 0; ds < 4; ++ds)
-          pt[si] = mfma(ld_lds16(ks + (16 * si + l16) * ROWKV + 32 * ds + 8 * grp), qa[ti][ds], pt[si]);
+        for (int ds = 0; ds < NDS; ++ds)
+          pt[si] = mfma(ld_lds16(ks + (16 * si + l16) * RKV + 32 * ds + 8 * grp), qa[ti][ds], pt[si]);
       }
       pt[ti] = causal_mask(pt[ti], l16, grp);
       if constexpr (kN) {
@@ -469,7 +484,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
     }
     if constexpr (kN) {
       // earlier tokens: phi(q_t) . z; lane (l16, grp) holds q_t entries 32ds + 8grp + j
-      for (int ds = 0; ds < 4; ++ds) {
+      for (int ds = 0; ds < NDS; ++ds) {
         const floatx4 za = *reinterpret_cast<const floatx4*>(&zs[32 * ds + 8 * grp]);
         const floatx4 zb = *reinterpret_cast<const floatx4*>(&zs[32 * ds + 8 * grp + 4]);
         for (int ti = 0; ti < 4; ++ti) {
@@ -489,20 +504,20 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
 
     // Output columns in quarters of 32 (one interleaved column pair m), so
     // only 32 accumulator registers are live at a time.
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < NM; ++m) {
       floatx4 acc[2][4];
       for (int h2 = 0; h2 < 2; ++h2)
         for (int ti = 0; ti < 4; ++ti) acc[h2][ti] = z4;
       // inter: O^T[n][t] = sum_d S[d][n] Q[t][d] (state before the block)
-      for (int ds = 0; ds < 4; ++ds)
+      for (int ds = 0; ds < NDS; ++ds)
         for (int h2 = 0; h2 < 2; ++h2) {
-          const bf16x8 sa = ld_lds16(st + (32 * m + 4 * h2 + nlane) * ROWST + 32 * ds + 8 * grp);
+          const bf16x8 sa = ld_lds16(st + (32 * m + 4 * h2 + nlane) * RST + 32 * ds + 8 * grp);
           for (int ti = 0; ti < 4; ++ti) acc[h2][ti] = mfma(sa, qa[ti][ds], acc[h2][ti]);
         }
       // intra: O^T[n][t] += sum_s V[s][n] P^T[s][t]
       for (int h2 = 0; h2 < 2; ++h2) {
-        const bf16x8 va0 = tr_operand(vs, 0, 32 * m + 4 * h2, l16, grp, 8);
-        const bf16x8 va1 = tr_operand(vs, 1, 32 * m + 4 * h2, l16, grp, 8);
+        const bf16x8 va0 = tr_operand(vs, 0, 32 * m + 4 * h2, l16, grp, 8, RKV);
+        const bf16x8 va1 = tr_operand(vs, 1, 32 * m + 4 * h2, l16, grp, 8, RKV);
         for (int ti = 0; ti < 4; ++ti) acc[h2][ti] = mfma(va0, pop[ti][0], acc[h2][ti]);
         acc[h2][2] = mfma(va1, pop[2][1], acc[h2][2]);
         acc[h2][3] = mfma(va1, pop[3][1], acc[h2][3]);
@@ -514,7 +529,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
       for (int ti = 0; ti < 4; ++ti) {
         const int64_t t = blk * C + 16 * ti + l16;
         if (t < N) {
-          const int64_t off = (head * N + t) * DV + 32 * m + 8 * grp;
+          const int64_t off = (head * N + t) * HD + 32 * m + 8 * grp;
           if (OUT_F32) {
             float* op = static_cast<float*>(o) + off;
             *reinterpret_cast<floatx4*>(op) = acc[0][ti];
@@ -530,43 +545,42 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
     if (blk + 1 < blk1) load_block(blk + 1);
     __syncthreads();  // every wave has finished reading the state
 
-    // state update: S[:, 32w:32w+32] += K_b^T V_b, then its bf16 copy
+    // state update: S[:, WC w:WC w+WC] += K_b^T V_b, then its bf16 copy
     {
-      bf16x8 vb[2][2];
-      for (int jn = 0; jn < 2; ++jn)
-        for (int p = 0; p < 2; ++p) vb[jn][p] = tr_operand(vs, p, 32 * w + 16 * jn, l16, grp);
-      for (int dt = 0; dt < 8; ++dt)
+      bf16x8 vb[NJ][2];
+      for (int jn = 0; jn < NJ; ++jn)
+        for (int p = 0; p < 2; ++p) vb[jn][p] = tr_operand(vs, p, WC * w + 16 * jn, l16, grp, 4, RKV);
+      for (int dt = 0; dt < NDT; ++dt)
         for (int p = 0; p < 2; ++p) {
-          const bf16x8 kt = tr_operand(ks, p, 16 * dt, l16, grp);
-          sacc[0][dt] = mfma(kt, vb[0][p], sacc[0][dt]);
-          sacc[1][dt] = mfma(kt, vb[1][p], sacc[1][dt]);
+          const bf16x8 kt = tr_operand(ks, p, 16 * dt, l16, grp, 4, RKV);
+          for (int jn = 0; jn < NJ; ++jn) sacc[jn][dt] = mfma(kt, vb[jn][p], sacc[jn][dt]);
         }
-      for (int jn = 0; jn < 2; ++jn)
-        for (int dt = 0; dt < 8; ++dt)
-          *reinterpret_cast<bf16x4*>(&st[(32 * w + 16 * jn + l16) * ROWST + 16 * dt + 4 * grp]) =
+      for (int jn = 0; jn < NJ; ++jn)
+        for (int dt = 0; dt < NDT; ++dt)
+          *reinterpret_cast<bf16x4*>(&st[(WC * w + 16 * jn + l16) * RST + 16 * dt + 4 * grp]) =
               to_bf16x4(sacc[jn][dt]);
       if constexpr (kN) {
         for (int p = 0; p < 2; ++p)
-          for (int jj = 0; jj < 2; ++jj)
-            zacc[jj] = mfma(tr_operand(ks, p, 32 * w + 16 * jj, l16, grp), ones_bf16x8(), zacc[jj]);
+          for (int jj = 0; jj < NJ; ++jj)
+            zacc[jj] = mfma(tr_operand(ks, p, WC * w + 16 * jj, l16, grp, 4, RKV), ones_bf16x8(), zacc[jj]);
         if (l16 == 0)
-          for (int jj = 0; jj < 2; ++jj)
-            *reinterpret_cast<floatx4*>(&zs[32 * w + 16 * jj + 4 * grp]) = zacc[jj];
+          for (int jj = 0; jj < NJ; ++jj)
+            *reinterpret_cast<floatx4*>(&zs[WC * w + 16 * jj + 4 * grp]) = zacc[jj];
       }
     }
     __syncthreads();  // K and V are free for the next block
   }
 
   if (s_out != nullptr && seg == P - 1 && sub == 0) {
-    float* so = s_out + int64_t(bg) * (D * DV);
-    for (int jn = 0; jn < 2; ++jn)
-      for (int dt = 0; dt < 8; ++dt)
-        for (int i = 0; i < 4; ++i) so[(16 * dt + 4 * grp + i) * DV + 32 * w + 16 * jn + l16] = sacc[jn][dt][i];
+    float* so = s_out + int64_t(bg) * (HD * HD);
+    for (int jn = 0; jn < NJ; ++jn)
+      for (int dt = 0; dt < NDT; ++dt)
+        for (int i = 0; i < 4; ++i) so[(16 * dt + 4 * grp + i) * HD + WC * w + 16 * jn + l16] = sacc[jn][dt][i];
   }
   if constexpr (kN)
     if (z_out != nullptr && seg == P - 1 && sub == 0 && l16 == 0)
-      for (int jj = 0; jj < 2; ++jj)
-        for (int i = 0; i < 4; ++i) z_out[int64_t(bg) * D + 32 * w + 16 * jj + 4 * grp + i] = zacc[jj][i];
+      for (int jj = 0; jj < NJ; ++jj)
+        for (int i = 0; i < 4; ++i) z_out[int64_t(bg) * HD + WC * w + 16 * jj + 4 * grp + i] = zacc[jj][i];
 }
 
 // Pre-pass: partial[c][j][r] = sum of K_b^T V_b over part r of segment
@@ -581,7 +595,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
 // LDS; kNorm also writes zpart[c][j][r] = sum of phi(k_b) over the part
 // (wave w: entries [32w, 32w+32), as K^T times a ones operand on the matrix
 // cores).
-template <int FL>
+template <int FL, int HD = 128>
 __global__ __launch_bounds__(kPartThreads, 3) void state_parts(const uint16_t* __restrict__ k,
                                                            const uint16_t* __restrict__ v,
                                                            float* __restrict__ partial,
@@ -589,8 +603,10 @@ __global__ __launch_bounds__(kPartThreads, 3) void state_parts(const uint16_t* _
                                                            int64_t nblocks, int64_t blocks_per_seg,
                                                            int64_t blocks_per_part, int P, int R,
                                                            int seg_offset) {
-  __shared__ __align__(16) uint16_t ksm[C * ROWKV];
-  __shared__ __align__(16) uint16_t vsm[C * ROWKV];
+  // head size HD = d = dv (64 or 128), as in fwd_bf16_g4
+  constexpr int NDT = HD / 16, WC = HD / 4, NJ = WC / 16, RKV = HD + 16, CPR = HD / 8, RPP = 256 / CPR;
+  __shared__ __align__(16) uint16_t ksm[C * RKV];
+  __shared__ __align__(16) uint16_t vsm[C * RKV];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
@@ -605,67 +621,67 @@ __global__ __launch_bounds__(kPartThreads, 3) void state_parts(const uint16_t* _
   if (b1 > seg_end) b1 = seg_end;
   if (b1 > nblocks) b1 = nblocks;
 
-  const uint16_t* kh = k + int64_t(c) * N * D;
-  const uint16_t* vh = v + int64_t(c) * N * DV;
+  const uint16_t* kh = k + int64_t(c) * N * HD;
+  const uint16_t* vh = v + int64_t(c) * N * HD;
 
-  floatx4 acc[2][8];
-  for (int jn = 0; jn < 2; ++jn)
-    for (int dt = 0; dt < 8; ++dt) acc[jn][dt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-  floatx4 zacc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+  floatx4 acc[NJ][NDT];
+  for (int jn = 0; jn < NJ; ++jn)
+    for (int dt = 0; dt < NDT; ++dt) acc[jn][dt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  floatx4 zacc[NJ];
+  for (int jj = 0; jj < NJ; ++jj) zacc[jj] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int ch = tid & 15;
-  auto load = [&](int64_t blk, uint4 (&kr)[4], uint4 (&vr)[4]) {
-    for (int i = 0; i < 4; ++i) {
-      const int64_t t = blk * C + (tid >> 4) + 16 * i;
+  const int ch = tid % CPR;
+  auto load = [&](int64_t blk, uint4 (&kr)[HD / 32], uint4 (&vr)[HD / 32]) {
+    for (int i = 0; i < HD / 32; ++i) {
+      const int64_t t = blk * C + tid / CPR + RPP * i;
       if (t < N) {
-        kr[i] = ld_stream16(kh + t * D + 8 * ch);
-        vr[i] = ld_stream16(vh + t * DV + 8 * ch);
+        kr[i] = ld_stream16(kh + t * HD + 8 * ch);
+        vr[i] = ld_stream16(vh + t * HD + 8 * ch);
       } else {
         kr[i] = make_uint4(0, 0, 0, 0);
         vr[i] = make_uint4(0, 0, 0, 0);
       }
     }
   };
-  auto store = [&](const uint4 (&kr)[4], const uint4 (&vr)[4]) {
-    for (int i = 0; i < 4; ++i) {
-      const int row = (tid >> 4) + 16 * i;
-      *reinterpret_cast<uint4*>(&ksm[row * ROWKV + 8 * ch]) = (FL & kRelu) ? relu_bf16x8(kr[i]) : kr[i];
-      *reinterpret_cast<uint4*>(&vsm[row * ROWKV + 8 * ch]) = vr[i];
+  auto store = [&](const uint4 (&kr)[HD / 32], const uint4 (&vr)[HD / 32]) {
+    for (int i = 0; i < HD / 32; ++i) {
+      const int row = tid / CPR + RPP * i;
+      *reinterpret_cast<uint4*>(&ksm[row * RKV + 8 * ch]) = (FL & kRelu) ? relu_bf16x8(kr[i]) : kr[i];
+      *reinterpret_cast<uint4*>(&vsm[row * RKV + 8 * ch]) = vr[i];
     }
   };
 
-  uint4 kr[4], vr[4];
+  uint4 kr[HD / 32], vr[HD / 32];
   if (b0 < b1) load(b0, kr, vr);
   for (int64_t blk = b0; blk < b1; ++blk) {
     store(kr, vr);
     __syncthreads();  // the block's K and V are in LDS
     if (blk + 1 < b1) load(blk + 1, kr, vr);
     for (int p = 0; p < 2; ++p) {
-      const bf16x8 vb0 = tr_operand(vsm, p, 32 * w, l16, grp);
-      const bf16x8 vb1 = tr_operand(vsm, p, 32 * w + 16, l16, grp);
-      for (int dt = 0; dt < 8; ++dt) {
-        const bf16x8 ka = tr_operand(ksm, p, 16 * dt, l16, grp);
-        acc[0][dt] = mfma(ka, vb0, acc[0][dt]);
-        acc[1][dt] = mfma(ka, vb1, acc[1][dt]);
+      bf16x8 vb[NJ];
+      for (int jn = 0; jn < NJ; ++jn) vb[jn] = tr_operand(vsm, p, WC * w + 16 * jn, l16, grp, 4, RKV);
+      for (int dt = 0; dt < NDT; ++dt) {
+        const bf16x8 ka = tr_operand(ksm, p, 16 * dt, l16, grp, 4, RKV);
+        for (int jn = 0; jn < NJ; ++jn) acc[jn][dt] = mfma(ka, vb[jn], acc[jn][dt]);
       }
       if constexpr ((FL & kNorm) != 0)
-        for (int jj = 0; jj < 2; ++jj)
-          zacc[jj] = mfma(tr_operand(ksm, p, 32 * w + 16 * jj, l16, grp), ones_bf16x8(), zacc[jj]);
+        for (int jj = 0; jj < NJ; ++jj)
+          zacc[jj] = mfma(tr_operand(ksm, p, WC * w + 16 * jj, l16, grp, 4, RKV), ones_bf16x8(), zacc[jj]);
     }
     __syncthreads();  // every wave is done with this block's K and V
   }
   if constexpr ((FL & kNorm) != 0) {
     // every column of the ones product holds the sum; lanes of column 0 write it
-    float* zo = zpart + ((int64_t(c) * (P - 1) + j) * R + r) * D;
+    float* zo = zpart + ((int64_t(c) * (P - 1) + j) * R + r) * HD;
     if (l16 == 0)
-      for (int jj = 0; jj < 2; ++jj)
-        for (int i = 0; i < 4; ++i) zo[32 * w + 16 * jj + 4 * grp + i] = zacc[jj][i];
+      for (int jj = 0; jj < NJ; ++jj)
+        for (int i = 0; i < 4; ++i) zo[WC * w + 16 * jj + 4 * grp + i] = zacc[jj][i];
   }
 
-  float* out = partial + ((int64_t(c) * (P - 1) + j) * R + r) * (D * DV);
-  for (int jn = 0; jn < 2; ++jn)
-    for (int dt = 0; dt < 8; ++dt)
-      for (int i = 0; i < 4; ++i) out[(16 * dt + 4 * grp + i) * DV + 32 * w + 16 * jn + l16] = acc[jn][dt][i];
+  float* out = partial + ((int64_t(c) * (P - 1) + j) * R + r) * (HD * HD);
+  for (int jn = 0; jn < NJ; ++jn)
+    for (int dt = 0; dt < NDT; ++dt)
+      for (int i = 0; i < 4; ++i) out[(16 * dt + 4 * grp + i) * HD + WC * w + 16 * jn + l16] = acc[jn][dt][i];
 }
 
 // starts[c][j] = s_in[c] + sum over segments i < j and parts r of partial[c][i][r],
@@ -815,12 +831,12 @@ __global__ __launch_bounds__(512, 1) void fwd_noncausal(
   }
 }
 
-template <bool OUT_F32, int FL = 0>
+template <bool OUT_F32, int FL = 0, int HD = 128>
 void launch_g4(dim3 grid, hipStream_t stream, const void* q, const void* k, const void* v, void* o,
                const float* starts, const float* s_in, float* s_out, int Hq, int Hkv, int subgroups, int64_t N,
                int64_t nblocks, int64_t bps, int P, const float* zstarts = nullptr, const float* z_in = nullptr,
                float* z_out = nullptr, float eps = 0.0f) {
-  hipLaunchKernelGGL((fwd_bf16_g4<OUT_F32, FL>), grid, dim3(256), 0, stream, static_cast<const uint16_t*>(q),
+  hipLaunchKernelGGL((fwd_bf16_g4<OUT_F32, FL, HD>), grid, dim3(256), 0, stream, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), o, starts, s_in, s_out, Hq,
                      Hkv, subgroups, N, nblocks, bps, P, zstarts, z_in, z_out, eps);
 }
@@ -843,16 +859,24 @@ hipError_t launch_segment_states(const void* k, const void* v, const float* s_in
   const int64_t kv_chains = B * Hkv;
   float* partial = static_cast<float*>(workspace);
   float* starts = partial + plan.partial_floats;
+  if (plan.hd != 128 && plan.hd != 64) return hipErrorInvalidValue;
   if (plan.P > 1) {
-    hipLaunchKernelGGL(state_parts<0>, dim3(unsigned(kv_chains * (plan.P - 1) * plan.R)), dim3(kPartThreads), 0,
-                       stream, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), partial, nullptr,
-                       N, plan.nblocks, plan.blocks_per_seg, plan.blocks_per_part, plan.P, plan.R, 0);
+    const dim3 grid(unsigned(kv_chains * (plan.P - 1) * plan.R));
+    const auto* k16 = static_cast<const uint16_t*>(k);
+    const auto* v16 = static_cast<const uint16_t*>(v);
+    if (plan.hd == 64)
+      hipLaunchKernelGGL((state_parts<0, 64>), grid, dim3(kPartThreads), 0, stream, k16, v16, partial, nullptr, N,
+                         plan.nblocks, plan.blocks_per_seg, plan.blocks_per_part, plan.P, plan.R, 0);
+    else
+      hipLaunchKernelGGL((state_parts<0, 128>), grid, dim3(kPartThreads), 0, stream, k16, v16, partial, nullptr, N,
+                         plan.nblocks, plan.blocks_per_seg, plan.blocks_per_part, plan.P, plan.R, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t total = kv_chains * D * DV;
+  const int E = plan.hd * plan.hd;
+  const int64_t total = kv_chains * E;
   hipLaunchKernelGGL(scan_starts, dim3(unsigned((total + 255) / 256)), dim3(256), 0, stream, partial, starts, s_in,
-                     plan.P, plan.R, D * DV, total);
+                     plan.P, plan.R, E, total);
   return hipGetLastError();
 }
 
@@ -972,7 +996,19 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
 #define LA_MAIN(GW, F32)                                                                                      \
   launch_main<GW, F32>(grid, stream, q, k, v, o, starts, plan.use_starts ? nullptr : s_in, s_out, iHq, iHkv, \
                        plan.subgroups, N, plan.nblocks, plan.blocks_per_seg, plan.P)
-  if (plan.gw == 4) {
+  if (plan.hd == 64) {
+    // head size 64: the four-wave kernel only (groups of four query heads)
+    if (plan.gw != 4) return hipErrorInvalidValue;
+    const float* si = plan.use_starts ? nullptr : s_in;
+    if (out_f32)
+      launch_g4<true, 0, 64>(grid, stream, q, k, v, o, starts, si, s_out, iHq, iHkv, plan.subgroups, N,
+                             plan.nblocks, plan.blocks_per_seg, plan.P);
+    else
+      launch_g4<false, 0, 64>(grid, stream, q, k, v, o, starts, si, s_out, iHq, iHkv, plan.subgroups, N,
+                              plan.nblocks, plan.blocks_per_seg, plan.P);
+  } else if (plan.hd != 128) {
+    return hipErrorInvalidValue;
+  } else if (plan.gw == 4) {
     const float* si = plan.use_starts ? nullptr : s_in;
     if (out_f32)
       launch_g4<true>(grid, stream, q, k, v, o, starts, si, s_out, iHq, iHkv, plan.subgroups, N, plan.nblocks,

@@ -20,6 +20,7 @@ namespace la {
 // the parts up in a fixed order.
 struct Bf16Plan {
   int64_t nblocks = 0;          // ceil(N / 64)
+  int hd = 128;                 // head size d = dv (128; 64 for groups of four query heads)
   int gw = 4;                   // query heads per workgroup (1, 2 or 4)
   int subgroups = 1;            // (Hq / Hkv) / gw workgroups per KV head and segment
   int P = 1;                    // segments per chain

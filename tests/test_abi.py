@@ -75,7 +75,7 @@ def test_forward_validation(lib):
     assert fwd(lib, o=Q, i=F32, out=F32) == ALIAS
     assert fwd(lib, o=Q, out=F32) == ALIAS
     assert fwd(lib, o=Q, Hq=2, Hkv=1) == ALIAS
-    assert fwd(lib, o=Q, d=64, dv=64) == ALIAS
+    assert fwd(lib, o=Q, d=64, dv=64, Hq=2, Hkv=1) == ALIAS   # head size 64: groups of four only
     assert fwd(lib, s_out=ctypes.c_void_p(GB * 3 + 64)) == ALIAS  # s_out inside v
     assert fwd(lib, ws=None) == WORKSPACE
     assert fwd(lib, ws_bytes=1024) == WORKSPACE
@@ -160,6 +160,9 @@ def test_workspace_plan(lib):
         assert lib.la_backward_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, blk, BF16) == \
             lib.la_backward_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, 64, BF16)
     assert lib.la_forward_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, 96, BF16) == 0   # unsupported -> 0
+    # head size 64 on the matrix cores for groups of four query heads (same split), else the scalar kernels
+    assert lib.la_forward_workspace_bytes(1, 128, 32, 1 << 20, 64, 64, 64, BF16) == (32 * 7 * 3 + 32 * 8) * 64 * 64 * 4
+    assert lib.la_forward_workspace_bytes(1, 64, 32, 1 << 20, 64, 64, 64, BF16) == 0
     assert lib.la_forward_workspace_bytes(256, 128, 32, 8192, 128, 128, 64, BF16) == 0
     assert lib.la_forward_workspace_bytes(1, 128, 32, 0, 128, 128, 64, BF16) == 0
     assert lib.la_forward_workspace_bytes(1, 6, 4, 64, 128, 128, 64, BF16) == 0   # invalid -> 0
@@ -174,7 +177,7 @@ def test_workspace_plan(lib):
     assert lib.la_backward_workspace_bytes(1, 4, 2, 64, 128, 96, 64, F32) == 2 * 128 * 96 * 4   # s_in^T
     assert lib.la_backward_workspace_bytes(1, 4, 2, 64, 48, 96, 64, F32) == 0                  # d not a multiple of 32
     # bf16 at other head sizes runs on the scalar kernels: no forward workspace, s_in^T for the backward
-    assert lib.la_forward_workspace_bytes(1, 4, 1, 1000, 64, 64, 64, BF16) == 0
+    assert lib.la_forward_workspace_bytes(1, 4, 1, 1000, 96, 96, 64, BF16) == 0
     assert lib.la_backward_workspace_bytes(1, 4, 2, 64, 64, 96, 64, BF16) == 2 * 64 * 96 * 4
     # Variants at 1M tokens: causal = the forward's split (+ normaliser sums);
     # non-causal sums all 8 segments of each chain (3 parts each) and scans

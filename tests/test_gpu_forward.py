@@ -161,6 +161,42 @@ def test_bf16_in_place_rejected_off_the_four_head_kernel():
         la.forward(q, k, v, out=q)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,N,out_dtype,s_in", [
+    (1, 8, 2, 3001, torch.bfloat16, True),    # G = 4, several segments, ragged tail
+    (2, 16, 2, 777, torch.float32, False),    # G = 8: two query-head subgroups
+    (1, 4, 1, 64, torch.bfloat16, False),     # one block
+    (1, 4, 1, 20000, torch.float32, True),    # many segments on one chain
+])
+def test_bf16_head_size_64(B, Hq, Hkv, N, out_dtype, s_in):
+    """Head size 64 on the four-wave matrix-core kernel (groups of four query
+    heads) and its pre-pass."""
+    need_gpu()
+    if N > 64:
+        assert la.workspace_bytes(B, Hq, Hkv, N, 64, 64, 64, torch.bfloat16) > 0   # the matrix-core split
+    run_case(B, Hq, Hkv, N, 64, 64, torch.bfloat16, out_dtype, seed=N + Hq, s_in=s_in)
+
+
+def test_bf16_head_size_64_in_place_and_resume():
+    """Head size 64: a 3000-token sequence resumed after 1000 tokens, the
+    second chunk written in place over its queries with the state carried in
+    place, matches the oracle; the in-place call equals the out-of-place one
+    bit for bit."""
+    need_gpu()
+    q, k, v = qkv(1, 8, 2, 3000, 64, 64, torch.bfloat16, seed=77)
+    sl = lambda t, a, b: t[:, :, a:b].contiguous()
+    o1, S1 = la.forward(sl(q, 0, 1000), sl(k, 0, 1000), sl(v, 0, 1000), return_state=True)
+    q2, k2, v2 = sl(q, 1000, 3000), sl(k, 1000, 3000), sl(v, 1000, 3000)
+    o2_ref = la.forward(q2, k2, v2, s_in=S1.clone())
+    qi = q2.clone()
+    o2 = la.forward(qi, k2, v2, s_in=S1, s_out=S1, out=qi)
+    torch.cuda.synchronize()
+    assert o2.data_ptr() == qi.data_ptr() and torch.equal(o2, o2_ref)
+    ref_o, ref_S = oracle.chunkwise(f64(q), f64(k), f64(v), 64)
+    check_close("resumed o (second chunk in place)", f64(torch.cat([o1, o2], dim=2)), ref_o, torch.bfloat16,
+                torch.bfloat16)
+    check_close("resumed state (in place)", f64(S1), ref_S, torch.bfloat16, torch.float32)
+
+
 def test_empty_sequence_state_passthrough():
     need_gpu()
     for dtype in (torch.bfloat16, torch.float32):
