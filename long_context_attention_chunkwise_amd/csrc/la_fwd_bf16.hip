@@ -891,7 +891,7 @@ hipError_t launch_state_parts(const void* a, const void* b, float* partial, int6
 
 namespace {
 
-template <int FL>
+template <int FL, int HD>
 hipError_t variant_states(const void* k, const void* v, const float* s_in, const float* z_in, int64_t kv_chains,
                           int64_t N, const VarPlan& vp, float* ws, hipStream_t stream) {
   // Segment starts (causal) or the totals (non-causal: the scan over Ppre + 1
@@ -903,19 +903,19 @@ hipError_t variant_states(const void* k, const void* v, const float* s_in, const
   float* zpart = starts + vp.start_floats;
   float* zstarts = zpart + vp.zpart_floats;
   if (Ppre > 1) {
-    hipLaunchKernelGGL(state_parts<FL>, dim3(unsigned(kv_chains * (Ppre - 1) * p.R)), dim3(kPartThreads), 0,
+    hipLaunchKernelGGL((state_parts<FL, HD>), dim3(unsigned(kv_chains * (Ppre - 1) * p.R)), dim3(kPartThreads), 0,
                        stream, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), partial, zpart, N,
                        p.nblocks, p.blocks_per_seg, p.blocks_per_part, Ppre, p.R, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t total = kv_chains * D * DV;
+  const int64_t total = kv_chains * HD * HD;
   hipLaunchKernelGGL(scan_starts, dim3(unsigned((total + 255) / 256)), dim3(256), 0, stream, partial, starts, s_in,
-                     Ppre, p.R, D * DV, total);
+                     Ppre, p.R, HD * HD, total);
   if ((FL & kNorm) != 0) {
-    const int64_t zt = kv_chains * D;
+    const int64_t zt = kv_chains * HD;
     hipLaunchKernelGGL(scan_starts, dim3(unsigned((zt + 255) / 256)), dim3(256), 0, stream, zpart, zstarts, z_in,
-                       Ppre, p.R, D, zt);
+                       Ppre, p.R, HD, zt);
   }
   return hipGetLastError();
 }
@@ -936,11 +936,15 @@ hipError_t variant_outputs(const void* q, const void* k, const void* v, void* o,
 #define LA_VAR(LAUNCH)                                                                                              \
   LAUNCH(grid, stream, q, k, v, o, st ? starts : nullptr, st ? nullptr : s_in, s_out, iHq, iHkv, p.subgroups, N, \
          p.nblocks, p.blocks_per_seg, p.P, zs, zi, z_out, eps)
-    if (p.gw == 4) LA_VAR((launch_g4<OUT_F32, FL>));
+    if (p.hd == 64) {
+      if (p.gw != 4) return hipErrorInvalidValue;
+      LA_VAR((launch_g4<OUT_F32, FL, 64>));
+    } else if (p.gw == 4) LA_VAR((launch_g4<OUT_F32, FL>));
     else if (p.gw == 2) LA_VAR((launch_main<2, OUT_F32, FL>));
     else LA_VAR((launch_main<1, OUT_F32, FL>));
 #undef LA_VAR
   } else {
+    if (p.hd != 128) return hipErrorInvalidValue;  // the non-causal kernel is built for head size 128
     // totals sit at entry P of each chain's P + 1 scanned entries
     const int64_t stride = p.P + 1;
     const dim3 grid(unsigned(B * Hkv * p.subgroups * vp.P_out));
@@ -960,8 +964,10 @@ template <int FL>
 hipError_t variant_run(const void* q, const void* k, const void* v, void* o, bool out_f32, const float* s_in,
                        float* s_out, const float* z_in, float* z_out, float eps, int64_t B, int64_t Hq, int64_t Hkv,
                        int64_t N, const VarPlan& vp, float* ws, hipStream_t stream) {
+  if (vp.base.hd != 128 && !(vp.base.hd == 64 && vp.causal)) return hipErrorInvalidValue;
   if (!vp.causal || vp.base.use_starts) {
-    hipError_t e = variant_states<FL>(k, v, s_in, z_in, B * Hkv, N, vp, ws, stream);
+    hipError_t e = vp.base.hd == 64 ? variant_states<FL, 64>(k, v, s_in, z_in, B * Hkv, N, vp, ws, stream)
+                                    : variant_states<FL, 128>(k, v, s_in, z_in, B * Hkv, N, vp, ws, stream);
     if (e != hipSuccess) return e;
   }
   return out_f32 ? variant_outputs<true, FL>(q, k, v, o, s_in, s_out, z_in, z_out, eps, B, Hq, Hkv, N, vp, ws, stream)
