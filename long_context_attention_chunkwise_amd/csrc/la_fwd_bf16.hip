@@ -30,8 +30,9 @@
 //  * Two layouts.  fwd_bf16_main (eight waves, groups of one or two query
 //    heads): K, V and the bf16 state are double-buffered in LDS, one barrier
 //    per block, wave w owns state columns [16w, 16w+16).  fwd_bf16_g4 (four
-//    waves, groups of four query heads, the 128/32-head shape): one wave per
-//    query head, single-buffered LDS, described above the kernel.
+//    waves, groups of four query heads, the 128/32-head shape, head size 128
+//    or 64): one wave per query head, single-buffered LDS, described above
+//    the kernel.
 //  * The sequence split into segments needs each segment's starting state:
 //    a pre-pass (state_parts) sums K_b^T V_b over parts of every segment but
 //    the last, and a scan (scan_starts) adds the parts up (s_in first, then
@@ -353,10 +354,11 @@ __device__ __forceinline__ void store_kv_tile(const KVTile<HD>& r, uint16_t* ks,
 }
 
 // ---------------------------------------------------------------------------
-// Four-wave kernel for groups of four query heads (the 128/32-head shape).
-// One wave per SIMD: wave h computes every row of the block for query head h
-// of the group (each wave reads the bf16 state once per block: half the LDS
-// traffic of the eight-wave layout) and owns state columns [32h, 32h+32).
+// Four-wave kernel for groups of four query heads (the 128/32-head shape;
+// head size d = dv = HD, 128 or 64).  One wave per SIMD: wave h computes every
+// row of the block for query head h of the group (each wave reads the bf16
+// state once per block: half the LDS traffic of the eight-wave layout) and
+// owns state columns [h HD/4, (h+1) HD/4).
 //
 // Output columns are processed in quarters of 32 as two interleaved 16-column
 // tiles (columns 32m + 8j + {0..3} and 32m + 8j + {4..7}, j = 0..3), so each
@@ -586,10 +588,11 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
 // Pre-pass: partial[c][j][r] = sum of K_b^T V_b over part r of segment
 // j + seg_offset of chain c, for j < P - 1 (the forward sums every segment but
 // the last with seg_offset 0; the backward every segment but the first with
-// seg_offset 1).  Four waves; wave w owns state
-// columns [32w, 32w+32).  A pure HBM stream: the K/V tile is single-buffered
-// in LDS (36 KiB) so three workgroups share a CU, each with the next block's
-// loads in flight while it multiplies the current one.
+// seg_offset 1).  Four waves; wave w owns state columns [w HD/4, (w+1) HD/4)
+// (head size HD = d = dv, 128 or 64).  A pure HBM stream: the K/V tile is
+// single-buffered in LDS (36 KiB at HD = 128) so three workgroups share a CU,
+// each with the next block's loads in flight while it multiplies the current
+// one.
 //
 // Flags (feature-map variants): kRelu applies phi = ReLU to k as it enters
 // LDS; kNorm also writes zpart[c][j][r] = sum of phi(k_b) over the part
