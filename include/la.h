@@ -252,7 +252,8 @@ size_t la_forward_variant_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, in
  *   q, k, v        the forward's inputs (layouts as above).
  *   grad_o         [B][Hq][N][dv], in_dtype.
  *   in_dtype       LA_BF16: grad_dtype LA_BF16 or LA_F32; matrix-core
- *                  kernels at d = dv = 128, block a multiple of 64.  LA_F32:
+ *                  kernels at d = dv = 128, and at d = dv = 64 when Hq / Hkv
+ *                  is a multiple of 4, block a multiple of 64.  LA_F32:
  *                  grad_dtype LA_F32.  Other shapes, d and dv multiples of 32
  *                  up to 128 and block as for la_forward, run on float32 FMA
  *                  kernels (a small-problem path), for bf16 inputs too.

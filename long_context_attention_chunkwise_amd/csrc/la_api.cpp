@@ -174,11 +174,14 @@ BwdPlan plan_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, 
   p.nblocks = (N + kBf16Block - 1) / kBf16Block;
   if (p.nblocks == 0) return p;
 
-  // dK/dV: one workgroup per (batch, KV head, segment), one per compute unit.
+  // dK/dV: one workgroup per (batch, KV head, segment).  At head size 128 it
+  // fills a compute unit (eight waves, 122 KiB of LDS); at 64 it takes four
+  // waves and 65 KiB, so two run on each unit.
   const int64_t chains = B * Hkv;
   constexpr int64_t kMinBlocks = 4;
+  const int64_t slots_kv = (d == 64 ? 2 : 1) * int64_t(cus);
   int64_t P = 1;
-  if (chains < cus) P = (cus + chains - 1) / chains;
+  if (chains < slots_kv) P = (slots_kv + chains - 1) / chains;
   P = std::min(P, std::max<int64_t>(1, p.nblocks / kMinBlocks));
   p.blocks_per_seg = (p.nblocks + P - 1) / P;
   P = (p.nblocks + p.blocks_per_seg - 1) / p.blocks_per_seg;
@@ -188,12 +191,13 @@ BwdPlan plan_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, 
     // Pre-pass over (Q, dO) of every query head and every segment but the
     // first.  Parts per segment: the count with the least (rounds of resident
     // workgroups, three per compute unit) x (blocks per part + the cost of
-    // its 64 KiB partial, written once and read once by the scan: about four
-    // 32 KiB blocks of streaming), i.e. the shortest pre-pass when every part
-    // streams at the same rate; ties go to fewer parts.
+    // its partial, written once and read once by the scan: 4 d dv floats
+    // against a block's 64 (d + dv) bf16 values, four blocks at d = dv = 128),
+    // i.e. the shortest pre-pass when every part streams at the same rate;
+    // ties go to fewer parts.
     constexpr int64_t kMinPartBlocks = 8;
     constexpr int64_t kPartWgsPerCu = 3;
-    constexpr int64_t kPartialCostBlocks = 4;
+    const int64_t kPartialCostBlocks = std::max<int64_t>(1, (4 * d * dv) / (kBf16Block * (d + dv)));
     const int64_t pre_chains = B * Hq * (P - 1);
     const int64_t slots = kPartWgsPerCu * int64_t(cus);
     int64_t best_R = 1, best_cost = -1;
@@ -419,13 +423,16 @@ la_status check_backward_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, in
   la_status st = check_forward_shape(B, Hq, Hkv, N, d, dv, block, in_dtype, grad_dtype);
   if (st != LA_OK) return st;
   // scalar kernels: dK is computed in 32-column slices of d (dv is already a multiple of 32)
-  if (!mfma_path(in_dtype, d, dv, block) && d % 32 != 0) return LA_ERR_UNSUPPORTED;
+  if (!fwd_mfma_path(in_dtype, d, dv, block, Hq, Hkv) && d % 32 != 0) return LA_ERR_UNSUPPORTED;
   return LA_OK;
 }
 
+// The backward runs on the matrix cores for the forward's shapes: its dQ pass
+// is the forward over (dO, V, K) and its dK/dV kernel is built for head sizes
+// 128 (eight waves) and 64 (four waves).
 size_t backward_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv, int64_t block,
                           la_dtype in_dtype) {
-  if (!mfma_path(in_dtype, d, dv, block)) return la::bwd_f32_workspace_floats(B, Hkv, d, dv) * sizeof(float);
+  if (!fwd_mfma_path(in_dtype, d, dv, block, Hq, Hkv)) return la::bwd_f32_workspace_floats(B, Hkv, d, dv) * sizeof(float);
   return la::plan_backward(B, Hq, Hkv, N, d, dv, device_cus()).workspace_bytes;
 }
 
@@ -491,7 +498,7 @@ la_status la_backward(const void* q, const void* k, const void* v, const void* g
   for (const Range& out : outputs)
     if (overlap(workspace, nw, out.p, out.n)) return LA_ERR_ALIAS;
 
-  if (!mfma_path(in_dtype, d, dv, block))
+  if (!fwd_mfma_path(in_dtype, d, dv, block, Hq, Hkv))
     return la::launch_bwd_f32(q, k, v, grad_o, grad_q, grad_k, grad_v, in_dtype == LA_BF16, grad_dtype == LA_BF16,
                               s_in, grad_s_out, grad_s_in, B, Hq, Hkv, N, d, dv, tile_block(block),
                               static_cast<float*>(workspace), hs) == hipSuccess
@@ -508,7 +515,7 @@ la_status la_backward(const void* q, const void* k, const void* v, const void* g
   // dQ: the forward over (queries dO, keys V, values K) from s_in^T.
   const float* s_t = nullptr;
   if (s_in != nullptr) {
-    if (la::launch_transpose_states(s_in, sin_t, B * Hkv, hs) != hipSuccess) return LA_ERR_HIP;
+    if (la::launch_transpose_states(s_in, sin_t, B * Hkv, d, hs) != hipSuccess) return LA_ERR_HIP;
     s_t = sin_t;
   }
   if (plan.fwd.use_starts && la::launch_segment_states(v, k, s_t, B, Hkv, N, plan.fwd, ws_fwd, hs) != hipSuccess)

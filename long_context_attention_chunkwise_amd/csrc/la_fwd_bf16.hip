@@ -885,10 +885,18 @@ hipError_t launch_segment_states(const void* k, const void* v, const float* s_in
 
 hipError_t launch_state_parts(const void* a, const void* b, float* partial, int64_t chains, int64_t N,
                               int64_t nblocks, int64_t blocks_per_seg, int64_t blocks_per_part, int P, int R,
-                              int seg_offset, hipStream_t stream) {
-  hipLaunchKernelGGL(state_parts<0>, dim3(unsigned(chains * (P - 1) * R)), dim3(kPartThreads), 0, stream,
-                     static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), partial, nullptr, N,
-                     nblocks, blocks_per_seg, blocks_per_part, P, R, seg_offset);
+                              int seg_offset, int hd, hipStream_t stream) {
+  const dim3 grid(unsigned(chains * (P - 1) * R));
+  const auto* a16 = static_cast<const uint16_t*>(a);
+  const auto* b16 = static_cast<const uint16_t*>(b);
+  if (hd == 64)
+    hipLaunchKernelGGL((state_parts<0, 64>), grid, dim3(kPartThreads), 0, stream, a16, b16, partial, nullptr, N,
+                       nblocks, blocks_per_seg, blocks_per_part, P, R, seg_offset);
+  else if (hd == 128)
+    hipLaunchKernelGGL((state_parts<0, 128>), grid, dim3(kPartThreads), 0, stream, a16, b16, partial, nullptr, N,
+                       nblocks, blocks_per_seg, blocks_per_part, P, R, seg_offset);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -64,11 +64,11 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                            const float* s_in, float* s_out, int64_t B, int64_t Hq, int64_t Hkv,
                            int64_t N, const Bf16Plan& plan, const void* workspace, hipStream_t stream);
 
-// Pre-pass over `chains` row-major [N][128] tile pairs (a, b): partial sums of
-// a_b^T b_b over part r of segment j + seg_offset, j < P - 1.
+// Pre-pass over `chains` row-major [N][hd] tile pairs (a, b), hd = 64 or 128:
+// partial sums of a_b^T b_b over part r of segment j + seg_offset, j < P - 1.
 hipError_t launch_state_parts(const void* a, const void* b, float* partial, int64_t chains, int64_t N,
                               int64_t nblocks, int64_t blocks_per_seg, int64_t blocks_per_part, int P, int R,
-                              int seg_offset, hipStream_t stream);
+                              int seg_offset, int hd, hipStream_t stream);
 
 // Forward variants (feature map, non-causal, normalised), bf16 inputs, any
 // query-head group size.  Causal: the forward's split, with the
@@ -114,7 +114,8 @@ struct BwdPlan {
 
 BwdPlan plan_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv, int cus);
 
-hipError_t launch_transpose_states(const float* in, float* out, int64_t count, hipStream_t stream);
+// out[c] = in[c]^T for `count` n x n float32 states (n = 64 or 128).
+hipError_t launch_transpose_states(const float* in, float* out, int64_t count, int64_t n, hipStream_t stream);
 
 // dK, dV and (if ds_in) the initial-state gradient; the reverse state starts
 // from ds_out (zeros if NULL).  workspace_f holds the plan's partials and

@@ -178,6 +178,12 @@ def test_workspace_plan(lib):
     n = lib.la_backward_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, 64, BF16)
     assert n == ((32 * 7 * 3 + 32 * 8) + 32 + 128 * 7 * 6 + 32 * 8) * 128 * 128 * 4
     assert lib.la_backward_workspace_bytes(1, 128, 32, 0, 128, 128, 64, BF16) == 0
+    # Head size 64 (groups of four): states of 64 x 64, and two dK/dV workgroups per compute unit, so
+    # 16 segments per chain whose 15 later segments are summed in 2 parts each (3840 pre-pass
+    # workgroups: five rounds); groups of two run on the scalar kernels (s_in^T only).
+    n64 = lib.la_backward_workspace_bytes(1, 128, 32, 1 << 20, 64, 64, 64, BF16)
+    assert n64 == ((32 * 7 * 3 + 32 * 8) + 32 + 128 * 15 * 2 + 32 * 16) * 64 * 64 * 4
+    assert lib.la_backward_workspace_bytes(1, 64, 32, 1 << 20, 64, 64, 64, BF16) == 32 * 64 * 64 * 4
     assert lib.la_backward_workspace_bytes(1, 4, 2, 64, 128, 96, 64, F32) == 2 * 128 * 96 * 4   # s_in^T
     assert lib.la_backward_workspace_bytes(1, 4, 2, 64, 48, 96, 64, F32) == 0                  # d not a multiple of 32
     # bf16 at other head sizes runs on the scalar kernels: no forward workspace, s_in^T for the backward

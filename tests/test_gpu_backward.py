@@ -6,10 +6,11 @@ Inputs are seeded and synthetic: q, k, v from synth.make_qkv (the forward
 workloads' distributions), the upstream gradient dO ~ N(0,1) from
 synth.make_grad, optional initial state and final-state gradient N(0,1)*0.5.
 Sizes span several 64-token blocks, several reverse segments per chain (the
-pre-pass over (Q, dO) and the reverse scan), ragged tails, group sizes 1 to 4
-and both gradient dtypes; the 1M-token workload is checked on its first and
-last 4096 tokens and on a window across a segment boundary in the middle, with
-the states entering each window computed in float64.
+pre-pass over (Q, dO) and the reverse scan), ragged tails, group sizes 1 to 8,
+head sizes 128 and 64 and both gradient dtypes; the 1M-token workloads (head
+sizes 128 and 64) are checked on their first and last 4096 tokens and on a
+window across a segment boundary in the middle, with the states entering each
+window computed in float64.
 """
 import numpy as np
 import pytest
@@ -25,10 +26,10 @@ DEV = "cuda:0"
 BF16 = torch.bfloat16
 
 
-def inputs(B, Hq, Hkv, N, seed):
-    w = synth.Workload("t", B, Hq, Hkv, N, 128, 128, 64, BF16, True, False)
+def inputs(B, Hq, Hkv, N, seed, d=128):
+    w = synth.Workload("t", B, Hq, Hkv, N, d, d, 64, BF16, True, False)
     q, k, v = synth.make_qkv(w, DEV, seed=seed)
-    do = synth.make_grad((B, Hq, N, 128), DEV, seed=seed + 1)
+    do = synth.make_grad((B, Hq, N, d), DEV, seed=seed + 1)
     return q, k, v, do
 
 
@@ -61,6 +62,29 @@ def test_backward_matches_oracle(B, Hq, Hkv, N, grad_dtype, s_in, ds_out):
     check_grads("", got, ref, grad_dtype)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,N,grad_dtype,s_in,ds_out", [
+    (1, 4, 1, 3000, torch.float32, False, False),     # G = 4, 11 segments, ragged tail
+    (2, 8, 2, 777, BF16, True, True),                 # bf16 gradients, both state terms
+    (1, 4, 2, 64, BF16, False, False),                # one full block
+    (1, 4, 1, 1, torch.float32, True, True),          # one token
+    (1, 8, 1, 4100, BF16, False, True),               # G = 8
+    (1, 16, 4, 20000, BF16, True, True),              # G = 4, four chains of many segments
+])
+def test_backward_head_size_64(B, Hq, Hkv, N, grad_dtype, s_in, ds_out):
+    """d = dv = 64 with groups of a multiple of four query heads: dQ on the
+    four-wave forward kernel, dK/dV on the four-wave reverse kernel."""
+    need_gpu()
+    say(f"case backward d=64 B={B} Hq={Hq} Hkv={Hkv} N={N} grad={grad_dtype} s_in={s_in} ds_out={ds_out}")
+    q, k, v, do = inputs(B, Hq, Hkv, N, seed=N + Hq + 64, d=64)
+    S0 = synth.random_state((B, Hkv, 64, 64), DEV, seed=N + 13, scale=0.5) if s_in else None
+    dS = synth.random_state((B, Hkv, 64, 64), DEV, seed=N + 14, scale=0.5) if ds_out else None
+    got = la.backward(q, k, v, do, grad_dtype=grad_dtype, s_in=S0, grad_s_out=dS, return_state_grad=True)
+    torch.cuda.synchronize()
+    ref = oracle.backward_chunkwise(f64(q), f64(k), f64(v), f64(do), 64, None if S0 is None else f64(S0),
+                                    None if dS is None else f64(dS))
+    check_grads("d=64", got, ref, grad_dtype)
+
+
 def test_backward_empty_sequence():
     """N = 0: no gradients to write; ds_in equals ds_out (zeros without it)."""
     need_gpu()
@@ -73,19 +97,20 @@ def test_backward_empty_sequence():
     assert torch.equal(got[3], dS) and bool((zero[3] == 0).all())
 
 
-def test_backward_in_place_state_gradient_and_chunks():
+@pytest.mark.parametrize("d", [128, 64])
+def test_backward_in_place_state_gradient_and_chunks(d):
     """A 6000-token sequence as two chunks: forward with the state carried,
     then backward from the last chunk to the first with grad_s_in written in
     place over grad_s_out; equals the oracle's whole-sequence gradients."""
     need_gpu()
     B, Hq, Hkv, N, a = 1, 8, 2, 6000, 2500
-    say(f"case backward chunks B={B} Hq={Hq} Hkv={Hkv} N={N} split={a}")
-    q, k, v, do = inputs(B, Hq, Hkv, N, seed=31)
-    S0 = synth.random_state((B, Hkv, 128, 128), DEV, seed=32, scale=0.5)
+    say(f"case backward chunks B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} split={a}")
+    q, k, v, do = inputs(B, Hq, Hkv, N, seed=31, d=d)
+    S0 = synth.random_state((B, Hkv, d, d), DEV, seed=32, scale=0.5)
     parts = [(0, a), (a, N)]
     S_a = la.forward(q[:, :, :a].contiguous(), k[:, :, :a].contiguous(), v[:, :, :a].contiguous(), s_in=S0,
                      return_state=True)[1]
-    dS = torch.zeros((B, Hkv, 128, 128), dtype=torch.float32, device=DEV)
+    dS = torch.zeros((B, Hkv, d, d), dtype=torch.float32, device=DEV)
     grads = {}
     for (lo, hi), s in reversed(list(zip(parts, (S0, S_a)))):
         sl = [x[:, :, lo:hi].contiguous() for x in (q, k, v, do)]
@@ -97,19 +122,22 @@ def test_backward_in_place_state_gradient_and_chunks():
     check_grads("chunked", got, ref, torch.float32)
 
 
-def test_backward_repeatable():
+@pytest.mark.parametrize("d", [128, 64])
+def test_backward_repeatable(d):
     """Two calls on the same inputs give bitwise-identical gradients (fixed
     reduction orders everywhere)."""
     need_gpu()
-    q, k, v, do = inputs(1, 8, 2, 20000, seed=41)
+    q, k, v, do = inputs(1, 8, 2, 20000, seed=41, d=d)
     a = la.backward(q, k, v, do, return_state_grad=True)
     b = la.backward(q, k, v, do, return_state_grad=True)
     torch.cuda.synchronize()
     assert all(torch.equal(x, y) for x, y in zip(a, b))
 
 
-def test_backward_gqa_1m_slices():
-    """B=1, 128/32 heads, N=1,048,576 (the forward workload), bf16 gradients.
+@pytest.mark.parametrize("workload", ["gqa_1m", "gqa_1m_d64"])
+def test_backward_gqa_1m_slices(workload):
+    """B=1, 128/32 heads, N=1,048,576 (the forward workloads at head sizes 128
+    and 64), bf16 gradients.
     For KV groups 0 and 31: dk, dv of the last 4096 tokens (they depend on
     those tokens only), dk, dv, dq of the first 4096 tokens (the reverse state
     entering them is sum over the group's heads of Q^T dO over every later
@@ -118,10 +146,10 @@ def test_backward_gqa_1m_slices():
     KV group 13, dq, dk, dv of a 4096-token window across a segment boundary
     in the middle of the sequence."""
     need_gpu()
-    w = synth.WORKLOADS["gqa_1m"]
+    w = synth.WORKLOADS[workload]
     G = w.Hq // w.Hkv
     N, W = w.N, 4096
-    say(f"case backward gqa_1m: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={N}")
+    say(f"case backward {workload}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={N} d={w.d}")
     q, k, v = synth.make_qkv(w, DEV, seed=0)
     do = synth.make_grad((w.B, w.Hq, N, w.dv), DEV, seed=1)
     dq, dk, dv, ds = la.backward(q, k, v, do, return_state_grad=True)
@@ -154,7 +182,7 @@ def test_backward_gqa_1m_slices():
         check_close(f"group {g} dv tokens [0, {W})", f64(dv[:, gs, :W]), head[2], BF16, BF16)
         check_close(f"group {g} dq tokens [0, {W})", f64(dq[:, hs, :W]), head[0], BF16, BF16)
         check_close(f"group {g} ds_in", f64(ds[:, gs]), head[3], BF16, torch.float32)
-    # KV group 13: a window across the boundary of segments 3/4 (4 of 8 segments per chain),
+    # KV group 13: a window across a segment boundary at the middle (8 or 16 segments per chain),
     # from the forward state of (K, V) before it and the reverse state after it, in float64
     g, c = 13, N // 2
     a, b = c - W // 2, c + W // 2
