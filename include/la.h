@@ -203,8 +203,8 @@ la_status la_decode_step(float* S, const void* q, const void* k, const void* v, 
  *                 normalize = 1 (LA_ERR_UNSUPPORTED otherwise).  z_out may
  *                 equal z_in.
  * in_dtype LA_BF16 (matrix-core kernels at d = dv = 128, block a multiple of
- * 64, and for causal = 1 also at d = dv = 64 when Hq / Hkv is a multiple of
- * 4; out_dtype LA_BF16 or LA_F32) or LA_F32 (out_dtype LA_F32).  Other shapes,
+ * 64, and also at d = dv = 64 when Hq / Hkv is a multiple of 4; out_dtype
+ * LA_BF16 or LA_F32) or LA_F32 (out_dtype LA_F32).  Other shapes,
  * d up to 128, dv a multiple of 32 up to 128, block as for la_forward, run on
  * the float32 FMA kernels (workspace size 0), for bf16 inputs too.  Any
  * Hq / Hkv.

@@ -56,10 +56,11 @@ bool fwd_mfma_path(la_dtype in_dtype, int64_t d, int64_t dv, int64_t block, int6
          Hq % Hkv == 0 && (Hq / Hkv) % 4 == 0;
 }
 
-// The causal variants run on the same kernels as the forward; the non-causal
-// kernel is built for head size 128 only.
-bool var_mfma_path(la_dtype in_dtype, int64_t d, int64_t dv, int64_t block, int64_t Hq, int64_t Hkv, bool causal) {
-  return causal ? fwd_mfma_path(in_dtype, d, dv, block, Hq, Hkv) : mfma_path(in_dtype, d, dv, block);
+// The variants run on the matrix cores for the forward's shapes: the causal
+// ones on the forward's kernels, the non-causal one on its own kernel, built
+// for the same head sizes and groups.
+bool var_mfma_path(la_dtype in_dtype, int64_t d, int64_t dv, int64_t block, int64_t Hq, int64_t Hkv) {
+  return fwd_mfma_path(in_dtype, d, dv, block, Hq, Hkv);
 }
 
 // Shape/dtype checks shared by la_forward_ex and la_forward_workspace_bytes.
@@ -558,7 +559,7 @@ size_t la_forward_variant_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, in
                                           int64_t block, la_dtype in_dtype, int causal, int normalize) {
   if (check_variant_args(B, Hq, Hkv, N, d, dv, block, in_dtype, in_dtype, causal, LA_FMAP_IDENTITY, normalize, 0.0f,
                          nullptr, nullptr) != LA_OK ||
-      N == 0 || !var_mfma_path(in_dtype, d, dv, block, Hq, Hkv, causal != 0))
+      N == 0 || !var_mfma_path(in_dtype, d, dv, block, Hq, Hkv))
     return 0;
   return la::plan_variant(B, Hq, Hkv, N, d, dv, device_cus(), causal != 0, normalize != 0).workspace_bytes;
 }
@@ -603,7 +604,7 @@ la_status la_forward_variant(const void* q, const void* k, const void* v, void* 
       return LA_ERR_HIP;
     return LA_OK;
   }
-  if (!var_mfma_path(in_dtype, d, dv, block, Hq, Hkv, causal != 0))
+  if (!var_mfma_path(in_dtype, d, dv, block, Hq, Hkv))
     return la::launch_fwd_f32_variant(q, k, v, o, in_dtype == LA_BF16, out_dtype == LA_BF16, causal != 0,
                                       fmap == LA_FMAP_RELU, normalize != 0, eps, s_in, s_out, z_in, z_out, B, Hq,
                                       Hkv, N, d, dv, tile_block(block), hs) == hipSuccess

@@ -37,8 +37,8 @@
 //    a pre-pass (state_parts) sums K_b^T V_b over parts of every segment but
 //    the last, and a scan (scan_starts) adds the parts up (s_in first, then
 //    parts in order), exact by associativity of the sums.
-//  * fwd_noncausal serves the non-causal variant: every output row reads
-//    the total state, which the same pre-pass computes.
+//  * fwd_noncausal serves the non-causal variant (head size 128 or 64): every
+//    output row reads the total state, which the same pre-pass computes.
 #include "la_internal.h"
 #include "la_mfma.h"
 
@@ -716,17 +716,21 @@ __global__ __launch_bounds__(256) void scan_starts(const float* __restrict__ par
 // takes query head w % GW and 16-token query tiles {2(w/GW), 2(w/GW) + 1} of
 // each step of 4/GW blocks (one block for GW = 4).  S_tot comes in float32
 // from the pre-pass and is rounded once to the bf16 n-major LDS layout of the
-// causal kernel's state copy.
+// causal kernel's state copy.  Built for head size 128 (GW = 4, 2, 1) and 64
+// (GW = 4, groups of a multiple of four query heads).
 // ---------------------------------------------------------------------------
-template <int GW, bool OUT_F32, int FL>
+template <int GW, bool OUT_F32, int FL, int HD = 128>
 __global__ __launch_bounds__(512, 1) void fwd_noncausal(
     const uint16_t* __restrict__ q, void* __restrict__ o, const float* __restrict__ stot,
     const float* __restrict__ ztot, int64_t tot_stride, float* s_out, float* z_out, int Hq, int Hkv,
     int subgroups, int64_t N, int64_t nblocks, int64_t blocks_per_seg, int P, float eps) {
   constexpr bool kN = (FL & kNorm) != 0;
   constexpr bool kR = (FL & kRelu) != 0;
-  __shared__ __align__(16) uint16_t st[DV * ROWST];
-  __shared__ __align__(16) float zs[kN ? D : 4];
+  // head size HD = d = dv (64 or 128): NDS 32-wide chunks of d, state rows at RST
+  static_assert(HD == 64 || HD == 128, "head size 64 or 128");
+  constexpr int NDS = HD / 32, RST = HD + 8, HH = HD * HD;
+  __shared__ __align__(16) uint16_t st[HD * RST];
+  __shared__ __align__(16) float zs[kN ? HD : 4];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
@@ -741,38 +745,39 @@ __global__ __launch_bounds__(512, 1) void fwd_noncausal(
   const int64_t blk0 = int64_t(seg) * blocks_per_seg;
   const int64_t blk1 = blk0 + blocks_per_seg < nblocks ? blk0 + blocks_per_seg : nblocks;
   const int64_t head = int64_t(b) * Hq + int64_t(g) * G + int64_t(sub) * GW + hw;
-  const uint16_t* qh = q + head * N * D;
+  const uint16_t* qh = q + head * N * HD;
   const int nlane = 8 * (l16 >> 2) + (l16 & 3);
   constexpr int SB = 4 / GW;  // blocks per step
   // tokens of this segment (a step of several blocks may run past its end)
   const int64_t tend = GW == 4 ? N : (blk1 * C < N ? blk1 * C : N);
 
-  // wave w rounds state columns [16w, 16w+16)
-  const float* S = stot + int64_t(bg) * tot_stride * (D * DV);
-  for (int dt = 0; dt < 8; ++dt) {
-    floatx4 x;
-    for (int i = 0; i < 4; ++i) x[i] = S[(16 * dt + 4 * grp + i) * DV + 16 * w + l16];
-    *reinterpret_cast<bf16x4*>(&st[(16 * w + l16) * ROWST + 16 * dt + 4 * grp]) = to_bf16x4(x);
-    if (s_out != nullptr && seg == 0 && sub == 0)
-      for (int i = 0; i < 4; ++i) s_out[int64_t(bg) * (D * DV) + (16 * dt + 4 * grp + i) * DV + 16 * w + l16] = x[i];
-  }
+  // wave w < HD/16 rounds state columns [16w, 16w+16) (all eight at 128)
+  const float* S = stot + int64_t(bg) * tot_stride * HH;
+  if (HD == 128 || w < HD / 16)
+    for (int dt = 0; dt < HD / 16; ++dt) {
+      floatx4 x;
+      for (int i = 0; i < 4; ++i) x[i] = S[(16 * dt + 4 * grp + i) * HD + 16 * w + l16];
+      *reinterpret_cast<bf16x4*>(&st[(16 * w + l16) * RST + 16 * dt + 4 * grp]) = to_bf16x4(x);
+      if (s_out != nullptr && seg == 0 && sub == 0)
+        for (int i = 0; i < 4; ++i) s_out[int64_t(bg) * HH + (16 * dt + 4 * grp + i) * HD + 16 * w + l16] = x[i];
+    }
   if constexpr (kN) {
-    const float* Z = ztot + int64_t(bg) * tot_stride * D;
-    if (tid < D) {
+    const float* Z = ztot + int64_t(bg) * tot_stride * HD;
+    if (tid < HD) {
       zs[tid] = Z[tid];
-      if (z_out != nullptr && seg == 0 && sub == 0) z_out[int64_t(bg) * D + tid] = Z[tid];
+      if (z_out != nullptr && seg == 0 && sub == 0) z_out[int64_t(bg) * HD + tid] = Z[tid];
     }
   }
   __syncthreads();  // S_tot (and z_tot) are in LDS
 
-  auto load_q = [&](bf16x8 (&qa)[2][4], int64_t blk) {
+  auto load_q = [&](bf16x8 (&qa)[2][NDS], int64_t blk) {
     for (int tj = 0; tj < 2; ++tj) {
       const int64_t t = blk * C + 16 * (t0 + tj) + l16;
-      for (int ds = 0; ds < 4; ++ds)
-        qa[tj][ds] = (t < tend) ? ld_global16(qh + t * D + 32 * ds + 8 * grp) : zero_bf16x8();
+      for (int ds = 0; ds < NDS; ++ds)
+        qa[tj][ds] = (t < tend) ? ld_global16(qh + t * HD + 32 * ds + 8 * grp) : zero_bf16x8();
     }
   };
-  bf16x8 qa[2][4], qn[2][4];
+  bf16x8 qa[2][NDS], qn[2][NDS];
   if (blk0 < blk1) load_q(qa, blk0);
   const floatx4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int64_t blk = blk0; blk < blk1; blk += SB) {
@@ -783,12 +788,12 @@ __global__ __launch_bounds__(512, 1) void fwd_noncausal(
     if (blk + SB < blk1) load_q(qn, blk + SB);
     if constexpr (kR)
       for (int tj = 0; tj < 2; ++tj)
-        for (int ds = 0; ds < 4; ++ds) qa[tj][ds] = relu_bf16x8(qa[tj][ds]);
+        for (int ds = 0; ds < NDS; ++ds) qa[tj][ds] = relu_bf16x8(qa[tj][ds]);
     float inv[2];
     (void)inv;
     if constexpr (kN) {
       float den[2] = {0.0f, 0.0f};
-      for (int ds = 0; ds < 4; ++ds) {
+      for (int ds = 0; ds < NDS; ++ds) {
         const floatx4 za = *reinterpret_cast<const floatx4*>(&zs[32 * ds + 8 * grp]);
         const floatx4 zb = *reinterpret_cast<const floatx4*>(&zs[32 * ds + 8 * grp + 4]);
         for (int tj = 0; tj < 2; ++tj)
@@ -802,13 +807,13 @@ __global__ __launch_bounds__(512, 1) void fwd_noncausal(
         inv[tj] = 1.0f / (x + eps);
       }
     }
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < HD / 32; ++m) {
       floatx4 acc[2][2];
       for (int h2 = 0; h2 < 2; ++h2)
         for (int tj = 0; tj < 2; ++tj) acc[h2][tj] = z4;
-      for (int ds = 0; ds < 4; ++ds)
+      for (int ds = 0; ds < NDS; ++ds)
         for (int h2 = 0; h2 < 2; ++h2) {
-          const bf16x8 sa = ld_lds16(st + (32 * m + 4 * h2 + nlane) * ROWST + 32 * ds + 8 * grp);
+          const bf16x8 sa = ld_lds16(st + (32 * m + 4 * h2 + nlane) * RST + 32 * ds + 8 * grp);
           for (int tj = 0; tj < 2; ++tj) acc[h2][tj] = mfma(sa, qa[tj][ds], acc[h2][tj]);
         }
       if constexpr (kN)
@@ -818,7 +823,7 @@ __global__ __launch_bounds__(512, 1) void fwd_noncausal(
       for (int tj = 0; tj < 2; ++tj) {
         const int64_t t = blk * C + 16 * (t0 + tj) + l16;
         if (t < tend) {
-          const int64_t off = (head * N + t) * DV + 32 * m + 8 * grp;
+          const int64_t off = (head * N + t) * HD + 32 * m + 8 * grp;
           if (OUT_F32) {
             float* op = static_cast<float*>(o) + off;
             *reinterpret_cast<floatx4*>(op) = acc[0][tj];
@@ -830,7 +835,7 @@ __global__ __launch_bounds__(512, 1) void fwd_noncausal(
       }
     }
     for (int tj = 0; tj < 2; ++tj)
-      for (int ds = 0; ds < 4; ++ds) qa[tj][ds] = qn[tj][ds];
+      for (int ds = 0; ds < NDS; ++ds) qa[tj][ds] = qn[tj][ds];
   }
 }
 
@@ -955,17 +960,19 @@ hipError_t variant_outputs(const void* q, const void* k, const void* v, void* o,
     else LA_VAR((launch_main<1, OUT_F32, FL>));
 #undef LA_VAR
   } else {
-    if (p.hd != 128) return hipErrorInvalidValue;  // the non-causal kernel is built for head size 128
     // totals sit at entry P of each chain's P + 1 scanned entries
     const int64_t stride = p.P + 1;
     const dim3 grid(unsigned(B * Hkv * p.subgroups * vp.P_out));
-#define LA_NC(GW)                                                                                                   \
-  hipLaunchKernelGGL((fwd_noncausal<GW, OUT_F32, FL>), grid, dim3(512), 0, stream, static_cast<const uint16_t*>(q), o, \
-                     starts + p.P * (D * DV), zstarts + p.P * D, stride, s_out, z_out, iHq, iHkv, p.subgroups, N,    \
-                     p.nblocks, vp.bps_out, vp.P_out, eps)
-    if (p.gw == 4) LA_NC(4);
-    else if (p.gw == 2) LA_NC(2);
-    else LA_NC(1);
+#define LA_NC(GW, HD)                                                                                               \
+  hipLaunchKernelGGL((fwd_noncausal<GW, OUT_F32, FL, HD>), grid, dim3(512), 0, stream,                              \
+                     static_cast<const uint16_t*>(q), o, starts + p.P * (HD * HD), zstarts + p.P * HD, stride, s_out, \
+                     z_out, iHq, iHkv, p.subgroups, N, p.nblocks, vp.bps_out, vp.P_out, eps)
+    if (p.hd == 64) {
+      if (p.gw != 4) return hipErrorInvalidValue;
+      LA_NC(4, 64);
+    } else if (p.gw == 4) LA_NC(4, 128);
+    else if (p.gw == 2) LA_NC(2, 128);
+    else LA_NC(1, 128);
 #undef LA_NC
   }
   return hipGetLastError();
@@ -975,7 +982,7 @@ template <int FL>
 hipError_t variant_run(const void* q, const void* k, const void* v, void* o, bool out_f32, const float* s_in,
                        float* s_out, const float* z_in, float* z_out, float eps, int64_t B, int64_t Hq, int64_t Hkv,
                        int64_t N, const VarPlan& vp, float* ws, hipStream_t stream) {
-  if (vp.base.hd != 128 && !(vp.base.hd == 64 && vp.causal)) return hipErrorInvalidValue;
+  if (vp.base.hd != 128 && vp.base.hd != 64) return hipErrorInvalidValue;
   if (!vp.causal || vp.base.use_starts) {
     hipError_t e = vp.base.hd == 64 ? variant_states<FL, 64>(k, v, s_in, z_in, B * Hkv, N, vp, ws, stream)
                                     : variant_states<FL, 128>(k, v, s_in, z_in, B * Hkv, N, vp, ws, stream);

@@ -163,10 +163,13 @@ def test_workspace_plan(lib):
     # head size 64 on the matrix cores for groups of four query heads (same split), else the scalar kernels
     assert lib.la_forward_workspace_bytes(1, 128, 32, 1 << 20, 64, 64, 64, BF16) == (32 * 7 * 3 + 32 * 8) * 64 * 64 * 4
     assert lib.la_forward_workspace_bytes(1, 64, 32, 1 << 20, 64, 64, 64, BF16) == 0
-    # causal variants at head size 64 on the same kernels; the non-causal kernel is built for 128 only
+    # variants at head size 64 on the matrix cores too: causal = the forward's split, non-causal sums
+    # all 8 segments of each chain (3 parts each) and scans 9 entries; groups of two: scalar (0)
     assert lib.la_forward_variant_workspace_bytes(1, 128, 32, 1 << 20, 64, 64, 64, BF16, 1, 0) == \
         (32 * 7 * 3 + 32 * 8) * 64 * 64 * 4
-    assert lib.la_forward_variant_workspace_bytes(1, 128, 32, 1 << 20, 64, 64, 64, BF16, 0, 0) == 0
+    assert lib.la_forward_variant_workspace_bytes(1, 128, 32, 1 << 20, 64, 64, 64, BF16, 0, 0) == \
+        (32 * 8 * 3 + 32 * 9) * 64 * 64 * 4
+    assert lib.la_forward_variant_workspace_bytes(1, 64, 32, 1 << 20, 64, 64, 64, BF16, 0, 0) == 0
     assert lib.la_forward_workspace_bytes(256, 128, 32, 8192, 128, 128, 64, BF16) == 0
     assert lib.la_forward_workspace_bytes(1, 128, 32, 0, 128, 128, 64, BF16) == 0
     assert lib.la_forward_workspace_bytes(1, 6, 4, 64, 128, 128, 64, BF16) == 0   # invalid -> 0

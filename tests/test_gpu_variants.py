@@ -193,27 +193,33 @@ def test_variant_in_place_state_and_normaliser(dtype):
     assert torch.equal(o, ref[0]) and torch.equal(S, ref[1]) and torch.equal(Z, ref[2])
 
 
-@pytest.mark.parametrize("fmap,norm,eps,out_dtype,Hq,Hkv,N", [
-    ("relu", True, 1e-6, torch.float32, 8, 2, 3000),   # G = 4, several segments
-    ("identity", False, 0.0, BF16, 8, 1, 1000),         # G = 8: two query-head subgroups
-    ("relu", False, 0.0, BF16, 4, 1, 100),              # two blocks
+@pytest.mark.parametrize("causal,fmap,norm,eps,out_dtype,Hq,Hkv,N", [
+    (True, "relu", True, 1e-6, torch.float32, 8, 2, 3000),   # G = 4, several segments
+    (True, "identity", False, 0.0, BF16, 8, 1, 1000),         # G = 8: two query-head subgroups
+    (True, "relu", False, 0.0, BF16, 4, 1, 100),              # two blocks
+    (False, "relu", True, 1e-6, torch.float32, 8, 2, 3000),  # non-causal: totals over 3000 tokens
+    (False, "identity", False, 0.0, BF16, 8, 1, 1000),        # G = 8
+    (False, "relu", False, 0.0, BF16, 4, 1, 100),             # two blocks, ragged
+    (False, "relu", True, 1e-6, BF16, 4, 1, 1),               # one token
 ])
-def test_causal_variant_head_size_64(fmap, norm, eps, out_dtype, Hq, Hkv, N):
-    """Causal variants at head size 64 run on the four-wave matrix-core kernel
-    (groups of four query heads) and its pre-pass with the variant flags."""
+def test_variant_head_size_64(causal, fmap, norm, eps, out_dtype, Hq, Hkv, N):
+    """Variants at head size 64 (groups of four query heads): causal ones on
+    the four-wave forward kernel, the non-causal one on its own kernel, both
+    after the pre-pass with the variant flags."""
     need_gpu()
-    say(f"case variant d=64 fmap={fmap} norm={norm} out={out_dtype} Hq={Hq} Hkv={Hkv} N={N}")
+    say(f"case variant d=64 causal={causal} fmap={fmap} norm={norm} out={out_dtype} Hq={Hq} Hkv={Hkv} N={N}")
     w = synth.Workload("t", 1, Hq, Hkv, N, 64, 64, 64, BF16, False, False)
     q, k, v = synth.make_qkv(w, DEV, seed=N + Hq)
     S0 = synth.random_state((1, Hkv, 64, 64), DEV, seed=N + 3, scale=0.5)
     Z0 = synth.random_state((1, Hkv, 64), DEV, seed=N + 4).abs() if norm else None
     if N > 256:
         lib = la.load_library()
-        assert lib.la_forward_variant_workspace_bytes(1, Hq, Hkv, N, 64, 64, 64, la.LA_BF16, 1, int(norm)) > 0
-    o, S, Z = la.forward_variant(q, k, v, causal=True, feature_map=fmap, normalize=norm, eps=eps,
+        assert lib.la_forward_variant_workspace_bytes(1, Hq, Hkv, N, 64, 64, 64, la.LA_BF16, int(causal),
+                                                      int(norm)) > 0
+    o, S, Z = la.forward_variant(q, k, v, causal=causal, feature_map=fmap, normalize=norm, eps=eps,
                                  out_dtype=out_dtype, s_in=S0, z_in=Z0, return_state=True)
     torch.cuda.synchronize()
-    ref_o, ref_S, ref_z = oracle.variant(f64(q), f64(k), f64(v), causal=True, relu=(fmap == "relu"),
+    ref_o, ref_S, ref_z = oracle.variant(f64(q), f64(k), f64(v), causal=causal, relu=(fmap == "relu"),
                                          normalize=norm, eps=eps, s_in=f64(S0),
                                          z_in=None if Z0 is None else f64(Z0))
     check_close("o", f64(o), ref_o, BF16, out_dtype, scale=rms(f64(v)) if norm else None)
