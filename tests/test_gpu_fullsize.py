@@ -40,16 +40,17 @@ def test_gqa_64k_groups_and_states():
     check_close("all final states", f64(S), oracle.final_state(f64(k), f64(v)), torch.bfloat16, torch.float32)
 
 
-def test_gqa_1m_slices_and_states():
-    """B=1, 128/32 heads, N=1,048,576, through la_forward_states +
-    la_forward_outputs (the benchmark's step): KV groups 0, 13 and 31 on the
-    first and last 65,536 tokens and on 8192-token windows across the
-    boundaries of segments 0/1 and 3/4, their final states, finiteness of every
-    output and bitwise repeatability of the whole pass."""
+@pytest.mark.parametrize("workload", ["gqa_1m", "gqa_1m_d64"])
+def test_gqa_1m_slices_and_states(workload):
+    """B=1, 128/32 heads, N=1,048,576, head sizes 128 and 64, through
+    la_forward_states + la_forward_outputs (the benchmark's step): KV groups
+    0, 13 and 31 on the first and last 65,536 tokens and on 8192-token windows
+    across the boundaries of segments 0/1 and 3/4, their final states,
+    finiteness of every output and bitwise repeatability of the whole pass."""
     need_gpu()
-    w = synth.WORKLOADS["gqa_1m"]
+    w = synth.WORKLOADS[workload]
     G = w.Hq // w.Hkv
-    say(f"case gqa_1m: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N}")
+    say(f"case {workload}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d}")
     q, k, v = synth.make_qkv(w, DEV, seed=0)
     import ctypes
     lib = la.load_library()
@@ -72,7 +73,8 @@ def test_gqa_1m_slices_and_states():
     torch.cuda.synchronize()
     assert bool(torch.isfinite(o).all())
     W = 65536
-    seg = w.N // 8   # 8 segments per chain at 1M tokens, one workgroup each
+    seg = w.N // 8   # 8 segments per chain at 1M tokens (both head sizes), one workgroup each
+    assert ws_bytes == (32 * 7 * 3 + 32 * 8) * w.d * w.dv * 4   # 7 summed segments in 3 parts + 8 starts
     for g in (0, 13, 31):
         ks_all, vs_all = f64(k[:, g:g + 1]), f64(v[:, g:g + 1])
         qs, ks, vs = group_slice(q, k, v, g, G, 0, W)
