@@ -74,8 +74,8 @@ typedef void* la_stream;
  *   LA_F32  -> LA_F32   float32 arithmetic throughout (no reduced precision);
  *                       d in 1..128, dv a multiple of 32 up to 128.
  *   LA_BF16 -> LA_BF16 or LA_F32
- *                       d = dv = 128, and d = dv = 64 when Hq / Hkv is a
- *                       multiple of 4: bf16 matrix-core products with float32
+ *                       d = dv = 128 or 64 (any Hq / Hkv): bf16
+ *                       matrix-core products with float32
  *                       accumulation and a float32 state.  Other shapes within
  *                       the LA_F32 limits: the float32 FMA kernels on the
  *                       exactly widened inputs (a small-problem path, workspace
@@ -203,8 +203,7 @@ la_status la_decode_step(float* S, const void* q, const void* k, const void* v, 
  *                 normalize = 1 (LA_ERR_UNSUPPORTED otherwise).  z_out may
  *                 equal z_in.
  * in_dtype LA_BF16 (matrix-core kernels at d = dv = 128, block a multiple of
- * 64, and also at d = dv = 64 when Hq / Hkv is a multiple of 4; out_dtype
- * LA_BF16 or LA_F32) or LA_F32 (out_dtype LA_F32).  Other shapes,
+ * 64, and also at d = dv = 64; out_dtype LA_BF16 or LA_F32) or LA_F32 (out_dtype LA_F32).  Other shapes,
  * d up to 128, dv a multiple of 32 up to 128, block as for la_forward, run on
  * the float32 FMA kernels (workspace size 0), for bf16 inputs too.  Any
  * Hq / Hkv.
@@ -252,8 +251,8 @@ size_t la_forward_variant_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, in
  *   q, k, v        the forward's inputs (layouts as above).
  *   grad_o         [B][Hq][N][dv], in_dtype.
  *   in_dtype       LA_BF16: grad_dtype LA_BF16 or LA_F32; matrix-core
- *                  kernels at d = dv = 128, and at d = dv = 64 when Hq / Hkv
- *                  is a multiple of 4, block a multiple of 64.  LA_F32:
+ *                  kernels at d = dv = 128 or 64, block a multiple of 64.
+ *                  LA_F32:
  *                  grad_dtype LA_F32.  Other shapes, d and dv multiples of 32
  *                  up to 128 and block as for la_forward, run on float32 FMA
  *                  kernels (a small-problem path), for bf16 inputs too.

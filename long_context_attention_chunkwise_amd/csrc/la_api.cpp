@@ -47,13 +47,15 @@ bool mfma_path(la_dtype in_dtype, int64_t d, int64_t dv, int64_t block) {
   return in_dtype == LA_BF16 && d == 128 && dv == 128 && tile_block(block) == kBf16Block;
 }
 
-// The forward also runs on the matrix cores at d = dv = 64 for groups of a
-// multiple of four query heads (the four-wave output kernel and its pre-pass
-// are built for head sizes 64 and 128).
+// The forward also runs on the matrix cores at d = dv = 64, any group size
+// (the four-wave output kernel and its pre-pass are built for head sizes 64
+// and 128; at 64 a workgroup serves four query heads, or one or two with the
+// other waves idle).
 bool fwd_mfma_path(la_dtype in_dtype, int64_t d, int64_t dv, int64_t block, int64_t Hq, int64_t Hkv) {
+  (void)Hq;
+  (void)Hkv;
   if (mfma_path(in_dtype, d, dv, block)) return true;
-  return in_dtype == LA_BF16 && d == 64 && dv == 64 && tile_block(block) == kBf16Block && Hkv > 0 &&
-         Hq % Hkv == 0 && (Hq / Hkv) % 4 == 0;
+  return in_dtype == LA_BF16 && d == 64 && dv == 64 && tile_block(block) == kBf16Block;
 }
 
 // The variants run on the matrix cores for the forward's shapes: the causal

@@ -31,8 +31,8 @@
 //    heads): K, V and the bf16 state are double-buffered in LDS, one barrier
 //    per block, wave w owns state columns [16w, 16w+16).  fwd_bf16_g4 (four
 //    waves, groups of four query heads, the 128/32-head shape, head size 128
-//    or 64): one wave per query head, single-buffered LDS, described above
-//    the kernel.
+//    or 64; at 64 also one or two query heads per workgroup): one wave per
+//    query head, single-buffered LDS, described above the kernel.
 //  * The sequence split into segments needs each segment's starting state:
 //    a pre-pass (state_parts) sums K_b^T V_b over parts of every segment but
 //    the last, and a scan (scan_starts) adds the parts up (s_in first, then
@@ -380,12 +380,17 @@ __device__ __forceinline__ void store_kv_tile(const KVTile<HD>& r, uint16_t* ks,
 // the earlier part phi(q_t) . z with z (float32, d entries) kept like the
 // state: wave w accumulates entries [32w, 32w+32) on the matrix cores (K^T
 // times a ones operand) and publishes them in LDS once per block.
-template <bool OUT_F32, int FL, int HD = 128>
+//
+// PARTIAL (head size 64, groups of one or two query heads, or any group size
+// not a multiple of four): a workgroup serves gw < 4 query heads.  Waves w >=
+// gw have no head: they skip the Q loads, scores and outputs (a wave-uniform
+// branch) but keep their share of the state update and its barriers.
+template <bool OUT_F32, int FL, int HD = 128, bool PARTIAL = false>
 __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     void* __restrict__ o, const float* starts, const float* s_in, float* s_out, int Hq, int Hkv, int subgroups,
     int64_t N, int64_t nblocks, int64_t blocks_per_seg, int P, const float* zstarts, const float* z_in,
-    float* z_out, float eps) {
+    float* z_out, float eps, int gw) {
   constexpr bool kN = (FL & kNorm) != 0;
   constexpr bool kR = (FL & kRelu) != 0;
   // Head size HD = d = dv (64 or 128): 32-wide chunks of d, 16-row tiles of
@@ -410,7 +415,10 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
   const int64_t blk0 = int64_t(seg) * blocks_per_seg;
   const int64_t blk1 = blk0 + blocks_per_seg < nblocks ? blk0 + blocks_per_seg : nblocks;
 
-  const int64_t head = int64_t(b) * Hq + int64_t(g) * G + int64_t(sub) * 4 + w;
+  // query heads of this workgroup: 4, or gw when PARTIAL (waves w >= gw idle)
+  const int gsz = PARTIAL ? gw : 4;
+  const bool act = !PARTIAL || __builtin_amdgcn_readfirstlane(w) < gsz;
+  const int64_t head = int64_t(b) * Hq + int64_t(g) * G + int64_t(sub) * gsz + (act ? w : 0);
   const uint16_t* qh = q + head * N * HD;
   const uint16_t* kh = k + int64_t(bg) * N * HD;
   const uint16_t* vh = v + int64_t(bg) * N * HD;
@@ -445,10 +453,15 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
   KVTile<HD> kv;
   auto load_block = [&](int64_t blk) {
     load_kv_tile<HD>(kv, kh, vh, blk, N, tid);
-    for (int ti = 0; ti < 4; ++ti) {
-      const int64_t t = blk * C + 16 * ti + l16;
-      for (int ds = 0; ds < NDS; ++ds)
-        qa[ti][ds] = (t < N) ? ld_global16(qh + t * HD + 32 * ds + 8 * grp) : zero_bf16x8();
+    if (act) {
+      for (int ti = 0; ti < 4; ++ti) {
+        const int64_t t = blk * C + 16 * ti + l16;
+        for (int ds = 0; ds < NDS; ++ds)
+          qa[ti][ds] = (t < N) ? ld_global16(qh + t * HD + 32 * ds + 8 * grp) : zero_bf16x8();
+      }
+    } else {
+      for (int ti = 0; ti < 4; ++ti)
+        for (int ds = 0; ds < NDS; ++ds) qa[ti][ds] = zero_bf16x8();
     }
   };
   if (blk0 < blk1) load_block(blk0);
@@ -463,6 +476,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
 
     // scores, one P^T tile at a time, packed to bf16 operands right away
     const floatx4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (act) {
     bf16x8 pop[4][2];
     float den[4], inv[4];  // normaliser of row 16ti + l16 (kNorm only)
     (void)den;
@@ -542,6 +556,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
         }
       }
     }
+    }  // act
     // The next block's loads go out now (Q operands are no longer needed), so
     // they overlap the state update and the barriers.
     if (blk + 1 < blk1) load_block(blk + 1);
@@ -716,8 +731,7 @@ __global__ __launch_bounds__(256) void scan_starts(const float* __restrict__ par
 // takes query head w % GW and 16-token query tiles {2(w/GW), 2(w/GW) + 1} of
 // each step of 4/GW blocks (one block for GW = 4).  S_tot comes in float32
 // from the pre-pass and is rounded once to the bf16 n-major LDS layout of the
-// causal kernel's state copy.  Built for head size 128 (GW = 4, 2, 1) and 64
-// (GW = 4, groups of a multiple of four query heads).
+// causal kernel's state copy.  Built for head sizes 128 and 64, GW = 4, 2, 1.
 // ---------------------------------------------------------------------------
 template <int GW, bool OUT_F32, int FL, int HD = 128>
 __global__ __launch_bounds__(512, 1) void fwd_noncausal(
@@ -839,14 +853,16 @@ __global__ __launch_bounds__(512, 1) void fwd_noncausal(
   }
 }
 
-template <bool OUT_F32, int FL = 0, int HD = 128>
+// gw: query heads per workgroup (4; 1 or 2 with PARTIAL)
+template <bool OUT_F32, int FL = 0, int HD = 128, bool PARTIAL = false>
 void launch_g4(dim3 grid, hipStream_t stream, const void* q, const void* k, const void* v, void* o,
                const float* starts, const float* s_in, float* s_out, int Hq, int Hkv, int subgroups, int64_t N,
                int64_t nblocks, int64_t bps, int P, const float* zstarts = nullptr, const float* z_in = nullptr,
-               float* z_out = nullptr, float eps = 0.0f) {
-  hipLaunchKernelGGL((fwd_bf16_g4<OUT_F32, FL, HD>), grid, dim3(256), 0, stream, static_cast<const uint16_t*>(q),
-                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), o, starts, s_in, s_out, Hq,
-                     Hkv, subgroups, N, nblocks, bps, P, zstarts, z_in, z_out, eps);
+               float* z_out = nullptr, float eps = 0.0f, int gw = 4) {
+  hipLaunchKernelGGL((fwd_bf16_g4<OUT_F32, FL, HD, PARTIAL>), grid, dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), o, starts, s_in, s_out, Hq, Hkv, subgroups, N, nblocks, bps,
+                     P, zstarts, z_in, z_out, eps, gw);
 }
 
 template <int GW, bool OUT_F32, int FL = 0>
@@ -953,8 +969,11 @@ hipError_t variant_outputs(const void* q, const void* k, const void* v, void* o,
   LAUNCH(grid, stream, q, k, v, o, st ? starts : nullptr, st ? nullptr : s_in, s_out, iHq, iHkv, p.subgroups, N, \
          p.nblocks, p.blocks_per_seg, p.P, zs, zi, z_out, eps)
     if (p.hd == 64) {
-      if (p.gw != 4) return hipErrorInvalidValue;
-      LA_VAR((launch_g4<OUT_F32, FL, 64>));
+      if (p.gw == 4) LA_VAR((launch_g4<OUT_F32, FL, 64>));
+      else
+        launch_g4<OUT_F32, FL, 64, true>(grid, stream, q, k, v, o, st ? starts : nullptr, st ? nullptr : s_in,
+                                         s_out, iHq, iHkv, p.subgroups, N, p.nblocks, p.blocks_per_seg, p.P, zs, zi,
+                                         z_out, eps, p.gw);
     } else if (p.gw == 4) LA_VAR((launch_g4<OUT_F32, FL>));
     else if (p.gw == 2) LA_VAR((launch_main<2, OUT_F32, FL>));
     else LA_VAR((launch_main<1, OUT_F32, FL>));
@@ -968,8 +987,9 @@ hipError_t variant_outputs(const void* q, const void* k, const void* v, void* o,
                      static_cast<const uint16_t*>(q), o, starts + p.P * (HD * HD), zstarts + p.P * HD, stride, s_out, \
                      z_out, iHq, iHkv, p.subgroups, N, p.nblocks, vp.bps_out, vp.P_out, eps)
     if (p.hd == 64) {
-      if (p.gw != 4) return hipErrorInvalidValue;
-      LA_NC(4, 64);
+      if (p.gw == 4) LA_NC(4, 64);
+      else if (p.gw == 2) LA_NC(2, 64);
+      else LA_NC(1, 64);
     } else if (p.gw == 4) LA_NC(4, 128);
     else if (p.gw == 2) LA_NC(2, 128);
     else LA_NC(1, 128);
@@ -1021,15 +1041,18 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
   launch_main<GW, F32>(grid, stream, q, k, v, o, starts, plan.use_starts ? nullptr : s_in, s_out, iHq, iHkv, \
                        plan.subgroups, N, plan.nblocks, plan.blocks_per_seg, plan.P)
   if (plan.hd == 64) {
-    // head size 64: the four-wave kernel only (groups of four query heads)
-    if (plan.gw != 4) return hipErrorInvalidValue;
+    // head size 64: the four-wave kernel, with gw = 1 or 2 query heads per
+    // workgroup (idle waves) for groups that are not a multiple of four
     const float* si = plan.use_starts ? nullptr : s_in;
-    if (out_f32)
-      launch_g4<true, 0, 64>(grid, stream, q, k, v, o, starts, si, s_out, iHq, iHkv, plan.subgroups, N,
-                             plan.nblocks, plan.blocks_per_seg, plan.P);
-    else
-      launch_g4<false, 0, 64>(grid, stream, q, k, v, o, starts, si, s_out, iHq, iHkv, plan.subgroups, N,
-                              plan.nblocks, plan.blocks_per_seg, plan.P);
+#define LA_G64(F32, PART)                                                                                     \
+  launch_g4<F32, 0, 64, PART>(grid, stream, q, k, v, o, starts, si, s_out, iHq, iHkv, plan.subgroups, N,     \
+                              plan.nblocks, plan.blocks_per_seg, plan.P, nullptr, nullptr, nullptr, 0.0f, plan.gw)
+    if (plan.gw == 4) {
+      if (out_f32) LA_G64(true, false); else LA_G64(false, false);
+    } else {
+      if (out_f32) LA_G64(true, true); else LA_G64(false, true);
+    }
+#undef LA_G64
   } else if (plan.hd != 128) {
     return hipErrorInvalidValue;
   } else if (plan.gw == 4) {

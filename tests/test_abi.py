@@ -160,16 +160,20 @@ def test_workspace_plan(lib):
         assert lib.la_backward_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, blk, BF16) == \
             lib.la_backward_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, 64, BF16)
     assert lib.la_forward_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, 96, BF16) == 0   # unsupported -> 0
-    # head size 64 on the matrix cores for groups of four query heads (same split), else the scalar kernels
+    # head size 64 on the matrix cores for every group size: groups of four and of two (one workgroup per
+    # KV head either way) give the same split; groups of three take one workgroup per query head (96
+    # chains: 3 segments, the first two summed in 12 parts)
     assert lib.la_forward_workspace_bytes(1, 128, 32, 1 << 20, 64, 64, 64, BF16) == (32 * 7 * 3 + 32 * 8) * 64 * 64 * 4
-    assert lib.la_forward_workspace_bytes(1, 64, 32, 1 << 20, 64, 64, 64, BF16) == 0
+    assert lib.la_forward_workspace_bytes(1, 64, 32, 1 << 20, 64, 64, 64, BF16) == (32 * 7 * 3 + 32 * 8) * 64 * 64 * 4
+    assert lib.la_forward_workspace_bytes(1, 96, 32, 1 << 20, 64, 64, 64, BF16) == (32 * 2 * 12 + 32 * 3) * 64 * 64 * 4
     # variants at head size 64 on the matrix cores too: causal = the forward's split, non-causal sums
-    # all 8 segments of each chain (3 parts each) and scans 9 entries; groups of two: scalar (0)
+    # all 8 segments of each chain (3 parts each) and scans 9 entries
     assert lib.la_forward_variant_workspace_bytes(1, 128, 32, 1 << 20, 64, 64, 64, BF16, 1, 0) == \
         (32 * 7 * 3 + 32 * 8) * 64 * 64 * 4
     assert lib.la_forward_variant_workspace_bytes(1, 128, 32, 1 << 20, 64, 64, 64, BF16, 0, 0) == \
         (32 * 8 * 3 + 32 * 9) * 64 * 64 * 4
-    assert lib.la_forward_variant_workspace_bytes(1, 64, 32, 1 << 20, 64, 64, 64, BF16, 0, 0) == 0
+    assert lib.la_forward_variant_workspace_bytes(1, 64, 32, 1 << 20, 64, 64, 64, BF16, 0, 0) == \
+        (32 * 8 * 3 + 32 * 9) * 64 * 64 * 4
     assert lib.la_forward_workspace_bytes(256, 128, 32, 8192, 128, 128, 64, BF16) == 0
     assert lib.la_forward_workspace_bytes(1, 128, 32, 0, 128, 128, 64, BF16) == 0
     assert lib.la_forward_workspace_bytes(1, 6, 4, 64, 128, 128, 64, BF16) == 0   # invalid -> 0
@@ -183,10 +187,11 @@ def test_workspace_plan(lib):
     assert lib.la_backward_workspace_bytes(1, 128, 32, 0, 128, 128, 64, BF16) == 0
     # Head size 64 (groups of four): states of 64 x 64, and two dK/dV workgroups per compute unit, so
     # 16 segments per chain whose 15 later segments are summed in 2 parts each (3840 pre-pass
-    # workgroups: five rounds); groups of two run on the scalar kernels (s_in^T only).
+    # workgroups: five rounds); with groups of two, 64 query heads' partials in 4 parts each.
     n64 = lib.la_backward_workspace_bytes(1, 128, 32, 1 << 20, 64, 64, 64, BF16)
     assert n64 == ((32 * 7 * 3 + 32 * 8) + 32 + 128 * 15 * 2 + 32 * 16) * 64 * 64 * 4
-    assert lib.la_backward_workspace_bytes(1, 64, 32, 1 << 20, 64, 64, 64, BF16) == 32 * 64 * 64 * 4
+    assert lib.la_backward_workspace_bytes(1, 64, 32, 1 << 20, 64, 64, 64, BF16) == \
+        ((32 * 7 * 3 + 32 * 8) + 32 + 64 * 15 * 4 + 32 * 16) * 64 * 64 * 4
     assert lib.la_backward_workspace_bytes(1, 4, 2, 64, 128, 96, 64, F32) == 2 * 128 * 96 * 4   # s_in^T
     assert lib.la_backward_workspace_bytes(1, 4, 2, 64, 48, 96, 64, F32) == 0                  # d not a multiple of 32
     # bf16 at other head sizes runs on the scalar kernels: no forward workspace, s_in^T for the backward

@@ -166,10 +166,14 @@ def test_bf16_in_place_rejected_off_the_four_head_kernel():
     (2, 16, 2, 777, torch.float32, False),    # G = 8: two query-head subgroups
     (1, 4, 1, 64, torch.bfloat16, False),     # one block
     (1, 4, 1, 20000, torch.float32, True),    # many segments on one chain
+    (2, 4, 4, 3001, torch.bfloat16, True),    # G = 1: one query head per workgroup, three waves idle
+    (1, 8, 4, 777, torch.float32, False),     # G = 2
+    (1, 6, 2, 2000, torch.bfloat16, True),    # G = 3: one query head per workgroup, three subgroups
+    (1, 1, 1, 20000, torch.float32, True),    # a single head, many segments
 ])
 def test_bf16_head_size_64(B, Hq, Hkv, N, out_dtype, s_in):
-    """Head size 64 on the four-wave matrix-core kernel (groups of four query
-    heads) and its pre-pass."""
+    """Head size 64 on the four-wave matrix-core kernel (four query heads per
+    workgroup, or one or two with the other waves idle) and its pre-pass."""
     need_gpu()
     if N > 64:
         assert la.workspace_bytes(B, Hq, Hkv, N, 64, 64, 64, torch.bfloat16) > 0   # the matrix-core split

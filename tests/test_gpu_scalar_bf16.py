@@ -1,6 +1,6 @@
 """bf16 inputs at shapes the matrix-core kernels are not built for (head sizes
-other than 128, blocks other than 64 tokens) run on the scalar float32-FMA
-kernels: forward, variants and backward against the oracle.
+other than 128 and 64, d != dv, blocks other than 64 tokens) run on the scalar
+float32-FMA kernels: forward, variants and backward against the oracle.
 
 The bf16 inputs widen to float32 exactly and the arithmetic is float32, so
 float32 outputs are held to the float32 bar (1e-5 of the RMS) and bf16
@@ -25,7 +25,7 @@ def inputs(B, Hq, Hkv, N, d, dv, seed, relu_gen=True):
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,N,d,dv,block,out_dtype", [
-    (1, 4, 2, 300, 64, 64, 64, F32),     # head size 64
+    (1, 4, 2, 300, 64, 64, 32, F32),     # head size 64 with 32-token blocks
     (2, 2, 2, 257, 96, 32, 64, BF16),    # d != dv, ragged tail, bf16 output
     (1, 8, 2, 200, 128, 128, 32, F32),   # head size 128 with 32-token blocks
 ])
@@ -43,12 +43,12 @@ def test_forward_bf16_scalar(B, Hq, Hkv, N, d, dv, block, out_dtype):
 
 
 def test_variants_bf16_scalar():
-    """ReLU-normalised causal and non-causal forms at head size 64."""
+    """ReLU-normalised causal and non-causal forms at head size 96."""
     need_gpu()
-    say("case scalar bf16 variants d=64")
-    q, k, v = inputs(1, 4, 2, 333, 64, 64, seed=7, relu_gen=False)
-    S0 = synth.random_state((1, 2, 64, 64), DEV, seed=8, scale=0.5)
-    Z0 = synth.random_state((1, 2, 64), DEV, seed=9).abs()
+    say("case scalar bf16 variants d=96")
+    q, k, v = inputs(1, 4, 2, 333, 96, 96, seed=7, relu_gen=False)
+    S0 = synth.random_state((1, 2, 96, 96), DEV, seed=8, scale=0.5)
+    Z0 = synth.random_state((1, 2, 96), DEV, seed=9).abs()
     for causal in (True, False):
         o, S, Z = la.forward_variant(q, k, v, causal=causal, feature_map="relu", normalize=True, eps=1e-6,
                                      out_dtype=F32, s_in=S0, z_in=Z0, return_state=True)

@@ -201,11 +201,15 @@ def test_variant_in_place_state_and_normaliser(dtype):
     (False, "identity", False, 0.0, BF16, 8, 1, 1000),        # G = 8
     (False, "relu", False, 0.0, BF16, 4, 1, 100),             # two blocks, ragged
     (False, "relu", True, 1e-6, BF16, 4, 1, 1),               # one token
+    (True, "relu", True, 1e-6, torch.float32, 4, 4, 3000),   # G = 1 (three idle waves per workgroup)
+    (False, "relu", True, 1e-6, torch.float32, 4, 4, 3000),  # G = 1, non-causal
+    (True, "identity", False, 0.0, BF16, 6, 3, 1000),         # G = 2
+    (False, "identity", False, 0.0, BF16, 6, 2, 1000),        # G = 3, non-causal
 ])
 def test_variant_head_size_64(causal, fmap, norm, eps, out_dtype, Hq, Hkv, N):
-    """Variants at head size 64 (groups of four query heads): causal ones on
-    the four-wave forward kernel, the non-causal one on its own kernel, both
-    after the pre-pass with the variant flags."""
+    """Variants at head size 64, any group size: causal ones on the four-wave
+    forward kernel, the non-causal one on its own kernel, both after the
+    pre-pass with the variant flags."""
     need_gpu()
     say(f"case variant d=64 causal={causal} fmap={fmap} norm={norm} out={out_dtype} Hq={Hq} Hkv={Hkv} N={N}")
     w = synth.Workload("t", 1, Hq, Hkv, N, 64, 64, 64, BF16, False, False)
