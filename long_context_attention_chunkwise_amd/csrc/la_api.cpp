@@ -40,29 +40,14 @@ int device_cus() {
 constexpr int64_t kMaxBlockArg = int64_t(1) << 20;
 int64_t tile_block(int64_t block) { return block % kBf16Block == 0 ? kBf16Block : block; }
 
-// bf16 inputs with d = dv = 128 and 64-token tiles run on the matrix-core
-// kernels; every other supported shape (float32 inputs, or bf16 at other head
-// or block sizes) on the scalar float32-FMA kernels.
+// bf16 inputs with d = dv = 128 or 64 and 64-token tiles run on the
+// matrix-core kernels, any query-head group size (at 64, groups that are not
+// a multiple of four run one or two query heads per four-wave workgroup with
+// the other waves idle); every other supported shape (float32 inputs, or bf16
+// at other head or block sizes) on the scalar float32-FMA kernels.  The
+// forward, the variants and the backward share this rule.
 bool mfma_path(la_dtype in_dtype, int64_t d, int64_t dv, int64_t block) {
-  return in_dtype == LA_BF16 && d == 128 && dv == 128 && tile_block(block) == kBf16Block;
-}
-
-// The forward also runs on the matrix cores at d = dv = 64, any group size
-// (the four-wave output kernel and its pre-pass are built for head sizes 64
-// and 128; at 64 a workgroup serves four query heads, or one or two with the
-// other waves idle).
-bool fwd_mfma_path(la_dtype in_dtype, int64_t d, int64_t dv, int64_t block, int64_t Hq, int64_t Hkv) {
-  (void)Hq;
-  (void)Hkv;
-  if (mfma_path(in_dtype, d, dv, block)) return true;
-  return in_dtype == LA_BF16 && d == 64 && dv == 64 && tile_block(block) == kBf16Block;
-}
-
-// The variants run on the matrix cores for the forward's shapes: the causal
-// ones on the forward's kernels, the non-causal one on its own kernel, built
-// for the same head sizes and groups.
-bool var_mfma_path(la_dtype in_dtype, int64_t d, int64_t dv, int64_t block, int64_t Hq, int64_t Hkv) {
-  return fwd_mfma_path(in_dtype, d, dv, block, Hq, Hkv);
+  return in_dtype == LA_BF16 && d == dv && (d == 128 || d == 64) && tile_block(block) == kBf16Block;
 }
 
 // Shape/dtype checks shared by la_forward_ex and la_forward_workspace_bytes.
@@ -248,7 +233,7 @@ size_t la_forward_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
                                   int64_t block, la_dtype in_dtype) {
   la_dtype out = in_dtype;
   if (check_forward_shape(B, Hq, Hkv, N, d, dv, block, in_dtype, out) != LA_OK) return 0;
-  if (!fwd_mfma_path(in_dtype, d, dv, block, Hq, Hkv) || N == 0) return 0;
+  if (!mfma_path(in_dtype, d, dv, block) || N == 0) return 0;
   return la::plan_bf16(B, Hq, Hkv, N, d, dv, device_cus()).workspace_bytes;
 }
 
@@ -280,11 +265,11 @@ la_status validate_forward(ForwardCall& fc, const void* q, const void* k, const 
   const size_t nv = size_t(B * Hkv * N * dv) * ei, no = size_t(B * Hq * N * dv) * eo;
   const size_t ns = size_t(B * Hkv * d * dv) * sizeof(float);
   fc.ns = ns;
-  fc.scalar = !fwd_mfma_path(in_dtype, d, dv, block, Hq, Hkv);
+  fc.scalar = !mfma_path(in_dtype, d, dv, block);
   // o may be q itself on the four-head matrix-core kernel, where each query
   // head's rows are read and then written by one wave in program order.
   const bool in_place = o != nullptr && o == q;
-  if (in_place && !(fwd_mfma_path(in_dtype, d, dv, block, Hq, Hkv) && out_dtype == in_dtype && (Hq / Hkv) % 4 == 0))
+  if (in_place && !(mfma_path(in_dtype, d, dv, block) && out_dtype == in_dtype && (Hq / Hkv) % 4 == 0))
     return LA_ERR_ALIAS;
   if ((!in_place && overlap(o, no, q, nq)) || overlap(o, no, k, nk) || overlap(o, no, v, nv) ||
       overlap(o, no, s_in, ns))
@@ -381,7 +366,7 @@ la_status la_forward(const void* q, const void* k, const void* v, void* o, int64
   la_status st = check_forward_shape(B, Hq, Hkv, N, d, dv, block, in_dtype, out_dtype);
   if (st != LA_OK) return st;
   size_t ws = 0;
-  if (fwd_mfma_path(in_dtype, d, dv, block, Hq, Hkv) && N > 0)
+  if (mfma_path(in_dtype, d, dv, block) && N > 0)
     ws = la::plan_bf16(B, Hq, Hkv, N, d, dv, device_cus()).workspace_bytes;
   if (ws == 0)
     return la_forward_ex(q, k, v, o, B, Hq, Hkv, N, d, dv, block, in_dtype, out_dtype, nullptr, nullptr,
@@ -426,7 +411,7 @@ la_status check_backward_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, in
   la_status st = check_forward_shape(B, Hq, Hkv, N, d, dv, block, in_dtype, grad_dtype);
   if (st != LA_OK) return st;
   // scalar kernels: dK is computed in 32-column slices of d (dv is already a multiple of 32)
-  if (!fwd_mfma_path(in_dtype, d, dv, block, Hq, Hkv) && d % 32 != 0) return LA_ERR_UNSUPPORTED;
+  if (!mfma_path(in_dtype, d, dv, block) && d % 32 != 0) return LA_ERR_UNSUPPORTED;
   return LA_OK;
 }
 
@@ -435,7 +420,7 @@ la_status check_backward_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, in
 // 128 (eight waves) and 64 (four waves).
 size_t backward_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv, int64_t block,
                           la_dtype in_dtype) {
-  if (!fwd_mfma_path(in_dtype, d, dv, block, Hq, Hkv)) return la::bwd_f32_workspace_floats(B, Hkv, d, dv) * sizeof(float);
+  if (!mfma_path(in_dtype, d, dv, block)) return la::bwd_f32_workspace_floats(B, Hkv, d, dv) * sizeof(float);
   return la::plan_backward(B, Hq, Hkv, N, d, dv, device_cus()).workspace_bytes;
 }
 
@@ -501,7 +486,7 @@ la_status la_backward(const void* q, const void* k, const void* v, const void* g
   for (const Range& out : outputs)
     if (overlap(workspace, nw, out.p, out.n)) return LA_ERR_ALIAS;
 
-  if (!fwd_mfma_path(in_dtype, d, dv, block, Hq, Hkv))
+  if (!mfma_path(in_dtype, d, dv, block))
     return la::launch_bwd_f32(q, k, v, grad_o, grad_q, grad_k, grad_v, in_dtype == LA_BF16, grad_dtype == LA_BF16,
                               s_in, grad_s_out, grad_s_in, B, Hq, Hkv, N, d, dv, tile_block(block),
                               static_cast<float*>(workspace), hs) == hipSuccess
@@ -561,7 +546,7 @@ size_t la_forward_variant_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, in
                                           int64_t block, la_dtype in_dtype, int causal, int normalize) {
   if (check_variant_args(B, Hq, Hkv, N, d, dv, block, in_dtype, in_dtype, causal, LA_FMAP_IDENTITY, normalize, 0.0f,
                          nullptr, nullptr) != LA_OK ||
-      N == 0 || !var_mfma_path(in_dtype, d, dv, block, Hq, Hkv))
+      N == 0 || !mfma_path(in_dtype, d, dv, block))
     return 0;
   return la::plan_variant(B, Hq, Hkv, N, d, dv, device_cus(), causal != 0, normalize != 0).workspace_bytes;
 }
@@ -606,7 +591,7 @@ la_status la_forward_variant(const void* q, const void* k, const void* v, void* 
       return LA_ERR_HIP;
     return LA_OK;
   }
-  if (!var_mfma_path(in_dtype, d, dv, block, Hq, Hkv))
+  if (!mfma_path(in_dtype, d, dv, block))
     return la::launch_fwd_f32_variant(q, k, v, o, in_dtype == LA_BF16, out_dtype == LA_BF16, causal != 0,
                                       fmap == LA_FMAP_RELU, normalize != 0, eps, s_in, s_out, z_in, z_out, B, Hq,
                                       Hkv, N, d, dv, tile_block(block), hs) == hipSuccess
