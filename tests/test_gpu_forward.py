@@ -170,6 +170,7 @@ def test_bf16_in_place_rejected_off_the_four_head_kernel():
     (1, 8, 4, 777, torch.float32, False),     # G = 2
     (1, 6, 2, 2000, torch.bfloat16, True),    # G = 3: one query head per workgroup, three subgroups
     (1, 1, 1, 20000, torch.float32, True),    # a single head, many segments
+    (1, 12, 2, 1500, torch.bfloat16, True),   # G = 6: two query heads per workgroup, three subgroups
 ])
 def test_bf16_head_size_64(B, Hq, Hkv, N, out_dtype, s_in):
     """Head size 64 on the four-wave matrix-core kernel (four query heads per

@@ -205,6 +205,7 @@ def test_variant_in_place_state_and_normaliser(dtype):
     (False, "relu", True, 1e-6, torch.float32, 4, 4, 3000),  # G = 1, non-causal
     (True, "identity", False, 0.0, BF16, 6, 3, 1000),         # G = 2
     (False, "identity", False, 0.0, BF16, 6, 2, 1000),        # G = 3, non-causal
+    (False, "relu", True, 1e-6, torch.float32, 4, 2, 2000),  # G = 2, non-causal (steps of two blocks)
 ])
 def test_variant_head_size_64(causal, fmap, norm, eps, out_dtype, Hq, Hkv, N):
     """Variants at head size 64, any group size: causal ones on the four-wave
