@@ -398,7 +398,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="gqa_1m", choices=["mha_4k", "gqa_64k", "gqa_1m", "gqa_1m_d64"],
+    ap.add_argument("--workload", default="gqa_1m", choices=["mha_4k", "gqa_64k", "gqa_1m", "gqa_1m_d64", "mha_1m_d64"],
                     help="bf16 forward workload (synth.WORKLOADS); the default is the 1M-token one")
     ap.add_argument("--decode-steps", type=int, default=1000, help="0 skips the decode measurement")
     ap.add_argument("--decode-warmup", type=int, default=10)

@@ -39,9 +39,11 @@ WORKLOADS = {
     "gqa_64k": Workload("gqa_64k", 1, 128, 32, 65536, 128, 128, 64, torch.bfloat16, True, False),
     "gqa_1m": Workload("gqa_1m", 1, 128, 32, 1048576, 128, 128, 64, torch.bfloat16, True, False),
     "decode_256": Workload("decode_256", 256, 128, 32, 8192, 128, 128, 64, torch.bfloat16, True, False, 1000),
-    # the same 1M-token GQA shape at head size 64 (not on the pages: a second
-    # head size of the matrix-core forward)
+    # the same 1M-token GQA shape at head size 64, and a 1M-token MHA shape at
+    # 64 (not on the pages: a second head size of the matrix-core kernels, and
+    # one query head per KV head)
     "gqa_1m_d64": Workload("gqa_1m_d64", 1, 128, 32, 1048576, 64, 64, 64, torch.bfloat16, True, False),
+    "mha_1m_d64": Workload("mha_1m_d64", 1, 32, 32, 1048576, 64, 64, 64, torch.bfloat16, True, False),
 }
 
 

@@ -40,9 +40,10 @@ def test_gqa_64k_groups_and_states():
     check_close("all final states", f64(S), oracle.final_state(f64(k), f64(v)), torch.bfloat16, torch.float32)
 
 
-@pytest.mark.parametrize("workload", ["gqa_1m", "gqa_1m_d64"])
+@pytest.mark.parametrize("workload", ["gqa_1m", "gqa_1m_d64", "mha_1m_d64"])
 def test_gqa_1m_slices_and_states(workload):
-    """B=1, 128/32 heads, N=1,048,576, head sizes 128 and 64, through
+    """B=1, 128/32 heads, N=1,048,576, head sizes 128 and 64 (and 32/32 heads
+    at 64: one query head per four-wave workgroup), through
     la_forward_states + la_forward_outputs (the benchmark's step): KV groups
     0, 13 and 31 on the first and last 65,536 tokens and on 8192-token windows
     across the boundaries of segments 0/1 and 3/4, their final states,
