@@ -111,35 +111,46 @@ def final_state(k, v, s_in=None):
 
 
 def chunkwise(q, k, v, block, s_in=None):
-    """Block recurrence in the teaching code's order.
+    """Chunkwise (block) evaluation of the causal sum, from its algebra.
 
-    State S starts at s_in (zeros by default).  For each block of `block`
-    tokens (the last one may be shorter):
-        inter = Q_b S          (queries against every earlier block)
-        intra = tril(Q_b K_b^T) V_b   (diagonal kept)
-        O_b   = inter + intra
-        S    <- S + K_b^T V_b  (after the block's output)
-    Returns (o, S_final).
+    Cut the tokens into blocks of `block` (the last one may be shorter).  By
+    associativity the causal sum splits, for a query t in block b, into the
+    keys of earlier blocks and the keys of block b up to t:
+        o_t = q_t . S_b + sum_{s in b, s <= t} (q_t . k_s) v_s,
+        S_b = s_in + sum_{i < b} K_i^T V_i     (exclusive prefix sum)
+    Every block's contribution K_i^T V_i is formed first, the start states
+    are their exclusive running sum, and then each block's output is its
+    inter term Q_b S_b plus its masked in-block term (Q_b K_b^T, entries with
+    s <= t kept, diagonal included) times V_b.  The final state is s_in plus
+    the sum over every block.  Returns (o, S_final).
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     s_in = None if s_in is None else _f64(s_in)
     B, Hq, Hkv, N, d, dv = _check(q, k, v, s_in)
     if block < 1:
         raise ValueError("block must be >= 1")
-    gidx = _heads_to_groups(Hq, Hkv)
-    S = np.zeros((B, Hkv, d, dv)) if s_in is None else s_in.copy()
-    o = np.zeros((B, Hq, N, dv))
-    for a in range(0, N, block):
-        e = min(a + block, N)
-        qb = q[:, :, a:e]                       # [B, Hq, c, d]
-        kb = k[:, :, a:e]                       # [B, Hkv, c, d]
-        vb = v[:, :, a:e]                       # [B, Hkv, c, dv]
-        kq = kb[:, gidx]                        # KV rows seen by each q head
-        vq = vb[:, gidx]
-        inter = np.matmul(qb, S[:, gidx])
-        intra = np.matmul(np.tril(np.matmul(qb, np.swapaxes(kq, -1, -2))), vq)
-        o[:, :, a:e] = inter + intra
-        S = S + np.matmul(np.swapaxes(kb, -1, -2), vb)
+    G = Hq // Hkv
+    nb = -(-N // block)
+    L = nb * block
+    # Zero rows pad the last block: a zero key or value adds nothing to any
+    # sum, and the rows of zero queries are dropped from the output.
+    pad = lambda x: np.concatenate([x, np.zeros(x.shape[:2] + (L - N, x.shape[3]))], axis=2)
+    # Query head j of KV head g is head g * G + j (kv_group: contiguous
+    # groups), so [B, Hq] splits into [B, Hkv, G].
+    Qb = pad(q).reshape(B, Hkv, G, nb, block, d)
+    Kb = pad(k).reshape(B, Hkv, nb, block, d)
+    Vb = pad(v).reshape(B, Hkv, nb, block, dv)
+    T = np.matmul(np.swapaxes(Kb, -1, -2), Vb)                # [B, Hkv, nb, d, dv]
+    before = np.zeros_like(T)
+    if nb > 1:
+        before[:, :, 1:] = np.cumsum(T[:, :, :-1], axis=2)    # sum over blocks i < b
+    starts = before if s_in is None else before + s_in[:, :, None]
+    inter = np.matmul(Qb, starts[:, :, None])                 # [B, Hkv, G, nb, block, dv]
+    keep = np.tril(np.ones((block, block)))                   # s <= t, diagonal kept
+    scores = np.matmul(Qb, np.swapaxes(Kb, -1, -2)[:, :, None]) * keep
+    intra = np.matmul(scores, Vb[:, :, None])
+    o = (inter + intra).reshape(B, Hq, L, dv)[:, :, :N]
+    S = T.sum(axis=2) if s_in is None else s_in + T.sum(axis=2)
     return o, S
 
 

@@ -279,28 +279,40 @@ def test_tile_update_then_read_is_not_causal():
 # ---------------------------------------------------------------------------
 
 def _mutant_chunkwise(mode):
+    """A copy of the oracle's chunkwise form with one mistake planted."""
     def chunkwise(q, k, v, block, s_in=None):
         q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
         B, Hq, N, d = q.shape
         Hkv, dv = k.shape[1], v.shape[3]
         G = Hq // Hkv
-        gidx = np.array([(h % Hkv) if mode == "gqa_modulo" else h // G for h in range(Hq)])
-        S = np.zeros((B, Hkv, d, dv)) if s_in is None else np.array(s_in, dtype=np.float64)
-        if mode == "s_in_ignored":
-            S = np.zeros((B, Hkv, d, dv))
-        o = np.zeros((B, Hq, N, dv))
-        for a in range(0, N, block):
-            e = min(a + block, N)
-            qb, kb, vb = q[:, :, a:e], k[:, :, a:e], v[:, :, a:e]
-            if mode == "update_first":
-                S = S + np.swapaxes(kb, -1, -2) @ vb
-            scores = qb @ np.swapaxes(kb[:, gidx], -1, -2)
-            mask = np.tril(np.ones((e - a, e - a)), -1 if mode == "strict_tril" else 0)
-            Suse = np.swapaxes(S, -1, -2) if mode == "transposed_state" and d == dv else S
-            inter = 0 if mode == "no_inter" else qb @ Suse[:, gidx]
-            o[:, :, a:e] = inter + (scores * mask) @ vb[:, gidx]
-            if mode != "update_first":
-                S = S + np.swapaxes(kb, -1, -2) @ vb
+        nb = -(-N // block)
+        L = nb * block
+        pad = lambda x: np.concatenate([x, np.zeros(x.shape[:2] + (L - N, x.shape[3]))], axis=2)
+        if mode == "gqa_modulo":   # query head h reads KV head h % Hkv
+            kq = pad(k)[:, [h % Hkv for h in range(Hq)]].reshape(B, Hq, nb, block, d)
+            vq = pad(v)[:, [h % Hkv for h in range(Hq)]].reshape(B, Hq, nb, block, dv)
+        else:
+            kq = pad(np.repeat(k, G, axis=1)).reshape(B, Hq, nb, block, d)
+            vq = pad(np.repeat(v, G, axis=1)).reshape(B, Hq, nb, block, dv)
+        Qb = pad(q).reshape(B, Hq, nb, block, d)
+        T = np.matmul(np.swapaxes(kq, -1, -2), vq)
+        if mode == "update_first":   # start states include the block's own keys
+            starts = np.cumsum(T, axis=2)
+        else:
+            starts = np.zeros_like(T)
+            if nb > 1:
+                starts[:, :, 1:] = np.cumsum(T[:, :, :-1], axis=2)
+        if s_in is not None and mode != "s_in_ignored":
+            starts = starts + np.repeat(np.asarray(s_in, dtype=np.float64), G, axis=1)[:, :, None]
+        if mode == "transposed_state" and d == dv:
+            starts = np.swapaxes(starts, -1, -2)
+        keep = np.tril(np.ones((block, block)), -1 if mode == "strict_tril" else 0)
+        inter = 0 if mode == "no_inter" else np.matmul(Qb, starts)
+        intra = np.matmul(np.matmul(Qb, np.swapaxes(kq, -1, -2)) * keep, vq)
+        o = (inter + intra).reshape(B, Hq, L, dv)[:, :, :N]
+        S = np.matmul(np.swapaxes(k, -1, -2), v)
+        if s_in is not None and mode != "s_in_ignored":
+            S = S + np.asarray(s_in, dtype=np.float64)
         return o, S
     return chunkwise
 
