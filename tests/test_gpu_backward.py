@@ -19,7 +19,7 @@ import torch
 import long_context_attention_chunkwise_amd as la
 import oracle
 from long_context_attention_chunkwise_amd import synth
-from gpu_util import check_close, f64, need_gpu, say
+from gpu_util import check_close, check_state, f64, need_gpu, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -37,7 +37,7 @@ def check_grads(tag, got, ref, grad_dtype):
     for name, g, r in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
         check_close(f"{tag} {name}", f64(g), r, BF16, grad_dtype)
     if len(got) > 3:
-        check_close(f"{tag} ds_in", f64(got[3]), ref[3], BF16, torch.float32)
+        check_state(f"{tag} ds_in", f64(got[3]), ref[3], BF16)
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,N,grad_dtype,s_in,ds_out", [
@@ -185,7 +185,7 @@ def test_backward_gqa_1m_slices(workload):
         check_close(f"group {g} dk tokens [0, {W})", f64(dk[:, gs, :W]), head[1], BF16, BF16)
         check_close(f"group {g} dv tokens [0, {W})", f64(dv[:, gs, :W]), head[2], BF16, BF16)
         check_close(f"group {g} dq tokens [0, {W})", f64(dq[:, hs, :W]), head[0], BF16, BF16)
-        check_close(f"group {g} ds_in", f64(ds[:, gs]), head[3], BF16, torch.float32)
+        check_state(f"group {g} ds_in", f64(ds[:, gs]), head[3], BF16)
     # KV group 13: a window across a segment boundary at the middle (8 or 16 segments per chain),
     # from the forward state of (K, V) before it and the reverse state after it, in float64
     g, c = 13, N // 2

@@ -16,7 +16,7 @@ import torch
 import long_context_attention_chunkwise_amd as la
 import oracle
 from long_context_attention_chunkwise_amd import synth
-from gpu_util import check_close, f64, need_gpu, say
+from gpu_util import check_close, check_state, f64, need_gpu, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -38,7 +38,7 @@ def test_zero_inputs(dtype, d):
     o, S = la.forward(zq, k, v, out_dtype=torch.float32, return_state=True)
     torch.cuda.synchronize()
     assert int(torch.count_nonzero(o)) == 0
-    check_close("state with zero queries", f64(S), oracle.final_state(f64(k), f64(v)), dtype, torch.float32)
+    check_state("state with zero queries", f64(S), oracle.final_state(f64(k), f64(v)), dtype)
     for name, kk, vv in (("zero keys", zk, v), ("zero values", k, zv)):
         o, S = la.forward(q, kk, vv, out_dtype=torch.float32, s_in=S0, return_state=True)
         torch.cuda.synchronize()
@@ -64,7 +64,7 @@ def test_many_segments_forward_and_backward():
                 BF16, torch.float32)
     check_close("o last tokens", f64(o[:, :, a:]), oracle.chunkwise(qf[:, :, a:], kf[:, :, a:], vf[:, :, a:], 64,
                                                                      S_a)[0], BF16, torch.float32)
-    check_close("final state", f64(S), oracle.final_state(kf, vf), BF16, torch.float32)
+    check_state("final state", f64(S), oracle.final_state(kf, vf), BF16)
     # backward: last tokens depend only on later tokens; first tokens on the reverse state after them
     tail = oracle.backward_chunkwise(qf[:, :, a:], kf[:, :, a:], vf[:, :, a:], dof[:, :, a:], 64)
     check_close("dk last tokens", f64(dk[:, :, a:]), tail[1], BF16, torch.float32)
@@ -76,7 +76,7 @@ def test_many_segments_forward_and_backward():
     check_close("dk first tokens", f64(dk[:, :, :W]), head[1], BF16, torch.float32)
     check_close("dv first tokens", f64(dv[:, :, :W]), head[2], BF16, torch.float32)
     check_close("dq first tokens", f64(dq[:, :, :W]), head[0], BF16, torch.float32)
-    check_close("ds_in", f64(ds), head[3], BF16, torch.float32)
+    check_state("ds_in", f64(ds), head[3], BF16)
 
 
 def test_large_values():
@@ -88,7 +88,7 @@ def test_large_values():
     torch.cuda.synchronize()
     ref_o, ref_S = oracle.chunkwise(f64(q), f64(k), f64(v), 64)
     check_close("o", f64(o), ref_o, BF16, torch.float32)
-    check_close("state", f64(S), ref_S, BF16, torch.float32)
+    check_state("state", f64(S), ref_S, BF16)
 
 
 def test_decode_zero_token_keeps_state():

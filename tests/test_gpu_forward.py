@@ -13,7 +13,7 @@ import torch
 import long_context_attention_chunkwise_amd as la
 import oracle
 from long_context_attention_chunkwise_amd import synth
-from gpu_util import check_close, f64, need_gpu, say
+from gpu_util import check_close, check_state, f64, need_gpu, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -32,7 +32,7 @@ def run_case(B, Hq, Hkv, N, d, dv, dtype, out_dtype, seed=0, block=64, s_in=Fals
     torch.cuda.synchronize()
     ref_o, ref_S = oracle.chunkwise(f64(q), f64(k), f64(v), block, None if S0 is None else f64(S0))
     check_close("o", f64(o), ref_o, dtype, out_dtype)
-    check_close("state", f64(S), ref_S, dtype, torch.float32)
+    check_state("state", f64(S), ref_S, dtype)
     return o, S
 
 
@@ -71,7 +71,7 @@ def test_mha_4k_bf16():
         o, S = la.forward(q, k, v, out_dtype=out_dtype, return_state=True)
         torch.cuda.synchronize()
         check_close(f"o ({out_dtype})", f64(o), ref_o, torch.bfloat16, out_dtype)
-        check_close("state", f64(S), ref_S, torch.bfloat16, torch.float32)
+        check_state("state", f64(S), ref_S, torch.bfloat16)
 
 
 # Group sizes 1, 2, 4, 8 (two subgroups of 4), 16 (four subgroups) and 3
@@ -126,7 +126,7 @@ def test_bf16_resume_equals_single_pass():
     ref_o, ref_S = oracle.chunkwise(f64(q), f64(k), f64(v), 64)
     check_close("single pass", f64(o_full), ref_o, torch.bfloat16, torch.float32)
     check_close("resumed", f64(torch.cat([o1, o2], dim=2)), ref_o, torch.bfloat16, torch.float32)
-    check_close("resumed state (in place)", f64(S1), ref_S, torch.bfloat16, torch.float32)
+    check_state("resumed state (in place)", f64(S1), ref_S, torch.bfloat16)
 
 
 def test_bf16_deterministic():
@@ -199,7 +199,7 @@ def test_bf16_head_size_64_in_place_and_resume():
     ref_o, ref_S = oracle.chunkwise(f64(q), f64(k), f64(v), 64)
     check_close("resumed o (second chunk in place)", f64(torch.cat([o1, o2], dim=2)), ref_o, torch.bfloat16,
                 torch.bfloat16)
-    check_close("resumed state (in place)", f64(S1), ref_S, torch.bfloat16, torch.float32)
+    check_state("resumed state (in place)", f64(S1), ref_S, torch.bfloat16)
 
 
 def test_empty_sequence_state_passthrough():
@@ -232,4 +232,4 @@ def test_forward_then_decode_equals_forward():
     ref_o, ref_S = oracle.chunkwise(f64(q), f64(k), f64(v), 64)
     check_close("decoded outputs", np.stack([f64(x) for x in outs], axis=2), ref_o[:, :, P:], torch.bfloat16,
                 torch.float32)
-    check_close("state after decode", f64(S), ref_S, torch.bfloat16, torch.float32)
+    check_state("state after decode", f64(S), ref_S, torch.bfloat16)

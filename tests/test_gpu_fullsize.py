@@ -11,7 +11,7 @@ import torch
 import long_context_attention_chunkwise_amd as la
 import oracle
 from long_context_attention_chunkwise_amd import synth
-from gpu_util import check_close, f64, need_gpu, say
+from gpu_util import check_close, check_state, f64, need_gpu, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -37,7 +37,7 @@ def test_gqa_64k_groups_and_states():
         ref, ref_S = oracle.chunkwise(qs, ks, vs, w.block)
         check_close(f"group {g} o (bf16 out)", f64(o16[:, g * G:(g + 1) * G]), ref, torch.bfloat16, torch.bfloat16)
         check_close(f"group {g} o (fp32 out)", f64(o32[:, g * G:(g + 1) * G]), ref, torch.bfloat16, torch.float32)
-    check_close("all final states", f64(S), oracle.final_state(f64(k), f64(v)), torch.bfloat16, torch.float32)
+    check_state("all final states", f64(S), oracle.final_state(f64(k), f64(v)), torch.bfloat16)
 
 
 @pytest.mark.parametrize("workload", ["gqa_1m", "gqa_1m_d64", "mha_1m_d64"])
@@ -93,8 +93,8 @@ def test_gqa_1m_slices_and_states(workload):
         qs, ks, vs = group_slice(q, k, v, g, G, a, w.N)
         check_close(f"group {g} tokens [{a}, {w.N})", f64(o[:, g * G:(g + 1) * G, a:]),
                     oracle.chunkwise(qs, ks, vs, w.block, S_a)[0], torch.bfloat16, torch.bfloat16)
-        check_close(f"group {g} final state", f64(S[:, g:g + 1]), oracle.final_state(ks_all, vs_all),
-                    torch.bfloat16, torch.float32)
+        check_state(f"group {g} final state", f64(S[:, g:g + 1]), oracle.final_state(ks_all, vs_all),
+                    torch.bfloat16)
         del ks_all, vs_all
     o2 = torch.empty_like(o)
     run(o2, None)
@@ -129,8 +129,8 @@ def test_decode_256_sequences():
         del q, k, v
     torch.cuda.synchronize()
     ref_pre = {s: oracle.final_state(pre_k[s], pre_v[s]) for s in seqs}
-    check_close("prefix states (16 sequences)", np.concatenate([f64(S[s:s + 1]) for s in seqs]),
-                np.concatenate([ref_pre[s] for s in seqs]), torch.bfloat16, torch.float32)
+    check_state("prefix states (16 sequences)", np.concatenate([f64(S[s:s + 1]) for s in seqs]),
+                np.concatenate([ref_pre[s] for s in seqs]), torch.bfloat16)
 
     qs, ks, vs = synth.make_decode_steps(w, DEV, seed=1, steps=w.steps)
     o = torch.empty((w.B, w.Hq, w.dv), dtype=torch.float32, device=DEV)
@@ -163,8 +163,7 @@ def test_decode_256_sequences():
     # final states of 16 sequences: prefix state + sum over steps of k^T v
     ref_final = oracle.final_state(np.transpose(k_s, (1, 2, 0, 3)), np.transpose(v_s, (1, 2, 0, 3)),
                                    np.concatenate([ref_pre[s] for s in seqs]))
-    check_close("final states (16 sequences)", f64(S.index_select(0, sidx)), ref_final, torch.bfloat16,
-                torch.float32)
+    check_state("final states (16 sequences)", f64(S.index_select(0, sidx)), ref_final, torch.bfloat16)
     check_close("oracle recurrence vs closed form (2 sequences)", Sref, ref_final[:2], torch.float32,
                 torch.float32)
 
@@ -198,6 +197,5 @@ def test_gqa_4m_chunked_prefill():
                         f64(o[:, g * G:(g + 1) * G, :W]),
                         oracle.chunkwise(qs, ks, vs, w.block, S_ref[g])[0], torch.bfloat16, torch.bfloat16)
             S_ref[g] = oracle.final_state(f64(k[:, g:g + 1]), f64(v[:, g:g + 1]), S_ref[g])
-            check_close(f"state after chunk {c} group {g}", f64(S[:, g:g + 1]), S_ref[g], torch.bfloat16,
-                        torch.float32)
+            check_state(f"state after chunk {c} group {g}", f64(S[:, g:g + 1]), S_ref[g], torch.bfloat16)
         del q, k, v

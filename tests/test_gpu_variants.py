@@ -2,8 +2,11 @@
 normalised) against the fp64 oracle's `variant`.
 
 Tolerance: the forward's bar (2e-2 of the output RMS, + 2^-8|ref| for bf16
-output), except that normalised outputs, weighted averages of value rows
-whose RMS shrinks as the averages widen, measure it in units of RMS(v).
+output).  Normalised outputs, weighted averages of value rows whose magnitude
+shrinks as the averages widen (about 1e-3 of RMS(v) a million tokens in),
+take the RMS row by row, so each row is held to the bar at its own scale
+(tests/test_parity_bar.py shows that this bar rejects a zero output, flipped
+signs and a dropped normaliser term at that range).
 
 Inputs are seeded and synthetic (synth): q, k ~ N(0,1)/sqrt(d) raw (so the
 ReLU inside the kernels matters) or ReLU'd by the generator (for the
@@ -20,7 +23,7 @@ import torch
 import long_context_attention_chunkwise_amd as la
 import oracle
 from long_context_attention_chunkwise_amd import synth
-from gpu_util import check_close, f64, need_gpu, rms, say
+from gpu_util import check_close, check_state, f64, need_gpu, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -70,10 +73,10 @@ def test_variant_matches_oracle(causal, fmap, norm, eps, use_s, use_z, out_dtype
                                          normalize=bool(norm), eps=eps, s_in=None if S0 is None else f64(S0),
                                          z_in=None if Z0 is None else f64(Z0))
     # normalised outputs are weighted averages of value rows: tolerance in units of RMS(v)
-    check_close("o", f64(o), ref_o, BF16, out_dtype, scale=rms(f64(v)) if norm else None)
-    check_close("S_out", f64(S), ref_S, BF16, torch.float32)
+    check_close("o", f64(o), ref_o, BF16, out_dtype, per_row=norm)
+    check_state("S_out", f64(S), ref_S, BF16)
     if norm:
-        check_close("z_out", f64(Z), ref_z, BF16, torch.float32)
+        check_state("z_out", f64(Z), ref_z, BF16)
 
 
 @pytest.mark.parametrize("Hq,Hkv", [(8, 2), (4, 2), (3, 3)])
@@ -121,20 +124,19 @@ def test_variants_gqa_1m_slices():
         for lo, hi, s_in, z_in in ((0, W, None, None), (a, N, S_a, z_a)):
             qs, ks, vs = f64(q[:, hs, lo:hi]), f64(k[:, gs, lo:hi]), vg[:, :, lo:hi]
             ref = oracle.variant(qs, ks, vs, causal=True, relu=True, normalize=True, eps=eps, s_in=s_in, z_in=z_in)
-            vscale = rms(vs)
             check_close(f"causal normalised group {g} tokens [{lo}, {hi})", f64(o[:, hs, lo:hi]), ref[0], BF16, BF16,
-                        scale=vscale)
+                        per_row=True)
             # non-causal: zero keys add nothing, the totals come in as the initial state
             zk, zv = np.zeros_like(ks), np.zeros_like(vs)
             ref_nc = oracle.variant(qs, zk, zv, causal=False, relu=True, normalize=True, eps=eps, s_in=S_t, z_in=z_t)
             check_close(f"non-causal normalised group {g} tokens [{lo}, {hi})", f64(onc[:, hs, lo:hi]), ref_nc[0],
-                        BF16, BF16, scale=vscale)
+                        BF16, BF16, per_row=True)
             ref_np = oracle.variant(qs, zk, zv, causal=False, relu=True, s_in=S_t)
             check_close(f"non-causal group {g} tokens [{lo}, {hi})", f64(onc_plain[:, hs, lo:hi]), ref_np[0], BF16,
                         BF16)
-        check_close(f"causal final state group {g}", f64(S[:, gs]), S_t, BF16, torch.float32)
-        check_close(f"causal final z group {g}", f64(Z[:, gs]), z_t, BF16, torch.float32)
-        check_close(f"non-causal state group {g}", f64(S_nc[:, gs]), S_t, BF16, torch.float32)
+        check_state(f"causal final state group {g}", f64(S[:, gs]), S_t, BF16)
+        check_state(f"causal final z group {g}", f64(Z[:, gs]), z_t, BF16)
+        check_state(f"non-causal state group {g}", f64(S_nc[:, gs]), S_t, BF16)
 
 
 F32_CASES = [
@@ -166,10 +168,10 @@ def test_variant_f32_matches_oracle(causal, fmap, norm, eps, use_s, use_z, B, Hq
     ref_o, ref_S, ref_z = oracle.variant(f64(q), f64(k), f64(v), causal=bool(causal), relu=(fmap == "relu"),
                                          normalize=bool(norm), eps=eps, s_in=None if S0 is None else f64(S0),
                                          z_in=None if Z0 is None else f64(Z0))
-    check_close("f32 o", f64(o), ref_o, F32, F32, scale=rms(f64(v)) if norm else None)
-    check_close("f32 S_out", f64(S), ref_S, F32, F32)
+    check_close("f32 o", f64(o), ref_o, F32, F32, per_row=norm)
+    check_state("f32 S_out", f64(S), ref_S, F32)
     if norm:
-        check_close("f32 z_out", f64(Z), ref_z, F32, F32)
+        check_state("f32 z_out", f64(Z), ref_z, F32)
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, BF16])
@@ -227,7 +229,7 @@ def test_variant_head_size_64(causal, fmap, norm, eps, out_dtype, Hq, Hkv, N):
     ref_o, ref_S, ref_z = oracle.variant(f64(q), f64(k), f64(v), causal=causal, relu=(fmap == "relu"),
                                          normalize=norm, eps=eps, s_in=f64(S0),
                                          z_in=None if Z0 is None else f64(Z0))
-    check_close("o", f64(o), ref_o, BF16, out_dtype, scale=rms(f64(v)) if norm else None)
-    check_close("S_out", f64(S), ref_S, BF16, torch.float32)
+    check_close("o", f64(o), ref_o, BF16, out_dtype, per_row=norm)
+    check_state("S_out", f64(S), ref_S, BF16)
     if norm:
-        check_close("z_out", f64(Z), ref_z, BF16, torch.float32)
+        check_state("z_out", f64(Z), ref_z, BF16)
