@@ -25,7 +25,8 @@
  * o [B][Hq][dv].
  *
  * Ownership and errors.  Every buffer is device memory owned by the caller;
- * the library keeps no global mutable state.  Calls are asynchronous on
+ * the library keeps no global mutable state other than the fixed scratch of
+ * la_forward_noalloc.  Calls are asynchronous on
  * `stream` (a hipStream_t; NULL is the default stream).  Arguments are
  * validated before anything is launched: on any error status nothing is
  * written and nothing is enqueued.  LA_ERR_HIP reports a failed launch or
@@ -51,6 +52,7 @@ typedef enum {
   LA_ERR_ALIAS = 5,       /* an output overlaps an input */
   LA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than la_forward_workspace_bytes */
   LA_ERR_HIP = 7,         /* HIP runtime or launch error */
+  LA_ERR_TOO_LARGE = 8,   /* la_forward_noalloc: the problem needs more than its fixed scratch */
   /* Range sentinels (not statuses): every 32-bit int is a value of the type, so
    * an out-of-range code passed in from C is well defined and reported as such
    * (the same holds for la_dtype and la_feature_map below). */
@@ -164,6 +166,37 @@ la_status la_forward_outputs(const void* q, const void* k, const void* v, void* 
 size_t la_forward_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
                                   int64_t d, int64_t dv, int64_t block,
                                   la_dtype in_dtype);
+
+/*
+ * la_forward_ex without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * and harnesses that forbid allocation.  It allocates nothing (no hipMalloc,
+ * hipFree or allocating library call) and computes exactly la_forward_ex
+ * (same kernels, bit-for-bit the same o and s_out).
+ *
+ * The segment-state workspace comes from a fixed array in this library's
+ * device code, LA_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, held from the
+ * library's first use on that GPU until the process ends.  A problem whose
+ * la_forward_workspace_bytes exceeds it returns LA_ERR_TOO_LARGE before
+ * anything is launched; use la_forward_ex with a caller workspace then.  At
+ * head size 128 on a 256-CU part, 128 query heads over 32 KV heads at
+ * 1,048,576 tokens need 58 MiB, and up to 200 (batch, KV head) pairs fit at
+ * any sequence length.
+ * Every call on one GPU shares that GPU's array and leaves its contents behind
+ * (nothing in it needs clearing: each call writes the entries it reads before
+ * reading them).  Calls that overlap in time on one GPU (two streams, or two
+ * host threads) race on it and must be ordered by the caller.
+ * Arguments, layouts, in-place rules and statuses otherwise as la_forward_ex.
+ * The first call on a device looks up the array's device address (once per
+ * device, with that device current).
+ */
+#define LA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+la_status la_forward_noalloc(const void* q, const void* k, const void* v, void* o,
+                             int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                             int64_t d, int64_t dv, int64_t block,
+                             la_dtype in_dtype, la_dtype out_dtype,
+                             const float* s_in, float* s_out, la_stream stream);
 
 /*
  * One decode token for a batch of sequences (page "MiniMax-01与Lightning

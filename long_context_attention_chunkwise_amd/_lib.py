@@ -14,10 +14,11 @@ LIB_PATH = os.path.join(HERE, "liblightning.so")
 LA_F32, LA_BF16 = 0, 1
 LA_OK = 0
 STATUS_NAMES = {0: "LA_OK", 1: "LA_ERR_NULL", 2: "LA_ERR_SHAPE", 3: "LA_ERR_UNSUPPORTED", 4: "LA_ERR_ALIGN",
-                5: "LA_ERR_ALIAS", 6: "LA_ERR_WORKSPACE", 7: "LA_ERR_HIP"}
+                5: "LA_ERR_ALIAS", 6: "LA_ERR_WORKSPACE", 7: "LA_ERR_HIP", 8: "LA_ERR_TOO_LARGE"}
 EXPORTS = ("la_forward", "la_forward_ex", "la_forward_states", "la_forward_outputs", "la_forward_workspace_bytes",
            "la_forward_variant", "la_forward_variant_workspace_bytes", "la_backward", "la_backward_workspace_bytes",
-           "la_decode_step", "la_status_str")
+           "la_decode_step", "la_status_str", "la_forward_noalloc")
+LA_NOALLOC_SCRATCH_BYTES = 64 << 20
 LA_FMAP_IDENTITY, LA_FMAP_RELU = 0, 1
 
 _lib = None
@@ -61,6 +62,8 @@ def load_library(path=LIB_PATH):
     lib.la_backward.restype = i32
     lib.la_backward_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, i64, i32]
     lib.la_backward_workspace_bytes.restype = sz
+    lib.la_forward_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i32, i32, vp, vp, vp]
+    lib.la_forward_noalloc.restype = i32
     lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp]
     lib.la_decode_step.restype = i32
     lib.la_status_str.argtypes = [i32]
@@ -178,6 +181,40 @@ def forward(q, k, v, block=64, out_dtype=None, s_in=None, return_state=False, ou
         raise LAError(st, "la_forward_ex")
     if return_state:
         return out, s_out
+    return out
+
+
+def forward_noalloc(q, k, v, out, block=64, s_in=None, s_out=None):
+    """la_forward_noalloc: the forward pass of `forward` writing into the
+    caller's `out` (and `s_out`, optional), with the library's fixed device
+    scratch as workspace; nothing is allocated, here or in the library.
+    The output dtype is out.dtype.  Raises LAError(LA_ERR_TOO_LARGE) when the
+    problem needs more than LA_NOALLOC_SCRATCH_BYTES of workspace."""
+    torch = _torch()
+    lib = load_library()
+    _check_tensor("q", q, 4, None)
+    dev = q.device
+    for name, t in (("k", k), ("v", v), ("out", out)):
+        _check_tensor(name, t, 4, dev)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    B, Hq, N, d = q.shape
+    Hkv, dv = k.shape[1], v.shape[3]
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != (B, Hkv, N, dv) or tuple(out.shape) != (B, Hq, N, dv):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}, "
+                         f"out {tuple(out.shape)}")
+    for name, t in (("s_in", s_in), ("s_out", s_out)):
+        if t is not None:
+            _check_tensor(name, t, 4, dev)
+            if t.dtype != torch.float32 or tuple(t.shape) != (B, Hkv, d, dv):
+                raise ValueError(f"{name} must be float32 [B, Hkv, d, dv]")
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.la_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, N, d, dv, block,
+                                    _dtype_code(q.dtype), _dtype_code(out.dtype), _ptr(s_in), _ptr(s_out),
+                                    ctypes.c_void_p(stream))
+    if st != LA_OK:
+        raise LAError(st, "la_forward_noalloc")
     return out
 
 

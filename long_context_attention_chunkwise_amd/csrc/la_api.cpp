@@ -224,6 +224,7 @@ const char* la_status_str(la_status s) {
     case LA_ERR_ALIAS: return "an output buffer overlaps an input buffer";
     case LA_ERR_WORKSPACE: return "workspace missing or too small";
     case LA_ERR_HIP: return "HIP runtime or launch error";
+    case LA_ERR_TOO_LARGE: return "problem needs more workspace than the allocation-free entry point's fixed scratch";
     default: break;
   }
   return "unknown status";
@@ -252,7 +253,8 @@ struct ForwardCall {
 la_status validate_forward(ForwardCall& fc, const void* q, const void* k, const void* v, const void* o,
                            bool need_q_o, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv,
                            int64_t block, la_dtype in_dtype, la_dtype out_dtype, const float* s_in,
-                           const float* s_out, const void* workspace, size_t workspace_bytes) {
+                           const float* s_out, const void* workspace, size_t workspace_bytes,
+                           bool check_workspace = true) {
   la_status st = check_forward_shape(B, Hq, Hkv, N, d, dv, block, in_dtype, out_dtype);
   if (st != LA_OK) return st;
   // With N == 0 the token tensors are empty and may be NULL.
@@ -282,7 +284,7 @@ la_status validate_forward(ForwardCall& fc, const void* q, const void* k, const 
   if (!fc.scalar && N > 0) {
     fc.plan = la::plan_bf16(B, Hq, Hkv, N, d, dv, device_cus());
     const size_t nw = fc.plan.workspace_bytes;
-    if (nw > 0) {
+    if (nw > 0 && check_workspace) {
       if (workspace == nullptr || workspace_bytes < nw) return LA_ERR_WORKSPACE;
       if (!aligned16(workspace)) return LA_ERR_ALIGN;
       if (overlap(workspace, nw, q, nq) || overlap(workspace, nw, k, nk) || overlap(workspace, nw, v, nv) ||
@@ -320,6 +322,20 @@ la_status run_outputs(const ForwardCall& fc, const void* q, const void* k, const
 }
 
 }  // namespace
+
+namespace la {
+
+la_status check_forward_args(const void* q, const void* k, const void* v, const void* o, int64_t B, int64_t Hq,
+                             int64_t Hkv, int64_t N, int64_t d, int64_t dv, int64_t block, la_dtype in_dtype,
+                             la_dtype out_dtype, const float* s_in, const float* s_out, size_t* workspace_bytes) {
+  ForwardCall fc;
+  la_status st = validate_forward(fc, q, k, v, o, true, B, Hq, Hkv, N, d, dv, block, in_dtype, out_dtype, s_in,
+                                  s_out, nullptr, 0, false);
+  *workspace_bytes = (st == LA_OK && !fc.scalar && N > 0) ? fc.plan.workspace_bytes : 0;
+  return st;
+}
+
+}  // namespace la
 
 extern "C" {
 

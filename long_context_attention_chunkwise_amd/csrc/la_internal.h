@@ -135,6 +135,13 @@ hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const voi
                           float* ds_in, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv,
                           int64_t block, float* workspace, hipStream_t stream);
 
+// Every check la_forward_ex makes except those on the workspace; on LA_OK,
+// *workspace_bytes is the workspace the call needs (0 when none).  Touches no
+// device memory.
+la_status check_forward_args(const void* q, const void* k, const void* v, const void* o, int64_t B, int64_t Hq,
+                             int64_t Hkv, int64_t N, int64_t d, int64_t dv, int64_t block, la_dtype in_dtype,
+                             la_dtype out_dtype, const float* s_in, const float* s_out, size_t* workspace_bytes);
+
 // dst[i] = src ? src[i] : 0 for i < n.
 hipError_t launch_copy_or_zero(float* dst, const float* src, size_t n, hipStream_t stream);
 

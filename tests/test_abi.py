@@ -13,7 +13,7 @@ from long_context_attention_chunkwise_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "la.h")
 
-OK, NULL, SHAPE, UNSUP, ALIGN, ALIAS, WORKSPACE = 0, 1, 2, 3, 4, 5, 6
+OK, NULL, SHAPE, UNSUP, ALIGN, ALIAS, WORKSPACE, TOO_LARGE = 0, 1, 2, 3, 4, 5, 6, 8
 F32, BF16 = la.LA_F32, la.LA_BF16
 
 # Fake, widely spaced, 16-byte aligned device addresses: validation only
@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(8):
+    for code in range(9):
         s = lib.la_status_str(code).decode()
         assert s and (code == 0) == (s == "ok")
     assert lib.la_status_str(99).decode() == "unknown status"
@@ -214,3 +214,22 @@ def test_binding_requires_gpu_tensors():
     x = torch.zeros((1, 1, 4, 128), dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         la.forward(x, x, x)
+
+
+def test_noalloc_rejects_before_touching_the_device(lib):
+    """la_forward_noalloc: argument errors come back as from la_forward_ex, and
+    a problem whose workspace exceeds the fixed scratch is LA_ERR_TOO_LARGE,
+    both decided before any device call.  1100 (batch, KV head) pairs with two
+    four-head subgroups each need one 64 KiB start state per pair (68.75 MiB)."""
+    assert _lib.LA_NOALLOC_SCRATCH_BYTES == 64 << 20
+
+    def na(q=Q, k=K, v=V, o=O, B=1, Hq=4, Hkv=1, N=1000, d=128, dv=128, block=64, i=BF16, out=BF16):
+        return lib.la_forward_noalloc(q, k, v, o, B, Hq, Hkv, N, d, dv, block, i, out, None, None, None)
+
+    assert na(q=None) == NULL
+    assert na(Hq=6, Hkv=4) == SHAPE
+    assert na(d=256) == UNSUP
+    assert na(B=1100, Hq=8, Hkv=1, N=64) == TOO_LARGE
+    assert lib.la_forward_workspace_bytes(1100, 8, 1, 64, 128, 128, 64, BF16) == 1100 * 128 * 128 * 4
+    # the 1M-token, 128/32-head workload fits (planned here for 256 compute units)
+    assert lib.la_forward_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, 64, BF16) == (32 * 7 * 3 + 32 * 8) * 65536

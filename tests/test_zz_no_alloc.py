@@ -1,0 +1,85 @@
+"""la_forward_noalloc (the allocation-free forward, for callers that cannot
+allocate device memory) against la_forward_ex with a caller workspace, through
+the C ABI: two calls in a row, the second on a smaller input, each bit for bit
+equal to la_forward_ex's output and final state (both run the same kernels on
+the same plan; la_forward_ex itself is held to the oracle by the forward
+tests).  The first call is the 1,048,576-token, 128/32-head workload, whose
+58 MiB workspace the fixed 64 MiB scratch is sized for; the second, 5000
+tokens with an initial state and float32 output, reuses the scratch the first
+left behind.  A problem beyond the scratch is refused and writes nothing.
+"""
+import ctypes
+
+import pytest
+import torch
+
+import long_context_attention_chunkwise_amd as la
+from long_context_attention_chunkwise_amd import synth
+from gpu_util import need_gpu, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+P = ctypes.c_void_p
+
+
+def ptr(t):
+    return None if t is None else P(t.data_ptr())
+
+
+def call_pair(lib, w, out_dtype, s_in):
+    q, k, v = synth.make_qkv(w, DEV, seed=w.N % 1000 + 3)
+    shape_o = (w.B, w.Hq, w.N, w.dv)
+    shape_s = (w.B, w.Hkv, w.d, w.dv)
+    o_ex = torch.empty(shape_o, dtype=out_dtype, device=DEV)
+    o_na = torch.full(shape_o, float("nan"), dtype=out_dtype, device=DEV)
+    s_ex = torch.empty(shape_s, dtype=torch.float32, device=DEV)
+    s_na = torch.full(shape_s, float("nan"), dtype=torch.float32, device=DEV)
+    ws_bytes = la.workspace_bytes(w.B, w.Hq, w.Hkv, w.N, w.d, w.dv, w.block, torch.bfloat16)
+    assert 0 < ws_bytes <= la._lib.LA_NOALLOC_SCRATCH_BYTES
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    sp = P(torch.cuda.current_stream().cuda_stream)
+    oc = la.LA_F32 if out_dtype == torch.float32 else la.LA_BF16
+    st = lib.la_forward_ex(ptr(q), ptr(k), ptr(v), ptr(o_ex), w.B, w.Hq, w.Hkv, w.N, w.d, w.dv, w.block,
+                           la.LA_BF16, oc, ptr(s_in), ptr(s_ex), ptr(ws), ws_bytes, sp)
+    assert st == 0, la.status_str(st)
+    del ws
+    st = lib.la_forward_noalloc(ptr(q), ptr(k), ptr(v), ptr(o_na), w.B, w.Hq, w.Hkv, w.N, w.d, w.dv, w.block,
+                                la.LA_BF16, oc, ptr(s_in), ptr(s_na), sp)
+    assert st == 0, la.status_str(st)
+    torch.cuda.synchronize()
+    assert torch.equal(o_na, o_ex), "output differs from la_forward_ex"
+    assert torch.equal(s_na, s_ex), "final state differs from la_forward_ex"
+    say(f"  bitwise equal to la_forward_ex: o {tuple(o_na.shape)}, state {tuple(s_na.shape)}, "
+        f"workspace {ws_bytes / 2**20:.1f} MiB")
+
+
+def test_noalloc_matches_forward_ex_twice():
+    need_gpu()
+    torch.cuda.empty_cache()
+    lib = la.load_library()
+    w = synth.WORKLOADS["gqa_1m"]
+    say(f"case noalloc 1: {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d}, bf16 out")
+    call_pair(lib, w, torch.bfloat16, None)
+    torch.cuda.empty_cache()
+    small = synth.Workload("noalloc_small", 1, 8, 2, 5000, 128, 128, 64, torch.bfloat16, True, False)
+    say("case noalloc 2: B=1 Hq=8 Hkv=2 N=5000 d=128, s_in, fp32 out")
+    s_in = synth.random_state((1, 2, 128, 128), DEV, seed=7, scale=0.5)
+    call_pair(lib, small, torch.float32, s_in)
+
+
+def test_noalloc_refuses_beyond_its_scratch():
+    need_gpu()
+    lib = la.load_library()
+    B, Hq, Hkv, N, d = 1100, 8, 1, 64, 128
+    say(f"case noalloc too large: B={B} Hq={Hq} Hkv={Hkv} N={N}")
+    assert la.workspace_bytes(B, Hq, Hkv, N, d, d, 64, torch.bfloat16) > la._lib.LA_NOALLOC_SCRATCH_BYTES
+    q = torch.zeros((B, Hq, N, d), dtype=torch.bfloat16, device=DEV)
+    k = torch.zeros((B, Hkv, N, d), dtype=torch.bfloat16, device=DEV)
+    o = torch.full((B, Hq, N, d), 7.0, dtype=torch.bfloat16, device=DEV)
+    st = lib.la_forward_noalloc(ptr(q), ptr(k), ptr(k), ptr(o), B, Hq, Hkv, N, d, d, 64, la.LA_BF16, la.LA_BF16,
+                                None, None, P(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert st == 8, la.status_str(st)
+    assert bool((o == 7.0).all())
+    with pytest.raises(la.LAError):
+        la.forward_noalloc(q, k, k, o)
