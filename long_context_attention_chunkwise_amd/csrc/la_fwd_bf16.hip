@@ -385,10 +385,14 @@ __device__ __forceinline__ void store_kv_tile(const KVTile<HD>& r, uint16_t* ks,
 // not a multiple of four): a workgroup serves gw < 4 query heads.  Waves w >=
 // gw have no head: they skip the Q loads, scores and outputs (a wave-uniform
 // branch) but keep their share of the state update and its barriers.
+//
+// o may be q itself (in-place output): q and o are therefore not restrict.
+// Each query row is loaded into the wave's operand registers before that
+// wave writes the same output row, and never read again.
 template <bool OUT_F32, int FL, int HD = 128, bool PARTIAL = false>
 __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    void* __restrict__ o, const float* starts, const float* s_in, float* s_out, int Hq, int Hkv, int subgroups,
+    const uint16_t* q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    void* o, const float* starts, const float* s_in, float* s_out, int Hq, int Hkv, int subgroups,
     int64_t N, int64_t nblocks, int64_t blocks_per_seg, int P, const float* zstarts, const float* z_in,
     float* z_out, float eps, int gw) {
   constexpr bool kN = (FL & kNorm) != 0;
