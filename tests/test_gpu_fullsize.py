@@ -46,8 +46,13 @@ def test_gqa_1m_slices_and_states(workload):
     at 64: one query head per four-wave workgroup), through
     la_forward_states + la_forward_outputs (the benchmark's step): KV groups
     0, 13 and 31 on the first and last 65,536 tokens and on 8192-token windows
-    across the boundaries of segments 0/1 and 3/4, their final states,
-    finiteness of every output and bitwise repeatability of the whole pass."""
+    across the boundaries of segments 0/1 and 3/4; the final state of every
+    KV head (each against an fp64 GEMM over all its tokens) and the start state
+    of every segment of KV heads 0, 13 and 31 as the pre-pass left it in the
+    workspace, at the state bar; finiteness of every output and bitwise
+    repeatability of the whole pass.  For the 128-head-size workload the same
+    slices are checked once more with float32 output at the literal 2e-2 RMS.
+    About 1-2 minutes per workload, most of it the fp64 state GEMMs on the host."""
     need_gpu()
     w = synth.WORKLOADS[workload]
     G = w.Hq // w.Hkv
@@ -61,11 +66,11 @@ def test_gqa_1m_slices_and_states(workload):
     S = torch.empty((w.B, w.Hkv, w.d, w.dv), dtype=torch.float32, device=DEV)
     sp = P(torch.cuda.current_stream().cuda_stream)
 
-    def run(o, s_out):
+    def run(o, s_out, out_code=la.LA_BF16):
         assert lib.la_forward_states(P(k.data_ptr()), P(v.data_ptr()), w.B, w.Hq, w.Hkv, w.N, w.d, w.dv, w.block,
                                      la.LA_BF16, None, P(ws.data_ptr()), ws_bytes, sp) == 0
         assert lib.la_forward_outputs(P(q.data_ptr()), P(k.data_ptr()), P(v.data_ptr()), P(o.data_ptr()), w.B,
-                                      w.Hq, w.Hkv, w.N, w.d, w.dv, w.block, la.LA_BF16, la.LA_BF16, None,
+                                      w.Hq, w.Hkv, w.N, w.d, w.dv, w.block, la.LA_BF16, out_code, None,
                                       None if s_out is None else P(s_out.data_ptr()), P(ws.data_ptr()), ws_bytes,
                                       sp) == 0
 
@@ -74,98 +79,119 @@ def test_gqa_1m_slices_and_states(workload):
     torch.cuda.synchronize()
     assert bool(torch.isfinite(o).all())
     W = 65536
-    seg = w.N // 8   # 8 segments per chain at 1M tokens (both head sizes), one workgroup each
-    assert ws_bytes == (32 * 7 * 3 + 32 * 8) * w.d * w.dv * 4   # 7 summed segments in 3 parts + 8 starts
-    for g in (0, 13, 31):
-        ks_all, vs_all = f64(k[:, g:g + 1]), f64(v[:, g:g + 1])
-        qs, ks, vs = group_slice(q, k, v, g, G, 0, W)
-        check_close(f"group {g} tokens [0, {W})", f64(o[:, g * G:(g + 1) * G, :W]),
-                    oracle.chunkwise(qs, ks, vs, w.block)[0], torch.bfloat16, torch.bfloat16)
-        # windows across the boundaries of segments 0/1 and 3/4, from the fp64 state before them
-        for c in (seg, 4 * seg):
-            a, b = c - 4096, c + 4096
-            S_a = oracle.final_state(ks_all[:, :, :a], vs_all[:, :, :a])
-            qs, ks, vs = group_slice(q, k, v, g, G, a, b)
-            check_close(f"group {g} tokens [{a}, {b})", f64(o[:, g * G:(g + 1) * G, a:b]),
-                        oracle.chunkwise(qs, ks, vs, w.block, S_a)[0], torch.bfloat16, torch.bfloat16)
-        a = w.N - W
-        S_a = oracle.final_state(ks_all[:, :, :a], vs_all[:, :, :a])
-        qs, ks, vs = group_slice(q, k, v, g, G, a, w.N)
-        check_close(f"group {g} tokens [{a}, {w.N})", f64(o[:, g * G:(g + 1) * G, a:]),
-                    oracle.chunkwise(qs, ks, vs, w.block, S_a)[0], torch.bfloat16, torch.bfloat16)
-        check_state(f"group {g} final state", f64(S[:, g:g + 1]), oracle.final_state(ks_all, vs_all),
-                    torch.bfloat16)
-        del ks_all, vs_all
+    nseg, nparts = 8, 3   # 8 segments per chain at 1M tokens (both head sizes), 7 summed in 3 parts each
+    seg = w.N // nseg
+    assert ws_bytes == (w.Hkv * (nseg - 1) * nparts + w.Hkv * nseg) * w.d * w.dv * 4
+    # segment start states as the pre-pass and scan left them: [Hkv][segment][d][dv] after the partials
+    starts = ws.view(torch.float32)[w.Hkv * (nseg - 1) * nparts * w.d * w.dv:].view(w.Hkv, nseg, w.d, w.dv)
+
     o2 = torch.empty_like(o)
     run(o2, None)
     torch.cuda.synchronize()
     assert torch.equal(o, o2)
+    del o2
+    o32 = None
+    if w.d == 128:
+        o32 = torch.empty((w.B, w.Hq, w.N, w.dv), dtype=torch.float32, device=DEV)
+        run(o32, None, la.LA_F32)
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(o32).all())
+
+    def check_slice(g, a, b, s_a):
+        qs, ks, vs = group_slice(q, k, v, g, G, a, b)
+        ref = oracle.chunkwise(qs, ks, vs, w.block, s_a)[0]
+        hs = slice(g * G, (g + 1) * G)
+        check_close(f"group {g} tokens [{a}, {b})", f64(o[:, hs, a:b]), ref, torch.bfloat16, torch.bfloat16)
+        if o32 is not None:
+            check_close(f"group {g} tokens [{a}, {b}) fp32 out", f64(o32[:, hs, a:b]), ref, torch.bfloat16,
+                        torch.float32)
+
+    for g in range(w.Hkv):
+        ks_all, vs_all = f64(k[:, g:g + 1]), f64(v[:, g:g + 1])
+        check_state(f"group {g} final state", f64(S[:, g:g + 1]), oracle.final_state(ks_all, vs_all),
+                    torch.bfloat16)
+        if g not in (0, 13, 31):
+            continue
+        # start state of every segment (j = 0 is zero: no initial state), the
+        # fp64 state of the tokens before it, summed segment by segment
+        ref_j = np.zeros((1, 1, w.d, w.dv))
+        for j in range(nseg):
+            check_state(f"group {g} segment {j} start state", f64(starts[g, j])[None, None], ref_j,
+                        torch.bfloat16)
+            ref_j = oracle.final_state(ks_all[:, :, j * seg:(j + 1) * seg], vs_all[:, :, j * seg:(j + 1) * seg],
+                                       ref_j)
+        check_slice(g, 0, W, None)
+        # windows across the boundaries of segments 0/1 and 3/4, from the fp64 state before them
+        for c in (seg, 4 * seg):
+            a, b = c - 4096, c + 4096
+            check_slice(g, a, b, oracle.final_state(ks_all[:, :, :a], vs_all[:, :, :a]))
+        a = w.N - W
+        check_slice(g, a, w.N, oracle.final_state(ks_all[:, :, :a], vs_all[:, :, :a]))
+        del ks_all, vs_all
 
 
 def test_decode_256_sequences():
     """256 sequences, 128/32 heads, d = dv = 128: state from the forward kernel
     over a seeded 8192-token prefix, then 1000 decode steps.  Checked against
-    the oracle: 16 sampled prefix states; every step's outputs of 2 of those
-    sequences (the oracle's token recurrence); the outputs of all 16 at sampled
-    steps (the oracle's state before the step in closed form, then its decode
-    step); and the final states of the 16."""
+    the oracle: the prefix state of every sequence (an fp64 GEMM over its 8192
+    tokens, one sequence at a time); every step's outputs of 16 sampled
+    sequences (for 2 of them by the oracle's decode step repeated 1000 times,
+    for all 16 by the oracle's causal sum over the 1000 step tokens from the
+    prefix state, which the oracle's pins equate with the recurrence); and the
+    final state of every sequence (its prefix state plus the sum over the steps
+    of k^T v, one sequence at a time).  About a minute, most of it the host's
+    fp64 work."""
     need_gpu()
     w = synth.WORKLOADS["decode_256"]
-    G = w.Hq // w.Hkv
     say(f"case decode_256: B={w.B} Hq={w.Hq} Hkv={w.Hkv} prefix={w.N} steps={w.steps}")
     rng = np.random.default_rng(123)
     seqs = np.sort(rng.choice(w.B, 16, replace=False))
-    out_seqs = seqs[:2]
-    check_steps = [0, 1, 2, 99, 500, 998, 999]
     S = torch.empty((w.B, w.Hkv, w.d, w.dv), dtype=torch.float32, device=DEV)
     batch = 32
-    pre_k, pre_v, pre_q = {}, {}, {}
+    ref_pre = np.empty((w.B, w.Hkv, w.d, w.dv))
     for i in range(0, w.B, batch):
         q, k, v = synth.make_qkv(w, DEV, seed=1000 + i // batch, B=batch)
         la.forward(q, k, v, s_out=S[i:i + batch])
-        for s in seqs:
-            if i <= s < i + batch:
-                pre_k[s], pre_v[s] = f64(k[s - i:s - i + 1]), f64(v[s - i:s - i + 1])
-        del q, k, v
+        del q
+        for j in range(batch):
+            ref_pre[i + j] = oracle.final_state(f64(k[j:j + 1]), f64(v[j:j + 1]))[0]
+        del k, v
     torch.cuda.synchronize()
-    ref_pre = {s: oracle.final_state(pre_k[s], pre_v[s]) for s in seqs}
-    check_state("prefix states (16 sequences)", np.concatenate([f64(S[s:s + 1]) for s in seqs]),
-                np.concatenate([ref_pre[s] for s in seqs]), torch.bfloat16)
+    check_state("prefix states (all 256 sequences)", f64(S), ref_pre, torch.bfloat16)
 
     qs, ks, vs = synth.make_decode_steps(w, DEV, seed=1, steps=w.steps)
     o = torch.empty((w.B, w.Hq, w.dv), dtype=torch.float32, device=DEV)
-    idx = torch.as_tensor(out_seqs, device=DEV)
     sidx = torch.as_tensor(seqs, device=DEV)
-    outs, sampled = [], {}
+    outs = []
     for t in range(w.steps):
         la.decode_step(S, qs[t], ks[t], vs[t], out=o)
-        outs.append(o.index_select(0, idx))
-        if t in check_steps:
-            sampled[t] = o.index_select(0, sidx)
+        outs.append(o.index_select(0, sidx))
     torch.cuda.synchronize()
-    got = np.stack([f64(x) for x in outs])            # [T, 2, Hq, dv]
+    got = f64(torch.stack(outs, dim=2))                 # [16, Hq, T, dv]
+    del outs
 
-    q_s, k_s, v_s = (f64(x.index_select(1, sidx)) for x in (qs, ks, vs))   # [T, 16, H, d]
-    # outputs of 2 sequences, all steps, by the oracle's token recurrence
-    Sref = np.concatenate([ref_pre[s] for s in out_seqs])
-    ref_out = np.empty_like(got)
+    # the 16 sequences' step tokens as sequences of length T: [16, H, T, dim]
+    q_s, k_s, v_s = (f64(x.index_select(1, sidx)).transpose(1, 2, 0, 3) for x in (qs, ks, vs))
+    pre16 = ref_pre[seqs]
+    ref_out = oracle.chunkwise(q_s, k_s, v_s, w.block, pre16)[0]
+    check_close("decode outputs (16 sequences x 1000 steps)", got, ref_out, torch.bfloat16, torch.float32)
+    # 2 of them by the token recurrence, one oracle decode step after another
+    Sref = pre16[:2].copy()
+    rec = np.empty((2, w.Hq, w.steps, w.dv))
     for t in range(w.steps):
-        Sref, ref_out[t] = oracle.decode_step(Sref, q_s[t, :2], k_s[t, :2], v_s[t, :2])
-    check_close("decode outputs (2 sequences x 1000 steps)", got, ref_out, torch.bfloat16, torch.float32)
-    # outputs of all 16 sequences at sampled steps: state before step t in closed form
-    pre16 = np.concatenate([ref_pre[s] for s in seqs])
-    for t in check_steps:
-        S_before = oracle.final_state(np.transpose(k_s[:t], (1, 2, 0, 3)), np.transpose(v_s[:t], (1, 2, 0, 3)),
-                                      pre16)
-        _, o_ref = oracle.decode_step(S_before, q_s[t], k_s[t], v_s[t])
-        check_close(f"decode outputs (16 sequences, step {t})", f64(sampled[t]), o_ref, torch.bfloat16,
-                    torch.float32)
-    # final states of 16 sequences: prefix state + sum over steps of k^T v
-    ref_final = oracle.final_state(np.transpose(k_s, (1, 2, 0, 3)), np.transpose(v_s, (1, 2, 0, 3)),
-                                   np.concatenate([ref_pre[s] for s in seqs]))
-    check_state("final states (16 sequences)", f64(S.index_select(0, sidx)), ref_final, torch.bfloat16)
-    check_close("oracle recurrence vs closed form (2 sequences)", Sref, ref_final[:2], torch.float32,
+        Sref, rec[:, :, t] = oracle.decode_step(Sref, q_s[:2, :, t], k_s[:2, :, t], v_s[:2, :, t])
+    check_close("decode outputs by the recurrence (2 sequences x 1000 steps)", got[:2], rec, torch.bfloat16,
                 torch.float32)
+    del q_s, got, ref_out, rec
+
+    # final state of every sequence: prefix state + sum over the steps of k^T v
+    ref_final = np.empty_like(ref_pre)
+    for b in range(w.B):
+        kb = f64(ks[:, b]).transpose(1, 0, 2)[None]    # [1, Hkv, T, d]
+        vb = f64(vs[:, b]).transpose(1, 0, 2)[None]
+        ref_final[b] = oracle.final_state(kb, vb, ref_pre[b:b + 1])[0]
+    check_state("final states (all 256 sequences)", f64(S), ref_final, torch.bfloat16)
+    check_state("oracle recurrence vs closed form (2 sequences)", Sref, ref_final[seqs[:2]], torch.float32)
 
 
 def test_gqa_4m_chunked_prefill():
