@@ -107,36 +107,80 @@ def forward_bytes(w, N, out_bytes=2):
     return w.B * N * (w.Hq * w.d * e + w.Hkv * (w.d + w.dv) * e + w.Hq * w.dv * out_bytes)
 
 
-def cpu_baseline(q, k, v, w, groups=3):
+def host_cores():
+    """Cores this process may run on (its affinity mask)."""
+    return len(os.sched_getaffinity(0))
+
+
+def blas_limit(threads):
+    """Context pinning the BLAS thread pools to `threads` (threadpoolctl), and
+    a function returning the thread count the pools report inside it."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    lim = threadpool_limits(limits=threads)
+
+    def used():
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return lim, used
+
+
+def cpu_baseline(q, k, v, w, groups=1):
     """Time the fp64 oracle on the first `groups` KV groups (each with its G
-    query heads, all tokens), one group at a time: about 12 s at 1M tokens."""
+    query heads, all tokens), one group at a time, with the BLAS pools pinned
+    to this process's affinity mask: about 13 s per group at 1M tokens."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # threadpoolctl missing: report the affinity mask
-        threads = len(os.sched_getaffinity(0))
+    cores = host_cores()
+    lim, used = blas_limit(cores)
     G = w.Hq // w.Hkv
     N = q.shape[2]
     groups = min(groups, w.Hkv)
     dt = 0.0
-    for g in range(groups):
-        qs = q[:, g * G:(g + 1) * G].float().cpu().numpy().astype(np.float64)
-        ks = k[:, g:g + 1].float().cpu().numpy().astype(np.float64)
-        vs = v[:, g:g + 1].float().cpu().numpy().astype(np.float64)
-        t0 = time.perf_counter()
-        oracle.chunkwise(qs, ks, vs, w.block)
-        dt += time.perf_counter() - t0
-        del qs, ks, vs
+    with lim:
+        threads = used()
+        for g in range(groups):
+            qs = q[:, g * G:(g + 1) * G].float().cpu().numpy().astype(np.float64)
+            ks = k[:, g:g + 1].float().cpu().numpy().astype(np.float64)
+            vs = v[:, g:g + 1].float().cpu().numpy().astype(np.float64)
+            t0 = time.perf_counter()
+            oracle.chunkwise(qs, ks, vs, w.block)
+            dt += time.perf_counter() - t0
+            del qs, ks, vs
     # The sample is groups/Hkv of the work per token of the full workload.
     return {"value": N * groups / dt / w.Hkv, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "affinity_cores": cores,
             "sample": f"fp64 chunkwise oracle on KV heads 0-{groups - 1} (query heads 0-{groups * G - 1}), "
                       f"all {N} tokens, {dt:.2f} s; value scaled to the full {w.Hkv}-KV-head workload "
                       f"(x{groups}/{w.Hkv})"}
 
 
-def bench_forward(la, synth, torch, w, steps, warmup):
+def cpu_small_baselines(synth, torch):
+    """The fp64 oracle over the two small workloads in full (the 256-token
+    float32 one and the 4096-token 8/8-head one), on all cores of the affinity
+    mask and on one thread: tokens/s (B * N / time), best of three runs."""
+    import numpy as np
+    import oracle
+    out = {}
+    cores = host_cores()
+    for name in ("tiny_f32", "mha_4k"):
+        w = synth.WORKLOADS[name]
+        q, k, v = (x.double().numpy() for x in synth.make_qkv(w, "cpu", seed=0))
+        rec = {"B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d}
+        for label, threads in (("all_cores", cores), ("one_thread", 1)):
+            lim, used = blas_limit(threads)
+            with lim:
+                n_used = used()
+                best = float("inf")
+                for _ in range(3):
+                    t0 = time.perf_counter()
+                    oracle.chunkwise(q, k, v, w.block)
+                    best = min(best, time.perf_counter() - t0)
+            rec[label] = {"tokens_per_s": round(w.B * w.N / best, 1), "seconds": round(best, 5), "threads": n_used}
+        out[name] = rec
+        del q, k, v
+    return out
+
+
+def bench_forward(la, synth, torch, w, steps, warmup, scrub_bytes=0):
     import ctypes
     lib = la.load_library()
     dev = torch.device("cuda:0")
@@ -183,7 +227,24 @@ def bench_forward(la, synth, torch, w, steps, warmup):
     if not finite:
         raise RuntimeError("non-finite forward output")
     events = {"median": round(statistics.median(t_step), 4), "min": round(min(t_step), 4),
-              "mean": round(statistics.mean(t_step), 4)}
+              "mean": round(statistics.mean(t_step), 4),
+              "cache": "warm: steps back to back, inputs may stay in the L2 / Infinity Cache if they fit"}
+    if scrub_bytes > 0:
+        # the same steps with scrub_bytes of device memory written between
+        # them (evicting the inputs from the 4 MB L2s and the 256 MB
+        # Infinity Cache), each step timed alone with events
+        scrub = torch.empty(scrub_bytes // 4, dtype=torch.int32, device=dev)
+        sevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for i in range(steps):
+            scrub.fill_(i)
+            step(sevs[i])
+        torch.cuda.synchronize()
+        t_scr = [e[0].elapsed_time(e[2]) for e in sevs]
+        t_scr_main = [e[1].elapsed_time(e[2]) for e in sevs]
+        events["scrubbed"] = {"scrub_bytes": scrub_bytes, "median": round(statistics.median(t_scr), 4),
+                              "min": round(min(t_scr), 4), "mean": round(statistics.mean(t_scr), 4),
+                              "outputs_mean": round(statistics.mean(t_scr_main), 4)}
+        del scrub
     return q, k, v, ms_step, statistics.mean(t_states), statistics.mean(t_main), ws_bytes, events
 
 
@@ -308,25 +369,53 @@ def bench_variants(la, torch, w, q, k, v, steps, warmup):
     return {"steps": steps, "warmup": warmup, "workload": w.name, "variants": out}
 
 
-def copy_bandwidth(torch, mib=1024, reps=7):
-    """Read + write GB/s of a plain device-to-device copy of `mib` MiB (the
-    runtime's copy kernel), median of `reps` event-timed copies: the practical
-    streaming ceiling the HBM-bound kernels are also compared with."""
-    n = mib << 20
-    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
-    b = torch.empty_like(a)
-    b.copy_(a)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    torch.cuda.synchronize()
-    for e0, e1 in evs:
-        e0.record()
-        b.copy_(a)
-        e1.record()
-    torch.cuda.synchronize()
-    ms = statistics.median(e0.elapsed_time(e1) for e0, e1 in evs)
-    del a, b
+STREAM_MODES = {0: "read", 1: "copy", 2: "read_write_3_2", 3: "in_place_update"}
+
+
+def stream_ceilings(torch, gib=4, reps=5):
+    """Practical HBM ceilings on this GPU: the best rate of the library's
+    streaming kernels (libla_stream.so) over a few launch shapes, per access
+    mix: read only, copy (read + write 1:1) and read + write 3:2 (the byte mix
+    of the forward output kernel) and an in-place update (the decode step's
+    pattern).  Each launch moves whole 64 KiB (60 KiB) steps of `gib` GiB
+    buffers; best event time of `reps` launches."""
+    import ctypes
+    from long_context_attention_chunkwise_amd import build as _build
+    lib = ctypes.CDLL(_build.STREAM_LIB_PATH)
+    lib.la_stream_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                  ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.la_stream_bytes_moved.argtypes = [ctypes.c_int, ctypes.c_size_t]
+    lib.la_stream_bytes_moved.restype = ctypes.c_size_t
+    n = gib << 30
+    src = torch.ones(n // 4, dtype=torch.int32, device="cuda:0")
+    dst = torch.empty(n // 4, dtype=torch.int32, device="cuda:0")
+    sink = torch.empty(8192 * 256, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    out = {}
+    for mode, name in STREAM_MODES.items():
+        best = None
+        for nt in (0, 1):
+            for grid in (256, 1024, 8192):
+                args = (mode, nt, ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), n,
+                        ctypes.c_void_p(sink.data_ptr()), grid, sp)
+                if lib.la_stream_run(*args) != 0:
+                    raise RuntimeError("stream kernel launch failed")
+                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(reps)]
+                for e0, e1 in evs:
+                    e0.record(stream)
+                    lib.la_stream_run(*args)
+                    e1.record(stream)
+                torch.cuda.synchronize()
+                ms = min(e0.elapsed_time(e1) for e0, e1 in evs)
+                gbs = lib.la_stream_bytes_moved(mode, n) / (ms * 1e-3) / 1e9
+                if best is None or gbs > best["gb_per_s"]:
+                    best = {"gb_per_s": round(gbs, 1), "nontemporal": bool(nt), "workgroups": grid}
+        out[name] = best
+    del src, dst, sink
     torch.cuda.empty_cache()
-    return 2 * n / (ms * 1e-3) / 1e9
+    return out
 
 
 def cpu_decode_baseline(S, qs, ks, vs, nseq=4, nsteps=10):
@@ -334,18 +423,16 @@ def cpu_decode_baseline(S, qs, ks, vs, nseq=4, nsteps=10):
     heads) for `nsteps` steps; sequence-steps per second."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
     f64 = lambda t: t[:nseq].float().cpu().numpy().astype(np.float64)
     St = f64(S)
     steps = [(f64(qs[t]), f64(ks[t]), f64(vs[t])) for t in range(nsteps)]
-    t0 = time.perf_counter()
-    for q, k, v in steps:
-        St, _ = oracle.decode_step(St, q, k, v)
-    dt = time.perf_counter() - t0
+    lim, used = blas_limit(host_cores())
+    with lim:
+        threads = used()
+        t0 = time.perf_counter()
+        for q, k, v in steps:
+            St, _ = oracle.decode_step(St, q, k, v)
+        dt = time.perf_counter() - t0
     return {"value": nseq * nsteps / dt, "unit": "sequence-steps/s", "cores": int(threads), "kind": "oracle",
             "sample": f"fp64 oracle decode_step on {nseq} sequences (all heads) x {nsteps} steps, {dt:.2f} s"}
 
@@ -393,6 +480,152 @@ def bench_decode(la, synth, torch, w, steps, warmup, cpu=False):
                          "bytes_per_launch": step_bytes}}
 
 
+# ---------------------------------------------------------------------------
+# Hardware counters of this run: bench.py starts itself as the program of
+# rocprofv3 --pmc (one pass per counter set, before this process touches the
+# GPU), the child runs two forward steps and a 4 GiB calibration copy, and the
+# parent reads the child's counter database.
+# ---------------------------------------------------------------------------
+COUNTER_PASSES = (("FETCH_SIZE",), ("WRITE_SIZE",), ("SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"))
+COUNTER_KERNELS = "fwd_bf16_g4|fwd_bf16_main|state_parts|stream_kernel"
+CALIBRATION_GIB = 4
+
+
+def counter_child(workload):
+    """The program rocprofv3 runs: two forward steps of `workload`, then a
+    copy of CALIBRATION_GIB GiB by the streaming library (known bytes)."""
+    import ctypes
+    import torch
+    import long_context_attention_chunkwise_amd as la
+    from long_context_attention_chunkwise_amd import synth
+    from long_context_attention_chunkwise_amd import build as _build
+    w = synth.WORKLOADS[workload]
+    q, k, v = synth.make_qkv(w, "cuda:0", seed=0)
+    o = torch.empty((w.B, w.Hq, w.N, w.dv), dtype=torch.bfloat16, device="cuda:0")
+    for _ in range(2):
+        la.forward(q, k, v, out=o)
+    torch.cuda.synchronize()
+    del q, k, v, o
+    torch.cuda.empty_cache()
+    lib = ctypes.CDLL(_build.STREAM_LIB_PATH)
+    lib.la_stream_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                  ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    n = CALIBRATION_GIB << 30
+    a = torch.ones(n // 4, dtype=torch.int32, device="cuda:0")
+    b = torch.empty_like(a)
+    if lib.la_stream_run(1, 0, ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b.data_ptr()), n, None, 1024,
+                         ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) != 0:
+        raise RuntimeError("calibration copy failed")
+    torch.cuda.synchronize()
+
+
+def read_counter_db(path):
+    """{kernel: {counter: mean over dispatches}} from a rocprofv3 database:
+    per dispatch, counters summed over their hardware instances, except
+    GRBM_* (one per XCD, equal): the largest instance, i.e. the cycles one XCD
+    was busy."""
+    import collections
+    import glob
+    import re
+    import sqlite3
+    files = glob.glob(os.path.join(path, "**", "*.db"), recursive=True)
+    if not files:
+        raise RuntimeError(f"no counter database under {path}")
+    per = collections.defaultdict(lambda: collections.defaultdict(dict))
+    for f in files:
+        db = sqlite3.connect(f)
+        for name, disp, dur, cname, val in db.execute(
+                "select name, dispatch_id, duration, counter_name, counter_value from pmc_events"):
+            m = re.search(r"(fwd_bf16_g4|fwd_bf16_main|state_parts|stream_kernel<1)", name)
+            if not m:
+                continue
+            d = per[m.group(1)][disp]
+            d["duration_ns"] = float(dur)
+            if cname.startswith("GRBM_"):
+                d[cname] = max(d.get(cname, 0.0), val)
+            else:
+                d[cname] = d.get(cname, 0.0) + val
+        db.close()
+    out = {}
+    for kern, disps in per.items():
+        names = {c for d in disps.values() for c in d}
+        out[kern] = {c: sum(d[c] for d in disps.values() if c in d) / sum(1 for d in disps.values() if c in d)
+                     for c in names}
+        out[kern]["dispatches"] = len(disps)
+    return out
+
+
+def collect_counters(workload, timeout_s=240):
+    """Run the counter passes on `workload`; returns per-kernel figures or a
+    reason why none were taken.  Must run before this process uses the GPU."""
+    import shutil
+    import signal
+    import subprocess
+    import tempfile
+    prof = shutil.which("rocprofv3") or ("/opt/rocm/bin/rocprofv3" if os.path.exists("/opt/rocm/bin/rocprofv3")
+                                         else None)
+    if prof is None:
+        return {"error": "rocprofv3 not found"}
+    tmp = tempfile.mkdtemp(prefix="la_counters_")
+    merged = {}
+    try:
+        for i, counters in enumerate(COUNTER_PASSES):
+            out_dir = os.path.join(tmp, f"pass{i}")
+            cmd = [prof, "--pmc", *counters, "--kernel-include-regex", COUNTER_KERNELS, "-d", out_dir, "-o", "run",
+                   "--", sys.executable, os.path.abspath(__file__), "--counter-child", "--workload", workload]
+            log(f"[bench] counters pass {i + 1}/{len(COUNTER_PASSES)}: {' '.join(counters)}")
+            env = dict(os.environ, TMPDIR=os.environ.get("TMPDIR", "/tmp"))
+            p = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, start_new_session=True,
+                                 env=env, cwd=tmp)
+            try:
+                text, _ = p.communicate(timeout=timeout_s)
+            except subprocess.TimeoutExpired:
+                os.killpg(p.pid, signal.SIGKILL)
+                p.communicate()
+                return {"error": f"counter pass {i + 1} timed out"}
+            try:
+                vals = read_counter_db(out_dir)
+            except Exception as e:  # the profiler may exit non-zero after writing its results
+                tail = text.decode(errors="replace").strip().splitlines()[-3:]
+                return {"error": f"counter pass {i + 1}: {e}; rc {p.returncode}; " + " | ".join(tail)}
+            for kern, d in vals.items():
+                merged.setdefault(kern, {}).update(d)
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    return merged
+
+
+def counter_figures(raw, cus, kernel, bytes_alg):
+    """Traffic (FETCH_SIZE and WRITE_SIZE scaled by the calibration copy), the
+    matrix-core busy fraction and the clock of `kernel` from collect_counters."""
+    if "error" in raw:
+        return {"error": raw["error"]}
+    cal = raw.get("stream_kernel<1")
+    kr = raw.get(kernel)
+    if not cal or not kr or "FETCH_SIZE" not in cal or "WRITE_SIZE" not in cal:
+        return {"error": "calibration or kernel counters missing"}
+    known = float(CALIBRATION_GIB << 30)
+    rscale = known / (cal["FETCH_SIZE"] * 1024.0)
+    wscale = known / (cal["WRITE_SIZE"] * 1024.0)
+    fetch = kr["FETCH_SIZE"] * 1024.0 * rscale
+    write = kr["WRITE_SIZE"] * 1024.0 * wscale
+    rec = {"source": "rocprofv3 --pmc child runs of this bench (2 forward steps + 4 GiB calibration copy)",
+           "fetch_bytes": round(fetch), "write_bytes": round(write), "traffic": round(fetch + write),
+           "fetch_scale": round(rscale, 4), "write_scale": round(wscale, 4)}
+    if bytes_alg:
+        rec["traffic_over_algorithmic"] = round((fetch + write) / bytes_alg, 4)
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in kr and kr.get("GRBM_GUI_ACTIVE"):
+        cycles = kr["GRBM_GUI_ACTIVE"]
+        rec["mfma_busy"] = round(kr["SQ_VALU_MFMA_BUSY_CYCLES"] / (4 * cus * cycles), 4)
+        rec["mfma_instructions"] = kr.get("SQ_INSTS_MFMA")
+        rec["active_cycles_per_xcd"] = cycles
+        dur_ns = kr.get("duration_ns")
+        if dur_ns:
+            rec["counter_run_kernel_ms"] = round(dur_ns * 1e-6, 4)
+            rec["clock_ghz_during_kernel"] = round(cycles / (dur_ns * 1e-9) / 1e9, 3)
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -406,14 +639,25 @@ def main():
     ap.add_argument("--backward-steps", type=int, default=5, help="0 skips the backward measurement")
     ap.add_argument("--backward-warmup", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-counters", action="store_true",
+                    help="skip the rocprofv3 counter passes (traffic then comes from the committed profile)")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the streaming-kernel HBM ceilings")
+    ap.add_argument("--counter-child", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (hardware-counter calibration)")
     args = ap.parse_args()
 
+    if args.counter_child:
+        counter_child(args.workload)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
+
+    # Counter passes first: they run bench.py itself under rocprofv3 in child
+    # processes, before this process initialises the GPU.
+    counters_raw = None if args.no_counters else collect_counters(args.workload)
 
     import torch
     if not torch.cuda.is_available():
@@ -425,21 +669,24 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     # the output kernel that serves this workload's query-head group size
-    main_kernel = "fwd_bf16_g4" if (w.Hq // w.Hkv) % 4 == 0 else "fwd_bf16_main"
+    main_kernel = "fwd_bf16_g4" if (w.Hq // w.Hkv) % 4 == 0 or w.d == 64 else "fwd_bf16_main"
     props = torch.cuda.get_device_properties(0)
+    bytes_main = forward_bytes(w, w.N)
+    # workloads small enough to stay in the caches are also timed behind a 1 GiB scrub
+    scrub = (1 << 30) if bytes_main < (4 << 30) else 0
     q, k, v, ms_step, ms_states, ms_main, ws_bytes, step_events = bench_forward(la, synth, torch, w, args.steps,
-                                                                                args.warmup)
+                                                                                args.warmup, scrub)
     tokens = w.B * w.N
     value = tokens / (ms_step * 1e-3)
     f_alg, f_tile = forward_flops(w, w.N)
-    bytes_main = forward_bytes(w, w.N)
     achieved = bytes_main / (ms_main * 1e-3) / 1e9
     log(f"[bench] forward: {ms_step:.3f} ms/step (states {ms_states:.3f} ms, outputs {ms_main:.3f} ms)")
 
-    cpu = None
+    cpu = cpu_small = None
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline (fp64 oracle) ...")
         cpu = cpu_baseline(q, k, v, w)
+        cpu_small = cpu_small_baselines(synth, torch)
     variants = None
     if args.variant_steps > 0:
         variants = bench_variants(la, torch, w, q, k, v, args.variant_steps, 1)
@@ -459,15 +706,49 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    copy_gbs = copy_bandwidth(torch)
-    log(f"[bench] device copy: {copy_gbs:.0f} GB/s (read + write)")
+    ceilings = None
+    if not args.no_ceilings:
+        ceilings = stream_ceilings(torch)
+        log("[bench] streaming ceilings: " + ", ".join(f"{n} {r['gb_per_s']:.0f} GB/s" for n, r in ceilings.items()))
 
     decode = None
     if args.decode_steps > 0:
         decode = bench_decode(la, synth, torch, synth.WORKLOADS["decode_256"], args.decode_steps,
                               args.decode_warmup, cpu=not args.no_cpu_baseline)
-        decode["roofline"]["frac_of_copy"] = round(decode["gb_per_s"] / copy_gbs, 4)
+        if ceilings:
+            # decode reads every state and writes it back in place
+            decode["roofline"]["frac_of_practical"] = round(
+                decode["gb_per_s"] / ceilings["in_place_update"]["gb_per_s"], 4)
+            decode["roofline"]["practical"] = "in-place update streaming kernel"
         log(f"[bench] decode: {decode['ms_per_step']:.4f} ms/step, {decode['gb_per_s']:.0f} GB/s")
+
+    counters = None
+    traffic = measured_traffic(main_kernel, w.name)
+    traffic_source = "committed profile (profiles/hbm_traffic_gqa_1m_decode_256.md)" if traffic else None
+    if counters_raw is not None:
+        counters = {main_kernel: counter_figures(counters_raw, props.multi_processor_count, main_kernel, bytes_main)}
+        if "traffic" in counters[main_kernel]:
+            traffic = counters[main_kernel]["traffic"]
+            traffic_source = "counters of this run"
+        if "state_parts" in counters_raw:
+            counters["state_parts"] = counter_figures(counters_raw, props.multi_processor_count, "state_parts",
+                                                      None)
+
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic, "traffic_source": traffic_source,
+                "kernel": main_kernel, "kernel_ms": round(ms_main, 4), "bytes_per_launch": bytes_main}
+    if ceilings:
+        # q, k, v read once and o written once: 3:2 when o is bf16
+        roofline["practical"] = "read + write 3:2 streaming kernel"
+        roofline["frac_of_practical"] = round(achieved / ceilings["read_write_3_2"]["gb_per_s"], 4)
+    mfma = {"tflops_alg": round(f_alg / (ms_step * 1e-3) / 1e12, 2),
+            "frac_alg": round(f_alg / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "tflops_tile": round(f_tile / (ms_step * 1e-3) / 1e12, 2),
+            "frac_tile": round(f_tile / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "peak_tflops": PEAK_BF16_TFLOPS, "flops_alg": f_alg, "flops_tile": f_tile}
+    if counters and "mfma_busy" in counters.get(main_kernel, {}):
+        mfma["busy_counter"] = counters[main_kernel]["mfma_busy"]
+        mfma["busy_counter_kernel"] = main_kernel
 
     rec = {
         "metric": METRIC,
@@ -484,16 +765,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "seq_len": w.N, "d": w.d,
                    "dv": w.dv, "block": w.block, "io_dtype": "bf16", "state_dtype": "f32"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": measured_traffic(main_kernel, w.name),
-                     "kernel": main_kernel, "kernel_ms": round(ms_main, 4), "bytes_per_launch": bytes_main,
-                     "frac_of_copy": round(achieved / copy_gbs, 4)},
-        "mfma": {"tflops_alg": round(f_alg / (ms_step * 1e-3) / 1e12, 2),
-                 "frac_alg": round(f_alg / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                 "tflops_tile": round(f_tile / (ms_step * 1e-3) / 1e12, 2),
-                 "frac_tile": round(f_tile / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                 "peak_tflops": PEAK_BF16_TFLOPS, "flops_alg": f_alg, "flops_tile": f_tile},
+        "roofline": roofline,
+        "mfma": mfma,
+        "counters": counters,
         "phases_ms": {"segment_states": round(ms_states, 4), "outputs": round(ms_main, 4)},
         "ms_per_step_events": step_events,
         "workspace_bytes": ws_bytes,
@@ -501,8 +775,9 @@ def main():
         "backward": backward,
         "decode": decode,
         "cpu_baseline": cpu,
+        "cpu_baseline_small_workloads": cpu_small,
         "device": {"name": props.name, "gcnArchName": getattr(props, "gcnArchName", ""),
-                   "cus": props.multi_processor_count, "copy_gb_per_s": round(copy_gbs, 1)},
+                   "cus": props.multi_processor_count, "stream_ceilings": ceilings},
         "inputs": {"generator": "synth.make_qkv (seeded torch draws)", "seed": 0,
                    "outputs_checked_finite": True},
         "software": {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None)},

@@ -1,7 +1,9 @@
 """Compile liblightning.so (the C-ABI library) for gfx950 with hipcc, in-tree.
 
 Every source under csrc/ is compiled on each call (hipcc cross-compiles
-without a GPU), then linked into ``liblightning.so`` next to this file.
+without a GPU) and linked into ``liblightning.so`` next to this file, except
+``la_stream.hip``, the benchmark's HBM streaming references, which becomes
+``libla_stream.so`` (C ABI in include/la_stream.h).
 """
 import os
 import subprocess
@@ -14,6 +16,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "liblightning.so")
+# Measurement helper for the benchmark (HBM streaming references), its own library.
+STREAM_SOURCE = "la_stream.hip"
+STREAM_LIB_PATH = os.path.join(HERE, "libla_stream.so")
 SOURCES = ["la_api.cpp", "la_fwd_f32.hip", "la_fwd_bf16.hip", "la_bwd_bf16.hip", "la_bwd_f32.hip", "la_decode.hip",
            "la_noalloc.hip"]
 ARCH = "gfx950"
@@ -43,7 +48,8 @@ def _run(cmd):
 
 
 def build(verbose=False):
-    """Compile all sources and link liblightning.so; returns its path."""
+    """Compile all sources and link liblightning.so (and the benchmark's
+    streaming-reference library libla_stream.so); returns liblightning's path."""
     hipcc = _hipcc()
     with tempfile.TemporaryDirectory(prefix="la_build_") as tmp:
         objs = [os.path.join(tmp, os.path.splitext(s)[0] + ".o") for s in SOURCES]
@@ -53,6 +59,9 @@ def build(verbose=False):
         tmp_lib = LIB_PATH + ".tmp"
         outs.append(_run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_lib, *objs]))
         os.replace(tmp_lib, LIB_PATH)
+        tmp_stream = STREAM_LIB_PATH + ".tmp"
+        outs.append(_run([hipcc, *HIP_FLAGS, "-shared", os.path.join(CSRC, STREAM_SOURCE), "-o", tmp_stream]))
+        os.replace(tmp_stream, STREAM_LIB_PATH)
     if verbose:
         for o in outs:
             if o.strip():

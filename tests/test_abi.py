@@ -22,8 +22,8 @@ GB = 1 << 40
 Q, K, V, O, S_IN, S_OUT, WS, DO, DQ, DK, DV, DS = (ctypes.c_void_p(GB * i) for i in range(1, 13))
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(la_[a-z_]+)\s*\(", text)))
 
@@ -233,3 +233,28 @@ def test_noalloc_rejects_before_touching_the_device(lib):
     assert lib.la_forward_workspace_bytes(1100, 8, 1, 64, 128, 128, 64, BF16) == 1100 * 128 * 128 * 4
     # the 1M-token, 128/32-head workload fits (planned here for 256 compute units)
     assert lib.la_forward_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, 64, BF16) == (32 * 7 * 3 + 32 * 8) * 65536
+
+
+def test_stream_library_exports_its_header():
+    """libla_stream.so (the benchmark's HBM streaming references) exports what
+    include/la_stream.h declares and refuses bad arguments without launching."""
+    from long_context_attention_chunkwise_amd import build
+    names = declared_functions(os.path.join(ROOT, "include", "la_stream.h"))
+    assert names == ["la_stream_bytes_moved", "la_stream_run"]
+    slib = ctypes.CDLL(build.STREAM_LIB_PATH)
+    for n in names:
+        assert getattr(slib, n) is not None
+    slib.la_stream_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                   ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    slib.la_stream_bytes_moved.argtypes = [ctypes.c_int, ctypes.c_size_t]
+    slib.la_stream_bytes_moved.restype = ctypes.c_size_t
+    assert slib.la_stream_run(4, 0, Q, K, 1 << 30, S_IN, 256, None) == 1       # no such mode
+    assert slib.la_stream_run(1, 0, Q, None, 1 << 30, S_IN, 256, None) == 1    # copy needs dst
+    assert slib.la_stream_run(0, 0, ctypes.c_void_p(GB + 4), None, 1 << 30, S_IN, 256, None) == 1   # misaligned
+    assert slib.la_stream_bytes_moved(0, 1 << 30) == 1 << 30
+    assert slib.la_stream_bytes_moved(1, 1 << 30) == 2 << 30
+    assert slib.la_stream_bytes_moved(3, 1 << 30) == 2 << 30                 # in place: read + write
+    assert slib.la_stream_bytes_moved(4, 1 << 30) == 0
+    # 3:2 mix: 60 KiB steps, 2/3 of what is read is written
+    steps = (1 << 30) // (256 * 15 * 16)
+    assert slib.la_stream_bytes_moved(2, 1 << 30) == steps * 256 * 15 * 16 + steps * 256 * 10 * 16
