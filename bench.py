@@ -487,13 +487,15 @@ def bench_decode(la, synth, torch, w, steps, warmup, cpu=False):
 # parent reads the child's counter database.
 # ---------------------------------------------------------------------------
 COUNTER_PASSES = (("FETCH_SIZE",), ("WRITE_SIZE",), ("SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"))
-COUNTER_KERNELS = "fwd_bf16_g4|fwd_bf16_main|state_parts|stream_kernel"
+COUNTER_KERNELS = "fwd_bf16_g4|fwd_bf16_main|state_parts|decode_kernel|stream_kernel"
 CALIBRATION_GIB = 4
 
 
 def counter_child(workload):
-    """The program rocprofv3 runs: two forward steps of `workload`, then a
-    copy of CALIBRATION_GIB GiB by the streaming library (known bytes)."""
+    """The program rocprofv3 runs: two forward steps of `workload`, three
+    decode steps of the 256-sequence decode workload (states drawn at random:
+    the traffic does not depend on their values), then a copy of
+    CALIBRATION_GIB GiB by the streaming library (known bytes)."""
     import ctypes
     import torch
     import long_context_attention_chunkwise_amd as la
@@ -506,6 +508,14 @@ def counter_child(workload):
         la.forward(q, k, v, out=o)
     torch.cuda.synchronize()
     del q, k, v, o
+    wd = synth.WORKLOADS["decode_256"]
+    S = synth.random_state((wd.B, wd.Hkv, wd.d, wd.dv), "cuda:0", seed=3)
+    qs, ks, vs = synth.make_decode_steps(wd, "cuda:0", seed=1, steps=3)
+    od = torch.empty((wd.B, wd.Hq, wd.dv), dtype=torch.float32, device="cuda:0")
+    for t in range(3):
+        la.decode_step(S, qs[t], ks[t], vs[t], out=od)
+    torch.cuda.synchronize()
+    del S, qs, ks, vs, od
     torch.cuda.empty_cache()
     lib = ctypes.CDLL(_build.STREAM_LIB_PATH)
     lib.la_stream_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
@@ -536,7 +546,7 @@ def read_counter_db(path):
         db = sqlite3.connect(f)
         for name, disp, dur, cname, val in db.execute(
                 "select name, dispatch_id, duration, counter_name, counter_value from pmc_events"):
-            m = re.search(r"(fwd_bf16_g4|fwd_bf16_main|state_parts|stream_kernel<1)", name)
+            m = re.search(r"(fwd_bf16_g4|fwd_bf16_main|state_parts|decode_kernel|stream_kernel<1)", name)
             if not m:
                 continue
             d = per[m.group(1)][disp]
@@ -614,7 +624,7 @@ def counter_figures(raw, cus, kernel, bytes_alg):
            "fetch_scale": round(rscale, 4), "write_scale": round(wscale, 4)}
     if bytes_alg:
         rec["traffic_over_algorithmic"] = round((fetch + write) / bytes_alg, 4)
-    if "SQ_VALU_MFMA_BUSY_CYCLES" in kr and kr.get("GRBM_GUI_ACTIVE"):
+    if cus and "SQ_VALU_MFMA_BUSY_CYCLES" in kr and kr.get("GRBM_GUI_ACTIVE"):
         cycles = kr["GRBM_GUI_ACTIVE"]
         rec["mfma_busy"] = round(kr["SQ_VALU_MFMA_BUSY_CYCLES"] / (4 * cus * cycles), 4)
         rec["mfma_instructions"] = kr.get("SQ_INSTS_MFMA")
@@ -720,6 +730,12 @@ def main():
             decode["roofline"]["frac_of_practical"] = round(
                 decode["gb_per_s"] / ceilings["in_place_update"]["gb_per_s"], 4)
             decode["roofline"]["practical"] = "in-place update streaming kernel"
+        if counters_raw is not None and "decode_kernel" in counters_raw:
+            dc = counter_figures(counters_raw, 0, "decode_kernel", decode["roofline"]["bytes_per_launch"])
+            if "traffic" in dc:
+                decode["roofline"]["traffic"] = dc["traffic"]
+                decode["roofline"]["traffic_source"] = "counters of this run"
+                decode["roofline"]["traffic_over_algorithmic"] = dc.get("traffic_over_algorithmic")
         log(f"[bench] decode: {decode['ms_per_step']:.4f} ms/step, {decode['gb_per_s']:.0f} GB/s")
 
     counters = None

@@ -17,8 +17,11 @@
 // sequence).  Thread (row group rg, column group
 // cg) owns columns [4cg, 4cg+4) of rows rg, rg + nrg, ...: a wave reads whole
 // 512-byte rows with 16-byte accesses.  Per-thread partial products over its
-// rows are reduced across row groups through LDS in a fixed order, so results
-// are deterministic.
+// rows are reduced in a fixed order, so results are deterministic: at dv = 128
+// first inside each wave (its two row groups, by a lane exchange), then over
+// the eight waves through LDS; at other dv over all row groups through LDS.
+// (Both reductions measured the same, 195.3 and 195.6 us per step on the
+// 256-sequence workload: the step is bound by streaming the states.)
 #include "la_internal.h"
 
 namespace la {
@@ -55,7 +58,11 @@ __device__ __forceinline__ float load_in(const void* p, int64_t i) {
 // G: query heads served by this launch.  CHUNKED: one chunk [h0, h0 + G) of a
 // larger group of Gfull heads (otherwise the whole group, Gfull = G, h0 = 0);
 // UPDATE: add k^T v to the state and write it back (otherwise read only).
-template <int G, bool IN_BF16, bool OUT_F32, bool CHUNKED, bool UPDATE>
+// WRED (wave-level reduction, dv = 128 only: a wave is two row groups of 32
+// column groups): the two row groups of each wave are first added with a
+// cross-half lane exchange, so only the eight waves' partials pass through
+// LDS; otherwise every row group's partial does.
+template <int G, bool IN_BF16, bool OUT_F32, bool CHUNKED, bool UPDATE, bool WRED = false>
 __global__ __launch_bounds__(kThreads) void decode_kernel(float* __restrict__ S, const void* __restrict__ q,
                                                          const void* __restrict__ k, const void* __restrict__ v,
                                                          void* __restrict__ o, int Hkv, int d, int dv, int Gfull,
@@ -63,7 +70,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(float* __restrict__ S,
   __shared__ float qs[G][kMaxD];
   __shared__ float ks[kMaxD];
   __shared__ float vs[kMaxDV];
-  __shared__ float4 red[kThreads * G];  // [row group][head][column group]
+  __shared__ float4 red[(WRED ? kThreads / 2 : kThreads) * G];  // [row group or wave][head][column group]
 
   const int bg = blockIdx.x;  // b * Hkv + g
   const int tid = threadIdx.x;
@@ -105,15 +112,32 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(float* __restrict__ S,
         acc[h].w = fmaf(qr, s.w, acc[h].w);
       }
     }
-    for (int h = 0; h < G; ++h) red[(rg * G + h) * ncg + cg] = acc[h];
+    if constexpr (!WRED)
+      for (int h = 0; h < G; ++h) red[(rg * G + h) * ncg + cg] = acc[h];
+  }
+  if constexpr (WRED) {
+    // lanes i and i + 32 of a wave hold row groups 2w and 2w + 1 of the same
+    // column group: add the upper half into the lower, which publishes the
+    // wave's partial (row groups 2w, 2w + 1 in that order)
+    const int wv = tid >> 6;
+    for (int h = 0; h < G; ++h) {
+      float4 x = acc[h];
+      x.x += __shfl_down(x.x, 32);
+      x.y += __shfl_down(x.y, 32);
+      x.z += __shfl_down(x.z, 32);
+      x.w += __shfl_down(x.w, 32);
+      if ((tid & 63) < 32) red[(wv * G + h) * ncg + cg] = x;
+    }
   }
   __syncthreads();
 
-  // o[h][4c..4c+3] = sum over row groups, in row-group order.
+  // o[h][4c..4c+3] = sum over row groups (or waves), in order.
+  constexpr int kParts = WRED ? kThreads / 64 : 0;
+  const int nparts = WRED ? kParts : nrg;
   for (int e = tid; e < G * ncg; e += kThreads) {
     const int h = e / ncg, c = e % ncg;
     float4 sum = red[h * ncg + c];
-    for (int r = 1; r < nrg; ++r) {
+    for (int r = 1; r < nparts; ++r) {
       const float4 x = red[(r * G + h) * ncg + c];
       sum.x += x.x;
       sum.y += x.y;
@@ -139,15 +163,24 @@ hipError_t launch_g(float* S, const void* q, const void* k, const void* v, void*
                     int64_t B, int64_t Hkv, int64_t d, int64_t dv, int Gfull, int h0, hipStream_t stream) {
   const dim3 grid(unsigned(B * Hkv)), block(kThreads);
   const int iHkv = int(Hkv), id = int(d), idv = int(dv);
-#define LA_DEC(BF, F32)                                                                                          \
-  hipLaunchKernelGGL((decode_kernel<G, BF, F32, CHUNKED, UPDATE>), grid, block, 0, stream, S, q, k, v, o, iHkv, id, \
-                     idv, Gfull, h0)
-  if (in_bf16) {
-    if (out_f32) LA_DEC(true, true);
-    else LA_DEC(true, false);
+  // dv = 128: the wave-level reduction (each wave is exactly two row groups)
+#define LA_DEC(BF, F32, WR)                                                                                       \
+  hipLaunchKernelGGL((decode_kernel<G, BF, F32, CHUNKED, UPDATE, WR>), grid, block, 0, stream, S, q, k, v, o, iHkv, \
+                     id, idv, Gfull, h0)
+  if (dv == kMaxDV) {
+    if (in_bf16) {
+      if (out_f32) LA_DEC(true, true, true);
+      else LA_DEC(true, false, true);
+    } else {
+      if (out_f32) LA_DEC(false, true, true);
+      else LA_DEC(false, false, true);
+    }
+  } else if (in_bf16) {
+    if (out_f32) LA_DEC(true, true, false);
+    else LA_DEC(true, false, false);
   } else {
-    if (out_f32) LA_DEC(false, true);
-    else LA_DEC(false, false);
+    if (out_f32) LA_DEC(false, true, false);
+    else LA_DEC(false, false, false);
   }
 #undef LA_DEC
   return hipGetLastError();
