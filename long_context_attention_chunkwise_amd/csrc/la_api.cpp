@@ -75,23 +75,29 @@ la_status check_forward_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int
 
 namespace la {
 
-Bf16Plan plan_bf16(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv, int cus) {
+Bf16Plan plan_bf16(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv, int cus,
+                   bool allow_solo) {
   Bf16Plan p;
   const int64_t G = Hq / Hkv;
   p.hd = static_cast<int>(d);
   (void)dv;  // d = dv on the matrix-core path
   p.gw = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
   p.subgroups = static_cast<int>(G / p.gw);
+  // head size 64 with one query head per KV head: one-wave workgroups, four
+  // per compute unit (one per SIMD)
+  p.solo = allow_solo && d == 64 && G == 1;
   p.nblocks = (N + kBf16Block - 1) / kBf16Block;
   if (p.nblocks == 0) return p;
 
   const int64_t kv_chains = B * Hkv;
   const int64_t main_chains = kv_chains * p.subgroups;
-  // Enough segments for one workgroup per compute unit, each at least
-  // kMinBlocks long so the pre-pass stays a small fraction of the traffic.
+  // Enough segments for one workgroup per compute unit (four one-wave ones),
+  // each at least kMinBlocks long so the pre-pass stays a small fraction of
+  // the traffic.
   constexpr int64_t kMinBlocks = 4;
+  const int64_t slots = p.solo ? 4 * int64_t(cus) : int64_t(cus);
   int64_t P = 1;
-  if (main_chains < cus) P = (cus + main_chains - 1) / main_chains;
+  if (main_chains < slots) P = (slots + main_chains - 1) / main_chains;
   P = std::min(P, std::max<int64_t>(1, p.nblocks / kMinBlocks));
   p.blocks_per_seg = (p.nblocks + P - 1) / P;
   P = (p.nblocks + p.blocks_per_seg - 1) / p.blocks_per_seg;
@@ -158,7 +164,7 @@ VarPlan plan_variant(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, i
 BwdPlan plan_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv, int cus) {
   BwdPlan p;
   // dQ is the forward over (dO, V, K): head sizes swap.
-  p.fwd = plan_bf16(B, Hq, Hkv, N, dv, d, cus);
+  p.fwd = plan_bf16(B, Hq, Hkv, N, dv, d, cus, true);
   p.nblocks = (N + kBf16Block - 1) / kBf16Block;
   if (p.nblocks == 0) return p;
 
@@ -235,7 +241,7 @@ size_t la_forward_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
   la_dtype out = in_dtype;
   if (check_forward_shape(B, Hq, Hkv, N, d, dv, block, in_dtype, out) != LA_OK) return 0;
   if (!mfma_path(in_dtype, d, dv, block) || N == 0) return 0;
-  return la::plan_bf16(B, Hq, Hkv, N, d, dv, device_cus()).workspace_bytes;
+  return la::plan_bf16(B, Hq, Hkv, N, d, dv, device_cus(), true).workspace_bytes;
 }
 
 }  // extern "C"
@@ -282,7 +288,7 @@ la_status validate_forward(ForwardCall& fc, const void* q, const void* k, const 
     return LA_ERR_ALIAS;
 
   if (!fc.scalar && N > 0) {
-    fc.plan = la::plan_bf16(B, Hq, Hkv, N, d, dv, device_cus());
+    fc.plan = la::plan_bf16(B, Hq, Hkv, N, d, dv, device_cus(), true);
     const size_t nw = fc.plan.workspace_bytes;
     if (nw > 0 && check_workspace) {
       if (workspace == nullptr || workspace_bytes < nw) return LA_ERR_WORKSPACE;
@@ -383,7 +389,7 @@ la_status la_forward(const void* q, const void* k, const void* v, void* o, int64
   if (st != LA_OK) return st;
   size_t ws = 0;
   if (mfma_path(in_dtype, d, dv, block) && N > 0)
-    ws = la::plan_bf16(B, Hq, Hkv, N, d, dv, device_cus()).workspace_bytes;
+    ws = la::plan_bf16(B, Hq, Hkv, N, d, dv, device_cus(), true).workspace_bytes;
   if (ws == 0)
     return la_forward_ex(q, k, v, o, B, Hq, Hkv, N, d, dv, block, in_dtype, out_dtype, nullptr, nullptr,
                          nullptr, 0, stream);

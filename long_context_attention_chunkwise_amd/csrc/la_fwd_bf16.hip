@@ -604,6 +604,156 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
         for (int i = 0; i < 4; ++i) z_out[int64_t(bg) * HD + WC * w + 16 * jj + 4 * grp + i] = zacc[jj][i];
 }
 
+// ---------------------------------------------------------------------------
+// One-wave workgroups for one query head per KV head at head size 64 (d = dv
+// = 64, Hq = Hkv).  With a single query head, the four-wave kernel keeps three
+// waves idle; here each wave is a workgroup of its own that owns one (batch,
+// head, segment): the head's whole 64 x 64 float32 state in VGPRs (16
+// accumulator tiles), its own K/V tiles and bf16 state copy in LDS (30 KiB),
+// so no wave ever waits for another, and four of them share a compute unit
+// (the host plans four segments per unit: 32 per chain for 32 heads).  The
+// block step is the four-wave kernel's with the wave owning every state
+// column: scores P^T = K Q^T, outputs O^T = S^T Q^T + V^T P^T in two 32-column
+// quarters, then S += K^T V and its bf16 copy.
+// ---------------------------------------------------------------------------
+template <bool OUT_F32>
+__global__ __launch_bounds__(64, 1) void fwd_bf16_solo(const uint16_t* __restrict__ q,
+                                                       const uint16_t* __restrict__ k,
+                                                       const uint16_t* __restrict__ v, void* __restrict__ o,
+                                                       const float* starts, const float* s_in, float* s_out,
+                                                       int64_t N, int64_t nblocks, int64_t blocks_per_seg, int P) {
+  constexpr int HD = 64, NDS = HD / 32, NDT = HD / 16, NM = HD / 32, NJ = HD / 16;
+  constexpr int RKV = HD + 16, RST = HD + 8, CPR = HD / 8, RPI = 64 / CPR, NLD = C / RPI;
+  __shared__ __align__(16) uint16_t ks[C * RKV];
+  __shared__ __align__(16) uint16_t vs[C * RKV];
+  __shared__ __align__(16) uint16_t st[HD * RST];
+
+  const int lane = threadIdx.x, l16 = lane & 15, grp = lane >> 4;
+  const int seg = blockIdx.x % P;
+  const int64_t bh = blockIdx.x / P;  // b * H + h: query head h reads KV head h
+  const int64_t blk0 = int64_t(seg) * blocks_per_seg;
+  const int64_t blk1 = blk0 + blocks_per_seg < nblocks ? blk0 + blocks_per_seg : nblocks;
+  const uint16_t* qh = q + bh * N * HD;
+  const uint16_t* kh = k + bh * N * HD;
+  const uint16_t* vh = v + bh * N * HD;
+  const int nlane = 8 * (l16 >> 2) + (l16 & 3);
+
+  // state tile (jn, dt): rows 16 dt + 4 grp + i, column 16 jn + l16
+  const float* s0 = starts ? starts + (bh * P + seg) * (HD * HD) : (s_in ? s_in + bh * (HD * HD) : nullptr);
+  floatx4 sacc[NJ][NDT];
+  for (int jn = 0; jn < NJ; ++jn)
+    for (int dt = 0; dt < NDT; ++dt)
+      for (int i = 0; i < 4; ++i) sacc[jn][dt][i] = s0 ? s0[(16 * dt + 4 * grp + i) * HD + 16 * jn + l16] : 0.0f;
+  for (int jn = 0; jn < NJ; ++jn)
+    for (int dt = 0; dt < NDT; ++dt)
+      *reinterpret_cast<bf16x4*>(&st[(16 * jn + l16) * RST + 16 * dt + 4 * grp]) = to_bf16x4(sacc[jn][dt]);
+
+  // one block's K and V: lane moves chunk lane % CPR of rows lane / CPR + RPI i
+  uint4 kr[NLD], vr[NLD];
+  bf16x8 qa[4][NDS];
+  auto load_block = [&](int64_t blk) {
+    const int c = lane % CPR;
+    for (int i = 0; i < NLD; ++i) {
+      const int64_t t = blk * C + lane / CPR + RPI * i;
+      if (t < N) {
+        kr[i] = ld_stream16(kh + t * HD + 8 * c);
+        vr[i] = ld_stream16(vh + t * HD + 8 * c);
+      } else {
+        kr[i] = make_uint4(0, 0, 0, 0);
+        vr[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    for (int ti = 0; ti < 4; ++ti) {
+      const int64_t t = blk * C + 16 * ti + l16;
+      for (int ds = 0; ds < NDS; ++ds)
+        qa[ti][ds] = (t < N) ? ld_global16(qh + t * HD + 32 * ds + 8 * grp) : zero_bf16x8();
+    }
+  };
+  if (blk0 < blk1) load_block(blk0);
+  for (int64_t blk = blk0; blk < blk1; ++blk) {
+    {
+      const int c = lane % CPR;
+      for (int i = 0; i < NLD; ++i) {
+        const int row = lane / CPR + RPI * i;
+        *reinterpret_cast<uint4*>(ks + row * RKV + 8 * c) = kr[i];
+        *reinterpret_cast<uint4*>(vs + row * RKV + 8 * c) = vr[i];
+      }
+    }
+    __syncthreads();  // (one wave: orders the tile stores before the reads below)
+
+    const floatx4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    bf16x8 pop[4][2];
+    for (int ti = 0; ti < 4; ++ti) {
+      floatx4 pt[4];
+      for (int si = 0; si <= ti; ++si) {
+        pt[si] = z4;
+        for (int ds = 0; ds < NDS; ++ds)
+          pt[si] = mfma(ld_lds16(ks + (16 * si + l16) * RKV + 32 * ds + 8 * grp), qa[ti][ds], pt[si]);
+      }
+      pt[ti] = causal_mask(pt[ti], l16, grp);
+      pop[ti][0] = pack_tiles(pt[0], ti >= 1 ? pt[1] : z4);
+      if (ti >= 2) pop[ti][1] = pack_tiles(pt[2], ti == 3 ? pt[3] : z4);
+    }
+    for (int m = 0; m < NM; ++m) {
+      floatx4 acc[2][4];
+      for (int h2 = 0; h2 < 2; ++h2)
+        for (int ti = 0; ti < 4; ++ti) acc[h2][ti] = z4;
+      // inter: O^T[n][t] = sum_d S[d][n] Q[t][d] (state before the block)
+      for (int ds = 0; ds < NDS; ++ds)
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const bf16x8 sa = ld_lds16(st + (32 * m + 4 * h2 + nlane) * RST + 32 * ds + 8 * grp);
+          for (int ti = 0; ti < 4; ++ti) acc[h2][ti] = mfma(sa, qa[ti][ds], acc[h2][ti]);
+        }
+      // intra: O^T[n][t] += sum_s V[s][n] P^T[s][t]
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const bf16x8 va0 = tr_operand(vs, 0, 32 * m + 4 * h2, l16, grp, 8, RKV);
+        const bf16x8 va1 = tr_operand(vs, 1, 32 * m + 4 * h2, l16, grp, 8, RKV);
+        for (int ti = 0; ti < 4; ++ti) acc[h2][ti] = mfma(va0, pop[ti][0], acc[h2][ti]);
+        acc[h2][2] = mfma(va1, pop[2][1], acc[h2][2]);
+        acc[h2][3] = mfma(va1, pop[3][1], acc[h2][3]);
+      }
+      for (int ti = 0; ti < 4; ++ti) {
+        const int64_t t = blk * C + 16 * ti + l16;
+        if (t < N) {
+          const int64_t off = (bh * N + t) * HD + 32 * m + 8 * grp;
+          if (OUT_F32) {
+            float* op = static_cast<float*>(o) + off;
+            *reinterpret_cast<floatx4*>(op) = acc[0][ti];
+            *reinterpret_cast<floatx4*>(op + 4) = acc[1][ti];
+          } else {
+            *reinterpret_cast<bf16x8*>(static_cast<uint16_t*>(o) + off) = pack_tiles(acc[0][ti], acc[1][ti]);
+          }
+        }
+      }
+    }
+    // the next block's loads go out once this block's Q operands are dead
+    if (blk + 1 < blk1) load_block(blk + 1);
+
+    // state update: S += K_b^T V_b (every column), then its bf16 copy
+    {
+      bf16x8 vb[NJ][2];
+      for (int jn = 0; jn < NJ; ++jn)
+        for (int p = 0; p < 2; ++p) vb[jn][p] = tr_operand(vs, p, 16 * jn, l16, grp, 4, RKV);
+      for (int dt = 0; dt < NDT; ++dt)
+        for (int p = 0; p < 2; ++p) {
+          const bf16x8 kt = tr_operand(ks, p, 16 * dt, l16, grp, 4, RKV);
+          for (int jn = 0; jn < NJ; ++jn) sacc[jn][dt] = mfma(kt, vb[jn][p], sacc[jn][dt]);
+        }
+      for (int jn = 0; jn < NJ; ++jn)
+        for (int dt = 0; dt < NDT; ++dt)
+          *reinterpret_cast<bf16x4*>(&st[(16 * jn + l16) * RST + 16 * dt + 4 * grp]) = to_bf16x4(sacc[jn][dt]);
+    }
+    __syncthreads();  // (one wave: the tile reads above precede the next block's stores)
+  }
+
+  if (s_out != nullptr && seg == P - 1) {
+    float* so = s_out + bh * (HD * HD);
+    for (int jn = 0; jn < NJ; ++jn)
+      for (int dt = 0; dt < NDT; ++dt)
+        for (int i = 0; i < 4; ++i) so[(16 * dt + 4 * grp + i) * HD + 16 * jn + l16] = sacc[jn][dt][i];
+  }
+}
+
 // Pre-pass: partial[c][j][r] = sum of K_b^T V_b over part r of segment
 // j + seg_offset of chain c, for j < P - 1 (the forward sums every segment but
 // the last with seg_offset 0; the backward every segment but the first with
@@ -1044,7 +1194,20 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
 #define LA_MAIN(GW, F32)                                                                                      \
   launch_main<GW, F32>(grid, stream, q, k, v, o, starts, plan.use_starts ? nullptr : s_in, s_out, iHq, iHkv, \
                        plan.subgroups, N, plan.nblocks, plan.blocks_per_seg, plan.P)
-  if (plan.hd == 64) {
+  if (plan.solo) {
+    // head size 64, one query head per KV head: one-wave workgroups
+    if (plan.hd != 64) return hipErrorInvalidValue;
+    const auto* q16 = static_cast<const uint16_t*>(q);
+    const auto* k16 = static_cast<const uint16_t*>(k);
+    const auto* v16 = static_cast<const uint16_t*>(v);
+    const float* si = plan.use_starts ? nullptr : s_in;
+    if (out_f32)
+      hipLaunchKernelGGL((fwd_bf16_solo<true>), grid, dim3(64), 0, stream, q16, k16, v16, o, starts, si, s_out, N,
+                         plan.nblocks, plan.blocks_per_seg, plan.P);
+    else
+      hipLaunchKernelGGL((fwd_bf16_solo<false>), grid, dim3(64), 0, stream, q16, k16, v16, o, starts, si, s_out, N,
+                         plan.nblocks, plan.blocks_per_seg, plan.P);
+  } else if (plan.hd == 64) {
     // head size 64: the four-wave kernel, with gw = 1 or 2 query heads per
     // workgroup (idle waves) for groups that are not a multiple of four
     const float* si = plan.use_starts ? nullptr : s_in;

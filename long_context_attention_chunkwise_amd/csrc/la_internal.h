@@ -22,6 +22,7 @@ struct Bf16Plan {
   int64_t nblocks = 0;          // ceil(N / 64)
   int hd = 128;                 // head size d = dv (128; 64 for groups of four query heads)
   int gw = 4;                   // query heads per workgroup (1, 2 or 4)
+  bool solo = false;            // one-wave workgroups (head size 64, one query head per KV head)
   int subgroups = 1;            // (Hq / Hkv) / gw workgroups per KV head and segment
   int P = 1;                    // segments per chain
   int R = 1;                    // pre-pass parts per segment
@@ -33,7 +34,11 @@ struct Bf16Plan {
   size_t workspace_bytes = 0;
 };
 
-Bf16Plan plan_bf16(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv, int cus);
+// allow_solo: the caller runs the output kernels of launch_fwd_bf16 (the
+// forward, the backward's dQ pass), which include the one-wave kernel for head
+// size 64 with one query head per KV head; the variants plan without it.
+Bf16Plan plan_bf16(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv, int cus,
+                   bool allow_solo = false);
 
 // Scalar (float32 FMA) forward: q, k, v stored as float32 or bf16 (in_bf16),
 // o as float32 or bf16 (out_bf16); d up to 128, dv a multiple of 32 up to

@@ -69,14 +69,15 @@ def test_backward_matches_oracle(B, Hq, Hkv, N, grad_dtype, s_in, ds_out):
     (1, 4, 1, 1, torch.float32, True, True),          # one token
     (1, 8, 1, 4100, BF16, False, True),               # G = 8
     (1, 16, 4, 20000, BF16, True, True),              # G = 4, four chains of many segments
-    (2, 4, 4, 3000, torch.float32, True, True),       # G = 1
+    (2, 4, 4, 3000, torch.float32, True, True),       # G = 1 (dQ on one-wave workgroups)
+    (1, 2, 2, 70, BF16, True, True),                  # G = 1, two blocks
     (1, 6, 3, 777, BF16, False, True),                # G = 2
     (1, 3, 1, 1000, torch.float32, True, False),      # G = 3
 ])
 def test_backward_head_size_64(B, Hq, Hkv, N, grad_dtype, s_in, ds_out):
-    """d = dv = 64, any group size: dQ on the four-wave forward kernel (one,
-    two or four query heads per workgroup), dK/dV on the four-wave reverse
-    kernel."""
+    """d = dv = 64, any group size: dQ on the forward kernels (four-wave
+    workgroups of one, two or four query heads, one-wave workgroups for one
+    query head per KV head), dK/dV on the four-wave reverse kernel."""
     need_gpu()
     say(f"case backward d=64 B={B} Hq={Hq} Hkv={Hkv} N={N} grad={grad_dtype} s_in={s_in} ds_out={ds_out}")
     q, k, v, do = inputs(B, Hq, Hkv, N, seed=N + Hq + 64, d=64)

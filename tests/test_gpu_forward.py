@@ -166,15 +166,19 @@ def test_bf16_in_place_rejected_off_the_four_head_kernel():
     (2, 16, 2, 777, torch.float32, False),    # G = 8: two query-head subgroups
     (1, 4, 1, 64, torch.bfloat16, False),     # one block
     (1, 4, 1, 20000, torch.float32, True),    # many segments on one chain
-    (2, 4, 4, 3001, torch.bfloat16, True),    # G = 1: one query head per workgroup, three waves idle
+    (2, 4, 4, 3001, torch.bfloat16, True),    # G = 1: one-wave workgroups, several segments per head
     (1, 8, 4, 777, torch.float32, False),     # G = 2
     (1, 6, 2, 2000, torch.bfloat16, True),    # G = 3: one query head per workgroup, three subgroups
-    (1, 1, 1, 20000, torch.float32, True),    # a single head, many segments
+    (1, 1, 1, 20000, torch.float32, True),    # a single head, many segments (one-wave workgroups)
+    (1, 2, 2, 64, torch.float32, True),       # G = 1, one block
+    (3, 3, 3, 1, torch.bfloat16, True),       # G = 1, one token
+    (1, 32, 32, 5000, torch.bfloat16, False), # G = 1, 32 heads: more heads than one workgroup per SIMD
     (1, 12, 2, 1500, torch.bfloat16, True),   # G = 6: two query heads per workgroup, three subgroups
 ])
 def test_bf16_head_size_64(B, Hq, Hkv, N, out_dtype, s_in):
-    """Head size 64 on the four-wave matrix-core kernel (four query heads per
-    workgroup, or one or two with the other waves idle) and its pre-pass."""
+    """Head size 64 on the matrix cores: the four-wave kernel (four query heads
+    per workgroup, or two with the other waves idle), one-wave workgroups for
+    one query head per KV head, and their pre-pass."""
     need_gpu()
     if N > 64:
         assert la.workspace_bytes(B, Hq, Hkv, N, 64, 64, 64, torch.bfloat16) > 0   # the matrix-core split
@@ -200,6 +204,24 @@ def test_bf16_head_size_64_in_place_and_resume():
     check_close("resumed o (second chunk in place)", f64(torch.cat([o1, o2], dim=2)), ref_o, torch.bfloat16,
                 torch.bfloat16)
     check_state("resumed state (in place)", f64(S1), ref_S, torch.bfloat16)
+
+
+def test_bf16_head_size_64_one_head_per_kv_head_in_place_state_and_resume():
+    """Head size 64, one query head per KV head (one-wave workgroups): a
+    9000-token sequence resumed after 2000 tokens with the state carried in
+    place (s_out = s_in), against the oracle, and the single pass."""
+    need_gpu()
+    q, k, v = qkv(2, 3, 3, 9000, 64, 64, torch.bfloat16, seed=91)
+    sl = lambda t, a, b: t[:, :, a:b].contiguous()
+    o_full, S_full = la.forward(q, k, v, return_state=True)
+    o1, S = la.forward(sl(q, 0, 2000), sl(k, 0, 2000), sl(v, 0, 2000), return_state=True)
+    o2 = la.forward(sl(q, 2000, 9000), sl(k, 2000, 9000), sl(v, 2000, 9000), s_in=S, s_out=S)
+    torch.cuda.synchronize()
+    ref_o, ref_S = oracle.chunkwise(f64(q), f64(k), f64(v), 64)
+    check_close("single pass", f64(o_full), ref_o, torch.bfloat16, torch.bfloat16)
+    check_state("single pass state", f64(S_full), ref_S, torch.bfloat16)
+    check_close("resumed", f64(torch.cat([o1, o2], dim=2)), ref_o, torch.bfloat16, torch.bfloat16)
+    check_state("resumed state (in place)", f64(S), ref_S, torch.bfloat16)
 
 
 def test_empty_sequence_state_passthrough():

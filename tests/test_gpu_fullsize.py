@@ -43,7 +43,7 @@ def test_gqa_64k_groups_and_states():
 @pytest.mark.parametrize("workload", ["gqa_1m", "gqa_1m_d64", "mha_1m_d64"])
 def test_gqa_1m_slices_and_states(workload):
     """B=1, 128/32 heads, N=1,048,576, head sizes 128 and 64 (and 32/32 heads
-    at 64: one query head per four-wave workgroup), through
+    at 64: one-wave workgroups, 32 segments per head), through
     la_forward_states + la_forward_outputs (the benchmark's step): KV groups
     0, 13 and 31 on the first and last 65,536 tokens and on 8192-token windows
     across the boundaries of segments 0/1 and 3/4; the final state of every
@@ -79,7 +79,9 @@ def test_gqa_1m_slices_and_states(workload):
     torch.cuda.synchronize()
     assert bool(torch.isfinite(o).all())
     W = 65536
-    nseg, nparts = 8, 3   # 8 segments per chain at 1M tokens (both head sizes), 7 summed in 3 parts each
+    # segments per chain at 1M tokens on 256 compute units, and pre-pass parts per summed segment:
+    # 8 in 3 parts (four-wave workgroups), 32 in 1 part (one-wave workgroups: head size 64, Hq = Hkv)
+    nseg, nparts = (32, 1) if (w.d == 64 and w.Hq == w.Hkv) else (8, 3)
     seg = w.N // nseg
     assert ws_bytes == (w.Hkv * (nseg - 1) * nparts + w.Hkv * nseg) * w.d * w.dv * 4
     # segment start states as the pre-pass and scan left them: [Hkv][segment][d][dv] after the partials
