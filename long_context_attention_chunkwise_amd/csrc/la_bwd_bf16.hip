@@ -266,6 +266,321 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel8(
 }
 
 // ---------------------------------------------------------------------------
+// Head size 128, four waves (one per SIMD) per (batch, KV head, segment), each
+// owning one kind of gradient for two key tiles of the block: waves 0 and 1
+// hold dV^T of key tiles {0, 3} and {1, 2}, waves 2 and 3 dK^T of the same
+// pairs.  A wave computes the score tiles of its own keys (X^T = Q K^T for
+// dV, Y^T = dO V^T for dK), which stay in registers as the operands of its
+// intra products: no score tile passes through LDS.  Pairing key tile j with
+// 3 - j evens out the causal work (five query tiles of scores and three query
+// tile pairs of intra products per wave).  The reverse state R (128 x 128,
+// float32) is split into four sets of 16 tiles: the dV waves hold row tiles
+// {0, 1} and {2, 3} (all columns) and update them with the dO^T operands of
+// their intra products; the dK waves hold row tiles 4..7 of column tiles
+// 0..3 and 4..7 and use the Q^T operands of theirs.  Every wave thus does 92
+// matrix products per query head.  Once per block R is rounded into an
+// n-major bf16 LDS copy that every wave reads for its inter terms.
+//
+// Items (a block's K/V pair, then each query head's Q/dO pair) pass through
+// two register slots and three LDS buffers: the block's K/V keeps one, its
+// heads alternate between the other two, so one barrier per item suffices.
+// ---------------------------------------------------------------------------
+constexpr int kThreads4 = 256;
+#ifndef LA_BWD_SLOTS4
+#define LA_BWD_SLOTS4 1
+#endif
+
+struct __align__(16) BwdSmem4 {
+  // Three buffers of one item each (two [64][128] bf16 tiles, row-major).
+  uint16_t t[3][2][C * ROWKV];
+  uint16_t rt[DV * ROWST];  // bf16 copy of R, n-major: rt[n][i]
+};
+
+// Two row-major [64][128] bf16 tiles moved by 256 threads: rows tid/16 + 16i
+// (i < 4), 16-byte chunk tid%16; rows past `rows` re-read the last valid row
+// and are stored to LDS as zeros.
+struct PairRegs4 {
+  u32x4 a[4], b[4];
+};
+
+__device__ __forceinline__ void load_pair4(PairRegs4& r, const uint16_t* ab, const uint16_t* bb, int rows, int tid) {
+  const int c = tid & 15;
+  for (int i = 0; i < 4; ++i) {
+    int row = (tid >> 4) + 16 * i;
+    row = row < rows ? row : rows - 1;
+    r.a[i] = ld_stream_v(ab + row * D + 8 * c);
+    r.b[i] = ld_stream_v(bb + row * DV + 8 * c);
+  }
+}
+
+__device__ __forceinline__ void store_pair4(const PairRegs4& r, uint16_t* as, uint16_t* bs, int rows, int tid) {
+  const int c = tid & 15;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int i = 0; i < 4; ++i) {
+    const int row = (tid >> 4) + 16 * i;
+    *reinterpret_cast<u32x4*>(as + row * ROWKV + 8 * c) = row < rows ? r.a[i] : z;
+    *reinterpret_cast<u32x4*>(bs + row * ROWKV + 8 * c) = row < rows ? r.b[i] : z;
+  }
+}
+
+// Diagonal X^T / Y^T tile (entry i of lane (l16, grp): token 4grp + i, key
+// l16 within the tile): keep token >= key.
+__device__ __forceinline__ floatx4 causal_mask_t(floatx4 x, int l16, int grp) {
+  for (int i = 0; i < 4; ++i)
+    if (4 * grp + i < l16) x[i] = 0.0f;
+  return x;
+}
+
+// Operand with a straight contraction order from a row-major [k][col] LDS
+// tile: lane (l16, grp) gets column col0 + l16 at rows k0 + 8grp + {0..7}
+// (the order of a plain 16-byte row load of the transposed tile).
+__device__ __forceinline__ bf16x8 tr_operand_lin(const uint16_t* tile, int k0, int col0, int l16, int grp,
+                                                 int pitch) {
+  const int r = k0 + 8 * grp + (l16 >> 2);
+  const int c = col0 + 4 * (l16 & 3);
+  const bf16x4 lo = ld_lds_tr(tile + r * pitch + c);
+  const bf16x4 hi = ld_lds_tr(tile + (r + 4) * pitch + c);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+struct BwdArgs4 {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;
+  void* dk;
+  void* dvg;
+  const float* rstarts;
+  float* ds_in;
+  int Hq, Hkv;
+  int64_t N, nblocks, blocks_per_seg;
+  int P;
+};
+
+// Tile m (0..15) of the part of R held by wave (SIDE, PAIR): its row and
+// column tile.
+template <int SIDE, int PAIR>
+__device__ constexpr int r_row(int m) { return SIDE == 0 ? 2 * PAIR + m / 8 : 4 + m / 4; }
+template <int SIDE, int PAIR>
+__device__ constexpr int r_col(int m) { return SIDE == 0 ? m % 8 : 4 * PAIR + m % 4; }
+
+// The whole reverse walk of one wave.  SIDE 0: dV of key tiles PAIR and
+// 3 - PAIR, scores X^T = Q K^T, operands (Q rows, dO^T); SIDE 1: dK of the
+// same keys, scores Y^T = dO V^T, operands (dO rows, Q^T).  Every wave runs
+// the same sequence of barriers.
+template <bool OUT_F32, int SIDE, int PAIR, int NS>
+__device__ __forceinline__ void bwd_kv_wave4(const BwdArgs4& A, BwdSmem4& sm) {
+  constexpr int KA = PAIR, KB = 3 - PAIR;  // key tiles (KA < 2 <= KB)
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+  const int seg = blockIdx.x % A.P;
+  const int bg = blockIdx.x / A.P;
+  const int b = bg / A.Hkv, g = bg % A.Hkv;
+  const int G = A.Hq / A.Hkv;
+  const int64_t N = A.N;
+  const int64_t blk0 = int64_t(seg) * A.blocks_per_seg;
+  const int64_t blk1 = blk0 + A.blocks_per_seg < A.nblocks ? blk0 + A.blocks_per_seg : A.nblocks;
+
+  const uint16_t* kh = A.k + int64_t(bg) * N * D;
+  const uint16_t* vh = A.v + int64_t(bg) * N * DV;
+  const uint16_t* qg = A.q + (int64_t(b) * A.Hq + int64_t(g) * G) * N * D;
+  const uint16_t* og = A.dout + (int64_t(b) * A.Hq + int64_t(g) * G) * N * DV;
+
+  // R tile m: rows 16 r_row(m) + 4grp + i, column 16 r_col(m) + l16
+  const float* r0 = A.rstarts ? A.rstarts + (int64_t(bg) * A.P + seg) * DD : nullptr;
+  floatx4 racc[16];
+#pragma unroll
+  for (int m = 0; m < 16; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      racc[m][i] = r0 ? r0[(16 * r_row<SIDE, PAIR>(m) + 4 * grp + i) * DV + 16 * r_col<SIDE, PAIR>(m) + l16] : 0.0f;
+  auto write_rt = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < 16; ++m)
+      *reinterpret_cast<bf16x4*>(
+          &sm.rt[(16 * r_col<SIDE, PAIR>(m) + l16) * ROWST + 16 * r_row<SIDE, PAIR>(m) + 4 * grp]) =
+          to_bf16x4(racc[m]);
+  };
+  write_rt();
+
+  const int per_blk = G + 1;
+  int64_t ld_blk = blk1 - 1;
+  int ld_r = 0;
+  auto load_next = [&](PairRegs4& r) __attribute__((always_inline)) {
+    const int rows = int(N - ld_blk * C < C ? N - ld_blk * C : C);
+    const uint16_t* a = ld_r == 0 ? kh : qg + int64_t(ld_r - 1) * N * D;
+    const uint16_t* bb = ld_r == 0 ? vh : og + int64_t(ld_r - 1) * N * DV;
+    load_pair4(r, a + ld_blk * C * D, bb + ld_blk * C * DV, rows, tid);
+    if (ld_blk > blk0 || ld_r < G) {
+      if (++ld_r == per_blk) {
+        ld_r = 0;
+        --ld_blk;
+      }
+    }
+  };
+
+  const int64_t nitems = (blk1 - blk0) * per_blk;
+  PairRegs4 slot[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i)
+    if (i < nitems) load_next(slot[i]);
+
+  const floatx4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
+  // acc[0][t] / acc[1][t]: dV^T (SIDE 0) or dK^T (SIDE 1) of key tile KA / KB,
+  // rows 16t + 4grp + i (column of dV or dK), column 16 key + l16 (key)
+  floatx4 acc[2][8];
+  int64_t blk = blk1 - 1;
+  int r_in = 0;
+  // Buffer of the current block's K/V and of the last query-head item.  Each
+  // item goes to the third buffer: the other two may still be read by waves
+  // that have not finished the previous item, and every earlier reader of the
+  // third one has passed the previous item's barrier.
+  int kvb = 0, hlast = 1;
+
+  auto step = [&](PairRegs4& cur) __attribute__((always_inline)) {
+    const int rows = int(N - blk * C < C ? N - blk * C : C);
+    const int nb = 3 - kvb - hlast;
+    store_pair4(cur, sm.t[nb][0], sm.t[nb][1], rows, tid);
+    __syncthreads();  // the item is in LDS
+    load_next(cur);
+    if (r_in == 0) {
+      // a block's K/V: start the gradients with the inter terms
+      //   dV^T[n][s] = sum_i R[i][n] K[s][i],  dK^T[i][s] = sum_n R[i][n] V[s][n]
+      // (R: the bf16 copy of the state after the later blocks)
+      kvb = nb;
+      const uint16_t* kv = sm.t[nb][SIDE] + l16 * ROWKV + 8 * grp;  // K rows (SIDE 0) or V rows
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 ba = ld_lds16(kv + 16 * KA * ROWKV + 32 * kk);
+        const bf16x8 bb = ld_lds16(kv + 16 * KB * ROWKV + 32 * kk);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const bf16x8 r = SIDE == 0 ? ld_lds16(sm.rt + (16 * t + l16) * ROWST + 32 * kk + 8 * grp)
+                                     : tr_operand_lin(sm.rt, 32 * kk, 16 * t, l16, grp, ROWST);
+          acc[0][t] = mfma(r, ba, kk ? acc[0][t] : z4);
+          acc[1][t] = mfma(r, bb, kk ? acc[1][t] : z4);
+        }
+      }
+      r_in = 1;
+      return;
+    }
+    const int h = r_in - 1;
+    hlast = nb;
+    // SIDE 0: score rows from Q, contraction operands from dO; SIDE 1: the reverse
+    const uint16_t* srow = sm.t[nb][SIDE];
+    const uint16_t* scol = sm.t[nb][1 - SIDE];
+    const uint16_t* kv = sm.t[kvb][SIDE] + l16 * ROWKV + 8 * grp;
+
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      // scores of key tiles KA (query tiles 2p, 2p + 1 from KA on) and, for
+      // p = 1, KB: entry i of tile u holds t = 32p + 16u + 4grp + i, key l16
+      floatx4 sa[2] = {z4, z4}, sb[2] = {z4, z4};
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds) {
+        const bf16x8 ba = ld_lds16(kv + 16 * KA * ROWKV + 32 * ds);
+        const bf16x8 bb = p == 1 ? ld_lds16(kv + 16 * KB * ROWKV + 32 * ds) : ba;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int ti = 2 * p + u;
+          if (ti < KA) continue;  // query tile before the key tile: all masked
+          const bf16x8 a = ld_lds16(srow + (16 * ti + l16) * ROWKV + 32 * ds + 8 * grp);
+          sa[u] = mfma(a, ba, sa[u]);
+          if (p == 1 && ti >= KB) sb[u] = mfma(a, bb, sb[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (2 * p + u == KA) sa[u] = causal_mask_t(sa[u], l16, grp);
+        if (2 * p + u == KB) sb[u] = causal_mask_t(sb[u], l16, grp);
+      }
+      const bf16x8 pa = pack_tiles(sa[0], sa[1]);
+      const bf16x8 pb = pack_tiles(sb[0], sb[1]);
+      // intra:  dV^T[n][s] += sum_t dO[t][n] X^T[t][s]  (SIDE 0)
+      //         dK^T[i][s] += sum_t Q[t][i] Y^T[t][s]   (SIDE 1)
+      // and R[i][n] += sum_t Q[t][i] dO[t][n] on this wave's tiles of R
+      if constexpr (SIDE == 0) {
+        bf16x8 qa[2];  // Q^T of row tiles 2 PAIR, 2 PAIR + 1
+#pragma unroll
+        for (int m = 0; m < 2; ++m) qa[m] = tr_operand(srow, p, 16 * (2 * PAIR + m), l16, grp);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const bf16x8 ot = tr_operand(scol, p, 16 * t, l16, grp);  // dO^T, column tile t
+          acc[0][t] = mfma(ot, pa, acc[0][t]);
+          if (p == 1) acc[1][t] = mfma(ot, pb, acc[1][t]);
+#pragma unroll
+          for (int m = 0; m < 2; ++m) racc[8 * m + t] = mfma(qa[m], ot, racc[8 * m + t]);
+        }
+      } else {
+        bf16x8 ob[4];  // dO^T of column tiles 4 PAIR .. 4 PAIR + 3
+#pragma unroll
+        for (int c = 0; c < 4; ++c) ob[c] = tr_operand(srow, p, 16 * (4 * PAIR + c), l16, grp);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const bf16x8 qt = tr_operand(scol, p, 16 * t, l16, grp);  // Q^T, row tile t
+          acc[0][t] = mfma(qt, pa, acc[0][t]);
+          if (p == 1) acc[1][t] = mfma(qt, pb, acc[1][t]);
+          if (t >= 4)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) racc[4 * (t - 4) + c] = mfma(qt, ob[c], racc[4 * (t - 4) + c]);
+        }
+      }
+    }
+
+    if (h == G - 1) {
+      // gradient rows of the block: tile t holds columns 16t + 4grp + {0..3} of a key
+      void* out = SIDE == 0 ? A.dvg : A.dk;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int64_t s = blk * C + 16 * (e ? KB : KA) + l16;
+        if (s < N) {
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            store_row4<OUT_F32>(out, (int64_t(bg) * N + s) * DV + 16 * t + 4 * grp, acc[e][t]);
+        }
+      }
+      write_rt();
+      r_in = 0;
+      --blk;
+    } else {
+      ++r_in;
+    }
+  };
+
+  // Whole rounds of NS items, then the remainder outside the loop: a
+  // conditional step inside the loop would make the compiler assume, at the
+  // loop head, that the newest loads may be those of any slot, and wait for
+  // all loads in flight before each store.
+  int64_t n = 0;
+  for (; n + NS <= nitems; n += NS) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) step(slot[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i)
+    if (n + i < nitems) step(slot[i]);
+
+  if (A.ds_in != nullptr && seg == 0) {
+    float* so = A.ds_in + int64_t(bg) * DD;
+#pragma unroll
+    for (int m = 0; m < 16; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        so[(16 * r_row<SIDE, PAIR>(m) + 4 * grp + i) * DV + 16 * r_col<SIDE, PAIR>(m) + l16] = racc[m][i];
+  }
+}
+
+template <bool OUT_F32, int NS>
+__global__ __launch_bounds__(kThreads4, 1) void bwd_kv_kernel4(BwdArgs4 args) {
+  __shared__ BwdSmem4 sm;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (w == 0) bwd_kv_wave4<OUT_F32, 0, 0, NS>(args, sm);
+  else if (w == 1) bwd_kv_wave4<OUT_F32, 0, 1, NS>(args, sm);
+  else if (w == 2) bwd_kv_wave4<OUT_F32, 1, 0, NS>(args, sm);
+  else bwd_kv_wave4<OUT_F32, 1, 1, NS>(args, sm);
+}
+
+// ---------------------------------------------------------------------------
 // Head size 64 (d = dv = 64): the same reverse recurrence with four waves, one
 // per SIMD.  Wave w owns columns [16w, 16w+16) of dV, dK and R and computes
 // both score tiles of key tile w for all four query tiles, X^T = Q K^T and
@@ -561,12 +876,21 @@ hipError_t launch_bwd_kv(const void* q, const void* k, const void* v, const void
                          ds_in, int(Hq), int(Hkv), N, plan.nblocks, plan.blocks_per_seg, plan.P);
     return hipGetLastError();
   }
+#ifdef LA_BWD_EIGHT_WAVES
   if (out_f32)
     hipLaunchKernelGGL((bwd_kv_kernel8<true, kSlots>), grid, dim3(kThreads), 0, stream, q16, k16, v16, o16, dk, dvg,
                        rs, ds_in, int(Hq), int(Hkv), N, plan.nblocks, plan.blocks_per_seg, plan.P);
   else
     hipLaunchKernelGGL((bwd_kv_kernel8<false, kSlots>), grid, dim3(kThreads), 0, stream, q16, k16, v16, o16, dk, dvg,
                        rs, ds_in, int(Hq), int(Hkv), N, plan.nblocks, plan.blocks_per_seg, plan.P);
+#else
+  const BwdArgs4 args{q16, k16, v16, o16, dk, dvg, rs, ds_in, int(Hq), int(Hkv), N, plan.nblocks,
+                      plan.blocks_per_seg, plan.P};
+  if (out_f32)
+    hipLaunchKernelGGL((bwd_kv_kernel4<true, LA_BWD_SLOTS4>), grid, dim3(kThreads4), 0, stream, args);
+  else
+    hipLaunchKernelGGL((bwd_kv_kernel4<false, LA_BWD_SLOTS4>), grid, dim3(kThreads4), 0, stream, args);
+#endif
   return hipGetLastError();
 }
 
