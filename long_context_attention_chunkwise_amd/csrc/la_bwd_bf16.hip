@@ -287,7 +287,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel8(
 // ---------------------------------------------------------------------------
 constexpr int kThreads4 = 256;
 #ifndef LA_BWD_SLOTS4
-#define LA_BWD_SLOTS4 1
+#define LA_BWD_SLOTS4 2
+#endif
+#ifndef LA_BWD_FOUR_WAVES
+#define LA_BWD_HELPER
 #endif
 
 struct __align__(16) BwdSmem4 {
@@ -567,6 +570,236 @@ __device__ __forceinline__ void bwd_kv_wave4(const BwdArgs4& A, BwdSmem4& sm) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         so[(16 * r_row<SIDE, PAIR>(m) + 4 * grp + i) * DV + 16 * r_col<SIDE, PAIR>(m) + l16] = racc[m][i];
+  }
+}
+
+// Eight-wave form of the same split: on SIMD s, wave s holds the gradient
+// (dV or dK of two key tiles: scores, intra and inter products) and wave
+// s + 4 that SIMD's 16 tiles of R (their update and the bf16 copy), so one
+// wave's LDS waits overlap the other's matrix products.  256 registers per
+// wave; items move through 512 threads.
+template <bool OUT_F32, int SIDE, int PAIR, bool HELPER, int NS>
+__device__ __forceinline__ void bwd_kv_wave8h(const BwdArgs4& A, BwdSmem4& sm) {
+  constexpr int KA = PAIR, KB = 3 - PAIR;  // key tiles (KA < 2 <= KB)
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+  const int seg = blockIdx.x % A.P;
+  const int bg = blockIdx.x / A.P;
+  const int b = bg / A.Hkv, g = bg % A.Hkv;
+  const int G = A.Hq / A.Hkv;
+  const int64_t N = A.N;
+  const int64_t blk0 = int64_t(seg) * A.blocks_per_seg;
+  const int64_t blk1 = blk0 + A.blocks_per_seg < A.nblocks ? blk0 + A.blocks_per_seg : A.nblocks;
+
+  const uint16_t* kh = A.k + int64_t(bg) * N * D;
+  const uint16_t* vh = A.v + int64_t(bg) * N * DV;
+  const uint16_t* qg = A.q + (int64_t(b) * A.Hq + int64_t(g) * G) * N * D;
+  const uint16_t* og = A.dout + (int64_t(b) * A.Hq + int64_t(g) * G) * N * DV;
+
+  // helper: R tile m holds rows 16 r_row(m) + 4grp + i, column 16 r_col(m) + l16
+  constexpr int NR = HELPER ? 16 : 1;
+  floatx4 racc[NR];
+  auto write_rt = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < NR; ++m)
+      *reinterpret_cast<bf16x4*>(
+          &sm.rt[(16 * r_col<SIDE, PAIR>(m) + l16) * ROWST + 16 * r_row<SIDE, PAIR>(m) + 4 * grp]) =
+          to_bf16x4(racc[m]);
+  };
+  if constexpr (HELPER) {
+    const float* r0 = A.rstarts ? A.rstarts + (int64_t(bg) * A.P + seg) * DD : nullptr;
+#pragma unroll
+    for (int m = 0; m < NR; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        racc[m][i] = r0 ? r0[(16 * r_row<SIDE, PAIR>(m) + 4 * grp + i) * DV + 16 * r_col<SIDE, PAIR>(m) + l16] : 0.0f;
+    write_rt();
+  }
+
+  const int per_blk = G + 1;
+  int64_t ld_blk = blk1 - 1;
+  int ld_r = 0;
+  auto load_next = [&](PairRegs8& r) __attribute__((always_inline)) {
+    const int rows = int(N - ld_blk * C < C ? N - ld_blk * C : C);
+    const uint16_t* a = ld_r == 0 ? kh : qg + int64_t(ld_r - 1) * N * D;
+    const uint16_t* bb = ld_r == 0 ? vh : og + int64_t(ld_r - 1) * N * DV;
+    load_pair8(r, a + ld_blk * C * D, bb + ld_blk * C * DV, rows, tid);
+    if (ld_blk > blk0 || ld_r < G) {
+      if (++ld_r == per_blk) {
+        ld_r = 0;
+        --ld_blk;
+      }
+    }
+  };
+
+  const int64_t nitems = (blk1 - blk0) * per_blk;
+  PairRegs8 slot[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i)
+    if (i < nitems) load_next(slot[i]);
+
+  const floatx4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
+  // gradient wave: acc[0][t] / acc[1][t] = dV^T (SIDE 0) or dK^T (SIDE 1) of
+  // key tile KA / KB, rows 16t + 4grp + i, column 16 key + l16
+  constexpr int NA = HELPER ? 1 : 8;
+  floatx4 acc[2][NA];
+  int64_t blk = blk1 - 1;
+  int r_in = 0;
+  int kvb = 0, hlast = 1;  // as in bwd_kv_wave4
+
+  auto step = [&](PairRegs8& cur) __attribute__((always_inline)) {
+    const int rows = int(N - blk * C < C ? N - blk * C : C);
+    const int nb = 3 - kvb - hlast;
+    store_pair8(cur, sm.t[nb][0], sm.t[nb][1], rows, tid);
+    __syncthreads();  // the item is in LDS
+    load_next(cur);
+    if (r_in == 0) {
+      kvb = nb;
+      if constexpr (!HELPER) {
+        // inter terms from the bf16 copy of R (the state after the later blocks)
+        const uint16_t* kv = sm.t[nb][SIDE] + l16 * ROWKV + 8 * grp;  // K rows (SIDE 0) or V rows
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const bf16x8 ba = ld_lds16(kv + 16 * KA * ROWKV + 32 * kk);
+          const bf16x8 bb = ld_lds16(kv + 16 * KB * ROWKV + 32 * kk);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const bf16x8 r = SIDE == 0 ? ld_lds16(sm.rt + (16 * t + l16) * ROWST + 32 * kk + 8 * grp)
+                                       : tr_operand_lin(sm.rt, 32 * kk, 16 * t, l16, grp, ROWST);
+            acc[0][t] = mfma(r, ba, kk ? acc[0][t] : z4);
+            acc[1][t] = mfma(r, bb, kk ? acc[1][t] : z4);
+          }
+        }
+      }
+      r_in = 1;
+      return;
+    }
+    const int h = r_in - 1;
+    hlast = nb;
+    const uint16_t* sq = sm.t[nb][0];
+    const uint16_t* so = sm.t[nb][1];
+
+    if constexpr (HELPER) {
+      // R[i][n] += sum_t Q[t][i] dO[t][n] on this SIMD's 16 tiles
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        if constexpr (SIDE == 0) {
+          bf16x8 qa[2];  // Q^T of row tiles 2 PAIR, 2 PAIR + 1
+#pragma unroll
+          for (int m = 0; m < 2; ++m) qa[m] = tr_operand(sq, p, 16 * (2 * PAIR + m), l16, grp);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const bf16x8 ot = tr_operand(so, p, 16 * t, l16, grp);
+#pragma unroll
+            for (int m = 0; m < 2; ++m) racc[8 * m + t] = mfma(qa[m], ot, racc[8 * m + t]);
+          }
+        } else {
+          bf16x8 ob[4];  // dO^T of column tiles 4 PAIR .. 4 PAIR + 3
+#pragma unroll
+          for (int c = 0; c < 4; ++c) ob[c] = tr_operand(so, p, 16 * (4 * PAIR + c), l16, grp);
+#pragma unroll
+          for (int t = 4; t < 8; ++t) {
+            const bf16x8 qt = tr_operand(sq, p, 16 * t, l16, grp);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) racc[4 * (t - 4) + c] = mfma(qt, ob[c], racc[4 * (t - 4) + c]);
+          }
+        }
+      }
+      if (h == G - 1) {
+        write_rt();
+        r_in = 0;
+        --blk;
+      } else {
+        ++r_in;
+      }
+      return;
+    } else {
+      const uint16_t* srow = sm.t[nb][SIDE];      // score rows: Q (SIDE 0) or dO
+      const uint16_t* scol = sm.t[nb][1 - SIDE];  // contraction operands: dO (SIDE 0) or Q
+      const uint16_t* kv = sm.t[kvb][SIDE] + l16 * ROWKV + 8 * grp;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        floatx4 sa[2] = {z4, z4}, sb[2] = {z4, z4};
+#pragma unroll
+        for (int ds = 0; ds < 4; ++ds) {
+          const bf16x8 ba = ld_lds16(kv + 16 * KA * ROWKV + 32 * ds);
+          const bf16x8 bb = p == 1 ? ld_lds16(kv + 16 * KB * ROWKV + 32 * ds) : ba;
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int ti = 2 * p + u;
+            if (ti < KA) continue;
+            const bf16x8 a = ld_lds16(srow + (16 * ti + l16) * ROWKV + 32 * ds + 8 * grp);
+            sa[u] = mfma(a, ba, sa[u]);
+            if (p == 1 && ti >= KB) sb[u] = mfma(a, bb, sb[u]);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          if (2 * p + u == KA) sa[u] = causal_mask_t(sa[u], l16, grp);
+          if (2 * p + u == KB) sb[u] = causal_mask_t(sb[u], l16, grp);
+        }
+        const bf16x8 pa = pack_tiles(sa[0], sa[1]);
+        const bf16x8 pb = pack_tiles(sb[0], sb[1]);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const bf16x8 ct = tr_operand(scol, p, 16 * t, l16, grp);
+          acc[0][t] = mfma(ct, pa, acc[0][t]);
+          if (p == 1) acc[1][t] = mfma(ct, pb, acc[1][t]);
+        }
+      }
+      if (h == G - 1) {
+        void* out = SIDE == 0 ? A.dvg : A.dk;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int64_t s = blk * C + 16 * (e ? KB : KA) + l16;
+          if (s < N) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+              store_row4<OUT_F32>(out, (int64_t(bg) * N + s) * DV + 16 * t + 4 * grp, acc[e][t]);
+          }
+        }
+        r_in = 0;
+        --blk;
+      } else {
+        ++r_in;
+      }
+    }
+  };
+
+  int64_t n = 0;
+  for (; n + NS <= nitems; n += NS) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) step(slot[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i)
+    if (n + i < nitems) step(slot[i]);
+
+  if constexpr (HELPER) {
+    if (A.ds_in != nullptr && seg == 0) {
+      float* so = A.ds_in + int64_t(bg) * DD;
+#pragma unroll
+      for (int m = 0; m < NR; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          so[(16 * r_row<SIDE, PAIR>(m) + 4 * grp + i) * DV + 16 * r_col<SIDE, PAIR>(m) + l16] = racc[m][i];
+    }
+  }
+}
+
+template <bool OUT_F32, int NS>
+__global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel8h(BwdArgs4 args) {
+  __shared__ BwdSmem4 sm;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  switch (w) {
+    case 0: bwd_kv_wave8h<OUT_F32, 0, 0, false, NS>(args, sm); break;
+    case 1: bwd_kv_wave8h<OUT_F32, 0, 1, false, NS>(args, sm); break;
+    case 2: bwd_kv_wave8h<OUT_F32, 1, 0, false, NS>(args, sm); break;
+    case 3: bwd_kv_wave8h<OUT_F32, 1, 1, false, NS>(args, sm); break;
+    case 4: bwd_kv_wave8h<OUT_F32, 0, 0, true, NS>(args, sm); break;
+    case 5: bwd_kv_wave8h<OUT_F32, 0, 1, true, NS>(args, sm); break;
+    case 6: bwd_kv_wave8h<OUT_F32, 1, 0, true, NS>(args, sm); break;
+    default: bwd_kv_wave8h<OUT_F32, 1, 1, true, NS>(args, sm); break;
   }
 }
 
@@ -886,10 +1119,17 @@ hipError_t launch_bwd_kv(const void* q, const void* k, const void* v, const void
 #else
   const BwdArgs4 args{q16, k16, v16, o16, dk, dvg, rs, ds_in, int(Hq), int(Hkv), N, plan.nblocks,
                       plan.blocks_per_seg, plan.P};
+#ifdef LA_BWD_HELPER
+  if (out_f32)
+    hipLaunchKernelGGL((bwd_kv_kernel8h<true, LA_BWD_SLOTS4>), grid, dim3(kThreads), 0, stream, args);
+  else
+    hipLaunchKernelGGL((bwd_kv_kernel8h<false, LA_BWD_SLOTS4>), grid, dim3(kThreads), 0, stream, args);
+#else
   if (out_f32)
     hipLaunchKernelGGL((bwd_kv_kernel4<true, LA_BWD_SLOTS4>), grid, dim3(kThreads4), 0, stream, args);
   else
     hipLaunchKernelGGL((bwd_kv_kernel4<false, LA_BWD_SLOTS4>), grid, dim3(kThreads4), 0, stream, args);
+#endif
 #endif
   return hipGetLastError();
 }
