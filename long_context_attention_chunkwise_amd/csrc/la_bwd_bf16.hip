@@ -717,36 +717,33 @@ __device__ __forceinline__ void bwd_kv_wave8h(const BwdArgs4& A, BwdSmem4& sm) {
       const uint16_t* srow = sm.t[nb][SIDE];      // score rows: Q (SIDE 0) or dO
       const uint16_t* scol = sm.t[nb][1 - SIDE];  // contraction operands: dO (SIDE 0) or Q
       const uint16_t* kv = sm.t[kvb][SIDE] + l16 * ROWKV + 8 * grp;
+      // all score tiles of the head first (independent product chains):
+      // sc[ti] of key tile KA for query tiles ti = KA..3, sb[u] of KB for
+      // query tiles 2 + u; entry i of a tile holds t = 16ti + 4grp + i, key l16
+      floatx4 sc[4] = {z4, z4, z4, z4}, sb[2] = {z4, z4};
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        floatx4 sa[2] = {z4, z4}, sb[2] = {z4, z4};
+      for (int ds = 0; ds < 4; ++ds) {
+        const bf16x8 ba = ld_lds16(kv + 16 * KA * ROWKV + 32 * ds);
+        const bf16x8 bb = ld_lds16(kv + 16 * KB * ROWKV + 32 * ds);
 #pragma unroll
-        for (int ds = 0; ds < 4; ++ds) {
-          const bf16x8 ba = ld_lds16(kv + 16 * KA * ROWKV + 32 * ds);
-          const bf16x8 bb = p == 1 ? ld_lds16(kv + 16 * KB * ROWKV + 32 * ds) : ba;
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int ti = 2 * p + u;
-            if (ti < KA) continue;
-            const bf16x8 a = ld_lds16(srow + (16 * ti + l16) * ROWKV + 32 * ds + 8 * grp);
-            sa[u] = mfma(a, ba, sa[u]);
-            if (p == 1 && ti >= KB) sb[u] = mfma(a, bb, sb[u]);
-          }
+        for (int ti = KA; ti < 4; ++ti) {
+          const bf16x8 a = ld_lds16(srow + (16 * ti + l16) * ROWKV + 32 * ds + 8 * grp);
+          sc[ti] = mfma(a, ba, sc[ti]);
+          if (ti >= KB) sb[ti - 2] = mfma(a, bb, sb[ti - 2]);
         }
+      }
+      sc[KA] = causal_mask_t(sc[KA], l16, grp);
+      sb[KB - 2] = causal_mask_t(sb[KB - 2], l16, grp);
+      const bf16x8 pa[2] = {pack_tiles(sc[0], sc[1]), pack_tiles(sc[2], sc[3])};
+      const bf16x8 pb = pack_tiles(sb[0], sb[1]);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          if (2 * p + u == KA) sa[u] = causal_mask_t(sa[u], l16, grp);
-          if (2 * p + u == KB) sb[u] = causal_mask_t(sb[u], l16, grp);
-        }
-        const bf16x8 pa = pack_tiles(sa[0], sa[1]);
-        const bf16x8 pb = pack_tiles(sb[0], sb[1]);
+      for (int p = 0; p < 2; ++p)
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           const bf16x8 ct = tr_operand(scol, p, 16 * t, l16, grp);
-          acc[0][t] = mfma(ct, pa, acc[0][t]);
+          acc[0][t] = mfma(ct, pa[p], acc[0][t]);
           if (p == 1) acc[1][t] = mfma(ct, pb, acc[1][t]);
         }
-      }
       if (h == G - 1) {
         void* out = SIDE == 0 ? A.dvg : A.dk;
 #pragma unroll
