@@ -180,7 +180,7 @@ size_t la_forward_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
  * la_forward_workspace_bytes exceeds it returns LA_ERR_TOO_LARGE before
  * anything is launched; use la_forward_ex with a caller workspace then.  At
  * head size 128 on a 256-CU part, 128 query heads over 32 KV heads at
- * 1,048,576 tokens need 58 MiB, and up to 200 (batch, KV head) pairs fit at
+ * 1,048,576 tokens need 44 MiB, and up to 1024 (batch, KV head) pairs fit at
  * any sequence length.
  * Every call on one GPU shares that GPU's array and leaves its contents behind
  * (nothing in it needs clearing: each call writes the entries it reads before

@@ -104,12 +104,12 @@ Bf16Plan plan_bf16(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int
   p.P = static_cast<int>(P);
 
   if (P > 1) {
-    // Pre-pass parts: as many as fit the chip in one round (three pre-pass
-    // workgroups are resident per compute unit), so no partial last round
-    // leaves compute units idle; each part sums at least kMinPartBlocks blocks
-    // (a part writes a 64 KiB partial).
+    // Pre-pass parts: as many as fit the chip in one round (two pre-pass
+    // workgroups are resident per compute unit at head size 128, three at
+    // 64), so no partial last round leaves compute units idle; each part sums
+    // at least kMinPartBlocks blocks (a part writes a 64 KiB partial).
     constexpr int64_t kMinPartBlocks = 8;
-    constexpr int64_t kPartWgsPerCu = 3;
+    const int64_t kPartWgsPerCu = d == 128 ? 2 : 3;
     int64_t R = (kPartWgsPerCu * int64_t(cus)) / (kv_chains * (P - 1));
     R = std::max<int64_t>(1, std::min(R, p.blocks_per_seg / kMinPartBlocks));
     p.blocks_per_part = (p.blocks_per_seg + R - 1) / R;
@@ -184,13 +184,13 @@ BwdPlan plan_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, 
   if (P > 1) {
     // Pre-pass over (Q, dO) of every query head and every segment but the
     // first.  Parts per segment: the count with the least (rounds of resident
-    // workgroups, three per compute unit) x (blocks per part + the cost of
-    // its partial, written once and read once by the scan: 4 d dv floats
-    // against a block's 64 (d + dv) bf16 values, four blocks at d = dv = 128),
-    // i.e. the shortest pre-pass when every part streams at the same rate;
-    // ties go to fewer parts.
+    // workgroups, two per compute unit at head size 128 and three at 64) x
+    // (blocks per part + the cost of its partial, written once and read once
+    // by the scan: 4 d dv floats against a block's 64 (d + dv) bf16 values,
+    // four blocks at d = dv = 128), i.e. the shortest pre-pass when every part
+    // streams at the same rate; ties go to fewer parts.
     constexpr int64_t kMinPartBlocks = 8;
-    constexpr int64_t kPartWgsPerCu = 3;
+    const int64_t kPartWgsPerCu = d == 128 ? 2 : 3;
     const int64_t kPartialCostBlocks = std::max<int64_t>(1, (4 * d * dv) / (kBf16Block * (d + dv)));
     const int64_t pre_chains = B * Hq * (P - 1);
     const int64_t slots = kPartWgsPerCu * int64_t(cus);

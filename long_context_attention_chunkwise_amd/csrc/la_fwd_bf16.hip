@@ -50,6 +50,8 @@ using namespace mfma16;
 
 constexpr int kMainThreads = 512;
 constexpr int kPartThreads = 256;
+// Pre-pass workgroups resident per compute unit (registers: two load slots).
+constexpr int part_wgs_per_cu(int hd) { return hd == 128 ? 2 : 3; }
 
 struct __align__(16) MainSmem {
   uint16_t k[2][C * ROWKV];
@@ -759,16 +761,18 @@ __global__ __launch_bounds__(64, 1) void fwd_bf16_solo(const uint16_t* __restric
 // the last with seg_offset 0; the backward every segment but the first with
 // seg_offset 1).  Four waves; wave w owns state columns [w HD/4, (w+1) HD/4)
 // (head size HD = d = dv, 128 or 64).  A pure HBM stream: the K/V tile is
-// single-buffered in LDS (36 KiB at HD = 128) so three workgroups share a CU,
-// each with the next block's loads in flight while it multiplies the current
-// one.
+// single-buffered in LDS (36 KiB at HD = 128) and the next two blocks' loads
+// are in flight in two register slots while a block is multiplied; two
+// workgroups share a CU at HD = 128 (148 + 32 registers per wave), three at
+// 64.  (At 128, two slots and two workgroups per CU measured 0.6 ms faster
+// per 1M-token backward than one slot and three.)
 //
 // Flags (feature-map variants): kRelu applies phi = ReLU to k as it enters
 // LDS; kNorm also writes zpart[c][j][r] = sum of phi(k_b) over the part
 // (wave w: entries [32w, 32w+32), as K^T times a ones operand on the matrix
 // cores).
 template <int FL, int HD = 128>
-__global__ __launch_bounds__(kPartThreads, 3) void state_parts(const uint16_t* __restrict__ k,
+__global__ __launch_bounds__(kPartThreads, part_wgs_per_cu(HD)) void state_parts(const uint16_t* __restrict__ k,
                                                            const uint16_t* __restrict__ v,
                                                            float* __restrict__ partial,
                                                            float* __restrict__ zpart, int64_t N,
@@ -823,12 +827,16 @@ __global__ __launch_bounds__(kPartThreads, 3) void state_parts(const uint16_t* _
     }
   };
 
-  uint4 kr[HD / 32], vr[HD / 32];
-  if (b0 < b1) load(b0, kr, vr);
-  for (int64_t blk = b0; blk < b1; ++blk) {
-    store(kr, vr);
+  // Two register slots; blocks past the part are loaded too (zeros past N,
+  // unused otherwise) so that every path issues the same loads.
+  constexpr int NSL = 2;
+  int64_t blk = b0;
+  uint4 kr[NSL][HD / 32], vr[NSL][HD / 32];
+  for (int sl = 0; sl < NSL; ++sl) load(b0 + sl, kr[sl], vr[sl]);
+  auto body = [&](int sl) __attribute__((always_inline)) {
+    store(kr[sl], vr[sl]);
     __syncthreads();  // the block's K and V are in LDS
-    if (blk + 1 < b1) load(blk + 1, kr, vr);
+    load(blk + NSL, kr[sl], vr[sl]);
     for (int p = 0; p < 2; ++p) {
       bf16x8 vb[NJ];
       for (int jn = 0; jn < NJ; ++jn) vb[jn] = tr_operand(vsm, p, WC * w + 16 * jn, l16, grp, 4, RKV);
@@ -841,7 +849,15 @@ __global__ __launch_bounds__(kPartThreads, 3) void state_parts(const uint16_t* _
           zacc[jj] = mfma(tr_operand(ksm, p, WC * w + 16 * jj, l16, grp, 4, RKV), ones_bf16x8(), zacc[jj]);
     }
     __syncthreads();  // every wave is done with this block's K and V
-  }
+    ++blk;
+  };
+  // whole rounds of NSL blocks in the loop, the remainder after it (a
+  // conditional step inside the loop would make the compiler wait for every
+  // load in flight before each store)
+  while (blk + NSL <= b1)
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl) body(sl);
+  if (blk < b1) body(0);
   if constexpr ((FL & kNorm) != 0) {
     // every column of the ones product holds the sum; lanes of column 0 write it
     float* zo = zpart + ((int64_t(c) * (P - 1) + j) * R + r) * HD;

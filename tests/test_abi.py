@@ -149,10 +149,10 @@ def test_variant_validation(lib):
 def test_workspace_plan(lib):
     # Host planning with the default 256 compute units (no device here): the
     # 1M-token GQA problem splits each of the 32 chains into 8 segments and
-    # every segment but the last into 3 pre-pass parts (672 pre-pass
-    # workgroups: one round at three per compute unit).
+    # every segment but the last into 2 pre-pass parts (448 pre-pass
+    # workgroups: one round at two per compute unit at head size 128).
     n = lib.la_forward_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, 64, BF16)
-    assert n == (32 * 7 * 3 + 32 * 8) * 128 * 128 * 4
+    assert n == (32 * 7 * 2 + 32 * 8) * 128 * 128 * 4
     assert lib.la_forward_workspace_bytes(1, 1, 1, 256, 64, 64, 64, F32) == 0
     # a block that is a multiple of 64 tokens is computed as 64-token blocks: same plan
     for blk in (128, 4096):
@@ -160,8 +160,8 @@ def test_workspace_plan(lib):
         assert lib.la_backward_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, blk, BF16) == \
             lib.la_backward_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, 64, BF16)
     assert lib.la_forward_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, 96, BF16) == 0   # unsupported -> 0
-    # head size 64 on the matrix cores for every group size: groups of four and of two (one workgroup per
-    # KV head either way) give the same split; groups of three take one workgroup per query head (96
+    # head size 64 on the matrix cores for every group size (three pre-pass workgroups per compute unit,
+    # so 3 parts): groups of four and of two (one workgroup per KV head either way) give the same split; groups of three take one workgroup per query head (96
     # chains: 3 segments, the first two summed in 12 parts)
     assert lib.la_forward_workspace_bytes(1, 128, 32, 1 << 20, 64, 64, 64, BF16) == (32 * 7 * 3 + 32 * 8) * 64 * 64 * 4
     assert lib.la_forward_workspace_bytes(1, 64, 32, 1 << 20, 64, 64, 64, BF16) == (32 * 7 * 3 + 32 * 8) * 64 * 64 * 4
@@ -179,11 +179,11 @@ def test_workspace_plan(lib):
     assert lib.la_forward_workspace_bytes(1, 6, 4, 64, 128, 128, 64, BF16) == 0   # invalid -> 0
     # Backward at 1M tokens: the dQ forward's workspace, the transposed
     # initial states, and for dK/dV 8 segments per chain whose 7 later
-    # segments are summed over (Q, dO) of 128 query heads in 6 parts each
-    # (5376 pre-pass workgroups: seven full rounds), plus 8 start states per
-    # chain.
+    # segments are summed over (Q, dO) of 128 query heads in 4 parts each
+    # (3584 pre-pass workgroups: seven full rounds at two per compute unit),
+    # plus 8 start states per chain.
     n = lib.la_backward_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, 64, BF16)
-    assert n == ((32 * 7 * 3 + 32 * 8) + 32 + 128 * 7 * 6 + 32 * 8) * 128 * 128 * 4
+    assert n == ((32 * 7 * 2 + 32 * 8) + 32 + 128 * 7 * 4 + 32 * 8) * 128 * 128 * 4
     assert lib.la_backward_workspace_bytes(1, 128, 32, 0, 128, 128, 64, BF16) == 0
     # Head size 64 (groups of four): states of 64 x 64, and two dK/dV workgroups per compute unit, so
     # 16 segments per chain whose 15 later segments are summed in 2 parts each (3840 pre-pass
@@ -198,13 +198,13 @@ def test_workspace_plan(lib):
     assert lib.la_forward_workspace_bytes(1, 4, 1, 1000, 96, 96, 64, BF16) == 0
     assert lib.la_backward_workspace_bytes(1, 4, 2, 64, 64, 96, 64, BF16) == 2 * 64 * 96 * 4
     # Variants at 1M tokens: causal = the forward's split (+ normaliser sums);
-    # non-causal sums all 8 segments of each chain (3 parts each) and scans
+    # non-causal sums all 8 segments of each chain (2 parts each) and scans
     # 9 entries, the last being the total.
     DD, d = 128 * 128, 128
     causal = lib.la_forward_variant_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, 64, BF16, 1, 1)
-    assert causal == ((32 * 7 * 3 + 32 * 8) * DD + (32 * 7 * 3 + 32 * 8) * d) * 4
+    assert causal == ((32 * 7 * 2 + 32 * 8) * DD + (32 * 7 * 2 + 32 * 8) * d) * 4
     nonc = lib.la_forward_variant_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, 64, BF16, 0, 0)
-    assert nonc == (32 * 8 * 3 + 32 * 9) * DD * 4
+    assert nonc == (32 * 8 * 2 + 32 * 9) * DD * 4
     assert lib.la_forward_variant_workspace_bytes(1, 8, 2, 256, 128, 128, 64, BF16, 0, 1) > 0  # one segment still sums
     assert lib.la_forward_variant_workspace_bytes(1, 2, 1, 256, 128, 128, 64, BF16, 1, 0) == 0  # unsupported -> 0
 
@@ -232,7 +232,7 @@ def test_noalloc_rejects_before_touching_the_device(lib):
     assert na(B=1100, Hq=8, Hkv=1, N=64) == TOO_LARGE
     assert lib.la_forward_workspace_bytes(1100, 8, 1, 64, 128, 128, 64, BF16) == 1100 * 128 * 128 * 4
     # the 1M-token, 128/32-head workload fits (planned here for 256 compute units)
-    assert lib.la_forward_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, 64, BF16) == (32 * 7 * 3 + 32 * 8) * 65536
+    assert lib.la_forward_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, 64, BF16) == (32 * 7 * 2 + 32 * 8) * 65536
 
 
 def test_stream_library_exports_its_header():

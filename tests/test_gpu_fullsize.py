@@ -80,8 +80,9 @@ def test_gqa_1m_slices_and_states(workload):
     assert bool(torch.isfinite(o).all())
     W = 65536
     # segments per chain at 1M tokens on 256 compute units, and pre-pass parts per summed segment:
-    # 8 in 3 parts (four-wave workgroups), 32 in 1 part (one-wave workgroups: head size 64, Hq = Hkv)
-    nseg, nparts = (32, 1) if (w.d == 64 and w.Hq == w.Hkv) else (8, 3)
+    # 8 segments (four-wave workgroups) in 2 parts at head size 128 and 3 at 64 (two and three pre-pass
+    # workgroups per compute unit), 32 in 1 part (one-wave workgroups: head size 64, Hq = Hkv)
+    nseg, nparts = (32, 1) if (w.d == 64 and w.Hq == w.Hkv) else (8, 2 if w.d == 128 else 3)
     seg = w.N // nseg
     assert ws_bytes == (w.Hkv * (nseg - 1) * nparts + w.Hkv * nseg) * w.d * w.dv * 4
     # segment start states as the pre-pass and scan left them: [Hkv][segment][d][dv] after the partials

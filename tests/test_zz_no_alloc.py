@@ -4,7 +4,7 @@ the C ABI: two calls in a row, the second on a smaller input, each bit for bit
 equal to la_forward_ex's output and final state (both run the same kernels on
 the same plan; la_forward_ex itself is held to the oracle by the forward
 tests).  The first call is the 1,048,576-token, 128/32-head workload, whose
-58 MiB workspace the fixed 64 MiB scratch is sized for; the second, 5000
+44 MiB workspace fits the fixed 64 MiB scratch; the second, 5000
 tokens with an initial state and float32 output, reuses the scratch the first
 left behind.  A problem beyond the scratch is refused and writes nothing.
 """
