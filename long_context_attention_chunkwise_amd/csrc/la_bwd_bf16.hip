@@ -15,21 +15,27 @@
 // walked from the last block to the first.  (dQ is the causal forward on
 // (dO, V, K) and runs on the forward kernels.)
 //
-// Design for MI355X: one workgroup of eight waves (two per SIMD, so one
-// wave's LDS and memory waits overlap the other's products) per (batch, KV
-// head, sequence segment); segment j starts from the sum over later segments,
-// produced by the forward's pre-pass kernel run on (Q, dO) pairs and a
-// reverse scan here.  Wave w owns columns [16w, 16w+16) of dV, dK and the
-// state R; the fp32 state stays in VGPRs and is rounded to bf16 once per
-// block into an n-major LDS copy for the inter terms.  Query heads are
-// processed one at a time through LDS: the K/V pair and each head's (Q, dO)
-// pair form one stream of 32 KiB items rotating over two register slots (two
-// items in flight).  Products are v_mfma_f32_16x16x32_bf16 with the
-// transposed-product layout of the forward kernel: wave w computes the score
-// tiles X^T = Q K^T (w < 4) or Y^T = dO V^T (w >= 4) of key tile w % 4 for all
-// four query tiles, masks t >= s arithmetically (no branch depends on the
-// wave) and publishes them in LDS as bf16 B operands of the token-contracting
-// products.
+// Design for MI355X (head size 128): one workgroup of eight waves per (batch,
+// KV head, sequence segment); segment j starts from the sum over later
+// segments, produced by the forward's pre-pass kernel run on (Q, dO) pairs
+// and a reverse scan here.  On SIMD s, wave s is a gradient wave and wave
+// s + 4 a state wave:
+//  * gradient waves 0 and 1 hold dV^T of key tiles {0, 3} and {1, 2} of the
+//    block, waves 2 and 3 dK^T of the same pairs (pairing key tile j with
+//    3 - j evens out the causal work).  A gradient wave computes the score
+//    tiles of its own keys (X^T = Q K^T for dV, Y^T = dO V^T for dK), which
+//    stay in registers as the operands of its intra products, and the inter
+//    products from the bf16 copy of R;
+//  * the state waves hold R (128 x 128, float32) in four sets of 16 tiles,
+//    update them per query head and round them once per block into an
+//    n-major bf16 LDS copy.
+// Each SIMD thus does 92 matrix products per query head, split 60 / 32
+// between its two waves, and one wave's LDS waits overlap the other's
+// products.  The block's K/V pair and each query head's Q/dO pair form one
+// stream of 32 KiB items through two register slots and three LDS buffers
+// (the block's K/V keeps one, its heads alternate between the other two), so
+// one barrier per item suffices.  Products are v_mfma_f32_16x16x32_bf16 in
+// the transposed-product layout of the forward kernel.
 #include "la_internal.h"
 #include "la_mfma.h"
 
@@ -39,7 +45,7 @@ namespace {
 using namespace mfma16;
 
 constexpr int kThreads = 512;  // eight waves, two per SIMD
-constexpr int kSlots = 2;      // 32 KiB tile pairs in flight per workgroup
+constexpr int kSlots = 2;      // 32 KiB items in flight per workgroup (register slots)
 constexpr int DD = D * DV;
 
 __device__ __forceinline__ u32x4 ld_stream_v(const uint16_t* p) {
@@ -47,12 +53,9 @@ __device__ __forceinline__ u32x4 ld_stream_v(const uint16_t* p) {
 }
 
 struct __align__(16) BwdSmem {
-  uint16_t k[C * ROWKV];    // K_b   [s][d]
-  uint16_t v[C * ROWKV];    // V_b   [s][n]
-  uint16_t q[C * ROWKV];    // Q_hb  [t][d]  (one query head at a time)
-  uint16_t o[C * ROWKV];    // dO_hb [t][n]
+  // Three buffers of one item each (two [64][128] bf16 tiles, row-major).
+  uint16_t t[3][2][C * ROWKV];
   uint16_t rt[DV * ROWST];  // bf16 copy of R, n-major: rt[n][i]
-  bf16x8 xb[2][8][64];      // X^T / Y^T operand packs: [X or Y][4p + s-tile][lane]
 };
 
 template <bool OUT_F32>
@@ -100,232 +103,6 @@ __device__ __forceinline__ void store_pair8(const PairRegs8& r, uint16_t* as, ui
   }
 }
 
-template <bool OUT_F32, int NS>
-__global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel8(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ dout, void* __restrict__ dk, void* __restrict__ dvg,
-    const float* __restrict__ rstarts, float* __restrict__ ds_in, int Hq, int Hkv, int64_t N,
-    int64_t nblocks, int64_t blocks_per_seg, int P) {
-  static_assert(NS == 1 || NS == 2, "one or two slots");
-  __shared__ BwdSmem sm;
-
-  const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7, uniform
-  const int lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
-  const int seg = blockIdx.x % P;
-  const int bg = blockIdx.x / P;
-  const int b = bg / Hkv, g = bg % Hkv;
-  const int G = Hq / Hkv;
-  const int64_t blk0 = int64_t(seg) * blocks_per_seg;
-  const int64_t blk1 = blk0 + blocks_per_seg < nblocks ? blk0 + blocks_per_seg : nblocks;
-
-  const uint16_t* kh = k + int64_t(bg) * N * D;
-  const uint16_t* vh = v + int64_t(bg) * N * DV;
-  const uint16_t* qg = q + (int64_t(b) * Hq + int64_t(g) * G) * N * D;
-  const uint16_t* og = dout + (int64_t(b) * Hq + int64_t(g) * G) * N * DV;
-
-  // R columns [16w, 16w+16): tile it holds rows 16it + 4grp + i, column 16w + l16
-  const float* r0 = rstarts ? rstarts + (int64_t(bg) * P + seg) * DD : nullptr;
-  floatx4 racc[8];
-  for (int it = 0; it < 8; ++it)
-    for (int i = 0; i < 4; ++i) racc[it][i] = 0.0f;
-  if (r0 != nullptr)
-    for (int it = 0; it < 8; ++it)
-      for (int i = 0; i < 4; ++i) racc[it][i] = r0[(16 * it + 4 * grp + i) * DV + 16 * w + l16];
-  for (int it = 0; it < 8; ++it)
-    *reinterpret_cast<bf16x4*>(&sm.rt[(16 * w + l16) * ROWST + 16 * it + 4 * grp]) = to_bf16x4(racc[it]);
-
-  const int per_blk = G + 1;
-  int64_t ld_blk = blk1 - 1;
-  int ld_r = 0;
-  auto load_next = [&](PairRegs8& r) __attribute__((always_inline)) {
-    const int rows = int(N - ld_blk * C < C ? N - ld_blk * C : C);
-    const uint16_t* a = ld_r == 0 ? kh : qg + int64_t(ld_r - 1) * N * D;
-    const uint16_t* bb = ld_r == 0 ? vh : og + int64_t(ld_r - 1) * N * DV;
-    load_pair8(r, a + ld_blk * C * D, bb + ld_blk * C * DV, rows, tid);
-    if (ld_blk > blk0 || ld_r < G) {
-      if (++ld_r == per_blk) {
-        ld_r = 0;
-        --ld_blk;
-      }
-    }
-  };
-
-  const int64_t nitems = (blk1 - blk0) * per_blk;
-  PairRegs8 s0, s1;
-  if (nitems > 0) {
-    load_next(s0);
-    if constexpr (NS == 2) load_next(s1);
-  }
-
-  const floatx4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
-  floatx4 adv[4], adk[4];  // dV^T / dK^T tiles of columns 16w.. for s-tiles 0..3
-  int64_t blk = blk1 - 1;
-  int r_in = 0;
-  const bool is_y = w >= 4;   // uniform: this wave's score tiles are Y^T = dO V^T
-  const int skey = w & 3;     // its key tile
-
-  auto step = [&](PairRegs8& cur) __attribute__((always_inline)) {
-    const int rows = int(N - blk * C < C ? N - blk * C : C);
-    if (r_in == 0) {
-      store_pair8(cur, sm.k, sm.v, rows, tid);
-      load_next(cur);
-      for (int si = 0; si < 4; ++si) {
-        adv[si] = z4;
-        adk[si] = z4;
-      }
-      r_in = 1;
-      return;
-    }
-    const int h = r_in - 1;
-    store_pair8(cur, sm.q, sm.o, rows, tid);
-    __syncthreads();  // K/V, this head's Q/dO and the state copy are in LDS
-    load_next(cur);
-
-    if (h == 0) {
-      // inter: dV^T[n][s] += sum_i R[i][n] K[s][i];  dK^T[i][s] += sum_n R[i][n] V[s][n]
-      for (int p = 0; p < 4; ++p) {
-        const bf16x8 ra = ld_lds16(sm.rt + (16 * w + l16) * ROWST + 32 * p + 8 * grp);
-        const bf16x8 rb = tr_operand(sm.rt, p, 16 * w, l16, grp, 4, ROWST);
-        for (int si = 0; si < 4; ++si) {
-          const uint16_t* krow = sm.k + (16 * si + l16) * ROWKV;
-          const uint16_t* vrow = sm.v + (16 * si + l16) * ROWKV;
-          const bf16x8 bk = ld_lds16(krow + 32 * p + 8 * grp);
-          const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(vrow + 32 * p + 4 * grp);
-          const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(vrow + 32 * p + 16 + 4 * grp);
-          const bf16x8 bv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-          adv[si] = mfma(ra, bk, adv[si]);
-          adk[si] = mfma(rb, bv, adk[si]);
-        }
-      }
-    }
-
-    // scores of key tile skey for all four query tiles: X^T = Q K^T or Y^T = dO V^T
-    {
-      const uint16_t* arows = is_y ? sm.o : sm.q;
-      const uint16_t* brows = (is_y ? sm.v : sm.k) + (16 * skey + l16) * ROWKV;
-      floatx4 xt[4];
-      for (int ti = 0; ti < 4; ++ti) xt[ti] = z4;
-      for (int ds = 0; ds < 4; ++ds) {
-        const bf16x8 bop = ld_lds16(brows + 32 * ds + 8 * grp);
-        for (int ti = 0; ti < 4; ++ti)
-          xt[ti] = mfma(ld_lds16(arows + (16 * ti + l16) * ROWKV + 32 * ds + 8 * grp), bop, xt[ti]);
-      }
-      // entry i of tile ti: t = 16ti + 4grp + i, s = 16skey + l16; keep t >= s
-      const int lim = 16 * skey + l16 - 4 * grp;
-      for (int ti = 0; ti < 4; ++ti)
-        for (int i = 0; i < 4; ++i)
-          if (16 * ti + i < lim) xt[ti][i] = 0.0f;
-      for (int p = 0; p < 2; ++p) sm.xb[is_y ? 1 : 0][4 * p + skey][lane] = pack_tiles(xt[2 * p], xt[2 * p + 1]);
-    }
-    __syncthreads();  // every wave's score packs are in LDS
-
-    // intra (dV, dK columns 16w..) and the state update (R columns 16w..)
-    for (int p = 0; p < 2; ++p) {
-      const bf16x8 ao = tr_operand(sm.o, p, 16 * w, l16, grp);
-      const bf16x8 aq = tr_operand(sm.q, p, 16 * w, l16, grp);
-      for (int si = 0; si < 4; ++si) {
-        if (p == 0 && si >= 2) continue;  // tokens 0..31 are all before key tiles 2, 3
-        adv[si] = mfma(ao, sm.xb[0][4 * p + si][lane], adv[si]);
-        adk[si] = mfma(aq, sm.xb[1][4 * p + si][lane], adk[si]);
-      }
-      for (int it = 0; it < 8; ++it) racc[it] = mfma(tr_operand(sm.q, p, 16 * it, l16, grp), ao, racc[it]);
-    }
-    __syncthreads();  // Q/dO and the packs may be overwritten
-
-    if (h == G - 1) {
-      // dV, dK rows of the block: tile si holds columns 16w + 4grp + {0..3} of row 16si + l16
-      for (int si = 0; si < 4; ++si) {
-        const int64_t s = blk * C + 16 * si + l16;
-        if (s < N) {
-          const int64_t off = (int64_t(bg) * N + s) * DV + 16 * w + 4 * grp;
-          store_row4<OUT_F32>(dvg, off, adv[si]);
-          store_row4<OUT_F32>(dk, off, adk[si]);
-        }
-      }
-      for (int it = 0; it < 8; ++it)
-        *reinterpret_cast<bf16x4*>(&sm.rt[(16 * w + l16) * ROWST + 16 * it + 4 * grp]) = to_bf16x4(racc[it]);
-      r_in = 0;
-      --blk;
-    } else {
-      ++r_in;
-    }
-  };
-
-  for (int64_t n = 0; n < nitems; n += NS) {
-    step(s0);
-    if constexpr (NS == 2)
-      if (n + 1 < nitems) step(s1);
-  }
-
-  if (ds_in != nullptr && seg == 0) {
-    float* so = ds_in + int64_t(bg) * DD;
-    for (int it = 0; it < 8; ++it)
-      for (int i = 0; i < 4; ++i) so[(16 * it + 4 * grp + i) * DV + 16 * w + l16] = racc[it][i];
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Head size 128, four waves (one per SIMD) per (batch, KV head, segment), each
-// owning one kind of gradient for two key tiles of the block: waves 0 and 1
-// hold dV^T of key tiles {0, 3} and {1, 2}, waves 2 and 3 dK^T of the same
-// pairs.  A wave computes the score tiles of its own keys (X^T = Q K^T for
-// dV, Y^T = dO V^T for dK), which stay in registers as the operands of its
-// intra products: no score tile passes through LDS.  Pairing key tile j with
-// 3 - j evens out the causal work (five query tiles of scores and three query
-// tile pairs of intra products per wave).  The reverse state R (128 x 128,
-// float32) is split into four sets of 16 tiles: the dV waves hold row tiles
-// {0, 1} and {2, 3} (all columns) and update them with the dO^T operands of
-// their intra products; the dK waves hold row tiles 4..7 of column tiles
-// 0..3 and 4..7 and use the Q^T operands of theirs.  Every wave thus does 92
-// matrix products per query head.  Once per block R is rounded into an
-// n-major bf16 LDS copy that every wave reads for its inter terms.
-//
-// Items (a block's K/V pair, then each query head's Q/dO pair) pass through
-// two register slots and three LDS buffers: the block's K/V keeps one, its
-// heads alternate between the other two, so one barrier per item suffices.
-// ---------------------------------------------------------------------------
-constexpr int kThreads4 = 256;
-#ifndef LA_BWD_SLOTS4
-#define LA_BWD_SLOTS4 2
-#endif
-#ifndef LA_BWD_FOUR_WAVES
-#define LA_BWD_HELPER
-#endif
-
-struct __align__(16) BwdSmem4 {
-  // Three buffers of one item each (two [64][128] bf16 tiles, row-major).
-  uint16_t t[3][2][C * ROWKV];
-  uint16_t rt[DV * ROWST];  // bf16 copy of R, n-major: rt[n][i]
-};
-
-// Two row-major [64][128] bf16 tiles moved by 256 threads: rows tid/16 + 16i
-// (i < 4), 16-byte chunk tid%16; rows past `rows` re-read the last valid row
-// and are stored to LDS as zeros.
-struct PairRegs4 {
-  u32x4 a[4], b[4];
-};
-
-__device__ __forceinline__ void load_pair4(PairRegs4& r, const uint16_t* ab, const uint16_t* bb, int rows, int tid) {
-  const int c = tid & 15;
-  for (int i = 0; i < 4; ++i) {
-    int row = (tid >> 4) + 16 * i;
-    row = row < rows ? row : rows - 1;
-    r.a[i] = ld_stream_v(ab + row * D + 8 * c);
-    r.b[i] = ld_stream_v(bb + row * DV + 8 * c);
-  }
-}
-
-__device__ __forceinline__ void store_pair4(const PairRegs4& r, uint16_t* as, uint16_t* bs, int rows, int tid) {
-  const int c = tid & 15;
-  const u32x4 z = {0u, 0u, 0u, 0u};
-  for (int i = 0; i < 4; ++i) {
-    const int row = (tid >> 4) + 16 * i;
-    *reinterpret_cast<u32x4*>(as + row * ROWKV + 8 * c) = row < rows ? r.a[i] : z;
-    *reinterpret_cast<u32x4*>(bs + row * ROWKV + 8 * c) = row < rows ? r.b[i] : z;
-  }
-}
-
 // Diagonal X^T / Y^T tile (entry i of lane (l16, grp): token 4grp + i, key
 // l16 within the tile): keep token >= key.
 __device__ __forceinline__ floatx4 causal_mask_t(floatx4 x, int l16, int grp) {
@@ -346,7 +123,7 @@ __device__ __forceinline__ bf16x8 tr_operand_lin(const uint16_t* tile, int k0, i
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-struct BwdArgs4 {
+struct BwdArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
@@ -360,19 +137,22 @@ struct BwdArgs4 {
   int P;
 };
 
-// Tile m (0..15) of the part of R held by wave (SIDE, PAIR): its row and
-// column tile.
+// Tile m (0..15) of the part of R held by state wave (SIDE, PAIR): its row
+// and column tile.  SIDE 0 takes row tiles 2 PAIR, 2 PAIR + 1 (all columns),
+// updated with Q^T of those rows and dO^T of every column; SIDE 1 row tiles
+// 4..7 of column tiles 4 PAIR .. 4 PAIR + 3.
 template <int SIDE, int PAIR>
 __device__ constexpr int r_row(int m) { return SIDE == 0 ? 2 * PAIR + m / 8 : 4 + m / 4; }
 template <int SIDE, int PAIR>
 __device__ constexpr int r_col(int m) { return SIDE == 0 ? m % 8 : 4 * PAIR + m % 4; }
 
-// The whole reverse walk of one wave.  SIDE 0: dV of key tiles PAIR and
-// 3 - PAIR, scores X^T = Q K^T, operands (Q rows, dO^T); SIDE 1: dK of the
-// same keys, scores Y^T = dO V^T, operands (dO rows, Q^T).  Every wave runs
-// the same sequence of barriers.
-template <bool OUT_F32, int SIDE, int PAIR, int NS>
-__device__ __forceinline__ void bwd_kv_wave4(const BwdArgs4& A, BwdSmem4& sm) {
+// The whole reverse walk of one wave.  Gradient wave (STATE false): SIDE 0
+// holds dV of key tiles PAIR and 3 - PAIR (scores X^T = Q K^T, contraction
+// operands dO^T), SIDE 1 dK of the same keys (Y^T = dO V^T, operands Q^T).
+// State wave (STATE true): tiles r_row/r_col<SIDE, PAIR> of R.  Every wave
+// runs the same sequence of barriers.
+template <bool OUT_F32, int SIDE, int PAIR, bool STATE, int NS>
+__device__ __forceinline__ void bwd_kv_wave(const BwdArgs& A, BwdSmem& sm) {
   constexpr int KA = PAIR, KB = 3 - PAIR;  // key tiles (KA < 2 <= KB)
   const int tid = threadIdx.x;
   const int lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
@@ -389,215 +169,8 @@ __device__ __forceinline__ void bwd_kv_wave4(const BwdArgs4& A, BwdSmem4& sm) {
   const uint16_t* qg = A.q + (int64_t(b) * A.Hq + int64_t(g) * G) * N * D;
   const uint16_t* og = A.dout + (int64_t(b) * A.Hq + int64_t(g) * G) * N * DV;
 
-  // R tile m: rows 16 r_row(m) + 4grp + i, column 16 r_col(m) + l16
-  const float* r0 = A.rstarts ? A.rstarts + (int64_t(bg) * A.P + seg) * DD : nullptr;
-  floatx4 racc[16];
-#pragma unroll
-  for (int m = 0; m < 16; ++m)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      racc[m][i] = r0 ? r0[(16 * r_row<SIDE, PAIR>(m) + 4 * grp + i) * DV + 16 * r_col<SIDE, PAIR>(m) + l16] : 0.0f;
-  auto write_rt = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int m = 0; m < 16; ++m)
-      *reinterpret_cast<bf16x4*>(
-          &sm.rt[(16 * r_col<SIDE, PAIR>(m) + l16) * ROWST + 16 * r_row<SIDE, PAIR>(m) + 4 * grp]) =
-          to_bf16x4(racc[m]);
-  };
-  write_rt();
-
-  const int per_blk = G + 1;
-  int64_t ld_blk = blk1 - 1;
-  int ld_r = 0;
-  auto load_next = [&](PairRegs4& r) __attribute__((always_inline)) {
-    const int rows = int(N - ld_blk * C < C ? N - ld_blk * C : C);
-    const uint16_t* a = ld_r == 0 ? kh : qg + int64_t(ld_r - 1) * N * D;
-    const uint16_t* bb = ld_r == 0 ? vh : og + int64_t(ld_r - 1) * N * DV;
-    load_pair4(r, a + ld_blk * C * D, bb + ld_blk * C * DV, rows, tid);
-    if (ld_blk > blk0 || ld_r < G) {
-      if (++ld_r == per_blk) {
-        ld_r = 0;
-        --ld_blk;
-      }
-    }
-  };
-
-  const int64_t nitems = (blk1 - blk0) * per_blk;
-  PairRegs4 slot[NS];
-#pragma unroll
-  for (int i = 0; i < NS; ++i)
-    if (i < nitems) load_next(slot[i]);
-
-  const floatx4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
-  // acc[0][t] / acc[1][t]: dV^T (SIDE 0) or dK^T (SIDE 1) of key tile KA / KB,
-  // rows 16t + 4grp + i (column of dV or dK), column 16 key + l16 (key)
-  floatx4 acc[2][8];
-  int64_t blk = blk1 - 1;
-  int r_in = 0;
-  // Buffer of the current block's K/V and of the last query-head item.  Each
-  // item goes to the third buffer: the other two may still be read by waves
-  // that have not finished the previous item, and every earlier reader of the
-  // third one has passed the previous item's barrier.
-  int kvb = 0, hlast = 1;
-
-  auto step = [&](PairRegs4& cur) __attribute__((always_inline)) {
-    const int rows = int(N - blk * C < C ? N - blk * C : C);
-    const int nb = 3 - kvb - hlast;
-    store_pair4(cur, sm.t[nb][0], sm.t[nb][1], rows, tid);
-    __syncthreads();  // the item is in LDS
-    load_next(cur);
-    if (r_in == 0) {
-      // a block's K/V: start the gradients with the inter terms
-      //   dV^T[n][s] = sum_i R[i][n] K[s][i],  dK^T[i][s] = sum_n R[i][n] V[s][n]
-      // (R: the bf16 copy of the state after the later blocks)
-      kvb = nb;
-      const uint16_t* kv = sm.t[nb][SIDE] + l16 * ROWKV + 8 * grp;  // K rows (SIDE 0) or V rows
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 ba = ld_lds16(kv + 16 * KA * ROWKV + 32 * kk);
-        const bf16x8 bb = ld_lds16(kv + 16 * KB * ROWKV + 32 * kk);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const bf16x8 r = SIDE == 0 ? ld_lds16(sm.rt + (16 * t + l16) * ROWST + 32 * kk + 8 * grp)
-                                     : tr_operand_lin(sm.rt, 32 * kk, 16 * t, l16, grp, ROWST);
-          acc[0][t] = mfma(r, ba, kk ? acc[0][t] : z4);
-          acc[1][t] = mfma(r, bb, kk ? acc[1][t] : z4);
-        }
-      }
-      r_in = 1;
-      return;
-    }
-    const int h = r_in - 1;
-    hlast = nb;
-    // SIDE 0: score rows from Q, contraction operands from dO; SIDE 1: the reverse
-    const uint16_t* srow = sm.t[nb][SIDE];
-    const uint16_t* scol = sm.t[nb][1 - SIDE];
-    const uint16_t* kv = sm.t[kvb][SIDE] + l16 * ROWKV + 8 * grp;
-
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      // scores of key tiles KA (query tiles 2p, 2p + 1 from KA on) and, for
-      // p = 1, KB: entry i of tile u holds t = 32p + 16u + 4grp + i, key l16
-      floatx4 sa[2] = {z4, z4}, sb[2] = {z4, z4};
-#pragma unroll
-      for (int ds = 0; ds < 4; ++ds) {
-        const bf16x8 ba = ld_lds16(kv + 16 * KA * ROWKV + 32 * ds);
-        const bf16x8 bb = p == 1 ? ld_lds16(kv + 16 * KB * ROWKV + 32 * ds) : ba;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int ti = 2 * p + u;
-          if (ti < KA) continue;  // query tile before the key tile: all masked
-          const bf16x8 a = ld_lds16(srow + (16 * ti + l16) * ROWKV + 32 * ds + 8 * grp);
-          sa[u] = mfma(a, ba, sa[u]);
-          if (p == 1 && ti >= KB) sb[u] = mfma(a, bb, sb[u]);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        if (2 * p + u == KA) sa[u] = causal_mask_t(sa[u], l16, grp);
-        if (2 * p + u == KB) sb[u] = causal_mask_t(sb[u], l16, grp);
-      }
-      const bf16x8 pa = pack_tiles(sa[0], sa[1]);
-      const bf16x8 pb = pack_tiles(sb[0], sb[1]);
-      // intra:  dV^T[n][s] += sum_t dO[t][n] X^T[t][s]  (SIDE 0)
-      //         dK^T[i][s] += sum_t Q[t][i] Y^T[t][s]   (SIDE 1)
-      // and R[i][n] += sum_t Q[t][i] dO[t][n] on this wave's tiles of R
-      if constexpr (SIDE == 0) {
-        bf16x8 qa[2];  // Q^T of row tiles 2 PAIR, 2 PAIR + 1
-#pragma unroll
-        for (int m = 0; m < 2; ++m) qa[m] = tr_operand(srow, p, 16 * (2 * PAIR + m), l16, grp);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const bf16x8 ot = tr_operand(scol, p, 16 * t, l16, grp);  // dO^T, column tile t
-          acc[0][t] = mfma(ot, pa, acc[0][t]);
-          if (p == 1) acc[1][t] = mfma(ot, pb, acc[1][t]);
-#pragma unroll
-          for (int m = 0; m < 2; ++m) racc[8 * m + t] = mfma(qa[m], ot, racc[8 * m + t]);
-        }
-      } else {
-        bf16x8 ob[4];  // dO^T of column tiles 4 PAIR .. 4 PAIR + 3
-#pragma unroll
-        for (int c = 0; c < 4; ++c) ob[c] = tr_operand(srow, p, 16 * (4 * PAIR + c), l16, grp);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const bf16x8 qt = tr_operand(scol, p, 16 * t, l16, grp);  // Q^T, row tile t
-          acc[0][t] = mfma(qt, pa, acc[0][t]);
-          if (p == 1) acc[1][t] = mfma(qt, pb, acc[1][t]);
-          if (t >= 4)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) racc[4 * (t - 4) + c] = mfma(qt, ob[c], racc[4 * (t - 4) + c]);
-        }
-      }
-    }
-
-    if (h == G - 1) {
-      // gradient rows of the block: tile t holds columns 16t + 4grp + {0..3} of a key
-      void* out = SIDE == 0 ? A.dvg : A.dk;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int64_t s = blk * C + 16 * (e ? KB : KA) + l16;
-        if (s < N) {
-#pragma unroll
-          for (int t = 0; t < 8; ++t)
-            store_row4<OUT_F32>(out, (int64_t(bg) * N + s) * DV + 16 * t + 4 * grp, acc[e][t]);
-        }
-      }
-      write_rt();
-      r_in = 0;
-      --blk;
-    } else {
-      ++r_in;
-    }
-  };
-
-  // Whole rounds of NS items, then the remainder outside the loop: a
-  // conditional step inside the loop would make the compiler assume, at the
-  // loop head, that the newest loads may be those of any slot, and wait for
-  // all loads in flight before each store.
-  int64_t n = 0;
-  for (; n + NS <= nitems; n += NS) {
-#pragma unroll
-    for (int i = 0; i < NS; ++i) step(slot[i]);
-  }
-#pragma unroll
-  for (int i = 0; i < NS - 1; ++i)
-    if (n + i < nitems) step(slot[i]);
-
-  if (A.ds_in != nullptr && seg == 0) {
-    float* so = A.ds_in + int64_t(bg) * DD;
-#pragma unroll
-    for (int m = 0; m < 16; ++m)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        so[(16 * r_row<SIDE, PAIR>(m) + 4 * grp + i) * DV + 16 * r_col<SIDE, PAIR>(m) + l16] = racc[m][i];
-  }
-}
-
-// Eight-wave form of the same split: on SIMD s, wave s holds the gradient
-// (dV or dK of two key tiles: scores, intra and inter products) and wave
-// s + 4 that SIMD's 16 tiles of R (their update and the bf16 copy), so one
-// wave's LDS waits overlap the other's matrix products.  256 registers per
-// wave; items move through 512 threads.
-template <bool OUT_F32, int SIDE, int PAIR, bool HELPER, int NS>
-__device__ __forceinline__ void bwd_kv_wave8h(const BwdArgs4& A, BwdSmem4& sm) {
-  constexpr int KA = PAIR, KB = 3 - PAIR;  // key tiles (KA < 2 <= KB)
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
-  const int seg = blockIdx.x % A.P;
-  const int bg = blockIdx.x / A.P;
-  const int b = bg / A.Hkv, g = bg % A.Hkv;
-  const int G = A.Hq / A.Hkv;
-  const int64_t N = A.N;
-  const int64_t blk0 = int64_t(seg) * A.blocks_per_seg;
-  const int64_t blk1 = blk0 + A.blocks_per_seg < A.nblocks ? blk0 + A.blocks_per_seg : A.nblocks;
-
-  const uint16_t* kh = A.k + int64_t(bg) * N * D;
-  const uint16_t* vh = A.v + int64_t(bg) * N * DV;
-  const uint16_t* qg = A.q + (int64_t(b) * A.Hq + int64_t(g) * G) * N * D;
-  const uint16_t* og = A.dout + (int64_t(b) * A.Hq + int64_t(g) * G) * N * DV;
-
-  // helper: R tile m holds rows 16 r_row(m) + 4grp + i, column 16 r_col(m) + l16
-  constexpr int NR = HELPER ? 16 : 1;
+  // state wave: R tile m holds rows 16 r_row(m) + 4grp + i, column 16 r_col(m) + l16
+  constexpr int NR = STATE ? 16 : 1;
   floatx4 racc[NR];
   auto write_rt = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -606,7 +179,7 @@ __device__ __forceinline__ void bwd_kv_wave8h(const BwdArgs4& A, BwdSmem4& sm) {
           &sm.rt[(16 * r_col<SIDE, PAIR>(m) + l16) * ROWST + 16 * r_row<SIDE, PAIR>(m) + 4 * grp]) =
           to_bf16x4(racc[m]);
   };
-  if constexpr (HELPER) {
+  if constexpr (STATE) {
     const float* r0 = A.rstarts ? A.rstarts + (int64_t(bg) * A.P + seg) * DD : nullptr;
 #pragma unroll
     for (int m = 0; m < NR; ++m)
@@ -641,11 +214,15 @@ __device__ __forceinline__ void bwd_kv_wave8h(const BwdArgs4& A, BwdSmem4& sm) {
   const floatx4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
   // gradient wave: acc[0][t] / acc[1][t] = dV^T (SIDE 0) or dK^T (SIDE 1) of
   // key tile KA / KB, rows 16t + 4grp + i, column 16 key + l16
-  constexpr int NA = HELPER ? 1 : 8;
+  constexpr int NA = STATE ? 1 : 8;
   floatx4 acc[2][NA];
   int64_t blk = blk1 - 1;
   int r_in = 0;
-  int kvb = 0, hlast = 1;  // as in bwd_kv_wave4
+  // Buffer of the current block's K/V and of the last query-head item.  Each
+  // item goes to the third buffer: the other two may still be read by waves
+  // that have not finished the previous item, and every earlier reader of the
+  // third one has passed the previous item's barrier.
+  int kvb = 0, hlast = 1;
 
   auto step = [&](PairRegs8& cur) __attribute__((always_inline)) {
     const int rows = int(N - blk * C < C ? N - blk * C : C);
@@ -655,7 +232,7 @@ __device__ __forceinline__ void bwd_kv_wave8h(const BwdArgs4& A, BwdSmem4& sm) {
     load_next(cur);
     if (r_in == 0) {
       kvb = nb;
-      if constexpr (!HELPER) {
+      if constexpr (!STATE) {
         // inter terms from the bf16 copy of R (the state after the later blocks)
         const uint16_t* kv = sm.t[nb][SIDE] + l16 * ROWKV + 8 * grp;  // K rows (SIDE 0) or V rows
 #pragma unroll
@@ -679,7 +256,7 @@ __device__ __forceinline__ void bwd_kv_wave8h(const BwdArgs4& A, BwdSmem4& sm) {
     const uint16_t* sq = sm.t[nb][0];
     const uint16_t* so = sm.t[nb][1];
 
-    if constexpr (HELPER) {
+    if constexpr (STATE) {
       // R[i][n] += sum_t Q[t][i] dO[t][n] on this SIMD's 16 tiles
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
@@ -772,7 +349,7 @@ __device__ __forceinline__ void bwd_kv_wave8h(const BwdArgs4& A, BwdSmem4& sm) {
   for (int i = 0; i < NS - 1; ++i)
     if (n + i < nitems) step(slot[i]);
 
-  if constexpr (HELPER) {
+  if constexpr (STATE) {
     if (A.ds_in != nullptr && seg == 0) {
       float* so = A.ds_in + int64_t(bg) * DD;
 #pragma unroll
@@ -785,29 +362,19 @@ __device__ __forceinline__ void bwd_kv_wave8h(const BwdArgs4& A, BwdSmem4& sm) {
 }
 
 template <bool OUT_F32, int NS>
-__global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel8h(BwdArgs4 args) {
-  __shared__ BwdSmem4 sm;
+__global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(BwdArgs args) {
+  __shared__ BwdSmem sm;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   switch (w) {
-    case 0: bwd_kv_wave8h<OUT_F32, 0, 0, false, NS>(args, sm); break;
-    case 1: bwd_kv_wave8h<OUT_F32, 0, 1, false, NS>(args, sm); break;
-    case 2: bwd_kv_wave8h<OUT_F32, 1, 0, false, NS>(args, sm); break;
-    case 3: bwd_kv_wave8h<OUT_F32, 1, 1, false, NS>(args, sm); break;
-    case 4: bwd_kv_wave8h<OUT_F32, 0, 0, true, NS>(args, sm); break;
-    case 5: bwd_kv_wave8h<OUT_F32, 0, 1, true, NS>(args, sm); break;
-    case 6: bwd_kv_wave8h<OUT_F32, 1, 0, true, NS>(args, sm); break;
-    default: bwd_kv_wave8h<OUT_F32, 1, 1, true, NS>(args, sm); break;
+    case 0: bwd_kv_wave<OUT_F32, 0, 0, false, NS>(args, sm); break;
+    case 1: bwd_kv_wave<OUT_F32, 0, 1, false, NS>(args, sm); break;
+    case 2: bwd_kv_wave<OUT_F32, 1, 0, false, NS>(args, sm); break;
+    case 3: bwd_kv_wave<OUT_F32, 1, 1, false, NS>(args, sm); break;
+    case 4: bwd_kv_wave<OUT_F32, 0, 0, true, NS>(args, sm); break;
+    case 5: bwd_kv_wave<OUT_F32, 0, 1, true, NS>(args, sm); break;
+    case 6: bwd_kv_wave<OUT_F32, 1, 0, true, NS>(args, sm); break;
+    default: bwd_kv_wave<OUT_F32, 1, 1, true, NS>(args, sm); break;
   }
-}
-
-template <bool OUT_F32, int NS>
-__global__ __launch_bounds__(kThreads4, 1) void bwd_kv_kernel4(BwdArgs4 args) {
-  __shared__ BwdSmem4 sm;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (w == 0) bwd_kv_wave4<OUT_F32, 0, 0, NS>(args, sm);
-  else if (w == 1) bwd_kv_wave4<OUT_F32, 0, 1, NS>(args, sm);
-  else if (w == 2) bwd_kv_wave4<OUT_F32, 1, 0, NS>(args, sm);
-  else bwd_kv_wave4<OUT_F32, 1, 1, NS>(args, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -1106,28 +673,12 @@ hipError_t launch_bwd_kv(const void* q, const void* k, const void* v, const void
                          ds_in, int(Hq), int(Hkv), N, plan.nblocks, plan.blocks_per_seg, plan.P);
     return hipGetLastError();
   }
-#ifdef LA_BWD_EIGHT_WAVES
+  const BwdArgs args{q16, k16, v16, o16, dk, dvg, rs, ds_in, int(Hq), int(Hkv), N, plan.nblocks,
+                     plan.blocks_per_seg, plan.P};
   if (out_f32)
-    hipLaunchKernelGGL((bwd_kv_kernel8<true, kSlots>), grid, dim3(kThreads), 0, stream, q16, k16, v16, o16, dk, dvg,
-                       rs, ds_in, int(Hq), int(Hkv), N, plan.nblocks, plan.blocks_per_seg, plan.P);
+    hipLaunchKernelGGL((bwd_kv_kernel<true, kSlots>), grid, dim3(kThreads), 0, stream, args);
   else
-    hipLaunchKernelGGL((bwd_kv_kernel8<false, kSlots>), grid, dim3(kThreads), 0, stream, q16, k16, v16, o16, dk, dvg,
-                       rs, ds_in, int(Hq), int(Hkv), N, plan.nblocks, plan.blocks_per_seg, plan.P);
-#else
-  const BwdArgs4 args{q16, k16, v16, o16, dk, dvg, rs, ds_in, int(Hq), int(Hkv), N, plan.nblocks,
-                      plan.blocks_per_seg, plan.P};
-#ifdef LA_BWD_HELPER
-  if (out_f32)
-    hipLaunchKernelGGL((bwd_kv_kernel8h<true, LA_BWD_SLOTS4>), grid, dim3(kThreads), 0, stream, args);
-  else
-    hipLaunchKernelGGL((bwd_kv_kernel8h<false, LA_BWD_SLOTS4>), grid, dim3(kThreads), 0, stream, args);
-#else
-  if (out_f32)
-    hipLaunchKernelGGL((bwd_kv_kernel4<true, LA_BWD_SLOTS4>), grid, dim3(kThreads4), 0, stream, args);
-  else
-    hipLaunchKernelGGL((bwd_kv_kernel4<false, LA_BWD_SLOTS4>), grid, dim3(kThreads4), 0, stream, args);
-#endif
-#endif
+    hipLaunchKernelGGL((bwd_kv_kernel<false, kSlots>), grid, dim3(kThreads), 0, stream, args);
   return hipGetLastError();
 }
 
