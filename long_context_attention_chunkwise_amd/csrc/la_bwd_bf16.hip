@@ -378,14 +378,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(BwdArgs args) {
 }
 
 // ---------------------------------------------------------------------------
-// Head size 64 (d = dv = 64): the same reverse recurrence with four waves, one
-// per SIMD.  Wave w owns columns [16w, 16w+16) of dV, dK and R and computes
-// both score tiles of key tile w for all four query tiles, X^T = Q K^T and
-// Y^T = dO V^T, published as the same bf16 operand packs.  The K/V pair and
-// each head's (Q, dO) pair form one stream of 16 KiB items over two register
-// slots; LDS: four 64 x 64 tiles (160-byte rows), the bf16 copy of R and the
-// packs = 65 KiB, so two workgroups share a compute unit (the host plans two
-// segments per unit at this head size).
+// Head size 64 (d = dv = 64), column-split form, used for one query head per
+// KV head: four waves, one per SIMD.  Wave w owns columns [16w, 16w+16) of
+// dV, dK and R and computes both score tiles of key tile w for all four query
+// tiles, X^T = Q K^T and Y^T = dO V^T, published in LDS as bf16 operand packs
+// that every wave reads for its columns (three barriers per query head).  The
+// K/V pair and each head's (Q, dO) pair form one stream of 16 KiB items over
+// two register slots; the K/V item is stored without a barrier of its own,
+// its inter products run with the block's first head.  LDS: four 64 x 64
+// tiles (160-byte rows), the bf16 copy of R and the packs = 65 KiB, so two
+// workgroups share a compute unit (the host plans two segments per unit at
+// this head size).
 // ---------------------------------------------------------------------------
 constexpr int H64 = 64;
 constexpr int ROW64 = H64 + 16;  // LDS row pitch of the 64-wide tiles (elements)
@@ -598,6 +601,226 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel_hd64(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Head size 64, split like the head-size-128 kernel's gradient waves: four
+// waves, each owning one kind of gradient for two key tiles of the block
+// (waves 0 and 1: dV^T of key tiles {0, 3} and {1, 2}; waves 2 and 3: dK^T of
+// the same pairs), computing the score tiles of its own keys in registers.
+// At this head size R (64 x 64, float32) is small enough to live in the same
+// waves: 4 tiles each (the dV waves row tile PAIR, all columns; the dK waves
+// row tiles 2..3 of column tiles 2 PAIR, 2 PAIR + 1), updated with the
+// operands of their intra products.  Every wave does 34 matrix products per
+// query head.  Items (16 KiB) pass through two register slots and three LDS
+// buffers (one barrier per item); LDS 69 KiB, so two workgroups share a
+// compute unit (the host plans two segments per unit at this head size).
+// ---------------------------------------------------------------------------
+struct __align__(16) BwdSmemH64 {
+  uint16_t t[3][2][C * ROW64];  // three item buffers of two [64][64] tiles
+  uint16_t rt[H64 * RST64];     // bf16 copy of R, n-major
+};
+
+template <int SIDE, int PAIR>
+__device__ constexpr int r_row64(int m) { return SIDE == 0 ? PAIR : 2 + m / 2; }
+template <int SIDE, int PAIR>
+__device__ constexpr int r_col64(int m) { return SIDE == 0 ? m : 2 * PAIR + m % 2; }
+
+template <bool OUT_F32, int SIDE, int PAIR, int NS>
+__device__ __forceinline__ void bwd_kv_wave64(const BwdArgs& A, BwdSmemH64& sm) {
+  constexpr int KA = PAIR, KB = 3 - PAIR;  // key tiles (KA < 2 <= KB)
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+  const int seg = blockIdx.x % A.P;
+  const int bg = blockIdx.x / A.P;
+  const int b = bg / A.Hkv, g = bg % A.Hkv;
+  const int G = A.Hq / A.Hkv;
+  const int64_t N = A.N;
+  const int64_t blk0 = int64_t(seg) * A.blocks_per_seg;
+  const int64_t blk1 = blk0 + A.blocks_per_seg < A.nblocks ? blk0 + A.blocks_per_seg : A.nblocks;
+
+  const uint16_t* kh = A.k + int64_t(bg) * N * H64;
+  const uint16_t* vh = A.v + int64_t(bg) * N * H64;
+  const uint16_t* qg = A.q + (int64_t(b) * A.Hq + int64_t(g) * G) * N * H64;
+  const uint16_t* og = A.dout + (int64_t(b) * A.Hq + int64_t(g) * G) * N * H64;
+
+  // R tile m: rows 16 r_row64(m) + 4grp + i, column 16 r_col64(m) + l16
+  const float* r0 = A.rstarts ? A.rstarts + (int64_t(bg) * A.P + seg) * DD64 : nullptr;
+  floatx4 racc[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      racc[m][i] = r0 ? r0[(16 * r_row64<SIDE, PAIR>(m) + 4 * grp + i) * H64 + 16 * r_col64<SIDE, PAIR>(m) + l16]
+                      : 0.0f;
+  auto write_rt = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      *reinterpret_cast<bf16x4*>(
+          &sm.rt[(16 * r_col64<SIDE, PAIR>(m) + l16) * RST64 + 16 * r_row64<SIDE, PAIR>(m) + 4 * grp]) =
+          to_bf16x4(racc[m]);
+  };
+  write_rt();
+
+  const int per_blk = G + 1;
+  int64_t ld_blk = blk1 - 1;
+  int ld_r = 0;
+  auto load_next = [&](PairRegs64& r) __attribute__((always_inline)) {
+    const int rows = int(N - ld_blk * C < C ? N - ld_blk * C : C);
+    const uint16_t* a = ld_r == 0 ? kh : qg + int64_t(ld_r - 1) * N * H64;
+    const uint16_t* bb = ld_r == 0 ? vh : og + int64_t(ld_r - 1) * N * H64;
+    load_pair64(r, a + ld_blk * C * H64, bb + ld_blk * C * H64, rows, tid);
+    if (ld_blk > blk0 || ld_r < G) {
+      if (++ld_r == per_blk) {
+        ld_r = 0;
+        --ld_blk;
+      }
+    }
+  };
+
+  const int64_t nitems = (blk1 - blk0) * per_blk;
+  PairRegs64 slot[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i)
+    if (i < nitems) load_next(slot[i]);
+
+  const floatx4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
+  // acc[0][t] / acc[1][t]: dV^T (SIDE 0) or dK^T (SIDE 1) of key tile KA / KB,
+  // rows 16t + 4grp + i (column of dV or dK), column 16 key + l16 (key)
+  floatx4 acc[2][4];
+  int64_t blk = blk1 - 1;
+  int r_in = 0;
+  int kvb = 0, hlast = 1;  // as in bwd_kv_wave: each item goes to the third buffer
+
+  auto step = [&](PairRegs64& cur) __attribute__((always_inline)) {
+    const int rows = int(N - blk * C < C ? N - blk * C : C);
+    const int nb = 3 - kvb - hlast;
+    store_pair64(cur, sm.t[nb][0], sm.t[nb][1], rows, tid);
+    __syncthreads();  // the item is in LDS
+    load_next(cur);
+    if (r_in == 0) {
+      // a block's K/V: start the gradients with the inter terms from the bf16
+      // copy of R (the state after the later blocks)
+      kvb = nb;
+      const uint16_t* kv = sm.t[nb][SIDE] + l16 * ROW64 + 8 * grp;  // K rows (SIDE 0) or V rows
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 ba = ld_lds16(kv + 16 * KA * ROW64 + 32 * kk);
+        const bf16x8 bb = ld_lds16(kv + 16 * KB * ROW64 + 32 * kk);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const bf16x8 r = SIDE == 0 ? ld_lds16(sm.rt + (16 * t + l16) * RST64 + 32 * kk + 8 * grp)
+                                     : tr_operand_lin(sm.rt, 32 * kk, 16 * t, l16, grp, RST64);
+          acc[0][t] = mfma(r, ba, kk ? acc[0][t] : z4);
+          acc[1][t] = mfma(r, bb, kk ? acc[1][t] : z4);
+        }
+      }
+      r_in = 1;
+      return;
+    }
+    const int h = r_in - 1;
+    hlast = nb;
+    const uint16_t* srow = sm.t[nb][SIDE];      // score rows: Q (SIDE 0) or dO
+    const uint16_t* scol = sm.t[nb][1 - SIDE];  // contraction operands: dO (SIDE 0) or Q
+    const uint16_t* kv = sm.t[kvb][SIDE] + l16 * ROW64 + 8 * grp;
+
+    // all score tiles of the head: sc[ti] of key tile KA for query tiles
+    // ti = KA..3, sb[u] of KB for query tiles 2 + u; entry i of a tile holds
+    // t = 16ti + 4grp + i, key l16
+    floatx4 sc[4] = {z4, z4, z4, z4}, sb[2] = {z4, z4};
+#pragma unroll
+    for (int ds = 0; ds < 2; ++ds) {
+      const bf16x8 ba = ld_lds16(kv + 16 * KA * ROW64 + 32 * ds);
+      const bf16x8 bb = ld_lds16(kv + 16 * KB * ROW64 + 32 * ds);
+#pragma unroll
+      for (int ti = KA; ti < 4; ++ti) {
+        const bf16x8 a = ld_lds16(srow + (16 * ti + l16) * ROW64 + 32 * ds + 8 * grp);
+        sc[ti] = mfma(a, ba, sc[ti]);
+        if (ti >= KB) sb[ti - 2] = mfma(a, bb, sb[ti - 2]);
+      }
+    }
+    sc[KA] = causal_mask_t(sc[KA], l16, grp);
+    sb[KB - 2] = causal_mask_t(sb[KB - 2], l16, grp);
+    const bf16x8 pa[2] = {pack_tiles(sc[0], sc[1]), pack_tiles(sc[2], sc[3])};
+    const bf16x8 pb = pack_tiles(sb[0], sb[1]);
+    // intra:  dV^T[n][s] += sum_t dO[t][n] X^T[t][s]  (SIDE 0)
+    //         dK^T[i][s] += sum_t Q[t][i] Y^T[t][s]   (SIDE 1)
+    // and R[i][n] += sum_t Q[t][i] dO[t][n] on this wave's tiles of R
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      if constexpr (SIDE == 0) {
+        const bf16x8 qa = tr_operand(srow, p, 16 * PAIR, l16, grp, 4, ROW64);  // Q^T, row tile PAIR
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const bf16x8 ot = tr_operand(scol, p, 16 * t, l16, grp, 4, ROW64);  // dO^T, column tile t
+          acc[0][t] = mfma(ot, pa[p], acc[0][t]);
+          if (p == 1) acc[1][t] = mfma(ot, pb, acc[1][t]);
+          racc[t] = mfma(qa, ot, racc[t]);
+        }
+      } else {
+        bf16x8 ob[2];  // dO^T of column tiles 2 PAIR, 2 PAIR + 1
+#pragma unroll
+        for (int c = 0; c < 2; ++c) ob[c] = tr_operand(srow, p, 16 * (2 * PAIR + c), l16, grp, 4, ROW64);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const bf16x8 qt = tr_operand(scol, p, 16 * t, l16, grp, 4, ROW64);  // Q^T, row tile t
+          acc[0][t] = mfma(qt, pa[p], acc[0][t]);
+          if (p == 1) acc[1][t] = mfma(qt, pb, acc[1][t]);
+          if (t >= 2)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) racc[2 * (t - 2) + c] = mfma(qt, ob[c], racc[2 * (t - 2) + c]);
+        }
+      }
+    }
+
+    if (h == G - 1) {
+      // gradient rows of the block: tile t holds columns 16t + 4grp + {0..3} of a key
+      void* out = SIDE == 0 ? A.dvg : A.dk;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int64_t s = blk * C + 16 * (e ? KB : KA) + l16;
+        if (s < N) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            store_row4<OUT_F32>(out, (int64_t(bg) * N + s) * H64 + 16 * t + 4 * grp, acc[e][t]);
+        }
+      }
+      write_rt();
+      r_in = 0;
+      --blk;
+    } else {
+      ++r_in;
+    }
+  };
+
+  // whole rounds of NS items in the loop, the remainder after it (as in bwd_kv_wave)
+  int64_t n = 0;
+  for (; n + NS <= nitems; n += NS) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) step(slot[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i)
+    if (n + i < nitems) step(slot[i]);
+
+  if (A.ds_in != nullptr && seg == 0) {
+    float* so = A.ds_in + int64_t(bg) * DD64;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        so[(16 * r_row64<SIDE, PAIR>(m) + 4 * grp + i) * H64 + 16 * r_col64<SIDE, PAIR>(m) + l16] = racc[m][i];
+  }
+}
+
+template <bool OUT_F32, int NS>
+__global__ __launch_bounds__(256, 2) void bwd_kv_kernel64(BwdArgs args) {
+  __shared__ BwdSmemH64 sm;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (w == 0) bwd_kv_wave64<OUT_F32, 0, 0, NS>(args, sm);
+  else if (w == 1) bwd_kv_wave64<OUT_F32, 0, 1, NS>(args, sm);
+  else if (w == 2) bwd_kv_wave64<OUT_F32, 1, 0, NS>(args, sm);
+  else bwd_kv_wave64<OUT_F32, 1, 1, NS>(args, sm);
+}
+
 // rstarts[c][j] = ds_out[c] + sum over segments i > j and the G query heads of
 // chain c of the pre-pass partials (partial index ((c G + h)(P - 1) + i - 1) R
 // + r), in a fixed order; E elements per state (d dv, a multiple of 256).
@@ -664,17 +887,28 @@ hipError_t launch_bwd_kv(const void* q, const void* k, const void* v, const void
   const auto* k16 = static_cast<const uint16_t*>(k);
   const auto* v16 = static_cast<const uint16_t*>(v);
   const auto* o16 = static_cast<const uint16_t*>(dout);
-  if (hd == 64) {
-    if (out_f32)
-      hipLaunchKernelGGL(bwd_kv_kernel_hd64<true>, grid, dim3(256), 0, stream, q16, k16, v16, o16, dk, dvg, rs, ds_in,
-                         int(Hq), int(Hkv), N, plan.nblocks, plan.blocks_per_seg, plan.P);
-    else
-      hipLaunchKernelGGL(bwd_kv_kernel_hd64<false>, grid, dim3(256), 0, stream, q16, k16, v16, o16, dk, dvg, rs,
-                         ds_in, int(Hq), int(Hkv), N, plan.nblocks, plan.blocks_per_seg, plan.P);
-    return hipGetLastError();
-  }
   const BwdArgs args{q16, k16, v16, o16, dk, dvg, rs, ds_in, int(Hq), int(Hkv), N, plan.nblocks,
                      plan.blocks_per_seg, plan.P};
+  if (hd == 64) {
+    // one query head per KV head: the column-split kernel, which stores the
+    // K/V item without a barrier and runs the inter products with the head
+    // (measured 11.8 against 12.3 ms per 1M-token backward at 32 over 32
+    // heads); groups of two or more: the key-tile-pair kernel (24.2 against
+    // 25.8 ms at 128 over 32 heads)
+    if (Hq == Hkv) {
+      if (out_f32)
+        hipLaunchKernelGGL(bwd_kv_kernel_hd64<true>, grid, dim3(256), 0, stream, q16, k16, v16, o16, dk, dvg, rs,
+                           ds_in, int(Hq), int(Hkv), N, plan.nblocks, plan.blocks_per_seg, plan.P);
+      else
+        hipLaunchKernelGGL(bwd_kv_kernel_hd64<false>, grid, dim3(256), 0, stream, q16, k16, v16, o16, dk, dvg, rs,
+                           ds_in, int(Hq), int(Hkv), N, plan.nblocks, plan.blocks_per_seg, plan.P);
+    } else if (out_f32) {
+      hipLaunchKernelGGL((bwd_kv_kernel64<true, kSlots>), grid, dim3(256), 0, stream, args);
+    } else {
+      hipLaunchKernelGGL((bwd_kv_kernel64<false, kSlots>), grid, dim3(256), 0, stream, args);
+    }
+    return hipGetLastError();
+  }
   if (out_f32)
     hipLaunchKernelGGL((bwd_kv_kernel<true, kSlots>), grid, dim3(kThreads), 0, stream, args);
   else
