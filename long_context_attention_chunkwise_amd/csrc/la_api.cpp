@@ -181,7 +181,17 @@ BwdPlan plan_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, 
   P = (p.nblocks + p.blocks_per_seg - 1) / p.blocks_per_seg;
   p.P = static_cast<int>(P);
 
-  if (P > 1) {
+  // Head size 128 with four query heads per dQ workgroup and the same
+  // segments in both passes: the dQ pass sums q^T dO per segment itself, so
+  // dO is read once for both (a separate pre-pass reads 7/8 of Q and dO).
+  p.fused = P > 1 && d == 128 && p.fwd.hd == 128 && p.fwd.gw == 4 && !p.fwd.solo && p.fwd.P == P &&
+            p.fwd.blocks_per_seg == p.blocks_per_seg;
+  if (p.fused) {
+    p.blocks_per_part = p.blocks_per_seg;
+    p.R = 1;
+    p.partial_floats = size_t(B * Hkv * p.fwd.subgroups) * size_t(P - 1) * size_t(d * dv);
+    p.rstart_floats = size_t(chains) * size_t(P) * size_t(d * dv);
+  } else if (P > 1) {
     // Pre-pass over (Q, dO) of every query head and every segment but the
     // first.  Parts per segment: the count with the least (rounds of resident
     // workgroups, two per compute unit at head size 128 and three at 64) x
@@ -530,9 +540,15 @@ la_status la_backward(const void* q, const void* k, const void* v, const void* g
   }
   if (plan.fwd.use_starts && la::launch_segment_states(v, k, s_t, B, Hkv, N, plan.fwd, ws_fwd, hs) != hipSuccess)
     return LA_ERR_HIP;
-  if (la::launch_fwd_bf16(grad_o, v, k, grad_q, out_f32, s_t, nullptr, B, Hq, Hkv, N, plan.fwd, ws_fwd, hs) !=
-      hipSuccess)
+  if (plan.fused) {
+    // ... and the per-segment sums of q^T dO that start the reverse recurrence
+    if (la::launch_fwd_bf16_rsum(grad_o, v, k, grad_q, out_f32, B, Hq, Hkv, N, plan.fwd, ws_fwd, q, ws_kv, hs) !=
+        hipSuccess)
+      return LA_ERR_HIP;
+  } else if (la::launch_fwd_bf16(grad_o, v, k, grad_q, out_f32, s_t, nullptr, B, Hq, Hkv, N, plan.fwd, ws_fwd,
+                                 hs) != hipSuccess) {
     return LA_ERR_HIP;
+  }
   // dK, dV, ds_in: the reverse recurrence.
   if (la::launch_bwd_kv(q, k, v, grad_o, grad_k, grad_v, out_f32, grad_s_out, grad_s_in, B, Hq, Hkv, N, plan,
                         ws_kv, hs) != hipSuccess)

@@ -873,12 +873,18 @@ hipError_t launch_bwd_kv(const void* q, const void* k, const void* v, const void
   float* rstarts = partial + plan.partial_floats;
   const float* rs = ds_out;  // one segment: it starts from ds_out
   if (plan.P > 1) {
-    hipError_t e = launch_state_parts(q, dout, partial, B * Hq, N, plan.nblocks, plan.blocks_per_seg,
-                                      plan.blocks_per_part, plan.P, plan.R, 1, hd, stream);
-    if (e != hipSuccess) return e;
+    // fused: the dQ pass has written one partial per (chain, query-head
+    // subgroup, segment); else the pre-pass writes R per query head
+    int scan_g = plan.fwd.subgroups;
+    if (!plan.fused) {
+      hipError_t e = launch_state_parts(q, dout, partial, B * Hq, N, plan.nblocks, plan.blocks_per_seg,
+                                        plan.blocks_per_part, plan.P, plan.R, 1, hd, stream);
+      if (e != hipSuccess) return e;
+      scan_g = int(Hq / Hkv);
+    }
     hipLaunchKernelGGL(scan_rstarts, dim3(unsigned(B * Hkv * E / 256)), dim3(256), 0, stream, partial, rstarts,
-                       ds_out, int(Hq / Hkv), plan.P, plan.R, E);
-    e = hipGetLastError();
+                       ds_out, scan_g, plan.P, plan.R, E);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     rs = rstarts;
   }

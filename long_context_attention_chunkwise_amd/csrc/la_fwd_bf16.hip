@@ -391,14 +391,27 @@ __device__ __forceinline__ void store_kv_tile(const KVTile<HD>& r, uint16_t* ks,
 // o may be q itself (in-place output): q and o are therefore not restrict.
 // Each query row is loaded into the wave's operand registers before that
 // wave writes the same output row, and never read again.
-template <bool OUT_F32, int FL, int HD = 128, bool PARTIAL = false>
+//
+// RS (the backward's dQ pass, which runs this kernel over queries dO, keys V
+// and values K): the workgroup also sums R = sum_t x_t^T q_t over its segment
+// and the group's query heads, x being a second [head][N][HD] input (the
+// forward's queries), and writes R to rpart (float32, HD x HD, entry [i][j] =
+// sum x[t][i] q[t][j]) at index chain (P - 1) + seg - 1; segment 0 skips it.
+// The reverse recurrence starts each segment from the sum of these over the
+// later segments, so the backward reads dO once for dQ and R together.  Wave h
+// writes head h's x and q rows to LDS, half a block at a time, and wave w sums
+// columns [w HD/4, (w+1) HD/4) of R over all four heads with the same
+// transpose-load products as the state update.  One more barrier per block:
+// the two halves take two write/read rounds of the staging tiles.
+template <bool OUT_F32, int FL, int HD = 128, bool PARTIAL = false, bool RS = false>
 __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
     const uint16_t* q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     void* o, const float* starts, const float* s_in, float* s_out, int Hq, int Hkv, int subgroups,
     int64_t N, int64_t nblocks, int64_t blocks_per_seg, int P, const float* zstarts, const float* z_in,
-    float* z_out, float eps, int gw) {
+    float* z_out, float eps, int gw, const uint16_t* __restrict__ qx, float* __restrict__ rpart) {
   constexpr bool kN = (FL & kNorm) != 0;
   constexpr bool kR = (FL & kRelu) != 0;
+  static_assert(!RS || (FL == 0 && !PARTIAL), "R sums: plain forward over four query heads");
   // Head size HD = d = dv (64 or 128): 32-wide chunks of d, 16-row tiles of
   // the state, 32-column output quarters, state columns per wave and their
   // 16-column tiles; LDS pitches as for 128 (16 and 8 elements of padding).
@@ -409,6 +422,8 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
   __shared__ __align__(16) uint16_t vs[C * RKV];
   __shared__ __align__(16) uint16_t st[HD * RST];
   __shared__ __align__(16) float zs[kN ? HD : 4];
+  // RS staging: tile 2h holds x rows, tile 2h + 1 q rows of head h (32 rows)
+  __shared__ __align__(16) uint16_t xs[RS ? 8 * 32 * RKV : 8];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
@@ -420,12 +435,14 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
   const int G = Hq / Hkv;
   const int64_t blk0 = int64_t(seg) * blocks_per_seg;
   const int64_t blk1 = blk0 + blocks_per_seg < nblocks ? blk0 + blocks_per_seg : nblocks;
+  const bool rs_on = RS && seg > 0;
 
   // query heads of this workgroup: 4, or gw when PARTIAL (waves w >= gw idle)
   const int gsz = PARTIAL ? gw : 4;
   const bool act = !PARTIAL || __builtin_amdgcn_readfirstlane(w) < gsz;
   const int64_t head = int64_t(b) * Hq + int64_t(g) * G + int64_t(sub) * gsz + (act ? w : 0);
   const uint16_t* qh = q + head * N * HD;
+  const uint16_t* xh = RS ? qx + head * N * HD : nullptr;
   const uint16_t* kh = k + int64_t(bg) * N * HD;
   const uint16_t* vh = v + int64_t(bg) * N * HD;
   const int nlane = 8 * (l16 >> 2) + (l16 & 3);
@@ -456,9 +473,13 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
   }
 
   bf16x8 qa[4][NDS];
+  bf16x8 xa[4][NDS];        // RS: x rows, in qa's layout
+  floatx4 racc[NJ][NDT];    // RS: R[16dt + 4grp + i][WC w + 16jn + l16]
+  if constexpr (RS)
+    for (int jn = 0; jn < NJ; ++jn)
+      for (int dt = 0; dt < NDT; ++dt) racc[jn][dt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   KVTile<HD> kv;
-  auto load_block = [&](int64_t blk) {
-    load_kv_tile<HD>(kv, kh, vh, blk, N, tid);
+  auto load_q = [&](int64_t blk) {
     if (act) {
       for (int ti = 0; ti < 4; ++ti) {
         const int64_t t = blk * C + 16 * ti + l16;
@@ -470,129 +491,216 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
         for (int ds = 0; ds < NDS; ++ds) qa[ti][ds] = zero_bf16x8();
     }
   };
-  if (blk0 < blk1) load_block(blk0);
-  for (int64_t blk = blk0; blk < blk1; ++blk) {
-    if constexpr (kR) {
-      for (int i = 0; i < HD / 32; ++i) kv.k[i] = relu_bf16x8(kv.k[i]);
-      for (int ti = 0; ti < 4; ++ti)
-        for (int ds = 0; ds < NDS; ++ds) qa[ti][ds] = relu_bf16x8(qa[ti][ds]);
-    }
-    store_kv_tile<HD>(kv, ks, vs, tid);
-    __syncthreads();  // K, V and the state of the previous block are in LDS
-
-    // scores, one P^T tile at a time, packed to bf16 operands right away
-    const floatx4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (act) {
-    bf16x8 pop[4][2];
-    float den[4], inv[4];  // normaliser of row 16ti + l16 (kNorm only)
-    (void)den;
-    (void)inv;
-    for (int ti = 0; ti < 4; ++ti) {
-      floatx4 pt[4];
-      for (int si = 0; si <= ti; ++si) {
-        pt[si] = z4;
-        for (int ds = 0; ds < NDS; ++ds)
-          pt[si] = mfma(ld_lds16(ks + (16 * si + l16) * RKV + 32 * ds + 8 * grp), qa[ti][ds], pt[si]);
-      }
-      pt[ti] = causal_mask(pt[ti], l16, grp);
-      if constexpr (kN) {
-        // this lane's share of sum_s P^T[s][t] for t = 16ti + l16
-        float sum = 0.0f;
-        for (int si = 0; si <= ti; ++si) sum += (pt[si][0] + pt[si][1]) + (pt[si][2] + pt[si][3]);
-        den[ti] = sum;
-      }
-      pop[ti][0] = pack_tiles(pt[0], ti >= 1 ? pt[1] : z4);
-      if (ti >= 2) pop[ti][1] = pack_tiles(pt[2], ti == 3 ? pt[3] : z4);
-    }
-    if constexpr (kN) {
-      // earlier tokens: phi(q_t) . z; lane (l16, grp) holds q_t entries 32ds + 8grp + j
-      for (int ds = 0; ds < NDS; ++ds) {
-        const floatx4 za = *reinterpret_cast<const floatx4*>(&zs[32 * ds + 8 * grp]);
-        const floatx4 zb = *reinterpret_cast<const floatx4*>(&zs[32 * ds + 8 * grp + 4]);
-        for (int ti = 0; ti < 4; ++ti) {
-          float dsum = 0.0f;
-          for (int j = 0; j < 4; ++j)
-            dsum += float(qa[ti][ds][j]) * za[j] + float(qa[ti][ds][j + 4]) * zb[j];
-          den[ti] += dsum;
-        }
-      }
-      for (int ti = 0; ti < 4; ++ti) {
-        float x = den[ti];
-        x += __shfl_xor(x, 16);
-        x += __shfl_xor(x, 32);
-        inv[ti] = 1.0f / (x + eps);
-      }
-    }
-
-    // Output columns in quarters of 32 (one interleaved column pair m), so
-    // only 32 accumulator registers are live at a time.
-    for (int m = 0; m < NM; ++m) {
-      floatx4 acc[2][4];
-      for (int h2 = 0; h2 < 2; ++h2)
-        for (int ti = 0; ti < 4; ++ti) acc[h2][ti] = z4;
-      // inter: O^T[n][t] = sum_d S[d][n] Q[t][d] (state before the block)
+  // RS: x rows 32 half .. 32 half + 31 of block blk
+  auto load_x_half = [&](int64_t blk, int half) {
+    for (int tj = 0; tj < 2; ++tj) {
+      const int ti = 2 * half + tj;
+      const int64_t t = blk * C + 16 * ti + l16;
       for (int ds = 0; ds < NDS; ++ds)
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const bf16x8 sa = ld_lds16(st + (32 * m + 4 * h2 + nlane) * RST + 32 * ds + 8 * grp);
-          for (int ti = 0; ti < 4; ++ti) acc[h2][ti] = mfma(sa, qa[ti][ds], acc[h2][ti]);
-        }
-      // intra: O^T[n][t] += sum_s V[s][n] P^T[s][t]
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const bf16x8 va0 = tr_operand(vs, 0, 32 * m + 4 * h2, l16, grp, 8, RKV);
-        const bf16x8 va1 = tr_operand(vs, 1, 32 * m + 4 * h2, l16, grp, 8, RKV);
-        for (int ti = 0; ti < 4; ++ti) acc[h2][ti] = mfma(va0, pop[ti][0], acc[h2][ti]);
-        acc[h2][2] = mfma(va1, pop[2][1], acc[h2][2]);
-        acc[h2][3] = mfma(va1, pop[3][1], acc[h2][3]);
+        xa[ti][ds] = (t < N) ? ld_global16(xh + t * HD + 32 * ds + 8 * grp) : zero_bf16x8();
+    }
+  };
+  // RS: wave w stages rows 32 half .. 32 half + 31 of its head's x and q.
+  auto stage_half = [&](int half) {
+    uint16_t* xt = xs + (2 * w) * (32 * RKV);
+    uint16_t* qt = xt + 32 * RKV;
+    for (int tj = 0; tj < 2; ++tj)
+      for (int ds = 0; ds < NDS; ++ds) {
+        const int off = (16 * tj + l16) * RKV + 32 * ds + 8 * grp;
+        *reinterpret_cast<bf16x8*>(xt + off) = xa[2 * half + tj][ds];
+        *reinterpret_cast<bf16x8*>(qt + off) = qa[2 * half + tj][ds];
       }
-      if constexpr (kN)
-        for (int h2 = 0; h2 < 2; ++h2)
-          for (int ti = 0; ti < 4; ++ti)
-            for (int i = 0; i < 4; ++i) acc[h2][ti][i] *= inv[ti];
+  };
+  // RS: R[:, WC w : WC w + WC] += sum over the four heads of the staged
+  // x^T q (32 tokens: one token-contracting step).
+  auto r_sum_half = [&]() {
+    for (int h = 0; h < 4; ++h) {
+      const uint16_t* xt = xs + (2 * h) * (32 * RKV);
+      const uint16_t* qt = xt + 32 * RKV;
+      bf16x8 qb[NJ];
+      for (int jn = 0; jn < NJ; ++jn) qb[jn] = tr_operand(qt, 0, WC * w + 16 * jn, l16, grp, 4, RKV);
+      for (int dt = 0; dt < NDT; ++dt) {
+        const bf16x8 xt_op = tr_operand(xt, 0, 16 * dt, l16, grp, 4, RKV);
+        for (int jn = 0; jn < NJ; ++jn) racc[jn][dt] = mfma(xt_op, qb[jn], racc[jn][dt]);
+      }
+    }
+  };
+  // The block walk, compiled separately with and without the R sums so that
+  // segment 0 (no sums) keeps the plain kernel's registers.
+  auto walk = [&](auto ron) {
+    constexpr bool RON = decltype(ron)::value;
+    if (blk0 < blk1) {
+      load_kv_tile<HD>(kv, kh, vh, blk0, N, tid);
+      load_q(blk0);
+      if constexpr (RON) {
+        load_x_half(blk0, 0);
+        load_x_half(blk0, 1);
+      }
+    }
+    for (int64_t blk = blk0; blk < blk1; ++blk) {
+      if constexpr (kR) {
+        for (int i = 0; i < HD / 32; ++i) kv.k[i] = relu_bf16x8(kv.k[i]);
+        for (int ti = 0; ti < 4; ++ti)
+          for (int ds = 0; ds < NDS; ++ds) qa[ti][ds] = relu_bf16x8(qa[ti][ds]);
+      }
+      store_kv_tile<HD>(kv, ks, vs, tid);
+      if constexpr (RON) {
+        // With the R sums, the next block's K/V and first x half go out as
+        // soon as their registers are free (measured 0.4 ms faster per 1M-token
+        // backward than loading everything after the outputs).
+        stage_half(0);
+        if (blk + 1 < blk1) {
+          load_kv_tile<HD>(kv, kh, vh, blk + 1, N, tid);
+          load_x_half(blk + 1, 0);
+        }
+      }
+      __syncthreads();  // K, V and the state of the previous block are in LDS
+
+      // scores, one P^T tile at a time, packed to bf16 operands right away
+      const floatx4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (act) {
+      bf16x8 pop[4][2];
+      float den[4], inv[4];  // normaliser of row 16ti + l16 (kNorm only)
+      (void)den;
+      (void)inv;
       for (int ti = 0; ti < 4; ++ti) {
-        const int64_t t = blk * C + 16 * ti + l16;
-        if (t < N) {
-          const int64_t off = (head * N + t) * HD + 32 * m + 8 * grp;
-          if (OUT_F32) {
-            float* op = static_cast<float*>(o) + off;
-            *reinterpret_cast<floatx4*>(op) = acc[0][ti];
-            *reinterpret_cast<floatx4*>(op + 4) = acc[1][ti];
-          } else {
-            *reinterpret_cast<bf16x8*>(static_cast<uint16_t*>(o) + off) = pack_tiles(acc[0][ti], acc[1][ti]);
+        floatx4 pt[4];
+        for (int si = 0; si <= ti; ++si) {
+          pt[si] = z4;
+          for (int ds = 0; ds < NDS; ++ds)
+            pt[si] = mfma(ld_lds16(ks + (16 * si + l16) * RKV + 32 * ds + 8 * grp), qa[ti][ds], pt[si]);
+        }
+        pt[ti] = causal_mask(pt[ti], l16, grp);
+        if constexpr (kN) {
+          // this lane's share of sum_s P^T[s][t] for t = 16ti + l16
+          float sum = 0.0f;
+          for (int si = 0; si <= ti; ++si) sum += (pt[si][0] + pt[si][1]) + (pt[si][2] + pt[si][3]);
+          den[ti] = sum;
+        }
+        pop[ti][0] = pack_tiles(pt[0], ti >= 1 ? pt[1] : z4);
+        if (ti >= 2) pop[ti][1] = pack_tiles(pt[2], ti == 3 ? pt[3] : z4);
+      }
+      if constexpr (kN) {
+        // earlier tokens: phi(q_t) . z; lane (l16, grp) holds q_t entries 32ds + 8grp + j
+        for (int ds = 0; ds < NDS; ++ds) {
+          const floatx4 za = *reinterpret_cast<const floatx4*>(&zs[32 * ds + 8 * grp]);
+          const floatx4 zb = *reinterpret_cast<const floatx4*>(&zs[32 * ds + 8 * grp + 4]);
+          for (int ti = 0; ti < 4; ++ti) {
+            float dsum = 0.0f;
+            for (int j = 0; j < 4; ++j)
+              dsum += float(qa[ti][ds][j]) * za[j] + float(qa[ti][ds][j + 4]) * zb[j];
+            den[ti] += dsum;
+          }
+        }
+        for (int ti = 0; ti < 4; ++ti) {
+          float x = den[ti];
+          x += __shfl_xor(x, 16);
+          x += __shfl_xor(x, 32);
+          inv[ti] = 1.0f / (x + eps);
+        }
+      }
+
+      // Output columns in quarters of 32 (one interleaved column pair m), so
+      // only 32 accumulator registers are live at a time.
+      for (int m = 0; m < NM; ++m) {
+        floatx4 acc[2][4];
+        for (int h2 = 0; h2 < 2; ++h2)
+          for (int ti = 0; ti < 4; ++ti) acc[h2][ti] = z4;
+        // inter: O^T[n][t] = sum_d S[d][n] Q[t][d] (state before the block)
+        for (int ds = 0; ds < NDS; ++ds)
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const bf16x8 sa = ld_lds16(st + (32 * m + 4 * h2 + nlane) * RST + 32 * ds + 8 * grp);
+            for (int ti = 0; ti < 4; ++ti) acc[h2][ti] = mfma(sa, qa[ti][ds], acc[h2][ti]);
+          }
+        // intra: O^T[n][t] += sum_s V[s][n] P^T[s][t]
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const bf16x8 va0 = tr_operand(vs, 0, 32 * m + 4 * h2, l16, grp, 8, RKV);
+          const bf16x8 va1 = tr_operand(vs, 1, 32 * m + 4 * h2, l16, grp, 8, RKV);
+          for (int ti = 0; ti < 4; ++ti) acc[h2][ti] = mfma(va0, pop[ti][0], acc[h2][ti]);
+          acc[h2][2] = mfma(va1, pop[2][1], acc[h2][2]);
+          acc[h2][3] = mfma(va1, pop[3][1], acc[h2][3]);
+        }
+        if constexpr (kN)
+          for (int h2 = 0; h2 < 2; ++h2)
+            for (int ti = 0; ti < 4; ++ti)
+              for (int i = 0; i < 4; ++i) acc[h2][ti][i] *= inv[ti];
+        for (int ti = 0; ti < 4; ++ti) {
+          const int64_t t = blk * C + 16 * ti + l16;
+          if (t < N) {
+            const int64_t off = (head * N + t) * HD + 32 * m + 8 * grp;
+            if (OUT_F32) {
+              float* op = static_cast<float*>(o) + off;
+              *reinterpret_cast<floatx4*>(op) = acc[0][ti];
+              *reinterpret_cast<floatx4*>(op + 4) = acc[1][ti];
+            } else {
+              *reinterpret_cast<bf16x8*>(static_cast<uint16_t*>(o) + off) = pack_tiles(acc[0][ti], acc[1][ti]);
+            }
           }
         }
       }
-    }
-    }  // act
-    // The next block's loads go out now (Q operands are no longer needed), so
-    // they overlap the state update and the barriers.
-    if (blk + 1 < blk1) load_block(blk + 1);
-    __syncthreads();  // every wave has finished reading the state
-
-    // state update: S[:, WC w:WC w+WC] += K_b^T V_b, then its bf16 copy
-    {
-      bf16x8 vb[NJ][2];
-      for (int jn = 0; jn < NJ; ++jn)
-        for (int p = 0; p < 2; ++p) vb[jn][p] = tr_operand(vs, p, WC * w + 16 * jn, l16, grp, 4, RKV);
-      for (int dt = 0; dt < NDT; ++dt)
-        for (int p = 0; p < 2; ++p) {
-          const bf16x8 kt = tr_operand(ks, p, 16 * dt, l16, grp, 4, RKV);
-          for (int jn = 0; jn < NJ; ++jn) sacc[jn][dt] = mfma(kt, vb[jn][p], sacc[jn][dt]);
+      }  // act
+      if constexpr (!RON) {
+        // The next block's loads go out now (Q operands are no longer needed),
+        // so they overlap the state update and the barriers.
+        if (blk + 1 < blk1) {
+          load_kv_tile<HD>(kv, kh, vh, blk + 1, N, tid);
+          load_q(blk + 1);
         }
-      for (int jn = 0; jn < NJ; ++jn)
+        __syncthreads();  // every wave has finished reading the state
+      } else {
+        r_sum_half();
+        __syncthreads();  // the state and the first staged half are read
+        stage_half(1);
+        if (blk + 1 < blk1) {
+          load_q(blk + 1);
+          load_x_half(blk + 1, 1);
+        }
+      }
+
+      // state update: S[:, WC w:WC w+WC] += K_b^T V_b, then its bf16 copy
+      {
+        bf16x8 vb[NJ][2];
+        for (int jn = 0; jn < NJ; ++jn)
+          for (int p = 0; p < 2; ++p) vb[jn][p] = tr_operand(vs, p, WC * w + 16 * jn, l16, grp, 4, RKV);
         for (int dt = 0; dt < NDT; ++dt)
-          *reinterpret_cast<bf16x4*>(&st[(WC * w + 16 * jn + l16) * RST + 16 * dt + 4 * grp]) =
-              to_bf16x4(sacc[jn][dt]);
-      if constexpr (kN) {
-        for (int p = 0; p < 2; ++p)
-          for (int jj = 0; jj < NJ; ++jj)
-            zacc[jj] = mfma(tr_operand(ks, p, WC * w + 16 * jj, l16, grp, 4, RKV), ones_bf16x8(), zacc[jj]);
-        if (l16 == 0)
-          for (int jj = 0; jj < NJ; ++jj)
-            *reinterpret_cast<floatx4*>(&zs[WC * w + 16 * jj + 4 * grp]) = zacc[jj];
+          for (int p = 0; p < 2; ++p) {
+            const bf16x8 kt = tr_operand(ks, p, 16 * dt, l16, grp, 4, RKV);
+            for (int jn = 0; jn < NJ; ++jn) sacc[jn][dt] = mfma(kt, vb[jn][p], sacc[jn][dt]);
+          }
+        for (int jn = 0; jn < NJ; ++jn)
+          for (int dt = 0; dt < NDT; ++dt)
+            *reinterpret_cast<bf16x4*>(&st[(WC * w + 16 * jn + l16) * RST + 16 * dt + 4 * grp]) =
+                to_bf16x4(sacc[jn][dt]);
+        if constexpr (kN) {
+          for (int p = 0; p < 2; ++p)
+            for (int jj = 0; jj < NJ; ++jj)
+              zacc[jj] = mfma(tr_operand(ks, p, WC * w + 16 * jj, l16, grp, 4, RKV), ones_bf16x8(), zacc[jj]);
+          if (l16 == 0)
+            for (int jj = 0; jj < NJ; ++jj)
+              *reinterpret_cast<floatx4*>(&zs[WC * w + 16 * jj + 4 * grp]) = zacc[jj];
+        }
+      }
+      __syncthreads();  // K and V are free for the next block
+      if constexpr (RON) {
+        r_sum_half();
+        __syncthreads();  // the staging tiles are free for the next block
       }
     }
-    __syncthreads();  // K and V are free for the next block
+  };
+  if constexpr (RS) {
+    if (rs_on) walk(std::integral_constant<bool, true>{});
+    else walk(std::integral_constant<bool, false>{});
+  } else {
+    walk(std::integral_constant<bool, false>{});
   }
+
+  if constexpr (RS)
+    if (rs_on) {
+      float* rp = rpart + (int64_t(chain) * (P - 1) + seg - 1) * (HD * HD);
+      for (int jn = 0; jn < NJ; ++jn)
+        for (int dt = 0; dt < NDT; ++dt)
+          for (int i = 0; i < 4; ++i) rp[(16 * dt + 4 * grp + i) * HD + WC * w + 16 * jn + l16] = racc[jn][dt][i];
+    }
 
   if (s_out != nullptr && seg == P - 1 && sub == 0) {
     float* so = s_out + int64_t(bg) * (HD * HD);
@@ -1024,15 +1132,16 @@ __global__ __launch_bounds__(512, 1) void fwd_noncausal(
 }
 
 // gw: query heads per workgroup (4; 1 or 2 with PARTIAL)
-template <bool OUT_F32, int FL = 0, int HD = 128, bool PARTIAL = false>
+template <bool OUT_F32, int FL = 0, int HD = 128, bool PARTIAL = false, bool RS = false>
 void launch_g4(dim3 grid, hipStream_t stream, const void* q, const void* k, const void* v, void* o,
                const float* starts, const float* s_in, float* s_out, int Hq, int Hkv, int subgroups, int64_t N,
                int64_t nblocks, int64_t bps, int P, const float* zstarts = nullptr, const float* z_in = nullptr,
-               float* z_out = nullptr, float eps = 0.0f, int gw = 4) {
-  hipLaunchKernelGGL((fwd_bf16_g4<OUT_F32, FL, HD, PARTIAL>), grid, dim3(256), 0, stream,
+               float* z_out = nullptr, float eps = 0.0f, int gw = 4, const void* qx = nullptr,
+               float* rpart = nullptr) {
+  hipLaunchKernelGGL((fwd_bf16_g4<OUT_F32, FL, HD, PARTIAL, RS>), grid, dim3(256), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), o, starts, s_in, s_out, Hq, Hkv, subgroups, N, nblocks, bps,
-                     P, zstarts, z_in, z_out, eps, gw);
+                     P, zstarts, z_in, z_out, eps, gw, static_cast<const uint16_t*>(qx), rpart);
 }
 
 template <int GW, bool OUT_F32, int FL = 0>
@@ -1252,6 +1361,23 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
     if (out_f32) LA_MAIN(1, true); else LA_MAIN(1, false);
   }
 #undef LA_MAIN
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_bf16_rsum(const void* q, const void* k, const void* v, void* o, bool out_f32,
+                                int64_t B, int64_t Hq, int64_t Hkv, int64_t N, const Bf16Plan& plan,
+                                const void* workspace, const void* x, float* rpart, hipStream_t stream) {
+  if (plan.hd != 128 || plan.gw != 4 || plan.solo || plan.P < 2 || !plan.use_starts) return hipErrorInvalidValue;
+  const float* starts = static_cast<const float*>(workspace) + plan.partial_floats;
+  const dim3 grid(unsigned(B * Hkv * plan.subgroups * plan.P));
+  if (out_f32)
+    launch_g4<true, 0, 128, false, true>(grid, stream, q, k, v, o, starts, nullptr, nullptr, int(Hq), int(Hkv),
+                                         plan.subgroups, N, plan.nblocks, plan.blocks_per_seg, plan.P, nullptr,
+                                         nullptr, nullptr, 0.0f, 4, x, rpart);
+  else
+    launch_g4<false, 0, 128, false, true>(grid, stream, q, k, v, o, starts, nullptr, nullptr, int(Hq), int(Hkv),
+                                          plan.subgroups, N, plan.nblocks, plan.blocks_per_seg, plan.P, nullptr,
+                                          nullptr, nullptr, 0.0f, 4, x, rpart);
   return hipGetLastError();
 }
 

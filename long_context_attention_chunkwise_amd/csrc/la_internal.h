@@ -69,6 +69,16 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                            const float* s_in, float* s_out, int64_t B, int64_t Hq, int64_t Hkv,
                            int64_t N, const Bf16Plan& plan, const void* workspace, hipStream_t stream);
 
+// The backward's dQ pass (launch_fwd_bf16 over queries q = dO, keys V, values
+// K) that also writes, for every segment j >= 1 of every (batch, KV head,
+// query-head subgroup) chain c, rpart[c (P - 1) + j - 1] = sum over the
+// segment and the subgroup's four query heads of x_t^T q_t (x = the forward's
+// queries, [B*Hq][N][128] bf16; float32 128 x 128 each).  Head size 128,
+// groups of four query heads per workgroup, at least two segments.
+hipError_t launch_fwd_bf16_rsum(const void* q, const void* k, const void* v, void* o, bool out_f32,
+                                int64_t B, int64_t Hq, int64_t Hkv, int64_t N, const Bf16Plan& plan,
+                                const void* workspace, const void* x, float* rpart, hipStream_t stream);
+
 // Pre-pass over `chains` row-major [N][hd] tile pairs (a, b), hd = 64 or 128:
 // partial sums of a_b^T b_b over part r of segment j + seg_offset, j < P - 1.
 hipError_t launch_state_parts(const void* a, const void* b, float* partial, int64_t chains, int64_t N,
@@ -110,9 +120,12 @@ struct BwdPlan {
   int64_t blocks_per_part = 0;
   int P = 1;
   int R = 1;
+  // The dQ pass also writes the partials (launch_fwd_bf16_rsum): its segments
+  // are these, and there is no separate pre-pass over (Q, dO).
+  bool fused = false;
   size_t fwd_floats = 0;        // forward workspace
   size_t sin_t_floats = 0;      // transposed initial state for dQ
-  size_t partial_floats = 0;    // B*Hq*(P-1)*R*d*dv
+  size_t partial_floats = 0;    // B*Hq*(P-1)*R*d*dv; fused: B*Hkv*subgroups*(P-1)*d*dv
   size_t rstart_floats = 0;     // B*Hkv*P*d*dv
   size_t workspace_bytes = 0;   // all four, in that order
 };
@@ -124,7 +137,8 @@ hipError_t launch_transpose_states(const float* in, float* out, int64_t count, i
 
 // dK, dV and (if ds_in) the initial-state gradient; the reverse state starts
 // from ds_out (zeros if NULL).  workspace_f holds the plan's partials and
-// segment start states.
+// segment start states; with plan.fused the partials are already there (the
+// dQ pass wrote them), else the pre-pass over (Q, dO) writes them first.
 hipError_t launch_bwd_kv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dvg,
                          bool out_f32, const float* ds_out, float* ds_in, int64_t B, int64_t Hq, int64_t Hkv,
                          int64_t N, const BwdPlan& plan, float* workspace_f, hipStream_t stream);

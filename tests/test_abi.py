@@ -179,11 +179,17 @@ def test_workspace_plan(lib):
     assert lib.la_forward_workspace_bytes(1, 6, 4, 64, 128, 128, 64, BF16) == 0   # invalid -> 0
     # Backward at 1M tokens: the dQ forward's workspace, the transposed
     # initial states, and for dK/dV 8 segments per chain whose 7 later
-    # segments are summed over (Q, dO) of 128 query heads in 4 parts each
-    # (3584 pre-pass workgroups: seven full rounds at two per compute unit),
-    # plus 8 start states per chain.
+    # segments' sums of q^T dO the dQ pass writes (one per chain and segment:
+    # its segments are the same), plus 8 start states per chain.
     n = lib.la_backward_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, 64, BF16)
-    assert n == ((32 * 7 * 2 + 32 * 8) + 32 + 128 * 7 * 4 + 32 * 8) * 128 * 128 * 4
+    assert n == ((32 * 7 * 2 + 32 * 8) + 32 + 32 * 7 + 32 * 8) * 128 * 128 * 4
+    # Eight query heads per KV head: the dQ pass splits each group in two and
+    # runs 4 segments per chain (its pre-pass: 3 segments of the 32 KV heads
+    # in 5 parts), the dK/dV kernel 8, so the pre-pass over (Q, dO) sums the
+    # 7 later segments of 256 query heads (2 parts each: 3584 workgroups,
+    # seven rounds at two per compute unit).
+    n8 = lib.la_backward_workspace_bytes(1, 256, 32, 1 << 20, 128, 128, 64, BF16)
+    assert n8 == ((32 * 3 * 5 + 32 * 4) + 32 + 256 * 7 * 2 + 32 * 8) * 128 * 128 * 4
     assert lib.la_backward_workspace_bytes(1, 128, 32, 0, 128, 128, 64, BF16) == 0
     # Head size 64 (groups of four): states of 64 x 64, and two dK/dV workgroups per compute unit, so
     # 16 segments per chain whose 15 later segments are summed in 2 parts each (3840 pre-pass

@@ -6,7 +6,9 @@ Inputs are seeded and synthetic: q, k, v from synth.make_qkv (the forward
 workloads' distributions), the upstream gradient dO ~ N(0,1) from
 synth.make_grad, optional initial state and final-state gradient N(0,1)*0.5.
 Sizes span several 64-token blocks, several reverse segments per chain (the
-pre-pass over (Q, dO) and the reverse scan), ragged tails, group sizes 1 to 8,
+per-segment sums of q^T dO, written by the dQ pass where its segments are the
+dK/dV kernel's and by the separate pre-pass over (Q, dO) otherwise, and the
+reverse scan), ragged tails, group sizes 1 to 8,
 head sizes 128 and 64 and both gradient dtypes; the 1M-token workloads (head
 sizes 128 and 64) are checked on their first and last 4096 tokens and on a
 window across a segment boundary in the middle, with the states entering each
@@ -47,7 +49,8 @@ def check_grads(tag, got, ref, grad_dtype):
     (1, 6, 2, 1000, torch.float32, False, True),      # G = 3 (dQ forward with one head per workgroup)
     (1, 4, 2, 64, BF16, False, False),                # one full block
     (1, 4, 2, 1, torch.float32, True, True),          # one token
-    (1, 8, 1, 4100, BF16, False, False),              # G = 8, dQ forward subgroups
+    (1, 8, 1, 4100, BF16, False, False),              # G = 8, dQ forward subgroups (sums from the dQ pass)
+    (1, 16, 2, 40000, BF16, True, True),              # G = 8, dQ and dK/dV segments differ: the pre-pass
 ])
 def test_backward_matches_oracle(B, Hq, Hkv, N, grad_dtype, s_in, ds_out):
     need_gpu()
