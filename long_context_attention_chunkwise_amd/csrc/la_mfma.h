@@ -88,6 +88,42 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int p, int co
   return out;
 }
 
+// Lane l receives x of lane l ^ 8 (the other half of its 16-lane row): a DPP
+// row rotation by 8, four 32-bit moves.
+__device__ __forceinline__ bf16x8 swap_row_halves(bf16x8 x) {
+  const u32x4 u = __builtin_bit_cast(u32x4, x);
+  u32x4 r;
+  for (int i = 0; i < 4; ++i) r[i] = unsigned(__builtin_amdgcn_update_dpp(0, int(u[i]), 0x128, 0xF, 0xF, false));
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Operand layout -> whole 128-byte lines.  In operand layout lane (l16, grp)
+// holds row l16 of a 16-row tile at two 16-byte pieces of a line: e, piece
+// grp, and o, piece grp + 4 of the line's eight.  In line layout it holds
+// piece grp + 4 (l16 / 8) of row l16 % 8 (a) and of row 8 + l16 % 8 (b), so
+// one 16-byte access per lane covers eight whole lines.
+__device__ __forceinline__ void operand_to_lines(bf16x8 e, bf16x8 o, int l16, bf16x8& a, bf16x8& b) {
+  const bool lo = l16 < 8;
+  const bf16x8 recv = swap_row_halves(lo ? o : e);
+  a = lo ? e : recv;
+  b = lo ? recv : o;
+}
+
+// Stores two packed bf16 output quarters of a 16-row tile, given in operand
+// layout (e: row row0 + l16, 8 columns at piece grp of a 128-byte line; od:
+// piece grp + 4), as whole lines: rows row0 + l16 % 8 and row0 + 8 + l16 % 8.
+// `line` points at the line's first element in row 0, `ld` is the row pitch
+// in elements; rows at or past `nrows` are not written.
+__device__ __forceinline__ void store_lines(uint16_t* line, int64_t ld, int64_t row0, int64_t nrows, bf16x8 e,
+                                            bf16x8 od, int l16, int grp) {
+  bf16x8 a, b;
+  operand_to_lines(e, od, l16, a, b);
+  const int64_t ra = row0 + (l16 & 7), rb = ra + 8;
+  uint16_t* p = line + 8 * grp + 32 * (l16 >> 3);
+  if (ra < nrows) *reinterpret_cast<bf16x8*>(p + ra * ld) = a;
+  if (rb < nrows) *reinterpret_cast<bf16x8*>(p + rb * ld) = b;
+}
+
 __device__ __forceinline__ bf16x4 to_bf16x4(floatx4 x) {
   bf16x4 r;
   for (int i = 0; i < 4; ++i) r[i] = (__bf16)x[i];
