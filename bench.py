@@ -487,7 +487,7 @@ def bench_decode(la, synth, torch, w, steps, warmup, cpu=False):
 # parent reads the child's counter database.
 # ---------------------------------------------------------------------------
 COUNTER_PASSES = (("FETCH_SIZE",), ("WRITE_SIZE",), ("SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"))
-COUNTER_KERNELS = "fwd_bf16_g4|fwd_bf16_main|state_parts|decode_kernel|stream_kernel"
+COUNTER_KERNELS = "fwd_bf16_g4|fwd_bf16_main|fwd_bf16_solo|state_parts|decode_kernel|stream_kernel"
 CALIBRATION_GIB = 4
 
 
@@ -546,7 +546,7 @@ def read_counter_db(path):
         db = sqlite3.connect(f)
         for name, disp, dur, cname, val in db.execute(
                 "select name, dispatch_id, duration, counter_name, counter_value from pmc_events"):
-            m = re.search(r"(fwd_bf16_g4|fwd_bf16_main|state_parts|decode_kernel|stream_kernel<1)", name)
+            m = re.search(r"(fwd_bf16_g4|fwd_bf16_main|fwd_bf16_solo|state_parts|decode_kernel|stream_kernel<1)", name)
             if not m:
                 continue
             d = per[m.group(1)][disp]
@@ -679,7 +679,13 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     # the output kernel that serves this workload's query-head group size
-    main_kernel = "fwd_bf16_g4" if (w.Hq // w.Hkv) % 4 == 0 or w.d == 64 else "fwd_bf16_main"
+    G = w.Hq // w.Hkv
+    if w.d == 64 and G == 1:
+        main_kernel = "fwd_bf16_solo"
+    elif G % 4 == 0 or w.d == 64:
+        main_kernel = "fwd_bf16_g4"
+    else:
+        main_kernel = "fwd_bf16_main"
     props = torch.cuda.get_device_properties(0)
     bytes_main = forward_bytes(w, w.N)
     # workloads small enough to stay in the caches are also timed behind a 1 GiB scrub
