@@ -51,6 +51,7 @@ def check_grads(tag, got, ref, grad_dtype):
     (1, 4, 2, 1, torch.float32, True, True),          # one token
     (1, 8, 1, 4100, BF16, False, False),              # G = 8, dQ forward subgroups (sums from the dQ pass)
     (1, 16, 2, 40000, BF16, True, True),              # G = 8, dQ and dK/dV segments differ: the pre-pass
+    (1, 24, 3, 19200, BF16, False, True),             # G = 8, three KV heads, dQ segments not whole dK/dV ones
 ])
 def test_backward_matches_oracle(B, Hq, Hkv, N, grad_dtype, s_in, ds_out):
     need_gpu()
@@ -76,6 +77,7 @@ def test_backward_matches_oracle(B, Hq, Hkv, N, grad_dtype, s_in, ds_out):
     (1, 2, 2, 70, BF16, True, True),                  # G = 1, two blocks
     (1, 6, 3, 777, BF16, False, True),                # G = 2
     (1, 3, 1, 1000, torch.float32, True, False),      # G = 3
+    (1, 8, 2, 65536, BF16, True, True),               # G = 4, two dK/dV segments per dQ segment
 ])
 def test_backward_head_size_64(B, Hq, Hkv, N, grad_dtype, s_in, ds_out):
     """d = dv = 64, any group size: dQ on the forward kernels (four-wave
