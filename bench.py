@@ -317,6 +317,47 @@ def bench_backward(la, synth, torch, w, q, k, v, steps, warmup):
             "workspace_bytes": ws_bytes}
 
 
+def bench_in_place(la, torch, w, q, k, v, steps, warmup):
+    """The forward step with the output written over q (o = q, allowed when
+    each query row is read before the same output row is written: groups of
+    four query heads on the matrix cores).  Overwrites q, so it runs after
+    everything that reads q; the timing does not depend on the values."""
+    import ctypes
+    lib = la.load_library()
+    dev = torch.device("cuda:0")
+    ws_bytes = la.workspace_bytes(w.B, w.Hq, w.Hkv, w.N, w.d, w.dv, w.block, torch.bfloat16)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = ctypes.c_void_p
+    args_states = (P(k.data_ptr()), P(v.data_ptr()), w.B, w.Hq, w.Hkv, w.N, w.d, w.dv, w.block, la.LA_BF16,
+                   None, P(ws.data_ptr()), ws_bytes, sp)
+    args_out = (P(q.data_ptr()), P(k.data_ptr()), P(v.data_ptr()), P(q.data_ptr()), w.B, w.Hq, w.Hkv, w.N, w.d,
+                w.dv, w.block, la.LA_BF16, la.LA_BF16, None, None, P(ws.data_ptr()), ws_bytes, sp)
+    evs = []
+    for i in range(warmup + steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        st = lib.la_forward_states(*args_states)
+        e[1].record(stream)
+        st2 = lib.la_forward_outputs(*args_out)
+        e[2].record(stream)
+        if st or st2:
+            raise RuntimeError(f"in-place forward failed: {la.status_str(st or st2)}")
+        if i >= warmup:
+            evs.append(e)
+    torch.cuda.synchronize()
+    t_step = [e[0].elapsed_time(e[2]) for e in evs]
+    t_out = [e[1].elapsed_time(e[2]) for e in evs]
+    nbytes = forward_bytes(w, w.N)
+    ms_out = statistics.mean(t_out)
+    del ws
+    return {"steps": steps, "warmup": warmup, "ms_per_step": round(statistics.mean(t_step), 4),
+            "outputs_ms": round(ms_out, 4), "tokens_per_s": round(w.B * w.N / (statistics.mean(t_step) * 1e-3), 1),
+            "outputs_hbm_frac": round(nbytes / (ms_out * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "note": "o written over q (separate timing; the headline uses a separate o buffer)"}
+
+
 VARIANTS = (
     # name, causal, feature map, normalize, eps
     ("relu_normalised_causal", True, "relu", True, 1e-6),
@@ -648,6 +689,8 @@ def main():
     ap.add_argument("--variant-steps", type=int, default=5, help="0 skips the forward-variant measurement")
     ap.add_argument("--backward-steps", type=int, default=5, help="0 skips the backward measurement")
     ap.add_argument("--backward-warmup", type=int, default=1)
+    ap.add_argument("--in-place-steps", type=int, default=5,
+                    help="steps of the forward with o written over q, timed last (0 skips)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-counters", action="store_true",
                     help="skip the rocprofv3 counter passes (traffic then comes from the committed profile)")
@@ -711,6 +754,10 @@ def main():
     if args.backward_steps > 0:
         backward = bench_backward(la, synth, torch, w, q, k, v, args.backward_steps, args.backward_warmup)
         log(f"[bench] backward: {backward['ms_per_step']:.3f} ms/step")
+    in_place = None
+    if args.in_place_steps > 0 and (w.Hq // w.Hkv) % 4 == 0:
+        in_place = bench_in_place(la, torch, w, q, k, v, args.in_place_steps, 1)
+        log(f"[bench] forward in place: {in_place['ms_per_step']:.3f} ms/step (outputs {in_place['outputs_ms']:.3f} ms)")
     del q, k, v
     torch.cuda.empty_cache()
 
@@ -795,6 +842,7 @@ def main():
         "workspace_bytes": ws_bytes,
         "variants": variants,
         "backward": backward,
+        "forward_in_place": in_place,
         "decode": decode,
         "cpu_baseline": cpu,
         "cpu_baseline_small_workloads": cpu_small,
