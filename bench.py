@@ -245,7 +245,45 @@ def bench_forward(la, synth, torch, w, steps, warmup, scrub_bytes=0):
                               "min": round(min(t_scr), 4), "mean": round(statistics.mean(t_scr), 4),
                               "outputs_mean": round(statistics.mean(t_scr_main), 4)}
         del scrub
+        events["graph"] = graph_steps(lib, torch, stream, args_states, args_out, steps)
     return q, k, v, ms_step, statistics.mean(t_states), statistics.mean(t_main), ws_bytes, events
+
+
+def graph_steps(lib, torch, stream, args_states, args_out, reps, per_graph=10):
+    """Steps of a small workload as a caller that captures them in a HIP graph
+    runs them: `per_graph` steps (both calls each) captured once, the graph
+    replayed `reps` times back to back (cache-warm), per-step time from
+    events around each replay.  Without the per-launch gaps this is what the
+    kernels themselves take."""
+    import ctypes
+
+    def launch(sp):
+        for _ in range(per_graph):
+            st = lib.la_forward_states(*args_states[:-1], sp)
+            st2 = lib.la_forward_outputs(*args_out[:-1], sp)
+            if st or st2:
+                raise RuntimeError("forward failed under graph capture")
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        launch(ctypes.c_void_p(side.cuda_stream))  # warm-up on the capture stream
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launch(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    g.replay()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) / per_graph for a, b in evs]
+    del g
+    return {"steps_per_graph": per_graph, "replays": reps, "median": round(statistics.median(per), 4),
+            "min": round(min(per), 4), "cache": "warm"}
 
 
 def backward_flops(w, N):
