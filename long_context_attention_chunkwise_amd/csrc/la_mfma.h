@@ -88,12 +88,17 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int p, int co
   return out;
 }
 
+// DPP control: rotate each 16-lane row right by 8 (row_ror:8).
+constexpr int kDppRowRor8 = 0x128;
+
 // Lane l receives x of lane l ^ 8 (the other half of its 16-lane row): a DPP
-// row rotation by 8, four 32-bit moves.
+// row rotation by 8, four 32-bit moves, every row and bank enabled (so no lane
+// keeps the `old` operand).
 __device__ __forceinline__ bf16x8 swap_row_halves(bf16x8 x) {
   const u32x4 u = __builtin_bit_cast(u32x4, x);
   u32x4 r;
-  for (int i = 0; i < 4; ++i) r[i] = unsigned(__builtin_amdgcn_update_dpp(0, int(u[i]), 0x128, 0xF, 0xF, false));
+  for (int i = 0; i < 4; ++i)
+    r[i] = unsigned(__builtin_amdgcn_update_dpp(0, int(u[i]), kDppRowRor8, 0xF, 0xF, false));
   return __builtin_bit_cast(bf16x8, r);
 }
 
