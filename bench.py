@@ -355,6 +355,40 @@ def bench_backward(la, synth, torch, w, q, k, v, steps, warmup):
             "workspace_bytes": ws_bytes}
 
 
+def bench_state(la, torch, w, k, v, steps, warmup):
+    """la_forward_state (the final state without outputs) on the workload's
+    k, v: per-call events; algorithmic bytes = k and v read once (the state
+    written is negligible)."""
+    import ctypes
+    lib = la.load_library()
+    dev = torch.device("cuda:0")
+    ws_bytes = int(lib.la_forward_state_workspace_bytes(w.B, w.Hkv, w.N, w.d, w.dv, la.LA_BF16))
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    S = torch.empty((w.B, w.Hkv, w.d, w.dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    P = ctypes.c_void_p
+    args = (P(k.data_ptr()), P(v.data_ptr()), w.B, w.Hkv, w.N, w.d, w.dv, la.LA_BF16, None, P(S.data_ptr()),
+            P(ws.data_ptr()), ws_bytes, P(stream.cuda_stream))
+    evs = []
+    for i in range(warmup + steps):
+        e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        e[0].record(stream)
+        st = lib.la_forward_state(*args)
+        e[1].record(stream)
+        if st:
+            raise RuntimeError(f"state-only pass failed: {la.status_str(st)}")
+        if i >= warmup:
+            evs.append(e)
+    torch.cuda.synchronize()
+    ms = statistics.mean(a.elapsed_time(b) for a, b in evs)
+    nbytes = w.B * w.Hkv * w.N * (w.d + w.dv) * 2
+    del ws, S
+    return {"steps": steps, "warmup": warmup, "ms_per_call": round(ms, 4),
+            "tokens_per_s": round(w.B * w.N / (ms * 1e-3), 1), "bytes_alg": nbytes,
+            "hbm_gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "workspace_bytes": ws_bytes}
+
+
 def bench_in_place(la, torch, w, q, k, v, steps, warmup):
     """The forward step with the output written over q (o = q, allowed when
     each query row is read before the same output row is written: groups of
@@ -727,6 +761,8 @@ def main():
     ap.add_argument("--variant-steps", type=int, default=5, help="0 skips the forward-variant measurement")
     ap.add_argument("--backward-steps", type=int, default=5, help="0 skips the backward measurement")
     ap.add_argument("--backward-warmup", type=int, default=1)
+    ap.add_argument("--state-steps", type=int, default=10,
+                    help="calls of la_forward_state (final state only) on the same k, v (0 skips)")
     ap.add_argument("--in-place-steps", type=int, default=5,
                     help="steps of the forward with o written over q, timed last (0 skips)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -792,6 +828,10 @@ def main():
     if args.backward_steps > 0:
         backward = bench_backward(la, synth, torch, w, q, k, v, args.backward_steps, args.backward_warmup)
         log(f"[bench] backward: {backward['ms_per_step']:.3f} ms/step")
+    state_only = None
+    if args.state_steps > 0:
+        state_only = bench_state(la, torch, w, k, v, args.state_steps, 1)
+        log(f"[bench] state only: {state_only['ms_per_call']:.3f} ms, {state_only['hbm_gb_per_s']:.0f} GB/s")
     in_place = None
     if args.in_place_steps > 0 and (w.Hq // w.Hkv) % 4 == 0:
         in_place = bench_in_place(la, torch, w, q, k, v, args.in_place_steps, 1)
@@ -881,6 +921,7 @@ def main():
         "variants": variants,
         "backward": backward,
         "forward_in_place": in_place,
+        "state_only": state_only,
         "decode": decode,
         "cpu_baseline": cpu,
         "cpu_baseline_small_workloads": cpu_small,

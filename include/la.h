@@ -168,6 +168,37 @@ size_t la_forward_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
                                   la_dtype in_dtype);
 
 /*
+ * State only, no outputs: for every (batch, KV head),
+ *     s_out = s_in + sum over the N tokens of k_t^T v_t
+ * (s_in zero if NULL): the state the forward pass ends with (its s_out),
+ * which is all a later chunk or a decode step needs from these tokens (page
+ * "MiniMax-01与Lightning Attention", section 4.1 table: the key-value state is
+ * updated incrementally), without reading q or writing o.  It is also the
+ * per-shard total that a sequence split over several devices exchanges: with
+ * shard totals T_0 .. T_{M-1}, shard j's forward starts from s_in + T_0 + ...
+ * + T_{j-1} (associativity; page "奧特曼的“溫和奇點”愿景，線性注意力的勝利？
+ * MiniMax-M1技術報告深度解析" (digipub.cc), the A*B*C = A*(B*C) passage).
+ *   k [B][Hkv][N][d], v [B][Hkv][N][dv] in in_dtype (NULL allowed when N = 0);
+ *   s_in, s_out [B][Hkv][d][dv] float32; s_out may be s_in (in place) and
+ *   must not overlap k or v; s_in may be NULL.
+ *   Shapes and dtypes as la_forward_ex with Hq = Hkv (bf16 with d = dv = 128
+ *   or 64 on the matrix cores; float32, or bf16 at other head sizes, on float32
+ *   FMA).  The result does not depend on a block size.
+ *   workspace / workspace_bytes: at least la_forward_state_workspace_bytes
+ *   bytes (may be NULL when that is 0); scratch, no initialisation needed.
+ * Statuses as la_forward_ex (LA_ERR_NULL also for a NULL s_out).
+ */
+la_status la_forward_state(const void* k, const void* v,
+                           int64_t B, int64_t Hkv, int64_t N, int64_t d, int64_t dv,
+                           la_dtype in_dtype, const float* s_in, float* s_out,
+                           void* workspace, size_t workspace_bytes, la_stream stream);
+
+/* Workspace bytes la_forward_state needs on the current device (0 when none
+ * or for invalid arguments). */
+size_t la_forward_state_workspace_bytes(int64_t B, int64_t Hkv, int64_t N, int64_t d, int64_t dv,
+                                        la_dtype in_dtype);
+
+/*
  * la_forward_ex without a workspace argument, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops
  * and harnesses that forbid allocation.  It allocates nothing (no hipMalloc,

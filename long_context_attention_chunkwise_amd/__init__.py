@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     decode_step,
     forward,
     forward_noalloc,
+    forward_state,
     forward_variant,
     load_library,
     status_str,

@@ -17,7 +17,8 @@ STATUS_NAMES = {0: "LA_OK", 1: "LA_ERR_NULL", 2: "LA_ERR_SHAPE", 3: "LA_ERR_UNSU
                 5: "LA_ERR_ALIAS", 6: "LA_ERR_WORKSPACE", 7: "LA_ERR_HIP", 8: "LA_ERR_TOO_LARGE"}
 EXPORTS = ("la_forward", "la_forward_ex", "la_forward_states", "la_forward_outputs", "la_forward_workspace_bytes",
            "la_forward_variant", "la_forward_variant_workspace_bytes", "la_backward", "la_backward_workspace_bytes",
-           "la_decode_step", "la_status_str", "la_forward_noalloc")
+           "la_decode_step", "la_status_str", "la_forward_noalloc", "la_forward_state",
+           "la_forward_state_workspace_bytes")
 LA_NOALLOC_SCRATCH_BYTES = 64 << 20
 LA_FMAP_IDENTITY, LA_FMAP_RELU = 0, 1
 
@@ -62,6 +63,10 @@ def load_library(path=LIB_PATH):
     lib.la_backward.restype = i32
     lib.la_backward_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, i64, i32]
     lib.la_backward_workspace_bytes.restype = sz
+    lib.la_forward_state.argtypes = [vp, vp, i64, i64, i64, i64, i64, i32, vp, vp, vp, sz, vp]
+    lib.la_forward_state.restype = i32
+    lib.la_forward_state_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
+    lib.la_forward_state_workspace_bytes.restype = sz
     lib.la_forward_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i32, i32, vp, vp, vp]
     lib.la_forward_noalloc.restype = i32
     lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp]
@@ -181,6 +186,41 @@ def forward(q, k, v, block=64, out_dtype=None, s_in=None, return_state=False, ou
         raise LAError(st, "la_forward_ex")
     if return_state:
         return out, s_out
+    return out
+
+
+def forward_state(k, v, s_in=None, out=None, workspace=None):
+    """la_forward_state: the final state s_in + sum_t k_t^T v_t per (batch,
+    KV head) without outputs.  k [B,Hkv,N,d], v [B,Hkv,N,dv] (float32 or
+    bfloat16, the same); s_in optional float32 [B,Hkv,d,dv]; returns the
+    float32 state [B,Hkv,d,dv] (`out`, which may be s_in, when given)."""
+    torch = _torch()
+    lib = load_library()
+    _check_tensor("k", k, 4, None)
+    dev = k.device
+    _check_tensor("v", v, 4, dev)
+    if k.dtype != v.dtype:
+        raise TypeError("k and v must share one dtype")
+    B, Hkv, N, d = k.shape
+    dv = v.shape[3]
+    if tuple(v.shape[:3]) != (B, Hkv, N):
+        raise ValueError(f"shape mismatch: k {tuple(k.shape)}, v {tuple(v.shape)}")
+    for name, t in (("s_in", s_in), ("out", out)):
+        if t is not None:
+            _check_tensor(name, t, 4, dev)
+            if t.dtype != torch.float32 or tuple(t.shape) != (B, Hkv, d, dv):
+                raise ValueError(f"{name} must be float32 [B, Hkv, d, dv]")
+    code = _dtype_code(k.dtype)
+    with torch.cuda.device(dev):
+        if out is None:
+            out = torch.empty((B, Hkv, d, dv), dtype=torch.float32, device=dev)
+        ws_bytes = int(lib.la_forward_state_workspace_bytes(B, Hkv, N, d, dv, code))
+        workspace = _workspace(workspace, ws_bytes, dev)
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.la_forward_state(_ptr(k), _ptr(v), B, Hkv, N, d, dv, code, _ptr(s_in), _ptr(out),
+                                  _ptr(workspace), ws_bytes, ctypes.c_void_p(stream))
+    if st != LA_OK:
+        raise LAError(st, "la_forward_state")
     return out
 
 

@@ -161,6 +161,27 @@ VarPlan plan_variant(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, i
   return vp;
 }
 
+StatePlan plan_state(int64_t B, int64_t Hkv, int64_t N, int64_t d, int cus) {
+  StatePlan p;
+  p.hd = static_cast<int>(d);
+  p.nblocks = (N + kBf16Block - 1) / kBf16Block;
+  if (p.nblocks == 0) return p;
+  // Parts: one round of resident pre-pass workgroups (two per compute unit at
+  // head size 128, three at 64) over all chains, each part at least
+  // kMinPartBlocks blocks.
+  constexpr int64_t kMinPartBlocks = 8;
+  const int64_t chains = B * Hkv;
+  const int64_t slots = (d == 128 ? 2 : 3) * int64_t(cus);
+  int64_t R = (slots + chains - 1) / chains;
+  R = std::max<int64_t>(1, std::min(R, p.nblocks / kMinPartBlocks));
+  p.blocks_per_part = (p.nblocks + R - 1) / R;
+  R = (p.nblocks + p.blocks_per_part - 1) / p.blocks_per_part;
+  p.R = static_cast<int>(R);
+  p.partial_floats = size_t(chains) * size_t(R) * size_t(d * d);
+  p.workspace_bytes = p.partial_floats * sizeof(float);
+  return p;
+}
+
 BwdPlan plan_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv, int cus) {
   BwdPlan p;
   // dQ is the forward over (dO, V, K): head sizes swap.
@@ -390,6 +411,49 @@ la_status la_forward_outputs(const void* q, const void* k, const void* v, void* 
   if (st != LA_OK) return st;
   return run_outputs(fc, q, k, v, o, B, Hq, Hkv, N, d, dv, block, in_dtype, out_dtype, s_in, s_out, workspace,
                      static_cast<hipStream_t>(stream));
+}
+
+size_t la_forward_state_workspace_bytes(int64_t B, int64_t Hkv, int64_t N, int64_t d, int64_t dv,
+                                        la_dtype in_dtype) {
+  if (check_forward_shape(B, Hkv, Hkv, N, d, dv, kBf16Block, in_dtype, in_dtype) != LA_OK) return 0;
+  if (!mfma_path(in_dtype, d, dv, kBf16Block) || N == 0) return 0;
+  return la::plan_state(B, Hkv, N, d, device_cus()).workspace_bytes;
+}
+
+la_status la_forward_state(const void* k, const void* v, int64_t B, int64_t Hkv, int64_t N, int64_t d, int64_t dv,
+                           la_dtype in_dtype, const float* s_in, float* s_out, void* workspace,
+                           size_t workspace_bytes, la_stream stream) {
+  // the forward's shape rules with one query head per KV head (no q, no o)
+  la_status st = check_forward_shape(B, Hkv, Hkv, N, d, dv, kBf16Block, in_dtype, in_dtype);
+  if (st != LA_OK) return st;
+  if (s_out == nullptr || (N > 0 && (k == nullptr || v == nullptr))) return LA_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(s_in) || !aligned16(s_out)) return LA_ERR_ALIGN;
+  const size_t ei = esize(in_dtype);
+  const size_t nk = size_t(B * Hkv * N * d) * ei, nv = size_t(B * Hkv * N * dv) * ei;
+  const size_t ns = size_t(B * Hkv * d * dv) * sizeof(float);
+  if (overlap(s_out, ns, k, nk) || overlap(s_out, ns, v, nv) || (s_out != s_in && overlap(s_out, ns, s_in, ns)))
+    return LA_ERR_ALIAS;
+  const bool mfma = mfma_path(in_dtype, d, dv, kBf16Block);
+  la::StatePlan plan;
+  if (mfma && N > 0) {
+    plan = la::plan_state(B, Hkv, N, d, device_cus());
+    const size_t nw = plan.workspace_bytes;
+    if (workspace == nullptr || workspace_bytes < nw) return LA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return LA_ERR_ALIGN;
+    if (overlap(workspace, nw, k, nk) || overlap(workspace, nw, v, nv) || overlap(workspace, nw, s_in, ns) ||
+        overlap(workspace, nw, s_out, ns))
+      return LA_ERR_ALIAS;
+  }
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t err = hipSuccess;
+  if (N == 0) {
+    if (s_out != s_in) err = la::launch_copy_or_zero(s_out, s_in, ns / sizeof(float), hs);
+  } else if (mfma) {
+    err = la::launch_state_total_bf16(k, v, s_in, s_out, B, Hkv, N, plan, static_cast<float*>(workspace), hs);
+  } else {
+    err = la::launch_state_total_f32(k, v, in_dtype == LA_BF16, s_in, s_out, B, Hkv, N, d, dv, hs);
+  }
+  return err == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 
 la_status la_forward(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t Hq, int64_t Hkv,

@@ -1017,6 +1017,20 @@ __global__ __launch_bounds__(256) void scan_starts(const float* __restrict__ par
   }
 }
 
+// s_out[c][e] = s_in[c][e] (0 without s_in) + sum over r < R of
+// partial[c][r][e], added in order of r; E elements per state.  s_out may be
+// s_in (each thread reads its element before writing it).
+__global__ __launch_bounds__(256) void sum_parts(const float* __restrict__ partial, const float* s_in, float* s_out,
+                                                 int R, int E, int64_t total) {
+  const int64_t gid = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (gid >= total) return;
+  const int64_t c = gid / E;
+  const int e = int(gid % E);
+  float run = s_in ? s_in[gid] : 0.0f;
+  for (int r = 0; r < R; ++r) run += partial[(c * R + r) * E + e];
+  s_out[gid] = run;
+}
+
 // ---------------------------------------------------------------------------
 // Non-causal variant (LinearAttentionCore of page "MiniMax-01与Lightning
 // Attention", section 2.2): o_t = phi(q_t) . S_tot for every t, with S_tot =
@@ -1206,6 +1220,21 @@ hipError_t launch_segment_states(const void* k, const void* v, const float* s_in
   const int64_t total = kv_chains * E;
   hipLaunchKernelGGL(scan_starts, dim3(unsigned((total + 255) / 256)), dim3(256), 0, stream, partial, starts, s_in,
                      plan.P, plan.R, E, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_total_bf16(const void* k, const void* v, const float* s_in, float* s_out, int64_t B,
+                                   int64_t Hkv, int64_t N, const StatePlan& plan, float* workspace,
+                                   hipStream_t stream) {
+  // one summed segment (the whole sequence) in plan.R parts per chain
+  const int64_t chains = B * Hkv;
+  hipError_t e = launch_state_parts(k, v, workspace, chains, N, plan.nblocks, plan.nblocks, plan.blocks_per_part, 2,
+                                    plan.R, 0, plan.hd, stream);
+  if (e != hipSuccess) return e;
+  const int E = plan.hd * plan.hd;
+  const int64_t total = chains * E;
+  hipLaunchKernelGGL(sum_parts, dim3(unsigned((total + 255) / 256)), dim3(256), 0, stream, workspace, s_in, s_out,
+                     plan.R, E, total);
   return hipGetLastError();
 }
 

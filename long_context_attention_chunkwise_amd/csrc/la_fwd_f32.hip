@@ -246,6 +246,74 @@ hipError_t launch_scalar(const void* q, const void* k, const void* v, void* o, b
 
 }  // namespace
 
+namespace {
+
+// State-only pass on float32 FMA: s_out[c] = s_in[c] + sum over all N
+// tokens of k_t^T v_t for chain c = b * Hkv + g.  Workgroup (c, i-tile) owns
+// rows [16 it, 16 it + 16) of the d x dv state, all dv columns; thread t owns
+// column t % 128 of rows 16 it + 8 (t / 128) + {0..7}.  The sequence is walked
+// in 64-token chunks staged in LDS.  s_out may be s_in (each entry is read
+// and written by one thread).
+template <typename TI>
+__global__ __launch_bounds__(kThreads) void state_total_f32(const TI* __restrict__ k, const TI* __restrict__ v,
+                                                           const float* s_in, float* s_out, int64_t N, int d,
+                                                           int dv) {
+  constexpr int CH = 64, RT = 16;
+  __shared__ float Ks[CH][RT];
+  __shared__ float Vs[CH][kMaxD];
+  const int nit = (d + RT - 1) / RT;
+  const int64_t c = blockIdx.x / nit;
+  const int i0 = (blockIdx.x % nit) * RT;
+  const int tid = threadIdx.x;
+  const int j = tid % kMaxD, rg = tid / kMaxD;
+  const TI* kc = k + c * N * d;
+  const TI* vc = v + c * N * dv;
+  float acc[8];
+  for (int r = 0; r < 8; ++r) acc[r] = 0.0f;
+  for (int64_t t0 = 0; t0 < N; t0 += CH) {
+    for (int e = tid; e < CH * RT; e += kThreads) {
+      const int tt = e / RT, ii = e % RT;
+      const int64_t t = t0 + tt;
+      Ks[tt][ii] = (t < N && i0 + ii < d) ? ldf(kc, t * d + i0 + ii) : 0.0f;
+    }
+    for (int e = tid; e < CH * kMaxD; e += kThreads) {
+      const int tt = e / kMaxD, jj = e % kMaxD;
+      const int64_t t = t0 + tt;
+      Vs[tt][jj] = (t < N && jj < dv) ? ldf(vc, t * dv + jj) : 0.0f;
+    }
+    __syncthreads();
+    for (int tt = 0; tt < CH; ++tt) {
+      const float vv = Vs[tt][j];
+      for (int r = 0; r < 8; ++r) acc[r] = fmaf(Ks[tt][8 * rg + r], vv, acc[r]);
+    }
+    __syncthreads();
+  }
+  if (j < dv)
+    for (int r = 0; r < 8; ++r) {
+      const int i = i0 + 8 * rg + r;
+      if (i < d) {
+        const int64_t idx = (c * d + i) * dv + j;
+        s_out[idx] = (s_in ? s_in[idx] : 0.0f) + acc[r];
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_state_total_f32(const void* k, const void* v, bool in_bf16, const float* s_in, float* s_out,
+                                  int64_t B, int64_t Hkv, int64_t N, int64_t d, int64_t dv, hipStream_t stream) {
+  if (d < 1 || d > kMaxD || dv < 1 || dv > kMaxD) return hipErrorInvalidValue;
+  const dim3 grid(unsigned(B * Hkv * ((d + 15) / 16)));
+  if (in_bf16)
+    hipLaunchKernelGGL((state_total_f32<uint16_t>), grid, dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), s_in, s_out, N, int(d),
+                       int(dv));
+  else
+    hipLaunchKernelGGL((state_total_f32<float>), grid, dim3(kThreads), 0, stream, static_cast<const float*>(k),
+                       static_cast<const float*>(v), s_in, s_out, N, int(d), int(dv));
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd_f32_variant(const void* q, const void* k, const void* v, void* o, bool in_bf16,
                                   bool out_bf16, bool causal, bool relu, bool norm, float eps, const float* s_in,
                                   float* s_out, const float* z_in, float* z_out, int64_t B, int64_t Hq,

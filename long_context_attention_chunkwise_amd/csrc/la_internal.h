@@ -111,6 +111,32 @@ hipError_t launch_variant(const void* q, const void* k, const void* v, void* o, 
                           int64_t Hq, int64_t Hkv, int64_t N, const VarPlan& plan, void* workspace,
                           hipStream_t stream);
 
+// State-only pass (la_forward_state) on the matrix cores: each (batch, KV
+// head) chain's blocks are summed in R parts of blocks_per_part blocks
+// (enough parts to fill the chip), then added up in order with s_in.
+struct StatePlan {
+  int64_t nblocks = 0;          // ceil(N / 64)
+  int64_t blocks_per_part = 0;
+  int R = 1;
+  int hd = 128;                 // head size d = dv (128 or 64)
+  size_t partial_floats = 0;    // B*Hkv*R*d*dv
+  size_t workspace_bytes = 0;
+};
+
+StatePlan plan_state(int64_t B, int64_t Hkv, int64_t N, int64_t d, int cus);
+
+// s_out = s_in (zeros if NULL) + sum over the N tokens of k_t^T v_t per chain,
+// bf16 inputs at d = dv = plan.hd, through the pre-pass kernel; the workspace
+// holds the plan's partials.  s_out may be s_in.
+hipError_t launch_state_total_bf16(const void* k, const void* v, const float* s_in, float* s_out, int64_t B,
+                                   int64_t Hkv, int64_t N, const StatePlan& plan, float* workspace,
+                                   hipStream_t stream);
+
+// The same on float32 FMA for float32 inputs, or bf16 inputs (in_bf16) off the
+// matrix-core shape: d and dv up to 128, no workspace.  s_out may be s_in.
+hipError_t launch_state_total_f32(const void* k, const void* v, bool in_bf16, const float* s_in, float* s_out,
+                                  int64_t B, int64_t Hkv, int64_t N, int64_t d, int64_t dv, hipStream_t stream);
+
 // Backward work split: dK/dV walk each chain's segments from the end; segment
 // j starts from the sum of q^T dO over later segments and the group's heads.
 struct BwdPlan {

@@ -222,6 +222,35 @@ def test_binding_requires_gpu_tensors():
         la.forward(x, x, x)
 
 
+def test_forward_state_validation(lib):
+    """la_forward_state (state only, no outputs): argument errors before any
+    launch, and the workspace of its parts (one round of two pre-pass
+    workgroups per compute unit at head size 128, three at 64, planned here
+    for 256 compute units)."""
+    def st(k=K, v=V, B=1, Hkv=4, N=1000, d=128, dv=128, i=BF16, s_in=None, s_out=S_OUT, ws=WS, ws_bytes=1 << 32):
+        return lib.la_forward_state(k, v, B, Hkv, N, d, dv, i, s_in, s_out, ws, ws_bytes, None)
+
+    assert st(k=None) == NULL
+    assert st(s_out=None) == NULL
+    assert st(B=0) == SHAPE
+    assert st(N=-1) == SHAPE
+    assert st(d=256) == UNSUP
+    assert st(i=7) == UNSUP
+    assert st(v=ctypes.c_void_p(GB * 3 + 8)) == ALIGN
+    assert st(s_out=ctypes.c_void_p(GB * 2 + 4096)) == ALIAS                  # inside k
+    assert st(s_in=S_IN, s_out=ctypes.c_void_p(GB * 5 + 1024)) == ALIAS      # partly over s_in
+    assert st(ws=None) == WORKSPACE
+    assert st(ws_bytes=16) == WORKSPACE
+    assert st(ws=ctypes.c_void_p(GB * 2 + 64)) == ALIAS                       # workspace inside k
+    # 1M tokens, 32 KV heads: 16 parts per chain (1024 blocks each) at 128, 24 at 64
+    assert lib.la_forward_state_workspace_bytes(1, 32, 1 << 20, 128, 128, BF16) == 32 * 16 * 128 * 128 * 4
+    assert lib.la_forward_state_workspace_bytes(1, 32, 1 << 20, 64, 64, BF16) == 32 * 24 * 64 * 64 * 4
+    assert lib.la_forward_state_workspace_bytes(1, 32, 100, 128, 128, BF16) == 32 * 128 * 128 * 4   # one part
+    assert lib.la_forward_state_workspace_bytes(1, 32, 1 << 20, 128, 128, F32) == 0   # float32 FMA path
+    assert lib.la_forward_state_workspace_bytes(1, 32, 0, 128, 128, BF16) == 0
+    assert lib.la_forward_state_workspace_bytes(1, 32, 1000, 256, 256, BF16) == 0     # invalid
+
+
 def test_noalloc_rejects_before_touching_the_device(lib):
     """la_forward_noalloc: argument errors come back as from la_forward_ex, and
     a problem whose workspace exceeds the fixed scratch is LA_ERR_TOO_LARGE,

@@ -50,7 +50,8 @@ def test_gqa_1m_slices_and_states(workload):
     KV head (each against an fp64 GEMM over all its tokens) and the start state
     of every segment of KV heads 0, 13 and 31 as the pre-pass left it in the
     workspace, at the state bar; finiteness of every output and bitwise
-    repeatability of the whole pass.  For the 128-head-size workload the same
+    repeatability of the whole pass; the final states once more from the
+    state-only call (la_forward_state).  For the 128-head-size workload the same
     slices are checked once more with float32 output at the literal 2e-2 RMS.
     About 1-2 minutes per workload, most of it the fp64 state GEMMs on the host."""
     need_gpu()
@@ -76,6 +77,7 @@ def test_gqa_1m_slices_and_states(workload):
 
     o = torch.empty((w.B, w.Hq, w.N, w.dv), dtype=torch.bfloat16, device=DEV)
     run(o, S)
+    S_only = la.forward_state(k, v)   # the same final state without the outputs
     torch.cuda.synchronize()
     assert bool(torch.isfinite(o).all())
     W = 65536
@@ -111,8 +113,9 @@ def test_gqa_1m_slices_and_states(workload):
 
     for g in range(w.Hkv):
         ks_all, vs_all = f64(k[:, g:g + 1]), f64(v[:, g:g + 1])
-        check_state(f"group {g} final state", f64(S[:, g:g + 1]), oracle.final_state(ks_all, vs_all),
-                    torch.bfloat16)
+        ref_final = oracle.final_state(ks_all, vs_all)
+        check_state(f"group {g} final state", f64(S[:, g:g + 1]), ref_final, torch.bfloat16)
+        check_state(f"group {g} final state (state only)", f64(S_only[:, g:g + 1]), ref_final, torch.bfloat16)
         if g not in (0, 13, 31):
             continue
         # start state of every segment (j = 0 is zero: no initial state), the
