@@ -351,6 +351,30 @@ size_t la_backward_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N
                                    int64_t d, int64_t dv, int64_t block,
                                    la_dtype in_dtype);
 
+/*
+ * The initial-state gradient alone, without dq, dk and dv:
+ *     grad_s_in = grad_s_out + sum_h sum_t q_ht^T grad_o_ht
+ * per (batch, KV head), h over the query heads of its group (grad_s_out zero
+ * if NULL): la_backward's grad_s_in, which depends on q and grad_o only.  In
+ * a sequence split over devices, shard j's backward takes as grad_s_out the
+ * global one plus these sums over the later shards (the mirror of
+ * la_forward_state).
+ *   q [B][Hq][N][d], grad_o [B][Hq][N][dv] in in_dtype (NULL allowed when
+ *   N = 0); grad_s_out, grad_s_in [B][Hkv][d][dv] float32, grad_s_in
+ *   required, may be grad_s_out (in place), must not overlap q or grad_o.
+ *   Shapes and dtypes as la_forward_state with Hq query heads over Hkv.
+ *   workspace / workspace_bytes: at least la_backward_state_workspace_bytes.
+ */
+la_status la_backward_state(const void* q, const void* grad_o,
+                            int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv,
+                            la_dtype in_dtype, const float* grad_s_out, float* grad_s_in,
+                            void* workspace, size_t workspace_bytes, la_stream stream);
+
+/* Workspace bytes la_backward_state needs on the current device (0 when none
+ * or for invalid arguments). */
+size_t la_backward_state_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                                         int64_t d, int64_t dv, la_dtype in_dtype);
+
 /* Static, NUL-terminated description of a status code. */
 const char* la_status_str(la_status status);
 

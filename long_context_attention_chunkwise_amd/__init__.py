@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     LA_F32,
     LAError,
     backward,
+    backward_state,
     backward_workspace_bytes,
     decode_step,
     forward,

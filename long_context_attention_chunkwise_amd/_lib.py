@@ -18,7 +18,7 @@ STATUS_NAMES = {0: "LA_OK", 1: "LA_ERR_NULL", 2: "LA_ERR_SHAPE", 3: "LA_ERR_UNSU
 EXPORTS = ("la_forward", "la_forward_ex", "la_forward_states", "la_forward_outputs", "la_forward_workspace_bytes",
            "la_forward_variant", "la_forward_variant_workspace_bytes", "la_backward", "la_backward_workspace_bytes",
            "la_decode_step", "la_status_str", "la_forward_noalloc", "la_forward_state",
-           "la_forward_state_workspace_bytes")
+           "la_forward_state_workspace_bytes", "la_backward_state", "la_backward_state_workspace_bytes")
 LA_NOALLOC_SCRATCH_BYTES = 64 << 20
 LA_FMAP_IDENTITY, LA_FMAP_RELU = 0, 1
 
@@ -67,6 +67,10 @@ def load_library(path=LIB_PATH):
     lib.la_forward_state.restype = i32
     lib.la_forward_state_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
     lib.la_forward_state_workspace_bytes.restype = sz
+    lib.la_backward_state.argtypes = [vp, vp, i64, i64, i64, i64, i64, i64, i32, vp, vp, vp, sz, vp]
+    lib.la_backward_state.restype = i32
+    lib.la_backward_state_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, i32]
+    lib.la_backward_state_workspace_bytes.restype = sz
     lib.la_forward_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i32, i32, vp, vp, vp]
     lib.la_forward_noalloc.restype = i32
     lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp]
@@ -221,6 +225,41 @@ def forward_state(k, v, s_in=None, out=None, workspace=None):
                                   _ptr(workspace), ws_bytes, ctypes.c_void_p(stream))
     if st != LA_OK:
         raise LAError(st, "la_forward_state")
+    return out
+
+
+def backward_state(q, grad_o, Hkv, grad_s_out=None, out=None, workspace=None):
+    """la_backward_state: grad_s_in = grad_s_out + sum over each KV head's
+    query heads and all tokens of q_t^T grad_o_t, without dq, dk, dv.  q
+    [B,Hq,N,d], grad_o [B,Hq,N,dv] (float32 or bfloat16, the same); Hkv KV
+    heads; returns float32 [B,Hkv,d,dv] (`out`, which may be grad_s_out)."""
+    torch = _torch()
+    lib = load_library()
+    _check_tensor("q", q, 4, None)
+    dev = q.device
+    _check_tensor("grad_o", grad_o, 4, dev)
+    if q.dtype != grad_o.dtype:
+        raise TypeError("q and grad_o must share one dtype")
+    B, Hq, N, d = q.shape
+    dv = grad_o.shape[3]
+    if tuple(grad_o.shape[:3]) != (B, Hq, N):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, grad_o {tuple(grad_o.shape)}")
+    for name, t in (("grad_s_out", grad_s_out), ("out", out)):
+        if t is not None:
+            _check_tensor(name, t, 4, dev)
+            if t.dtype != torch.float32 or tuple(t.shape) != (B, Hkv, d, dv):
+                raise ValueError(f"{name} must be float32 [B, Hkv, d, dv]")
+    code = _dtype_code(q.dtype)
+    with torch.cuda.device(dev):
+        if out is None:
+            out = torch.empty((B, Hkv, d, dv), dtype=torch.float32, device=dev)
+        ws_bytes = int(lib.la_backward_state_workspace_bytes(B, Hq, Hkv, N, d, dv, code))
+        workspace = _workspace(workspace, ws_bytes, dev)
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.la_backward_state(_ptr(q), _ptr(grad_o), B, Hq, Hkv, N, d, dv, code, _ptr(grad_s_out),
+                                   _ptr(out), _ptr(workspace), ws_bytes, ctypes.c_void_p(stream))
+    if st != LA_OK:
+        raise LAError(st, "la_backward_state")
     return out
 
 

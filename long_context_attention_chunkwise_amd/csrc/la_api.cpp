@@ -449,9 +449,9 @@ la_status la_forward_state(const void* k, const void* v, int64_t B, int64_t Hkv,
   if (N == 0) {
     if (s_out != s_in) err = la::launch_copy_or_zero(s_out, s_in, ns / sizeof(float), hs);
   } else if (mfma) {
-    err = la::launch_state_total_bf16(k, v, s_in, s_out, B, Hkv, N, plan, static_cast<float*>(workspace), hs);
+    err = la::launch_state_total_bf16(k, v, s_in, s_out, B * Hkv, 1, N, plan, static_cast<float*>(workspace), hs);
   } else {
-    err = la::launch_state_total_f32(k, v, in_dtype == LA_BF16, s_in, s_out, B, Hkv, N, d, dv, hs);
+    err = la::launch_state_total_f32(k, v, in_dtype == LA_BF16, s_in, s_out, B * Hkv, 1, N, d, dv, hs);
   }
   return err == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
@@ -528,6 +528,52 @@ size_t la_backward_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N
                                    int64_t block, la_dtype in_dtype) {
   if (check_backward_shape(B, Hq, Hkv, N, d, dv, block, in_dtype, in_dtype) != LA_OK || N == 0) return 0;
   return backward_workspace(B, Hq, Hkv, N, d, dv, block, in_dtype);
+}
+
+size_t la_backward_state_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv,
+                                         la_dtype in_dtype) {
+  if (check_forward_shape(B, Hq, Hkv, N, d, dv, kBf16Block, in_dtype, in_dtype) != LA_OK) return 0;
+  if (!mfma_path(in_dtype, d, dv, kBf16Block) || N == 0) return 0;
+  return la::plan_state(B, Hq, N, d, device_cus()).workspace_bytes;
+}
+
+la_status la_backward_state(const void* q, const void* grad_o, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                            int64_t d, int64_t dv, la_dtype in_dtype, const float* grad_s_out, float* grad_s_in,
+                            void* workspace, size_t workspace_bytes, la_stream stream) {
+  la_status st = check_forward_shape(B, Hq, Hkv, N, d, dv, kBf16Block, in_dtype, in_dtype);
+  if (st != LA_OK) return st;
+  if (grad_s_in == nullptr || (N > 0 && (q == nullptr || grad_o == nullptr))) return LA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(grad_o) || !aligned16(grad_s_out) || !aligned16(grad_s_in)) return LA_ERR_ALIGN;
+  const size_t ei = esize(in_dtype);
+  const size_t nq = size_t(B * Hq * N * d) * ei, ndo = size_t(B * Hq * N * dv) * ei;
+  const size_t ns = size_t(B * Hkv * d * dv) * sizeof(float);
+  if (overlap(grad_s_in, ns, q, nq) || overlap(grad_s_in, ns, grad_o, ndo) ||
+      (grad_s_in != grad_s_out && overlap(grad_s_in, ns, grad_s_out, ns)))
+    return LA_ERR_ALIAS;
+  const bool mfma = mfma_path(in_dtype, d, dv, kBf16Block);
+  la::StatePlan plan;
+  if (mfma && N > 0) {
+    plan = la::plan_state(B, Hq, N, d, device_cus());
+    const size_t nw = plan.workspace_bytes;
+    if (workspace == nullptr || workspace_bytes < nw) return LA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return LA_ERR_ALIGN;
+    if (overlap(workspace, nw, q, nq) || overlap(workspace, nw, grad_o, ndo) ||
+        overlap(workspace, nw, grad_s_out, ns) || overlap(workspace, nw, grad_s_in, ns))
+      return LA_ERR_ALIAS;
+  }
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int G = static_cast<int>(Hq / Hkv);
+  hipError_t err = hipSuccess;
+  if (N == 0) {
+    if (grad_s_in != grad_s_out) err = la::launch_copy_or_zero(grad_s_in, grad_s_out, ns / sizeof(float), hs);
+  } else if (mfma) {
+    err = la::launch_state_total_bf16(q, grad_o, grad_s_out, grad_s_in, B * Hkv, G, N, plan,
+                                      static_cast<float*>(workspace), hs);
+  } else {
+    err = la::launch_state_total_f32(q, grad_o, in_dtype == LA_BF16, grad_s_out, grad_s_in, B * Hkv, G, N, d, dv,
+                                     hs);
+  }
+  return err == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 
 la_status la_backward(const void* q, const void* k, const void* v, const void* grad_o, void* grad_q,

@@ -1223,18 +1223,17 @@ hipError_t launch_segment_states(const void* k, const void* v, const float* s_in
   return hipGetLastError();
 }
 
-hipError_t launch_state_total_bf16(const void* k, const void* v, const float* s_in, float* s_out, int64_t B,
-                                   int64_t Hkv, int64_t N, const StatePlan& plan, float* workspace,
-                                   hipStream_t stream) {
-  // one summed segment (the whole sequence) in plan.R parts per chain
-  const int64_t chains = B * Hkv;
-  hipError_t e = launch_state_parts(k, v, workspace, chains, N, plan.nblocks, plan.nblocks, plan.blocks_per_part, 2,
-                                    plan.R, 0, plan.hd, stream);
+hipError_t launch_state_total_bf16(const void* a, const void* b, const float* s_in, float* s_out, int64_t chains,
+                                   int G, int64_t N, const StatePlan& plan, float* workspace, hipStream_t stream) {
+  // one summed segment (the whole sequence) of each of the chains * G input
+  // chains in plan.R parts; output chain c sums input chains c G .. c G + G - 1
+  hipError_t e = launch_state_parts(a, b, workspace, chains * G, N, plan.nblocks, plan.nblocks, plan.blocks_per_part,
+                                    2, plan.R, 0, plan.hd, stream);
   if (e != hipSuccess) return e;
   const int E = plan.hd * plan.hd;
   const int64_t total = chains * E;
   hipLaunchKernelGGL(sum_parts, dim3(unsigned((total + 255) / 256)), dim3(256), 0, stream, workspace, s_in, s_out,
-                     plan.R, E, total);
+                     G * plan.R, E, total);
   return hipGetLastError();
 }
 

@@ -248,8 +248,10 @@ hipError_t launch_scalar(const void* q, const void* k, const void* v, void* o, b
 
 namespace {
 
-// State-only pass on float32 FMA: s_out[c] = s_in[c] + sum over all N
-// tokens of k_t^T v_t for chain c = b * Hkv + g.  Workgroup (c, i-tile) owns
+// State-only pass on float32 FMA: s_out[c] = s_in[c] + sum over the G input
+// chains c G .. c G + G - 1 and all N tokens of k_t^T v_t (the forward's state:
+// G = 1, k and v of KV head c; the backward's: G query heads' q and dO).
+// Workgroup (c, i-tile) owns
 // rows [16 it, 16 it + 16) of the d x dv state, all dv columns; thread t owns
 // column t % 128 of rows 16 it + 8 (t / 128) + {0..7}.  The sequence is walked
 // in 64-token chunks staged in LDS.  s_out may be s_in (each entry is read
@@ -257,7 +259,7 @@ namespace {
 template <typename TI>
 __global__ __launch_bounds__(kThreads) void state_total_f32(const TI* __restrict__ k, const TI* __restrict__ v,
                                                            const float* s_in, float* s_out, int64_t N, int d,
-                                                           int dv) {
+                                                           int dv, int G) {
   constexpr int CH = 64, RT = 16;
   __shared__ float Ks[CH][RT];
   __shared__ float Vs[CH][kMaxD];
@@ -266,10 +268,11 @@ __global__ __launch_bounds__(kThreads) void state_total_f32(const TI* __restrict
   const int i0 = (blockIdx.x % nit) * RT;
   const int tid = threadIdx.x;
   const int j = tid % kMaxD, rg = tid / kMaxD;
-  const TI* kc = k + c * N * d;
-  const TI* vc = v + c * N * dv;
   float acc[8];
   for (int r = 0; r < 8; ++r) acc[r] = 0.0f;
+  for (int h = 0; h < G; ++h) {
+  const TI* kc = k + (c * G + h) * N * d;
+  const TI* vc = v + (c * G + h) * N * dv;
   for (int64_t t0 = 0; t0 < N; t0 += CH) {
     for (int e = tid; e < CH * RT; e += kThreads) {
       const int tt = e / RT, ii = e % RT;
@@ -288,6 +291,7 @@ __global__ __launch_bounds__(kThreads) void state_total_f32(const TI* __restrict
     }
     __syncthreads();
   }
+  }
   if (j < dv)
     for (int r = 0; r < 8; ++r) {
       const int i = i0 + 8 * rg + r;
@@ -301,16 +305,16 @@ __global__ __launch_bounds__(kThreads) void state_total_f32(const TI* __restrict
 }  // namespace
 
 hipError_t launch_state_total_f32(const void* k, const void* v, bool in_bf16, const float* s_in, float* s_out,
-                                  int64_t B, int64_t Hkv, int64_t N, int64_t d, int64_t dv, hipStream_t stream) {
-  if (d < 1 || d > kMaxD || dv < 1 || dv > kMaxD) return hipErrorInvalidValue;
-  const dim3 grid(unsigned(B * Hkv * ((d + 15) / 16)));
+                                  int64_t chains, int G, int64_t N, int64_t d, int64_t dv, hipStream_t stream) {
+  if (d < 1 || d > kMaxD || dv < 1 || dv > kMaxD || G < 1) return hipErrorInvalidValue;
+  const dim3 grid(unsigned(chains * ((d + 15) / 16)));
   if (in_bf16)
     hipLaunchKernelGGL((state_total_f32<uint16_t>), grid, dim3(kThreads), 0, stream,
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), s_in, s_out, N, int(d),
-                       int(dv));
+                       int(dv), G);
   else
     hipLaunchKernelGGL((state_total_f32<float>), grid, dim3(kThreads), 0, stream, static_cast<const float*>(k),
-                       static_cast<const float*>(v), s_in, s_out, N, int(d), int(dv));
+                       static_cast<const float*>(v), s_in, s_out, N, int(d), int(dv), G);
   return hipGetLastError();
 }
 

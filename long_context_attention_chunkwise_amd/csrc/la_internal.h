@@ -125,17 +125,19 @@ struct StatePlan {
 
 StatePlan plan_state(int64_t B, int64_t Hkv, int64_t N, int64_t d, int cus);
 
-// s_out = s_in (zeros if NULL) + sum over the N tokens of k_t^T v_t per chain,
-// bf16 inputs at d = dv = plan.hd, through the pre-pass kernel; the workspace
-// holds the plan's partials.  s_out may be s_in.
-hipError_t launch_state_total_bf16(const void* k, const void* v, const float* s_in, float* s_out, int64_t B,
-                                   int64_t Hkv, int64_t N, const StatePlan& plan, float* workspace,
-                                   hipStream_t stream);
+// s_out[c] = s_in[c] (zeros if NULL) + sum over the G input chains c G ..
+// c G + G - 1 and their N tokens of a_t^T b_t, for c < chains: the forward's
+// final state (a = k, b = v, G = 1) or the backward's initial-state gradient
+// (a = q, b = dO of the G query heads of a KV head).  bf16 inputs at d = dv =
+// plan.hd (plan_state over chains * G input chains), through the pre-pass
+// kernel; the workspace holds the plan's partials.  s_out may be s_in.
+hipError_t launch_state_total_bf16(const void* a, const void* b, const float* s_in, float* s_out, int64_t chains,
+                                   int G, int64_t N, const StatePlan& plan, float* workspace, hipStream_t stream);
 
 // The same on float32 FMA for float32 inputs, or bf16 inputs (in_bf16) off the
 // matrix-core shape: d and dv up to 128, no workspace.  s_out may be s_in.
-hipError_t launch_state_total_f32(const void* k, const void* v, bool in_bf16, const float* s_in, float* s_out,
-                                  int64_t B, int64_t Hkv, int64_t N, int64_t d, int64_t dv, hipStream_t stream);
+hipError_t launch_state_total_f32(const void* a, const void* b, bool in_bf16, const float* s_in, float* s_out,
+                                  int64_t chains, int G, int64_t N, int64_t d, int64_t dv, hipStream_t stream);
 
 // Backward work split: dK/dV walk each chain's segments from the end; segment
 // j starts from the sum of q^T dO over later segments and the group's heads.

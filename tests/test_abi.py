@@ -251,6 +251,28 @@ def test_forward_state_validation(lib):
     assert lib.la_forward_state_workspace_bytes(1, 32, 1000, 256, 256, BF16) == 0     # invalid
 
 
+def test_backward_state_validation(lib):
+    """la_backward_state (the initial-state gradient alone): argument errors
+    before any launch; its parts run over the query heads (128 chains at 1M
+    tokens: 4 parts each on 256 compute units)."""
+    def bs(q=Q, do=DO, B=1, Hq=8, Hkv=2, N=1000, d=128, dv=128, i=BF16, gso=None, gsi=DS, ws=WS, ws_bytes=1 << 32):
+        return lib.la_backward_state(q, do, B, Hq, Hkv, N, d, dv, i, gso, gsi, ws, ws_bytes, None)
+
+    assert bs(q=None) == NULL
+    assert bs(do=None) == NULL
+    assert bs(gsi=None) == NULL
+    assert bs(Hq=6, Hkv=4) == SHAPE
+    assert bs(d=256) == UNSUP
+    assert bs(do=ctypes.c_void_p(GB * 8 + 2)) == ALIGN
+    assert bs(gsi=ctypes.c_void_p(GB + 4096)) == ALIAS                        # inside q
+    assert bs(gso=S_OUT, gsi=ctypes.c_void_p(GB * 6 + 1024)) == ALIAS         # partly over grad_s_out
+    assert bs(ws=None) == WORKSPACE
+    assert bs(ws=ctypes.c_void_p(GB * 8 + 64)) == ALIAS                       # workspace inside grad_o
+    assert lib.la_backward_state_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, BF16) == 128 * 4 * 128 * 128 * 4
+    assert lib.la_backward_state_workspace_bytes(1, 128, 32, 1 << 20, 128, 128, F32) == 0
+    assert lib.la_backward_state_workspace_bytes(1, 6, 4, 1000, 128, 128, BF16) == 0   # invalid
+
+
 def test_noalloc_rejects_before_touching_the_device(lib):
     """la_forward_noalloc: argument errors come back as from la_forward_ex, and
     a problem whose workspace exceeds the fixed scratch is LA_ERR_TOO_LARGE,

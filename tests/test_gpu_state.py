@@ -1,7 +1,9 @@
-"""la_forward_state (the final state without outputs) against the oracle, and
-the sequence split it serves: shard totals computed independently, added up
-in order, and each shard's forward started from the sum of the earlier ones
-must reproduce one pass over the whole sequence."""
+"""la_forward_state (the final state without outputs) and la_backward_state
+(the initial-state gradient without dq, dk, dv) against the oracle, and the
+sequence split they serve: shard totals computed independently, added up in
+order, and each shard's forward started from the sum of the earlier ones, and
+each shard's backward from the global grad_s_out plus the later shards' sums,
+must reproduce one pass over the whole sequence, forward and backward."""
 import pytest
 import torch
 
@@ -92,3 +94,77 @@ def test_sequence_shards_equal_one_pass(d):
     ref_o, ref_S = oracle.chunkwise(f64(q), f64(k), f64(v), 64, f64(S0))
     check_close("sharded outputs", f64(torch.cat(outs, dim=2)), ref_o, BF16, BF16)
     check_state("sharded final state", f64(s), ref_S, BF16)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,dv,dtype,with_ds", [
+    (1, 8, 2, 3000, 128, 128, BF16, True),            # four query heads per KV head, ragged
+    (2, 4, 4, 777, 64, 64, BF16, False),              # one query head per KV head, head size 64
+    (1, 4, 1, 1, 128, 128, BF16, True),               # one token
+    (1, 16, 2, 5000, 128, 128, BF16, False),          # eight query heads per KV head
+    (1, 6, 2, 1000, 64, 96, torch.float32, True),     # float32, d != dv
+    (1, 3, 1, 500, 96, 64, BF16, False),              # bf16 off the matrix-core shape
+])
+def test_backward_state_matches_oracle(B, Hq, Hkv, N, d, dv, dtype, with_ds):
+    need_gpu()
+    say(f"case backward state B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} dv={dv} {dtype} grad_s_out={with_ds}")
+    w = synth.Workload("t", B, Hq, Hkv, N, d, dv, 64, dtype, dtype == BF16, dtype == torch.float32)
+    q, k, v = synth.make_qkv(w, DEV, seed=N + 31)
+    do = synth.make_grad((B, Hq, N, dv), DEV, seed=N + 32, dtype=dtype)
+    dS = synth.random_state((B, Hkv, d, dv), DEV, seed=N + 33, scale=0.5) if with_ds else None
+    got = la.backward_state(q, do, Hkv, grad_s_out=dS)
+    torch.cuda.synchronize()
+    ref = oracle.backward_chunkwise(f64(q), f64(k), f64(v), f64(do), 64, None, None if dS is None else f64(dS))[3]
+    check_state("grad_s_in", f64(got), ref, dtype)
+
+
+def test_backward_state_in_place_and_empty():
+    need_gpu()
+    say("case backward state: in place over grad_s_out; N = 0 passes grad_s_out through")
+    w = synth.Workload("t", 1, 8, 2, 2000, 128, 128, 64, BF16, True, False)
+    q, k, v = synth.make_qkv(w, DEV, seed=41)
+    do = synth.make_grad((1, 8, 2000, 128), DEV, seed=42)
+    dS = synth.random_state((1, 2, 128, 128), DEV, seed=43, scale=0.5)
+    ref = oracle.backward_chunkwise(f64(q), f64(k), f64(v), f64(do), 64, None, f64(dS))[3]
+    assert la.backward_state(q, do, 2, grad_s_out=dS, out=dS).data_ptr() == dS.data_ptr()
+    torch.cuda.synchronize()
+    check_state("grad_s_in in place", f64(dS), ref, BF16)
+    e = torch.empty((1, 8, 0, 128), dtype=BF16, device=DEV)
+    assert torch.equal(la.backward_state(e, e, 2, grad_s_out=dS), dS)
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_sequence_shards_backward_equals_one_pass(d):
+    """The backward of a 30,000-token sequence (8 query heads over 2 KV heads)
+    split into three shards: forward shard totals (la_forward_state) give each
+    shard's initial state, backward shard sums (la_backward_state) give each
+    shard's grad_s_out (the global one plus the later shards' sums), and each
+    shard's la_backward then yields its slice of dq, dk, dv; the first shard's
+    grad_s_in is the whole sequence's.  All against the oracle's backward over
+    the whole sequence."""
+    need_gpu()
+    B, Hq, Hkv, N = 1, 8, 2, 30000
+    cuts = [0, 9000, 21000, N]
+    say(f"case backward shards d={d} N={N} cuts={cuts}")
+    w = synth.Workload("t", B, Hq, Hkv, N, d, d, 64, BF16, True, False)
+    q, k, v = synth.make_qkv(w, DEV, seed=51)
+    do = synth.make_grad((B, Hq, N, d), DEV, seed=52)
+    S0 = synth.random_state((B, Hkv, d, d), DEV, seed=53, scale=0.5)
+    dS = synth.random_state((B, Hkv, d, d), DEV, seed=54, scale=0.5)
+    shards = [(a, b) for a, b in zip(cuts[:-1], cuts[1:])]
+    sl = lambda t, a, b: t[:, :, a:b].contiguous()
+    T = [la.forward_state(sl(k, a, b), sl(v, a, b)) for a, b in shards]           # independent
+    U = [la.backward_state(sl(q, a, b), sl(do, a, b), Hkv) for a, b in shards]    # independent
+    grads, ds_in = [], None
+    for j, (a, b) in enumerate(shards):
+        s_j = S0 + sum(T[:j], torch.zeros_like(S0))
+        g_j = dS + sum(U[j + 1:], torch.zeros_like(dS))
+        dq, dk, dv, ds_j = la.backward(sl(q, a, b), sl(k, a, b), sl(v, a, b), sl(do, a, b), s_in=s_j,
+                                       grad_s_out=g_j, return_state_grad=True)
+        grads.append((dq, dk, dv))
+        if j == 0:
+            ds_in = ds_j
+    torch.cuda.synchronize()
+    ref = oracle.backward_chunkwise(f64(q), f64(k), f64(v), f64(do), 64, f64(S0), f64(dS))
+    for i, name in enumerate(("dq", "dk", "dv")):
+        check_close(f"sharded {name}", f64(torch.cat([g[i] for g in grads], dim=2)), ref[i], BF16, BF16)
+    check_state("sharded grad_s_in", f64(ds_in), ref[3], BF16)
