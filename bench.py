@@ -344,8 +344,32 @@ def bench_backward(la, synth, torch, w, q, k, v, steps, warmup):
     ms = statistics.mean(per)
     nbytes = backward_bytes(w, w.N)
     flops = backward_flops(w, w.N)
-    del do, dq, dk, dv, ds, ws
+    del dq, dk, dv, ws
+    # the initial-state gradient alone (la_backward_state): q and dO read once
+    sws_bytes = int(lib.la_backward_state_workspace_bytes(w.B, w.Hq, w.Hkv, w.N, w.d, w.dv, la.LA_BF16))
+    sws = torch.empty(max(sws_bytes, 16), dtype=torch.uint8, device=dev)
+    sargs = (P(q.data_ptr()), P(do.data_ptr()), w.B, w.Hq, w.Hkv, w.N, w.d, w.dv, la.LA_BF16, None,
+             P(ds.data_ptr()), P(sws.data_ptr()), sws_bytes, P(stream.cuda_stream))
+    sev = []
+    for i in range(1 + steps):
+        e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        e[0].record(stream)
+        st = lib.la_backward_state(*sargs)
+        e[1].record(stream)
+        if st:
+            raise RuntimeError(f"backward state failed: {la.status_str(st)}")
+        if i:
+            sev.append(e)
+    torch.cuda.synchronize()
+    sms = statistics.mean(a.elapsed_time(b) for a, b in sev)
+    sbytes = w.B * w.Hq * w.N * (w.d + w.dv) * 2
+    state_only = {"ms_per_call": round(sms, 4), "bytes_alg": sbytes,
+                  "hbm_gb_per_s": round(sbytes / (sms * 1e-3) / 1e9, 1),
+                  "hbm_frac": round(sbytes / (sms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                  "what": "la_backward_state: grad_s_in alone (q and dO read once)"}
+    del do, ds, sws
     return {"steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4), "ms_per_step_wall": round(wall, 4),
+            "state_only": state_only,
             "tokens_per_s": round(w.B * w.N / (ms * 1e-3), 1),
             "config": {"workload": w.name, "grad_dtype": "bf16", "s_in": False, "grad_s_out": False},
             "hbm": {"bytes_alg": nbytes, "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
