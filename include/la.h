@@ -1,7 +1,8 @@
 /*
  * la.h — C ABI of liblightning.so: causal chunkwise linear attention
  * (Lightning Attention) forward pass, its backward pass, its feature-map,
- * normalised and non-causal variants, and batched single-token decode on AMD
+ * normalised and non-causal variants, state-only passes (the final state and
+ * the initial-state gradient alone), and batched single-token decode on AMD
  * Instinct MI355X (gfx950).
  *
  * What is computed.  Page "如何理解MiniMax股价创历史新高？拆解国产大模型技术底座"
