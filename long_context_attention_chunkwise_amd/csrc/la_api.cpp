@@ -358,6 +358,54 @@ la_status run_outputs(const ForwardCall& fc, const void* q, const void* k, const
   return err == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 
+// The state-only passes: s_out[c] = s_in[c] + sum over the Hin / Hkv input
+// chains of output chain c and their N tokens of a_t^T b_t, c < B * Hkv; the
+// forward's final state (a = k, b = v, Hin = Hkv) or the backward's
+// initial-state gradient (a = q, b = dO, Hin = Hq).  The forward's shape rules
+// apply with Hin heads over Hkv.
+size_t state_only_workspace(int64_t B, int64_t Hin, int64_t Hkv, int64_t N, int64_t d, int64_t dv,
+                            la_dtype in_dtype) {
+  if (check_forward_shape(B, Hin, Hkv, N, d, dv, kBf16Block, in_dtype, in_dtype) != LA_OK) return 0;
+  if (!mfma_path(in_dtype, d, dv, kBf16Block) || N == 0) return 0;
+  return la::plan_state(B, Hin, N, d, device_cus()).workspace_bytes;
+}
+
+la_status run_state_only(const void* a, const void* b, int64_t B, int64_t Hin, int64_t Hkv, int64_t N, int64_t d,
+                         int64_t dv, la_dtype in_dtype, const float* s_in, float* s_out, void* workspace,
+                         size_t workspace_bytes, la_stream stream) {
+  la_status st = check_forward_shape(B, Hin, Hkv, N, d, dv, kBf16Block, in_dtype, in_dtype);
+  if (st != LA_OK) return st;
+  if (s_out == nullptr || (N > 0 && (a == nullptr || b == nullptr))) return LA_ERR_NULL;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(s_in) || !aligned16(s_out)) return LA_ERR_ALIGN;
+  const size_t ei = esize(in_dtype);
+  const size_t na = size_t(B * Hin * N * d) * ei, nb = size_t(B * Hin * N * dv) * ei;
+  const size_t ns = size_t(B * Hkv * d * dv) * sizeof(float);
+  if (overlap(s_out, ns, a, na) || overlap(s_out, ns, b, nb) || (s_out != s_in && overlap(s_out, ns, s_in, ns)))
+    return LA_ERR_ALIAS;
+  const bool mfma = mfma_path(in_dtype, d, dv, kBf16Block);
+  la::StatePlan plan;
+  if (mfma && N > 0) {
+    plan = la::plan_state(B, Hin, N, d, device_cus());
+    const size_t nw = plan.workspace_bytes;
+    if (workspace == nullptr || workspace_bytes < nw) return LA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return LA_ERR_ALIGN;
+    if (overlap(workspace, nw, a, na) || overlap(workspace, nw, b, nb) || overlap(workspace, nw, s_in, ns) ||
+        overlap(workspace, nw, s_out, ns))
+      return LA_ERR_ALIAS;
+  }
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int G = static_cast<int>(Hin / Hkv);
+  hipError_t err = hipSuccess;
+  if (N == 0) {
+    if (s_out != s_in) err = la::launch_copy_or_zero(s_out, s_in, ns / sizeof(float), hs);
+  } else if (mfma) {
+    err = la::launch_state_total_bf16(a, b, s_in, s_out, B * Hkv, G, N, plan, static_cast<float*>(workspace), hs);
+  } else {
+    err = la::launch_state_total_f32(a, b, in_dtype == LA_BF16, s_in, s_out, B * Hkv, G, N, d, dv, hs);
+  }
+  return err == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
 }  // namespace
 
 namespace la {
@@ -415,45 +463,25 @@ la_status la_forward_outputs(const void* q, const void* k, const void* v, void* 
 
 size_t la_forward_state_workspace_bytes(int64_t B, int64_t Hkv, int64_t N, int64_t d, int64_t dv,
                                         la_dtype in_dtype) {
-  if (check_forward_shape(B, Hkv, Hkv, N, d, dv, kBf16Block, in_dtype, in_dtype) != LA_OK) return 0;
-  if (!mfma_path(in_dtype, d, dv, kBf16Block) || N == 0) return 0;
-  return la::plan_state(B, Hkv, N, d, device_cus()).workspace_bytes;
+  return state_only_workspace(B, Hkv, Hkv, N, d, dv, in_dtype);
 }
 
 la_status la_forward_state(const void* k, const void* v, int64_t B, int64_t Hkv, int64_t N, int64_t d, int64_t dv,
                            la_dtype in_dtype, const float* s_in, float* s_out, void* workspace,
                            size_t workspace_bytes, la_stream stream) {
-  // the forward's shape rules with one query head per KV head (no q, no o)
-  la_status st = check_forward_shape(B, Hkv, Hkv, N, d, dv, kBf16Block, in_dtype, in_dtype);
-  if (st != LA_OK) return st;
-  if (s_out == nullptr || (N > 0 && (k == nullptr || v == nullptr))) return LA_ERR_NULL;
-  if (!aligned16(k) || !aligned16(v) || !aligned16(s_in) || !aligned16(s_out)) return LA_ERR_ALIGN;
-  const size_t ei = esize(in_dtype);
-  const size_t nk = size_t(B * Hkv * N * d) * ei, nv = size_t(B * Hkv * N * dv) * ei;
-  const size_t ns = size_t(B * Hkv * d * dv) * sizeof(float);
-  if (overlap(s_out, ns, k, nk) || overlap(s_out, ns, v, nv) || (s_out != s_in && overlap(s_out, ns, s_in, ns)))
-    return LA_ERR_ALIAS;
-  const bool mfma = mfma_path(in_dtype, d, dv, kBf16Block);
-  la::StatePlan plan;
-  if (mfma && N > 0) {
-    plan = la::plan_state(B, Hkv, N, d, device_cus());
-    const size_t nw = plan.workspace_bytes;
-    if (workspace == nullptr || workspace_bytes < nw) return LA_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return LA_ERR_ALIGN;
-    if (overlap(workspace, nw, k, nk) || overlap(workspace, nw, v, nv) || overlap(workspace, nw, s_in, ns) ||
-        overlap(workspace, nw, s_out, ns))
-      return LA_ERR_ALIAS;
-  }
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  hipError_t err = hipSuccess;
-  if (N == 0) {
-    if (s_out != s_in) err = la::launch_copy_or_zero(s_out, s_in, ns / sizeof(float), hs);
-  } else if (mfma) {
-    err = la::launch_state_total_bf16(k, v, s_in, s_out, B * Hkv, 1, N, plan, static_cast<float*>(workspace), hs);
-  } else {
-    err = la::launch_state_total_f32(k, v, in_dtype == LA_BF16, s_in, s_out, B * Hkv, 1, N, d, dv, hs);
-  }
-  return err == hipSuccess ? LA_OK : LA_ERR_HIP;
+  return run_state_only(k, v, B, Hkv, Hkv, N, d, dv, in_dtype, s_in, s_out, workspace, workspace_bytes, stream);
+}
+
+size_t la_backward_state_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv,
+                                         la_dtype in_dtype) {
+  return state_only_workspace(B, Hq, Hkv, N, d, dv, in_dtype);
+}
+
+la_status la_backward_state(const void* q, const void* grad_o, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                            int64_t d, int64_t dv, la_dtype in_dtype, const float* grad_s_out, float* grad_s_in,
+                            void* workspace, size_t workspace_bytes, la_stream stream) {
+  return run_state_only(q, grad_o, B, Hq, Hkv, N, d, dv, in_dtype, grad_s_out, grad_s_in, workspace,
+                        workspace_bytes, stream);
 }
 
 la_status la_forward(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t Hq, int64_t Hkv,
@@ -528,52 +556,6 @@ size_t la_backward_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N
                                    int64_t block, la_dtype in_dtype) {
   if (check_backward_shape(B, Hq, Hkv, N, d, dv, block, in_dtype, in_dtype) != LA_OK || N == 0) return 0;
   return backward_workspace(B, Hq, Hkv, N, d, dv, block, in_dtype);
-}
-
-size_t la_backward_state_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t dv,
-                                         la_dtype in_dtype) {
-  if (check_forward_shape(B, Hq, Hkv, N, d, dv, kBf16Block, in_dtype, in_dtype) != LA_OK) return 0;
-  if (!mfma_path(in_dtype, d, dv, kBf16Block) || N == 0) return 0;
-  return la::plan_state(B, Hq, N, d, device_cus()).workspace_bytes;
-}
-
-la_status la_backward_state(const void* q, const void* grad_o, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
-                            int64_t d, int64_t dv, la_dtype in_dtype, const float* grad_s_out, float* grad_s_in,
-                            void* workspace, size_t workspace_bytes, la_stream stream) {
-  la_status st = check_forward_shape(B, Hq, Hkv, N, d, dv, kBf16Block, in_dtype, in_dtype);
-  if (st != LA_OK) return st;
-  if (grad_s_in == nullptr || (N > 0 && (q == nullptr || grad_o == nullptr))) return LA_ERR_NULL;
-  if (!aligned16(q) || !aligned16(grad_o) || !aligned16(grad_s_out) || !aligned16(grad_s_in)) return LA_ERR_ALIGN;
-  const size_t ei = esize(in_dtype);
-  const size_t nq = size_t(B * Hq * N * d) * ei, ndo = size_t(B * Hq * N * dv) * ei;
-  const size_t ns = size_t(B * Hkv * d * dv) * sizeof(float);
-  if (overlap(grad_s_in, ns, q, nq) || overlap(grad_s_in, ns, grad_o, ndo) ||
-      (grad_s_in != grad_s_out && overlap(grad_s_in, ns, grad_s_out, ns)))
-    return LA_ERR_ALIAS;
-  const bool mfma = mfma_path(in_dtype, d, dv, kBf16Block);
-  la::StatePlan plan;
-  if (mfma && N > 0) {
-    plan = la::plan_state(B, Hq, N, d, device_cus());
-    const size_t nw = plan.workspace_bytes;
-    if (workspace == nullptr || workspace_bytes < nw) return LA_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return LA_ERR_ALIGN;
-    if (overlap(workspace, nw, q, nq) || overlap(workspace, nw, grad_o, ndo) ||
-        overlap(workspace, nw, grad_s_out, ns) || overlap(workspace, nw, grad_s_in, ns))
-      return LA_ERR_ALIAS;
-  }
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  const int G = static_cast<int>(Hq / Hkv);
-  hipError_t err = hipSuccess;
-  if (N == 0) {
-    if (grad_s_in != grad_s_out) err = la::launch_copy_or_zero(grad_s_in, grad_s_out, ns / sizeof(float), hs);
-  } else if (mfma) {
-    err = la::launch_state_total_bf16(q, grad_o, grad_s_out, grad_s_in, B * Hkv, G, N, plan,
-                                      static_cast<float*>(workspace), hs);
-  } else {
-    err = la::launch_state_total_f32(q, grad_o, in_dtype == LA_BF16, grad_s_out, grad_s_in, B * Hkv, G, N, d, dv,
-                                     hs);
-  }
-  return err == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 
 la_status la_backward(const void* q, const void* k, const void* v, const void* grad_o, void* grad_q,
