@@ -560,8 +560,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
       const floatx4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
       if (act) {
       bf16x8 pop[4][2];
-      float den[4], inv[4];  // normaliser of row 16ti + l16 (kNorm only)
-      (void)den;
+      float inv[4];  // 1 / normaliser of row 16ti + l16 (kNorm only)
       (void)inv;
       for (int ti = 0; ti < 4; ++ti) {
         floatx4 pt[4];
@@ -571,32 +570,34 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
             pt[si] = mfma(ld_lds16(ks + (16 * si + l16) * RKV + 32 * ds + 8 * grp), qa[ti][ds], pt[si]);
         }
         pt[ti] = causal_mask(pt[ti], l16, grp);
-        if constexpr (kN) {
-          // this lane's share of sum_s P^T[s][t] for t = 16ti + l16
-          float sum = 0.0f;
-          for (int si = 0; si <= ti; ++si) sum += (pt[si][0] + pt[si][1]) + (pt[si][2] + pt[si][3]);
-          den[ti] = sum;
-        }
         pop[ti][0] = pack_tiles(pt[0], ti >= 1 ? pt[1] : z4);
         if (ti >= 2) pop[ti][1] = pack_tiles(pt[2], ti == 3 ? pt[3] : z4);
       }
       if constexpr (kN) {
-        // earlier tokens: phi(q_t) . z; lane (l16, grp) holds q_t entries 32ds + 8grp + j
+        // Denominators on the matrix cores, as one more 16-column output
+        // tile: rows 0-7 of its A operand hold the high bf16 part of z and
+        // ones against the bf16 score operands the numerator uses, rows 8-15
+        // the low part of z (z = hi + lo to about 16 significant bits), so
+        // output row 0 of column t is phi(q_t) . z_hi + sum_s P^T[s][t] and
+        // row 8 is phi(q_t) . z_lo; lane (l16, grp) holds rows 4grp.., and
+        // lanes l and l ^ 32 hold rows 0 and 8 of column 16ti + l16.
+        const bool hi_row = l16 < 8;
+        bf16x8 za_op[NDS];
         for (int ds = 0; ds < NDS; ++ds) {
           const floatx4 za = *reinterpret_cast<const floatx4*>(&zs[32 * ds + 8 * grp]);
           const floatx4 zb = *reinterpret_cast<const floatx4*>(&zs[32 * ds + 8 * grp + 4]);
-          for (int ti = 0; ti < 4; ++ti) {
-            float dsum = 0.0f;
-            for (int j = 0; j < 4; ++j)
-              dsum += float(qa[ti][ds][j]) * za[j] + float(qa[ti][ds][j + 4]) * zb[j];
-            den[ti] += dsum;
+          for (int j = 0; j < 4; ++j) {
+            const __bf16 ha = (__bf16)za[j], hb = (__bf16)zb[j];
+            za_op[ds][j] = hi_row ? ha : (__bf16)(za[j] - float(ha));
+            za_op[ds][j + 4] = hi_row ? hb : (__bf16)(zb[j] - float(hb));
           }
         }
+        const bf16x8 ones = hi_row ? ones_bf16x8() : zero_bf16x8();
         for (int ti = 0; ti < 4; ++ti) {
-          float x = den[ti];
-          x += __shfl_xor(x, 16);
-          x += __shfl_xor(x, 32);
-          inv[ti] = 1.0f / (x + eps);
+          floatx4 dt = mfma(ones, pop[ti][0], z4);
+          if (ti >= 2) dt = mfma(ones, pop[ti][1], dt);
+          for (int ds = 0; ds < NDS; ++ds) dt = mfma(za_op[ds], qa[ti][ds], dt);
+          inv[ti] = 1.0f / ((dt[0] + __shfl_xor(dt[0], 32)) + eps);
         }
       }
 
