@@ -130,7 +130,9 @@ VarPlan plan_variant(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, i
   VarPlan vp;
   vp.causal = causal;
   vp.norm = norm;
-  vp.base = plan_bf16(B, Hq, Hkv, N, d, dv, cus);
+  // causal forms at head size 64 with one query head per KV head run the
+  // one-wave kernel, as the plain forward does
+  vp.base = plan_bf16(B, Hq, Hkv, N, d, dv, cus, causal);
   Bf16Plan& p = vp.base;
   if (p.nblocks == 0) return vp;
   const size_t chains = size_t(B * Hkv);

@@ -741,18 +741,29 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
 // block step is the four-wave kernel's with the wave owning every state
 // column: scores P^T = K Q^T, outputs O^T = S^T Q^T + V^T P^T in two 32-column
 // quarters, then S += K^T V and its bf16 copy.
+//
+// Flags (causal feature-map variants), as in the four-wave kernel: kRelu
+// applies phi = ReLU to q and to k before it enters LDS; kNorm divides each
+// output row by phi(q_t) . z + eps, z (64 floats) running beside the state:
+// kept in float32 accumulator tiles (K^T times a ones operand), published in
+// LDS once per block, and read back in operand layout for the denominators.
 // ---------------------------------------------------------------------------
-template <bool OUT_F32>
+template <bool OUT_F32, int FL = 0>
 __global__ __launch_bounds__(64, 1) void fwd_bf16_solo(const uint16_t* __restrict__ q,
                                                        const uint16_t* __restrict__ k,
                                                        const uint16_t* __restrict__ v, void* __restrict__ o,
                                                        const float* starts, const float* s_in, float* s_out,
-                                                       int64_t N, int64_t nblocks, int64_t blocks_per_seg, int P) {
+                                                       int64_t N, int64_t nblocks, int64_t blocks_per_seg, int P,
+                                                       const float* zstarts, const float* z_in, float* z_out,
+                                                       float eps) {
+  constexpr bool kN = (FL & kNorm) != 0;
+  constexpr bool kR = (FL & kRelu) != 0;
   constexpr int HD = 64, NDS = HD / 32, NDT = HD / 16, NM = HD / 32, NJ = HD / 16;
   constexpr int RKV = HD + 16, RST = HD + 8, CPR = HD / 8, RPI = 64 / CPR, NLD = C / RPI;
   __shared__ __align__(16) uint16_t ks[C * RKV];
   __shared__ __align__(16) uint16_t vs[C * RKV];
   __shared__ __align__(16) uint16_t st[HD * RST];
+  __shared__ __align__(16) float zs[kN ? HD : 4];
 
   const int lane = threadIdx.x, l16 = lane & 15, grp = lane >> 4;
   const int seg = blockIdx.x % P;
@@ -773,6 +784,18 @@ __global__ __launch_bounds__(64, 1) void fwd_bf16_solo(const uint16_t* __restric
   for (int jn = 0; jn < NJ; ++jn)
     for (int dt = 0; dt < NDT; ++dt)
       *reinterpret_cast<bf16x4*>(&st[(16 * jn + l16) * RST + 16 * dt + 4 * grp]) = to_bf16x4(sacc[jn][dt]);
+
+  // normaliser sums, entries 16jj + 4grp + i (every column equal)
+  floatx4 zacc[NJ];
+  for (int jj = 0; jj < NJ; ++jj) zacc[jj] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (kN) {
+    const float* z0 = zstarts ? zstarts + (bh * P + seg) * HD : (z_in ? z_in + bh * HD : nullptr);
+    if (z0 != nullptr)
+      for (int jj = 0; jj < NJ; ++jj)
+        for (int i = 0; i < 4; ++i) zacc[jj][i] = z0[16 * jj + 4 * grp + i];
+    if (l16 == 0)
+      for (int jj = 0; jj < NJ; ++jj) *reinterpret_cast<floatx4*>(&zs[16 * jj + 4 * grp]) = zacc[jj];
+  }
 
   // one block's K and V: lane moves chunk lane % CPR of rows lane / CPR + RPI i
   uint4 kr[NLD], vr[NLD];
@@ -797,6 +820,11 @@ __global__ __launch_bounds__(64, 1) void fwd_bf16_solo(const uint16_t* __restric
   };
   if (blk0 < blk1) load_block(blk0);
   for (int64_t blk = blk0; blk < blk1; ++blk) {
+    if constexpr (kR) {
+      for (int i = 0; i < NLD; ++i) kr[i] = relu_bf16x8(kr[i]);
+      for (int ti = 0; ti < 4; ++ti)
+        for (int ds = 0; ds < NDS; ++ds) qa[ti][ds] = relu_bf16x8(qa[ti][ds]);
+    }
     {
       const int c = lane % CPR;
       for (int i = 0; i < NLD; ++i) {
@@ -820,6 +848,32 @@ __global__ __launch_bounds__(64, 1) void fwd_bf16_solo(const uint16_t* __restric
       pop[ti][0] = pack_tiles(pt[0], ti >= 1 ? pt[1] : z4);
       if (ti >= 2) pop[ti][1] = pack_tiles(pt[2], ti == 3 ? pt[3] : z4);
     }
+    float inv[4];  // 1 / normaliser of row 16ti + l16 (kNorm only)
+    (void)inv;
+    if constexpr (kN) {
+      // denominators as one more MFMA output tile, formed as in the
+      // four-wave kernel: rows 0-7 of the A operand hold z's high bf16 part
+      // and ones, rows 8-15 its low part; lanes l and l ^ 32 add up
+      const bool hi_row = l16 < 8;
+      const bf16x8 ones = hi_row ? ones_bf16x8() : zero_bf16x8();
+      floatx4 dt[4];
+      for (int ti = 0; ti < 4; ++ti) {
+        dt[ti] = mfma(ones, pop[ti][0], z4);
+        if (ti >= 2) dt[ti] = mfma(ones, pop[ti][1], dt[ti]);
+      }
+      for (int ds = 0; ds < NDS; ++ds) {
+        const floatx4 za = *reinterpret_cast<const floatx4*>(&zs[32 * ds + 8 * grp]);
+        const floatx4 zb = *reinterpret_cast<const floatx4*>(&zs[32 * ds + 8 * grp + 4]);
+        bf16x8 zop;
+        for (int j = 0; j < 4; ++j) {
+          const __bf16 ha = (__bf16)za[j], hb = (__bf16)zb[j];
+          zop[j] = hi_row ? ha : (__bf16)(za[j] - float(ha));
+          zop[j + 4] = hi_row ? hb : (__bf16)(zb[j] - float(hb));
+        }
+        for (int ti = 0; ti < 4; ++ti) dt[ti] = mfma(zop, qa[ti][ds], dt[ti]);
+      }
+      for (int ti = 0; ti < 4; ++ti) inv[ti] = 1.0f / ((dt[ti][0] + __shfl_xor(dt[ti][0], 32)) + eps);
+    }
     bf16x8 held[4];  // bf16 outputs of quarter 0, stored with quarter 1
     for (int m = 0; m < NM; ++m) {
       floatx4 acc[2][4];
@@ -839,6 +893,10 @@ __global__ __launch_bounds__(64, 1) void fwd_bf16_solo(const uint16_t* __restric
         acc[h2][2] = mfma(va1, pop[2][1], acc[h2][2]);
         acc[h2][3] = mfma(va1, pop[3][1], acc[h2][3]);
       }
+      if constexpr (kN)
+        for (int h2 = 0; h2 < 2; ++h2)
+          for (int ti = 0; ti < 4; ++ti)
+            for (int i = 0; i < 4; ++i) acc[h2][ti][i] *= inv[ti];
       if constexpr (OUT_F32) {
         for (int ti = 0; ti < 4; ++ti) {
           const int64_t t = blk * C + 16 * ti + l16;
@@ -873,6 +931,14 @@ __global__ __launch_bounds__(64, 1) void fwd_bf16_solo(const uint16_t* __restric
       for (int jn = 0; jn < NJ; ++jn)
         for (int dt = 0; dt < NDT; ++dt)
           *reinterpret_cast<bf16x4*>(&st[(16 * jn + l16) * RST + 16 * dt + 4 * grp]) = to_bf16x4(sacc[jn][dt]);
+      if constexpr (kN) {
+        // z += K_b^T 1 (after this block's denominators have read z)
+        for (int p = 0; p < 2; ++p)
+          for (int jj = 0; jj < NJ; ++jj)
+            zacc[jj] = mfma(tr_operand(ks, p, 16 * jj, l16, grp, 4, RKV), ones_bf16x8(), zacc[jj]);
+        if (l16 == 0)
+          for (int jj = 0; jj < NJ; ++jj) *reinterpret_cast<floatx4*>(&zs[16 * jj + 4 * grp]) = zacc[jj];
+      }
     }
     __syncthreads();  // (one wave: the tile reads above precede the next block's stores)
   }
@@ -883,6 +949,10 @@ __global__ __launch_bounds__(64, 1) void fwd_bf16_solo(const uint16_t* __restric
       for (int dt = 0; dt < NDT; ++dt)
         for (int i = 0; i < 4; ++i) so[(16 * dt + 4 * grp + i) * HD + 16 * jn + l16] = sacc[jn][dt][i];
   }
+  if constexpr (kN)
+    if (z_out != nullptr && seg == P - 1 && l16 == 0)
+      for (int jj = 0; jj < NJ; ++jj)
+        for (int i = 0; i < 4; ++i) z_out[bh * HD + 16 * jj + 4 * grp + i] = zacc[jj][i];
 }
 
 // Pre-pass: partial[c][j][r] = sum of K_b^T V_b over part r of segment
@@ -1302,7 +1372,12 @@ hipError_t variant_outputs(const void* q, const void* k, const void* v, void* o,
 #define LA_VAR(LAUNCH)                                                                                              \
   LAUNCH(grid, stream, q, k, v, o, st ? starts : nullptr, st ? nullptr : s_in, s_out, iHq, iHkv, p.subgroups, N, \
          p.nblocks, p.blocks_per_seg, p.P, zs, zi, z_out, eps)
-    if (p.hd == 64) {
+    if (p.solo) {
+      hipLaunchKernelGGL((fwd_bf16_solo<OUT_F32, FL>), grid, dim3(64), 0, stream, static_cast<const uint16_t*>(q),
+                         static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), o,
+                         st ? starts : nullptr, st ? nullptr : s_in, s_out, N, p.nblocks, p.blocks_per_seg, p.P, zs,
+                         zi, z_out, eps);
+    } else if (p.hd == 64) {
       if (p.gw == 4) LA_VAR((launch_g4<OUT_F32, FL, 64>));
       else
         launch_g4<OUT_F32, FL, 64, true>(grid, stream, q, k, v, o, st ? starts : nullptr, st ? nullptr : s_in,
@@ -1383,10 +1458,10 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
     const float* si = plan.use_starts ? nullptr : s_in;
     if (out_f32)
       hipLaunchKernelGGL((fwd_bf16_solo<true>), grid, dim3(64), 0, stream, q16, k16, v16, o, starts, si, s_out, N,
-                         plan.nblocks, plan.blocks_per_seg, plan.P);
+                         plan.nblocks, plan.blocks_per_seg, plan.P, nullptr, nullptr, nullptr, 0.0f);
     else
       hipLaunchKernelGGL((fwd_bf16_solo<false>), grid, dim3(64), 0, stream, q16, k16, v16, o, starts, si, s_out, N,
-                         plan.nblocks, plan.blocks_per_seg, plan.P);
+                         plan.nblocks, plan.blocks_per_seg, plan.P, nullptr, nullptr, nullptr, 0.0f);
   } else if (plan.hd == 64) {
     // head size 64: the four-wave kernel, with gw = 1 or 2 query heads per
     // workgroup (idle waves) for groups that are not a multiple of four

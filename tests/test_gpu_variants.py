@@ -92,6 +92,20 @@ def test_plain_variant_is_the_forward(Hq, Hkv):
     assert torch.equal(a, b) and torch.equal(Sa, Sb)
 
 
+def test_plain_variant_is_the_forward_head_size_64_one_head_per_kv_head():
+    """The same at head size 64 with one query head per KV head, where both
+    calls run the one-wave kernel over many segments."""
+    need_gpu()
+    say("case plain variant = forward, d=64, Hq=Hkv=4, N=9000")
+    w = synth.Workload("t", 1, 4, 4, 9000, 64, 64, 64, BF16, False, False)
+    q, k, v = synth.make_qkv(w, DEV, seed=8)
+    S0 = synth.random_state((1, 4, 64, 64), DEV, seed=9, scale=0.5)
+    a, Sa, _ = la.forward_variant(q, k, v, s_in=S0, return_state=True)
+    b, Sb = la.forward(q, k, v, s_in=S0, return_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(Sa, Sb)
+
+
 def test_variants_gqa_1m_slices():
     """The 1M-token GQA workload (raw q, k; phi = ReLU inside): the causal
     normalised variant on the first and last 4096 tokens of KV groups 0 and
@@ -203,7 +217,10 @@ def test_variant_in_place_state_and_normaliser(dtype):
     (False, "identity", False, 0.0, BF16, 8, 1, 1000),        # G = 8
     (False, "relu", False, 0.0, BF16, 4, 1, 100),             # two blocks, ragged
     (False, "relu", True, 1e-6, BF16, 4, 1, 1),               # one token
-    (True, "relu", True, 1e-6, torch.float32, 4, 4, 3000),   # G = 1 (three idle waves per workgroup)
+    (True, "relu", True, 1e-6, torch.float32, 4, 4, 3000),   # G = 1: one-wave workgroups, ten segments
+    (True, "relu", True, 1e-6, BF16, 2, 2, 20000),            # G = 1, 79 segments per head
+    (True, "relu", True, 1e-6, BF16, 2, 2, 1),                # G = 1, one token (z_in read directly)
+    (True, "relu", False, 0.0, BF16, 4, 4, 1000),             # G = 1, ReLU without normalisation
     (False, "relu", True, 1e-6, torch.float32, 4, 4, 3000),  # G = 1, non-causal
     (True, "identity", False, 0.0, BF16, 6, 3, 1000),         # G = 2
     (False, "identity", False, 0.0, BF16, 6, 2, 1000),        # G = 3, non-causal
@@ -211,8 +228,9 @@ def test_variant_in_place_state_and_normaliser(dtype):
 ])
 def test_variant_head_size_64(causal, fmap, norm, eps, out_dtype, Hq, Hkv, N):
     """Variants at head size 64, any group size: causal ones on the four-wave
-    forward kernel, the non-causal one on its own kernel, both after the
-    pre-pass with the variant flags."""
+    forward kernel (on one-wave workgroups for one query head per KV head),
+    the non-causal one on its own kernel, both after the pre-pass with the
+    variant flags."""
     need_gpu()
     say(f"case variant d=64 causal={causal} fmap={fmap} norm={norm} out={out_dtype} Hq={Hq} Hkv={Hkv} N={N}")
     w = synth.Workload("t", 1, Hq, Hkv, N, 64, 64, 64, BF16, False, False)
