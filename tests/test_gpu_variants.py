@@ -92,6 +92,26 @@ def test_plain_variant_is_the_forward(Hq, Hkv):
     assert torch.equal(a, b) and torch.equal(Sa, Sb)
 
 
+def test_variant_head_size_64_one_head_per_kv_head_two_batches():
+    """Two batch entries of three heads (one query head per KV head) on the
+    one-wave kernel: every (batch, head) chain reads its own s_in and z_in and
+    writes its own S_out and z_out, over several segments and a ragged tail."""
+    need_gpu()
+    say("case variant d=64 B=2 Hq=Hkv=3 N=2500 ReLU-normalised")
+    w = synth.Workload("t", 2, 3, 3, 2500, 64, 64, 64, BF16, False, False)
+    q, k, v = synth.make_qkv(w, DEV, seed=12)
+    S0 = synth.random_state((2, 3, 64, 64), DEV, seed=13, scale=0.5)
+    Z0 = synth.random_state((2, 3, 64), DEV, seed=14).abs()
+    o, S, Z = la.forward_variant(q, k, v, feature_map="relu", normalize=True, eps=1e-6, s_in=S0, z_in=Z0,
+                                 return_state=True)
+    torch.cuda.synchronize()
+    ref_o, ref_S, ref_z = oracle.variant(f64(q), f64(k), f64(v), causal=True, relu=True, normalize=True, eps=1e-6,
+                                         s_in=f64(S0), z_in=f64(Z0))
+    check_close("o", f64(o), ref_o, BF16, BF16, per_row=True)
+    check_state("S_out", f64(S), ref_S, BF16)
+    check_state("z_out", f64(Z), ref_z, BF16)
+
+
 def test_plain_variant_is_the_forward_head_size_64_one_head_per_kv_head():
     """The same at head size 64 with one query head per KV head, where both
     calls run the one-wave kernel over many segments."""
