@@ -173,6 +173,38 @@ def test_variants_gqa_1m_slices():
         check_state(f"non-causal state group {g}", f64(S_nc[:, gs]), S_t, BF16)
 
 
+def test_variants_mha_1m_d64_slices():
+    """The 1M-token workload with one query head per KV head at head size 64
+    (32 heads), where the causal ReLU-normalised variant runs the one-wave
+    kernel over 32 segments per head: heads 0 and 31 on their first and last
+    4096 tokens and on a window across the first segment boundary (token
+    32768), each from the oracle's carried (S, z), and their final (S, z)."""
+    need_gpu()
+    w = synth.WORKLOADS["mha_1m_d64"]
+    N, W = w.N, 4096
+    say(f"case variants mha_1m_d64: N={N}")
+    q, k, v = synth.make_qkv(w, DEV, seed=0)
+    eps = 1e-6
+    o, S, Z = la.forward_variant(q, k, v, causal=True, feature_map="relu", normalize=True, eps=eps,
+                                 return_state=True)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all())
+    for h in (0, 31):
+        hs = slice(h, h + 1)
+        kr = np.maximum(f64(k[:, hs]), 0.0)
+        vh = f64(v[:, hs])
+        ones = np.ones(kr.shape[:3] + (1,))
+        for lo, hi in ((0, W), (32768 - W // 2, 32768 + W // 2), (N - W, N)):
+            s_in = oracle.final_state(kr[:, :, :lo], vh[:, :, :lo]) if lo else None
+            z_in = oracle.final_state(kr[:, :, :lo], ones[:, :, :lo])[..., 0] if lo else None
+            ref = oracle.variant(f64(q[:, hs, lo:hi]), f64(k[:, hs, lo:hi]), vh[:, :, lo:hi], causal=True, relu=True,
+                                 normalize=True, eps=eps, s_in=s_in, z_in=z_in)
+            check_close(f"causal normalised head {h} tokens [{lo}, {hi})", f64(o[:, hs, lo:hi]), ref[0], BF16, BF16,
+                        per_row=True)
+        check_state(f"final state head {h}", f64(S[:, hs]), oracle.final_state(kr, vh), BF16)
+        check_state(f"final z head {h}", f64(Z[:, hs]), oracle.final_state(kr, ones)[..., 0], BF16)
+
+
 F32_CASES = [
     # causal, fmap, normalize, eps, s_in, z_in, B, Hq, Hkv, N, d, dv, block, generator ReLU
     (1, "relu", 1, 1e-6, True, True, 1, 4, 2, 300, 64, 64, 64, False),
