@@ -823,18 +823,37 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel64(BwdArgs args) {
 
 // rstarts[c][j] = ds_out[c] + sum over segments i > j and the G query heads of
 // chain c of the pre-pass partials (partial index ((c G + h)(P - 1) + i - 1) R
-// + r), in a fixed order; E elements per state (d dv, a multiple of 256).
+// + r), in a fixed order (segments from the last, then heads, then parts); E
+// elements per state (d dv, a multiple of 256).  The partials are independent
+// loads, issued kRScanBatch at a time ahead of the additions.
+constexpr int kRScanBatch = 16;
+
 __global__ __launch_bounds__(256) void scan_rstarts(const float* __restrict__ partial, float* __restrict__ rstarts,
                                                     const float* ds_out, int G, int P, int R, int E) {
   const int64_t gid = int64_t(blockIdx.x) * 256 + threadIdx.x;
   const int64_t c = gid / E;
   const int e = int(gid % E);
+  const int GR = G * R, n = (P - 1) * GR;  // partials of the chain, in summation order
+  float* rc = rstarts + c * P * E + e;
   float run = ds_out ? ds_out[c * E + e] : 0.0f;
-  for (int j = P - 1; j >= 0; --j) {
-    rstarts[(c * P + j) * E + e] = run;
-    if (j >= 1)
-      for (int h = 0; h < G; ++h)
-        for (int r = 0; r < R; ++r) run += partial[(((c * G + h) * (P - 1) + (j - 1)) * R + r) * E + e];
+  rc[int64_t(P - 1) * E] = run;
+  for (int b = 0; b < n; b += kRScanBatch) {
+    float x[kRScanBatch];
+#pragma unroll
+    for (int i = 0; i < kRScanBatch; ++i) {
+      // summation step s adds head h, part r of segment j = P - 1 - s / GR
+      // (past the end: the last step again, so no load is conditional)
+      const int s = b + i < n ? b + i : n - 1, j = P - 1 - s / GR, h = (s / R) % G, r = s % R;
+      x[i] = partial[(((c * G + h) * (P - 1) + (j - 1)) * R + r) * E + e];
+    }
+#pragma unroll
+    for (int i = 0; i < kRScanBatch; ++i) {
+      const int s = b + i;
+      if (s < n) {
+        run += x[i];
+        if ((s + 1) % GR == 0) rc[int64_t(P - 2 - s / GR) * E] = run;
+      }
+    }
   }
 }
 

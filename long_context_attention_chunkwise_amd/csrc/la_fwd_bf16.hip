@@ -1073,32 +1073,61 @@ __global__ __launch_bounds__(kPartThreads, part_wgs_per_cu(HD)) void state_parts
 
 // starts[c][j] = s_in[c] + sum over segments i < j and parts r of partial[c][i][r],
 // accumulated in that fixed order; E elements per chain (d*dv for the state,
-// d for the normaliser sums), `total` threads.
+// d for the normaliser sums), `total` threads.  A thread's partials are
+// independent loads, issued kScanBatch at a time ahead of the additions (the
+// batch's tail re-reads the last partial instead of branching, which would
+// make the compiler wait for each load before the next), so a scan waits a
+// few memory latencies instead of one per partial.
+constexpr int kScanBatch = 16;
+
 __global__ __launch_bounds__(256) void scan_starts(const float* __restrict__ partial, float* __restrict__ starts,
                                                    const float* s_in, int P, int R, int E, int64_t total) {
   const int64_t gid = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (gid >= total) return;
   const int64_t c = gid / E;
   const int e = int(gid % E);
+  const int n = (P - 1) * R;  // the chain's partials, in summation order
+  const float* pc = partial + c * n * E + e;
+  float* sc = starts + c * P * E + e;
   float run = s_in ? s_in[c * E + e] : 0.0f;
-  for (int j = 0; j < P; ++j) {
-    starts[(c * P + j) * E + e] = run;
-    if (j < P - 1)
-      for (int r = 0; r < R; ++r) run += partial[((c * (P - 1) + j) * R + r) * E + e];
+  sc[0] = run;
+  int r = 0, j = 0;
+  for (int b = 0; b < n; b += kScanBatch) {
+    float x[kScanBatch];
+#pragma unroll
+    for (int i = 0; i < kScanBatch; ++i) x[i] = pc[int64_t(b + i < n ? b + i : n - 1) * E];  // no branch
+#pragma unroll
+    for (int i = 0; i < kScanBatch; ++i)
+      if (b + i < n) {
+        run += x[i];
+        if (++r == R) {
+          r = 0;
+          sc[int64_t(++j) * E] = run;
+        }
+      }
   }
 }
 
 // s_out[c][e] = s_in[c][e] (0 without s_in) + sum over r < R of
 // partial[c][r][e], added in order of r; E elements per state.  s_out may be
-// s_in (each thread reads its element before writing it).
+// s_in (each thread reads its element before writing it).  Loads are batched
+// as in scan_starts.
 __global__ __launch_bounds__(256) void sum_parts(const float* __restrict__ partial, const float* s_in, float* s_out,
                                                  int R, int E, int64_t total) {
   const int64_t gid = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (gid >= total) return;
   const int64_t c = gid / E;
   const int e = int(gid % E);
+  const float* pc = partial + c * R * E + e;
   float run = s_in ? s_in[gid] : 0.0f;
-  for (int r = 0; r < R; ++r) run += partial[(c * R + r) * E + e];
+  for (int b = 0; b < R; b += kScanBatch) {
+    float x[kScanBatch];
+#pragma unroll
+    for (int i = 0; i < kScanBatch; ++i) x[i] = pc[int64_t(b + i < R ? b + i : R - 1) * E];
+#pragma unroll
+    for (int i = 0; i < kScanBatch; ++i)
+      if (b + i < R) run += x[i];
+  }
   s_out[gid] = run;
 }
 
