@@ -53,6 +53,22 @@ constexpr int kPartThreads = 256;
 // Pre-pass workgroups resident per compute unit (registers: two load slots).
 constexpr int part_wgs_per_cu(int hd) { return hd == 128 ? 2 : 3; }
 
+// Shifted segment boundaries (plan flag `shifted`): the inner boundaries of
+// KV chain c sit seg_shift(c) blocks before the multiples of the segment
+// length, an odd number from -15 to 15 over sixteen chains.  All workgroups
+// walk their segments in step, so with plain boundaries every chain's q, o,
+// k and v streams stand at the same offsets at the same moment, and a
+// placement of the caller's buffers in which those offsets collide in the
+// memory system slows every workgroup at once (measured at 1M tokens: one
+// (q, o) buffer pair 17.9 ms against 16.1-16.8 for others); sixteen phases
+// of two blocks each spread the collisions (17.0-17.4 ms for that pair).
+__device__ __forceinline__ int64_t seg_shift(int64_t c) { return (c % 16 - 8) * 2 + 1; }
+
+// First block of segment j of chain c (j < P; segment P - 1 ends at nblocks).
+__device__ __forceinline__ int64_t seg_first(int64_t j, int64_t blocks_per_seg, int64_t shift) {
+  return j == 0 ? 0 : j * blocks_per_seg - shift;
+}
+
 struct __align__(16) MainSmem {
   uint16_t k[2][C * ROWKV];
   uint16_t v[2][C * ROWKV];
@@ -408,7 +424,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
     const uint16_t* q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     void* o, const float* starts, const float* s_in, float* s_out, int Hq, int Hkv, int subgroups,
     int64_t N, int64_t nblocks, int64_t blocks_per_seg, int P, const float* zstarts, const float* z_in,
-    float* z_out, float eps, int gw, const uint16_t* __restrict__ qx, float* __restrict__ rpart) {
+    float* z_out, float eps, int gw, const uint16_t* __restrict__ qx, float* __restrict__ rpart, int shifted) {
   constexpr bool kN = (FL & kNorm) != 0;
   constexpr bool kR = (FL & kRelu) != 0;
   static_assert(!RS || (FL == 0 && !PARTIAL), "R sums: plain forward over four query heads");
@@ -433,8 +449,10 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_g4(
   const int bg = chain / subgroups;  // b * Hkv + g
   const int b = bg / Hkv, g = bg % Hkv;
   const int G = Hq / Hkv;
-  const int64_t blk0 = int64_t(seg) * blocks_per_seg;
-  const int64_t blk1 = blk0 + blocks_per_seg < nblocks ? blk0 + blocks_per_seg : nblocks;
+  const int64_t shift = shifted ? seg_shift(bg) : 0;
+  const int64_t blk0 = seg_first(seg, blocks_per_seg, shift);
+  const int64_t blk_end = seg == P - 1 ? nblocks : seg_first(seg + 1, blocks_per_seg, shift);
+  const int64_t blk1 = blk_end < nblocks ? blk_end : nblocks;
   const bool rs_on = RS && seg > 0;
 
   // query heads of this workgroup: 4, or gw when PARTIAL (waves w >= gw idle)
@@ -977,7 +995,7 @@ __global__ __launch_bounds__(kPartThreads, part_wgs_per_cu(HD)) void state_parts
                                                            float* __restrict__ zpart, int64_t N,
                                                            int64_t nblocks, int64_t blocks_per_seg,
                                                            int64_t blocks_per_part, int P, int R,
-                                                           int seg_offset) {
+                                                           int seg_offset, int shifted) {
   // head size HD = d = dv (64 or 128), as in fwd_bf16_g4
   constexpr int NDT = HD / 16, WC = HD / 4, NJ = WC / 16, RKV = HD + 16, CPR = HD / 8, RPP = 256 / CPR;
   __shared__ __align__(16) uint16_t ksm[C * RKV];
@@ -990,9 +1008,12 @@ __global__ __launch_bounds__(kPartThreads, part_wgs_per_cu(HD)) void state_parts
   const int rem = blockIdx.x % per_chain;
   const int j = rem / R, r = rem % R;
   const int64_t js = int64_t(j) + seg_offset;  // segment summed by this part
-  const int64_t seg_end = (js + 1) * blocks_per_seg;
-  int64_t b0 = js * blocks_per_seg + int64_t(r) * blocks_per_part;
-  int64_t b1 = b0 + blocks_per_part;
+  // shifted boundaries (forward pre-pass only, js + 1 < P): the last part runs
+  // to the segment's end, which may lie up to 15 blocks past R parts
+  const int64_t shift = shifted ? seg_shift(c) : 0;
+  const int64_t seg_end = seg_first(js + 1, blocks_per_seg, shift);
+  int64_t b0 = seg_first(js, blocks_per_seg, shift) + int64_t(r) * blocks_per_part;
+  int64_t b1 = r == R - 1 ? seg_end : b0 + blocks_per_part;
   if (b1 > seg_end) b1 = seg_end;
   if (b1 > nblocks) b1 = nblocks;
 
@@ -1277,11 +1298,11 @@ void launch_g4(dim3 grid, hipStream_t stream, const void* q, const void* k, cons
                const float* starts, const float* s_in, float* s_out, int Hq, int Hkv, int subgroups, int64_t N,
                int64_t nblocks, int64_t bps, int P, const float* zstarts = nullptr, const float* z_in = nullptr,
                float* z_out = nullptr, float eps = 0.0f, int gw = 4, const void* qx = nullptr,
-               float* rpart = nullptr) {
+               float* rpart = nullptr, bool shifted = false) {
   hipLaunchKernelGGL((fwd_bf16_g4<OUT_F32, FL, HD, PARTIAL, RS>), grid, dim3(256), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), o, starts, s_in, s_out, Hq, Hkv, subgroups, N, nblocks, bps,
-                     P, zstarts, z_in, z_out, eps, gw, static_cast<const uint16_t*>(qx), rpart);
+                     P, zstarts, z_in, z_out, eps, gw, static_cast<const uint16_t*>(qx), rpart, int(shifted));
 }
 
 template <int GW, bool OUT_F32, int FL = 0>
@@ -1309,10 +1330,12 @@ hipError_t launch_segment_states(const void* k, const void* v, const float* s_in
     const auto* v16 = static_cast<const uint16_t*>(v);
     if (plan.hd == 64)
       hipLaunchKernelGGL((state_parts<0, 64>), grid, dim3(kPartThreads), 0, stream, k16, v16, partial, nullptr, N,
-                         plan.nblocks, plan.blocks_per_seg, plan.blocks_per_part, plan.P, plan.R, 0);
+                         plan.nblocks, plan.blocks_per_seg, plan.blocks_per_part, plan.P, plan.R, 0,
+                         int(plan.shifted));
     else
       hipLaunchKernelGGL((state_parts<0, 128>), grid, dim3(kPartThreads), 0, stream, k16, v16, partial, nullptr, N,
-                         plan.nblocks, plan.blocks_per_seg, plan.blocks_per_part, plan.P, plan.R, 0);
+                         plan.nblocks, plan.blocks_per_seg, plan.blocks_per_part, plan.P, plan.R, 0,
+                         int(plan.shifted));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1345,10 +1368,10 @@ hipError_t launch_state_parts(const void* a, const void* b, float* partial, int6
   const auto* b16 = static_cast<const uint16_t*>(b);
   if (hd == 64)
     hipLaunchKernelGGL((state_parts<0, 64>), grid, dim3(kPartThreads), 0, stream, a16, b16, partial, nullptr, N,
-                       nblocks, blocks_per_seg, blocks_per_part, P, R, seg_offset);
+                       nblocks, blocks_per_seg, blocks_per_part, P, R, seg_offset, 0);
   else if (hd == 128)
     hipLaunchKernelGGL((state_parts<0, 128>), grid, dim3(kPartThreads), 0, stream, a16, b16, partial, nullptr, N,
-                       nblocks, blocks_per_seg, blocks_per_part, P, R, seg_offset);
+                       nblocks, blocks_per_seg, blocks_per_part, P, R, seg_offset, 0);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -1370,7 +1393,7 @@ hipError_t variant_states(const void* k, const void* v, const float* s_in, const
   if (Ppre > 1) {
     hipLaunchKernelGGL((state_parts<FL, HD>), dim3(unsigned(kv_chains * (Ppre - 1) * p.R)), dim3(kPartThreads), 0,
                        stream, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), partial, zpart, N,
-                       p.nblocks, p.blocks_per_seg, p.blocks_per_part, Ppre, p.R, 0);
+                       p.nblocks, p.blocks_per_seg, p.blocks_per_part, Ppre, p.R, 0, int(p.shifted));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1412,8 +1435,11 @@ hipError_t variant_outputs(const void* q, const void* k, const void* v, void* o,
         launch_g4<OUT_F32, FL, 64, true>(grid, stream, q, k, v, o, st ? starts : nullptr, st ? nullptr : s_in,
                                          s_out, iHq, iHkv, p.subgroups, N, p.nblocks, p.blocks_per_seg, p.P, zs, zi,
                                          z_out, eps, p.gw);
-    } else if (p.gw == 4) LA_VAR((launch_g4<OUT_F32, FL>));
-    else if (p.gw == 2) LA_VAR((launch_main<2, OUT_F32, FL>));
+    } else if (p.gw == 4) {
+      launch_g4<OUT_F32, FL>(grid, stream, q, k, v, o, st ? starts : nullptr, st ? nullptr : s_in, s_out, iHq, iHkv,
+                             p.subgroups, N, p.nblocks, p.blocks_per_seg, p.P, zs, zi, z_out, eps, 4, nullptr,
+                             nullptr, p.shifted);
+    } else if (p.gw == 2) LA_VAR((launch_main<2, OUT_F32, FL>));
     else LA_VAR((launch_main<1, OUT_F32, FL>));
 #undef LA_VAR
   } else {
@@ -1510,10 +1536,12 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
     const float* si = plan.use_starts ? nullptr : s_in;
     if (out_f32)
       launch_g4<true>(grid, stream, q, k, v, o, starts, si, s_out, iHq, iHkv, plan.subgroups, N, plan.nblocks,
-                      plan.blocks_per_seg, plan.P);
+                      plan.blocks_per_seg, plan.P, nullptr, nullptr, nullptr, 0.0f, 4, nullptr, nullptr,
+                      plan.shifted);
     else
       launch_g4<false>(grid, stream, q, k, v, o, starts, si, s_out, iHq, iHkv, plan.subgroups, N, plan.nblocks,
-                       plan.blocks_per_seg, plan.P);
+                       plan.blocks_per_seg, plan.P, nullptr, nullptr, nullptr, 0.0f, 4, nullptr, nullptr,
+                       plan.shifted);
   } else if (plan.gw == 2) {
     if (out_f32) LA_MAIN(2, true); else LA_MAIN(2, false);
   } else {

@@ -17,7 +17,11 @@ namespace la {
 // chip.  Segment j starts from s_in + sum over earlier segments of K_b^T V_b
 // (exact by associativity).  Those earlier sums are produced by a pre-pass
 // that splits every segment but the last into R parts, and a scan that adds
-// the parts up in a fixed order.
+// the parts up in a fixed order.  With `shifted`, every inner boundary of
+// chain c moves by a small per-chain number of blocks (the first and last
+// segments absorb it), so that the chains' concurrent streams do not all sit
+// at the same offsets; the pre-pass and the output kernel use the same
+// boundaries.
 struct Bf16Plan {
   int64_t nblocks = 0;          // ceil(N / 64)
   int hd = 128;                 // head size d = dv (128; 64 for groups of four query heads)
@@ -29,6 +33,7 @@ struct Bf16Plan {
   int64_t blocks_per_seg = 0;
   int64_t blocks_per_part = 0;
   bool use_starts = false;      // segment start states come from the workspace
+  bool shifted = false;         // segment boundaries moved per KV chain (seg_shift in la_fwd_bf16.hip)
   size_t partial_floats = 0;    // B*Hkv*(P-1)*R*d*dv
   size_t start_floats = 0;      // B*Hkv*P*d*dv
   size_t workspace_bytes = 0;

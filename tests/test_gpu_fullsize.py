@@ -49,7 +49,9 @@ def test_gqa_1m_slices_and_states(workload):
     across the boundaries of segments 0/1 and 3/4; the final state of every
     KV head (each against an fp64 GEMM over all its tokens) and the start state
     of every segment of KV heads 0, 13 and 31 as the pre-pass left it in the
-    workspace, at the state bar; finiteness of every output and bitwise
+    workspace, at the state bar (at head size 128 the inner segment boundaries
+    of KV head g sit ((g mod 16) - 8) * 2 + 1 blocks before the multiples of
+    the segment length: heads 0, 13 and 31 cover shifts -15, 11 and 15); finiteness of every output and bitwise
     repeatability of the whole pass; the final states once more from the
     state-only call (la_forward_state).  For the 128-head-size workload the same
     slices are checked once more with float32 output at the literal 2e-2 RMS.
@@ -86,6 +88,16 @@ def test_gqa_1m_slices_and_states(workload):
     # workgroups per compute unit), 32 in 1 part (one-wave workgroups: head size 64, Hq = Hkv)
     nseg, nparts = (32, 1) if (w.d == 64 and w.Hq == w.Hkv) else (8, 2 if w.d == 128 else 3)
     seg = w.N // nseg
+    shifted = w.d == 128 and G % 4 == 0
+
+    def bound(g, j):
+        """First token of segment j of KV head g, as the library places it."""
+        if j == 0:
+            return 0
+        if j == nseg:
+            return w.N
+        return j * seg - ((((g % 16) - 8) * 2 + 1) * w.block if shifted else 0)
+
     assert ws_bytes == (w.Hkv * (nseg - 1) * nparts + w.Hkv * nseg) * w.d * w.dv * 4
     # segment start states as the pre-pass and scan left them: [Hkv][segment][d][dv] after the partials
     starts = ws.view(torch.float32)[w.Hkv * (nseg - 1) * nparts * w.d * w.dv:].view(w.Hkv, nseg, w.d, w.dv)
@@ -124,11 +136,11 @@ def test_gqa_1m_slices_and_states(workload):
         for j in range(nseg):
             check_state(f"group {g} segment {j} start state", f64(starts[g, j])[None, None], ref_j,
                         torch.bfloat16)
-            ref_j = oracle.final_state(ks_all[:, :, j * seg:(j + 1) * seg], vs_all[:, :, j * seg:(j + 1) * seg],
-                                       ref_j)
+            a, b = bound(g, j), bound(g, j + 1)
+            ref_j = oracle.final_state(ks_all[:, :, a:b], vs_all[:, :, a:b], ref_j)
         check_slice(g, 0, W, None)
         # windows across the boundaries of segments 0/1 and 3/4, from the fp64 state before them
-        for c in (seg, 4 * seg):
+        for c in (bound(g, 1), bound(g, 4)):
             a, b = c - 4096, c + 4096
             check_slice(g, a, b, oracle.final_state(ks_all[:, :, :a], vs_all[:, :, :a]))
         a = w.N - W
