@@ -116,13 +116,14 @@ Bf16Plan plan_bf16(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int
     R = (p.blocks_per_seg + p.blocks_per_part - 1) / p.blocks_per_part;
     p.R = static_cast<int>(R);
   }
-  // Boundaries shifted per KV chain by up to 15 blocks (the four-head kernel
-  // at head size 128, long segments only: the longest segment grows by at
-  // most 15 blocks, under 1.5%).  Measured at 1M tokens on the same buffer
-  // pairs: a pair whose streams collided in the memory system went from 17.9
-  // to 17.0-17.4 ms, the others stayed within -0.3 to +0.02 ms.
+  // Boundaries shifted per KV chain by up to 15 blocks (the four-head kernel,
+  // long segments only: the longest segment grows by at most 15 blocks, under
+  // 1.5%).  Measured at 1M tokens on the same buffer pairs: at head size 128
+  // a pair whose streams collided in the memory system went from 17.9 to
+  // 17.0-17.4 ms and no pair got slower; at 64 the mean over four pairs went
+  // from 8.77 to 8.66 ms.
   constexpr int64_t kShiftMinBlocks = 1024;
-  p.shifted = P > 1 && d == 128 && p.gw == 4 && !p.solo && p.blocks_per_seg >= kShiftMinBlocks &&
+  p.shifted = P > 1 && p.gw == 4 && !p.solo && p.blocks_per_seg >= kShiftMinBlocks &&
               p.nblocks - (P - 1) * p.blocks_per_seg >= 32;
   p.use_starts = (P > 1) || (p.subgroups > 1);
   if (p.use_starts) {

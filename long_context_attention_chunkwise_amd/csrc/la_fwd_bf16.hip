@@ -1430,7 +1430,10 @@ hipError_t variant_outputs(const void* q, const void* k, const void* v, void* o,
                          st ? starts : nullptr, st ? nullptr : s_in, s_out, N, p.nblocks, p.blocks_per_seg, p.P, zs,
                          zi, z_out, eps);
     } else if (p.hd == 64) {
-      if (p.gw == 4) LA_VAR((launch_g4<OUT_F32, FL, 64>));
+      if (p.gw == 4)
+        launch_g4<OUT_F32, FL, 64>(grid, stream, q, k, v, o, st ? starts : nullptr, st ? nullptr : s_in, s_out, iHq,
+                                   iHkv, p.subgroups, N, p.nblocks, p.blocks_per_seg, p.P, zs, zi, z_out, eps, 4,
+                                   nullptr, nullptr, p.shifted);
       else
         launch_g4<OUT_F32, FL, 64, true>(grid, stream, q, k, v, o, st ? starts : nullptr, st ? nullptr : s_in,
                                          s_out, iHq, iHkv, p.subgroups, N, p.nblocks, p.blocks_per_seg, p.P, zs, zi,
@@ -1523,7 +1526,8 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
     const float* si = plan.use_starts ? nullptr : s_in;
 #define LA_G64(F32, PART)                                                                                     \
   launch_g4<F32, 0, 64, PART>(grid, stream, q, k, v, o, starts, si, s_out, iHq, iHkv, plan.subgroups, N,     \
-                              plan.nblocks, plan.blocks_per_seg, plan.P, nullptr, nullptr, nullptr, 0.0f, plan.gw)
+                              plan.nblocks, plan.blocks_per_seg, plan.P, nullptr, nullptr, nullptr, 0.0f, plan.gw, \
+                              nullptr, nullptr, plan.shifted)
     if (plan.gw == 4) {
       if (out_f32) LA_G64(true, false); else LA_G64(false, false);
     } else {

@@ -49,9 +49,10 @@ def test_gqa_1m_slices_and_states(workload):
     across the boundaries of segments 0/1 and 3/4; the final state of every
     KV head (each against an fp64 GEMM over all its tokens) and the start state
     of every segment of KV heads 0, 13 and 31 as the pre-pass left it in the
-    workspace, at the state bar (at head size 128 the inner segment boundaries
-    of KV head g sit ((g mod 16) - 8) * 2 + 1 blocks before the multiples of
-    the segment length: heads 0, 13 and 31 cover shifts -15, 11 and 15); finiteness of every output and bitwise
+    workspace, at the state bar (with four query heads per KV head the inner
+    segment boundaries of KV head g sit ((g mod 16) - 8) * 2 + 1 blocks before
+    the multiples of the segment length: heads 0, 13 and 31 cover shifts -15,
+    11 and 15); finiteness of every output and bitwise
     repeatability of the whole pass; the final states once more from the
     state-only call (la_forward_state).  For the 128-head-size workload the same
     slices are checked once more with float32 output at the literal 2e-2 RMS.
@@ -88,7 +89,7 @@ def test_gqa_1m_slices_and_states(workload):
     # workgroups per compute unit), 32 in 1 part (one-wave workgroups: head size 64, Hq = Hkv)
     nseg, nparts = (32, 1) if (w.d == 64 and w.Hq == w.Hkv) else (8, 2 if w.d == 128 else 3)
     seg = w.N // nseg
-    shifted = w.d == 128 and G % 4 == 0
+    shifted = G % 4 == 0  # the four-head kernel (not the one-wave one)
 
     def bound(g, j):
         """First token of segment j of KV head g, as the library places it."""
