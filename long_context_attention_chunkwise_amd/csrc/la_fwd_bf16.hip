@@ -1009,8 +1009,8 @@ __global__ __launch_bounds__(kPartThreads, part_wgs_per_cu(HD)) void state_parts
   const int j = rem / R, r = rem % R;
   const int64_t js = int64_t(j) + seg_offset;  // segment summed by this part
   // shifted boundaries (pre-passes of the forward and the causal variants,
-  // js + 1 < P): the last part runs
-  // to the segment's end, which may lie up to 15 blocks past R parts
+  // js + 1 < P): the last part runs to the segment's end, which may lie up to
+  // 15 blocks past R parts
   const int64_t shift = shifted ? seg_shift(c) : 0;
   const int64_t seg_end = seg_first(js + 1, blocks_per_seg, shift);
   int64_t b0 = seg_first(js, blocks_per_seg, shift) + int64_t(r) * blocks_per_part;
