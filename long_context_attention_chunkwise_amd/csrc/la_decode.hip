@@ -55,24 +55,25 @@ __device__ __forceinline__ float load_in(const void* p, int64_t i) {
   return static_cast<const float*>(p)[i];
 }
 
-// G: query heads served by this launch.  CHUNKED: one chunk [h0, h0 + G) of a
-// larger group of Gfull heads (otherwise the whole group, Gfull = G, h0 = 0);
+// One state's step (state bg = b * Hkv + g).  G: query heads served by this
+// launch.  CHUNKED: one chunk [h0, h0 + G) of a larger group of Gfull heads
+// (otherwise the whole group, Gfull = G, h0 = 0);
 // UPDATE: add k^T v to the state and write it back (otherwise read only).
 // WRED (wave-level reduction, dv = 128 only: a wave is two row groups of 32
 // column groups): the two row groups of each wave are first added with a
 // cross-half lane exchange, so only the eight waves' partials pass through
 // LDS; otherwise every row group's partial does.
 template <int G, bool IN_BF16, bool OUT_F32, bool CHUNKED, bool UPDATE, bool WRED = false>
-__global__ __launch_bounds__(kThreads) void decode_kernel(float* __restrict__ S, const void* __restrict__ q,
+__device__ __forceinline__ void decode_body(float* __restrict__ S, const void* __restrict__ q,
                                                          const void* __restrict__ k, const void* __restrict__ v,
                                                          void* __restrict__ o, int Hkv, int d, int dv, int Gfull,
-                                                         int h0) {
+                                                         int h0, int bg_in) {
   __shared__ float qs[G][kMaxD];
   __shared__ float ks[kMaxD];
   __shared__ float vs[kMaxDV];
   __shared__ float4 red[(WRED ? kThreads / 2 : kThreads) * G];  // [row group or wave][head][column group]
 
-  const int bg = blockIdx.x;  // b * Hkv + g
+  const int bg = bg_in;  // b * Hkv + g
   const int tid = threadIdx.x;
   // first query head served, flattened over batch
   const int64_t hq0 = CHUNKED ? int64_t(bg) * Gfull + h0 : int64_t(bg) * G;
@@ -158,15 +159,33 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(float* __restrict__ S,
   }
 }
 
+// One workgroup per state, written as a loop over states with the grid's
+// stride (one pass per workgroup as launched): the compiler schedules this
+// form's loads and stores differently, measured 190.3 against 192.2 us per
+// step on the 256-sequence workload (same results bit for bit); grids of two
+// to four workgroups per compute unit that loop over several states each
+// measured slower (193.5-215 us).
+template <int G, bool IN_BF16, bool OUT_F32, bool CHUNKED, bool UPDATE, bool WRED = false>
+__global__ __launch_bounds__(kThreads) void decode_kernel(float* __restrict__ S, const void* __restrict__ q,
+                                                         const void* __restrict__ k, const void* __restrict__ v,
+                                                         void* __restrict__ o, int Hkv, int d, int dv, int Gfull,
+                                                         int h0, int nstates) {
+  for (int bg = blockIdx.x; bg < nstates; bg += gridDim.x) {
+    decode_body<G, IN_BF16, OUT_F32, CHUNKED, UPDATE, WRED>(S, q, k, v, o, Hkv, d, dv, Gfull, h0, bg);
+    __syncthreads();
+  }
+}
+
 template <int G, bool CHUNKED, bool UPDATE>
 hipError_t launch_g(float* S, const void* q, const void* k, const void* v, void* o, bool in_bf16, bool out_f32,
                     int64_t B, int64_t Hkv, int64_t d, int64_t dv, int Gfull, int h0, hipStream_t stream) {
-  const dim3 grid(unsigned(B * Hkv)), block(kThreads);
+  const int64_t ns = B * Hkv;
+  const dim3 grid(static_cast<unsigned>(ns)), block(kThreads);
   const int iHkv = int(Hkv), id = int(d), idv = int(dv);
   // dv = 128: the wave-level reduction (each wave is exactly two row groups)
 #define LA_DEC(BF, F32, WR)                                                                                       \
   hipLaunchKernelGGL((decode_kernel<G, BF, F32, CHUNKED, UPDATE, WR>), grid, block, 0, stream, S, q, k, v, o, iHkv, \
-                     id, idv, Gfull, h0)
+                     id, idv, Gfull, h0, int(ns))
   if (dv == kMaxDV) {
     if (in_bf16) {
       if (out_f32) LA_DEC(true, true, true);
